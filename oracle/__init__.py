@@ -1,0 +1,214 @@
+"""CPU oracle for one rank's share of tensor-parallel linear layers.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import this module.  The GPU library never
+imports, links or runs it, and it imports nothing from the GPU library.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, naive
+loops); this module marshals numpy arrays to it and does the slicing with
+plain numpy indexing.  Pages cited (by title and section):
+
+* mlxcel manual, "Tensor parallelism" (텐서 병렬화) -- sections "Column
+  Parallel", "Row Parallel", "Replicated", "Architecture-aware shard plan",
+  "GQA-aware attention sharding", "Configuration".
+* wiki entry "Tensor parallel processing" (텐서 병렬 처리) -- "Details" §1
+  (column: Y = [X W_1, ..., X W_n]; row: Y = sum_i X_i W_i) and "Examples"
+  §1 (the column-parallel simulation: concat of the shard outputs).
+
+Every function here has a pin in ``tests/test_oracle.py`` against something
+other than itself (closed forms, invariants, library routines, the pages'
+worked shapes and examples).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+# plan record layout (one int64 per field)
+FIELDS = ("proj", "rank", "strategy", "combine", "K", "N", "k_off", "k_len",
+          "n_off", "n_len", "head_off", "head_cnt")
+PROJS = ("q", "k", "v", "o", "gate", "up", "down")
+COLUMN, ROW, REPLICATED = 0, 1, 2
+NONE, CONCAT, SUM = 0, 1, 2
+
+# error classes of oracle_plan
+OK, INVALID, NOT_DIVISIBLE, TP_NOT_POW2, GROUP_ALIGN = 0, -1, -2, -3, -4
+
+
+class OracleError(ValueError):
+    def __init__(self, code):
+        super().__init__("oracle_plan rejected the dimensions (class %d)" % code)
+        self.code = code
+
+
+def lib():
+    """Load liboracle.so, compiling it with gcc first if it is missing."""
+    global _LIB
+    if _LIB is None:
+        path = os.path.join(HERE, "liboracle.so")
+        if not os.path.exists(path):
+            from . import build as _build
+            _build.build()
+        L = ctypes.CDLL(path)
+        i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        L.oracle_plan.argtypes = [i32] * 7 + [vp, i64]
+        L.oracle_plan.restype = ctypes.c_int
+        L.oracle_plan_linear.argtypes = [i64, i64, i32, i32, i32, vp, i64]
+        L.oracle_plan_linear.restype = ctypes.c_int
+        L.oracle_bf16_to_f64.argtypes = [vp, vp, i64]
+        L.oracle_f64_to_bf16_rne.argtypes = [vp, vp, i64]
+        L.oracle_dequant_q4.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        L.oracle_gemm.argtypes = [vp, vp, vp, i64, i64, i64]
+        L.oracle_gemm_at.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp]
+        L.oracle_sum.argtypes = [vp, i64, i64, vp]
+        L.oracle_sum_f32_seq.argtypes = [vp, i64, i64, vp]
+        for f in ("oracle_bf16_to_f64", "oracle_f64_to_bf16_rne", "oracle_dequant_q4",
+                  "oracle_gemm", "oracle_gemm_at", "oracle_sum", "oracle_sum_f32_seq"):
+            getattr(L, f).restype = None
+        _LIB = L
+    return _LIB
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def plan(hidden, n_q_heads, n_kv_heads, head_dim, ffn, tp, group=0):
+    """The GQA-aware shard plan: int64 array [tp][7][12] (fields FIELDS).
+
+    Raises OracleError(code) when the dimensions are rejected.
+    """
+    out = np.zeros((max(tp, 1), len(PROJS), len(FIELDS)), dtype=np.int64)
+    rc = lib().oracle_plan(hidden, n_q_heads, n_kv_heads, head_dim, ffn, tp, group,
+                           out.ctypes.data_as(ctypes.c_void_p), out.size)
+    if rc != OK:
+        raise OracleError(rc)
+    return out
+
+
+def plan_linear(K, N, tp, strategy, group=0):
+    """Shards of one lone linear W[K][N]: int64 array [tp][12]."""
+    out = np.zeros((max(tp, 1), len(FIELDS)), dtype=np.int64)
+    rc = lib().oracle_plan_linear(K, N, tp, strategy, group,
+                                  out.ctypes.data_as(ctypes.c_void_p), out.size)
+    if rc != OK:
+        raise OracleError(rc)
+    return out
+
+
+def spec(plan_array, rank, proj):
+    """One plan record as a dict."""
+    p = PROJS.index(proj) if isinstance(proj, str) else proj
+    return dict(zip(FIELDS, (int(v) for v in plan_array[rank, p])))
+
+
+def bf16_to_f64(bits):
+    bits, pb = _c(bits, np.uint16)
+    out = np.empty(bits.shape, dtype=np.float64)
+    lib().oracle_bf16_to_f64(pb, out.ctypes.data_as(ctypes.c_void_p), bits.size)
+    return out
+
+
+def f64_to_bf16(x):
+    """Round doubles to bf16 (nearest, ties to even); returns uint16 bits."""
+    x, px = _c(x, np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().oracle_f64_to_bf16_rne(px, out.ctypes.data_as(ctypes.c_void_p), x.size)
+    return out
+
+
+def dequant_q4(codes, scales, biases, group=64):
+    """W[k][n] = scale[k//group][n] * q[k][n] + bias[k//group][n], in double.
+
+    codes: uint8 [K][N] in 0..15; scales, biases: bf16 bits [K/group][N].
+    """
+    codes, pc = _c(codes, np.uint8)
+    K, N = codes.shape
+    scales, ps = _c(scales, np.uint16)
+    biases, pb = _c(biases, np.uint16)
+    assert scales.shape == (K // group, N) and biases.shape == scales.shape
+    W = np.empty((K, N), dtype=np.float64)
+    lib().oracle_dequant_q4(pc, ps, pb, K, N, group, W.ctypes.data_as(ctypes.c_void_p))
+    return W
+
+
+def gemm(X, W):
+    """Y = X W in double, naive loop with k ascending."""
+    X, px = _c(X, np.float64)
+    W, pw = _c(W, np.float64)
+    M, K = X.shape
+    K2, N = W.shape
+    assert K == K2
+    Y = np.empty((M, N), dtype=np.float64)
+    lib().oracle_gemm(px, pw, Y.ctypes.data_as(ctypes.c_void_p), M, K, N)
+    return Y
+
+
+def gemm_at(X, W, rows, cols):
+    """(X W)[rows[i], cols[i]] for each i, in double."""
+    X, px = _c(X, np.float64)
+    W, pw = _c(W, np.float64)
+    rows, pr = _c(rows, np.int64)
+    cols, pcol = _c(cols, np.int64)
+    K, N = W.shape
+    assert X.shape[1] == K and rows.shape == cols.shape
+    out = np.empty(rows.shape, dtype=np.float64)
+    lib().oracle_gemm_at(px, pw, K, N, pr, pcol, rows.size, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def slice_weight(W, s):
+    """The rank's shard of the full logical W[K][N].
+
+    Column shard: W[:, n_off:n_off+n_len]; row shard: W[k_off:k_off+k_len, :];
+    replicated: the whole W (mlxcel manual "Column Parallel", "Row Parallel",
+    "Replicated").
+    """
+    if s["strategy"] == COLUMN:
+        return W[:, s["n_off"]:s["n_off"] + s["n_len"]]
+    if s["strategy"] == ROW:
+        return W[s["k_off"]:s["k_off"] + s["k_len"], :]
+    return W
+
+
+def slice_input(X, s):
+    """The rank's input: the full X for column/replicated shards, the matching
+    column block X_i = X[:, k_off:k_off+k_len] for row shards (wiki "Details"
+    §1, row-parallel: each rank multiplies its split X_i by its W_i)."""
+    if s["strategy"] == ROW:
+        return X[:, s["k_off"]:s["k_off"] + s["k_len"]]
+    return X
+
+
+def shard_forward(s, X, W):
+    """One rank's output: slice_input(X) @ slice_weight(W), in double."""
+    return gemm(slice_input(X, s), slice_weight(W, s))
+
+
+def combine_concat(parts):
+    """Y = [Y_0, ..., Y_{n-1}] along the feature (last) dimension (wiki
+    "Details" §1, column-parallel; "Examples" §1 concatenates on the last
+    dimension)."""
+    return np.concatenate([np.asarray(p) for p in parts], axis=-1)
+
+
+def combine_sum(parts):
+    """Y = sum_i Y_i over ranks, ascending rank order, in double."""
+    P, pp = _c(np.stack([np.asarray(p, dtype=np.float64) for p in parts]), np.float64)
+    R = P.shape[0]
+    Y = np.empty(P.shape[1:], dtype=np.float64)
+    lib().oracle_sum(pp, R, Y.size, Y.ctypes.data_as(ctypes.c_void_p))
+    return Y
+
+
+def sum_f32_seq(parts):
+    """((P0 + P1) + P2) + ... in binary32, ascending rank order."""
+    P, pp = _c(np.stack([np.asarray(p, dtype=np.float32) for p in parts]), np.float32)
+    R = P.shape[0]
+    Y = np.empty(P.shape[1:], dtype=np.float32)
+    lib().oracle_sum_f32_seq(pp, R, Y.size, Y.ctypes.data_as(ctypes.c_void_p))
+    return Y

@@ -1,0 +1,71 @@
+"""Seeded synthetic inputs (numpy, PCG64).
+
+This module only draws numbers: activations, dense weights, 4-bit codes,
+scales and biases, as bf16 bit patterns, binary32 values or bytes.  It
+contains none of the sharded-linear arithmetic and is the one piece of code
+that both the GPU path's tests and the CPU oracle consume (as input bytes).
+
+Seeds are derived from (config, projection, tensor, variant) so that every
+tensor of every workload is reproducible on its own:
+    seed = 100000 * config + 1000 * projection + 10 * tensor + variant
+with tensor ids X=1, W=2, codes=3, scales=4, biases=5 and variant 0 for the
+random draw, 1 for the small-integer draw.
+"""
+import numpy as np
+
+T_X, T_W, T_CODES, T_SCALES, T_BIASES = 1, 2, 3, 4, 5
+
+
+def seed_of(config, proj, tensor, variant=0):
+    return 100000 * int(config) + 1000 * int(proj) + 10 * int(tensor) + int(variant)
+
+
+def rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def f32_to_bf16_bits(x):
+    """Round binary32 values to bf16 (nearest, ties to even): uint16 bits.
+
+    Used only to draw bf16-valued inputs; NaN is not expected here.
+    """
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (b >> 16) & 1
+    r = (b + 0x7FFF + lsb) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits):
+    """Exact widening of bf16 bit patterns to binary32 (for building inputs)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_f32(seed, shape, std=1.0):
+    return (rng(seed).standard_normal(shape, dtype=np.float32) * np.float32(std)).astype(np.float32)
+
+
+def normal_bf16(seed, shape, std=1.0):
+    """bf16 bit patterns of N(0, std^2) draws."""
+    return f32_to_bf16_bits(normal_f32(seed, shape, std))
+
+
+def small_int(seed, shape, lo=-3, hi=3):
+    """Integers uniform on {lo..hi} as binary32 values."""
+    return rng(seed).integers(lo, hi + 1, size=shape).astype(np.float32)
+
+
+def small_int_bf16(seed, shape, lo=-3, hi=3):
+    return f32_to_bf16_bits(small_int(seed, shape, lo, hi))
+
+
+def q4_codes(seed, shape):
+    """4-bit codes uniform on 0..15, one byte each."""
+    return rng(seed).integers(0, 16, size=shape, dtype=np.uint8)
+
+
+def uniform_bf16(seed, shape, lo, hi):
+    return f32_to_bf16_bits(rng(seed).uniform(lo, hi, size=shape).astype(np.float32))
+
+
+def const_bf16(shape, value):
+    return np.full(shape, f32_to_bf16_bits(np.float32(value)), dtype=np.uint16)

@@ -1,0 +1,373 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one oracle function to something the pages or mathematics
+fix: a value or shape the pages print (fixtures under tests/golden/), a
+closed form, an invariant, an exact integer result, or a library routine
+(numpy) on small inputs.  A plausible slip in the oracle -- a dropped term,
+a wrong sign, a transposed operand, a wrong slice edge or group axis, a
+wrong rounding rule or summation order -- fails at least one of them.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from conftest import golden_rows
+from tensor_sharded_linear_plan_amd import synth
+
+STRAT = {"column": oracle.COLUMN, "row": oracle.ROW}
+COMM = {"all-gather": oracle.CONCAT, "all-reduce": oracle.SUM, "none": oracle.NONE}
+
+
+# --------------------------------------------------------------------------
+# plan: the page's table, the page's GQA examples, brute-force properties
+# --------------------------------------------------------------------------
+
+def test_plan_matches_page_table():
+    # mlxcel "Architecture-aware shard plan": strategies and communication
+    rows = golden_rows("plan_table.txt")
+    for hkv, tp in ((8, 4), (4, 8)):  # K/V sharded, then replicated
+        plan = oracle.plan(2048, 32, hkv, 64, 8192, tp)
+        for r in range(tp):
+            for (name, strat, comm), proj in zip(rows, oracle.PROJS):
+                assert name == proj + "_proj"
+                s = oracle.spec(plan, r, proj)
+                if comm == "gqa":
+                    if hkv >= tp:
+                        assert (s["strategy"], s["combine"]) == (oracle.COLUMN, oracle.CONCAT)
+                    else:
+                        assert (s["strategy"], s["combine"]) == (oracle.REPLICATED, oracle.NONE)
+                else:
+                    assert s["strategy"] == STRAT[strat]
+                    assert s["combine"] == COMM[comm]
+
+
+def test_plan_gqa_examples_from_page():
+    # mlxcel "GQA-aware attention sharding", figure examples
+    for tp, hq, hkv, _printed, q_per, kv_per, mode in golden_rows("gqa_examples.txt"):
+        tp, hq, hkv, q_per = int(tp), int(hq), int(hkv), int(q_per)
+        plan = oracle.plan(4096, hq, hkv, 128, 14336, tp)
+        for r in range(tp):
+            q = oracle.spec(plan, r, "q")
+            assert (q["head_off"], q["head_cnt"]) == (r * q_per, q_per)
+            for p in ("k", "v"):
+                s = oracle.spec(plan, r, p)
+                if mode == "sharded":
+                    assert s["strategy"] == oracle.COLUMN
+                    assert (s["head_off"], s["head_cnt"]) == (r * int(kv_per), int(kv_per))
+                    assert s["n_len"] == int(kv_per) * 128
+                else:
+                    assert s["strategy"] == oracle.REPLICATED
+                    assert (s["n_off"], s["n_len"]) == (0, hkv * 128)
+
+
+def _check_plan_properties(hidden, hq, hkv, hd, ffn, tp):
+    plan = oracle.plan(hidden, hq, hkv, hd, ffn, tp)
+    for proj in oracle.PROJS:
+        specs = [oracle.spec(plan, r, proj) for r in range(tp)]
+        for r, s in enumerate(specs):
+            assert s["rank"] == r and oracle.PROJS[s["proj"]] == proj
+            assert 0 <= s["k_off"] and s["k_off"] + s["k_len"] <= s["K"]
+            assert 0 <= s["n_off"] and s["n_off"] + s["n_len"] <= s["N"]
+        strat = specs[0]["strategy"]
+        if strat == oracle.COLUMN:
+            cover = np.zeros(specs[0]["N"], dtype=int)
+            for s in specs:
+                assert s["k_off"] == 0 and s["k_len"] == s["K"]
+                cover[s["n_off"]:s["n_off"] + s["n_len"]] += 1
+            assert (cover == 1).all()  # disjoint and covering
+            assert [s["n_off"] for s in specs] == sorted(s["n_off"] for s in specs)
+        elif strat == oracle.ROW:
+            cover = np.zeros(specs[0]["K"], dtype=int)
+            for s in specs:
+                assert s["n_off"] == 0 and s["n_len"] == s["N"]
+                cover[s["k_off"]:s["k_off"] + s["k_len"]] += 1
+            assert (cover == 1).all()
+        else:
+            for s in specs:
+                assert (s["k_off"], s["k_len"], s["n_off"], s["n_len"]) == (0, s["K"], 0, s["N"])
+    for r in range(tp):
+        q, o = oracle.spec(plan, r, "q"), oracle.spec(plan, r, "o")
+        g, d = oracle.spec(plan, r, "gate"), oracle.spec(plan, r, "down")
+        # the row block of o is exactly the q columns this rank produced
+        assert (o["k_off"], o["k_len"]) == (q["n_off"], q["n_len"])
+        assert (d["k_off"], d["k_len"]) == (g["n_off"], g["n_len"])
+        assert oracle.spec(plan, r, "up")["n_off"] == g["n_off"]
+        k = oracle.spec(plan, r, "k")
+        if hkv >= tp:
+            # GQA locality: every local query head's KV head is local
+            for h in range(q["head_off"], q["head_off"] + q["head_cnt"]):
+                kvh = h // (hq // hkv)
+                assert k["head_off"] <= kvh < k["head_off"] + k["head_cnt"]
+        # shapes: q has hq/tp heads of hd
+        assert q["n_len"] == (hq // tp) * hd and q["K"] == hidden
+
+
+def test_plan_properties_brute_force():
+    count = 0
+    for tp in (1, 2, 4, 8, 16):
+        for hkv in (1, 2, 4, 8, 16):
+            for ratio in (1, 2, 4, 7):
+                hq = hkv * ratio
+                if hq % tp or (hkv >= tp and hkv % tp):
+                    continue
+                for hd, ffn in ((8, 32 * tp), (16, 48 * tp)):
+                    _check_plan_properties(64, hq, hkv, hd, ffn, tp)
+                    count += 1
+    assert count > 40
+
+
+def test_plan_rejections():
+    ok = dict(hidden=2048, n_q_heads=32, n_kv_heads=8, head_dim=64, ffn=8192, tp=4)
+    oracle.plan(**ok)
+    cases = [
+        (dict(tp=3), oracle.TP_NOT_POW2),
+        (dict(tp=6), oracle.TP_NOT_POW2),
+        (dict(tp=0), oracle.INVALID),
+        (dict(hidden=0), oracle.INVALID),
+        (dict(n_q_heads=30), oracle.NOT_DIVISIBLE),      # 30 % 8
+        (dict(n_q_heads=24, n_kv_heads=12, tp=8), oracle.NOT_DIVISIBLE),  # 12 >= 8, 12 % 8
+        (dict(ffn=8190), oracle.NOT_DIVISIBLE),
+        (dict(n_q_heads=48, n_kv_heads=8, tp=32), oracle.NOT_DIVISIBLE),  # 48 % 32
+    ]
+    for change, code in cases:
+        args = dict(ok, **change)
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.plan(**args)
+        assert e.value.code == code, change
+    # 4-bit: a row shard edge off a 64 boundary (o: 8 heads * 4 = 32 columns)
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.plan(2048, 32, 8, 4, 8192, 4, group=64)
+    assert e.value.code == oracle.GROUP_ALIGN
+    oracle.plan(2048, 32, 8, 64, 8192, 4, group=64)
+
+
+def test_plan_linear_worked_example_and_properties():
+    # wiki "Examples" §1: 1024 -> 2048 on 2 ranks -> two [1024][1024] shards
+    g = {r[0]: [int(v) for v in r[1:]] for r in golden_rows("worked_example.txt")}
+    K, N, tp = g["in_features"][0], g["out_features"][0], g["num_gpus"][0]
+    p = oracle.plan_linear(K, N, tp, oracle.COLUMN)
+    for r in range(tp):
+        s = dict(zip(oracle.FIELDS, (int(v) for v in p[r])))
+        assert [s["k_len"], s["n_len"]] == g["shard_shape"]
+        assert s["n_off"] == r * g["shard_shape"][1] and s["combine"] == oracle.CONCAT
+    p = oracle.plan_linear(K, N, tp, oracle.ROW)
+    for r in range(tp):
+        s = dict(zip(oracle.FIELDS, (int(v) for v in p[r])))
+        assert (s["k_off"], s["k_len"], s["n_len"]) == (r * 512, 512, 2048)
+        assert s["combine"] == oracle.SUM
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.plan_linear(1024, 2047, 2, oracle.COLUMN)
+    assert e.value.code == oracle.NOT_DIVISIBLE
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.plan_linear(1024, 2048, 3, oracle.COLUMN)
+    assert e.value.code == oracle.TP_NOT_POW2
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.plan_linear(192, 64, 2, oracle.ROW, group=64)  # 96-row shards
+    assert e.value.code == oracle.GROUP_ALIGN
+
+
+# --------------------------------------------------------------------------
+# GEMM: library routine, closed forms, exact integers
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K,N", [(1, 1, 1), (3, 5, 7), (32, 64, 48), (17, 200, 33), (64, 256, 128)])
+def test_gemm_vs_numpy_f64(M, K, N):
+    X = synth.normal_f32(11, (M, K)).astype(np.float64)
+    W = synth.normal_f32(12, (K, N)).astype(np.float64)
+    Y = oracle.gemm(X, W)
+    R = np.matmul(X, W)
+    assert Y.shape == (M, N)
+    assert np.max(np.abs(Y - R)) <= 1e-12 * max(1.0, np.max(np.abs(R)))
+
+
+def test_gemm_closed_forms():
+    K = 40
+    X = synth.normal_f32(21, (9, K)).astype(np.float64)
+    W = synth.normal_f32(22, (K, 13)).astype(np.float64)
+    # W = I gives Y = X exactly
+    assert np.array_equal(oracle.gemm(X, np.eye(K)), X)
+    # a one-hot row of X picks the matching row of W exactly
+    E = np.zeros((K, K))
+    E[np.arange(K), np.arange(K)[::-1]] = 1.0
+    assert np.array_equal(oracle.gemm(E, W), W[::-1])
+    # an all-ones row sums the columns of W (integer W: exact)
+    Wi = synth.small_int(23, (K, 13)).astype(np.float64)
+    assert np.array_equal(oracle.gemm(np.ones((1, K)), Wi)[0], Wi.sum(axis=0))
+    # the operand order is X @ W, not W @ X or X @ W^T: a non-square case
+    A = np.array([[1.0, 2.0, 3.0]])
+    B = np.array([[1.0, 0.0], [0.0, 10.0], [100.0, 0.0]])
+    assert np.array_equal(oracle.gemm(A, B), np.array([[301.0, 20.0]]))
+
+
+def test_gemm_integer_exact_and_sampled():
+    X = synth.small_int(31, (24, 300))
+    W = synth.small_int(32, (300, 70))
+    exact = X.astype(np.int64) @ W.astype(np.int64)
+    Y = oracle.gemm(X, W)
+    assert np.array_equal(Y, exact.astype(np.float64))
+    rows = np.array([0, 5, 23, 23, 11])
+    cols = np.array([0, 69, 0, 69, 34])
+    assert np.array_equal(oracle.gemm_at(X, W, rows, cols), exact[rows, cols].astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# The method's invariants: concat of column shards and sum of row partials
+# equal the unsharded product (wiki "Details" §1; blog: one logical layer)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tp", [1, 2, 4, 8])
+def test_column_shards_concat_to_full(tp):
+    X = synth.normal_f32(41, (16, 96)).astype(np.float64)
+    W = synth.normal_f32(42, (96, 64)).astype(np.float64)
+    full = oracle.gemm(X, W)
+    plan = oracle.plan_linear(96, 64, tp, oracle.COLUMN)
+    parts = [oracle.shard_forward(dict(zip(oracle.FIELDS, map(int, plan[r]))), X, W)
+             for r in range(tp)]
+    # bitwise: slicing columns does not change any element's k-sum
+    assert np.array_equal(oracle.combine_concat(parts), full)
+
+
+@pytest.mark.parametrize("tp", [1, 2, 4, 8])
+def test_row_shards_sum_to_full(tp):
+    Xi = synth.small_int(51, (16, 128))
+    Wi = synth.small_int(52, (128, 40))
+    plan = oracle.plan_linear(128, 40, tp, oracle.ROW)
+    specs = [dict(zip(oracle.FIELDS, map(int, plan[r]))) for r in range(tp)]
+    parts = [oracle.shard_forward(s, Xi, Wi) for s in specs]
+    exact = (Xi.astype(np.int64) @ Wi.astype(np.int64)).astype(np.float64)
+    assert np.array_equal(oracle.combine_sum(parts), exact)
+    X = synth.normal_f32(53, (16, 128)).astype(np.float64)
+    W = synth.normal_f32(54, (128, 40)).astype(np.float64)
+    full = np.matmul(X, W)
+    got = oracle.combine_sum([oracle.shard_forward(s, X, W) for s in specs])
+    assert np.max(np.abs(got - full)) <= 1e-12 * np.max(np.abs(full))
+
+
+def test_transformer_layer_shards_reassemble():
+    # every projection of a small GQA layer: sharded == unsharded
+    for hkv, tp in ((4, 2), (2, 4)):
+        plan = oracle.plan(32, 8, hkv, 4, 64, tp)
+        for pi, proj in enumerate(oracle.PROJS):
+            s0 = oracle.spec(plan, 0, proj)
+            X = synth.small_int(60 + pi, (5, s0["K"]))
+            W = synth.small_int(70 + pi, (s0["K"], s0["N"]))
+            full = (X.astype(np.int64) @ W.astype(np.int64)).astype(np.float64)
+            parts = [oracle.shard_forward(oracle.spec(plan, r, proj), X, W) for r in range(tp)]
+            if s0["strategy"] == oracle.COLUMN:
+                assert np.array_equal(oracle.combine_concat(parts), full)
+            elif s0["strategy"] == oracle.ROW:
+                assert np.array_equal(oracle.combine_sum(parts), full)
+            else:
+                for p in parts:
+                    assert np.array_equal(p, full)
+
+
+# --------------------------------------------------------------------------
+# 4-bit dequantisation
+# --------------------------------------------------------------------------
+
+def test_dequant_closed_forms_and_group_axis():
+    K, N = 192, 24
+    codes = synth.q4_codes(81, (K, N))
+    one = synth.const_bf16((K // 64, N), 1.0)
+    m8 = synth.const_bf16((K // 64, N), -8.0)
+    # scale 1, bias -8: w = q - 8 exactly
+    assert np.array_equal(oracle.dequant_q4(codes, one, m8), codes.astype(np.float64) - 8.0)
+    # scale 2, bias 0.5: w = 2q + 0.5 exactly
+    two = synth.const_bf16((K // 64, N), 2.0)
+    half = synth.const_bf16((K // 64, N), 0.5)
+    assert np.array_equal(oracle.dequant_q4(codes, two, half), 2.0 * codes + 0.5)
+    # groups run along K (64 input rows of one output column): zeroing the
+    # pair (g=1, n=5) zeroes exactly W[64:128, 5]
+    s = one.copy()
+    b = m8.copy()
+    s[1, 5] = 0
+    b[1, 5] = 0
+    W = oracle.dequant_q4(codes, s, b)
+    ref = codes.astype(np.float64) - 8.0
+    ref[64:128, 5] = 0.0
+    assert np.array_equal(W, ref)
+
+
+def test_dequant_group_sum_identity():
+    # sum_k x_k (s q_k + b) = s sum_k x_k q_k + b sum_k x_k, per group
+    K, N = 128, 6
+    codes = synth.q4_codes(91, (K, N))
+    sc = synth.uniform_bf16(92, (K // 64, N), 0.005, 0.02)
+    bi = synth.normal_bf16(93, (K // 64, N), 0.05)
+    x = synth.small_int(94, (1, K))
+    W = oracle.dequant_q4(codes, sc, bi)
+    y = oracle.gemm(x, W)[0]
+    s = oracle.bf16_to_f64(sc)
+    b = oracle.bf16_to_f64(bi)
+    alt = np.zeros(N)
+    for g in range(K // 64):
+        xs = x[0, 64 * g:64 * (g + 1)].astype(np.float64)
+        qs = codes[64 * g:64 * (g + 1)].astype(np.float64)
+        alt += s[g] * (xs @ qs) + b[g] * xs.sum()
+    assert np.max(np.abs(y - alt)) <= 1e-12 * np.max(np.abs(alt))
+
+
+# --------------------------------------------------------------------------
+# bf16 conversions
+# --------------------------------------------------------------------------
+
+def test_bf16_widening_known_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x3E80, 0x0000, 0x8000, 0x7F7F, 0x0001, 0x4300], np.uint16)
+    want = [1.0, -2.0, 0.25, 0.0, -0.0, (2 - 2 ** -7) * 2.0 ** 127, 2.0 ** -133, 128.0]
+    got = oracle.bf16_to_f64(bits)
+    assert list(got) == want
+    assert np.signbit(got[4])
+
+
+def test_bf16_rounding_rule():
+    f = oracle.f64_to_bf16
+    assert f(np.array([1 + 2 ** -8]))[0] == 0x3F80          # tie -> even (down)
+    assert f(np.array([1 + 3 * 2 ** -8]))[0] == 0x3F82      # tie -> even (up)
+    assert f(np.array([1 + 2 ** -8 + 2 ** -40]))[0] == 0x3F81  # above the tie
+    assert f(np.array([-1.5]))[0] == 0xBFC0
+    assert f(np.array([2.0 ** 200]))[0] == 0x7F80            # overflow -> inf
+    # every finite bf16 value rounds to itself
+    allbits = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    finite = allbits[(allbits & 0x7F80) != 0x7F80]
+    assert np.array_equal(f(oracle.bf16_to_f64(finite)), finite)
+    # midpoints of neighbouring positive values go to the even pattern, and
+    # anything strictly between goes to the nearer one
+    lo = np.arange(0x0001, 0x7F7F, 97, dtype=np.uint16)
+    a = oracle.bf16_to_f64(lo)
+    b = oracle.bf16_to_f64(lo + 1)
+    mid = (a + b) / 2
+    even = np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint16)
+    assert np.array_equal(f(mid), even)
+    assert np.array_equal(f(a + (b - a) * 0.25), lo)
+    assert np.array_equal(f(a + (b - a) * 0.75), (lo + 1).astype(np.uint16))
+    assert np.array_equal(f(-mid), even | 0x8000)
+
+
+# --------------------------------------------------------------------------
+# combine
+# --------------------------------------------------------------------------
+
+def test_combine_sum_and_f32_order():
+    parts = [synth.small_int(100 + r, (7, 9)) for r in range(5)]
+    exact = np.sum(np.stack(parts).astype(np.int64), axis=0).astype(np.float64)
+    assert np.array_equal(oracle.combine_sum(parts), exact)
+    # ascending-rank binary32 order: (1e8 + 1) - 1e8 == 0 in binary32
+    P = [np.array([1e8], np.float32), np.array([1.0], np.float32), np.array([-1e8], np.float32)]
+    assert oracle.sum_f32_seq(P)[0] == np.float32(0.0)
+    assert oracle.combine_sum(P)[0] == 1.0
+    # against numpy binary32 additions done one rank at a time
+    R = [synth.normal_f32(110 + r, (33, 17)) for r in range(8)]
+    acc = R[0].copy()
+    for r in R[1:]:
+        acc = (acc + r).astype(np.float32)
+    assert np.array_equal(oracle.sum_f32_seq(R), acc)
+
+
+def test_combine_concat_layout():
+    parts = [np.full((3, 2), r, dtype=np.float32) for r in range(4)]
+    Y = oracle.combine_concat(parts)
+    assert Y.shape == (3, 8)
+    assert list(Y[1]) == [0, 0, 1, 1, 2, 2, 3, 3]
