@@ -1,0 +1,263 @@
+/*
+ * tsl.h -- one rank's share of tensor-parallel linear layers on one AMD
+ * Instinct MI355X (gfx950).  C ABI; every function returns a tsl_status and
+ * nothing throws across it.
+ *
+ * The method is defined by three web pages, cited by title and section:
+ *   [mlxcel] mlxcel manual, "Tensor parallelism" (텐서 병렬화)
+ *   [wiki]   wiki entry "Tensor parallel processing" (텐서 병렬 처리)
+ *   [blog]   "How does tensor parallelism split local AI inference across
+ *            multiple GPUs?" (텐서 병렬 처리는 여러 GPU에서 로컬 AI 추론을
+ *            어떻게 분할하나요?)
+ *
+ * Notation.  A linear layer computes Y[M][N] = X[M][K] * W[K][N]; K is the
+ * input dimension (D_in), N the output dimension (D_out), M the number of
+ * token rows (batch x sequence).  [mlxcel] "Column Parallel" and "Row
+ * Parallel" draw W as [D_in x D_out]; that logical W[K][N] is the one used
+ * throughout, whatever order its bytes are stored in.
+ *
+ * Conventions shared by every entry point:
+ *   - Memory.  Every device buffer is allocated and owned by the caller
+ *     (packed weights, activations, outputs, partials, workspace).  The
+ *     library allocates nothing and frees nothing.
+ *   - Streams.  `stream` is a hipStream_t passed as void*; NULL is the null
+ *     stream.  Device work is enqueued on it asynchronously; no entry point
+ *     synchronises the device.
+ *   - Validation.  Shapes, strides, dtypes, buffer sizes and alignments are
+ *     checked on the host before anything is enqueued; a failed check
+ *     returns a negative status and has no side effects.  A HIP error from
+ *     a launch is returned as TSL_ERR_HIP.
+ *   - Alignment.  Device pointers must be 16-byte aligned; the packed-weight
+ *     and workspace buffers 256-byte aligned.
+ *   - Leading dimensions (ldx, ldy, ld_part) are in elements, not bytes.
+ */
+#ifndef TSL_H
+#define TSL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tsl_status {
+    TSL_OK = 0,
+    TSL_ERR_INVALID_ARG = -1,      /* null pointer, non-positive size, bad enum */
+    TSL_ERR_NOT_DIVISIBLE = -2,    /* a dimension does not split evenly across ranks */
+    TSL_ERR_TP_NOT_POW2 = -3,      /* tp_size is not a power of two */
+    TSL_ERR_GROUP_ALIGN = -4,      /* a 4-bit group would straddle a shard edge */
+    TSL_ERR_BUFFER_TOO_SMALL = -5, /* an output, packed or workspace buffer is short */
+    TSL_ERR_UNSUPPORTED = -6,      /* dtype combination or size the kernels do not take */
+    TSL_ERR_MISALIGNED = -7,       /* pointer or leading dimension breaks alignment */
+    TSL_ERR_HIP = -8               /* the HIP runtime reported an error */
+} tsl_status;
+
+/* How a weight is split across ranks ([mlxcel] "Weight sharding strategy"). */
+typedef enum tsl_strategy {
+    TSL_COLUMN = 0,    /* rank r holds W[:, n_off : n_off + n_len] ("Column Parallel") */
+    TSL_ROW = 1,       /* rank r holds W[k_off : k_off + k_len, :] ("Row Parallel")    */
+    TSL_REPLICATED = 2 /* every rank holds the whole W ("Replicated")                  */
+} tsl_strategy;
+
+/* How rank outputs are joined ([mlxcel] "Communication patterns"): the
+ * concat is what an all-gather of column shards yields, the sum what an
+ * all-reduce of row partials yields ([wiki] "Details" §1). */
+typedef enum tsl_combine {
+    TSL_COMBINE_NONE = 0,   /* the output stays sharded (no communication) */
+    TSL_COMBINE_CONCAT = 1, /* Y = [Y_0, ..., Y_{tp-1}] along N            */
+    TSL_COMBINE_SUM = 2     /* Y = Y_0 + ... + Y_{tp-1}, ascending rank    */
+} tsl_combine;
+
+/* Projections of a standard transformer layer, in plan order; TSL_LINEAR
+ * tags a lone linear layer planned with plan_linear(). */
+typedef enum tsl_proj {
+    TSL_Q = 0, TSL_K = 1, TSL_V = 2, TSL_O = 3,
+    TSL_GATE = 4, TSL_UP = 5, TSL_DOWN = 6,
+    TSL_NPROJ = 7,
+    TSL_LINEAR = 7
+} tsl_proj;
+
+typedef enum tsl_dtype {
+    TSL_F32 = 0,   /* IEEE binary32                                         */
+    TSL_BF16 = 1,  /* bfloat16 (upper half of a binary32)                   */
+    TSL_Q4G64 = 2  /* weights only: 4-bit codes q in 0..15, affine groups of
+                      64 input elements with a bf16 scale s and bias b:
+                      w = s * q + b                                         */
+} tsl_dtype;
+
+/* Dimensions of one transformer layer and the TP degree. */
+typedef struct tsl_dims {
+    int32_t hidden;     /* model width: q/k/v/gate/up input, o/down output */
+    int32_t n_q_heads;
+    int32_t n_kv_heads; /* grouped-query attention: n_q_heads % n_kv_heads == 0 */
+    int32_t head_dim;
+    int32_t ffn;        /* FFN width: gate/up output, down input */
+    int32_t tp_size;    /* number of ranks; a power of two */
+    int32_t group_size; /* 0 for dense weights, 64 for TSL_Q4G64 weights */
+} tsl_dims;
+
+/* One rank's share of one weight.  K, N describe the full logical W[K][N];
+ * the shard is W[k_off : k_off + k_len, n_off : n_off + n_len].  For a
+ * column shard k_len == K; for a row shard n_len == N; a replicated shard
+ * covers all of W.  head_off/head_cnt give the attention heads a q/k/v/o
+ * shard covers (-1 for FFN weights and lone linears). */
+typedef struct tsl_shard {
+    int32_t proj;     /* tsl_proj */
+    int32_t rank;
+    int32_t strategy; /* tsl_strategy */
+    int32_t combine;  /* tsl_combine */
+    int64_t K, N;
+    int64_t k_off, k_len;
+    int64_t n_off, n_len;
+    int32_t head_off, head_cnt;
+} tsl_shard;
+
+/*
+ * plan_shards -- the architecture-aware, GQA-aware shard plan of one
+ * standard transformer layer ([mlxcel] "Architecture-aware shard plan",
+ * table "Standard transformer"; "GQA-aware attention sharding").
+ *
+ *   q           column shard over query heads [r*hq/tp, (r+1)*hq/tp),
+ *               combine CONCAT (the table's all-gather)
+ *   k, v        n_kv_heads >= tp: column shard over KV heads, combine CONCAT;
+ *               n_kv_heads <  tp: TSL_REPLICATED (the full K/V projection on
+ *               every rank), combine NONE
+ *   o           row shard over the same head range as q, combine SUM
+ *   gate, up    column shard over [r*ffn/tp, (r+1)*ffn/tp), combine NONE
+ *   down        row shard over the same ffn range, combine SUM
+ *
+ * Output: out[r * TSL_NPROJ + p] for rank r and projection p; out_len is
+ * the number of records `out` can hold and must be >= tp_size * TSL_NPROJ.
+ * Errors, checked in this order: TSL_ERR_INVALID_ARG (null, a size < 1,
+ * group_size not 0 or 64, out_len short), TSL_ERR_TP_NOT_POW2 ([mlxcel]
+ * "Configuration": --tp-size must be a power of two), TSL_ERR_NOT_DIVISIBLE
+ * (n_q_heads % n_kv_heads, n_q_heads % tp, ffn % tp, or n_kv_heads >= tp
+ * with n_kv_heads % tp), TSL_ERR_GROUP_ALIGN (a 4-bit projection input or
+ * row-shard edge not on a multiple of group_size).  Host only.
+ */
+tsl_status plan_shards(const tsl_dims *dims, tsl_shard *out, int64_t out_len);
+
+/*
+ * plan_linear -- the shards of one lone linear layer W[K][N] split `tp`
+ * ways with `strategy` ([mlxcel] "Column Parallel", "Row Parallel",
+ * "Replicated"; [wiki] "Examples" §1 splits one 1024 -> 2048 layer into two
+ * column shards).  Combine is CONCAT for column, SUM for row, NONE for
+ * replicated; proj is TSL_LINEAR; heads are -1.  group_size 64 requires
+ * every row-shard edge on a group boundary.  out_len >= tp.  Host only.
+ */
+tsl_status plan_linear(int64_t K, int64_t N, int32_t tp_size, int32_t strategy,
+                       int32_t group_size, tsl_shard *out, int64_t out_len);
+
+/*
+ * pack_shard_size -- bytes of the packed, kernel-ready copy of a shard.
+ * Let Ks = shard rows (k_len), Ns = shard columns (n_len),
+ * Nt = ceil(Ns / 16).  Packed layouts (all little-endian, zero padded):
+ *   TSL_F32   [Nt][ceil(Ks/64)*4][64][4] f32: element (k, n) of the shard
+ *             sits in tile (n/16, k/16), lane ((k%16)/4)*16 + n%16, slot k%4.
+ *   TSL_BF16  [Nt][ceil(Ks/64)*2][64][8] bf16: tile (n/16, k/32),
+ *             lane ((k%32)/8)*16 + n%16, slot k%8.
+ *   TSL_Q4G64 codes [Nt][ceil(Ks/128)][64][4] u32, then at the next
+ *             256-byte boundary scale/bias pairs [Nt][ceil(Ks/128)*2][16]
+ *             u32 (bf16 scale in the low half, bf16 bias in the high half).
+ *             Code (k, n): block (n/16, k/128); with kk = k%128, word
+ *             kk/32 of lane ((kk%32)/8)*16 + n%16; with j = kk%8 the nibble
+ *             at bit 4*(j/2) for even j and 16 + 4*(j/2) for odd j.
+ *             Pair (g, n) for group g = k/64: entry [n/16][g][n%16].
+ * Errors: TSL_ERR_INVALID_ARG, TSL_ERR_GROUP_ALIGN (Q4 with k_len % 64).
+ */
+tsl_status pack_shard_size(const tsl_shard *shard, tsl_dtype wdtype, size_t *bytes);
+
+/*
+ * pack_shard -- slice a rank's shard out of the full logical W and write it
+ * in the packed layout above ([mlxcel] "Column Parallel" / "Row Parallel":
+ * rank r holds a contiguous block of columns or rows, in rank order).
+ *   W (F32/BF16): device pointer; element W[k][n] of the FULL weight is at
+ *       W[k * stride_k + n * stride_n] (stride_k = N, stride_n = 1 for a
+ *       [K][N] array; stride_k = 1, stride_n = K for an [N][K] array).
+ *   Q4G64: W points at one byte per code (values 0..15) addressed the same
+ *       way; scales and biases are device bf16 arrays addressed
+ *       [g * sb_stride_g + n * sb_stride_n] for group g = k / 64 of the
+ *       full weight.  For F32/BF16 scales/biases must be NULL.
+ *   packed: device buffer of at least pack_shard_size() bytes,
+ *       256-byte aligned.
+ * Runs one kernel on `stream`.  Source strides may be any non-negative
+ * values; the caller guarantees every addressed element lies in its
+ * allocation.  Errors: TSL_ERR_INVALID_ARG, TSL_ERR_GROUP_ALIGN,
+ * TSL_ERR_BUFFER_TOO_SMALL, TSL_ERR_MISALIGNED, TSL_ERR_HIP.
+ */
+tsl_status pack_shard(const tsl_shard *shard, tsl_dtype wdtype, const void *W, int64_t stride_k,
+                      int64_t stride_n, const void *scales, const void *biases,
+                      int64_t sb_stride_g, int64_t sb_stride_n, void *packed,
+                      size_t packed_bytes, void *stream);
+
+/*
+ * shard_linear_workspace_size -- workspace bytes shard_linear needs for
+ * this shard, weight type and row count (0 when none is needed).
+ */
+tsl_status shard_linear_workspace_size(const tsl_shard *shard, tsl_dtype wdtype, int64_t M,
+                                       size_t *bytes);
+
+/*
+ * shard_linear -- one rank's share of a linear layer ([wiki] "Details" §1:
+ * column shard Y_i = X W_i with the input replicated, row shard
+ * Y_i = X_i W_i with X_i the rank's block of input columns; [mlxcel]
+ * "Column Parallel", "Row Parallel"):
+ *     Y[m][j] (+)= sum_{i < k_len} X[m][i] * Wshard[i][j],  m < M, j < n_len
+ *   packed:  the shard packed by pack_shard with the same `wdtype`.
+ *   X:       device, xdtype, row m at X + m * ldx; k_len columns are read.
+ *            For a row shard pass the rank's block X_i -- e.g. a pointer to
+ *            column k_off of the full X with ldx = full width.
+ *   Y:       device, ydtype, row m at Y + m * ldy; n_len columns written.
+ *            For a concat-free column layer pass column n_off of the full
+ *            output with ldy = N.
+ *   accumulate: 0 stores the product; 1 adds it to Y (ydtype must be F32),
+ *            which sums rank partials in call order.
+ *   workspace: device, >= shard_linear_workspace_size() bytes (may be NULL
+ *            when that is 0); its contents on entry do not matter.
+ * Supported types: (wdtype, xdtype) = (F32, F32), (BF16, BF16),
+ * (Q4G64, BF16); ydtype F32 or BF16 (round to nearest even).  Products
+ * accumulate in binary32.  For Q4G64 with M > 16 the activations are
+ * converted to binary16 inside the kernel (exact for |x| < 65520; larger
+ * magnitudes overflow).  M may be 0 (nothing is enqueued).
+ * Errors: TSL_ERR_INVALID_ARG, TSL_ERR_UNSUPPORTED,
+ * TSL_ERR_BUFFER_TOO_SMALL, TSL_ERR_MISALIGNED (X, Y 16-byte aligned;
+ * ldx, ldy multiples of 8 for 16-bit and of 4 for 32-bit types), TSL_ERR_HIP.
+ */
+tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, const void *packed,
+                        size_t packed_bytes, tsl_dtype xdtype, const void *X, int64_t ldx,
+                        int64_t M, tsl_dtype ydtype, void *Y, int64_t ldy, int accumulate,
+                        void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * combine_partials -- join rank outputs that all live on this one GPU
+ * ([mlxcel] "Communication patterns": all-gather after column shards,
+ * all-reduce after row shards; [wiki] "Details" §1 and "Examples" §1).
+ *   parts:   HOST array of n_parts DEVICE pointers; part r is [M][n_each]
+ *            with row stride ld_part, type pdtype.
+ *   CONCAT:  Y[m][r * n_each + j] = part_r[m][j]; pdtype must equal ydtype
+ *            (a copy).
+ *   SUM:     Y[m][j] = (((part_0 + part_1) + part_2) + ...)[m][j], each
+ *            addition in binary32 in ascending rank order; pdtype F32;
+ *            ydtype F32 or BF16 (rounded once, nearest even).
+ *   Y:       device, row stride ldy.  Y may alias part 0 for SUM.
+ * 1 <= n_parts <= 64.  M == 0 or n_each == 0 enqueues nothing.
+ * Errors: TSL_ERR_INVALID_ARG, TSL_ERR_UNSUPPORTED, TSL_ERR_MISALIGNED,
+ * TSL_ERR_HIP.
+ */
+tsl_status combine_partials(tsl_combine mode, int32_t n_parts, const void *const *parts,
+                            tsl_dtype pdtype, int64_t M, int64_t n_each, int64_t ld_part,
+                            tsl_dtype ydtype, void *Y, int64_t ldy, void *stream);
+
+/* A static, human-readable description of a status code. */
+const char *tsl_status_string(tsl_status status);
+
+/* The HIP runtime's description of the error behind the most recent
+ * TSL_ERR_HIP returned on the calling thread ("no error" if none). */
+const char *tsl_last_hip_error_string(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSL_H */

@@ -175,6 +175,22 @@ def slice_weight(W, s):
     return W
 
 
+def slice_q4(codes, scales, biases, s, group=64):
+    """The shard of a 4-bit weight before dequantisation: the code block as in
+    slice_weight, and the (scale, bias) groups that cover it -- groups run
+    along K, so a row block [k_off, k_off + k_len) owns groups
+    [k_off / group, (k_off + k_len) / group) and a column block keeps every
+    group of its columns."""
+    c = slice_weight(codes, s)
+    if s["strategy"] == ROW:
+        g0, g1 = s["k_off"] // group, (s["k_off"] + s["k_len"]) // group
+        return c, scales[g0:g1], biases[g0:g1]
+    if s["strategy"] == COLUMN:
+        sl = slice(s["n_off"], s["n_off"] + s["n_len"])
+        return c, scales[:, sl], biases[:, sl]
+    return c, scales, biases
+
+
 def slice_input(X, s):
     """The rank's input: the full X for column/replicated shards, the matching
     column block X_i = X[:, k_off:k_off+k_len] for row shards (wiki "Details"

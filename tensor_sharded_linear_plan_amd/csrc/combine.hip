@@ -1,0 +1,184 @@
+// combine_partials kernels: the on-device stand-ins for the collectives that
+// join rank outputs (mlxcel manual "Tensor parallelism", "Communication
+// patterns": all-reduce after a row-parallel layer, all-gather after a
+// column-parallel one; wiki "Tensor parallel processing", "Details" §1:
+// Y = sum_i Y_i and Y = [Y_1 ... Y_n]).  Every part already sits on this
+// GPU, so the join is a streaming pass over HBM: 16-byte loads and stores,
+// one thread per 4 columns (SUM) or per 16 bytes (CONCAT), rows over
+// blockIdx.y.  The sum runs in ascending rank order in binary32.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace tsl {
+namespace {
+
+struct PartPtrs {
+    const void *p[kMaxParts];
+};
+
+__device__ __forceinline__ void store4(float *y, f32x4 v) { *reinterpret_cast<f32x4 *>(y) = v; }
+__device__ __forceinline__ void store4(uint16_t *y, f32x4 v) {
+    u32x2 w = {pack_bf16(v.x, v.y), pack_bf16(v.z, v.w)};
+    *reinterpret_cast<u32x2 *>(y) = w;
+}
+__device__ __forceinline__ void store1(float *y, float v) { *y = v; }
+__device__ __forceinline__ void store1(uint16_t *y, float v) {
+    __bf16 b = (__bf16)v;
+    *y = __builtin_bit_cast(uint16_t, b);
+}
+
+// Vector path: n_each, ld_part and ldy are multiples of 4 and every base is
+// 16-byte aligned (checked on the host).
+template <typename TY>
+__global__ void __launch_bounds__(256) sum_vec_kernel(PartPtrs parts, int n_parts, int64_t M,
+                                                      int64_t n_each, int64_t ld_part,
+                                                      TY *__restrict__ Y, int64_t ldy) {
+    const int64_t j = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (j >= n_each)
+        return;
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+        const int64_t off = m * ld_part + j;
+        f32x4 acc = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(parts.p[0]) + off);
+        for (int r = 1; r < n_parts; ++r) {
+            f32x4 v =
+                *reinterpret_cast<const f32x4 *>(static_cast<const float *>(parts.p[r]) + off);
+            acc.x = acc.x + v.x;
+            acc.y = acc.y + v.y;
+            acc.z = acc.z + v.z;
+            acc.w = acc.w + v.w;
+        }
+        store4(Y + m * ldy + j, acc);
+    }
+}
+
+template <typename TY>
+__global__ void __launch_bounds__(256) sum_scalar_kernel(PartPtrs parts, int n_parts, int64_t M,
+                                                         int64_t n_each, int64_t ld_part,
+                                                         TY *__restrict__ Y, int64_t ldy) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= n_each)
+        return;
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+        const int64_t off = m * ld_part + j;
+        float acc = static_cast<const float *>(parts.p[0])[off];
+        for (int r = 1; r < n_parts; ++r)
+            acc = acc + static_cast<const float *>(parts.p[r])[off];
+        store1(Y + m * ldy + j, acc);
+    }
+}
+
+// CONCAT, moving VEC-byte units (16 when every row start is 16-byte aligned).
+template <int VEC>
+__global__ void __launch_bounds__(256) concat_kernel(PartPtrs parts, int64_t M, int64_t row_units,
+                                                     int64_t ld_part_bytes, char *__restrict__ Y,
+                                                     int64_t ldy_bytes, int64_t part_bytes) {
+    typedef uint8_t unit_t __attribute__((ext_vector_type(VEC)));
+    const int r = blockIdx.z;
+    const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= row_units)
+        return;
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+        const char *src = static_cast<const char *>(parts.p[r]) + m * ld_part_bytes + u * VEC;
+        char *dst = Y + m * ldy_bytes + (int64_t)r * part_bytes + u * VEC;
+        *reinterpret_cast<unit_t *>(dst) = *reinterpret_cast<const unit_t *>(src);
+    }
+}
+
+// Split-K finish: Y (+)= sum_s P[s], ascending s.
+template <typename TY>
+__global__ void __launch_bounds__(256) splitk_kernel(const float *__restrict__ P, int ks, int64_t M,
+                                                     int64_t N, TY *__restrict__ Y, int64_t ldy,
+                                                     int accumulate) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= N)
+        return;
+    const int64_t plane = M * N;
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+        float acc = P[m * N + j];
+        for (int s = 1; s < ks; ++s)
+            acc = acc + P[s * plane + m * N + j];
+        TY *y = Y + m * ldy + j;
+        if (accumulate)
+            acc = *reinterpret_cast<float *>(y) + acc; // accumulate implies F32 output
+        store1(y, acc);
+    }
+}
+
+inline unsigned rows_grid(int64_t M) { return (unsigned)(M < 65535 ? M : 65535); }
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+} // namespace
+
+hipError_t launch_combine_sum(int n_parts, const float *const *parts, int64_t M, int64_t n_each,
+                              int64_t ld_part, tsl_dtype ydtype, void *Y, int64_t ldy,
+                              hipStream_t stream) {
+    PartPtrs pp{};
+    bool vec = (n_each % 4 == 0) && (ld_part % 4 == 0) && (ldy % 4 == 0) && aligned16(Y);
+    for (int r = 0; r < n_parts; ++r) {
+        pp.p[r] = parts[r];
+        vec = vec && aligned16(parts[r]);
+    }
+    if (ydtype == TSL_BF16)
+        vec = vec && ((reinterpret_cast<uintptr_t>(Y) & 7) == 0);
+    if (vec) {
+        dim3 grid((unsigned)((n_each / 4 + 255) / 256), rows_grid(M));
+        if (ydtype == TSL_F32)
+            hipLaunchKernelGGL(sum_vec_kernel<float>, grid, dim3(256), 0, stream, pp, n_parts, M,
+                               n_each, ld_part, static_cast<float *>(Y), ldy);
+        else
+            hipLaunchKernelGGL(sum_vec_kernel<uint16_t>, grid, dim3(256), 0, stream, pp, n_parts, M,
+                               n_each, ld_part, static_cast<uint16_t *>(Y), ldy);
+    } else {
+        dim3 grid((unsigned)((n_each + 255) / 256), rows_grid(M));
+        if (ydtype == TSL_F32)
+            hipLaunchKernelGGL(sum_scalar_kernel<float>, grid, dim3(256), 0, stream, pp, n_parts, M,
+                               n_each, ld_part, static_cast<float *>(Y), ldy);
+        else
+            hipLaunchKernelGGL(sum_scalar_kernel<uint16_t>, grid, dim3(256), 0, stream, pp,
+                               n_parts, M, n_each, ld_part, static_cast<uint16_t *>(Y), ldy);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_concat(int n_parts, const void *const *parts, size_t elem_bytes,
+                                 int64_t M, int64_t n_each, int64_t ld_part, void *Y, int64_t ldy,
+                                 hipStream_t stream) {
+    PartPtrs pp{};
+    const int64_t row_bytes = n_each * (int64_t)elem_bytes;
+    const int64_t ldp_b = ld_part * (int64_t)elem_bytes, ldy_b = ldy * (int64_t)elem_bytes;
+    bool vec = (row_bytes % 16 == 0) && (ldp_b % 16 == 0) && (ldy_b % 16 == 0) && aligned16(Y);
+    for (int r = 0; r < n_parts; ++r) {
+        pp.p[r] = parts[r];
+        vec = vec && aligned16(parts[r]);
+    }
+    if (vec) {
+        const int64_t units = row_bytes / 16;
+        dim3 grid((unsigned)((units + 255) / 256), rows_grid(M), (unsigned)n_parts);
+        hipLaunchKernelGGL(concat_kernel<16>, grid, dim3(256), 0, stream, pp, M, units, ldp_b,
+                           static_cast<char *>(Y), ldy_b, row_bytes);
+    } else if (elem_bytes == 4) {
+        dim3 grid((unsigned)((n_each + 255) / 256), rows_grid(M), (unsigned)n_parts);
+        hipLaunchKernelGGL(concat_kernel<4>, grid, dim3(256), 0, stream, pp, M, n_each, ldp_b,
+                           static_cast<char *>(Y), ldy_b, row_bytes);
+    } else {
+        dim3 grid((unsigned)((n_each + 255) / 256), rows_grid(M), (unsigned)n_parts);
+        hipLaunchKernelGGL(concat_kernel<2>, grid, dim3(256), 0, stream, pp, M, n_each, ldp_b,
+                           static_cast<char *>(Y), ldy_b, row_bytes);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const float *P, int ks, int64_t M, int64_t N, tsl_dtype ydtype,
+                                void *Y, int64_t ldy, int accumulate, hipStream_t stream) {
+    dim3 grid((unsigned)((N + 255) / 256), rows_grid(M));
+    if (ydtype == TSL_F32)
+        hipLaunchKernelGGL(splitk_kernel<float>, grid, dim3(256), 0, stream, P, ks, M, N,
+                           static_cast<float *>(Y), ldy, accumulate);
+    else
+        hipLaunchKernelGGL(splitk_kernel<uint16_t>, grid, dim3(256), 0, stream, P, ks, M, N,
+                           static_cast<uint16_t *>(Y), ldy, accumulate);
+    return hipGetLastError();
+}
+
+} // namespace tsl

@@ -1,0 +1,93 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, number
+// format conversions and the MFMA wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---- number formats -------------------------------------------------------
+
+// bf16 bit pattern -> binary32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// Two binary32 values -> packed bf16 pair, round to nearest even
+// (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// A bf16 pair -> f16 pair.  Exact for |x| < 65520 (bf16 carries 8
+// significant bits, binary16 11); truncation toward zero never alters an
+// exactly representable value.
+__device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t p) {
+    typedef __fp16 h2 __attribute__((ext_vector_type(2)));
+    h2 v = __builtin_amdgcn_cvt_pkrtz(bf16_lo(p), bf16_hi(p));
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---- 4-bit codes ------------------------------------------------------------
+// A packed code word holds eight consecutive k of one column: even k in the
+// low half-word (nibbles 0..3), odd k in the high half-word (nibbles 4..7),
+// so (w >> 4j) & 0x000F000F isolates the pair (k = 2j, 2j + 1).
+
+// Word -> four bf16 pairs holding 128 + q (0x4300 is bf16 128.0 and its 7
+// mantissa bits count units of 1 there).
+__device__ __forceinline__ bf16x8 q4_to_bf16_plus128(uint32_t w) {
+    u32x4 r;
+    r.x = (w & 0x000F000Fu) | 0x43004300u;
+    r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+    r.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+    r.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+// Word -> eight binary16 weights s * q + b, each rounded once to nearest
+// even: 0x6400 is f16 1024.0 with unit mantissa steps, so the pair
+// (w >> 4j) & 0x000F000F | 0x64006400 holds 1024 + q exactly and
+// fma(s, 1024 + q, b - 1024 s) = s q + b up to the rounding of c.
+__device__ __forceinline__ f16x8 q4_dequant_f16(uint32_t w, float s, float c) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    u32x4 out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t p = ((w >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+        h2 v = __builtin_bit_cast(h2, p);
+        h2 r;
+        r.x = (_Float16)__builtin_fmaf(s, (float)v.x, c);
+        r.y = (_Float16)__builtin_fmaf(s, (float)v.y, c);
+        out[j] = __builtin_bit_cast(uint32_t, r);
+    }
+    return __builtin_bit_cast(f16x8, out);
+}
+
+// ---- MFMA ---------------------------------------------------------------------
+// 16x16 output tile per wave.  Operand lane layout (as used by every kernel
+// here): lane l feeds row (A) / column (B) l % 16 with a run of k values
+// selected by l / 16; both operands use the same k run, which is all a dot
+// product needs.  Accumulator: lane l holds rows 4 * (l / 16) + i, i < 4,
+// of column l % 16.
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+} // namespace tsl

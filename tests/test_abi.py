@@ -1,0 +1,232 @@
+"""The C-ABI library on the host: it loads, exports every entry point that
+include/tsl.h declares, plans bit-exactly like the oracle, and rejects bad
+arguments before anything reaches the GPU (no compute call is made here).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from conftest import ROOT
+from tensor_sharded_linear_plan_amd import configs
+
+HEADER = os.path.join(ROOT, "include", "tsl.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol(tsl_lib):
+    names = declared_functions()
+    assert set(names) == {"plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
+                          "shard_linear_workspace_size", "shard_linear", "combine_partials",
+                          "tsl_status_string", "tsl_last_hip_error_string"}
+    lib = ctypes.CDLL(tsl_lib.LIBRARY)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(tsl_lib.EXPORTS) == set(names)
+
+
+def test_shard_struct_layout_matches_header(tsl_lib):
+    assert ctypes.sizeof(tsl_lib.Shard) == 72
+    assert tsl_lib.Shard.K.offset == 16 and tsl_lib.Shard.head_off.offset == 64
+    assert ctypes.sizeof(tsl_lib.Dims) == 28
+
+
+def _lib_plan(tsl_lib, hidden, hq, hkv, hd, ffn, tp, group=0):
+    shards = tsl_lib.plan_shards(hidden, hq, hkv, hd, ffn, tp, group)
+    return np.array([s.as_tuple() for s in shards], dtype=np.int64).reshape(tp, 7, 12)
+
+
+@pytest.mark.parametrize("layer", configs.LAYERS, ids=lambda l: l.name)
+def test_plan_shards_bit_exact_vs_oracle(tsl_lib, layer):
+    args = (layer.hidden, layer.n_q_heads, layer.n_kv_heads, layer.head_dim, layer.ffn, layer.tp,
+            layer.group)
+    assert np.array_equal(_lib_plan(tsl_lib, *args), oracle.plan(*args))
+
+
+def test_plan_shards_expected_rank0_shapes(tsl_lib):
+    # rank-0 shards of the workloads: (K_s, N_s) per projection
+    want = {
+        "llama2k": [(2048, 512), (2048, 128), (2048, 128), (512, 2048), (2048, 2048),
+                    (2048, 2048), (2048, 2048)],
+        "dec7b": [(3584, 896), (3584, 128), (3584, 128), (896, 3584), (3584, 4736),
+                  (3584, 4736), (4736, 3584)],
+        "pre27b": [(5120, 2048), (5120, 256), (5120, 256), (2048, 5120), (5120, 4352),
+                   (5120, 4352), (4352, 5120)],
+        "gqa8": [(4096, 512), (4096, 512), (4096, 512), (512, 4096), (4096, 1792),
+                 (4096, 1792), (1792, 4096)],
+    }
+    for layer in configs.LAYERS:
+        shards = tsl_lib.plan_shards(layer.hidden, layer.n_q_heads, layer.n_kv_heads,
+                                     layer.head_dim, layer.ffn, layer.tp, layer.group)
+        got = [(s.k_len, s.n_len) for s in shards[:7]]
+        assert got == want[layer.name], layer.name
+    g = tsl_lib.plan_shards(4096, 32, 4, 128, 14336, 8)
+    assert g[tsl_lib.K].strategy == tsl_lib.REPLICATED and g[tsl_lib.V].strategy == tsl_lib.REPLICATED
+
+
+def test_plan_shards_grid_vs_oracle(tsl_lib):
+    n = 0
+    for tp in (1, 2, 4, 8, 16, 32):
+        for hkv in (1, 2, 3, 4, 8, 12, 16):
+            for ratio in (1, 2, 3, 4):
+                for hd, ffn in ((64, 256), (128, 384), (8, 96)):
+                    for group in (0, 64):
+                        args = (512, hkv * ratio, hkv, hd, ffn, tp, group)
+                        try:
+                            want = oracle.plan(*args)
+                        except oracle.OracleError as e:
+                            with pytest.raises(tsl_lib.TslError) as got:
+                                tsl_lib.plan_shards(*args)
+                            assert got.value.status == e.code, args
+                            continue
+                        assert np.array_equal(_lib_plan(tsl_lib, *args), want), args
+                        n += 1
+    assert n > 100
+
+
+def test_plan_shards_rejections(tsl_lib):
+    ok = (2048, 32, 8, 64, 8192, 4, 0)
+    tsl_lib.plan_shards(*ok)
+    bad = [((2048, 32, 8, 64, 8192, 3, 0), tsl_lib.ERR_TP_NOT_POW2),
+           ((2048, 32, 8, 64, 8192, 0, 0), tsl_lib.ERR_INVALID_ARG),
+           ((0, 32, 8, 64, 8192, 4, 0), tsl_lib.ERR_INVALID_ARG),
+           ((2048, 30, 8, 64, 8192, 4, 0), tsl_lib.ERR_NOT_DIVISIBLE),
+           ((2048, 24, 12, 64, 8192, 8, 0), tsl_lib.ERR_NOT_DIVISIBLE),
+           ((2048, 32, 8, 64, 8190, 4, 0), tsl_lib.ERR_NOT_DIVISIBLE),
+           ((2048, 32, 8, 4, 8192, 4, 64), tsl_lib.ERR_GROUP_ALIGN),
+           ((2048, 32, 8, 64, 8192, 4, 32), tsl_lib.ERR_INVALID_ARG)]
+    for args, status in bad:
+        with pytest.raises(tsl_lib.TslError) as e:
+            tsl_lib.plan_shards(*args)
+        assert e.value.status == status, args
+    # short output buffer
+    d = tsl_lib.Dims(*ok)
+    out = (tsl_lib.Shard * 27)()
+    assert tsl_lib._lib.plan_shards(ctypes.byref(d), out, 27) == tsl_lib.ERR_INVALID_ARG
+    assert tsl_lib._lib.plan_shards(None, out, 28) == tsl_lib.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("strategy", [0, 1, 2])
+def test_plan_linear_vs_oracle(tsl_lib, strategy):
+    for K, N, tp, group in ((1024, 2048, 2, 0), (512, 2048, 2, 0), (192, 64, 2, 64),
+                            (256, 48, 4, 64), (100, 30, 2, 0), (64, 64, 3, 0), (4096, 1, 1, 64)):
+        try:
+            want = oracle.plan_linear(K, N, tp, strategy, group)
+        except oracle.OracleError as e:
+            with pytest.raises(tsl_lib.TslError) as got:
+                tsl_lib.plan_linear(K, N, tp, strategy, group)
+            assert got.value.status == e.code
+            continue
+        got = np.array([s.as_tuple() for s in tsl_lib.plan_linear(K, N, tp, strategy, group)])
+        assert np.array_equal(got, want), (K, N, tp, strategy, group)
+
+
+def test_pack_shard_size_geometry(tsl_lib):
+    s = tsl_lib.plan_linear(1024, 2048, 2, tsl_lib.COLUMN)[0]
+    # f32: Nt=64 tiles, 64 k-tiles of 16, 64 lanes x 16 bytes
+    assert tsl_lib.pack_shard_size(s, tsl_lib.F32) == 64 * 64 * 64 * 16
+    assert tsl_lib.pack_shard_size(s, tsl_lib.BF16) == 64 * 32 * 64 * 16
+    # Q4: codes 64 tiles x 8 blocks x 1 KiB, pairs 64 x 16 groups x 16 x 4 bytes
+    assert tsl_lib.pack_shard_size(s, tsl_lib.Q4G64) == 64 * 8 * 1024 + 64 * 16 * 64
+    # ragged: 100 x 30 bf16 -> 2 tiles of 16 columns, k padded to 128 (4 tiles of 32)
+    r = tsl_lib.plan_linear(100, 30, 1, tsl_lib.COLUMN)[0]
+    assert tsl_lib.pack_shard_size(r, tsl_lib.BF16) == 2 * 4 * 1024
+    with pytest.raises(tsl_lib.TslError) as e:
+        tsl_lib.pack_shard_size(r, tsl_lib.Q4G64)
+    assert e.value.status == tsl_lib.ERR_GROUP_ALIGN
+
+
+def test_shard_linear_rejections_before_launch(tsl_lib):
+    s = tsl_lib.plan_linear(1024, 2048, 2, tsl_lib.COLUMN)[0]
+    nb = tsl_lib.pack_shard_size(s, tsl_lib.BF16)
+    P, X, Y = 1 << 20, 1 << 21, 1 << 22  # fake, aligned addresses: never dereferenced
+    call = lambda **kw: tsl_lib.shard_linear(**dict(dict(
+        shard=s, wdtype=tsl_lib.BF16, packed=P, packed_bytes=nb, xdtype=tsl_lib.BF16, X=X,
+        ldx=1024, M=4, ydtype=tsl_lib.F32, Y=Y, ldy=1024), **kw))
+    cases = [(dict(X=0), tsl_lib.ERR_INVALID_ARG),
+             (dict(M=-1), tsl_lib.ERR_INVALID_ARG),
+             (dict(xdtype=tsl_lib.F32), tsl_lib.ERR_UNSUPPORTED),
+             (dict(wdtype=tsl_lib.F32, xdtype=tsl_lib.BF16, packed_bytes=1 << 30),
+              tsl_lib.ERR_UNSUPPORTED),
+             (dict(ydtype=tsl_lib.BF16, accumulate=1), tsl_lib.ERR_UNSUPPORTED),
+             (dict(accumulate=2), tsl_lib.ERR_INVALID_ARG),
+             (dict(packed_bytes=nb - 1), tsl_lib.ERR_BUFFER_TOO_SMALL),
+             (dict(packed=P + 16), tsl_lib.ERR_MISALIGNED),
+             (dict(X=X + 8), tsl_lib.ERR_MISALIGNED),
+             (dict(ldx=1028), tsl_lib.ERR_MISALIGNED),
+             (dict(ldx=1000), tsl_lib.ERR_INVALID_ARG),
+             (dict(ldy=1000), tsl_lib.ERR_INVALID_ARG),
+             (dict(Y=Y + 2), tsl_lib.ERR_MISALIGNED)]
+    for kw, status in cases:
+        with pytest.raises(tsl_lib.TslError) as e:
+            call(**kw)
+        assert e.value.status == status, kw
+    # M == 0 enqueues nothing and succeeds
+    call(M=0)
+    bad = tsl_lib.Shard(*s.as_tuple())
+    bad.n_len = 4000  # beyond W
+    with pytest.raises(tsl_lib.TslError) as e:
+        call(shard=bad)
+    assert e.value.status == tsl_lib.ERR_INVALID_ARG
+
+
+def test_pack_and_combine_rejections_before_launch(tsl_lib):
+    s = tsl_lib.plan_linear(256, 128, 2, tsl_lib.ROW, 64)[0]
+    nb = tsl_lib.pack_shard_size(s, tsl_lib.Q4G64)
+    W, S, B, P = 1 << 20, 1 << 21, 1 << 22, 1 << 23
+    with pytest.raises(tsl_lib.TslError) as e:
+        tsl_lib.pack_shard(s, tsl_lib.Q4G64, W, 128, 1, None, B, 128, 1, P, nb)
+    assert e.value.status == tsl_lib.ERR_INVALID_ARG
+    with pytest.raises(tsl_lib.TslError) as e:
+        tsl_lib.pack_shard(s, tsl_lib.Q4G64, W, 128, 1, S, B, 128, 1, P, nb - 1)
+    assert e.value.status == tsl_lib.ERR_BUFFER_TOO_SMALL
+    with pytest.raises(tsl_lib.TslError) as e:
+        tsl_lib.pack_shard(s, tsl_lib.Q4G64, W, 128, 1, S, B, 128, 1, P + 64, nb)
+    assert e.value.status == tsl_lib.ERR_MISALIGNED
+    with pytest.raises(tsl_lib.TslError) as e:
+        tsl_lib.pack_shard(s, tsl_lib.BF16, W, 128, 1, S, B, 128, 1, P, nb)
+    assert e.value.status == tsl_lib.ERR_INVALID_ARG
+    parts = [1 << 20, 1 << 21]
+    Y = 1 << 22
+    with pytest.raises(tsl_lib.TslError) as e:
+        tsl_lib.combine_partials(tsl_lib.COMBINE_SUM, parts, tsl_lib.BF16, 4, 8, 8, tsl_lib.F32, Y, 8)
+    assert e.value.status == tsl_lib.ERR_UNSUPPORTED
+    with pytest.raises(tsl_lib.TslError) as e:
+        tsl_lib.combine_partials(tsl_lib.COMBINE_CONCAT, parts, tsl_lib.F32, 4, 8, 8, tsl_lib.F32, Y, 8)
+    assert e.value.status == tsl_lib.ERR_INVALID_ARG  # ldy < 2 * 8
+    with pytest.raises(tsl_lib.TslError) as e:
+        tsl_lib.combine_partials(tsl_lib.COMBINE_CONCAT, parts, tsl_lib.F32, 4, 8, 8, tsl_lib.BF16, Y, 16)
+    assert e.value.status == tsl_lib.ERR_UNSUPPORTED
+    with pytest.raises(tsl_lib.TslError) as e:
+        tsl_lib.combine_partials(tsl_lib.COMBINE_SUM, [0, 1 << 21], tsl_lib.F32, 4, 8, 8, tsl_lib.F32, Y, 8)
+    assert e.value.status == tsl_lib.ERR_INVALID_ARG
+    with pytest.raises(tsl_lib.TslError) as e:
+        tsl_lib.combine_partials(tsl_lib.COMBINE_SUM, [1 << 20] * 65, tsl_lib.F32, 4, 8, 8, tsl_lib.F32, Y, 8)
+    assert e.value.status == tsl_lib.ERR_INVALID_ARG
+    with pytest.raises(tsl_lib.TslError) as e:
+        tsl_lib.combine_partials(7, parts, tsl_lib.F32, 4, 8, 8, tsl_lib.F32, Y, 8)
+    assert e.value.status == tsl_lib.ERR_INVALID_ARG
+    # empty work succeeds without a launch
+    tsl_lib.combine_partials(tsl_lib.COMBINE_SUM, parts, tsl_lib.F32, 0, 8, 8, tsl_lib.F32, Y, 8)
+
+
+def test_status_strings(tsl_lib):
+    for st in range(0, -9, -1):
+        assert tsl_lib.tsl_status_string(st) not in ("", "unknown status")
+    assert tsl_lib.tsl_status_string(-99) == "unknown status"
+    assert tsl_lib.tsl_last_hip_error_string() == "no error"
+
+
+def test_one_hip_runtime_in_process(tsl_lib):
+    # the binding loads torch's HIP runtime before libtsl.so: one runtime only
+    maps = open("/proc/self/maps").read().splitlines()
+    runtimes = {l.split()[-1] for l in maps if "libamdhip64" in l}
+    assert len(runtimes) == 1, runtimes

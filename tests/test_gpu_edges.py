@@ -1,0 +1,149 @@
+"""Edge cases of shard_linear on the GPU against the oracle: ragged M, N and
+K (tails of every tile), both kernel families, the split-K path, bf16 and
+f32 outputs, accumulate, strided inputs and outputs, M = 0 and very large M,
+and tp = 1 (the unsharded layer)."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import Q4Weight, dev, host, linear, normwise, pack, spec_dict, torch
+from tensor_sharded_linear_plan_amd import binding as tsl
+from tensor_sharded_linear_plan_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def dense_case(K, N, M, wdtype, tp=1, strategy=0, ldx=None, seed=700, integer=False):
+    ldx = ldx or K
+    if wdtype == tsl.F32:
+        W = synth.small_int(seed, (K, N)) if integer else synth.normal_f32(seed, (K, N))
+        X = synth.small_int(seed + 1, (M, ldx)) if integer else synth.normal_f32(seed + 1, (M, ldx))
+        Wf, Xf = W.astype(np.float64), X.astype(np.float64)
+        xcode = tsl.F32
+    else:
+        W = synth.small_int_bf16(seed, (K, N)) if integer else synth.normal_bf16(seed, (K, N), 0.02)
+        X = synth.small_int_bf16(seed + 1, (M, ldx)) if integer else synth.normal_bf16(seed + 1, (M, ldx))
+        Wf, Xf = oracle.bf16_to_f64(W), oracle.bf16_to_f64(X)
+        xcode = tsl.BF16
+    dW, dX = dev(W), dev(X)
+    out = []
+    for sh in tsl.plan_linear(K, N, tp, strategy):
+        s = spec_dict(sh)
+        buf, nb = pack(sh, wdtype, dW, N, 1)
+        Y = linear(sh, wdtype, buf, nb, xcode, dX[:, sh.k_off:], ldx, M)
+        ref = oracle.gemm(oracle.slice_input(Xf[:, :K], s), oracle.slice_weight(Wf, s))
+        out.append((host(Y)[:M], ref))
+    return out
+
+
+@pytest.mark.parametrize("wdtype", [tsl.F32, tsl.BF16])
+@pytest.mark.parametrize("M", [1, 3, 17, 63, 64, 65, 100, 129, 300])
+@pytest.mark.parametrize("K,N,ldx", [(200, 40, 200), (100, 24, 104), (64, 16, 64), (520, 272, 520)])
+def test_dense_ragged(wdtype, M, K, N, ldx):
+    if wdtype == tsl.F32 and ldx % 4:
+        pytest.skip("f32 rows need ldx % 4 == 0")
+    tol = 1e-5 if wdtype == tsl.F32 else 2e-3
+    for y, ref in dense_case(K, N, M, wdtype, ldx=ldx, seed=701 + M):
+        assert normwise(y, ref) <= tol
+    for y, ref in dense_case(K, N, M, wdtype, ldx=ldx, seed=801 + M, integer=True):
+        assert np.array_equal(y, ref)
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 16, 17, 33, 64, 65, 100, 300])
+@pytest.mark.parametrize("K,N,tp,strategy", [(192, 40, 1, 0), (640, 400, 1, 0), (256, 96, 2, 1),
+                                             (1152, 48, 1, 0)])
+def test_q4_ragged(M, K, N, tp, strategy):
+    for integer in (False, True):
+        w = Q4Weight(K, N, 900 + M, 901, 902, integer=integer)
+        X = (synth.small_int_bf16 if integer else synth.normal_bf16)(903 + M, (M, K))
+        dX = dev(X)
+        Xf = oracle.bf16_to_f64(X)
+        for sh in tsl.plan_linear(K, N, tp, strategy, 64):
+            s = spec_dict(sh)
+            buf, nb = w.pack(sh)
+            Y = linear(sh, tsl.Q4G64, buf, nb, tsl.BF16, dX[:, sh.k_off:], K, M)
+            ref = oracle.gemm(oracle.slice_input(Xf, s), w.shard_f64(s))
+            if integer:
+                assert np.array_equal(host(Y), ref), (M, K, N, s["rank"])
+            else:
+                assert normwise(host(Y), ref) <= 2e-3, (M, K, N, s["rank"])
+
+
+@pytest.mark.parametrize("wdtype", [tsl.BF16, tsl.Q4G64])
+def test_split_k_path(wdtype):
+    # one column tile, long K: the decode kernel splits K across workgroups
+    K, N, M = 8192, 16, 3
+    sh = tsl.plan_linear(K, N, 1, tsl.COLUMN, 64 if wdtype == tsl.Q4G64 else 0)[0]
+    assert tsl.shard_linear_workspace_size(sh, wdtype, M) > 0
+    X = synth.normal_bf16(950, (M, K))
+    if wdtype == tsl.Q4G64:
+        w = Q4Weight(K, N, 951, 952, 953)
+        buf, nb = w.pack(sh)
+        Wf = w.shard_f64(spec_dict(sh))
+    else:
+        W = synth.normal_bf16(951, (K, N), 0.02)
+        buf, nb = pack(sh, tsl.BF16, dev(W), N, 1)
+        Wf = oracle.bf16_to_f64(W)
+    dX = dev(X)
+    ref = oracle.gemm(oracle.bf16_to_f64(X), Wf)
+    Y = linear(sh, wdtype, buf, nb, tsl.BF16, dX, K, M)
+    assert normwise(host(Y), ref) <= 2e-3
+    # accumulate through the split-K finish, and bf16 output through it
+    Ya = torch().ones((M, N), dtype=torch().float32, device="cuda")
+    linear(sh, wdtype, buf, nb, tsl.BF16, dX, K, M, Y=Ya, ldy=N, accumulate=1)
+    assert normwise(host(Ya), ref + 1.0) <= 2e-3
+    Yb = linear(sh, wdtype, buf, nb, tsl.BF16, dX, K, M, ydtype=tsl.BF16)
+    assert np.array_equal(Yb.view(torch().int16).cpu().numpy().view(np.uint16),
+                          oracle.f64_to_bf16(host(Y)))
+
+
+@pytest.mark.parametrize("wdtype", [tsl.BF16, tsl.Q4G64])
+@pytest.mark.parametrize("M", [8, 200])
+def test_strided_output_and_accumulate(wdtype, M):
+    K, N = 256, 64
+    sh = tsl.plan_linear(K, N, 1, tsl.COLUMN, 64 if wdtype == tsl.Q4G64 else 0)[0]
+    X = synth.small_int_bf16(960, (M, K))
+    if wdtype == tsl.Q4G64:
+        w = Q4Weight(K, N, 961, 0, 0, integer=True)
+        buf, nb = w.pack(sh)
+        Wf = w.shard_f64(spec_dict(sh))
+    else:
+        W = synth.small_int_bf16(961, (K, N))
+        buf, nb = pack(sh, tsl.BF16, dev(W), N, 1)
+        Wf = oracle.bf16_to_f64(W)
+    ref = oracle.gemm(oracle.bf16_to_f64(X), Wf)
+    big = torch().full((M, 3 * N), -1.0, dtype=torch().float32, device="cuda")
+    linear(sh, wdtype, buf, nb, tsl.BF16, dev(X), K, M, Y=big[:, N:], ldy=3 * N)
+    got = host(big)
+    assert np.array_equal(got[:, N:2 * N], ref)
+    assert (got[:, :N] == -1).all() and (got[:, 2 * N:] == -1).all()
+    linear(sh, wdtype, buf, nb, tsl.BF16, dev(X), K, M, Y=big[:, N:], ldy=3 * N, accumulate=1)
+    assert np.array_equal(host(big)[:, N:2 * N], 2 * ref)
+
+
+def test_zero_rows_and_large_m():
+    K, N = 64, 16
+    sh = tsl.plan_linear(K, N, 1, tsl.COLUMN)[0]
+    W = synth.small_int_bf16(970, (K, N))
+    buf, nb = pack(sh, tsl.BF16, dev(W), N, 1)
+    Y = torch().full((1, N), 5.0, dtype=torch().float32, device="cuda")
+    tsl.shard_linear(sh, tsl.BF16, buf, nb, tsl.BF16, dev(synth.small_int_bf16(971, (1, K))), K, 0,
+                     tsl.F32, Y, N)
+    assert (host(Y) == 5.0).all()
+    M = 70000  # more rows than one grid dimension holds in the combine kernels
+    X = synth.small_int_bf16(972, (M, K))
+    Yl = linear(sh, tsl.BF16, buf, nb, tsl.BF16, dev(X), K, M)
+    assert np.array_equal(host(Yl), oracle.gemm(oracle.bf16_to_f64(X), oracle.bf16_to_f64(W)))
+    parts = [Yl, Yl]
+    S = torch().zeros((M, N), dtype=torch().float32, device="cuda")
+    tsl.combine_partials(tsl.COMBINE_SUM, parts, tsl.F32, M, N, N, tsl.F32, S, N)
+    assert torch().equal(S, 2 * Yl)
+
+
+def test_tp1_is_the_unsharded_layer():
+    # degenerate plan: one rank holds the whole weight; q/k/v/... all full
+    sh = tsl.plan_shards(256, 4, 2, 64, 512, 1)
+    for s in sh:
+        assert (s.k_len, s.n_len) == (s.K, s.N)
+    for y, ref in dense_case(256, 512, 40, tsl.BF16, tp=1, seed=980, integer=True):
+        assert np.array_equal(y, ref)

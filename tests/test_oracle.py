@@ -371,3 +371,18 @@ def test_combine_concat_layout():
     Y = oracle.combine_concat(parts)
     assert Y.shape == (3, 8)
     assert list(Y[1]) == [0, 0, 1, 1, 2, 2, 3, 3]
+
+
+def test_slice_q4_commutes_with_dequant():
+    # slicing codes and groups, then dequantising == dequantising, then slicing
+    K, N = 256, 32
+    codes = synth.q4_codes(121, (K, N))
+    sc = synth.uniform_bf16(122, (K // 64, N), 0.005, 0.02)
+    bi = synth.normal_bf16(123, (K // 64, N), 0.05)
+    full = oracle.dequant_q4(codes, sc, bi)
+    for strategy in (oracle.COLUMN, oracle.ROW, oracle.REPLICATED):
+        p = oracle.plan_linear(K, N, 2, strategy, 64)
+        for r in range(2):
+            s = dict(zip(oracle.FIELDS, map(int, p[r])))
+            got = oracle.dequant_q4(*oracle.slice_q4(codes, sc, bi, s))
+            assert np.array_equal(got, oracle.slice_weight(full, s))
