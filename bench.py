@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Throughput of the sharded-linear hot path on one MI355X.
+
+One step is the in-process multi-rank pass the mlxcel manual describes
+("Tensor parallelism", "Current runtime support": one process holds every
+rank's shards and runs them in lockstep), here for one tp=4 layer of a
+27B-class model with 4-bit weights at M = 2048 prefill tokens: for every
+rank r and projection p, shard_linear(r, p) -- column outputs written
+straight into their block of the full output (the concat), row partials
+kept apart -- then combine_partials(SUM) of the 4 o and the 4 down partials.
+The plan is recomputed each step (host only); packing is load-time work
+and is timed separately.
+
+value = algorithmic FLOP of the step / step time (inputs resident in HBM).
+A decode figure (7B-class, 4-bit, M = 1, 4, 16, every rank of one layer,
+HIP-graph replay over weight copies that together exceed the 256 MB
+Infinity Cache) is reported beside it in GB/s.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "shard-linear TFLOP/s (prefill) and HBM GB/s (decode) + % roofline, 1 MI355X"
+PEAK_MFMA_F16 = 2500.0  # TFLOP/s, dense fp16/bf16 MFMA, MI355X
+PEAK_HBM = 8000.0       # GB/s, MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_layer(layer, M, copies, tsl, torch, synth, configs):
+    """Pack every rank's shard of every projection (copies times)."""
+    shards = tsl.plan_shards(layer.hidden, layer.n_q_heads, layer.n_kv_heads, layer.head_dim,
+                             layer.ffn, layer.tp, layer.group)
+    packs = [dict() for _ in range(copies)]
+    pack_s, pack_bytes = 0.0, 0
+    for pi, proj in enumerate(configs.PROJS):
+        K, N = shards[pi].K, shards[pi].N
+        seed = lambda t: synth.seed_of(layer.index, pi, t)
+        codes = torch.from_numpy(synth.q4_codes(seed(synth.T_CODES), (K, N))).cuda()
+        sc = torch.from_numpy(synth.uniform_bf16(seed(synth.T_SCALES), (K // 64, N),
+                                                 layer.scale_lo, layer.scale_hi).view("int16")).cuda()
+        bi = torch.from_numpy(synth.normal_bf16(seed(synth.T_BIASES), (K // 64, N),
+                                                layer.bias_std).view("int16")).cuda()
+        for c in range(copies):
+            for r in range(layer.tp):
+                sh = shards[r * tsl.NPROJ + pi]
+                nb = tsl.pack_shard_size(sh, tsl.Q4G64)
+                buf = torch.empty(nb, dtype=torch.uint8, device="cuda")
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                tsl.pack_shard(sh, tsl.Q4G64, codes, N, 1, sc, bi, N, 1, buf, nb)
+                torch.cuda.synchronize()
+                pack_s += time.perf_counter() - t0
+                pack_bytes += sh.k_len * sh.n_len + (sh.k_len // 64) * sh.n_len * 4 + nb
+                packs[c][(r, proj)] = (sh, buf, nb)
+        del codes, sc, bi
+    return shards, packs, pack_s, pack_bytes
+
+
+class Launch:
+    """One prepared shard_linear call (ctypes arguments built once)."""
+
+    def __init__(self, tsl, torch, sh, buf, nb, X, ldx, M, ydtype, Y, ldy, prefill_flops=0.0):
+        import ctypes
+        self.tsl = tsl
+        ws = tsl.shard_linear_workspace_size(sh, tsl.Q4G64, M)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device="cuda") if ws else None
+        self.sh = sh
+        self.args = (ctypes.byref(sh), tsl.Q4G64, buf.data_ptr(), nb, tsl.BF16, X.data_ptr(), ldx, M,
+                     ydtype, Y.data_ptr(), ldy, 0, self.ws.data_ptr() if ws else None, ws)
+        self.flops = 2.0 * M * sh.k_len * sh.n_len
+        self.bytes = (sh.k_len * sh.n_len // 2 + (sh.k_len // 64) * sh.n_len * 4 + M * sh.k_len * 2
+                      + M * sh.n_len * (4 if ydtype == tsl.F32 else 2))
+
+    def __call__(self, stream):
+        st = self.tsl._lib.shard_linear(*self.args, stream)
+        if st != 0:
+            raise self.tsl.TslError(st, "shard_linear")
+
+
+def make_step(layer, M, shards, packs, tsl, torch, synth, configs, seed_base):
+    """Buffers and the launch list of one multi-rank layer pass."""
+    hq_hd = layer.n_q_heads * layer.head_dim
+    kv = layer.n_kv_heads * layer.head_dim
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed_base)
+    bf = torch.bfloat16
+    x = torch.randn((M, layer.hidden), generator=g, device="cuda").to(bf)     # layer input
+    attn = torch.randn((M, hq_hd), generator=g, device="cuda").to(bf)         # o input
+    act = torch.randn((M, layer.ffn), generator=g, device="cuda").to(bf)      # down input
+    out = {"q": torch.empty((M, hq_hd), dtype=bf, device="cuda"),
+           "k": torch.empty((M, kv), dtype=bf, device="cuda"),
+           "v": torch.empty((M, kv), dtype=bf, device="cuda"),
+           "gate": torch.empty((M, layer.ffn), dtype=bf, device="cuda"),
+           "up": torch.empty((M, layer.ffn), dtype=bf, device="cuda"),
+           "o": torch.empty((M, layer.hidden), dtype=bf, device="cuda"),
+           "down": torch.empty((M, layer.hidden), dtype=bf, device="cuda")}
+    parts = {p: [torch.empty((M, layer.hidden), dtype=torch.float32, device="cuda")
+                 for _ in range(layer.tp)] for p in ("o", "down")}
+    steps = []
+    for c, pk in enumerate(packs):
+        launches, sums = [], []
+        for proj in configs.PROJS:
+            for r in range(layer.tp):
+                sh, buf, nb = pk[(r, proj)]
+                if proj in ("o", "down"):
+                    X = attn if proj == "o" else act
+                    Xr = X[:, sh.k_off:]
+                    launches.append(Launch(tsl, torch, sh, buf, nb, Xr, X.shape[1], M, tsl.F32,
+                                           parts[proj][r], layer.hidden))
+                else:
+                    Y = out[proj]
+                    launches.append(Launch(tsl, torch, sh, buf, nb, x, layer.hidden, M, tsl.BF16,
+                                           Y[:, sh.n_off:], Y.shape[1]))
+            if proj in ("o", "down"):
+                sums.append((len(launches), proj))
+        steps.append((launches, sums))
+    comb_bytes = 2 * (layer.tp * M * layer.hidden * 4 + M * layer.hidden * 2)
+
+    def run(step_index, stream, timers=None):
+        launches, sums = steps[step_index % len(steps)]
+        # plan (host) each step, as a runtime would for a new topology check
+        tsl.plan_shards(layer.hidden, layer.n_q_heads, layer.n_kv_heads, layer.head_dim,
+                        layer.ffn, layer.tp, layer.group)
+        s_i = 0
+        for i, L in enumerate(launches):
+            if timers is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                L(stream)
+                e1.record()
+                timers.append((L, e0, e1))
+            else:
+                L(stream)
+            while s_i < len(sums) and sums[s_i][0] == i + 1:
+                proj = sums[s_i][1]
+                tsl.combine_partials(tsl.COMBINE_SUM, parts[proj], tsl.F32, M, layer.hidden,
+                                     layer.hidden, tsl.BF16, out[proj], layer.hidden, stream)
+                s_i += 1
+
+    flops = sum(L.flops for L in steps[0][0])
+    nbytes = sum(L.bytes for L in steps[0][0]) + comb_bytes
+    return run, flops, nbytes, len(steps[0][0])
+
+
+def prefill_bench(args, tsl, torch, synth, configs):
+    layer = configs.PRE27B
+    M = layer.ms[0]
+    t0 = time.perf_counter()
+    shards, packs, pack_s, pack_bytes = build_layer(layer, M, 1, tsl, torch, synth, configs)
+    log("prefill: packed %d shards (%.1f s)" % (len(packs[0]), time.perf_counter() - t0))
+    run, flops, nbytes, nlaunch = make_step(layer, M, shards, packs, tsl, torch, synth, configs, 31)
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(args.warmup):
+        run(i, stream)
+    torch.cuda.synchronize()
+    log("prefill: warmup done")
+    timers = []
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        run(i, stream, timers)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = start.elapsed_time(end) / args.steps
+    k_ms = sum(e0.elapsed_time(e1) for _, e0, e1 in timers)
+    k_flops = sum(L.flops for L, _, _ in timers)
+    log("prefill: %.3f ms/step, %d launches/step, wall %.2f s" % (ms, nlaunch, wall))
+    return dict(ms=ms, flops=flops, bytes=nbytes, wall=wall, kernel_ms=k_ms / len(timers),
+                kernel_tflops=k_flops / (k_ms * 1e-3) / 1e12, launches=len(timers),
+                pack_gbs=pack_bytes / pack_s / 1e9, nlaunch=nlaunch)
+
+
+def decode_bench(args, tsl, torch, synth, configs):
+    layer = configs.DEC7B
+    # weights of the whole layer (all ranks) are ~131 MB: 4 copies > 256 MB MALL + L2
+    copies = 4
+    t0 = time.perf_counter()
+    shards, packs, _, _ = build_layer(layer, 16, copies, tsl, torch, synth, configs)
+    log("decode: packed %d copies (%.1f s)" % (copies, time.perf_counter() - t0))
+    res = []
+    for M in layer.ms:
+        run, flops, nbytes, nlaunch = make_step(layer, M, shards, packs, tsl, torch, synth,
+                                                configs, 41 + M)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in range(copies):  # eager warmup of every launch
+                run(c, side.cuda_stream)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream().cuda_stream
+            for c in range(copies):
+                run(c, cap)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        reps = max(5, args.steps)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        us = start.elapsed_time(end) * 1e3 / (reps * copies)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res.append({"M": M, "us_per_step": round(us, 2), "GB/s": round(gbs, 1),
+                    "frac": round(gbs / PEAK_HBM, 4), "launches_per_step": nlaunch + 2,
+                    "bytes_per_step": nbytes})
+        log("decode M=%d: %.1f us/step, %.0f GB/s" % (M, us, gbs))
+        del graph
+    return res
+
+
+def cpu_baseline(synth, configs):
+    """The oracle, as it stands, on a bounded sample of the prefill workload:
+    rank 0's gate shard (5120 -> 4352, 4-bit), dequantised and multiplied
+    for the first R token rows, R sized for ~10 s of host work."""
+    import numpy as np
+    import oracle
+    layer = configs.PRE27B
+    sh = oracle.spec(oracle.plan(layer.hidden, layer.n_q_heads, layer.n_kv_heads, layer.head_dim,
+                                 layer.ffn, layer.tp, layer.group), 0, "gate")
+    pi = configs.PROJS.index("gate")
+    seed = lambda t: synth.seed_of(layer.index, pi, t)
+    K, N = sh["K"], sh["N"]
+    codes = synth.q4_codes(seed(synth.T_CODES), (K, N))
+    sc = synth.uniform_bf16(seed(synth.T_SCALES), (K // 64, N), layer.scale_lo, layer.scale_hi)
+    bi = synth.normal_bf16(seed(synth.T_BIASES), (K // 64, N), layer.bias_std)
+    X = oracle.bf16_to_f64(synth.normal_bf16(seed(synth.T_X), (layer.ms[0], K)))
+    t0 = time.perf_counter()
+    W = oracle.dequant_q4(*oracle.slice_q4(codes, sc, bi, sh))
+    t_deq = time.perf_counter() - t0
+    probe = 32
+    t0 = time.perf_counter()
+    oracle.gemm(X[:probe], W)
+    t_probe = time.perf_counter() - t0
+    R = int(min(layer.ms[0], max(probe, probe * 10.0 / max(t_probe, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.gemm(X[:R], W)
+    t = time.perf_counter() - t0 + t_deq
+    Ks, Ns = sh["k_len"], sh["n_len"]
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    return {"value": round(2.0 * R * Ks * Ns / t / 1e12, 5), "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "rank-0 gate shard of the prefill workload (%d->%d, 4-bit g64): dequantise "
+                      "+ naive fp64 GEMM over the first %d of %d token rows, %.1f s"
+                      % (Ks, Ns, R, layer.ms[0], t)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library runs every rank's shard on a single "
+              "MI355X and has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tensor_sharded_linear_plan_amd import binding as tsl
+    from tensor_sharded_linear_plan_amd import configs, synth
+    torch.cuda.set_device(0)
+    log("device:", torch.cuda.get_device_name(0))
+
+    pre = prefill_bench(args, tsl, torch, synth, configs)
+    dec = [] if args.no_decode else decode_bench(args, tsl, torch, synth, configs)
+    cpu = None
+    if not args.no_cpu_baseline:
+        sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+        cpu = cpu_baseline(synth, configs)
+        log("cpu baseline:", cpu["sample"])
+
+    value = pre["flops"] / (pre["ms"] * 1e-3) / 1e12
+    layer = configs.PRE27B
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(pre["ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "pre27b: every rank of one tp=4 27B-class layer on one GPU "
+                               "(hidden 5120, ffn 17408, 64 Q / 8 KV heads of 128), 4-bit "
+                               "affine g64 weights, bf16 activations, M=2048 prefill tokens; "
+                               "%d shard GEMMs (f16 MFMA, f32 accumulate) + 2 on-device rank sums"
+                               % pre["nlaunch"],
+                   "tp": layer.tp, "M": layer.ms[0], "weights": "q4g64", "activations": "bf16",
+                   "parallelism": "tp4 in-process on 1 GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(pre["kernel_tflops"], 2),
+                     "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                     "frac": round(pre["kernel_tflops"] / PEAK_MFMA_F16, 4), "traffic": None,
+                     "kernel": "prefill_kernel (4-bit, f16 MFMA)",
+                     "avg_launch_us": round(pre["kernel_ms"] * 1e3, 2)},
+        "cpu_baseline": cpu,
+        "decode": {"workload": "dec7b: every rank of one tp=4 7B-class layer (hidden 3584, ffn "
+                               "18944, 28 Q / 4 KV heads of 128), 4-bit g64, 28 shard GEMVs + 2 "
+                               "rank sums per step, HIP-graph replay over 4 weight copies",
+                   "unit": "GB/s", "peak": PEAK_HBM, "rows": dec},
+        "pack_GBps": round(pre["pack_gbs"], 1),
+        "wall_s_timed": round(pre["wall"], 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

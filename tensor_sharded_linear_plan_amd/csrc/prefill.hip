@@ -19,6 +19,10 @@
 // The grid is one workgroup per tile, ordered so that the 8 XCDs (which
 // receive workgroups round-robin) each own a contiguous run of row-major
 // tiles and keep those activation rows in their own L2.
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -275,6 +279,25 @@ PrefillFn pick(int mtw, int nt, int *lds) {
     return nullptr;
 }
 
+// Raise a kernel's dynamic-LDS limit once per (device, kernel), so that
+// later launches -- including ones recorded into a graph -- only launch.
+hipError_t ensure_lds(const void *fn, int lds) {
+    static std::mutex mu;
+    static std::vector<std::pair<int, const void *>> done;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto &d : done)
+        if (d.first == dev && d.second == fn)
+            return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess)
+        done.emplace_back(dev, fn);
+    return e;
+}
+
 } // namespace
 
 bool prefill_supported(tsl_dtype wdtype) { return wdtype == TSL_BF16 || wdtype == TSL_Q4G64; }
@@ -333,8 +356,7 @@ hipError_t launch_prefill(const PrefillPlan &p, const PackGeom &g, tsl_dtype wdt
     PrefillFn fn = wdtype == TSL_BF16 ? pick<P_BF16>(p.mtw, p.nt, &lds) : pick<P_Q4>(p.mtw, p.nt, &lds);
     if (!fn)
         return hipErrorInvalidValue;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipError_t e = ensure_lds(reinterpret_cast<const void *>(fn), lds);
     if (e != hipSuccess)
         return e;
     const int64_t tiles = p.m_blocks * p.n_blocks;
