@@ -193,7 +193,9 @@ tsl_status pack_shard(const tsl_shard *shard, tsl_dtype wdtype, const void *W, i
 
 /*
  * shard_linear_workspace_size -- workspace bytes shard_linear needs for
- * this shard, weight type and row count (0 when none is needed).
+ * this shard, weight type and row count (0 when none is needed): split-K
+ * partial sums for decode-sized M, and for 4-bit weights with M > 64 the
+ * shard expanded to binary16 (2 bytes per weight).
  */
 tsl_status shard_linear_workspace_size(const tsl_shard *shard, tsl_dtype wdtype, int64_t M,
                                        size_t *bytes);
@@ -217,9 +219,11 @@ tsl_status shard_linear_workspace_size(const tsl_shard *shard, tsl_dtype wdtype,
  *            when that is 0); its contents on entry do not matter.
  * Supported types: (wdtype, xdtype) = (F32, F32), (BF16, BF16),
  * (Q4G64, BF16); ydtype F32 or BF16 (round to nearest even).  Products
- * accumulate in binary32.  For Q4G64 with M > 16 the activations are
- * converted to binary16 inside the kernel (exact for |x| < 65520; larger
- * magnitudes overflow).  M may be 0 (nothing is enqueued).
+ * accumulate in binary32.  Q4G64 with M <= 64 applies the affine groups
+ * exactly (binary32 group sums); with M > 64 the weights are expanded to
+ * binary16 (s * q + b rounded once) and the activations narrowed to
+ * binary16, exact for |x| < 65536 (bf16 values from 65536 up overflow, and
+ * magnitudes below 2^-17 lose low bits).  M may be 0 (nothing is enqueued).
  * Errors: TSL_ERR_INVALID_ARG, TSL_ERR_UNSUPPORTED,
  * TSL_ERR_BUFFER_TOO_SMALL, TSL_ERR_MISALIGNED (X, Y 16-byte aligned;
  * ldx, ldy multiples of 8 for 16-bit and of 4 for 32-bit types), TSL_ERR_HIP.

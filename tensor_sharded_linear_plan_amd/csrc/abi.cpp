@@ -159,7 +159,12 @@ extern "C" tsl_status shard_linear_workspace_size(const tsl_shard *shard, tsl_dt
     tsl_status st = geometry(*shard, wdtype, &g);
     if (st != TSL_OK)
         return st;
-    *bytes = (M > 0 && use_skinny(wdtype, M)) ? skinny_plan(g, wdtype, M).ws_bytes : 0;
+    if (M == 0)
+        *bytes = 0;
+    else if (use_skinny(wdtype, M))
+        *bytes = skinny_plan(g, wdtype, M).ws_bytes;
+    else
+        *bytes = prefill_workspace_bytes(g, wdtype);
     return TSL_OK;
 }
 
@@ -211,8 +216,15 @@ extern "C" tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, con
     PrefillPlan p = prefill_plan(g, M);
     if (p.m_blocks * p.n_blocks > 0x7FFFFFFF)
         return TSL_ERR_UNSUPPORTED;
-    return from_hip(
-        launch_prefill(p, g, wdtype, packed, X, ldx, M, ydtype, Y, ldy, accumulate, s));
+    const size_t need = prefill_workspace_bytes(g, wdtype);
+    if (need > 0) {
+        if (!workspace || ws_bytes < need)
+            return TSL_ERR_BUFFER_TOO_SMALL;
+        if (!aligned(workspace, 256))
+            return TSL_ERR_MISALIGNED;
+    }
+    return from_hip(launch_prefill(p, g, wdtype, packed, X, ldx, M, ydtype, Y, ldy, accumulate,
+                                   workspace, s));
 }
 
 extern "C" tsl_status combine_partials(tsl_combine mode, int32_t n_parts, const void *const *parts,

@@ -60,17 +60,19 @@ hipError_t launch_skinny(const SkinnyPlan &p, const PackGeom &g, tsl_dtype wdtyp
                          tsl_dtype ydtype, void *Y, int64_t ldy, int accumulate, void *workspace,
                          hipStream_t stream);
 
-// ---- prefill.hip: MFMA GEMM with LDS-staged tiles ----
+// ---- prefill.hip: 32x32x16 MFMA GEMM with LDS-staged tiles ----
 struct PrefillPlan {
-    int mtw = 2;  // 16-row m-tiles per wave; block rows = 64 * mtw
-    int nt = 16;  // 16-column n-tiles per block
+    int bm = 256, bn = 256; // block tile
+    int wm = 2, wn = 2;     // wave grid
     int64_t m_blocks = 0, n_blocks = 0;
 };
 bool prefill_supported(tsl_dtype wdtype);
 PrefillPlan prefill_plan(const PackGeom &g, int64_t M);
+// workspace the prefill path needs (4-bit weights expanded to binary16)
+size_t prefill_workspace_bytes(const PackGeom &g, tsl_dtype wdtype);
 hipError_t launch_prefill(const PrefillPlan &p, const PackGeom &g, tsl_dtype wdtype,
                           const void *packed, const void *X, int64_t ldx, int64_t M,
-                          tsl_dtype ydtype, void *Y, int64_t ldy, int accumulate,
+                          tsl_dtype ydtype, void *Y, int64_t ldy, int accumulate, void *workspace,
                           hipStream_t stream);
 
 // Rows at or below which shard_linear takes the skinny (decode) path.
