@@ -7,7 +7,8 @@ rank's shards and runs them in lockstep), here for one tp=4 layer of a
 27B-class model with 4-bit weights at M = 2048 prefill tokens: for every
 rank r and projection p, shard_linear(r, p) -- column outputs written
 straight into their block of the full output (the concat), row partials
-kept apart -- then combine_partials(SUM) of the 4 o and the 4 down partials.
+kept apart, all 28 products in one shard_linear_group call -- then
+combine_partials(SUM) of the 4 o and the 4 down partials.
 The plan is recomputed each step (host only); packing is load-time work
 and is timed separately.
 
@@ -63,91 +64,97 @@ def build_layer(layer, M, copies, tsl, torch, synth, configs):
     return shards, packs, pack_s, pack_bytes
 
 
-class Launch:
-    """One prepared shard_linear call (ctypes arguments built once)."""
+def step_items(layer, M, pk, bufs, tsl, configs):
+    """The shard products of one multi-rank layer pass, as group items:
+    column shards write their block of the full bf16 output (the concat),
+    row shards write their own f32 partial."""
+    items, flops, nbytes = [], 0.0, 0
+    for proj in configs.PROJS:
+        for r in range(layer.tp):
+            sh, buf, nb = pk[(r, proj)]
+            if proj in ("o", "down"):
+                X = bufs["attn"] if proj == "o" else bufs["act"]
+                items.append(dict(shard=sh, packed=buf, packed_bytes=nb, X=X[:, sh.k_off:],
+                                  ldx=X.shape[1], Y=bufs["parts"][proj][r], ldy=layer.hidden,
+                                  ydtype=tsl.F32))
+                yb = 4
+            else:
+                Y = bufs["out"][proj]
+                items.append(dict(shard=sh, packed=buf, packed_bytes=nb, X=bufs["x"],
+                                  ldx=layer.hidden, Y=Y[:, sh.n_off:], ldy=Y.shape[1],
+                                  ydtype=tsl.BF16))
+                yb = 2
+            flops += 2.0 * M * sh.k_len * sh.n_len
+            nbytes += (sh.k_len * sh.n_len // 2 + (sh.k_len // 64) * sh.n_len * 4
+                       + M * sh.k_len * 2 + M * sh.n_len * yb)
+    return items, flops, nbytes
 
-    def __init__(self, tsl, torch, sh, buf, nb, X, ldx, M, ydtype, Y, ldy, prefill_flops=0.0):
-        import ctypes
-        self.tsl = tsl
-        ws = tsl.shard_linear_workspace_size(sh, tsl.Q4G64, M)
-        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device="cuda") if ws else None
-        self.sh = sh
-        self.args = (ctypes.byref(sh), tsl.Q4G64, buf.data_ptr(), nb, tsl.BF16, X.data_ptr(), ldx, M,
-                     ydtype, Y.data_ptr(), ldy, 0, self.ws.data_ptr() if ws else None, ws)
-        self.flops = 2.0 * M * sh.k_len * sh.n_len
-        self.bytes = (sh.k_len * sh.n_len // 2 + (sh.k_len // 64) * sh.n_len * 4 + M * sh.k_len * 2
-                      + M * sh.n_len * (4 if ydtype == tsl.F32 else 2))
 
-    def __call__(self, stream):
-        st = self.tsl._lib.shard_linear(*self.args, stream)
-        if st != 0:
-            raise self.tsl.TslError(st, "shard_linear")
-
-
-def make_step(layer, M, shards, packs, tsl, torch, synth, configs, seed_base):
-    """Buffers and the launch list of one multi-rank layer pass."""
+def make_step(layer, M, shards, packs, tsl, torch, configs, seed_base):
+    """Buffers and the calls of one multi-rank layer pass: one
+    shard_linear_group over every rank's 7 projections, then two
+    combine_partials(SUM)."""
     hq_hd = layer.n_q_heads * layer.head_dim
     kv = layer.n_kv_heads * layer.head_dim
     g = torch.Generator(device="cuda")
     g.manual_seed(seed_base)
     bf = torch.bfloat16
-    x = torch.randn((M, layer.hidden), generator=g, device="cuda").to(bf)     # layer input
-    attn = torch.randn((M, hq_hd), generator=g, device="cuda").to(bf)         # o input
-    act = torch.randn((M, layer.ffn), generator=g, device="cuda").to(bf)      # down input
-    out = {"q": torch.empty((M, hq_hd), dtype=bf, device="cuda"),
-           "k": torch.empty((M, kv), dtype=bf, device="cuda"),
-           "v": torch.empty((M, kv), dtype=bf, device="cuda"),
-           "gate": torch.empty((M, layer.ffn), dtype=bf, device="cuda"),
-           "up": torch.empty((M, layer.ffn), dtype=bf, device="cuda"),
-           "o": torch.empty((M, layer.hidden), dtype=bf, device="cuda"),
-           "down": torch.empty((M, layer.hidden), dtype=bf, device="cuda")}
-    parts = {p: [torch.empty((M, layer.hidden), dtype=torch.float32, device="cuda")
-                 for _ in range(layer.tp)] for p in ("o", "down")}
+    bufs = {"x": torch.randn((M, layer.hidden), generator=g, device="cuda").to(bf),   # input
+            "attn": torch.randn((M, hq_hd), generator=g, device="cuda").to(bf),       # o input
+            "act": torch.randn((M, layer.ffn), generator=g, device="cuda").to(bf),    # down input
+            "out": {"q": torch.empty((M, hq_hd), dtype=bf, device="cuda"),
+                    "k": torch.empty((M, kv), dtype=bf, device="cuda"),
+                    "v": torch.empty((M, kv), dtype=bf, device="cuda"),
+                    "gate": torch.empty((M, layer.ffn), dtype=bf, device="cuda"),
+                    "up": torch.empty((M, layer.ffn), dtype=bf, device="cuda"),
+                    "o": torch.empty((M, layer.hidden), dtype=bf, device="cuda"),
+                    "down": torch.empty((M, layer.hidden), dtype=bf, device="cuda")},
+            "parts": {p: [torch.empty((M, layer.hidden), dtype=torch.float32, device="cuda")
+                          for _ in range(layer.tp)] for p in ("o", "down")}}
     steps = []
-    for c, pk in enumerate(packs):
-        launches, sums = [], []
-        for proj in configs.PROJS:
-            for r in range(layer.tp):
-                sh, buf, nb = pk[(r, proj)]
-                if proj in ("o", "down"):
-                    X = attn if proj == "o" else act
-                    Xr = X[:, sh.k_off:]
-                    launches.append(Launch(tsl, torch, sh, buf, nb, Xr, X.shape[1], M, tsl.F32,
-                                           parts[proj][r], layer.hidden))
-                else:
-                    Y = out[proj]
-                    launches.append(Launch(tsl, torch, sh, buf, nb, x, layer.hidden, M, tsl.BF16,
-                                           Y[:, sh.n_off:], Y.shape[1]))
-            if proj in ("o", "down"):
-                sums.append((len(launches), proj))
-        steps.append((launches, sums))
+    ws_max = 0
+    for pk in packs:
+        items, flops, nbytes = step_items(layer, M, pk, bufs, tsl, configs)
+        arr, n = tsl._items(items)
+        ws_max = max(ws_max, tsl.shard_linear_group_workspace_size(items, tsl.Q4G64, M))
+        steps.append((arr, n, items))
+    # the copies run one after another on one stream: one workspace serves all
+    wsbuf = torch.empty(max(ws_max, 256), dtype=torch.uint8, device="cuda")
     comb_bytes = 2 * (layer.tp * M * layer.hidden * 4 + M * layer.hidden * 2)
 
     def run(step_index, stream, timers=None):
-        launches, sums = steps[step_index % len(steps)]
+        arr, n, _ = steps[step_index % len(steps)]
         # plan (host) each step, as a runtime would for a new topology check
         tsl.plan_shards(layer.hidden, layer.n_q_heads, layer.n_kv_heads, layer.head_dim,
                         layer.ffn, layer.tp, layer.group)
-        s_i = 0
-        for i, L in enumerate(launches):
-            if timers is not None:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                L(stream)
-                e1.record()
-                timers.append((L, e0, e1))
-            else:
-                L(stream)
-            while s_i < len(sums) and sums[s_i][0] == i + 1:
-                proj = sums[s_i][1]
-                tsl.combine_partials(tsl.COMBINE_SUM, parts[proj], tsl.F32, M, layer.hidden,
-                                     layer.hidden, tsl.BF16, out[proj], layer.hidden, stream)
-                s_i += 1
+        if timers is not None:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+        st = tsl._lib.shard_linear_group(n, arr, tsl.Q4G64, tsl.BF16, M, wsbuf.data_ptr(),
+                                         ws_max, stream)
+        if st != 0:
+            raise tsl.TslError(st, "shard_linear_group")
+        if timers is not None:
+            e1.record()
+            timers.append((e0, e1))
+        for proj in ("o", "down"):
+            tsl.combine_partials(tsl.COMBINE_SUM, bufs["parts"][proj], tsl.F32, M, layer.hidden,
+                                 layer.hidden, tsl.BF16, bufs["out"][proj], layer.hidden, stream)
 
-    flops = sum(L.flops for L in steps[0][0])
-    nbytes = sum(L.bytes for L in steps[0][0]) + comb_bytes
-    return run, flops, nbytes, len(steps[0][0])
+    def run_separate(step_index, stream):
+        """The same pass as 28 separate shard_linear calls (for comparison)."""
+        _, _, items = steps[step_index % len(steps)]
+        for it in items:
+            tsl.shard_linear(it["shard"], tsl.Q4G64, it["packed"], it["packed_bytes"], tsl.BF16,
+                             it["X"], it["ldx"], M, it["ydtype"], it["Y"], it["ldy"], 0, wsbuf,
+                             ws_max, stream)
+        for proj in ("o", "down"):
+            tsl.combine_partials(tsl.COMBINE_SUM, bufs["parts"][proj], tsl.F32, M, layer.hidden,
+                                 layer.hidden, tsl.BF16, bufs["out"][proj], layer.hidden, stream)
+
+    _, flops, nbytes = step_items(layer, M, packs[0], bufs, tsl, configs)
+    return run, run_separate, flops, nbytes + comb_bytes, len(steps[0][2])
 
 
 def prefill_bench(args, tsl, torch, synth, configs):
@@ -156,7 +163,8 @@ def prefill_bench(args, tsl, torch, synth, configs):
     t0 = time.perf_counter()
     shards, packs, pack_s, pack_bytes = build_layer(layer, M, 1, tsl, torch, synth, configs)
     log("prefill: packed %d shards (%.1f s)" % (len(packs[0]), time.perf_counter() - t0))
-    run, flops, nbytes, nlaunch = make_step(layer, M, shards, packs, tsl, torch, synth, configs, 31)
+    run, run_separate, flops, nbytes, nitems = make_step(layer, M, shards, packs, tsl, torch,
+                                                         configs, 31)
     stream = torch.cuda.current_stream().cuda_stream
     for i in range(args.warmup):
         run(i, stream)
@@ -173,12 +181,22 @@ def prefill_bench(args, tsl, torch, synth, configs):
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = start.elapsed_time(end) / args.steps
-    k_ms = sum(e0.elapsed_time(e1) for _, e0, e1 in timers)
-    k_flops = sum(L.flops for L, _, _ in timers)
-    log("prefill: %.3f ms/step, %d launches/step, wall %.2f s" % (ms, nlaunch, wall))
-    return dict(ms=ms, flops=flops, bytes=nbytes, wall=wall, kernel_ms=k_ms / len(timers),
-                kernel_tflops=k_flops / (k_ms * 1e-3) / 1e12, launches=len(timers),
-                pack_gbs=pack_bytes / pack_s / 1e9, nlaunch=nlaunch)
+    k_ms = sum(e0.elapsed_time(e1) for e0, e1 in timers) / len(timers)
+    log("prefill: %.3f ms/step (%d shard products in one group call, %.3f ms), wall %.2f s"
+        % (ms, nitems, k_ms, wall))
+    # context: the same pass as separate calls
+    for i in range(2):
+        run_separate(i, stream)
+    start.record()
+    for i in range(5):
+        run_separate(i, stream)
+    end.record()
+    torch.cuda.synchronize()
+    sep_ms = start.elapsed_time(end) / 5
+    log("prefill: %.3f ms/step as %d separate shard_linear calls" % (sep_ms, nitems))
+    return dict(ms=ms, flops=flops, bytes=nbytes, wall=wall, kernel_ms=k_ms,
+                kernel_tflops=flops / (k_ms * 1e-3) / 1e12, pack_gbs=pack_bytes / pack_s / 1e9,
+                nitems=nitems, separate_ms=sep_ms)
 
 
 def decode_bench(args, tsl, torch, synth, configs):
@@ -190,8 +208,8 @@ def decode_bench(args, tsl, torch, synth, configs):
     log("decode: packed %d copies (%.1f s)" % (copies, time.perf_counter() - t0))
     res = []
     for M in layer.ms:
-        run, flops, nbytes, nlaunch = make_step(layer, M, shards, packs, tsl, torch, synth,
-                                                configs, 41 + M)
+        run, _, flops, nbytes, nitems = make_step(layer, M, shards, packs, tsl, torch, configs,
+                                                  41 + M)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -218,7 +236,7 @@ def decode_bench(args, tsl, torch, synth, configs):
         us = start.elapsed_time(end) * 1e3 / (reps * copies)
         gbs = nbytes / (us * 1e-6) / 1e9
         res.append({"M": M, "us_per_step": round(us, 2), "GB/s": round(gbs, 1),
-                    "frac": round(gbs / PEAK_HBM, 4), "launches_per_step": nlaunch + 2,
+                    "frac": round(gbs / PEAK_HBM, 4), "shard_products_per_step": nitems,
                     "bytes_per_step": nbytes})
         log("decode M=%d: %.1f us/step, %.0f GB/s" % (M, us, gbs))
         del graph
@@ -298,21 +316,24 @@ def main():
         "config": {"workload": "pre27b: every rank of one tp=4 27B-class layer on one GPU "
                                "(hidden 5120, ffn 17408, 64 Q / 8 KV heads of 128), 4-bit "
                                "affine g64 weights, bf16 activations, M=2048 prefill tokens; "
-                               "%d shard GEMMs (f16 MFMA, f32 accumulate) + 2 on-device rank sums"
-                               % pre["nlaunch"],
+                               "%d shard GEMMs (f16 MFMA, f32 accumulate) in one grouped call + "
+                               "2 on-device rank sums" % pre["nitems"],
                    "tp": layer.tp, "M": layer.ms[0], "weights": "q4g64", "activations": "bf16",
                    "parallelism": "tp4 in-process on 1 GPU"},
         "roofline": {"bound": "mfma", "achieved": round(pre["kernel_tflops"], 2),
                      "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
                      "frac": round(pre["kernel_tflops"] / PEAK_MFMA_F16, 4), "traffic": None,
-                     "kernel": "prefill_kernel (4-bit, f16 MFMA)",
+                     "kernel": "shard_linear_group prefill launch: prep_kernel (4-bit -> f16 "
+                               "fragments) + gemm_kernel (f16 MFMA), all 28 shard GEMMs",
                      "avg_launch_us": round(pre["kernel_ms"] * 1e3, 2)},
         "cpu_baseline": cpu,
         "decode": {"workload": "dec7b: every rank of one tp=4 7B-class layer (hidden 3584, ffn "
-                               "18944, 28 Q / 4 KV heads of 128), 4-bit g64, 28 shard GEMVs + 2 "
-                               "rank sums per step, HIP-graph replay over 4 weight copies",
+                               "18944, 28 Q / 4 KV heads of 128), 4-bit g64, 28 shard GEMVs in "
+                               "one grouped call + 2 rank sums per step, HIP-graph replay over 4 "
+                               "weight copies",
                    "unit": "GB/s", "peak": PEAK_HBM, "rows": dec},
         "pack_GBps": round(pre["pack_gbs"], 1),
+        "prefill_separate_calls_ms_per_step": round(pre["separate_ms"], 4),
         "wall_s_timed": round(pre["wall"], 3),
     }
     print(json.dumps(line), flush=True)

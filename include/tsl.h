@@ -194,8 +194,9 @@ tsl_status pack_shard(const tsl_shard *shard, tsl_dtype wdtype, const void *W, i
 /*
  * shard_linear_workspace_size -- workspace bytes shard_linear needs for
  * this shard, weight type and row count (0 when none is needed): split-K
- * partial sums for decode-sized M, and for 4-bit weights with M > 64 the
- * shard expanded to binary16 (2 bytes per weight).
+ * partial sums for decode-sized M; with M > 64 the shard expanded to
+ * binary16 for 4-bit weights (2 bytes per weight), or a zero-padded copy of
+ * the activations for BF16 weights when k_len is not a multiple of 64.
  */
 tsl_status shard_linear_workspace_size(const tsl_shard *shard, tsl_dtype wdtype, int64_t M,
                                        size_t *bytes);
@@ -224,6 +225,8 @@ tsl_status shard_linear_workspace_size(const tsl_shard *shard, tsl_dtype wdtype,
  * binary16 (s * q + b rounded once) and the activations narrowed to
  * binary16, exact for |x| < 65536 (bf16 values from 65536 up overflow, and
  * magnitudes below 2^-17 lose low bits).  M may be 0 (nothing is enqueued).
+ * BF16 and Q4G64 weights with M > 64 require ldx and the shard's K below
+ * 2^22 elements (else TSL_ERR_UNSUPPORTED).
  * Errors: TSL_ERR_INVALID_ARG, TSL_ERR_UNSUPPORTED,
  * TSL_ERR_BUFFER_TOO_SMALL, TSL_ERR_MISALIGNED (X, Y 16-byte aligned;
  * ldx, ldy multiples of 8 for 16-bit and of 4 for 32-bit types), TSL_ERR_HIP.
@@ -232,6 +235,51 @@ tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, const void *pa
                         size_t packed_bytes, tsl_dtype xdtype, const void *X, int64_t ldx,
                         int64_t M, tsl_dtype ydtype, void *Y, int64_t ldy, int accumulate,
                         void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * One product of a grouped call: the per-product arguments of
+ * shard_linear.  shard points at HOST memory read during the call only;
+ * packed, X and Y are device pointers with the same meaning, layout and
+ * alignment rules as in shard_linear; ydtype is this product's output type
+ * (F32 or BF16).
+ */
+typedef struct {
+    const tsl_shard *shard;
+    const void *packed;
+    size_t packed_bytes;
+    const void *X;
+    int64_t ldx;
+    void *Y;
+    int64_t ldy;
+    int32_t ydtype;
+    int32_t accumulate;
+} tsl_linear_item;
+
+/*
+ * shard_linear_group_workspace_size -- workspace bytes shard_linear_group
+ * needs for these items (only their shards are read), weight type and M.
+ */
+tsl_status shard_linear_group_workspace_size(int32_t n_items, const tsl_linear_item *items,
+                                             tsl_dtype wdtype, int64_t M, size_t *bytes);
+
+/*
+ * shard_linear_group -- several shard products with the same M, weight and
+ * activation types in one pass: the projections that read the same input
+ * (q, k and v, or gate and up, of a column-parallel block; [wiki]
+ * "Details" §1, [mlxcel] "Column Parallel"), or the shards of every rank
+ * when all ranks' shares run on one GPU.  Each item computes what
+ * shard_linear computes for its arguments, to the same accuracy (the
+ * decode path may split k differently, so results need not be bitwise
+ * equal to separate calls).  The items run in no particular order: no
+ * item's Y may share an element with another item's Y or any item's X
+ * (TSL_ERR_INVALID_ARG); column blocks of one output matrix with a common
+ * ldy are fine.  Up to 32 items share one kernel launch;
+ * 1 <= n_items <= 4096.  items is a HOST array.
+ * Errors: as shard_linear, for any item.
+ */
+tsl_status shard_linear_group(int32_t n_items, const tsl_linear_item *items, tsl_dtype wdtype,
+                              tsl_dtype xdtype, int64_t M, void *workspace, size_t ws_bytes,
+                              void *stream);
 
 /*
  * combine_partials -- join rank outputs that all live on this one GPU
@@ -244,7 +292,10 @@ tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, const void *pa
  *   SUM:     Y[m][j] = (((part_0 + part_1) + part_2) + ...)[m][j], each
  *            addition in binary32 in ascending rank order; pdtype F32;
  *            ydtype F32 or BF16 (rounded once, nearest even).
- *   Y:       device, row stride ldy.  Y may alias part 0 for SUM.
+ *   Y:       device, row stride ldy.  For SUM with ydtype F32 and
+ *            ldy == ld_part, Y may be part 0 itself (each element is read
+ *            before it is written); any other overlap of Y with a part is
+ *            rejected (TSL_ERR_INVALID_ARG).
  * 1 <= n_parts <= 64.  M == 0 or n_each == 0 enqueues nothing.
  * Errors: TSL_ERR_INVALID_ARG, TSL_ERR_UNSUPPORTED, TSL_ERR_MISALIGNED,
  * TSL_ERR_HIP.

@@ -81,8 +81,17 @@ class Shard(ctypes.Structure):
         return "Shard(%s)" % ", ".join("%s=%d" % (f, getattr(self, f)) for f in self.FIELDS)
 
 
+class LinearItem(ctypes.Structure):
+    """One product of shard_linear_group (tsl_linear_item)."""
+    _fields_ = [("shard", ctypes.POINTER(Shard)), ("packed", ctypes.c_void_p),
+                ("packed_bytes", ctypes.c_size_t), ("X", ctypes.c_void_p),
+                ("ldx", ctypes.c_int64), ("Y", ctypes.c_void_p), ("ldy", ctypes.c_int64),
+                ("ydtype", ctypes.c_int32), ("accumulate", ctypes.c_int32)]
+
+
 _i32, _i64, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 _P_SHARD = ctypes.POINTER(Shard)
+_P_ITEM = ctypes.POINTER(LinearItem)
 _lib.plan_shards.argtypes = [ctypes.POINTER(Dims), _P_SHARD, _i64]
 _lib.plan_linear.argtypes = [_i64, _i64, _i32, _i32, _i32, _P_SHARD, _i64]
 _lib.pack_shard_size.argtypes = [_P_SHARD, ctypes.c_int, ctypes.POINTER(_sz)]
@@ -91,6 +100,10 @@ _lib.pack_shard.argtypes = [_P_SHARD, ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _
 _lib.shard_linear_workspace_size.argtypes = [_P_SHARD, ctypes.c_int, _i64, ctypes.POINTER(_sz)]
 _lib.shard_linear.argtypes = [_P_SHARD, ctypes.c_int, _vp, _sz, ctypes.c_int, _vp, _i64, _i64,
                               ctypes.c_int, _vp, _i64, ctypes.c_int, _vp, _sz, _vp]
+_lib.shard_linear_group_workspace_size.argtypes = [_i32, _P_ITEM, ctypes.c_int, _i64,
+                                                   ctypes.POINTER(_sz)]
+_lib.shard_linear_group.argtypes = [_i32, _P_ITEM, ctypes.c_int, ctypes.c_int, _i64, _vp, _sz,
+                                    _vp]
 _lib.combine_partials.argtypes = [ctypes.c_int, _i32, ctypes.POINTER(_vp), ctypes.c_int, _i64,
                                   _i64, _i64, ctypes.c_int, _vp, _i64, _vp]
 _lib.tsl_status_string.argtypes = [ctypes.c_int]
@@ -98,12 +111,14 @@ _lib.tsl_status_string.restype = ctypes.c_char_p
 _lib.tsl_last_hip_error_string.argtypes = []
 _lib.tsl_last_hip_error_string.restype = ctypes.c_char_p
 for _f in ("plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
-           "shard_linear_workspace_size", "shard_linear", "combine_partials"):
+           "shard_linear_workspace_size", "shard_linear", "shard_linear_group_workspace_size",
+           "shard_linear_group", "combine_partials"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
-           "shard_linear_workspace_size", "shard_linear", "combine_partials",
-           "tsl_status_string", "tsl_last_hip_error_string")
+           "shard_linear_workspace_size", "shard_linear", "shard_linear_group_workspace_size",
+           "shard_linear_group", "combine_partials", "tsl_status_string",
+           "tsl_last_hip_error_string")
 
 
 def _check(status, where):
@@ -176,6 +191,40 @@ def shard_linear(shard, wdtype, packed, packed_bytes, xdtype, X, ldx, M, ydtype,
     _check(_lib.shard_linear(ctypes.byref(shard), wdtype, _ptr(packed), packed_bytes, xdtype,
                              _ptr(X), ldx, M, ydtype, _ptr(Y), ldy, accumulate, _ptr(workspace),
                              ws_bytes, _stream(stream)), "shard_linear")
+
+
+def _items(items):
+    """items: sequence of dicts (or LinearItem) with the tsl_linear_item
+    fields (ydtype defaults to F32, accumulate to 0); shard is a Shard.
+    Returns the ctypes array (which keeps the shard copies alive) and its
+    length."""
+    arr = (LinearItem * max(len(items), 1))()
+    keep = []
+    for i, it in enumerate(items):
+        if isinstance(it, LinearItem):
+            arr[i] = it
+            continue
+        sh = Shard(*it["shard"].as_tuple())
+        keep.append(sh)
+        arr[i] = LinearItem(ctypes.pointer(sh), _ptr(it["packed"]), it["packed_bytes"],
+                            _ptr(it["X"]), it["ldx"], _ptr(it["Y"]), it["ldy"],
+                            it.get("ydtype", F32), it.get("accumulate", 0))
+    arr._keep = keep
+    return arr, len(items)
+
+
+def shard_linear_group_workspace_size(items, wdtype, M):
+    arr, n = _items(items)
+    b = _sz(0)
+    _check(_lib.shard_linear_group_workspace_size(n, arr, wdtype, M, ctypes.byref(b)),
+           "shard_linear_group_workspace_size")
+    return b.value
+
+
+def shard_linear_group(items, wdtype, xdtype, M, workspace=None, ws_bytes=0, stream=None):
+    arr, n = _items(items)
+    _check(_lib.shard_linear_group(n, arr, wdtype, xdtype, M, _ptr(workspace), ws_bytes,
+                                   _stream(stream)), "shard_linear_group")
 
 
 def combine_partials(mode, parts, pdtype, M, n_each, ld_part, ydtype, Y, ldy, stream=None):

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "internal.hpp"
 #include "tsl.h"
 
@@ -146,48 +149,40 @@ extern "C" tsl_status pack_shard(const tsl_shard *shard, tsl_dtype wdtype, const
 
 namespace {
 
-// Which kernel family shard_linear uses for this call.
+// Which kernel family serves a product of M rows.
 bool use_skinny(tsl_dtype wdtype, int64_t M) { return wdtype == TSL_F32 || M <= kSkinnyMaxM; }
 
-} // namespace
+// Most items one grouped call takes.
+constexpr int32_t kMaxItems = 4096;
+// Workgroups per launch: the dispatch grid counts work-items in 32 bits.
+constexpr int64_t kMaxBlocks = (int64_t(1) << 24) - 1;
 
-extern "C" tsl_status shard_linear_workspace_size(const tsl_shard *shard, tsl_dtype wdtype,
-                                                  int64_t M, size_t *bytes) {
-    if (!shard || !bytes || M < 0)
-        return TSL_ERR_INVALID_ARG;
-    PackGeom g;
-    tsl_status st = geometry(*shard, wdtype, &g);
-    if (st != TSL_OK)
-        return st;
-    if (M == 0)
-        *bytes = 0;
-    else if (use_skinny(wdtype, M))
-        *bytes = skinny_plan(g, wdtype, M).ws_bytes;
-    else
-        *bytes = prefill_workspace_bytes(g, wdtype);
-    return TSL_OK;
-}
-
-extern "C" tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, const void *packed,
-                                   size_t packed_bytes, tsl_dtype xdtype, const void *X,
-                                   int64_t ldx, int64_t M, tsl_dtype ydtype, void *Y, int64_t ldy,
-                                   int accumulate, void *workspace, size_t ws_bytes,
-                                   void *stream) {
-    if (!shard || !packed || !X || !Y || M < 0)
-        return TSL_ERR_INVALID_ARG;
-    PackGeom g;
-    tsl_status st = geometry(*shard, wdtype, &g);
-    if (st != TSL_OK)
-        return st;
-    if (!valid_dtype(xdtype) || !valid_dtype(ydtype) || xdtype == TSL_Q4G64 || ydtype == TSL_Q4G64)
-        return TSL_ERR_INVALID_ARG;
-    if (accumulate != 0 && accumulate != 1)
+tsl_status check_types(tsl_dtype wdtype, tsl_dtype xdtype) {
+    if (!valid_dtype(wdtype) || !valid_dtype(xdtype) || xdtype == TSL_Q4G64)
         return TSL_ERR_INVALID_ARG;
     // (weights, activations) pairs the kernels implement
     const bool pair_ok = (wdtype == TSL_F32 && xdtype == TSL_F32) ||
                          (wdtype == TSL_BF16 && xdtype == TSL_BF16) ||
                          (wdtype == TSL_Q4G64 && xdtype == TSL_BF16);
-    if (!pair_ok || (accumulate && ydtype != TSL_F32))
+    return pair_ok ? TSL_OK : TSL_ERR_UNSUPPORTED;
+}
+
+// Validates one shard product (weight and activation types already
+// checked) and fills its item.
+tsl_status check_item(const tsl_shard *shard, tsl_dtype wdtype, const void *packed,
+                      size_t packed_bytes, tsl_dtype xdtype, const void *X, int64_t ldx, int64_t M,
+                      int ydtype, void *Y, int64_t ldy, int accumulate, LinearItem *out) {
+    if (!shard || !packed || !X || !Y)
+        return TSL_ERR_INVALID_ARG;
+    if (ydtype != TSL_F32 && ydtype != TSL_BF16)
+        return TSL_ERR_INVALID_ARG;
+    PackGeom g;
+    tsl_status st = geometry(*shard, wdtype, &g);
+    if (st != TSL_OK)
+        return st;
+    if (accumulate != 0 && accumulate != 1)
+        return TSL_ERR_INVALID_ARG;
+    if (accumulate && ydtype != TSL_F32)
         return TSL_ERR_UNSUPPORTED;
     if (ldx < g.Ks || ldy < g.Ns)
         return TSL_ERR_INVALID_ARG;
@@ -197,35 +192,214 @@ extern "C" tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, con
     const uintptr_t ya = ydtype == TSL_F32 ? 4 : 2;
     if (!aligned(packed, 256) || !aligned(X, 16) || ldx % xa || !aligned(Y, ya))
         return TSL_ERR_MISALIGNED;
+    // the kernels' item tables hold shard sizes in 32 bits, and the GEMM
+    // addresses a tile's operands with 32-bit offsets
+    if (g.Kpad >= INT32_MAX || g.Ns >= INT32_MAX)
+        return TSL_ERR_UNSUPPORTED;
+    if (!use_skinny(wdtype, M) && (ldx >= kPrefillMaxStride || g.Kpad >= kPrefillMaxStride))
+        return TSL_ERR_UNSUPPORTED;
+    out->g = g;
+    out->packed = packed;
+    out->X = X;
+    out->ldx = ldx;
+    out->Y = Y;
+    out->ldy = ldy;
+    out->ydtype = (tsl_dtype)ydtype;
+    out->accumulate = accumulate;
+    return TSL_OK;
+}
+
+// Launch order of a group: longest k first, so the longest tiles are
+// dispatched first and the short ones fill in at the end.
+std::vector<LinearItem> launch_order(const std::vector<LinearItem> &items) {
+    std::vector<LinearItem> v = items;
+    std::stable_sort(v.begin(), v.end(), [](const LinearItem &a, const LinearItem &b) {
+        return a.g.Kpad > b.g.Kpad;
+    });
+    return v;
+}
+
+size_t span(int64_t M, int64_t n, int64_t ld, size_t elem);
+bool overlaps(const void *a, size_t na, const void *b, size_t nb);
+
+// Whether two [M][w] row-strided matrices share a byte (M > 0).  With equal
+// strides this is exact -- column blocks of one output matrix written by
+// different items do not overlap -- otherwise it compares address ranges.
+bool matrices_overlap(const void *pa, int64_t wa, int64_t lda, size_t ea, const void *pb,
+                      int64_t wb, int64_t ldb, size_t eb, int64_t M) {
+    const int64_t L = lda * (int64_t)ea;
+    const int64_t Wa = wa * (int64_t)ea, Wb = wb * (int64_t)eb;
+    if (L != ldb * (int64_t)eb || Wa > L || Wb > L)
+        return overlaps(pa, span(M, wa, lda, ea), pb, span(M, wb, ldb, eb));
+    // b - a = q L + rem, 0 <= rem < L: rows r1 - r2 = q need rem < Wa, rows
+    // r1 - r2 = q + 1 need L - rem < Wb, each with |r1 - r2| < M
+    const int64_t d = (int64_t)(reinterpret_cast<uintptr_t>(pb) - reinterpret_cast<uintptr_t>(pa));
+    int64_t q = d / L, rem = d % L;
+    if (rem < 0) {
+        rem += L;
+        q -= 1;
+    }
+    const bool same_row = (q > -M && q < M) && rem < Wa;
+    const bool next_row = (q + 1 > -M && q + 1 < M) && L - rem < Wb;
+    return same_row || next_row;
+}
+
+// Workspace bytes of a validated group.
+size_t group_workspace(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_t M) {
+    if (M == 0 || in.empty())
+        return 0;
+    const std::vector<LinearItem> items = launch_order(in);
+    if (use_skinny(wdtype, M))
+        return skinny_plan(items.data(), (int)items.size(), wdtype, M).ws_bytes;
+    return prefill_plan(items.data(), (int)items.size(), wdtype, M).ws_bytes;
+}
+
+// Plans and enqueues a validated group.
+tsl_status run_group(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_t M,
+                     void *workspace, size_t ws_bytes, void *stream) {
     if (M == 0)
         return TSL_OK;
+    const std::vector<LinearItem> items = launch_order(in);
+    const int n = (int)items.size();
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (use_skinny(wdtype, M)) {
-        SkinnyPlan p = skinny_plan(g, wdtype, M);
-        if (p.m_blocks > 65535 || p.n_groups > 0x7FFFFFFF)
-            return TSL_ERR_UNSUPPORTED;
-        if (p.ws_bytes > 0) {
-            if (!workspace || ws_bytes < p.ws_bytes)
-                return TSL_ERR_BUFFER_TOO_SMALL;
-            if (!aligned(workspace, 256))
-                return TSL_ERR_MISALIGNED;
-        }
-        return from_hip(launch_skinny(p, g, wdtype, packed, X, ldx, M, ydtype, Y, ldy, accumulate,
-                                      workspace, s));
+    size_t need;
+    int64_t blocks;
+    SkinnyPlan sp;
+    PrefillPlan pp;
+    const bool skinny = use_skinny(wdtype, M);
+    if (skinny) {
+        sp = skinny_plan(items.data(), n, wdtype, M);
+        need = sp.ws_bytes;
+        blocks = skinny_blocks(sp, items.data(), n);
+    } else {
+        pp = prefill_plan(items.data(), n, wdtype, M);
+        need = pp.ws_bytes;
+        blocks = prefill_blocks(pp, items.data(), n, M);
     }
-    PrefillPlan p = prefill_plan(g, M);
-    if (p.m_blocks * p.n_blocks > 0x7FFFFFFF)
+    if (blocks > kMaxBlocks)
         return TSL_ERR_UNSUPPORTED;
-    const size_t need = prefill_workspace_bytes(g, wdtype);
     if (need > 0) {
         if (!workspace || ws_bytes < need)
             return TSL_ERR_BUFFER_TOO_SMALL;
         if (!aligned(workspace, 256))
             return TSL_ERR_MISALIGNED;
     }
-    return from_hip(launch_prefill(p, g, wdtype, packed, X, ldx, M, ydtype, Y, ldy, accumulate,
-                                   workspace, s));
+    if (skinny)
+        return from_hip(launch_skinny(sp, items.data(), n, wdtype, M, workspace, s));
+    return from_hip(launch_prefill(pp, items.data(), n, wdtype, M, workspace, s));
 }
+
+// Gathers and validates the items of a grouped call.
+tsl_status gather(int32_t n_items, const tsl_linear_item *items, tsl_dtype wdtype,
+                  tsl_dtype xdtype, int64_t M, std::vector<LinearItem> *out) {
+    if (!items || n_items < 1 || n_items > kMaxItems || M < 0)
+        return TSL_ERR_INVALID_ARG;
+    tsl_status st = check_types(wdtype, xdtype);
+    if (st != TSL_OK)
+        return st;
+    out->resize(n_items);
+    for (int32_t i = 0; i < n_items; ++i) {
+        const tsl_linear_item &it = items[i];
+        st = check_item(it.shard, wdtype, it.packed, it.packed_bytes, xdtype, it.X, it.ldx, M,
+                        it.ydtype, it.Y, it.ldy, it.accumulate, &(*out)[i]);
+        if (st != TSL_OK)
+            return st;
+    }
+    if (M == 0)
+        return TSL_OK;
+    // the products run in no particular order: no output may overlap
+    // another output or any input
+    const size_t xe = xdtype == TSL_F32 ? 4 : 2;
+    for (int32_t i = 0; i < n_items; ++i) {
+        const LinearItem &a = (*out)[i];
+        const size_t ea = a.ydtype == TSL_F32 ? 4 : 2;
+        for (int32_t j = 0; j < n_items; ++j) {
+            const LinearItem &b = (*out)[j];
+            const size_t eb = b.ydtype == TSL_F32 ? 4 : 2;
+            if (matrices_overlap(a.Y, a.g.Ns, a.ldy, ea, b.X, b.g.Ks, b.ldx, xe, M))
+                return TSL_ERR_INVALID_ARG;
+            if (j > i && matrices_overlap(a.Y, a.g.Ns, a.ldy, ea, b.Y, b.g.Ns, b.ldy, eb, M))
+                return TSL_ERR_INVALID_ARG;
+        }
+    }
+    return TSL_OK;
+}
+
+} // namespace
+
+extern "C" tsl_status shard_linear_workspace_size(const tsl_shard *shard, tsl_dtype wdtype,
+                                                  int64_t M, size_t *bytes) {
+    if (!shard || !bytes || M < 0)
+        return TSL_ERR_INVALID_ARG;
+    std::vector<LinearItem> items(1);
+    tsl_status st = geometry(*shard, wdtype, &items[0].g);
+    if (st != TSL_OK)
+        return st;
+    *bytes = group_workspace(items, wdtype, M);
+    return TSL_OK;
+}
+
+extern "C" tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, const void *packed,
+                                   size_t packed_bytes, tsl_dtype xdtype, const void *X,
+                                   int64_t ldx, int64_t M, tsl_dtype ydtype, void *Y, int64_t ldy,
+                                   int accumulate, void *workspace, size_t ws_bytes,
+                                   void *stream) {
+    if (M < 0)
+        return TSL_ERR_INVALID_ARG;
+    tsl_status st = check_types(wdtype, xdtype);
+    if (st != TSL_OK)
+        return shard && packed && X && Y ? st : TSL_ERR_INVALID_ARG;
+    std::vector<LinearItem> items(1);
+    st = check_item(shard, wdtype, packed, packed_bytes, xdtype, X, ldx, M, ydtype, Y, ldy,
+                    accumulate, &items[0]);
+    if (st != TSL_OK)
+        return st;
+    return run_group(items, wdtype, M, workspace, ws_bytes, stream);
+}
+
+extern "C" tsl_status shard_linear_group_workspace_size(int32_t n_items,
+                                                        const tsl_linear_item *items,
+                                                        tsl_dtype wdtype, int64_t M,
+                                                        size_t *bytes) {
+    if (!items || !bytes || n_items < 1 || n_items > kMaxItems || M < 0)
+        return TSL_ERR_INVALID_ARG;
+    std::vector<LinearItem> v(n_items);
+    for (int32_t i = 0; i < n_items; ++i) {
+        if (!items[i].shard)
+            return TSL_ERR_INVALID_ARG;
+        tsl_status st = geometry(*items[i].shard, wdtype, &v[i].g);
+        if (st != TSL_OK)
+            return st;
+    }
+    *bytes = group_workspace(v, wdtype, M);
+    return TSL_OK;
+}
+
+extern "C" tsl_status shard_linear_group(int32_t n_items, const tsl_linear_item *items,
+                                         tsl_dtype wdtype, tsl_dtype xdtype, int64_t M,
+                                         void *workspace, size_t ws_bytes, void *stream) {
+    std::vector<LinearItem> v;
+    tsl_status st = gather(n_items, items, wdtype, xdtype, M, &v);
+    if (st != TSL_OK)
+        return st;
+    return run_group(v, wdtype, M, workspace, ws_bytes, stream);
+}
+
+namespace {
+
+// Bytes from the first to one past the last element of an [M][n] matrix
+// with row stride ld (M, n > 0).
+size_t span(int64_t M, int64_t n, int64_t ld, size_t elem) {
+    return (size_t)((M - 1) * ld + n) * elem;
+}
+
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+} // namespace
 
 extern "C" tsl_status combine_partials(tsl_combine mode, int32_t n_parts, const void *const *parts,
                                        tsl_dtype pdtype, int64_t M, int64_t n_each,
@@ -255,6 +429,14 @@ extern "C" tsl_status combine_partials(tsl_combine mode, int32_t n_parts, const 
             return TSL_ERR_MISALIGNED;
         if (M == 0 || n_each == 0)
             return TSL_OK;
+        const size_t ye = ydtype == TSL_F32 ? 4 : 2;
+        for (int r = 0; r < n_parts; ++r) {
+            const bool in_place =
+                r == 0 && parts[0] == Y && ydtype == TSL_F32 && ldy == ld_part;
+            if (!in_place && overlaps(parts[r], span(M, n_each, ld_part, 4), Y,
+                                      span(M, n_each, ldy, ye)))
+                return TSL_ERR_INVALID_ARG;
+        }
         return from_hip(launch_combine_sum(n_parts, reinterpret_cast<const float *const *>(parts),
                                            M, n_each, ld_part, ydtype, Y, ldy, s));
     }
@@ -271,6 +453,10 @@ extern "C" tsl_status combine_partials(tsl_combine mode, int32_t n_parts, const 
             return TSL_ERR_MISALIGNED;
         if (M == 0 || n_each == 0)
             return TSL_OK;
+        for (int r = 0; r < n_parts; ++r)
+            if (overlaps(parts[r], span(M, n_each, ld_part, ea), Y,
+                         span(M, n_each * n_parts, ldy, ea)))
+                return TSL_ERR_INVALID_ARG;
         return from_hip(launch_combine_concat(n_parts, parts, ea, M, n_each, ld_part, Y, ldy, s));
     }
     return TSL_ERR_INVALID_ARG;

@@ -32,7 +32,7 @@ __device__ __forceinline__ void store1(uint16_t *y, float v) {
 template <typename TY>
 __global__ void __launch_bounds__(256) sum_vec_kernel(PartPtrs parts, int n_parts, int64_t M,
                                                       int64_t n_each, int64_t ld_part,
-                                                      TY *__restrict__ Y, int64_t ldy) {
+                                                      TY *Y, int64_t ldy) {
     const int64_t j = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (j >= n_each)
         return;
@@ -54,7 +54,7 @@ __global__ void __launch_bounds__(256) sum_vec_kernel(PartPtrs parts, int n_part
 template <typename TY>
 __global__ void __launch_bounds__(256) sum_scalar_kernel(PartPtrs parts, int n_parts, int64_t M,
                                                          int64_t n_each, int64_t ld_part,
-                                                         TY *__restrict__ Y, int64_t ldy) {
+                                                         TY *Y, int64_t ldy) {
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= n_each)
         return;

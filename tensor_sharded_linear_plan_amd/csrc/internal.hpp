@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "tsl.h"
 
 namespace tsl {
@@ -45,35 +47,59 @@ hipError_t launch_combine_concat(int n_parts, const void *const *parts, size_t e
 hipError_t launch_splitk_reduce(const float *P, int ks, int64_t M, int64_t N, tsl_dtype ydtype,
                                 void *Y, int64_t ldy, int accumulate, hipStream_t stream);
 
+// One shard product of a (possibly grouped) shard_linear call, validated.
+struct LinearItem {
+    PackGeom g;
+    const void *packed = nullptr;
+    const void *X = nullptr;
+    int64_t ldx = 0;
+    void *Y = nullptr;
+    int64_t ldy = 0;
+    tsl_dtype ydtype = TSL_F32;
+    int accumulate = 0;
+};
+
+// Items per kernel launch (the item table travels in the kernel arguments);
+// longer groups are launched in chunks of this size.
+constexpr int kGroupMax = 32;
+
 // ---- skinny.hip: decode-sized M (streams the weights once per 64 rows) ----
 struct SkinnyPlan {
     int mt = 1;      // 16-row m-tiles per workgroup (1, 2 or 4)
     int ntw = 1;     // 16-column n-tiles per wave (1, 2 or 4)
-    int ks = 1;      // k-split across workgroups (partials go to the workspace)
     int cmax = 8;    // max k-chunks per wave (compile-time register budget)
-    int64_t n_groups = 0, m_blocks = 0;
+    int64_t m_blocks = 0;
+    // per item: k-split across workgroups (partials go to the workspace)
+    // and the byte offset of its partials in the workspace
+    std::vector<int> ks;
+    std::vector<size_t> ws_off;
     size_t ws_bytes = 0;
 };
-SkinnyPlan skinny_plan(const PackGeom &g, tsl_dtype wdtype, int64_t M);
-hipError_t launch_skinny(const SkinnyPlan &p, const PackGeom &g, tsl_dtype wdtype,
-                         const void *packed, const void *X, int64_t ldx, int64_t M,
-                         tsl_dtype ydtype, void *Y, int64_t ldy, int accumulate, void *workspace,
-                         hipStream_t stream);
+SkinnyPlan skinny_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t M);
+// most workgroups any one launch of the group takes (bounded by the host)
+int64_t skinny_blocks(const SkinnyPlan &p, const LinearItem *items, int n);
+hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, tsl_dtype wdtype,
+                         int64_t M, void *workspace, hipStream_t stream);
 
-// ---- prefill.hip: 32x32x16 MFMA GEMM with LDS-staged tiles ----
+// ---- prefill.hip: 32x32x16 MFMA GEMM, operands copied straight into LDS ----
 struct PrefillPlan {
-    int bm = 256, bn = 256; // block tile
-    int wm = 2, wn = 2;     // wave grid
-    int64_t m_blocks = 0, n_blocks = 0;
+    int bm = 256, bn = 160; // block tile
+    int wm = 4, wn = 1;     // wave grid
+    // per item: byte offsets in the workspace of its binary16 weights (4-bit
+    // shards) and of its zero-padded activation copy (K not a multiple of 64)
+    std::vector<size_t> w_off, x_off;
+    size_t ws_bytes = 0;
 };
 bool prefill_supported(tsl_dtype wdtype);
-PrefillPlan prefill_plan(const PackGeom &g, int64_t M);
-// workspace the prefill path needs (4-bit weights expanded to binary16)
-size_t prefill_workspace_bytes(const PackGeom &g, tsl_dtype wdtype);
-hipError_t launch_prefill(const PrefillPlan &p, const PackGeom &g, tsl_dtype wdtype,
-                          const void *packed, const void *X, int64_t ldx, int64_t M,
-                          tsl_dtype ydtype, void *Y, int64_t ldy, int accumulate, void *workspace,
-                          hipStream_t stream);
+PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t M);
+// most workgroups any one launch of the group takes (bounded by the host)
+int64_t prefill_blocks(const PrefillPlan &p, const LinearItem *items, int n, int64_t M);
+hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, tsl_dtype wdtype,
+                          int64_t M, void *workspace, hipStream_t stream);
+
+// Bound (elements, exclusive) on the activation row stride and padded K of
+// the prefill path, which keeps its 32-bit operand offsets in range.
+constexpr int64_t kPrefillMaxStride = int64_t(1) << 22;
 
 // Rows at or below which shard_linear takes the skinny (decode) path.
 constexpr int64_t kSkinnyMaxM = 64;

@@ -4,27 +4,41 @@
 // "Column Parallel" / "Row Parallel").  A dense contraction, so it runs on
 // the matrix cores with the full-rate 32x32x16 MFMA.
 //
-// Block tile BM x BN x 64, 4 waves arranged WM x WN, wave tile
-// (BM/WM) x (BN/WN) made of 32x32 accumulator tiles.  Both operands are
-// staged through LDS in MFMA fragment order (one 1 KB fragment = 32 rows or
-// columns x 16 k; a lane reads its 16 bytes with one ds_read_b128), double
-// buffered, one barrier per 64 k.  Inside a stage the fragments of the next
-// 16-k step are read while the MFMAs of the current one run; the next
-// stage's LDS writes and the global loads of the stage after it are issued
-// between the MFMA groups.  Activation fragments are XOR-swizzled by k so
-// that both the row-coalesced global->LDS writes and the fragment reads hit
-// distinct LDS banks.
+// Block tile BM x BN x 64 per stage, 4 waves arranged WM x WN, wave tile
+// (BM/WM) x (BN/WN) made of 32x32 accumulator tiles.  Operands move from
+// global memory straight into LDS with gfx950's global_load_lds_dwordx4
+// (a wave instruction fills 1 KB of LDS, lane l at byte 16 l), so staging
+// costs no VGPRs and no LDS write instructions:
+//   - activations: one instruction fetches 8 full 128-byte row segments
+//     (the access pattern the L2 serves fastest) into an 8-row block whose
+//     16-byte chunks are XOR-swizzled by row, which keeps the MFMA fragment
+//     reads bank-conflict free;
+//   - weights: the packed layout already holds 16 columns x 8 k per
+//     16-byte chunk, so a 32-column x 16-k MFMA fragment is two 512-byte
+//     runs.
+// Stages rotate through 3 LDS buffers (2 when 3 do not fit in 160 KB): the
+// loads of stage k + 2 are issued right after the barrier that opens stage
+// k, and each wave waits only for its own loads of stage k before that
+// barrier.  Inside a stage the fragments of the next 16-k step are read
+// while the MFMAs of the current one run.
 //
-// Operands: bf16 x bf16, or f16 x f16 for 4-bit weights -- those are first
-// dequantised into binary16 fragments (w = s q + b rounded once) by a
-// pre-pass, and the bf16 activations are narrowed to binary16 while they
-// are staged (exact below 65536 in magnitude).  Accumulation is binary32.
+// Operands: bf16 x bf16, or f16 x f16 for 4-bit weights.  For the latter a
+// prep kernel first expands the weights to binary16 fragments (w = s q + b
+// rounded once) in the workspace, and the GEMM narrows each bf16 activation
+// fragment to binary16 as it leaves LDS (exact below 65536 in magnitude).
+// bf16 activations are copied, zero-padded, only when K is not a multiple
+// of 64.  Accumulation is binary32.
 //
-// The grid is one workgroup per tile, ordered so that each of the 8 XCDs
-// (which receive workgroups round-robin) works on a contiguous run of
-// row-major tiles and keeps those activation rows in its own L2.
-#include <mutex>
-#include <utility>
+// One launch serves a group of shard products with the same M and types;
+// the item table rides in the kernel arguments.  Each item's tiles take a
+// run of workgroups starting at a multiple of 8.  Workgroups reach the 8
+// XCDs round-robin, so XCD x takes the x-th eighth of the item's tiles in
+// band order (bands of up to 8 m-blocks, m fastest), a compact patch whose
+// activation rows and weight columns stay in that XCD's L2.
+#include <hip/hip_runtime.h>
+
+#include <functional>
+#include <queue>
 #include <vector>
 
 #include "device.hpp"
@@ -37,31 +51,39 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 enum { OP_BF16 = 0, OP_F16 = 1 };
 
-struct GemmArgs {
-    const u32x4 *B;    // dense fragment-packed weights [Nt16][KT32][64] x 16 B
-    const uint16_t *X; // bf16 activations
-    int64_t ldx;
-    int64_t M, Ks, Ns, Nt16;
-    int64_t KT32;      // 32-k tiles per column tile in B
-    int64_t KT64;      // 64-k stages to run
-    int64_t MB, NB;    // tile grid
+struct GemmItem {
+    const u32x4 *B;    // fragment-packed weights [Nt16][KT32][64] x 16 B (bf16 or f16)
+    const uint16_t *X; // bf16 activations, K padded to 64
     void *Y;
-    int64_t ldy;
-    int y_bf16, accumulate;
+    int64_t ldx, ldy;
+    int32_t Ns, Nt16;
+    int32_t KT32;      // 32-k tiles per column tile in B
+    int32_t KT64;      // 64-k stages
+    int32_t MB, NB;    // tile grid
+    int32_t T8;        // tiles per XCD, ceil(MB * NB / 8)
+    int32_t start;     // first workgroup (a multiple of 8)
+    int32_t accumulate, y_bf16;
 };
+
+struct GemmGroup {
+    int64_t M;
+    int32_t n, pad_;
+    GemmItem it[kGroupMax];
+};
+
+constexpr int kLdsLimit = 160 * 1024;
 
 template <int OP, int BM, int BN, int WM, int WN>
 struct G {
     static constexpr int TM = BM / WM, TN = BN / WN; // wave tile
     static constexpr int MT = TM / 32, NT = TN / 32; // 32x32 tiles per wave
-    static constexpr int A_CH = BM * 8 / 256;        // 16-byte A chunks per thread per stage
-    static constexpr int B_CH = (BN * 8 + 255) / 256;
-    static constexpr int A_BYTES = BM * 128;          // BM x 64 k x 2 bytes
-    static constexpr int B_BYTES = BN * 128;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int LDS = 2 * STAGE;
+    static constexpr int AF = BM / 8, BF = BN / 8;   // 1 KB LDS blocks per stage
+    static constexpr int FPW = (AF + BF) / 4;        // DMA instructions per wave per stage
+    static constexpr int STAGE = (AF + BF) * 1024;
+    static constexpr int NS = 3 * STAGE <= kLdsLimit ? 3 : 2;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 tiles");
-    static_assert((BM * 8) % 256 == 0, "A chunks must divide over 256 threads");
+    static_assert(AF % 4 == 0 && BF % 4 == 0, "LDS blocks must divide over 4 waves");
+    static_assert(2 * STAGE <= kLdsLimit, "two stages must fit in LDS");
 };
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c, int op) {
@@ -72,108 +94,95 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c, int op) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// LDS slot of activation chunk (row, kc) inside its fragment: logical slot
-// row%32 + 32*(kc%2) XOR 2*kc (kc = 8-k chunk index 0..7 within the stage).
-__device__ __forceinline__ int a_lds_offset(int row, int kc) {
-    const int frag = (row >> 5) * 4 + (kc >> 1);
-    const int slot = ((row & 31) + 32 * (kc & 1)) ^ (2 * kc);
-    return (frag * 64 + slot) * 16;
+// One wave instruction: lane l copies the 16 bytes at base + off (base
+// wave-uniform, off a per-lane 32-bit byte offset) into LDS at lds + 16 l.
+// Issued as inline assembly so that the compiler's wait-count tracking does
+// not drain every outstanding copy before each LDS read; completion is
+// awaited explicitly (vmcnt) before the barrier that publishes a stage.
+__device__ __forceinline__ void dma16(const char *base, uint32_t off, void *lds) {
+    const unsigned l = (unsigned)(uintptr_t)(void __attribute__((address_space(3))) *)lds;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(off), "s"(base)
+                 : "memory", "m0");
 }
+
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+}
+
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int OP, int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_kernel(GemmArgs a) {
+gemm_kernel(GemmGroup grp) {
     using C = G<OP, BM, BN, WM, WN>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    __shared__ __attribute__((aligned(1024))) char lds0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) char lds1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) char lds2[C::NS == 3 ? C::STAGE : 1024];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
 
-    const int64_t T = a.MB * a.NB;
-    int64_t tile = blockIdx.x;
-    if ((T & 7) == 0)
-        tile = (tile & 7) * (T >> 3) + (tile >> 3);
-    const int64_t mb = tile / a.NB, nb = tile % a.NB;
+    const int bid = blockIdx.x;
+    int lo = 0, hi = grp.n - 1; // last item whose first workgroup is <= bid
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (grp.it[mid].start <= bid)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const GemmItem &a = grp.it[lo];
+    const int64_t M = grp.M;
+    const int local = bid - a.start;
+    const int t = (local & 7) * a.T8 + (local >> 3); // tile in band order
+    if (t >= a.MB * a.NB)
+        return; // padding workgroup
+    const int band = t / (8 * a.NB);
+    const int first_m = band * 8;
+    const int bm_cnt = a.MB - first_m < 8 ? a.MB - first_m : 8;
+    const int in_band = t - band * 8 * a.NB;
+    const int64_t mb = first_m + in_band % bm_cnt, nb = in_band / bm_cnt;
     const int64_t m0 = mb * BM, n0 = nb * BN;
 
-    // ---- global -> registers ----
-    // Rows past M and column tiles past the shard are clamped to the last
-    // valid one: the loads stay in bounds and those outputs are never
-    // stored.  Only a stage reaching past K (K % 64 != 0) takes the
-    // element-wise guarded path, so every other load is unconditional.
-    u32x4 ra[C::A_CH], rb[C::B_CH];
-    const int64_t last_row = a.M - 1;
-    auto gload = [&](int64_t kt) {
-        const int64_t k0 = kt * 64;
-        if (k0 + 64 <= a.Ks) {
+    // Sources of this wave's LDS blocks: block f < AF holds activation rows
+    // 8f..8f+7 of the tile, the others weight fragments (32 columns x 16 k).
+    // Each is a per-lane byte offset from a tile base that advances by a
+    // constant per stage (f < AF exactly when j < AF / 4).  Rows past M and
+    // columns past the shard are clamped to the last valid ones: in bounds,
+    // and those outputs are never stored.  Offsets stay below 2^32 because
+    // the activation row stride and K are below 2^22 elements (checked by
+    // the caller).
+    const char *xbase = reinterpret_cast<const char *>(a.X + m0 * a.ldx);
+    const int64_t t0 = n0 >> 4;
+    const char *bbase = reinterpret_cast<const char *>(a.B + t0 * a.KT32 * 64);
+    uint32_t off[C::FPW];
 #pragma unroll
-            for (int i = 0; i < C::A_CH; ++i) {
-                const int c = tid + 256 * i;
-                int64_t row = m0 + (c >> 3);
-                row = row < last_row ? row : last_row;
-                ra[i] = *reinterpret_cast<const u32x4 *>(a.X + row * a.ldx + k0 + (c & 7) * 8);
-            }
+    for (int j = 0; j < C::FPW; ++j) {
+        const int f = wave + 4 * j;
+        if (j < C::AF / 4) {
+            int64_t row = m0 + 8 * f + (lane >> 3);
+            row = row < M - 1 ? row : M - 1;
+            off[j] = (uint32_t)(((row - m0) * a.ldx + 8 * ((lane & 7) ^ (lane >> 3))) * 2);
         } else {
-#pragma unroll
-            for (int i = 0; i < C::A_CH; ++i) {
-                const int c = tid + 256 * i;
-                int64_t row = m0 + (c >> 3);
-                row = row < last_row ? row : last_row;
-                const int64_t k = k0 + (c & 7) * 8;
-                const uint16_t *p = a.X + row * a.ldx + k;
-                uint32_t w[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t lo = (k + 2 * j < a.Ks) ? p[2 * j] : 0u;
-                    const uint32_t hi = (k + 2 * j + 1 < a.Ks) ? p[2 * j + 1] : 0u;
-                    w[j] = lo | (hi << 16);
-                }
-                ra[i] = u32x4{w[0], w[1], w[2], w[3]};
-            }
+            const int g = f - C::AF, nt = g >> 2, s = g & 3;
+            const int64_t n = n0 + nt * 32 + (lane & 31);
+            int64_t t16 = n >> 4;
+            t16 = t16 < a.Nt16 - 1 ? t16 : a.Nt16 - 1;
+            const int kr = 2 * s + (lane >> 5); // 8-k run within the stage
+            off[j] = (uint32_t)((((t16 - t0) * a.KT32 + (kr >> 2)) * 64 + (kr & 3) * 16 + (n & 15)) * 16);
         }
+    }
+    auto issue = [&](int64_t kt, char *buf) __attribute__((always_inline)) {
+        const char *xb = xbase + kt * (64 * 2);
+        const char *bb = bbase + kt * (2 * 64 * 16);
 #pragma unroll
-        for (int i = 0; i < C::B_CH; ++i) {
-            const int c = tid + 256 * i;
-            if (c < BN * 8) {
-                int64_t t16 = (n0 >> 4) + (c >> 7); // 16-column packed tile
-                t16 = t16 < a.Nt16 - 1 ? t16 : a.Nt16 - 1;
-                const int64_t kt32 = kt * 2 + ((c >> 6) & 1);
-                rb[i] = a.B[(t16 * a.KT32 + kt32) * 64 + (c & 63)];
-            }
-        }
-    };
-    // ---- registers -> LDS (fragment order) ----
-    auto lwrite_a = [&](int stage, int i) {
-        char *As = smem + stage * C::STAGE;
-        const int c = tid + 256 * i;
-        u32x4 v = ra[i];
-        if constexpr (OP == OP_F16) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                v[j] = bf16pair_to_f16pair(v[j]);
-        }
-        *reinterpret_cast<u32x4 *>(As + a_lds_offset(c >> 3, c & 7)) = v;
-    };
-    auto lwrite_b = [&](int stage, int i) {
-        char *Bs = smem + stage * C::STAGE + C::A_BYTES;
-        const int c = tid + 256 * i;
-        if (c < BN * 8) {
-            const int l16 = c & 63;
-            const int n = (c >> 7) * 16 + (l16 & 15);       // column within the block
-            const int kr = ((c >> 6) & 1) * 4 + (l16 >> 4); // 8-k chunk within the stage
-            const int frag = (n >> 5) * 4 + (kr >> 1);
-            const int slot = (n & 31) + 32 * (kr & 1);
-            *reinterpret_cast<u32x4 *>(Bs + (frag * 64 + slot) * 16) = rb[i];
-        }
-    };
-    auto lwrite = [&](int stage) {
-#pragma unroll
-        for (int i = 0; i < C::A_CH; ++i)
-            lwrite_a(stage, i);
-#pragma unroll
-        for (int i = 0; i < C::B_CH; ++i)
-            lwrite_b(stage, i);
+        for (int j = 0; j < C::FPW; ++j)
+            dma16(j < C::AF / 4 ? xb : bb, off[j], buf + (wave + 4 * j) * 1024);
     };
 
     f32x16 acc[C::MT][C::NT];
@@ -185,72 +194,76 @@ gemm_kernel(GemmArgs a) {
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.f;
 
-    // fragment readers: A fragment (mt32, s16) lane l reads logical slot l
-    const int a_slot_h = lane >> 5; // k half of this lane
-    auto read_frags = [&](int stage, int s, u32x4 (&af)[C::MT], u32x4 (&bf)[C::NT]) {
-        const char *As = smem + stage * C::STAGE;
-        const char *Bs = As + C::A_BYTES;
-        const int kc = 2 * s + a_slot_h;
-#pragma unroll
-        for (int i = 0; i < C::MT; ++i) {
-            const int frag = (wm * C::MT + i) * 4 + s;
-            af[i] = *reinterpret_cast<const u32x4 *>(As + (frag * 64 + (lane ^ (2 * kc))) * 16);
-        }
-#pragma unroll
-        for (int j = 0; j < C::NT; ++j) {
-            const int frag = (wn * C::NT + j) * 4 + s;
-            bf[j] = *reinterpret_cast<const u32x4 *>(Bs + (frag * 64 + lane) * 16);
-        }
-    };
-
     u32x4 af[2][C::MT], bfr[2][C::NT];
-    // One 64-k stage from LDS buffer `cur`.  With `more`, the registers
-    // (holding the next stage) are written to the other buffer in slices
-    // between the MFMA groups of steps 1 and 2, and the stage after next is
-    // fetched from memory during step 3.
-    auto stage_body = [&](int cur, bool more, int64_t next2) {
-        read_frags(cur, 0, af[0], bfr[0]);
+    auto stage = [&](int64_t kt, const char *cur, char *nxt) __attribute__((always_inline)) {
+        // this wave's copies of stage kt are done once only the younger
+        // stages' copies may still be in flight
+        if (C::NS == 3 && kt + 1 < a.KT64)
+            wait_vmcnt<C::FPW>();
+        else
+            wait_vmcnt<0>();
+        barrier();
+        if (kt + C::NS - 1 < a.KT64)
+            issue(kt + C::NS - 1, nxt);
+        const char *As = cur;
+        const char *Bs = cur + C::AF * 1024;
+        auto rd = [&](int s, u32x4 (&x)[C::MT], u32x4 (&y)[C::NT]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < C::MT; ++i) {
+                const int r = (wm * C::MT + i) * 32 + (lane & 31); // row in the block tile
+                const int kr = 2 * s + (lane >> 5);                // 8-k run in the stage
+                x[i] = *reinterpret_cast<const u32x4 *>(As + (r >> 3) * 1024 + (r & 7) * 128 +
+                                                        ((kr ^ (r & 7)) * 16));
+            }
+#pragma unroll
+            for (int j = 0; j < C::NT; ++j)
+                y[j] = *reinterpret_cast<const u32x4 *>(
+                    Bs + (((wn * C::NT + j) * 4 + s) * 64 + lane) * 16);
+        };
+        rd(0, af[0], bfr[0]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             if (s < 3)
-                read_frags(cur, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
-            int w = 0; // LDS-write slices handed out between this step's MFMAs
+                rd(s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
+            u32x4 au[C::MT];
+#pragma unroll
+            for (int i = 0; i < C::MT; ++i) {
+                au[i] = af[s & 1][i];
+                if constexpr (OP == OP_F16) // bf16 activations meet f16 weights
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        au[i][q] = bf16pair_to_f16pair(au[i][q]);
+            }
 #pragma unroll
             for (int i = 0; i < C::MT; ++i)
 #pragma unroll
-                for (int j = 0; j < C::NT; ++j) {
-                    acc[i][j] = mfma32(af[s & 1][i], bfr[s & 1][j], acc[i][j], OP);
-                    if (more && (s == 1 || s == 2)) {
-                        // spread the A+B chunk writes over steps 1 and 2
-                        const int total = C::A_CH + C::B_CH;
-                        const int per = (total + 2 * C::MT * C::NT - 1) / (2 * C::MT * C::NT);
-                        for (int q = 0; q < per; ++q) {
-                            const int idx = (s - 1) * C::MT * C::NT * per + w * per + q;
-                            if (idx < C::A_CH)
-                                lwrite_a(cur ^ 1, idx);
-                            else if (idx < total)
-                                lwrite_b(cur ^ 1, idx - C::A_CH);
-                        }
-                        ++w;
-                    }
-                }
-            if (more && s == 3)
-                gload(next2);
+                for (int j = 0; j < C::NT; ++j)
+                    acc[i][j] = mfma32(au[i], bfr[s & 1][j], acc[i][j], OP);
         }
     };
 
-    gload(0);
-    lwrite(0);
-    if (a.KT64 > 1)
-        gload(1);
-    __syncthreads();
-
-    for (int64_t kt = 0; kt + 1 < a.KT64; ++kt) {
-        const int64_t next2 = kt + 2 < a.KT64 ? kt + 2 : a.KT64 - 1; // re-fetch of the last stage is harmless
-        stage_body((int)(kt & 1), true, next2);
-        __syncthreads();
+    issue(0, lds0);
+    if (C::NS == 3 && a.KT64 > 1)
+        issue(1, lds1);
+    int64_t kt = 0;
+    if constexpr (C::NS == 3) {
+        for (; kt + 3 <= a.KT64; kt += 3) {
+            stage(kt, lds0, lds2);
+            stage(kt + 1, lds1, lds0);
+            stage(kt + 2, lds2, lds1);
+        }
+        if (kt < a.KT64)
+            stage(kt, lds0, lds2);
+        if (kt + 1 < a.KT64)
+            stage(kt + 1, lds1, lds0);
+    } else {
+        for (; kt + 2 <= a.KT64; kt += 2) {
+            stage(kt, lds0, lds1);
+            stage(kt + 1, lds1, lds0);
+        }
+        if (kt < a.KT64)
+            stage(kt, lds0, lds1);
     }
-    stage_body((int)((a.KT64 - 1) & 1), false, 0);
 
     // ---- epilogue: acc reg r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32 ----
 #pragma unroll
@@ -264,7 +277,7 @@ gemm_kernel(GemmArgs a) {
             for (int r = 0; r < 16; ++r) {
                 const int64_t row =
                     m0 + (wm * C::MT + i) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (row >= a.M)
+                if (row >= M)
                     continue;
                 const float v = acc[i][j][r];
                 if (a.y_bf16) {
@@ -278,54 +291,107 @@ gemm_kernel(GemmArgs a) {
     }
 }
 
-// 4-bit -> binary16 fragments: one thread per packed 16-byte code chunk
-// (16 columns x 128 k per 64 lanes), writing the four 32-k fragments it
-// covers in the dense packed layout.
-__global__ void __launch_bounds__(256) dequant_f16_kernel(const u32x4 *__restrict__ codes,
-                                                          const uint32_t *__restrict__ sb,
-                                                          int64_t KB, int64_t GP, int64_t Gs,
-                                                          int64_t chunks, u32x4 *__restrict__ out) {
-    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= chunks)
+// ---- prep: 4-bit weights -> binary16 fragments, ragged-K activations -> padded copy ----
+struct PrepItem {
+    // weights (4-bit items): codes and scale/bias pairs -> fragments
+    const u32x4 *codes;
+    const uint32_t *sb;
+    u32x4 *w_out;
+    // activations (K not a multiple of 64): rows of ldx_in -> rows of Kpad
+    const uint16_t *x_in;
+    uint16_t *x_out;
+    int64_t ldx_in;
+    int64_t w_chunks;  // 16-byte code chunks
+    int64_t x_units;   // 8-element output units (M * Kpad / 8)
+    int32_t KB, GP, Gs;
+    int32_t Ks, Kpad;
+    int32_t w_blocks;  // workgroups [start, start + w_blocks) do weights
+    int32_t start, pad_;
+};
+
+struct PrepGroup {
+    int32_t n, pad_;
+    PrepItem it[kGroupMax];
+};
+
+__global__ void __launch_bounds__(256) prep_kernel(PrepGroup grp) {
+    const int bid = blockIdx.x;
+    int lo = 0, hi = grp.n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (grp.it[mid].start <= bid)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const PrepItem &p = grp.it[lo];
+    const int local = bid - p.start;
+    if (local < p.w_blocks) {
+        // one thread per packed 16-byte code chunk (16 columns x 128 k per
+        // 64 lanes), writing the four 32-k fragments it covers
+        const int64_t c = (int64_t)local * blockDim.x + threadIdx.x;
+        if (c >= p.w_chunks)
+            return;
+        const int lane = (int)(c & 63);
+        const int64_t t = c >> 6;
+        const int64_t nt = t / p.KB, blk = t % p.KB;
+        const u32x4 w = p.codes[c];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t g = 2 * blk + h;
+            if (g >= p.Gs)
+                break; // pad group of a half-filled last block: never read
+            const uint32_t sbp = p.sb[(nt * p.GP + g) * 16 + (lane & 15)];
+            const float s = bf16_lo(sbp);
+            const float cb = __builtin_fmaf(-1024.f, s, bf16_hi(sbp));
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int tt = 2 * h + q;
+                const f16x8 v = q4_dequant_f16(w[tt], s, cb);
+                p.w_out[((nt * ((int64_t)p.KB * 4) + blk * 4 + tt) * 64) + lane] =
+                    __builtin_bit_cast(u32x4, v);
+            }
+        }
         return;
-    const int lane = (int)(c & 63);
-    const int64_t t = c >> 6;
-    const int64_t nt = t / KB, blk = t % KB;
-    const u32x4 w = codes[c];
+    }
+    // activations: one thread per 8 output elements
+    const int64_t units = p.Kpad / 8;
+    const int64_t u = (int64_t)(local - p.w_blocks) * blockDim.x + threadIdx.x;
+    if (u >= p.x_units)
+        return;
+    const int64_t m = u / units, k = (u % units) * 8;
+    const uint16_t *src = p.x_in + m * p.ldx_in + k;
+    u32x4 v = {0, 0, 0, 0};
+    if (k + 8 <= p.Ks) {
+        v = *reinterpret_cast<const u32x4 *>(src);
+    } else if (k < p.Ks) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int64_t g = 2 * blk + h;
-        if (g >= Gs)
-            break; // pad group of a half-filled last block: its fragments are never read
-        const uint32_t p = sb[(nt * GP + g) * 16 + (lane & 15)];
-        const float s = bf16_lo(p);
-        const float cb = __builtin_fmaf(-1024.f, s, bf16_hi(p));
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int tt = 2 * h + q;
-            const f16x8 v = q4_dequant_f16(w[tt], s, cb);
-            out[((nt * (KB * 4) + blk * 4 + tt) * 64) + lane] = __builtin_bit_cast(u32x4, v);
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t lo2 = (k + 2 * j < p.Ks) ? src[2 * j] : 0u;
+            const uint32_t hi2 = (k + 2 * j + 1 < p.Ks) ? src[2 * j + 1] : 0u;
+            v[j] = lo2 | (hi2 << 16);
         }
     }
+    *reinterpret_cast<u32x4 *>(p.x_out + m * p.Kpad + k) = v;
 }
 
-typedef void (*GemmFn)(GemmArgs);
+typedef void (*GemmFn)(GemmGroup);
 
 struct Variant {
     int bm, bn, wm, wn;
 };
 // tile shapes with a kernel instance
+// (256 x 256 needs more than the 512 registers a lane has at one wave per
+// SIMD and is left out)
 constexpr Variant kVariants[] = {{256, 160, 4, 1}, {256, 128, 2, 2}, {128, 256, 2, 2},
                                  {128, 128, 2, 2}, {256, 64, 4, 1},  {128, 64, 2, 2},
                                  {64, 64, 2, 2}};
 
 template <int OP>
-GemmFn pick(const Variant &v, int *lds) {
+GemmFn pick(const Variant &v) {
 #define TSL_CASE(BM_, BN_, WM_, WN_)                                                               \
-    if (v.bm == BM_ && v.bn == BN_ && v.wm == WM_ && v.wn == WN_) {                                \
-        *lds = G<OP, BM_, BN_, WM_, WN_>::LDS;                                                     \
-        return gemm_kernel<OP, BM_, BN_, WM_, WN_>;                                                \
-    }
+    if (v.bm == BM_ && v.bn == BN_ && v.wm == WM_ && v.wn == WN_)                                  \
+        return gemm_kernel<OP, BM_, BN_, WM_, WN_>;
     TSL_CASE(256, 160, 4, 1) TSL_CASE(256, 128, 2, 2)
     TSL_CASE(128, 256, 2, 2) TSL_CASE(128, 128, 2, 2) TSL_CASE(256, 64, 4, 1)
     TSL_CASE(128, 64, 2, 2) TSL_CASE(64, 64, 2, 2)
@@ -333,110 +399,179 @@ GemmFn pick(const Variant &v, int *lds) {
     return nullptr;
 }
 
-// Raise a kernel's dynamic-LDS limit once per (device, kernel), so that
-// later launches -- including ones recorded into a graph -- only launch.
-hipError_t ensure_lds(const void *fn, int lds) {
-    static std::mutex mu;
-    static std::vector<std::pair<int, const void *>> done;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess)
-        return e;
-    std::lock_guard<std::mutex> lock(mu);
-    for (const auto &d : done)
-        if (d.first == dev && d.second == fn)
-            return hipSuccess;
-    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e == hipSuccess)
-        done.emplace_back(dev, fn);
-    return e;
+inline int64_t kpad64(int64_t k) { return (k + 63) / 64 * 64; }
+
+// Modelled time of a variant over a group: greedy list scheduling of the
+// tiles (in launch order) on 256 CUs, one workgroup each, times the larger
+// of two per-CU penalties relative to the 4096 flop/clk the MFMAs retire:
+// LDS traffic (fragment reads of (TM + TN) x 2 bytes per k per wave plus
+// the (BM + BN) x 2 bytes the copies write, at 128 B/clk) and L2 delivery
+// ((BM + BN) x 2 bytes per 2 BM BN flops at a sustained ~40 B/clk).
+double variant_cost(const Variant &v, const LinearItem *items, int n, int64_t M) {
+    const double TM = v.bm / v.wm, TN = v.bn / v.wn;
+    const double flops = 2.0 * v.bm * v.bn; // per k
+    const double lds = 4096.0 * (4.0 * (TM + TN) * 2 + (v.bm + v.bn) * 2) / flops / 128.0;
+    const double l2 = 4096.0 * (v.bm + v.bn) * 2 / flops / 40.0;
+    double pen = lds > l2 ? lds : l2;
+    pen = pen > 1.0 ? pen : 1.0;
+    const int64_t mbk = (M + v.bm - 1) / v.bm;
+    std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
+    for (int i = 0; i < 256; ++i)
+        cu.push(0.0);
+    double span = 0.0;
+    int64_t tiles = 0;
+    for (int i = 0; i < n; ++i)
+        tiles += mbk * ((items[i].g.Ns + v.bn - 1) / v.bn);
+    if (tiles > 16384) { // large: every CU busy to the end, to a tile
+        double work = 0.0, longest = 0.0;
+        for (int i = 0; i < n; ++i) {
+            const double len = (double)kpad64(items[i].g.Ks) / 64.0;
+            work += (double)(mbk * ((items[i].g.Ns + v.bn - 1) / v.bn)) * len;
+            longest = len > longest ? len : longest;
+        }
+        span = work / 256.0 + longest;
+    } else {
+        for (int i = 0; i < n; ++i) {
+            const double len = (double)kpad64(items[i].g.Ks) / 64.0;
+            const int64_t T = mbk * ((items[i].g.Ns + v.bn - 1) / v.bn);
+            for (int64_t t = 0; t < T; ++t) {
+                const double f = cu.top() + len;
+                cu.pop();
+                cu.push(f);
+                span = f > span ? f : span;
+            }
+        }
+    }
+    return span * (double)(v.bm * v.bn) * pen;
 }
 
 } // namespace
 
 bool prefill_supported(tsl_dtype wdtype) { return wdtype == TSL_BF16 || wdtype == TSL_Q4G64; }
 
-size_t prefill_workspace_bytes(const PackGeom &g, tsl_dtype wdtype) {
-    // 4-bit weights are expanded to binary16 fragments: 16 columns x 32 k
-    // per KiB, k padded to whole 128-k blocks
-    return wdtype == TSL_Q4G64 ? (size_t)g.Nt * (size_t)g.KT * 4 * 1024 : 0;
-}
-
-PrefillPlan prefill_plan(const PackGeom &g, int64_t M) {
-    // Least modelled time on 256 CUs, one workgroup per CU: rounds of
-    // tiles x padded tile area x an LDS-read penalty.  A wave reads
-    // (TM + TN) x 2 bytes per k for 2 TM TN flops; a CU reads LDS at
-    // 128 B/clk and retires 4096 flop/clk, so the penalty is
-    // max(1, 64 (TM + TN) / (TM TN)) with 20% headroom for the LDS writes.
+PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t M) {
     PrefillPlan best;
     double best_cost = 1e300;
-    const int64_t N = g.Nt * 16;
     for (const Variant &v : kVariants) {
-        const int64_t TM = v.bm / v.wm, TN = v.bn / v.wn;
-        const int64_t mbk = (M + v.bm - 1) / v.bm, nbk = (N + v.bn - 1) / v.bn;
-        const int64_t rounds = (mbk * nbk + 255) / 256;
-        const double lds = 1.2 * 64.0 * (double)(TM + TN) / (double)(TM * TN);
-        const double cost = (double)rounds * (double)(v.bm * v.bn) * (lds > 1.0 ? lds : 1.0);
+        const double cost = variant_cost(v, items, n, M);
         if (cost < best_cost - 1e-9) {
             best_cost = cost;
             best.bm = v.bm;
             best.bn = v.bn;
             best.wm = v.wm;
             best.wn = v.wn;
-            best.m_blocks = mbk;
-            best.n_blocks = nbk;
         }
     }
+    // workspace: binary16 weight fragments of 4-bit items, padded
+    // activation copies of ragged-K bf16 items
+    best.w_off.assign(n, 0);
+    best.x_off.assign(n, 0);
+    size_t off = 0;
+    for (int i = 0; i < n; ++i) {
+        const PackGeom &g = items[i].g;
+        if (wdtype == TSL_Q4G64) {
+            best.w_off[i] = off;
+            off += (size_t)g.Nt * (size_t)g.KT * 4 * 1024;
+        } else if (g.Ks % 64 != 0) {
+            best.x_off[i] = off;
+            off += ((size_t)M * (size_t)kpad64(g.Ks) * 2 + 255) / 256 * 256;
+        }
+    }
+    best.ws_bytes = off;
     return best;
 }
 
-hipError_t launch_prefill(const PrefillPlan &p, const PackGeom &g, tsl_dtype wdtype,
-                          const void *packed, const void *X, int64_t ldx, int64_t M,
-                          tsl_dtype ydtype, void *Y, int64_t ldy, int accumulate, void *workspace,
-                          hipStream_t stream) {
-    GemmArgs a{};
-    const void *B = packed;
-    int op = OP_BF16;
-    if (wdtype == TSL_Q4G64) {
-        // expand the 4-bit shard to binary16 fragments in the workspace
-        const int64_t chunks = g.Nt * g.KT * 64;
-        const uint32_t *sb =
-            reinterpret_cast<const uint32_t *>(static_cast<const char *>(packed) + g.codes_bytes);
-        hipLaunchKernelGGL(dequant_f16_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256),
-                           0, stream, static_cast<const u32x4 *>(packed), sb, g.KT, g.KT * 2,
-                           g.Ks / 64, chunks, static_cast<u32x4 *>(workspace));
+hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, tsl_dtype wdtype,
+                          int64_t M, void *workspace, hipStream_t stream) {
+    const Variant v{p.bm, p.bn, p.wm, p.wn};
+    GemmFn fn = wdtype == TSL_Q4G64 ? pick<OP_F16>(v) : pick<OP_BF16>(v);
+    if (!fn)
+        return hipErrorInvalidValue;
+    char *ws = static_cast<char *>(workspace);
+    for (int c0 = 0; c0 < n; c0 += kGroupMax) {
+        const int cn = n - c0 < kGroupMax ? n - c0 : kGroupMax;
+        // 1. prep: expand 4-bit weights, pad ragged-K activations
+        PrepGroup pg{};
+        int64_t pblocks = 0;
+        for (int i = 0; i < cn; ++i) {
+            const LinearItem &L = items[c0 + i];
+            const PackGeom &g = L.g;
+            const bool q4 = wdtype == TSL_Q4G64, pad = !q4 && g.Ks % 64 != 0;
+            if (!q4 && !pad)
+                continue;
+            PrepItem &a = pg.it[pg.n++];
+            a.codes = static_cast<const u32x4 *>(L.packed);
+            a.sb = reinterpret_cast<const uint32_t *>(static_cast<const char *>(L.packed) +
+                                                      g.codes_bytes);
+            a.w_out = reinterpret_cast<u32x4 *>(ws + p.w_off[c0 + i]);
+            a.x_in = static_cast<const uint16_t *>(L.X);
+            a.x_out = reinterpret_cast<uint16_t *>(ws + p.x_off[c0 + i]);
+            a.ldx_in = L.ldx;
+            a.w_chunks = q4 ? g.Nt * g.KT * 64 : 0;
+            a.Kpad = (int32_t)kpad64(g.Ks);
+            a.x_units = pad ? M * (a.Kpad / 8) : 0;
+            a.KB = (int32_t)g.KT;
+            a.GP = (int32_t)(g.KT * 2);
+            a.Gs = (int32_t)(g.Ks / 64);
+            a.Ks = (int32_t)g.Ks;
+            a.w_blocks = (int32_t)((a.w_chunks + 255) / 256);
+            a.start = (int32_t)pblocks;
+            pblocks += a.w_blocks + (a.x_units + 255) / 256;
+        }
+        if (pg.n > 0) {
+            hipLaunchKernelGGL(prep_kernel, dim3((unsigned)pblocks), dim3(256), 0, stream, pg);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+        // 2. the GEMM over every item's tiles
+        GemmGroup grp{};
+        grp.M = M;
+        grp.n = cn;
+        int64_t blocks = 0;
+        for (int i = 0; i < cn; ++i) {
+            const LinearItem &L = items[c0 + i];
+            const PackGeom &g = L.g;
+            GemmItem &a = grp.it[i];
+            const bool q4 = wdtype == TSL_Q4G64, pad = !q4 && g.Ks % 64 != 0;
+            a.B = static_cast<const u32x4 *>(q4 ? static_cast<const void *>(ws + p.w_off[c0 + i])
+                                                : L.packed);
+            a.X = pad ? reinterpret_cast<const uint16_t *>(ws + p.x_off[c0 + i])
+                      : static_cast<const uint16_t *>(L.X);
+            a.ldx = pad ? kpad64(g.Ks) : L.ldx;
+            a.Y = L.Y;
+            a.ldy = L.ldy;
+            a.Ns = (int32_t)g.Ns;
+            a.Nt16 = (int32_t)g.Nt;
+            a.KT32 = (int32_t)(q4 ? g.KT * 4 : g.KT);
+            a.KT64 = (int32_t)(kpad64(g.Ks) / 64);
+            a.MB = (int32_t)((M + p.bm - 1) / p.bm);
+            a.NB = (int32_t)((g.Ns + p.bn - 1) / p.bn);
+            a.T8 = (a.MB * a.NB + 7) / 8;
+            a.start = (int32_t)blocks;
+            a.accumulate = L.accumulate;
+            a.y_bf16 = L.ydtype == TSL_BF16;
+            blocks += 8 * (int64_t)a.T8;
+        }
+        hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, stream, grp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        B = workspace;
-        op = OP_F16;
     }
-    a.B = static_cast<const u32x4 *>(B);
-    a.X = static_cast<const uint16_t *>(X);
-    a.ldx = ldx;
-    a.M = M;
-    a.Ks = g.Ks;
-    a.Ns = g.Ns;
-    a.Nt16 = g.Nt;
-    a.KT32 = wdtype == TSL_Q4G64 ? g.KT * 4 : g.KT;
-    a.KT64 = (g.Ks + 63) / 64;
-    a.MB = p.m_blocks;
-    a.NB = p.n_blocks;
-    a.Y = Y;
-    a.ldy = ldy;
-    a.y_bf16 = ydtype == TSL_BF16;
-    a.accumulate = accumulate;
+    return hipSuccess;
+}
 
-    const Variant v{p.bm, p.bn, p.wm, p.wn};
-    int lds = 0;
-    GemmFn fn = op == OP_BF16 ? pick<OP_BF16>(v, &lds) : pick<OP_F16>(v, &lds);
-    if (!fn)
-        return hipErrorInvalidValue;
-    hipError_t e = ensure_lds(reinterpret_cast<const void *>(fn), lds);
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL(fn, dim3((unsigned)(p.m_blocks * p.n_blocks)), dim3(256), lds, stream, a);
-    return hipGetLastError();
+int64_t prefill_blocks(const PrefillPlan &p, const LinearItem *items, int n, int64_t M) {
+    int64_t most = 0;
+    for (int c0 = 0; c0 < n; c0 += kGroupMax) {
+        int64_t blocks = 0;
+        for (int i = c0; i < n && i < c0 + kGroupMax; ++i) {
+            const int64_t T = ((M + p.bm - 1) / p.bm) * ((items[i].g.Ns + p.bn - 1) / p.bn);
+            blocks += 8 * ((T + 7) / 8);
+        }
+        most = blocks > most ? blocks : most;
+    }
+    return most;
 }
 
 } // namespace tsl

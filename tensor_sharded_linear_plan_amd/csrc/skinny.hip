@@ -15,6 +15,12 @@
 // workgroup partials go to the workspace and a second kernel sums them in
 // ascending order, so results are run-to-run deterministic.
 //
+// One launch serves a group of shard products with the same M and types
+// (several projections, or every rank's shard of one): the item table
+// rides in the kernel arguments and each workgroup finds its item by
+// binary search over the items' first workgroup indices.  Large groups
+// need no k-split at all, which removes the second kernel.
+//
 // 4-bit weights (w = s q + b per group of 64 k) are applied exactly:
 // the MFMA multiplies the bf16 activations by 128 + q (an exact bf16), and
 // per group the accumulator takes s * sum(x (128 + q)) + (b - 128 s) * sum(x),
@@ -28,19 +34,25 @@ namespace {
 
 enum { W_F32 = 0, W_BF16 = 1, W_Q4 = 2 };
 
-struct SkinnyArgs {
+struct SkinnyItem {
     const void *B;       // packed weights (codes for Q4)
     const uint32_t *SB;  // Q4 scale/bias pairs
     const void *X;
-    int64_t ldx;
-    int64_t M, Ks, Ns, Nt;
-    int64_t KC;          // chunks along k (16, 32 or 128 k each)
-    int64_t GP;          // Q4: groups per column in the packed pairs
-    int ks;
     void *Y;
-    int64_t ldy;
-    int y_bf16, accumulate;
     float *P;            // workspace partials [ks][M][Ns] (ks > 1)
+    int64_t ldx, ldy;
+    int32_t Ks, Ns, Nt;
+    int32_t KC;          // chunks along k (16, 32 or 128 k each)
+    int32_t GP;          // Q4: groups per column in the packed pairs
+    int32_t ks, n_groups;
+    int32_t start;       // first workgroup of this item
+    int32_t accumulate, y_bf16;
+};
+
+struct SkinnyGroup {
+    int64_t M;
+    int32_t n, pad_;
+    SkinnyItem it[kGroupMax];
 };
 
 // Activation fragment, bf16: 8 consecutive k of one row (zero outside).
@@ -82,13 +94,25 @@ __device__ __forceinline__ f32x4 load_x_f32(const float *X, int64_t ldx, int64_t
 }
 
 template <int WT, int MT, int NTW, int CMAX>
-__global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs a) {
+__global__ void __launch_bounds__(256) skinny_kernel(SkinnyGroup grp) {
     constexpr int KCH = WT == W_F32 ? 16 : (WT == W_BF16 ? 32 : 128); // k per chunk
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t nt0 = (int64_t)blockIdx.x * NTW;
-    const int ksi = blockIdx.y;
-    const int64_t m0 = (int64_t)blockIdx.z * (16 * MT);
+    const int bid = blockIdx.x;
+    int lo = 0, hi = grp.n - 1; // last item whose first workgroup is <= bid
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (grp.it[mid].start <= bid)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const SkinnyItem &a = grp.it[lo];
+    const int64_t M = grp.M;
+    const int u = bid - a.start;
+    const int64_t nt0 = (int64_t)(u % a.n_groups) * NTW;
+    const int ksi = (u / a.n_groups) % a.ks;
+    const int64_t m0 = (int64_t)(u / a.n_groups / a.ks) * (16 * MT);
 
     // this wave's chunk range
     const int64_t S = (int64_t)a.ks * 4;
@@ -144,7 +168,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs a) {
                 bf16x8 xa[MT];
 #pragma unroll
                 for (int i = 0; i < MT; ++i)
-                    xa[i] = load_x_bf16(X, a.ldx, arow + 16 * i, a.M, kb + 8 * kg, a.Ks);
+                    xa[i] = load_x_bf16(X, a.ldx, arow + 16 * i, M, kb + 8 * kg, a.Ks);
 #pragma unroll
                 for (int j = 0; j < NTW; ++j) {
                     bf16x8 b = __builtin_bit_cast(bf16x8, breg[j][c]);
@@ -157,7 +181,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs a) {
                 f32x4 xa[MT];
 #pragma unroll
                 for (int i = 0; i < MT; ++i)
-                    xa[i] = load_x_f32(X, a.ldx, arow + 16 * i, a.M, kb + 4 * kg, a.Ks);
+                    xa[i] = load_x_f32(X, a.ldx, arow + 16 * i, M, kb + 4 * kg, a.Ks);
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -177,7 +201,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs a) {
                     bf16x8 xa[MT];
 #pragma unroll
                     for (int i = 0; i < MT; ++i) {
-                        xa[i] = load_x_bf16(X, a.ldx, arow + 16 * i, a.M, kb + 32 * t + 8 * kg,
+                        xa[i] = load_x_bf16(X, a.ldx, arow + 16 * i, M, kb + 32 * t + 8 * kg,
                                             a.Ks);
                         xs[i] = mfma_bf16(xa[i], ones,
                                           (t & 1) ? xs[i] : f32x4{0.f, 0.f, 0.f, 0.f});
@@ -245,11 +269,11 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t row = m0 + 16 * i + 4 * kg + r;
-                if (row >= a.M)
+                if (row >= M)
                     continue;
                 const float v = acc[i][j][r];
                 if (a.ks > 1) {
-                    a.P[((int64_t)ksi * a.M + row) * a.Ns + col] = v;
+                    a.P[((int64_t)ksi * M + row) * a.Ns + col] = v;
                 } else if (a.y_bf16) {
                     __bf16 h = (__bf16)v;
                     static_cast<uint16_t *>(a.Y)[row * a.ldy + col] =
@@ -262,7 +286,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs a) {
     }
 }
 
-typedef void (*SkinnyFn)(SkinnyArgs);
+typedef void (*SkinnyFn)(SkinnyGroup);
 
 template <int WT, int MT>
 SkinnyFn pick_ntw(int ntw) {
@@ -287,7 +311,7 @@ SkinnyFn pick_mt(int mt, int ntw) {
 
 } // namespace
 
-SkinnyPlan skinny_plan(const PackGeom &g, tsl_dtype wdtype, int64_t M) {
+SkinnyPlan skinny_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t M) {
     SkinnyPlan p;
     const int64_t rows = M < 64 ? M : 64;
     p.mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
@@ -301,56 +325,95 @@ SkinnyPlan skinny_plan(const PackGeom &g, tsl_dtype wdtype, int64_t M) {
     else
         p.ntw = 1;
     p.cmax = p.ntw == 1 ? 16 : (p.ntw == 2 ? 8 : 4);
-    p.n_groups = (g.Nt + p.ntw - 1) / p.ntw;
-    const int64_t KC = g.KT;
-    const int64_t base = p.n_groups * p.m_blocks;
-    int64_t ks_min = (KC + 4 * p.cmax - 1) / (4 * p.cmax);
-    int64_t ks_want = (200 + base - 1) / base;
-    int64_t ks_cap = KC / 4 > 1 ? KC / 4 : 1;
-    int64_t ks = ks_want < ks_cap ? ks_want : ks_cap;
-    if (ks < ks_min)
-        ks = ks_min;
-    p.ks = (int)ks;
-    p.ws_bytes = ks > 1 ? (size_t)ks * (size_t)M * (size_t)g.Ns * sizeof(float) : 0;
+    // k-split only as far as needed for ~200 workgroups over the whole group
+    // (and at least as far as the register budget of a wave requires)
+    int64_t base = 0;
+    for (int i = 0; i < n; ++i)
+        base += (items[i].g.Nt + p.ntw - 1) / p.ntw * p.m_blocks;
+    const int64_t ks_want = base > 0 ? (200 + base - 1) / base : 1;
+    p.ks.resize(n);
+    p.ws_off.resize(n);
+    size_t off = 0;
+    for (int i = 0; i < n; ++i) {
+        const int64_t KC = items[i].g.KT;
+        const int64_t ks_min = (KC + 4 * p.cmax - 1) / (4 * p.cmax);
+        const int64_t ks_cap = KC / 4 > 1 ? KC / 4 : 1;
+        int64_t ks = ks_want < ks_cap ? ks_want : ks_cap;
+        if (ks < ks_min)
+            ks = ks_min;
+        p.ks[i] = (int)ks;
+        p.ws_off[i] = off;
+        if (ks > 1)
+            off += ((size_t)ks * (size_t)M * (size_t)items[i].g.Ns * sizeof(float) + 255) / 256 *
+                   256;
+    }
+    p.ws_bytes = off;
     return p;
 }
 
-hipError_t launch_skinny(const SkinnyPlan &p, const PackGeom &g, tsl_dtype wdtype,
-                         const void *packed, const void *X, int64_t ldx, int64_t M,
-                         tsl_dtype ydtype, void *Y, int64_t ldy, int accumulate, void *workspace,
-                         hipStream_t stream) {
-    SkinnyArgs a{};
-    a.B = packed;
-    a.SB = wdtype == TSL_Q4G64
-               ? reinterpret_cast<const uint32_t *>(static_cast<const char *>(packed) + g.codes_bytes)
-               : nullptr;
-    a.X = X;
-    a.ldx = ldx;
-    a.M = M;
-    a.Ks = g.Ks;
-    a.Ns = g.Ns;
-    a.Nt = g.Nt;
-    a.KC = g.KT;
-    a.GP = g.KT * 2;
-    a.ks = p.ks;
-    a.Y = Y;
-    a.ldy = ldy;
-    a.y_bf16 = ydtype == TSL_BF16;
-    a.accumulate = accumulate;
-    a.P = static_cast<float *>(workspace);
+int64_t skinny_blocks(const SkinnyPlan &p, const LinearItem *items, int n) {
+    int64_t most = 0;
+    for (int c0 = 0; c0 < n; c0 += kGroupMax) {
+        int64_t blocks = 0;
+        for (int i = c0; i < n && i < c0 + kGroupMax; ++i)
+            blocks += (items[i].g.Nt + p.ntw - 1) / p.ntw * p.ks[i] * p.m_blocks;
+        most = blocks > most ? blocks : most;
+    }
+    return most;
+}
 
+hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, tsl_dtype wdtype,
+                         int64_t M, void *workspace, hipStream_t stream) {
     SkinnyFn fn = wdtype == TSL_F32    ? pick_mt<W_F32>(p.mt, p.ntw)
                   : wdtype == TSL_BF16 ? pick_mt<W_BF16>(p.mt, p.ntw)
                                        : pick_mt<W_Q4>(p.mt, p.ntw);
     if (!fn)
         return hipErrorInvalidValue;
-    dim3 grid((unsigned)p.n_groups, (unsigned)p.ks, (unsigned)p.m_blocks);
-    hipLaunchKernelGGL(fn, grid, dim3(256), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.ks == 1)
-        return e;
-    return launch_splitk_reduce(static_cast<const float *>(workspace), p.ks, M, g.Ns, ydtype, Y,
-                                ldy, accumulate, stream);
+    for (int c0 = 0; c0 < n; c0 += kGroupMax) {
+        const int cn = n - c0 < kGroupMax ? n - c0 : kGroupMax;
+        SkinnyGroup grp{};
+        grp.M = M;
+        grp.n = cn;
+        int64_t blocks = 0;
+        for (int i = 0; i < cn; ++i) {
+            const LinearItem &L = items[c0 + i];
+            SkinnyItem &a = grp.it[i];
+            a.B = L.packed;
+            a.SB = wdtype == TSL_Q4G64 ? reinterpret_cast<const uint32_t *>(
+                                             static_cast<const char *>(L.packed) + L.g.codes_bytes)
+                                       : nullptr;
+            a.X = L.X;
+            a.Y = L.Y;
+            a.P = reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ws_off[c0 + i]);
+            a.ldx = L.ldx;
+            a.ldy = L.ldy;
+            a.Ks = (int32_t)L.g.Ks;
+            a.Ns = (int32_t)L.g.Ns;
+            a.Nt = (int32_t)L.g.Nt;
+            a.KC = (int32_t)L.g.KT;
+            a.GP = (int32_t)(L.g.KT * 2);
+            a.ks = p.ks[c0 + i];
+            a.n_groups = (int32_t)((L.g.Nt + p.ntw - 1) / p.ntw);
+            a.start = (int32_t)blocks;
+            a.accumulate = L.accumulate;
+            a.y_bf16 = L.ydtype == TSL_BF16;
+            blocks += (int64_t)a.n_groups * a.ks * p.m_blocks;
+        }
+        hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, stream, grp);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        for (int i = 0; i < cn; ++i) {
+            const SkinnyItem &a = grp.it[i];
+            if (a.ks == 1)
+                continue;
+            e = launch_splitk_reduce(a.P, a.ks, M, a.Ns, items[c0 + i].ydtype, a.Y, a.ldy,
+                                     a.accumulate, stream);
+            if (e != hipSuccess)
+                return e;
+        }
+    }
+    return hipSuccess;
 }
 
 } // namespace tsl

@@ -25,8 +25,9 @@ def declared_functions():
 def test_library_exports_every_declared_symbol(tsl_lib):
     names = declared_functions()
     assert set(names) == {"plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
-                          "shard_linear_workspace_size", "shard_linear", "combine_partials",
-                          "tsl_status_string", "tsl_last_hip_error_string"}
+                          "shard_linear_workspace_size", "shard_linear",
+                          "shard_linear_group_workspace_size", "shard_linear_group",
+                          "combine_partials", "tsl_status_string", "tsl_last_hip_error_string"}
     lib = ctypes.CDLL(tsl_lib.LIBRARY)
     for n in names:
         assert hasattr(lib, n), n
@@ -37,6 +38,9 @@ def test_shard_struct_layout_matches_header(tsl_lib):
     assert ctypes.sizeof(tsl_lib.Shard) == 72
     assert tsl_lib.Shard.K.offset == 16 and tsl_lib.Shard.head_off.offset == 64
     assert ctypes.sizeof(tsl_lib.Dims) == 28
+    # tsl_linear_item: 5 pointer/size_t/int64 pairs of 8 bytes, then two int32
+    assert ctypes.sizeof(tsl_lib.LinearItem) == 64
+    assert tsl_lib.LinearItem.ldy.offset == 48 and tsl_lib.LinearItem.ydtype.offset == 56
 
 
 def _lib_plan(tsl_lib, hidden, hq, hkv, hd, ffn, tp, group=0):
@@ -164,7 +168,9 @@ def test_shard_linear_rejections_before_launch(tsl_lib):
              (dict(ldx=1028), tsl_lib.ERR_MISALIGNED),
              (dict(ldx=1000), tsl_lib.ERR_INVALID_ARG),
              (dict(ldy=1000), tsl_lib.ERR_INVALID_ARG),
-             (dict(Y=Y + 2), tsl_lib.ERR_MISALIGNED)]
+             (dict(Y=Y + 2), tsl_lib.ERR_MISALIGNED),
+             # prefill path: 32-bit operand offsets bound the activation stride
+             (dict(M=128, ldx=1 << 22), tsl_lib.ERR_UNSUPPORTED)]
     for kw, status in cases:
         with pytest.raises(tsl_lib.TslError) as e:
             call(**kw)
@@ -214,8 +220,20 @@ def test_pack_and_combine_rejections_before_launch(tsl_lib):
     with pytest.raises(tsl_lib.TslError) as e:
         tsl_lib.combine_partials(7, parts, tsl_lib.F32, 4, 8, 8, tsl_lib.F32, Y, 8)
     assert e.value.status == tsl_lib.ERR_INVALID_ARG
+    # outputs overlapping a part are rejected, except F32 SUM into part 0 itself
+    overlap = [
+        (tsl_lib.COMBINE_SUM, parts[0], tsl_lib.BF16, 8),       # in place, but bf16
+        (tsl_lib.COMBINE_SUM, parts[0], tsl_lib.F32, 16),       # in place, other stride
+        (tsl_lib.COMBINE_SUM, parts[1] + 64, tsl_lib.F32, 8),   # inside part 1
+        (tsl_lib.COMBINE_CONCAT, parts[1] - 64, tsl_lib.F32, 16),  # runs into part 1
+    ]
+    for mode, Yo, yd, ldy in overlap:
+        with pytest.raises(tsl_lib.TslError) as e:
+            tsl_lib.combine_partials(mode, parts, tsl_lib.F32, 4, 8, 8, yd, Yo, ldy)
+        assert e.value.status == tsl_lib.ERR_INVALID_ARG, (mode, Yo, yd, ldy)
     # empty work succeeds without a launch
     tsl_lib.combine_partials(tsl_lib.COMBINE_SUM, parts, tsl_lib.F32, 0, 8, 8, tsl_lib.F32, Y, 8)
+    tsl_lib.combine_partials(tsl_lib.COMBINE_SUM, parts, tsl_lib.F32, 0, 8, 8, tsl_lib.BF16, parts[0], 8)
 
 
 def test_status_strings(tsl_lib):
@@ -230,3 +248,76 @@ def test_one_hip_runtime_in_process(tsl_lib):
     maps = open("/proc/self/maps").read().splitlines()
     runtimes = {l.split()[-1] for l in maps if "libamdhip64" in l}
     assert len(runtimes) == 1, runtimes
+
+
+def test_group_rejections_and_workspace(tsl_lib):
+    sh = tsl_lib.plan_linear(1024, 512, 2, tsl_lib.COLUMN, 64)
+    nb = tsl_lib.pack_shard_size(sh[0], tsl_lib.Q4G64)
+    P0, P1, X = 1 << 24, 1 << 25, 1 << 26          # fake, aligned: never dereferenced
+    Y0, Y1 = 1 << 27, (1 << 27) + (1 << 22)
+    M = 256
+
+    def item(s, P, Y, **kw):
+        return dict(dict(shard=s, packed=P, packed_bytes=nb, X=X, ldx=1024, Y=Y, ldy=256), **kw)
+
+    good = [item(sh[0], P0, Y0), item(sh[1], P1, Y1)]
+    # the group's workspace is the sum of its items' (4-bit prefill: binary16 weights)
+    w = [tsl_lib.shard_linear_workspace_size(s, tsl_lib.Q4G64, M) for s in sh]
+    assert w[0] == 1024 * 256 * 2
+    assert tsl_lib.shard_linear_group_workspace_size(good, tsl_lib.Q4G64, M) == sum(w)
+    assert tsl_lib.shard_linear_group_workspace_size(good[:1], tsl_lib.Q4G64, 4) == \
+        tsl_lib.shard_linear_workspace_size(sh[0], tsl_lib.Q4G64, 4)
+    call = lambda items, **kw: tsl_lib.shard_linear_group(
+        items, **dict(dict(wdtype=tsl_lib.Q4G64, xdtype=tsl_lib.BF16, M=M), **kw))
+    cases = [([item(sh[0], P0, Y0), item(sh[1], P1, Y0 + 512)], {}, tsl_lib.ERR_INVALID_ARG),
+             ([item(sh[0], P0, X + 64), item(sh[1], P1, Y1)], {}, tsl_lib.ERR_INVALID_ARG),
+             ([item(sh[0], P0, Y0, ydtype=tsl_lib.Q4G64)], {}, tsl_lib.ERR_INVALID_ARG),
+             ([item(sh[0], P0, Y0, ydtype=tsl_lib.BF16, accumulate=1)], {},
+              tsl_lib.ERR_UNSUPPORTED),
+             # bf16 Y0 column block beside f32 Y1: byte ranges of unequal strides
+             ([item(sh[0], P0, Y0, ydtype=tsl_lib.BF16), item(sh[1], P1, Y0 + 512)], {},
+              tsl_lib.ERR_INVALID_ARG),
+             ([item(sh[0], P0, Y0, packed_bytes=nb - 1)], {}, tsl_lib.ERR_BUFFER_TOO_SMALL),
+             ([item(sh[0], P0 + 16, Y0)], {}, tsl_lib.ERR_MISALIGNED),
+             ([item(sh[0], P0, Y0, ldx=1 << 22)], {}, tsl_lib.ERR_UNSUPPORTED),
+             (good, dict(xdtype=tsl_lib.F32), tsl_lib.ERR_UNSUPPORTED),
+             (good, dict(M=-1), tsl_lib.ERR_INVALID_ARG),
+             (good, {}, tsl_lib.ERR_BUFFER_TOO_SMALL),  # no workspace for the binary16 weights
+             ([], {}, tsl_lib.ERR_INVALID_ARG)]
+    for items, kw, status in cases:
+        with pytest.raises(tsl_lib.TslError) as e:
+            call(items, **kw)
+        assert e.value.status == status, (items, kw)
+    # empty row count: validated, nothing enqueued
+    call(good, M=0)
+
+
+def test_group_output_overlap_rule(tsl_lib):
+    """Items may write disjoint column blocks of one output (same stride);
+    any shared element is rejected.  Checked with a group whose workspace is
+    missing, so an accepted layout reports BUFFER_TOO_SMALL before any
+    launch."""
+    sh = tsl_lib.plan_linear(1024, 512, 2, tsl_lib.COLUMN, 64)
+    nb = tsl_lib.pack_shard_size(sh[0], tsl_lib.Q4G64)
+    P0, P1, X, Y = 1 << 24, 1 << 25, 1 << 26, 1 << 27
+    M, N = 256, 512
+
+    def status(y0, y1, ldy0=N, ldy1=N):
+        items = [dict(shard=sh[0], packed=P0, packed_bytes=nb, X=X, ldx=1024, Y=y0, ldy=ldy0),
+                 dict(shard=sh[1], packed=P1, packed_bytes=nb, X=X, ldx=1024, Y=y1, ldy=ldy1)]
+        try:
+            tsl_lib.shard_linear_group(items, tsl_lib.Q4G64, tsl_lib.BF16, M)
+        except tsl_lib.TslError as e:
+            return e.status
+        return tsl_lib.OK
+
+    ok, bad = tsl_lib.ERR_BUFFER_TOO_SMALL, tsl_lib.ERR_INVALID_ARG
+    assert status(Y, Y + 4 * 256) == ok                 # the two column halves of Y
+    assert status(Y + 4 * 256, Y) == ok
+    assert status(Y, Y + 4 * 252) == bad                # 4 shared columns per row
+    assert status(Y, Y + 4 * N * M) == ok               # the next matrix
+    assert status(Y, Y + 4 * (N * (M - 1) + 256)) == ok  # last row's free half
+    assert status(Y, Y + 4 * (N * (M - 1) + 255)) == bad
+    assert status(Y + 4 * N * M, Y + 4 * 256) == ok     # b before a
+    assert status(Y + 4 * (N * (M - 1) + 255), Y) == bad  # a starts on the last element of b
+    assert status(Y, Y + 4 * 256, ldy1=N + 4) == bad    # unequal strides: address ranges
