@@ -6,9 +6,9 @@ One step is the in-process multi-rank pass the mlxcel manual describes
 rank's shards and runs them in lockstep), here for one tp=4 layer of a
 27B-class model with 4-bit weights at M = 2048 prefill tokens: for every
 rank r and projection p, shard_linear(r, p) -- column outputs written
-straight into their block of the full output (the concat), row partials
-kept apart, all 28 products in one shard_linear_group call -- then
-combine_partials(SUM) of the 4 o and the 4 down partials.
+straight into their block of the full output (the concat), the 4 o and
+the 4 down shards each a sum set (their on-device rank sum) -- all 28
+products in one shard_linear_group call.
 The plan is recomputed each step (host only); packing is load-time work
 and is timed separately.
 
@@ -64,20 +64,28 @@ def build_layer(layer, M, copies, tsl, torch, synth, configs):
     return shards, packs, pack_s, pack_bytes
 
 
-def step_items(layer, M, pk, bufs, tsl, configs):
+def step_items(layer, M, pk, bufs, tsl, configs, sets=True):
     """The shard products of one multi-rank layer pass, as group items:
-    column shards write their block of the full bf16 output (the concat),
-    row shards write their own f32 partial."""
+    column shards write their block of the full bf16 output (the concat);
+    row shards form one sum set per projection (the rank sum, into the bf16
+    output), or with sets=False write their own f32 partial."""
     items, flops, nbytes = [], 0.0, 0
     for proj in configs.PROJS:
         for r in range(layer.tp):
             sh, buf, nb = pk[(r, proj)]
             if proj in ("o", "down"):
                 X = bufs["attn"] if proj == "o" else bufs["act"]
-                items.append(dict(shard=sh, packed=buf, packed_bytes=nb, X=X[:, sh.k_off:],
-                                  ldx=X.shape[1], Y=bufs["parts"][proj][r], ldy=layer.hidden,
-                                  ydtype=tsl.F32))
-                yb = 4
+                if sets:
+                    items.append(dict(shard=sh, packed=buf, packed_bytes=nb, X=X[:, sh.k_off:],
+                                      ldx=X.shape[1], Y=bufs["out"][proj] if r == 0 else None,
+                                      ldy=layer.hidden, ydtype=tsl.BF16,
+                                      sum_next=int(r < layer.tp - 1)))
+                else:
+                    items.append(dict(shard=sh, packed=buf, packed_bytes=nb, X=X[:, sh.k_off:],
+                                      ldx=X.shape[1], Y=bufs["parts"][proj][r], ldy=layer.hidden,
+                                      ydtype=tsl.F32))
+                # a set writes its bf16 sum once; separate partials are f32
+                yb = (2 if r == 0 else 0) if sets else 4
             else:
                 Y = bufs["out"][proj]
                 items.append(dict(shard=sh, packed=buf, packed_bytes=nb, X=bufs["x"],
@@ -92,8 +100,8 @@ def step_items(layer, M, pk, bufs, tsl, configs):
 
 def make_step(layer, M, shards, packs, tsl, torch, configs, seed_base):
     """Buffers and the calls of one multi-rank layer pass: one
-    shard_linear_group over every rank's 7 projections, then two
-    combine_partials(SUM)."""
+    shard_linear_group over every rank's 7 projections, the rank sums of o
+    and down included (sum sets)."""
     hq_hd = layer.n_q_heads * layer.head_dim
     kv = layer.n_kv_heads * layer.head_dim
     g = torch.Generator(device="cuda")
@@ -117,10 +125,12 @@ def make_step(layer, M, shards, packs, tsl, torch, configs, seed_base):
         items, flops, nbytes = step_items(layer, M, pk, bufs, tsl, configs)
         arr, n = tsl._items(items)
         ws_max = max(ws_max, tsl.shard_linear_group_workspace_size(items, tsl.Q4G64, M))
-        steps.append((arr, n, items))
+        sep, _, _ = step_items(layer, M, pk, bufs, tsl, configs, sets=False)
+        for it in sep:
+            ws_max = max(ws_max, tsl.shard_linear_workspace_size(it["shard"], tsl.Q4G64, M))
+        steps.append((arr, n, sep))
     # the copies run one after another on one stream: one workspace serves all
     wsbuf = torch.empty(max(ws_max, 256), dtype=torch.uint8, device="cuda")
-    comb_bytes = 2 * (layer.tp * M * layer.hidden * 4 + M * layer.hidden * 2)
 
     def run(step_index, stream, timers=None):
         arr, n, _ = steps[step_index % len(steps)]
@@ -138,12 +148,10 @@ def make_step(layer, M, shards, packs, tsl, torch, configs, seed_base):
         if timers is not None:
             e1.record()
             timers.append((e0, e1))
-        for proj in ("o", "down"):
-            tsl.combine_partials(tsl.COMBINE_SUM, bufs["parts"][proj], tsl.F32, M, layer.hidden,
-                                 layer.hidden, tsl.BF16, bufs["out"][proj], layer.hidden, stream)
 
     def run_separate(step_index, stream):
-        """The same pass as 28 separate shard_linear calls (for comparison)."""
+        """The same pass as 28 separate shard_linear calls and two
+        combine_partials (for comparison)."""
         _, _, items = steps[step_index % len(steps)]
         for it in items:
             tsl.shard_linear(it["shard"], tsl.Q4G64, it["packed"], it["packed_bytes"], tsl.BF16,
@@ -154,7 +162,7 @@ def make_step(layer, M, shards, packs, tsl, torch, configs, seed_base):
                                  layer.hidden, tsl.BF16, bufs["out"][proj], layer.hidden, stream)
 
     _, flops, nbytes = step_items(layer, M, packs[0], bufs, tsl, configs)
-    return run, run_separate, flops, nbytes + comb_bytes, len(steps[0][2])
+    return run, run_separate, flops, nbytes, len(steps[0][2])
 
 
 def prefill_bench(args, tsl, torch, synth, configs):
@@ -316,21 +324,22 @@ def main():
         "config": {"workload": "pre27b: every rank of one tp=4 27B-class layer on one GPU "
                                "(hidden 5120, ffn 17408, 64 Q / 8 KV heads of 128), 4-bit "
                                "affine g64 weights, bf16 activations, M=2048 prefill tokens; "
-                               "%d shard GEMMs (f16 MFMA, f32 accumulate) in one grouped call + "
-                               "2 on-device rank sums" % pre["nitems"],
+                               "%d shard GEMMs (f16 MFMA, f32 accumulate) and the rank sums of "
+                               "o and down, all in one shard_linear_group call" % pre["nitems"],
                    "tp": layer.tp, "M": layer.ms[0], "weights": "q4g64", "activations": "bf16",
                    "parallelism": "tp4 in-process on 1 GPU"},
         "roofline": {"bound": "mfma", "achieved": round(pre["kernel_tflops"], 2),
                      "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
                      "frac": round(pre["kernel_tflops"] / PEAK_MFMA_F16, 4), "traffic": None,
-                     "kernel": "shard_linear_group prefill launch: prep_kernel (4-bit -> f16 "
-                               "fragments) + gemm_kernel (f16 MFMA), all 28 shard GEMMs",
+                     "kernel": "the step's shard_linear_group call: prep_kernel (4-bit -> "
+                               "f16 fragments), gemm_kernel (f16 MFMA, all 28 shard GEMMs), "
+                               "2 x sum_vec_kernel (rank sums)",
                      "avg_launch_us": round(pre["kernel_ms"] * 1e3, 2)},
         "cpu_baseline": cpu,
         "decode": {"workload": "dec7b: every rank of one tp=4 7B-class layer (hidden 3584, ffn "
-                               "18944, 28 Q / 4 KV heads of 128), 4-bit g64, 28 shard GEMVs in "
-                               "one grouped call + 2 rank sums per step, HIP-graph replay over 4 "
-                               "weight copies",
+                               "18944, 28 Q / 4 KV heads of 128), 4-bit g64, 28 shard GEMVs and "
+                               "the o/down rank sums in one shard_linear_group call per step, "
+                               "HIP-graph replay over 4 weight copies",
                    "unit": "GB/s", "peak": PEAK_HBM, "rows": dec},
         "pack_GBps": round(pre["pack_gbs"], 1),
         "prefill_separate_calls_ms_per_step": round(pre["separate_ms"], 4),

@@ -242,6 +242,21 @@ tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, const void *pa
  * packed, X and Y are device pointers with the same meaning, layout and
  * alignment rules as in shard_linear; ydtype is this product's output type
  * (F32 or BF16).
+ *
+ * sum_next = 1 links the item to the next one.  A maximal run of linked
+ * items is a SUM SET: the row-parallel shards of one layer, whose products
+ * are added into the run's first item's Y -- the on-device rank sum
+ * ([mlxcel] "Communication patterns", all-reduce after row shards; [wiki]
+ * "Details" §1):
+ *     Y = (((X_0 W_0 + X_1 W_1) + X_2 W_2) + ...)
+ * each product in binary32, the sum in item order, rounded once to the first
+ * item's ydtype -- the result of shard_linear for each item followed by
+ * combine_partials(SUM).  All items of a set have the same n_len; the first
+ * item's Y, ldy and ydtype apply and its accumulate must be 0; the Y, ldy,
+ * ydtype and accumulate of the other items are ignored.  The last item of
+ * a call has sum_next = 0.  reserved must be 0.  The products of a set go
+ * to binary32 partials in the workspace (M x n_len x 4 bytes each, counted
+ * by shard_linear_group_workspace_size); one more launch adds them.
  */
 typedef struct {
     const tsl_shard *shard;
@@ -253,11 +268,14 @@ typedef struct {
     int64_t ldy;
     int32_t ydtype;
     int32_t accumulate;
+    int32_t sum_next;
+    int32_t reserved;
 } tsl_linear_item;
 
 /*
  * shard_linear_group_workspace_size -- workspace bytes shard_linear_group
- * needs for these items (only their shards are read), weight type and M.
+ * needs for these items (only their shards and sum_next are read), weight
+ * type and M.
  */
 tsl_status shard_linear_group_workspace_size(int32_t n_items, const tsl_linear_item *items,
                                              tsl_dtype wdtype, int64_t M, size_t *bytes);

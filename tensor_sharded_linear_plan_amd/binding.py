@@ -86,7 +86,8 @@ class LinearItem(ctypes.Structure):
     _fields_ = [("shard", ctypes.POINTER(Shard)), ("packed", ctypes.c_void_p),
                 ("packed_bytes", ctypes.c_size_t), ("X", ctypes.c_void_p),
                 ("ldx", ctypes.c_int64), ("Y", ctypes.c_void_p), ("ldy", ctypes.c_int64),
-                ("ydtype", ctypes.c_int32), ("accumulate", ctypes.c_int32)]
+                ("ydtype", ctypes.c_int32), ("accumulate", ctypes.c_int32),
+                ("sum_next", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _i32, _i64, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
@@ -195,7 +196,8 @@ def shard_linear(shard, wdtype, packed, packed_bytes, xdtype, X, ldx, M, ydtype,
 
 def _items(items):
     """items: sequence of dicts (or LinearItem) with the tsl_linear_item
-    fields (ydtype defaults to F32, accumulate to 0); shard is a Shard.
+    fields (ydtype defaults to F32, accumulate and sum_next to 0); shard is
+    a Shard; a set member's Y may be None.
     Returns the ctypes array (which keeps the shard copies alive) and its
     length."""
     arr = (LinearItem * max(len(items), 1))()
@@ -207,8 +209,9 @@ def _items(items):
         sh = Shard(*it["shard"].as_tuple())
         keep.append(sh)
         arr[i] = LinearItem(ctypes.pointer(sh), _ptr(it["packed"]), it["packed_bytes"],
-                            _ptr(it["X"]), it["ldx"], _ptr(it["Y"]), it["ldy"],
-                            it.get("ydtype", F32), it.get("accumulate", 0))
+                            _ptr(it["X"]), it["ldx"], _ptr(it.get("Y")), it.get("ldy", 0),
+                            it.get("ydtype", F32), it.get("accumulate", 0),
+                            it.get("sum_next", 0), it.get("reserved", 0))
     arr._keep = keep
     return arr, len(items)
 

@@ -169,9 +169,18 @@ tsl_status check_types(tsl_dtype wdtype, tsl_dtype xdtype) {
 
 // Validates one shard product (weight and activation types already
 // checked) and fills its item.
+// A member of a sum set after its first item has no output of its own
+// (need_y false): its Y fields are not checked.
 tsl_status check_item(const tsl_shard *shard, tsl_dtype wdtype, const void *packed,
                       size_t packed_bytes, tsl_dtype xdtype, const void *X, int64_t ldx, int64_t M,
-                      int ydtype, void *Y, int64_t ldy, int accumulate, LinearItem *out) {
+                      int ydtype, void *Y, int64_t ldy, int accumulate, LinearItem *out,
+                      bool need_y = true) {
+    if (!need_y) {
+        Y = reinterpret_cast<void *>(uintptr_t(256));
+        ydtype = TSL_F32;
+        accumulate = 0;
+        ldy = INT64_MAX;
+    }
     if (!shard || !packed || !X || !Y)
         return TSL_ERR_INVALID_ARG;
     if (ydtype != TSL_F32 && ydtype != TSL_BF16)
@@ -206,17 +215,66 @@ tsl_status check_item(const tsl_shard *shard, tsl_dtype wdtype, const void *pack
     out->ldy = ldy;
     out->ydtype = (tsl_dtype)ydtype;
     out->accumulate = accumulate;
+    if (!need_y) {
+        out->Y = nullptr;
+        out->ldy = 0;
+    }
     return TSL_OK;
 }
 
 // Launch order of a group: longest k first, so the longest tiles are
 // dispatched first and the short ones fill in at the end.
 std::vector<LinearItem> launch_order(const std::vector<LinearItem> &items) {
-    std::vector<LinearItem> v = items;
-    std::stable_sort(v.begin(), v.end(), [](const LinearItem &a, const LinearItem &b) {
-        return a.g.Kpad > b.g.Kpad;
-    });
+    // sum sets move as units (first item, then its members in order)
+    struct Unit {
+        size_t first, len;
+        int64_t kpad;
+    };
+    std::vector<Unit> units;
+    for (size_t i = 0; i < items.size(); i += items[i].set_len) {
+        Unit u{i, (size_t)items[i].set_len, 0};
+        for (size_t r = 0; r < u.len; ++r)
+            u.kpad = items[i + r].g.Kpad > u.kpad ? items[i + r].g.Kpad : u.kpad;
+        units.push_back(u);
+    }
+    std::stable_sort(units.begin(), units.end(),
+                     [](const Unit &a, const Unit &b) { return a.kpad > b.kpad; });
+    std::vector<LinearItem> v;
+    v.reserve(items.size());
+    for (const Unit &u : units)
+        for (size_t r = 0; r < u.len; ++r)
+            v.push_back(items[u.first + r]);
     return v;
+}
+
+// Sum sets: each member of a set runs into its own binary32 partial (in
+// the workspace, ahead of what the plan needs), balanced with every other
+// product of the group; one more launch then adds the partials of all sets
+// in order.
+
+// Rewrites every sum set of *items into lone items writing binary32
+// partials at ws, ws + ...; returns the bytes used.  Call it once: the
+// items it leaves are no longer sets.  With ws == nullptr the partials'
+// addresses are null (for sizing; such items are never launched).
+size_t split_sets(std::vector<LinearItem> *items, int64_t M, char *ws) {
+    size_t off = 0;
+    for (size_t i = 0; i < items->size();) {
+        const size_t len = (*items)[i].set_len;
+        if (len > 1) {
+            for (size_t r = 0; r < len; ++r) {
+                LinearItem &L = (*items)[i + r];
+                L.Y = ws ? ws + off : nullptr;
+                L.ldy = L.g.Ns;
+                L.ydtype = TSL_F32;
+                L.accumulate = 0;
+                L.set_len = 1;
+                L.set_pos = 0;
+                off += ((size_t)M * (size_t)L.g.Ns * 4 + 255) / 256 * 256;
+            }
+        }
+        i += len;
+    }
+    return off;
 }
 
 size_t span(int64_t M, int64_t n, int64_t ld, size_t elem);
@@ -248,10 +306,11 @@ bool matrices_overlap(const void *pa, int64_t wa, int64_t lda, size_t ea, const 
 size_t group_workspace(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_t M) {
     if (M == 0 || in.empty())
         return 0;
-    const std::vector<LinearItem> items = launch_order(in);
+    std::vector<LinearItem> items = launch_order(in);
+    const size_t parts = split_sets(&items, M, nullptr);
     if (use_skinny(wdtype, M))
-        return skinny_plan(items.data(), (int)items.size(), wdtype, M).ws_bytes;
-    return prefill_plan(items.data(), (int)items.size(), wdtype, M).ws_bytes;
+        return parts + skinny_plan(items.data(), (int)items.size(), wdtype, M).ws_bytes;
+    return parts + prefill_plan(items.data(), (int)items.size(), wdtype, M).ws_bytes;
 }
 
 // Plans and enqueues a validated group.
@@ -259,7 +318,11 @@ tsl_status run_group(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_
                      void *workspace, size_t ws_bytes, void *stream) {
     if (M == 0)
         return TSL_OK;
-    const std::vector<LinearItem> items = launch_order(in);
+    const std::vector<LinearItem> ordered = launch_order(in);
+    std::vector<LinearItem> items = ordered;
+    // (a null or short workspace is rejected below, before any launch)
+    char *ws = static_cast<char *>(workspace);
+    const size_t parts = split_sets(&items, M, ws);
     const int n = (int)items.size();
     hipStream_t s = static_cast<hipStream_t>(stream);
     size_t need;
@@ -269,11 +332,11 @@ tsl_status run_group(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_
     const bool skinny = use_skinny(wdtype, M);
     if (skinny) {
         sp = skinny_plan(items.data(), n, wdtype, M);
-        need = sp.ws_bytes;
+        need = parts + sp.ws_bytes;
         blocks = skinny_blocks(sp, items.data(), n);
     } else {
         pp = prefill_plan(items.data(), n, wdtype, M);
-        need = pp.ws_bytes;
+        need = parts + pp.ws_bytes;
         blocks = prefill_blocks(pp, items.data(), n, M);
     }
     if (blocks > kMaxBlocks)
@@ -284,9 +347,43 @@ tsl_status run_group(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_
         if (!aligned(workspace, 256))
             return TSL_ERR_MISALIGNED;
     }
-    if (skinny)
-        return from_hip(launch_skinny(sp, items.data(), n, wdtype, M, workspace, s));
-    return from_hip(launch_prefill(pp, items.data(), n, wdtype, M, workspace, s));
+    // every product that is launched writes somewhere
+    for (const LinearItem &L : items)
+        if (!L.Y)
+            return TSL_ERR_INVALID_ARG;
+    hipError_t e = skinny ? launch_skinny(sp, items.data(), n, wdtype, M, ws + parts, s)
+                          : launch_prefill(pp, items.data(), n, wdtype, M, ws + parts, s);
+    if (e != hipSuccess || !parts)
+        return from_hip(e);
+    // the rank sums of the split sets, in item order: sets of up to
+    // kSetParts members share one launch, longer ones get their own
+    std::vector<SumSpec> sums;
+    for (size_t i = 0; i < ordered.size(); i += ordered[i].set_len) {
+        const LinearItem &L = ordered[i];
+        if (L.set_len == 1)
+            continue;
+        if (L.set_len > kSetParts) {
+            const float *p[kMaxParts];
+            for (int r = 0; r < L.set_len; ++r)
+                p[r] = static_cast<const float *>(items[i + r].Y);
+            e = launch_combine_sum(L.set_len, p, M, L.g.Ns, L.g.Ns, L.ydtype, L.Y, L.ldy, s);
+            if (e != hipSuccess)
+                return from_hip(e);
+            continue;
+        }
+        SumSpec sp;
+        for (int r = 0; r < L.set_len; ++r)
+            sp.parts[r] = static_cast<const float *>(items[i + r].Y);
+        sp.n_parts = L.set_len;
+        sp.n = L.g.Ns;
+        sp.Y = L.Y;
+        sp.ldy = L.ldy;
+        sp.ydtype = L.ydtype;
+        sums.push_back(sp);
+    }
+    if (!sums.empty())
+        e = launch_sum_sets((int)sums.size(), sums.data(), M, s);
+    return from_hip(e);
 }
 
 // Gathers and validates the items of a grouped call.
@@ -298,12 +395,32 @@ tsl_status gather(int32_t n_items, const tsl_linear_item *items, tsl_dtype wdtyp
     if (st != TSL_OK)
         return st;
     out->resize(n_items);
+    int32_t first = 0; // first item of the current sum set
     for (int32_t i = 0; i < n_items; ++i) {
         const tsl_linear_item &it = items[i];
+        const bool member = i > first;
+        if ((it.sum_next != 0 && it.sum_next != 1) || it.reserved != 0)
+            return TSL_ERR_INVALID_ARG;
+        if (it.sum_next && i == n_items - 1)
+            return TSL_ERR_INVALID_ARG;
         st = check_item(it.shard, wdtype, it.packed, it.packed_bytes, xdtype, it.X, it.ldx, M,
-                        it.ydtype, it.Y, it.ldy, it.accumulate, &(*out)[i]);
+                        it.ydtype, it.Y, it.ldy, it.accumulate, &(*out)[i], !member);
         if (st != TSL_OK)
             return st;
+        LinearItem &L = (*out)[i];
+        L.set_pos = i - first;
+        if (member && L.g.Ns != (*out)[first].g.Ns)
+            return TSL_ERR_INVALID_ARG;
+        if (!it.sum_next) { // the set [first, i] is complete
+            (*out)[first].set_len = i - first + 1;
+            if (i > first && (*out)[first].accumulate)
+                return TSL_ERR_INVALID_ARG;
+            if (i - first + 1 > kMaxParts)
+                return TSL_ERR_INVALID_ARG;
+            for (int32_t r = first + 1; r <= i; ++r)
+                (*out)[r].set_len = 0;
+            first = i + 1;
+        }
     }
     if (M == 0)
         return TSL_OK;
@@ -312,13 +429,16 @@ tsl_status gather(int32_t n_items, const tsl_linear_item *items, tsl_dtype wdtyp
     const size_t xe = xdtype == TSL_F32 ? 4 : 2;
     for (int32_t i = 0; i < n_items; ++i) {
         const LinearItem &a = (*out)[i];
+        if (!a.Y)
+            continue; // a sum-set member writes into its set's output
         const size_t ea = a.ydtype == TSL_F32 ? 4 : 2;
         for (int32_t j = 0; j < n_items; ++j) {
             const LinearItem &b = (*out)[j];
             const size_t eb = b.ydtype == TSL_F32 ? 4 : 2;
             if (matrices_overlap(a.Y, a.g.Ns, a.ldy, ea, b.X, b.g.Ks, b.ldx, xe, M))
                 return TSL_ERR_INVALID_ARG;
-            if (j > i && matrices_overlap(a.Y, a.g.Ns, a.ldy, ea, b.Y, b.g.Ns, b.ldy, eb, M))
+            if (j > i && b.Y &&
+                matrices_overlap(a.Y, a.g.Ns, a.ldy, ea, b.Y, b.g.Ns, b.ldy, eb, M))
                 return TSL_ERR_INVALID_ARG;
         }
     }
@@ -364,12 +484,20 @@ extern "C" tsl_status shard_linear_group_workspace_size(int32_t n_items,
     if (!items || !bytes || n_items < 1 || n_items > kMaxItems || M < 0)
         return TSL_ERR_INVALID_ARG;
     std::vector<LinearItem> v(n_items);
+    int32_t first = 0;
     for (int32_t i = 0; i < n_items; ++i) {
-        if (!items[i].shard)
+        if (!items[i].shard || (items[i].sum_next != 0 && items[i].sum_next != 1))
             return TSL_ERR_INVALID_ARG;
         tsl_status st = geometry(*items[i].shard, wdtype, &v[i].g);
         if (st != TSL_OK)
             return st;
+        v[i].set_pos = i - first;
+        if (!items[i].sum_next || i == n_items - 1) {
+            v[first].set_len = i - first + 1;
+            for (int32_t r = first + 1; r <= i; ++r)
+                v[r].set_len = 0;
+            first = i + 1;
+        }
     }
     *bytes = group_workspace(v, wdtype, M);
     return TSL_OK;

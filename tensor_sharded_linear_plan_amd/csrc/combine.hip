@@ -104,6 +104,64 @@ __global__ void __launch_bounds__(256) splitk_kernel(const float *__restrict__ P
     }
 }
 
+// Several sums in one launch (the rank sums of a grouped shard_linear):
+// set s adds its parts (contiguous [M][n] binary32, ascending order) into
+// its own output; workgroup x -> (set, 1024-column block) by binary search.
+struct SumSet {
+    const float *p[kSetParts];
+    void *Y;
+    int64_t ldy, n;
+    int32_t n_parts, y_bf16;
+    int32_t start, pad_; // first workgroup of the set
+};
+struct SumSets {
+    int32_t n, pad_;
+    SumSet s[kMaxSets];
+};
+
+template <bool VEC>
+__global__ void __launch_bounds__(256) sum_sets_kernel(SumSets g, int64_t M) {
+    const int bid = blockIdx.x;
+    int lo = 0, hi = g.n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (g.s[mid].start <= bid)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const SumSet &st = g.s[lo];
+    constexpr int E = VEC ? 4 : 1;
+    const int64_t j = ((int64_t)(bid - st.start) * 256 + threadIdx.x) * E;
+    if (j >= st.n)
+        return;
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+        const int64_t off = m * st.n + j;
+        if constexpr (VEC) {
+            f32x4 acc = *reinterpret_cast<const f32x4 *>(st.p[0] + off);
+            for (int r = 1; r < st.n_parts; ++r) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(st.p[r] + off);
+                acc.x = acc.x + v.x;
+                acc.y = acc.y + v.y;
+                acc.z = acc.z + v.z;
+                acc.w = acc.w + v.w;
+            }
+            if (st.y_bf16)
+                store4(static_cast<uint16_t *>(st.Y) + m * st.ldy + j, acc);
+            else
+                store4(static_cast<float *>(st.Y) + m * st.ldy + j, acc);
+        } else {
+            float acc = st.p[0][off];
+            for (int r = 1; r < st.n_parts; ++r)
+                acc = acc + st.p[r][off];
+            if (st.y_bf16)
+                store1(static_cast<uint16_t *>(st.Y) + m * st.ldy + j, acc);
+            else
+                store1(static_cast<float *>(st.Y) + m * st.ldy + j, acc);
+        }
+    }
+}
+
 inline unsigned rows_grid(int64_t M) { return (unsigned)(M < 65535 ? M : 65535); }
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -167,6 +225,45 @@ hipError_t launch_combine_concat(int n_parts, const void *const *parts, size_t e
                            static_cast<char *>(Y), ldy_b, row_bytes);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_sum_sets(int n_sets, const SumSpec *sets, int64_t M, hipStream_t stream) {
+    for (int c0 = 0; c0 < n_sets; c0 += kMaxSets) {
+        const int cn = n_sets - c0 < kMaxSets ? n_sets - c0 : kMaxSets;
+        SumSets g{};
+        g.n = cn;
+        bool vec = true;
+        for (int i = 0; i < cn; ++i) {
+            const SumSpec &sp = sets[c0 + i];
+            vec = vec && sp.n % 4 == 0 && sp.ldy % 4 == 0 &&
+                  (reinterpret_cast<uintptr_t>(sp.Y) & (sp.ydtype == TSL_F32 ? 15 : 7)) == 0;
+            for (int r = 0; r < sp.n_parts; ++r)
+                vec = vec && aligned16(sp.parts[r]);
+        }
+        int64_t blocks = 0;
+        for (int i = 0; i < cn; ++i) {
+            const SumSpec &sp = sets[c0 + i];
+            SumSet &st = g.s[i];
+            for (int r = 0; r < sp.n_parts; ++r)
+                st.p[r] = sp.parts[r];
+            st.Y = sp.Y;
+            st.ldy = sp.ldy;
+            st.n = sp.n;
+            st.n_parts = sp.n_parts;
+            st.y_bf16 = sp.ydtype == TSL_BF16;
+            st.start = (int32_t)blocks;
+            blocks += (sp.n + 256 * (vec ? 4 : 1) - 1) / (256 * (vec ? 4 : 1));
+        }
+        dim3 grid((unsigned)blocks, rows_grid(M));
+        if (vec)
+            hipLaunchKernelGGL(sum_sets_kernel<true>, grid, dim3(256), 0, stream, g, M);
+        else
+            hipLaunchKernelGGL(sum_sets_kernel<false>, grid, dim3(256), 0, stream, g, M);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_splitk_reduce(const float *P, int ks, int64_t M, int64_t N, tsl_dtype ydtype,

@@ -43,6 +43,20 @@ hipError_t launch_combine_sum(int n_parts, const float *const *parts, int64_t M,
 hipError_t launch_combine_concat(int n_parts, const void *const *parts, size_t elem_bytes,
                                  int64_t M, int64_t n_each, int64_t ld_part, void *Y, int64_t ldy,
                                  hipStream_t stream);
+// Rank sums of several sum sets in one launch: set i adds its n_parts
+// contiguous [M][n] binary32 parts in order into Y (row stride ldy, F32 or
+// BF16).  n_parts <= kSetParts.
+constexpr int kSetParts = 8;
+constexpr int kMaxSets = 16;
+struct SumSpec {
+    const float *parts[kSetParts];
+    int n_parts = 0;
+    int64_t n = 0;
+    void *Y = nullptr;
+    int64_t ldy = 0;
+    tsl_dtype ydtype = TSL_F32;
+};
+hipError_t launch_sum_sets(int n_sets, const SumSpec *sets, int64_t M, hipStream_t stream);
 // Y (+)= sum_{s < ks} P[s], P is [ks][M][N] f32 contiguous, ascending s.
 hipError_t launch_splitk_reduce(const float *P, int ks, int64_t M, int64_t N, tsl_dtype ydtype,
                                 void *Y, int64_t ldy, int accumulate, hipStream_t stream);
@@ -57,6 +71,11 @@ struct LinearItem {
     int64_t ldy = 0;
     tsl_dtype ydtype = TSL_F32;
     int accumulate = 0;
+    // sum sets (rank partials added in item order into the first item's
+    // Y): the first item holds the set's length, the others 0, and each
+    // item its position in the set
+    int set_len = 1;
+    int set_pos = 0;
 };
 
 // Items per kernel launch (the item table travels in the kernel arguments);
@@ -65,12 +84,18 @@ constexpr int kGroupMax = 32;
 
 // ---- skinny.hip: decode-sized M (streams the weights once per 64 rows) ----
 struct SkinnyPlan {
-    int mt = 1;      // 16-row m-tiles per workgroup (1, 2 or 4)
-    int ntw = 1;     // 16-column n-tiles per wave (1, 2 or 4)
-    int cmax = 8;    // max k-chunks per wave (compile-time register budget)
+    bool stream = true; // bf16 / 4-bit: streaming kernel; fp32: k-split kernel
+    int mt = 1;         // 16-row m-tiles per workgroup (1, 2 or 4)
+    int ntw = 1;        // 16-column tiles per wave (1 or 2)
+    int cmax = 16;      // fp32 kernel: max k-chunks per wave
+    bool resident = false; // streaming kernel: whole k-range of X kept in LDS
+    int xstr = 0;          // ... LDS bytes per activation row
+    int xsum_off = 0;      // ... LDS offset of the 4-bit group sums
+    size_t lds_bytes = 0;  // dynamic LDS per workgroup
     int64_t m_blocks = 0;
-    // per item: k-split across workgroups (partials go to the workspace)
-    // and the byte offset of its partials in the workspace
+    // per item: workgroups across its columns, k-split across workgroups
+    // (partials go to the workspace) and the byte offset of its partials
+    std::vector<int64_t> n_groups;
     std::vector<int> ks;
     std::vector<size_t> ws_off;
     size_t ws_bytes = 0;

@@ -3,29 +3,30 @@
 // (wiki "Tensor parallel processing", "Details" §1; mlxcel manual "Tensor
 // parallelism", "Column Parallel" / "Row Parallel").
 //
-// The weights dominate the bytes, so the kernel streams every packed weight
-// byte exactly once per 64 rows: each lane issues all of its 16-byte loads
-// up front (contiguous 1 KB per wave instruction, the packed layout is
-// already in MFMA operand order), then runs 16x16 MFMAs with the
-// activations read straight from L2 as operand fragments.
+// The weights dominate the bytes, so every packed weight byte is streamed
+// from HBM exactly once per 64 rows, as contiguous 1 KB wave loads (the
+// packed layout is already in MFMA operand order), into 16x16 MFMAs.
 //
-// Work split: a workgroup = 4 waves owns NTW 16-column tiles and one of
-// `ks` k-ranges; its 4 waves take consecutive quarters of that range.  The
-// wave partials are summed in LDS in ascending k order; with ks > 1 the
-// workgroup partials go to the workspace and a second kernel sums them in
-// ascending order, so results are run-to-run deterministic.
+// bf16 and 4-bit weights use the streaming kernel below (the 4 waves of a
+// workgroup stream different column tiles over one k-range and share the
+// activations through LDS).  fp32 weights, only used at small sizes, use a
+// simpler kernel whose 4 waves split k and reduce in LDS.  When a call is
+// too small to fill the chip, a shard's k-range is split across
+// workgroups: their partials go to the workspace and a second kernel sums
+// them in ascending order, so results are run-to-run deterministic.
 //
 // One launch serves a group of shard products with the same M and types
 // (several projections, or every rank's shard of one): the item table
 // rides in the kernel arguments and each workgroup finds its item by
-// binary search over the items' first workgroup indices.  Large groups
-// need no k-split at all, which removes the second kernel.
+// binary search over the items' first workgroup indices.
 //
 // 4-bit weights (w = s q + b per group of 64 k) are applied exactly:
 // the MFMA multiplies the bf16 activations by 128 + q (an exact bf16), and
 // per group the accumulator takes s * sum(x (128 + q)) + (b - 128 s) * sum(x),
 // sum(x) coming from one extra MFMA against a ones operand.  This is the
 // group-sum identity of the affine format, evaluated in binary32.
+#include <type_traits>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -51,30 +52,12 @@ struct SkinnyItem {
 
 struct SkinnyGroup {
     int64_t M;
-    int32_t n, pad_;
+    int32_t n;
+    int32_t xstr;     // streaming kernel, resident activations: LDS bytes per row
+    int32_t xsum_off; // ... and LDS byte offset of the 4-bit group sums
+    int32_t pad_;
     SkinnyItem it[kGroupMax];
 };
-
-// Activation fragment, bf16: 8 consecutive k of one row (zero outside).
-__device__ __forceinline__ bf16x8 load_x_bf16(const uint16_t *X, int64_t ldx, int64_t row,
-                                              int64_t M, int64_t k, int64_t Ks) {
-    u32x4 v = {0, 0, 0, 0};
-    if (row < M) {
-        const uint16_t *p = X + row * ldx + k;
-        if (k + 8 <= Ks) {
-            v = *reinterpret_cast<const u32x4 *>(p);
-        } else if (k < Ks) {
-            uint16_t t[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                t[j] = (k + j < Ks) ? p[j] : (uint16_t)0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                v[j] = (uint32_t)t[2 * j] | ((uint32_t)t[2 * j + 1] << 16);
-        }
-    }
-    return __builtin_bit_cast(bf16x8, v);
-}
 
 // Activation fragment, f32: 4 consecutive k of one row (zero outside).
 __device__ __forceinline__ f32x4 load_x_f32(const float *X, int64_t ldx, int64_t row, int64_t M,
@@ -93,9 +76,14 @@ __device__ __forceinline__ f32x4 load_x_f32(const float *X, int64_t ldx, int64_t
     return v;
 }
 
-template <int WT, int MT, int NTW, int CMAX>
-__global__ void __launch_bounds__(256) skinny_kernel(SkinnyGroup grp) {
-    constexpr int KCH = WT == W_F32 ? 16 : (WT == W_BF16 ? 32 : 128); // k per chunk
+// ---- fp32 weights: k-split kernel ---------------------------------------
+// A workgroup owns one 16-column tile and one of `ks` k-ranges; its 4 waves
+// take consecutive quarters of that range, each issuing all of its weight
+// loads (up to CMAX 16-k chunks) before the 16x16x4 f32 MFMAs, and the wave
+// partials are summed in LDS in ascending k order.
+template <int MT, int CMAX>
+__global__ void __launch_bounds__(256) f32_kernel(SkinnyGroup grp) {
+    constexpr int KCH = 16; // k per chunk
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int bid = blockIdx.x;
@@ -110,7 +98,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyGroup grp) {
     const SkinnyItem &a = grp.it[lo];
     const int64_t M = grp.M;
     const int u = bid - a.start;
-    const int64_t nt0 = (int64_t)(u % a.n_groups) * NTW;
+    const int64_t nt = u % a.n_groups;
     const int ksi = (u / a.n_groups) % a.ks;
     const int64_t m0 = (int64_t)(u / a.n_groups / a.ks) * (16 * MT);
 
@@ -122,126 +110,48 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyGroup grp) {
     const int nc = (int)(c1 - c0); // <= CMAX, guaranteed by the host plan
 
     // 1. issue every weight load of this wave
-    u32x4 breg[NTW][CMAX];
-    uint32_t sbreg[NTW][CMAX][2];
+    u32x4 breg[CMAX];
     const u32x4 *B = static_cast<const u32x4 *>(a.B);
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-        const int64_t nt = nt0 + j;
-        const bool nt_ok = nt < a.Nt;
-#pragma unroll
-        for (int c = 0; c < CMAX; ++c) {
-            u32x4 v = {0, 0, 0, 0};
-            if (nt_ok && c < nc)
-                v = B[(nt * a.KC + c0 + c) * 64 + lane];
-            breg[j][c] = v;
-            if (WT == W_Q4) {
-                uint32_t s0 = 0, s1 = 0;
-                if (nt_ok && c < nc) {
-                    const uint32_t *sb = a.SB + (nt * a.GP + 2 * (c0 + c)) * 16 + (lane & 15);
-                    s0 = sb[0];
-                    s1 = sb[16];
-                }
-                sbreg[j][c][0] = s0;
-                sbreg[j][c][1] = s1;
-            }
-        }
+    for (int c = 0; c < CMAX; ++c) {
+        u32x4 v = {0, 0, 0, 0};
+        if (c < nc)
+            v = B[(nt * a.KC + c0 + c) * 64 + lane];
+        breg[c] = v;
     }
 
     // 2. multiply
-    f32x4 acc[MT][NTW];
+    f32x4 acc[MT];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NTW; ++j)
-            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int64_t arow = m0 + (lane & 15);
     const int kg = lane >> 4; // which run of k this lane feeds
-
+    const float *X = static_cast<const float *>(a.X);
 #pragma unroll
     for (int c = 0; c < CMAX; ++c) {
         if (c < nc) {
             const int64_t kb = (c0 + c) * KCH;
-            if constexpr (WT == W_BF16) {
-                const uint16_t *X = static_cast<const uint16_t *>(a.X);
-                bf16x8 xa[MT];
+            f32x4 xa[MT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+                xa[i] = load_x_f32(X, a.ldx, arow + 16 * i, M, kb + 4 * kg, a.Ks);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float b = __uint_as_float(breg[c][t]);
 #pragma unroll
                 for (int i = 0; i < MT; ++i)
-                    xa[i] = load_x_bf16(X, a.ldx, arow + 16 * i, M, kb + 8 * kg, a.Ks);
-#pragma unroll
-                for (int j = 0; j < NTW; ++j) {
-                    bf16x8 b = __builtin_bit_cast(bf16x8, breg[j][c]);
-#pragma unroll
-                    for (int i = 0; i < MT; ++i)
-                        acc[i][j] = mfma_bf16(xa[i], b, acc[i][j]);
-                }
-            } else if constexpr (WT == W_F32) {
-                const float *X = static_cast<const float *>(a.X);
-                f32x4 xa[MT];
-#pragma unroll
-                for (int i = 0; i < MT; ++i)
-                    xa[i] = load_x_f32(X, a.ldx, arow + 16 * i, M, kb + 4 * kg, a.Ks);
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int j = 0; j < NTW; ++j) {
-                        const float b = __uint_as_float(breg[j][c][t]);
-#pragma unroll
-                        for (int i = 0; i < MT; ++i)
-                            acc[i][j] = mfma_f32(xa[i][t], b, acc[i][j]);
-                    }
-            } else { // W_Q4: 4 MFMA steps of 32 k = 2 groups of 64
-                const uint16_t *X = static_cast<const uint16_t *>(a.X);
-                const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u,
-                                                                     0x3F803F80u, 0x3F803F80u});
-                f32x4 xs[MT], ag[MT][NTW];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    bf16x8 xa[MT];
-#pragma unroll
-                    for (int i = 0; i < MT; ++i) {
-                        xa[i] = load_x_bf16(X, a.ldx, arow + 16 * i, M, kb + 32 * t + 8 * kg,
-                                            a.Ks);
-                        xs[i] = mfma_bf16(xa[i], ones,
-                                          (t & 1) ? xs[i] : f32x4{0.f, 0.f, 0.f, 0.f});
-                    }
-#pragma unroll
-                    for (int j = 0; j < NTW; ++j) {
-                        const bf16x8 b = q4_to_bf16_plus128(breg[j][c][t]);
-#pragma unroll
-                        for (int i = 0; i < MT; ++i)
-                            ag[i][j] = mfma_bf16(xa[i], b,
-                                                 (t & 1) ? ag[i][j] : f32x4{0.f, 0.f, 0.f, 0.f});
-                    }
-                    if (t & 1) { // end of group 2 * chunk + t / 2
-#pragma unroll
-                        for (int j = 0; j < NTW; ++j) {
-                            const uint32_t sb = sbreg[j][c][t >> 1];
-                            const float s = bf16_lo(sb);
-                            const float cb = __builtin_fmaf(-128.f, s, bf16_hi(sb));
-#pragma unroll
-                            for (int i = 0; i < MT; ++i)
-#pragma unroll
-                                for (int r = 0; r < 4; ++r) {
-                                    acc[i][j][r] = __builtin_fmaf(s, ag[i][j][r], acc[i][j][r]);
-                                    acc[i][j][r] = __builtin_fmaf(cb, xs[i][r], acc[i][j][r]);
-                                }
-                        }
-                    }
-                }
+                    acc[i] = mfma_f32(xa[i][t], b, acc[i]);
             }
         }
     }
 
     // 3. sum the 4 wave partials in ascending k order (wave 0 first)
-    __shared__ f32x4 red[3][MT][NTW][64];
+    __shared__ f32x4 red[3][MT][64];
     if (wave > 0) {
 #pragma unroll
         for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int j = 0; j < NTW; ++j)
-                red[wave - 1][i][j][lane] = acc[i][j];
+            red[wave - 1][i][lane] = acc[i];
     }
     __syncthreads();
     if (wave != 0)
@@ -249,19 +159,361 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyGroup grp) {
 #pragma unroll
     for (int w = 0; w < 3; ++w)
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+        for (int i = 0; i < MT; ++i) {
+            const f32x4 v = red[w][i][lane];
 #pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-                const f32x4 v = red[w][i][j][lane];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[i][j][r] = acc[i][j][r] + v[r];
-            }
+            for (int r = 0; r < 4; ++r)
+                acc[i][r] = acc[i][r] + v[r];
+        }
 
     // 4. write: lane holds rows 4 * (lane / 16) + r of column lane % 16
+    const int64_t col = nt * 16 + (lane & 15);
+    if (col >= a.Ns)
+        return;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = m0 + 16 * i + 4 * kg + r;
+            if (row >= M)
+                continue;
+            const float v = acc[i][r];
+            if (a.ks > 1) {
+                a.P[((int64_t)ksi * M + row) * a.Ns + col] = v;
+            } else if (a.y_bf16) {
+                __bf16 h = (__bf16)v;
+                static_cast<uint16_t *>(a.Y)[row * a.ldy + col] = __builtin_bit_cast(uint16_t, h);
+            } else {
+                float *y = static_cast<float *>(a.Y) + row * a.ldy + col;
+                *y = a.accumulate ? *y + v : v;
+            }
+        }
+}
+
+// ---- streaming decode kernel (bf16 and 4-bit weights) ----------------------
+// A workgroup's 4 waves take 4 x NTW different 16-column tiles over one
+// k-range and share the activations through LDS; every wave keeps the
+// weight loads of the next two blocks (BK k each) in flight in a 3-deep
+// register ring.  Each wave owns whole output tiles, so there is no
+// cross-wave reduction.
+//   XRES (M <= 4): the workgroup's activation rows for its whole k-range are
+//     copied into LDS once; the block loop then has no barrier at all.
+//   otherwise: activation blocks of 16 MT rows x BK are staged through a
+//     double-buffered LDS window, loaded two blocks ahead like the weights
+//     and published with one barrier per block (rows padded by 16 bytes so
+//     the fragment reads do not conflict).
+
+// Barrier that publishes LDS writes only: the compiler's __syncthreads
+// also waits for every outstanding global load, which would drain the
+// weight prefetch each block.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// k per block of the streaming kernel: 2 (16-byte) weight loads per tile
+// per block
+constexpr int stream_bk(int wt) { return wt == W_Q4 ? 256 : 64; }
+
+// Rows whose activations stay resident in LDS for a whole k-range.
+constexpr int64_t kResidentRows = 4;
+// LDS a workgroup may use for resident activations.
+constexpr int64_t kResidentBytes = 40 * 1024;
+
+template <int WT, int MT>
+struct SB {
+    static constexpr int BK = stream_bk(WT);
+    static constexpr int LPB = WT == W_Q4 ? BK / 128 : BK / 32; // 16-byte loads per tile
+    static constexpr int ROWS = 16 * MT;
+    static constexpr int XROW = BK * 2 + 16;                     // LDS row bytes (window)
+    static constexpr int UNITS = ROWS * (BK / 8);                // 16-byte x units per block
+    static constexpr int XU = (UNITS + 255) / 256;               // per thread
+};
+
+template <int WT, int MT, int NTW, bool XRES>
+__global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
+    using S = SB<WT, MT>;
+    // XRES: [M rows][xstr bytes] sized at launch; else two [ROWS][XROW] windows
+    extern __shared__ __attribute__((aligned(16))) char xl[];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int bid = blockIdx.x;
+    int lo = 0, hi = grp.n - 1; // last item whose first workgroup is <= bid
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (grp.it[mid].start <= bid)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const SkinnyItem &a = grp.it[lo];
+    const int64_t M = grp.M;
+    const int u = bid - a.start;
+    const int tg = u % a.n_groups;
+    const int ksi = (u / a.n_groups) % a.ks;
+    const int64_t m0 = (int64_t)(u / a.n_groups / a.ks) * S::ROWS;
+    const int kg = lane >> 4; // k-run of this lane in a 32-k step
+    const int nblk = (a.Ks + S::BK - 1) / S::BK;
+    const int b0 = (int)((int64_t)ksi * nblk / a.ks);
+    const int b1 = (int)((int64_t)(ksi + 1) * nblk / a.ks);
+
+    // this wave's tiles (clamped in range; tiles past the shard are not stored)
+    const u32x4 *B = static_cast<const u32x4 *>(a.B);
+    const u32x4 *wsrc[NTW];
+    const uint32_t *ssrc[NTW];
+    int64_t ntile[NTW];
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
-        const int64_t col = (nt0 + j) * 16 + (lane & 15);
+        ntile[j] = ((int64_t)tg * 4 + wave) * NTW + j;
+        const int64_t nt = ntile[j] < a.Nt - 1 ? ntile[j] : a.Nt - 1;
+        wsrc[j] = B + nt * (int64_t)a.KC * 64 + lane;
+        ssrc[j] = WT == W_Q4 ? a.SB + nt * (int64_t)a.GP * 16 + (lane & 15) : nullptr;
+    }
+
+    // weight ring: [slot][tile][load], plus scale/bias pairs for 4-bit
+    u32x4 cw[3][NTW][S::LPB];
+    uint32_t sbw[3][NTW][S::LPB][2];
+    auto load_w = [&](auto SLOT, int b) __attribute__((always_inline)) {
+        constexpr int s = decltype(SLOT)::value;
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+            for (int l = 0; l < S::LPB; ++l) {
+                const int c = b * S::LPB + l; // chunk (4-bit) or 32-k tile (bf16)
+                const int cc = c < a.KC ? c : a.KC - 1;
+                cw[s][j][l] = wsrc[j][(int64_t)cc * 64];
+                if constexpr (WT == W_Q4) {
+                    sbw[s][j][l][0] = ssrc[j][(int64_t)(2 * cc) * 16];
+                    sbw[s][j][l][1] = ssrc[j][(int64_t)(2 * cc + 1) * 16];
+                }
+            }
+    };
+
+    // 16 bytes of activations: row m0 + r, k .. k + 7 (zero past M and K)
+    const uint16_t *X = static_cast<const uint16_t *>(a.X);
+    auto xload = [&](int64_t r, int64_t k) __attribute__((always_inline)) {
+        const int64_t row = m0 + r;
+        u32x4 v = {0, 0, 0, 0};
+        if (row < M) {
+            const uint16_t *p = X + row * a.ldx + k;
+            if (k + 8 <= a.Ks) {
+                v = *reinterpret_cast<const u32x4 *>(p);
+            } else if (k < a.Ks) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t l0 = k + 2 * e < a.Ks ? p[2 * e] : 0u;
+                    const uint32_t h0 = k + 2 * e + 1 < a.Ks ? p[2 * e + 1] : 0u;
+                    v[e] = l0 | (h0 << 16);
+                }
+            }
+        }
+        return v;
+    };
+
+    // window mode: x ring in registers, matching the weight ring slots
+    constexpr int XU = XRES ? 1 : S::XU;
+    u32x4 xr[3][XU];
+    auto load_x = [&](auto SLOT, int b) __attribute__((always_inline)) {
+        constexpr int s = decltype(SLOT)::value;
+#pragma unroll
+        for (int i = 0; i < XU; ++i) {
+            const int unit = threadIdx.x + 256 * i;
+            const int r = unit / (S::BK / 8), cu = unit % (S::BK / 8);
+            xr[s][i] = unit < S::UNITS ? xload(r, (int64_t)b * S::BK + cu * 8) : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto store_x = [&](auto SLOT, int buf) __attribute__((always_inline)) {
+        constexpr int s = decltype(SLOT)::value;
+#pragma unroll
+        for (int i = 0; i < XU; ++i) {
+            const int unit = threadIdx.x + 256 * i;
+            if (unit < S::UNITS) {
+                const int r = unit / (S::BK / 8), cu = unit % (S::BK / 8);
+                *reinterpret_cast<u32x4 *>(&xl[(buf * S::ROWS + r) * S::XROW + cu * 16]) =
+                    xr[s][i];
+            }
+        }
+    };
+
+    f32x4 acc[MT][NTW];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int kr0 = b0 * S::BK;
+    // resident rows past M read row M - 1 (finite; those outputs are not stored)
+    const int xrow = XRES ? ((lane & 15) < M - m0 ? (lane & 15) : (int)(M - m0) - 1) : 0;
+    // XRES, 4-bit: per 64-k group of the k-range, the sum of each row's
+    // activations ([group][16 rows] binary32, rows past M zero)
+    float *xsum = reinterpret_cast<float *>(xl + grp.xsum_off);
+    auto xfrag = [&](int buf, int i, int b, int k) __attribute__((always_inline)) {
+        if constexpr (XRES) {
+            return *reinterpret_cast<const bf16x8 *>(
+                &xl[xrow * grp.xstr + ((int64_t)b * S::BK + k + 8 * kg - kr0) * 2]);
+        } else {
+            const int r = 16 * i + (lane & 15);
+            return *reinterpret_cast<const bf16x8 *>(
+                &xl[(buf * S::ROWS + r) * S::XROW + (k + 8 * kg) * 2]);
+        }
+    };
+
+    auto compute = [&](auto SLOT, int buf, int b) __attribute__((always_inline)) {
+        constexpr int s = decltype(SLOT)::value;
+        if constexpr (WT == W_BF16) {
+#pragma unroll
+            for (int l = 0; l < S::LPB; ++l) {
+                bf16x8 xa[MT];
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+                    xa[i] = xfrag(buf, i, b, 32 * l);
+#pragma unroll
+                for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                    for (int i = 0; i < MT; ++i)
+                        acc[i][j] = mfma_bf16(xa[i], __builtin_bit_cast(bf16x8, cw[s][j][l]),
+                                              acc[i][j]);
+            }
+        } else {
+            const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u,
+                                                                 0x3F803F80u, 0x3F803F80u});
+#pragma unroll
+            for (int l = 0; l < S::LPB; ++l) { // 128-k chunk = 2 groups of 64
+                if (b * S::LPB + l >= a.KC)
+                    break; // odd chunk count: the block's second chunk is past K
+                f32x4 xs[MT], ag[MT][NTW];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    bf16x8 xa[MT];
+#pragma unroll
+                    for (int i = 0; i < MT; ++i) {
+                        xa[i] = xfrag(buf, i, b, 128 * l + 32 * t);
+                        if constexpr (XRES) { // group sums precomputed in LDS
+                            if (t & 1) {
+                                const int gl = (b * S::BK + 128 * l + 64 * (t >> 1) - kr0) / 64;
+                                xs[i] = *reinterpret_cast<const f32x4 *>(
+                                    &xsum[gl * 16 + 4 * kg]);
+                            }
+                        } else {
+                            xs[i] = mfma_bf16(xa[i], ones,
+                                              (t & 1) ? xs[i] : f32x4{0.f, 0.f, 0.f, 0.f});
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < NTW; ++j) {
+                        const bf16x8 bq = q4_to_bf16_plus128(cw[s][j][l][t]);
+#pragma unroll
+                        for (int i = 0; i < MT; ++i)
+                            ag[i][j] = mfma_bf16(xa[i], bq,
+                                                 (t & 1) ? ag[i][j] : f32x4{0.f, 0.f, 0.f, 0.f});
+                    }
+                    if (t & 1) { // end of a group: y += s sum(x (128 + q)) + (b - 128 s) sum(x)
+#pragma unroll
+                        for (int j = 0; j < NTW; ++j) {
+                            const uint32_t sbp = sbw[s][j][l][t >> 1];
+                            const float sc = bf16_lo(sbp);
+                            const float cb = __builtin_fmaf(-128.f, sc, bf16_hi(sbp));
+#pragma unroll
+                            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    acc[i][j][r] = __builtin_fmaf(sc, ag[i][j][r], acc[i][j][r]);
+                                    acc[i][j][r] = __builtin_fmaf(cb, xs[i][r], acc[i][j][r]);
+                                }
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    // one block in slot SLOT: prefetch block b + 2 into slot NEXT2, compute b,
+    // (window mode) publish the activations of b + 1 from slot NEXT1
+    auto step = [&](auto SLOT, auto NEXT1, auto NEXT2, int b) __attribute__((always_inline)) {
+        const int buf = (b - b0) & 1;
+        if (b + 2 < b1) {
+            if constexpr (!XRES)
+                load_x(NEXT2, b + 2);
+            load_w(NEXT2, b + 2);
+        }
+        compute(SLOT, buf, b);
+        if constexpr (!XRES) {
+            if (b + 1 < b1)
+                store_x(NEXT1, buf ^ 1);
+            lds_barrier();
+        }
+    };
+
+    if (b0 < b1) {
+        if constexpr (XRES) {
+            load_w(I0{}, b0);
+            if (b0 + 1 < b1)
+                load_w(I1{}, b0 + 1);
+            // activation rows [m0, M) x [kr0, b1 BK) into LDS, 4 units per
+            // thread per round, zero past K
+            const int64_t rows = M - m0;
+            const int per_row = (b1 - b0) * (S::BK / 8);
+            const int units = (int)rows * per_row;
+            for (int base = 0; base < units; base += 1024) {
+                u32x4 v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int unit = base + 256 * q + threadIdx.x;
+                    v[q] = unit < units ? xload(unit / per_row, kr0 + (int64_t)(unit % per_row) * 8)
+                                        : u32x4{0, 0, 0, 0};
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int unit = base + 256 * q + threadIdx.x;
+                    if (unit < units)
+                        *reinterpret_cast<u32x4 *>(
+                            &xl[(unit / per_row) * grp.xstr + (unit % per_row) * 16]) = v[q];
+                }
+            }
+            if constexpr (WT == W_Q4) {
+                lds_barrier();
+                const int groups = (b1 - b0) * (S::BK / 64);
+                for (int e = threadIdx.x; e < groups * 16; e += 256) {
+                    const int g = e >> 4, r = e & 15;
+                    float sum = 0.f;
+                    if (r < rows) {
+                        const uint16_t *xp =
+                            reinterpret_cast<const uint16_t *>(&xl[r * grp.xstr + g * 128]);
+                        for (int k = 0; k < 64; ++k)
+                            sum += __uint_as_float((uint32_t)xp[k] << 16);
+                    }
+                    xsum[e] = sum;
+                }
+            }
+        } else {
+            load_x(I0{}, b0);
+            load_w(I0{}, b0);
+            if (b0 + 1 < b1) {
+                load_x(I1{}, b0 + 1);
+                load_w(I1{}, b0 + 1);
+            }
+            store_x(I0{}, 0);
+        }
+        lds_barrier();
+        int b = b0;
+        for (; b + 3 <= b1; b += 3) {
+            step(I0{}, I1{}, I2{}, b);
+            step(I1{}, I2{}, I0{}, b + 1);
+            step(I2{}, I0{}, I1{}, b + 2);
+        }
+        if (b < b1)
+            step(I0{}, I1{}, I2{}, b);
+        if (b + 1 < b1)
+            step(I1{}, I2{}, I0{}, b + 1);
+    }
+
+    // acc[i][j] lane l: rows 16 i + 4 (l / 16) + r, column l % 16 of tile j
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+        const int64_t col = ntile[j] * 16 + (lane & 15);
         if (col >= a.Ns)
             continue;
 #pragma unroll
@@ -288,24 +540,28 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyGroup grp) {
 
 typedef void (*SkinnyFn)(SkinnyGroup);
 
-template <int WT, int MT>
-SkinnyFn pick_ntw(int ntw) {
-    switch (ntw) {
-    case 1: return skinny_kernel<WT, MT, 1, 16>;
-    case 2: return skinny_kernel<WT, MT, 2, 8>;
-    default:
-        if constexpr (MT <= 2)
-            return skinny_kernel<WT, MT, 4, 4>;
-        return nullptr;
+// fp32 weights: the k-split kernel (4 waves split k, LDS reduction)
+SkinnyFn pick_f32(int mt) {
+    switch (mt) {
+    case 1: return f32_kernel<1, 16>;
+    case 2: return f32_kernel<2, 16>;
+    default: return f32_kernel<4, 16>;
     }
 }
 
+template <int WT, int MT>
+SkinnyFn pick_stream_ntw(int ntw) {
+    return ntw == 1 ? stream_kernel<WT, MT, 1, false> : stream_kernel<WT, MT, 2, false>;
+}
+
 template <int WT>
-SkinnyFn pick_mt(int mt, int ntw) {
+SkinnyFn pick_stream(int mt, int ntw, bool resident) {
+    if (resident)
+        return ntw == 1 ? stream_kernel<WT, 1, 1, true> : stream_kernel<WT, 1, 2, true>;
     switch (mt) {
-    case 1: return pick_ntw<WT, 1>(ntw);
-    case 2: return pick_ntw<WT, 2>(ntw);
-    default: return pick_ntw<WT, 4>(ntw);
+    case 1: return pick_stream_ntw<WT, 1>(ntw);
+    case 2: return pick_stream_ntw<WT, 2>(ntw);
+    default: return pick_stream_ntw<WT, 4>(ntw);
     }
 }
 
@@ -316,47 +572,83 @@ SkinnyPlan skinny_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t
     const int64_t rows = M < 64 ? M : 64;
     p.mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
     p.m_blocks = (M + 16 * p.mt - 1) / (16 * p.mt);
-    // n-tiles per wave: reuse each activation fragment over several weight
-    // tiles once the fragment is as large as the weight bytes it meets
-    if (wdtype == TSL_Q4G64)
-        p.ntw = rows <= 2 ? 1 : (rows <= 8 ? 2 : (p.mt <= 2 ? 4 : 2));
-    else if (wdtype == TSL_BF16)
-        p.ntw = rows <= 16 ? 1 : 2;
-    else
-        p.ntw = 1;
-    p.cmax = p.ntw == 1 ? 16 : (p.ntw == 2 ? 8 : 4);
-    // k-split only as far as needed for ~200 workgroups over the whole group
-    // (and at least as far as the register budget of a wave requires)
-    int64_t base = 0;
-    for (int i = 0; i < n; ++i)
-        base += (items[i].g.Nt + p.ntw - 1) / p.ntw * p.m_blocks;
-    const int64_t ks_want = base > 0 ? (200 + base - 1) / base : 1;
+    p.stream = wdtype != TSL_F32;
     p.ks.resize(n);
     p.ws_off.resize(n);
+    p.n_groups.resize(n);
+    if (p.stream) {
+        // 4 waves x NTW tiles per workgroup, each wave over the whole k-range;
+        // k split across workgroups only when the group is too small to put
+        // ~2 workgroups on every CU
+        p.ntw = rows <= 16 ? 1 : 2;
+        const int bk = stream_bk(wdtype == TSL_Q4G64 ? W_Q4 : W_BF16);
+        int64_t base = 0;
+        for (int i = 0; i < n; ++i) {
+            p.n_groups[i] = (items[i].g.Nt + 4 * p.ntw - 1) / (4 * p.ntw);
+            base += p.n_groups[i] * p.m_blocks;
+        }
+        const int64_t ks_want = base > 0 ? (512 + base - 1) / base : 1;
+        for (int i = 0; i < n; ++i) {
+            const int64_t nblk = (items[i].g.Ks + bk - 1) / bk;
+            const int64_t cap = nblk / 2 > 1 ? nblk / 2 : 1;
+            p.ks[i] = (int)(ks_want < cap ? ks_want : cap);
+        }
+        // few rows: each workgroup keeps its activations for its whole
+        // k-range in LDS (no barrier in the block loop)
+        int64_t span = 0;
+        for (int i = 0; i < n; ++i) {
+            const int64_t nblk = (items[i].g.Ks + bk - 1) / bk;
+            const int64_t per = (nblk + p.ks[i] - 1) / p.ks[i] + 1; // blocks of a k-range
+            span = per * bk > span ? per * bk : span;
+        }
+        const int64_t xstr = span * 2 + 16;
+        const int64_t xsum = wdtype == TSL_Q4G64 ? span / 64 * 16 * 4 : 0;
+        if (M <= kResidentRows && M * xstr + xsum <= kResidentBytes) {
+            p.resident = true;
+            p.xstr = (int)xstr;
+            p.xsum_off = (int)((M * xstr + 15) / 16 * 16);
+            p.lds_bytes = (size_t)p.xsum_off + (size_t)xsum;
+        } else {
+            p.lds_bytes = 2 * (size_t)(16 * p.mt) * (size_t)(bk * 2 + 16);
+        }
+    } else {
+        // fp32: a workgroup owns one 16-column tile and one k-range split
+        // over its 4 waves; k split further for ~200 workgroups (and as far
+        // as the register budget of a wave requires)
+        p.ntw = 1;
+        p.cmax = 16;
+        int64_t base = 0;
+        for (int i = 0; i < n; ++i) {
+            p.n_groups[i] = items[i].g.Nt;
+            base += p.n_groups[i] * p.m_blocks;
+        }
+        const int64_t ks_want = base > 0 ? (200 + base - 1) / base : 1;
+        for (int i = 0; i < n; ++i) {
+            const int64_t KC = items[i].g.KT;
+            const int64_t ks_min = (KC + 4 * p.cmax - 1) / (4 * p.cmax);
+            const int64_t ks_cap = KC / 4 > 1 ? KC / 4 : 1;
+            int64_t ks = ks_want < ks_cap ? ks_want : ks_cap;
+            p.ks[i] = (int)(ks < ks_min ? ks_min : ks);
+        }
+    }
     size_t off = 0;
     for (int i = 0; i < n; ++i) {
-        const int64_t KC = items[i].g.KT;
-        const int64_t ks_min = (KC + 4 * p.cmax - 1) / (4 * p.cmax);
-        const int64_t ks_cap = KC / 4 > 1 ? KC / 4 : 1;
-        int64_t ks = ks_want < ks_cap ? ks_want : ks_cap;
-        if (ks < ks_min)
-            ks = ks_min;
-        p.ks[i] = (int)ks;
         p.ws_off[i] = off;
-        if (ks > 1)
-            off += ((size_t)ks * (size_t)M * (size_t)items[i].g.Ns * sizeof(float) + 255) / 256 *
-                   256;
+        if (p.ks[i] > 1)
+            off += ((size_t)p.ks[i] * (size_t)M * (size_t)items[i].g.Ns * sizeof(float) + 255) /
+                   256 * 256;
     }
     p.ws_bytes = off;
     return p;
 }
 
 int64_t skinny_blocks(const SkinnyPlan &p, const LinearItem *items, int n) {
+    (void)items;
     int64_t most = 0;
     for (int c0 = 0; c0 < n; c0 += kGroupMax) {
         int64_t blocks = 0;
         for (int i = c0; i < n && i < c0 + kGroupMax; ++i)
-            blocks += (items[i].g.Nt + p.ntw - 1) / p.ntw * p.ks[i] * p.m_blocks;
+            blocks += p.n_groups[i] * p.ks[i] * p.m_blocks;
         most = blocks > most ? blocks : most;
     }
     return most;
@@ -364,9 +656,9 @@ int64_t skinny_blocks(const SkinnyPlan &p, const LinearItem *items, int n) {
 
 hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, tsl_dtype wdtype,
                          int64_t M, void *workspace, hipStream_t stream) {
-    SkinnyFn fn = wdtype == TSL_F32    ? pick_mt<W_F32>(p.mt, p.ntw)
-                  : wdtype == TSL_BF16 ? pick_mt<W_BF16>(p.mt, p.ntw)
-                                       : pick_mt<W_Q4>(p.mt, p.ntw);
+    SkinnyFn fn = wdtype == TSL_F32    ? pick_f32(p.mt)
+                  : wdtype == TSL_BF16 ? pick_stream<W_BF16>(p.mt, p.ntw, p.resident)
+                                       : pick_stream<W_Q4>(p.mt, p.ntw, p.resident);
     if (!fn)
         return hipErrorInvalidValue;
     for (int c0 = 0; c0 < n; c0 += kGroupMax) {
@@ -374,6 +666,8 @@ hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, ts
         SkinnyGroup grp{};
         grp.M = M;
         grp.n = cn;
+        grp.xstr = p.xstr;
+        grp.xsum_off = p.xsum_off;
         int64_t blocks = 0;
         for (int i = 0; i < cn; ++i) {
             const LinearItem &L = items[c0 + i];
@@ -393,13 +687,20 @@ hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, ts
             a.KC = (int32_t)L.g.KT;
             a.GP = (int32_t)(L.g.KT * 2);
             a.ks = p.ks[c0 + i];
-            a.n_groups = (int32_t)((L.g.Nt + p.ntw - 1) / p.ntw);
-            a.start = (int32_t)blocks;
+            a.n_groups = (int32_t)p.n_groups[c0 + i];
             a.accumulate = L.accumulate;
             a.y_bf16 = L.ydtype == TSL_BF16;
+            a.start = (int32_t)blocks;
             blocks += (int64_t)a.n_groups * a.ks * p.m_blocks;
         }
-        hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, stream, grp);
+        if (p.lds_bytes > 64 * 1024) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)p.lds_bytes);
+            if (e != hipSuccess)
+                return e;
+        }
+        hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), p.lds_bytes, stream, grp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;

@@ -38,9 +38,10 @@ def test_shard_struct_layout_matches_header(tsl_lib):
     assert ctypes.sizeof(tsl_lib.Shard) == 72
     assert tsl_lib.Shard.K.offset == 16 and tsl_lib.Shard.head_off.offset == 64
     assert ctypes.sizeof(tsl_lib.Dims) == 28
-    # tsl_linear_item: 5 pointer/size_t/int64 pairs of 8 bytes, then two int32
-    assert ctypes.sizeof(tsl_lib.LinearItem) == 64
+    # tsl_linear_item: seven 8-byte fields, then four int32
+    assert ctypes.sizeof(tsl_lib.LinearItem) == 72
     assert tsl_lib.LinearItem.ldy.offset == 48 and tsl_lib.LinearItem.ydtype.offset == 56
+    assert tsl_lib.LinearItem.sum_next.offset == 64
 
 
 def _lib_plan(tsl_lib, hidden, hq, hkv, hd, ffn, tp, group=0):
@@ -321,3 +322,48 @@ def test_group_output_overlap_rule(tsl_lib):
     assert status(Y + 4 * N * M, Y + 4 * 256) == ok     # b before a
     assert status(Y + 4 * (N * (M - 1) + 255), Y) == bad  # a starts on the last element of b
     assert status(Y, Y + 4 * 256, ldy1=N + 4) == bad    # unequal strides: address ranges
+
+
+def test_sum_set_rules(tsl_lib):
+    """Sum sets: validation before launch and their workspace."""
+    K, N, tp, M = 1024, 512, 4, 256
+    sh = tsl_lib.plan_linear(K, N, tp, tsl_lib.ROW, 64)
+    nb = tsl_lib.pack_shard_size(sh[0], tsl_lib.Q4G64)
+    X, Y = 1 << 26, 1 << 27
+
+    def items(changes=None):
+        out = []
+        for r, s in enumerate(sh):
+            it = dict(shard=s, packed=(1 << 24) + r * (1 << 20), packed_bytes=nb,
+                      X=X + 2 * s.k_off, ldx=K, Y=Y if r == 0 else None, ldy=N,
+                      sum_next=1 if r < tp - 1 else 0)
+            it.update((changes or {}).get(r, {}))
+            out.append(it)
+        return out
+
+    # prefill: the set's products go to binary32 partials in the workspace
+    # first (M x N x 4 bytes each), then the binary16 weights
+    w = sum(tsl_lib.shard_linear_workspace_size(s, tsl_lib.Q4G64, M) for s in sh)
+    assert tsl_lib.shard_linear_group_workspace_size(items(), tsl_lib.Q4G64, M) == \
+        w + tp * M * N * 4
+    # decode: the same partials (the products themselves need no workspace here)
+    assert tsl_lib.shard_linear_group_workspace_size(items(), tsl_lib.Q4G64, 4) == tp * 4 * N * 4
+    call = lambda its, M=M: tsl_lib.shard_linear_group(its, tsl_lib.Q4G64, tsl_lib.BF16, M)
+    bad = [items({3: dict(sum_next=1)}),                 # the last item links on
+           items({1: dict(sum_next=2)}),
+           items({2: dict(reserved=1)}),
+           items({0: dict(accumulate=1)}),               # a set's output cannot accumulate
+           items({0: dict(Y=None)})]
+    for its in bad:
+        with pytest.raises(tsl_lib.TslError) as e:
+            call(its)
+        assert e.value.status == tsl_lib.ERR_INVALID_ARG
+    # members must share n_len
+    other = tsl_lib.plan_linear(K, 2 * N, tp, tsl_lib.ROW, 64)[1]
+    with pytest.raises(tsl_lib.TslError) as e:
+        call(items({1: dict(shard=other, packed_bytes=1 << 30)}))
+    assert e.value.status == tsl_lib.ERR_INVALID_ARG
+    # a well-formed set passes validation (no workspace given -> too small)
+    with pytest.raises(tsl_lib.TslError) as e:
+        call(items())
+    assert e.value.status == tsl_lib.ERR_BUFFER_TOO_SMALL

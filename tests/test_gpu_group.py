@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import Q4Weight, dev, empty_bytes, host, linear, normwise, spec_dict, torch
+from gpu_util import (Q4Weight, dev, empty_bytes, host, host_bits, linear, normwise, spec_dict,
+                      torch)
 from tensor_sharded_linear_plan_amd import binding as tsl
 from tensor_sharded_linear_plan_amd import configs, synth
 from test_gpu_layers import LayerWeights, activations, check, sample_rows
@@ -113,3 +114,73 @@ def test_long_group_concat_free(M, wdtype):
         ref = oracle.gemm(ref_x, full)
         err = normwise(host(outs), ref)
         assert err <= TOL + 2.0 ** -9, err
+
+
+@pytest.mark.parametrize("variant", ["random", "integer"])
+@pytest.mark.parametrize("layer,M", CASES, ids=["%s-M%d" % (l.name, m) for l, m in CASES])
+def test_row_layers_as_sum_sets(layer, M, variant):
+    """o and down of every rank in one group, each projection's ranks a sum
+    set: the on-device rank sum happens inside the grouped call."""
+    t = torch()
+    shards = tsl.plan_shards(layer.hidden, layer.n_q_heads, layer.n_kv_heads, layer.head_dim,
+                             layer.ffn, layer.tp, layer.group)
+    items, checks, keep = [], [], []
+    for proj in ("o", "down"):
+        pi = configs.PROJS.index(proj)
+        w = LayerWeights(layer, proj, variant)
+        X = activations(layer, proj, M, w.K, variant)
+        dX = dev(X)
+        bf = variant == "random" and proj == "down"  # one bf16 output
+        Y = t.full((M, w.N), float("nan"), dtype=t.bfloat16 if bf else t.float32, device="cuda")
+        rows = sample_rows(M, w.K // layer.tp, w.N)
+        Xf = oracle.bf16_to_f64(X[rows])
+        refs = []
+        for r in range(layer.tp):
+            sh = shards[r * tsl.NPROJ + pi]
+            buf, nb = w.pack(sh)
+            keep.append(buf)
+            items.append(dict(shard=sh, packed=buf, packed_bytes=nb, X=dX[:, sh.k_off:], ldx=w.K,
+                              Y=Y if r == 0 else None, ldy=w.N,
+                              ydtype=tsl.BF16 if bf else tsl.F32,
+                              sum_next=1 if r < layer.tp - 1 else 0))
+            s = spec_dict(sh)
+            refs.append(oracle.gemm(oracle.slice_input(Xf, s), w.shard_f64(s)))
+        keep.append(dX)
+        checks.append((proj, Y, rows, oracle.combine_sum(refs)))
+    run_group(items, tsl.Q4G64 if layer.wdtype == configs.Q4 else tsl.BF16, M)
+    for proj, Y, rows, ref in checks:
+        what = "%s M=%d %s sum set" % (layer.name, M, proj)
+        if Y.dtype == t.bfloat16:
+            assert normwise(host(Y)[rows], ref) <= TOL + 2.0 ** -9, what
+        else:
+            check(host(Y)[rows], ref, variant, what)
+
+
+@pytest.mark.parametrize("M", [1, 3, 16, 100])
+def test_sum_set_equals_products_then_combine(M):
+    """A sum set gives the ordered binary32 sum of its members' products:
+    bit for bit what separate products + combine_partials(SUM) give when the
+    products are computed the same way (here: one group without sets, with
+    every item large enough to need no k split), and the bf16 output is that
+    sum rounded once."""
+    t = torch()
+    K, N, tp = 2048, 4096, 4
+    w = Q4Weight(K, N, 3300, 3301, 3302)
+    X = dev(synth.normal_bf16(3303 + M, (M, K)))
+    shards = tsl.plan_linear(K, N, tp, tsl.ROW, 64)
+    packs = [w.pack(sh) for sh in shards]
+    parts = [t.full((M, N), float("nan"), dtype=t.float32, device="cuda") for _ in shards]
+    plain = [dict(shard=sh, packed=b, packed_bytes=nb, X=X[:, sh.k_off:], ldx=K, Y=P, ldy=N)
+             for sh, (b, nb), P in zip(shards, packs, parts)]
+    run_group(plain, tsl.Q4G64, M)
+    want = t.empty((M, N), dtype=t.float32, device="cuda")
+    tsl.combine_partials(tsl.COMBINE_SUM, parts, tsl.F32, M, N, N, tsl.F32, want, N)
+    for ydt, tdt in ((tsl.F32, t.float32), (tsl.BF16, t.bfloat16)):
+        Y = t.full((M, N), float("nan"), dtype=tdt, device="cuda")
+        sets = [dict(p, Y=Y if r == 0 else None, ydtype=ydt, sum_next=int(r < tp - 1))
+                for r, p in enumerate(plain)]
+        run_group(sets, tsl.Q4G64, M)
+        if ydt == tsl.F32:
+            assert t.equal(Y, want)
+        else:
+            assert np.array_equal(host_bits(Y), oracle.f64_to_bf16(host(want)))
