@@ -194,9 +194,10 @@ tsl_status pack_shard(const tsl_shard *shard, tsl_dtype wdtype, const void *W, i
 /*
  * shard_linear_workspace_size -- workspace bytes shard_linear needs for
  * this shard, weight type and row count (0 when none is needed): split-K
- * partial sums for decode-sized M; with M > 64 the shard expanded to
- * binary16 for 4-bit weights (2 bytes per weight), or a zero-padded copy of
- * the activations for BF16 weights when k_len is not a multiple of 64.
+ * partial sums for decode-sized M; with M > 64, for 4-bit weights the shard
+ * expanded to binary16 (2 bytes per weight) and a binary16 copy of the
+ * activations (M x k_len x 2 bytes), for BF16 weights a zero-padded copy of
+ * the activations when k_len is not a multiple of 64.
  */
 tsl_status shard_linear_workspace_size(const tsl_shard *shard, tsl_dtype wdtype, int64_t M,
                                        size_t *bytes);
@@ -275,7 +276,8 @@ typedef struct {
 /*
  * shard_linear_group_workspace_size -- workspace bytes shard_linear_group
  * needs for these items (only their shards and sum_next are read), weight
- * type and M.
+ * type and M.  An upper bound: a call whose items read the same X (same
+ * pointer, ldx and k_len) shares one activation copy and uses less.
  */
 tsl_status shard_linear_group_workspace_size(int32_t n_items, const tsl_linear_item *items,
                                              tsl_dtype wdtype, int64_t M, size_t *bytes);

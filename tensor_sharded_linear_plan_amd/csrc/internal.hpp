@@ -111,8 +111,11 @@ struct PrefillPlan {
     int bm = 256, bn = 160; // block tile
     int wm = 4, wn = 1;     // wave grid
     // per item: byte offsets in the workspace of its binary16 weights (4-bit
-    // shards) and of its zero-padded activation copy (K not a multiple of 64)
+    // shards) and of its activation copy (binary16 for 4-bit shards,
+    // zero-padded bf16 when K is not a multiple of 64), and the item whose
+    // copy it reads (itself for the first reader of an X; -1: no copy)
     std::vector<size_t> w_off, x_off;
+    std::vector<int> x_first;
     size_t ws_bytes = 0;
 };
 bool prefill_supported(tsl_dtype wdtype);

@@ -24,10 +24,10 @@
 //
 // Operands: bf16 x bf16, or f16 x f16 for 4-bit weights.  For the latter a
 // prep kernel first expands the weights to binary16 fragments (w = s q + b
-// rounded once) in the workspace, and the GEMM narrows each bf16 activation
-// fragment to binary16 as it leaves LDS (exact below 65536 in magnitude).
-// bf16 activations are copied, zero-padded, only when K is not a multiple
-// of 64.  Accumulation is binary32.
+// rounded once) and narrows each distinct activation matrix once to
+// binary16 (exact below 65536 in magnitude; items reading the same X share
+// the copy) in the workspace.  bf16 activations are copied, zero-padded,
+// only when K is not a multiple of 64.  Accumulation is binary32.
 //
 // One launch serves a group of shard products with the same M and types;
 // the item table rides in the kernel arguments.  Each item's tiles take a
@@ -149,40 +149,44 @@ gemm_kernel(GemmGroup grp) {
     const int64_t mb = first_m + in_band % bm_cnt, nb = in_band / bm_cnt;
     const int64_t m0 = mb * BM, n0 = nb * BN;
 
-    // Sources of this wave's LDS blocks: block f < AF holds activation rows
-    // 8f..8f+7 of the tile, the others weight fragments (32 columns x 16 k).
-    // Each is a per-lane byte offset from a tile base that advances by a
-    // constant per stage (f < AF exactly when j < AF / 4).  Rows past M and
-    // columns past the shard are clamped to the last valid ones: in bounds,
-    // and those outputs are never stored.  Offsets stay below 2^32 because
-    // the activation row stride and K are below 2^22 elements (checked by
-    // the caller).
+    // Sources of this wave's LDS blocks: block f = wave + 4 j < AF holds
+    // activation rows 8f..8f+7 of the tile, the others weight fragments
+    // (32 columns x 16 k; f < AF exactly when j < AF / 4).  Each is a
+    // per-lane byte offset from a tile base that advances by a constant per
+    // stage; the offsets are recomputed at every issue (a few VALU ops)
+    // rather than held in registers.  Rows past M and columns past the
+    // shard are clamped to the last valid ones: in bounds, and those outputs
+    // are never stored.  Offsets stay below 2^32 because the activation row
+    // stride and K are below 2^22 elements (checked by the caller).
     const char *xbase = reinterpret_cast<const char *>(a.X + m0 * a.ldx);
     const int64_t t0 = n0 >> 4;
-    const char *bbase = reinterpret_cast<const char *>(a.B + t0 * a.KT32 * 64);
-    uint32_t off[C::FPW];
-#pragma unroll
-    for (int j = 0; j < C::FPW; ++j) {
-        const int f = wave + 4 * j;
-        if (j < C::AF / 4) {
-            int64_t row = m0 + 8 * f + (lane >> 3);
-            row = row < M - 1 ? row : M - 1;
-            off[j] = (uint32_t)(((row - m0) * a.ldx + 8 * ((lane & 7) ^ (lane >> 3))) * 2);
-        } else {
-            const int g = f - C::AF, nt = g >> 2, s = g & 3;
-            const int64_t n = n0 + nt * 32 + (lane & 31);
-            int64_t t16 = n >> 4;
-            t16 = t16 < a.Nt16 - 1 ? t16 : a.Nt16 - 1;
-            const int kr = 2 * s + (lane >> 5); // 8-k run within the stage
-            off[j] = (uint32_t)((((t16 - t0) * a.KT32 + (kr >> 2)) * 64 + (kr & 3) * 16 + (n & 15)) * 16);
-        }
-    }
+    const char *bbase = reinterpret_cast<const char *>(a.B + t0 * (int64_t)a.KT32 * 64);
+    const uint32_t chunk = 8 * ((lane & 7) ^ (lane >> 3));
+    const uint32_t aoff0 = ((uint32_t)(8 * wave + (lane >> 3)) * (uint32_t)a.ldx + chunk) * 2;
+    const uint32_t astep = 32 * (uint32_t)a.ldx * 2; // 32 rows
+    const uint32_t alim = ((uint32_t)(M - 1 - m0) * (uint32_t)a.ldx + chunk) * 2;
+    const int kr = 2 * wave + (lane >> 5); // 8-k run of this wave's weight blocks
+    const uint32_t boff0 = ((uint32_t)((kr >> 2) * 64 + (kr & 3) * 16 + (lane & 15))) * 16;
+    const uint32_t tstep = (uint32_t)a.KT32 * 1024; // one 16-column tile
+    const int tmax = (int)(a.Nt16 - 1 - t0);
+    const int th = (lane & 31) >> 4;
     auto issue = [&](int64_t kt, char *buf) __attribute__((always_inline)) {
         const char *xb = xbase + kt * (64 * 2);
         const char *bb = bbase + kt * (2 * 64 * 16);
+        uint32_t a0 = aoff0, b0 = boff0;
+        asm volatile("" : "+v"(a0), "+v"(b0)); // keep the per-j offsets out of registers
 #pragma unroll
-        for (int j = 0; j < C::FPW; ++j)
-            dma16(j < C::AF / 4 ? xb : bb, off[j], buf + (wave + 4 * j) * 1024);
+        for (int j = 0; j < C::FPW; ++j) {
+            uint32_t off;
+            if (j < C::AF / 4) {
+                const uint32_t o = a0 + (uint32_t)j * astep;
+                off = o < alim ? o : alim;
+            } else {
+                const int tt = 2 * (j - C::AF / 4) + th;
+                off = b0 + (uint32_t)(tt < tmax ? tt : tmax) * tstep;
+            }
+            dma16(j < C::AF / 4 ? xb : bb, off, buf + (wave + 4 * j) * 1024);
+        }
     };
 
     f32x16 acc[C::MT][C::NT];
@@ -225,20 +229,11 @@ gemm_kernel(GemmGroup grp) {
         for (int s = 0; s < 4; ++s) {
             if (s < 3)
                 rd(s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
-            u32x4 au[C::MT];
-#pragma unroll
-            for (int i = 0; i < C::MT; ++i) {
-                au[i] = af[s & 1][i];
-                if constexpr (OP == OP_F16) // bf16 activations meet f16 weights
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        au[i][q] = bf16pair_to_f16pair(au[i][q]);
-            }
 #pragma unroll
             for (int i = 0; i < C::MT; ++i)
 #pragma unroll
                 for (int j = 0; j < C::NT; ++j)
-                    acc[i][j] = mfma32(au[i], bfr[s & 1][j], acc[i][j], OP);
+                    acc[i][j] = mfma32(af[s & 1][i], bfr[s & 1][j], acc[i][j], OP);
         }
     };
 
@@ -266,29 +261,39 @@ gemm_kernel(GemmGroup grp) {
     }
 
     // ---- epilogue: acc reg r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32 ----
+    // One base address per lane; every store is that base plus a
+    // compile-time row/column step times the (uniform) row stride.
+    const int64_t row0 = m0 + wm * C::MT * 32 + 4 * (lane >> 5);
+    const int64_t col0 = n0 + wn * C::NT * 32 + (lane & 31);
+    const int esz = a.y_bf16 ? 2 : 4;
+    char *ybase = static_cast<char *>(a.Y) + (row0 * a.ldy + col0) * esz;
+    const int64_t rstride = a.ldy * esz;
+    bool colok[C::NT];
 #pragma unroll
-    for (int j = 0; j < C::NT; ++j) {
-        const int64_t col = n0 + (wn * C::NT + j) * 32 + (lane & 31);
-        if (col >= a.Ns)
-            continue;
+    for (int j = 0; j < C::NT; ++j)
+        colok[j] = col0 + 32 * j < a.Ns;
 #pragma unroll
-        for (int i = 0; i < C::MT; ++i)
+    for (int i = 0; i < C::MT; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row =
-                    m0 + (wm * C::MT + i) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (row >= M)
+        for (int r = 0; r < 16; ++r) {
+            const int rr = i * 32 + 8 * (r >> 2) + (r & 3); // row step from row0
+            if (row0 + rr >= M)
+                continue;
+            char *yr = ybase + rr * rstride;
+#pragma unroll
+            for (int j = 0; j < C::NT; ++j) {
+                if (!colok[j])
                     continue;
                 const float v = acc[i][j][r];
                 if (a.y_bf16) {
                     __bf16 h = (__bf16)v;
-                    static_cast<uint16_t *>(a.Y)[row * a.ldy + col] = __builtin_bit_cast(uint16_t, h);
+                    *reinterpret_cast<uint16_t *>(yr + j * 64) = __builtin_bit_cast(uint16_t, h);
                 } else {
-                    float *y = static_cast<float *>(a.Y) + row * a.ldy + col;
+                    float *y = reinterpret_cast<float *>(yr + j * 128);
                     *y = a.accumulate ? *y + v : v;
                 }
             }
-    }
+        }
 }
 
 // ---- prep: 4-bit weights -> binary16 fragments, ragged-K activations -> padded copy ----
@@ -310,7 +315,8 @@ struct PrepItem {
 };
 
 struct PrepGroup {
-    int32_t n, pad_;
+    int32_t n;
+    int32_t to_f16; // activations narrowed to binary16 (4-bit weights)
     PrepItem it[kGroupMax];
 };
 
@@ -372,6 +378,11 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepGroup grp) {
             v[j] = lo2 | (hi2 << 16);
         }
     }
+    if (grp.to_f16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = bf16pair_to_f16pair(v[j]);
+    }
     *reinterpret_cast<u32x4 *>(p.x_out + m * p.Kpad + k) = v;
 }
 
@@ -381,18 +392,16 @@ struct Variant {
     int bm, bn, wm, wn;
 };
 // tile shapes with a kernel instance
-// (256 x 256 needs more than the 512 registers a lane has at one wave per
-// SIMD and is left out)
-constexpr Variant kVariants[] = {{256, 160, 4, 1}, {256, 128, 2, 2}, {128, 256, 2, 2},
-                                 {128, 128, 2, 2}, {256, 64, 4, 1},  {128, 64, 2, 2},
-                                 {64, 64, 2, 2}};
+constexpr Variant kVariants[] = {{256, 256, 2, 2}, {256, 160, 4, 1}, {256, 128, 2, 2},
+                                 {128, 256, 2, 2}, {128, 128, 2, 2}, {256, 64, 4, 1},
+                                 {128, 64, 2, 2},  {64, 64, 2, 2}};
 
 template <int OP>
 GemmFn pick(const Variant &v) {
 #define TSL_CASE(BM_, BN_, WM_, WN_)                                                               \
     if (v.bm == BM_ && v.bn == BN_ && v.wm == WM_ && v.wn == WN_)                                  \
         return gemm_kernel<OP, BM_, BN_, WM_, WN_>;
-    TSL_CASE(256, 160, 4, 1) TSL_CASE(256, 128, 2, 2)
+    TSL_CASE(256, 256, 2, 2) TSL_CASE(256, 160, 4, 1) TSL_CASE(256, 128, 2, 2)
     TSL_CASE(128, 256, 2, 2) TSL_CASE(128, 128, 2, 2) TSL_CASE(256, 64, 4, 1)
     TSL_CASE(128, 64, 2, 2) TSL_CASE(64, 64, 2, 2)
 #undef TSL_CASE
@@ -462,19 +471,35 @@ PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64
             best.wn = v.wn;
         }
     }
-    // workspace: binary16 weight fragments of 4-bit items, padded
-    // activation copies of ragged-K bf16 items
+    // workspace: binary16 weight fragments of 4-bit items; activation
+    // copies (binary16 for 4-bit items, zero-padded bf16 for ragged-K bf16
+    // items), one per distinct (X, ldx, K) -- items without a known X
+    // (sizing) never share
     best.w_off.assign(n, 0);
     best.x_off.assign(n, 0);
+    best.x_first.assign(n, -1);
     size_t off = 0;
     for (int i = 0; i < n; ++i) {
         const PackGeom &g = items[i].g;
         if (wdtype == TSL_Q4G64) {
             best.w_off[i] = off;
             off += (size_t)g.Nt * (size_t)g.KT * 4 * 1024;
-        } else if (g.Ks % 64 != 0) {
-            best.x_off[i] = off;
-            off += ((size_t)M * (size_t)kpad64(g.Ks) * 2 + 255) / 256 * 256;
+        }
+        if (wdtype == TSL_Q4G64 || g.Ks % 64 != 0) {
+            int first = i;
+            for (int j = 0; j < i && items[i].X; ++j)
+                if (items[j].X == items[i].X && items[j].ldx == items[i].ldx &&
+                    items[j].g.Ks == g.Ks && best.x_first[j] == j) {
+                    first = j;
+                    break;
+                }
+            best.x_first[i] = first;
+            if (first == i) {
+                best.x_off[i] = off;
+                off += ((size_t)M * (size_t)kpad64(g.Ks) * 2 + 255) / 256 * 256;
+            } else {
+                best.x_off[i] = best.x_off[first];
+            }
         }
     }
     best.ws_bytes = off;
@@ -490,14 +515,16 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
     char *ws = static_cast<char *>(workspace);
     for (int c0 = 0; c0 < n; c0 += kGroupMax) {
         const int cn = n - c0 < kGroupMax ? n - c0 : kGroupMax;
-        // 1. prep: expand 4-bit weights, pad ragged-K activations
+        // 1. prep: expand 4-bit weights, copy activations (once per X)
         PrepGroup pg{};
+        pg.to_f16 = wdtype == TSL_Q4G64;
         int64_t pblocks = 0;
         for (int i = 0; i < cn; ++i) {
             const LinearItem &L = items[c0 + i];
             const PackGeom &g = L.g;
-            const bool q4 = wdtype == TSL_Q4G64, pad = !q4 && g.Ks % 64 != 0;
-            if (!q4 && !pad)
+            const bool q4 = wdtype == TSL_Q4G64;
+            const bool xcopy = p.x_first[c0 + i] == c0 + i;
+            if (!q4 && !xcopy)
                 continue;
             PrepItem &a = pg.it[pg.n++];
             a.codes = static_cast<const u32x4 *>(L.packed);
@@ -509,7 +536,7 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
             a.ldx_in = L.ldx;
             a.w_chunks = q4 ? g.Nt * g.KT * 64 : 0;
             a.Kpad = (int32_t)kpad64(g.Ks);
-            a.x_units = pad ? M * (a.Kpad / 8) : 0;
+            a.x_units = xcopy ? M * (a.Kpad / 8) : 0;
             a.KB = (int32_t)g.KT;
             a.GP = (int32_t)(g.KT * 2);
             a.Gs = (int32_t)(g.Ks / 64);
@@ -533,12 +560,12 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
             const LinearItem &L = items[c0 + i];
             const PackGeom &g = L.g;
             GemmItem &a = grp.it[i];
-            const bool q4 = wdtype == TSL_Q4G64, pad = !q4 && g.Ks % 64 != 0;
+            const bool q4 = wdtype == TSL_Q4G64, copied = p.x_first[c0 + i] >= 0;
             a.B = static_cast<const u32x4 *>(q4 ? static_cast<const void *>(ws + p.w_off[c0 + i])
                                                 : L.packed);
-            a.X = pad ? reinterpret_cast<const uint16_t *>(ws + p.x_off[c0 + i])
-                      : static_cast<const uint16_t *>(L.X);
-            a.ldx = pad ? kpad64(g.Ks) : L.ldx;
+            a.X = copied ? reinterpret_cast<const uint16_t *>(ws + p.x_off[c0 + i])
+                         : static_cast<const uint16_t *>(L.X);
+            a.ldx = copied ? kpad64(g.Ks) : L.ldx;
             a.Y = L.Y;
             a.ldy = L.ldy;
             a.Ns = (int32_t)g.Ns;
