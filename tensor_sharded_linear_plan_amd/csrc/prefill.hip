@@ -73,18 +73,35 @@ struct GemmGroup {
 
 constexpr int kLdsLimit = 160 * 1024;
 
+// Tile geometry.  A stage covers BK k: 64, or 32 when three 64-k stages do
+// not fit in LDS (then four 32-k stages do).  Activation rows are copied in
+// 1 KB LDS blocks of RPB rows (RPB x BK x 2 bytes); weight blocks are 32
+// columns x 16 k.
 template <int OP, int BM, int BN, int WM, int WN>
 struct G {
     static constexpr int TM = BM / WM, TN = BN / WN; // wave tile
     static constexpr int MT = TM / 32, NT = TN / 32; // 32x32 tiles per wave
-    static constexpr int AF = BM / 8, BF = BN / 8;   // 1 KB LDS blocks per stage
-    static constexpr int FPW = (AF + BF) / 4;        // DMA instructions per wave per stage
+    static constexpr int BK = 3 * (BM + BN) * 128 <= kLdsLimit ? 64 : 32;
+    static constexpr int S16 = BK / 16;             // 16-k MFMA steps per stage
+    static constexpr int CPR = BK / 8;              // 16-byte chunks per activation row
+    static constexpr int RPB = 64 / CPR;            // activation rows per 1 KB block
+    static constexpr int AF = BM / RPB;             // activation blocks per stage
+    static constexpr int BF = (BN / 32) * S16;      // weight blocks per stage
+    static constexpr int FPW = (AF + BF) / 4;       // copy instructions per wave per stage
     static constexpr int STAGE = (AF + BF) * 1024;
-    static constexpr int NS = 3 * STAGE <= kLdsLimit ? 3 : 2;
+    static constexpr int NS = kLdsLimit / STAGE >= 4 ? 4 : kLdsLimit / STAGE;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 tiles");
     static_assert(AF % 4 == 0 && BF % 4 == 0, "LDS blocks must divide over 4 waves");
-    static_assert(2 * STAGE <= kLdsLimit, "two stages must fit in LDS");
+    static_assert(NS >= 2, "two stages must fit in LDS");
+    static_assert(FPW * (NS - 2) < 64, "vmcnt range");
 };
+
+// XOR swizzle of an activation row's 16-byte chunks in its LDS block, so
+// that the 32 rows of a fragment read spread over all banks.
+template <int CPR>
+__device__ __forceinline__ int swz(int row_in_block) {
+    return CPR == 8 ? (row_in_block & 7) : ((row_in_block >> 2) & 3);
+}
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c, int op) {
     if (op == OP_BF16)
@@ -95,15 +112,15 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c, int op) {
 }
 
 // One wave instruction: lane l copies the 16 bytes at base + off (base
-// wave-uniform, off a per-lane 32-bit byte offset) into LDS at lds + 16 l.
-// Issued as inline assembly so that the compiler's wait-count tracking does
-// not drain every outstanding copy before each LDS read; completion is
-// awaited explicitly (vmcnt) before the barrier that publishes a stage.
-__device__ __forceinline__ void dma16(const char *base, uint32_t off, void *lds) {
-    const unsigned l = (unsigned)(uintptr_t)(void __attribute__((address_space(3))) *)lds;
+// wave-uniform, off a per-lane 32-bit byte offset) into LDS at lds + 16 l
+// (lds wave-uniform).  Issued as inline assembly so that the compiler's
+// wait-count tracking does not drain every outstanding copy before each LDS
+// read; completion is awaited explicitly (vmcnt) before the barrier that
+// publishes a stage.
+__device__ __forceinline__ void dma16(const char *base, uint32_t off, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(off), "s"(base)
+                 : "s"(lds), "v"(off), "s"(base)
                  : "memory", "m0");
 }
 
@@ -120,11 +137,9 @@ template <int OP, int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_kernel(GemmGroup grp) {
     using C = G<OP, BM, BN, WM, WN>;
-    __shared__ __attribute__((aligned(1024))) char lds0[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) char lds1[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) char lds2[C::NS == 3 ? C::STAGE : 1024];
+    __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // scalar
     const int wm = wave / WN, wn = wave % WN;
 
     const int bid = blockIdx.x;
@@ -148,31 +163,37 @@ gemm_kernel(GemmGroup grp) {
     const int in_band = t - band * 8 * a.NB;
     const int64_t mb = first_m + in_band % bm_cnt, nb = in_band / bm_cnt;
     const int64_t m0 = mb * BM, n0 = nb * BN;
+    const int nst = a.KT64 * (64 / C::BK); // stages
 
     // Sources of this wave's LDS blocks: block f = wave + 4 j < AF holds
-    // activation rows 8f..8f+7 of the tile, the others weight fragments
-    // (32 columns x 16 k; f < AF exactly when j < AF / 4).  Each is a
-    // per-lane byte offset from a tile base that advances by a constant per
-    // stage; the offsets are recomputed at every issue (a few VALU ops)
-    // rather than held in registers.  Rows past M and columns past the
-    // shard are clamped to the last valid ones: in bounds, and those outputs
-    // are never stored.  Offsets stay below 2^32 because the activation row
-    // stride and K are below 2^22 elements (checked by the caller).
+    // activation rows RPB f .. RPB f + RPB - 1 of the tile, the others weight
+    // blocks g = f - AF (columns 32 (g / S16) of the tile, 16-k step g % S16;
+    // f < AF exactly when j < AF / 4).  Each is a per-lane byte offset from a
+    // tile base that advances by a constant per stage; the offsets are
+    // recomputed at every issue (a few VALU ops) rather than held in
+    // registers.  Rows past M and columns past the shard are clamped to the
+    // last valid ones: in bounds, and those outputs are never stored.
+    // Offsets stay below 2^32 because the activation row stride and K are
+    // below 2^22 elements (checked by the caller).
     const char *xbase = reinterpret_cast<const char *>(a.X + m0 * a.ldx);
     const int64_t t0 = n0 >> 4;
     const char *bbase = reinterpret_cast<const char *>(a.B + t0 * (int64_t)a.KT32 * 64);
-    const uint32_t chunk = 8 * ((lane & 7) ^ (lane >> 3));
-    const uint32_t aoff0 = ((uint32_t)(8 * wave + (lane >> 3)) * (uint32_t)a.ldx + chunk) * 2;
-    const uint32_t astep = 32 * (uint32_t)a.ldx * 2; // 32 rows
+    const int arow = lane / C::CPR; // row of this lane in its block
+    const uint32_t chunk = 8 * ((lane % C::CPR) ^ swz<C::CPR>(arow));
+    const uint32_t aoff0 = ((uint32_t)(C::RPB * wave + arow) * (uint32_t)a.ldx + chunk) * 2;
+    const uint32_t astep = 4 * C::RPB * (uint32_t)a.ldx * 2;
     const uint32_t alim = ((uint32_t)(M - 1 - m0) * (uint32_t)a.ldx + chunk) * 2;
-    const int kr = 2 * wave + (lane >> 5); // 8-k run of this wave's weight blocks
+    const int kr = 2 * (wave % C::S16) + (lane >> 5); // 8-k run of this wave's weight blocks
     const uint32_t boff0 = ((uint32_t)((kr >> 2) * 64 + (kr & 3) * 16 + (lane & 15))) * 16;
     const uint32_t tstep = (uint32_t)a.KT32 * 1024; // one 16-column tile
     const int tmax = (int)(a.Nt16 - 1 - t0);
-    const int th = (lane & 31) >> 4;
-    auto issue = [&](int64_t kt, char *buf) __attribute__((always_inline)) {
-        const char *xb = xbase + kt * (64 * 2);
-        const char *bb = bbase + kt * (2 * 64 * 16);
+    const int tfirst = 2 * (wave / C::S16) + ((lane & 31) >> 4);
+    constexpr int TPJ = 2 * (4 / C::S16); // 16-column tiles per weight block step
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(void __attribute__((address_space(3))) *)lds;
+    auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
+        const char *xb = xbase + kt * (C::BK * 2);
+        const char *bb = bbase + kt * (C::BK / 32 * 1024);
+        const uint32_t dst = lds0 + slot * C::STAGE + wave * 1024;
         uint32_t a0 = aoff0, b0 = boff0;
         asm volatile("" : "+v"(a0), "+v"(b0)); // keep the per-j offsets out of registers
 #pragma unroll
@@ -182,10 +203,10 @@ gemm_kernel(GemmGroup grp) {
                 const uint32_t o = a0 + (uint32_t)j * astep;
                 off = o < alim ? o : alim;
             } else {
-                const int tt = 2 * (j - C::AF / 4) + th;
+                const int tt = tfirst + TPJ * (j - C::AF / 4);
                 off = b0 + (uint32_t)(tt < tmax ? tt : tmax) * tstep;
             }
-            dma16(j < C::AF / 4 ? xb : bb, off, buf + (wave + 4 * j) * 1024);
+            dma16(j < C::AF / 4 ? xb : bb, off, dst + 4 * j * 1024);
         }
     };
 
@@ -199,35 +220,40 @@ gemm_kernel(GemmGroup grp) {
                 acc[i][j][r] = 0.f;
 
     u32x4 af[2][C::MT], bfr[2][C::NT];
-    auto stage = [&](int64_t kt, const char *cur, char *nxt) __attribute__((always_inline)) {
+    auto stage = [&](int kt, int slot) __attribute__((always_inline)) {
         // this wave's copies of stage kt are done once only the younger
-        // stages' copies may still be in flight
-        if (C::NS == 3 && kt + 1 < a.KT64)
+        // stages' copies (at most NS - 2) may still be in flight
+        const int younger = nst - 1 - kt < C::NS - 2 ? nst - 1 - kt : C::NS - 2;
+        if (C::NS >= 4 && younger >= 2)
+            wait_vmcnt<C::FPW * 2>();
+        else if (C::NS >= 3 && younger >= 1)
             wait_vmcnt<C::FPW>();
         else
             wait_vmcnt<0>();
         barrier();
-        if (kt + C::NS - 1 < a.KT64)
-            issue(kt + C::NS - 1, nxt);
-        const char *As = cur;
-        const char *Bs = cur + C::AF * 1024;
+        const char *As = lds + slot * C::STAGE;
+        const char *Bs = As + C::AF * 1024;
         auto rd = [&](int s, u32x4 (&x)[C::MT], u32x4 (&y)[C::NT]) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < C::MT; ++i) {
                 const int r = (wm * C::MT + i) * 32 + (lane & 31); // row in the block tile
-                const int kr = 2 * s + (lane >> 5);                // 8-k run in the stage
-                x[i] = *reinterpret_cast<const u32x4 *>(As + (r >> 3) * 1024 + (r & 7) * 128 +
-                                                        ((kr ^ (r & 7)) * 16));
+                const int k8 = 2 * s + (lane >> 5);                // 8-k run in the stage
+                const int rb = r % C::RPB;
+                x[i] = *reinterpret_cast<const u32x4 *>(As + (r / C::RPB) * 1024 + rb * (C::BK * 2) +
+                                                        ((k8 ^ swz<C::CPR>(rb)) * 16));
             }
 #pragma unroll
             for (int j = 0; j < C::NT; ++j)
                 y[j] = *reinterpret_cast<const u32x4 *>(
-                    Bs + (((wn * C::NT + j) * 4 + s) * 64 + lane) * 16);
+                    Bs + (((wn * C::NT + j) * C::S16 + s) * 64 + lane) * 16);
         };
         rd(0, af[0], bfr[0]);
+        // the copies of stage kt + NS - 1 go into the slot read in stage kt - 1
+        if (kt + C::NS - 1 < nst)
+            issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            if (s < 3)
+        for (int s = 0; s < C::S16; ++s) {
+            if (s + 1 < C::S16)
                 rd(s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
 #pragma unroll
             for (int i = 0; i < C::MT; ++i)
@@ -237,27 +263,12 @@ gemm_kernel(GemmGroup grp) {
         }
     };
 
-    issue(0, lds0);
-    if (C::NS == 3 && a.KT64 > 1)
-        issue(1, lds1);
-    int64_t kt = 0;
-    if constexpr (C::NS == 3) {
-        for (; kt + 3 <= a.KT64; kt += 3) {
-            stage(kt, lds0, lds2);
-            stage(kt + 1, lds1, lds0);
-            stage(kt + 2, lds2, lds1);
-        }
-        if (kt < a.KT64)
-            stage(kt, lds0, lds2);
-        if (kt + 1 < a.KT64)
-            stage(kt + 1, lds1, lds0);
-    } else {
-        for (; kt + 2 <= a.KT64; kt += 2) {
-            stage(kt, lds0, lds1);
-            stage(kt + 1, lds1, lds0);
-        }
-        if (kt < a.KT64)
-            stage(kt, lds0, lds1);
+    for (int k = 0; k < C::NS - 1 && k < nst; ++k)
+        issue(k, k);
+    int slot = 0;
+    for (int kt = 0; kt < nst; ++kt) {
+        stage(kt, slot);
+        slot = slot + 1 == C::NS ? 0 : slot + 1;
     }
 
     // ---- epilogue: acc reg r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32 ----
