@@ -26,12 +26,48 @@ import sys
 import time
 
 METRIC = "shard-linear TFLOP/s (prefill) and HBM GB/s (decode) + % roofline, 1 MI355X"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# HBM bytes of the prefill step's grouped call, from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE runs scaled by a plain copy's readings; valid only for the
+# kernel sources it was measured on (their SHA-256 is recorded with it)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pre27b.json")
+TRAFFIC_SOURCES = ("tensor_sharded_linear_plan_amd/csrc/prefill.hip",
+                   "tensor_sharded_linear_plan_amd/csrc/combine.hip",
+                   "tensor_sharded_linear_plan_amd/csrc/abi.cpp")
 PEAK_MFMA_F16 = 2500.0  # TFLOP/s, dense fp16/bf16 MFMA, MI355X
 PEAK_HBM = 8000.0       # GB/s, MI355X HBM3E
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def sources_digest():
+    """SHA-256 of the kernel sources' code: comments and blank space do not
+    count, so a documentation edit keeps a measurement valid."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """Bytes per grouped call from the committed counter runs, or None when
+    the kernels have changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_digest():
+        return None
+    return rec.get("bytes_per_call")
 
 
 def build_layer(layer, M, copies, tsl, torch, synth, configs):
@@ -294,6 +330,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB five times (the reference "
+                         "for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs every rank's shard on a single "
@@ -305,6 +344,15 @@ def main():
     from tensor_sharded_linear_plan_amd import configs, synth
     torch.cuda.set_device(0)
     log("device:", torch.cuda.get_device_name(0))
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: %d MiB x 5" % args.copy_probe)
+        del src, dst
 
     pre = prefill_bench(args, tsl, torch, synth, configs)
     dec = [] if args.no_decode else decode_bench(args, tsl, torch, synth, configs)
@@ -330,10 +378,11 @@ def main():
                    "parallelism": "tp4 in-process on 1 GPU"},
         "roofline": {"bound": "mfma", "achieved": round(pre["kernel_tflops"], 2),
                      "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                     "frac": round(pre["kernel_tflops"] / PEAK_MFMA_F16, 4), "traffic": None,
+                     "frac": round(pre["kernel_tflops"] / PEAK_MFMA_F16, 4),
+                     "traffic": measured_traffic(),
                      "kernel": "the step's shard_linear_group call: prep_kernel (4-bit -> "
-                               "f16 fragments), gemm_kernel (f16 MFMA, all 28 shard GEMMs), "
-                               "2 x sum_vec_kernel (rank sums)",
+                               "f16 weights, activations -> f16), gemm_kernel (f16 MFMA, all 28 "
+                               "shard GEMMs), sum_sets_kernel (the o and down rank sums)",
                      "avg_launch_us": round(pre["kernel_ms"] * 1e3, 2)},
         "cpu_baseline": cpu,
         "decode": {"workload": "dec7b: every rank of one tp=4 7B-class layer (hidden 3584, ffn "

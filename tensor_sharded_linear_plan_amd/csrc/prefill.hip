@@ -4,23 +4,23 @@
 // "Column Parallel" / "Row Parallel").  A dense contraction, so it runs on
 // the matrix cores with the full-rate 32x32x16 MFMA.
 //
-// Block tile BM x BN x 64 per stage, 4 waves arranged WM x WN, wave tile
-// (BM/WM) x (BN/WN) made of 32x32 accumulator tiles.  Operands move from
-// global memory straight into LDS with gfx950's global_load_lds_dwordx4
-// (a wave instruction fills 1 KB of LDS, lane l at byte 16 l), so staging
-// costs no VGPRs and no LDS write instructions:
-//   - activations: one instruction fetches 8 full 128-byte row segments
-//     (the access pattern the L2 serves fastest) into an 8-row block whose
-//     16-byte chunks are XOR-swizzled by row, which keeps the MFMA fragment
-//     reads bank-conflict free;
+// Block tile BM x BN, 4 waves arranged WM x WN, wave tile (BM/WM) x
+// (BN/WN) made of 32x32 accumulator tiles.  Operands move from global
+// memory straight into LDS with gfx950's global_load_lds_dwordx4 (a wave
+// instruction fills 1 KB of LDS, lane l at byte 16 l), so staging costs no
+// VGPRs and no LDS write instructions:
+//   - activations: one instruction fetches whole 128- or 64-byte row
+//     segments into an LDS block whose 16-byte chunks are XOR-swizzled by
+//     row, which keeps the MFMA fragment reads bank-conflict free;
 //   - weights: the packed layout already holds 16 columns x 8 k per
 //     16-byte chunk, so a 32-column x 16-k MFMA fragment is two 512-byte
 //     runs.
-// Stages rotate through 3 LDS buffers (2 when 3 do not fit in 160 KB): the
-// loads of stage k + 2 are issued right after the barrier that opens stage
-// k, and each wave waits only for its own loads of stage k before that
-// barrier.  Inside a stage the fragments of the next 16-k step are read
-// while the MFMAs of the current one run.
+// A stage covers 64 k (32 k when three 64-k stages would not fit in 160 KB)
+// and stages rotate through up to 4 LDS slots: the copies of stage k + S - 1
+// (S slots) are issued right after the barrier that opens stage k and the
+// first fragment reads, and each wave waits only for its own copies of
+// stage k before that barrier.  Inside a stage the fragments of the next
+// 16-k step are read while the MFMAs of the current one run.
 //
 // Operands: bf16 x bf16, or f16 x f16 for 4-bit weights.  For the latter a
 // prep kernel first expands the weights to binary16 fragments (w = s q + b
