@@ -157,13 +157,14 @@ tsl_status plan_linear(int64_t K, int64_t N, int32_t tp_size, int32_t strategy,
  *             sits in tile (n/16, k/16), lane ((k%16)/4)*16 + n%16, slot k%4.
  *   TSL_BF16  [Nt][ceil(Ks/64)*2][64][8] bf16: tile (n/16, k/32),
  *             lane ((k%32)/8)*16 + n%16, slot k%8.
- *   TSL_Q4G64 codes [Nt][ceil(Ks/128)][64][4] u32, then at the next
- *             256-byte boundary scale/bias pairs [Nt][ceil(Ks/128)*2][16]
- *             u32 (bf16 scale in the low half, bf16 bias in the high half).
- *             Code (k, n): block (n/16, k/128); with kk = k%128, word
+ *   TSL_Q4G64 records [Nt][ceil(Ks/128)] of 1152 bytes (total rounded up
+ *             to 256): codes [64][4] u32, then scale/bias pairs [16][2] u32
+ *             (bf16 scale in the low half, bf16 bias in the high half).
+ *             Code (k, n): record (n/16, k/128); with kk = k%128, word
  *             kk/32 of lane ((kk%32)/8)*16 + n%16; with j = kk%8 the nibble
  *             at bit 4*(j/2) for even j and 16 + 4*(j/2) for odd j.
- *             Pair (g, n) for group g = k/64: entry [n/16][g][n%16].
+ *             Pair (g, n) for group g = k/64: record (n/16, g/2), entry
+ *             [n%16][g%2] (the two groups of a 128-k block side by side).
  * Errors: TSL_ERR_INVALID_ARG, TSL_ERR_GROUP_ALIGN (Q4 with k_len % 64).
  */
 tsl_status pack_shard_size(const tsl_shard *shard, tsl_dtype wdtype, size_t *bytes);

@@ -85,9 +85,7 @@ tsl_status geometry(const tsl_shard &s, tsl_dtype wdtype, PackGeom *g) {
             return TSL_ERR_GROUP_ALIGN;
         r.KT = (r.Ks + 127) / 128;
         r.Kpad = r.KT * 128;
-        r.codes_bytes = round_up((size_t)r.Nt * (size_t)r.KT * 64 * 16, 256);
-        r.sb_bytes = round_up((size_t)r.Nt * (size_t)r.KT * 2 * 16 * 4, 256);
-        r.total_bytes = r.codes_bytes + r.sb_bytes;
+        r.total_bytes = round_up((size_t)r.Nt * (size_t)r.KT * kQ4Record, 256);
         break;
     }
     *g = r;

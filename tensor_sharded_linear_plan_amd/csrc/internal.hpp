@@ -19,12 +19,15 @@ struct PackGeom {
     int64_t Kpad = 0;       // Ks rounded up to the k granularity of the layout
     // F32: 16-k tiles; BF16: 32-k tiles; Q4G64: 128-k blocks
     int64_t KT = 0;
-    size_t codes_bytes = 0; // Q4G64: bytes of the code region (256-byte rounded)
-    size_t sb_bytes = 0;    // Q4G64: bytes of the scale/bias region
     size_t total_bytes = 0;
 };
 
 tsl_status geometry(const tsl_shard &s, tsl_dtype wdtype, PackGeom *g);
+
+// Q4G64 packed record of 16 columns x 128 k: 1 KB of codes, then the 128
+// bytes of (scale, bias) pairs of its two 64-k groups.
+constexpr int kQ4Record = 1152;
+constexpr int kQ4PairsAt = 1024;
 
 // ---- pack.hip ----
 hipError_t launch_pack_dense(const PackGeom &g, tsl_dtype wdtype, const void *W, int64_t stride_k,

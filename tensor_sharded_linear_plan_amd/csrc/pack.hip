@@ -44,7 +44,7 @@ __global__ void __launch_bounds__(256) pack_q4_codes_kernel(const uint8_t *__res
                                                             int64_t k_off, int64_t n_off,
                                                             int64_t Ks, int64_t Ns, int64_t KB,
                                                             int64_t chunks,
-                                                            uint32_t *__restrict__ out) {
+                                                            char *__restrict__ out) {
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (c >= chunks)
         return;
@@ -69,30 +69,34 @@ __global__ void __launch_bounds__(256) pack_q4_codes_kernel(const uint8_t *__res
         words[t] = w;
     }
     u32x4 v = {words[0], words[1], words[2], words[3]};
-    *reinterpret_cast<u32x4 *>(out + c * 4) = v;
+    *reinterpret_cast<u32x4 *>(out + tile * kQ4Record + lane * 16) = v;
 }
 
-// Q4 scale/bias pairs: entry (nt, g, i) for column nt*16 + i and group g.
+// Q4 scale/bias pairs: entry (nt, blk, i, h) for column nt*16 + i and group
+// g = 2 blk + h (the two groups of a 128-k block side by side), stored after
+// the codes of record (nt, blk).
 __global__ void __launch_bounds__(256) pack_q4_sb_kernel(const uint16_t *__restrict__ scales,
                                                          const uint16_t *__restrict__ biases,
                                                          int64_t sb_stride_g, int64_t sb_stride_n,
                                                          int64_t g_off, int64_t n_off,
                                                          int64_t Gs, int64_t Ns, int64_t GP,
                                                          int64_t entries,
-                                                         uint32_t *__restrict__ out) {
+                                                         char *__restrict__ out) {
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= entries)
         return;
-    const int i = (int)(e & 15);
-    const int64_t t = e >> 4;
-    const int64_t nt = t / GP, g = t % GP;
+    const int h = (int)(e & 1);
+    const int i = (int)((e >> 1) & 15);
+    const int64_t t = e >> 5;
+    const int64_t KB = GP / 2;
+    const int64_t nt = t / KB, g = 2 * (t % KB) + h;
     const int64_t n = nt * 16 + i;
     uint32_t v = 0;
     if (n < Ns && g < Gs) {
         const int64_t at = (g_off + g) * sb_stride_g + (n_off + n) * sb_stride_n;
         v = (uint32_t)scales[at] | ((uint32_t)biases[at] << 16);
     }
-    out[e] = v;
+    *reinterpret_cast<uint32_t *>(out + t * kQ4Record + kQ4PairsAt + (e & 31) * 4) = v;
 }
 
 inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
@@ -125,11 +129,9 @@ hipError_t launch_pack_q4(const PackGeom &g, const uint8_t *codes, int64_t strid
     const int64_t chunks = g.Nt * g.KT * 64;
     if (chunks == 0)
         return hipSuccess;
-    uint32_t *code_out = static_cast<uint32_t *>(packed);
-    uint32_t *sb_out = reinterpret_cast<uint32_t *>(static_cast<char *>(packed) + g.codes_bytes);
+    char *out = static_cast<char *>(packed);
     hipLaunchKernelGGL(pack_q4_codes_kernel, dim3(blocks_for(chunks, 256)), dim3(256), 0, stream,
-                       codes, stride_k, stride_n, k_off, n_off, g.Ks, g.Ns, g.KT, chunks,
-                       code_out);
+                       codes, stride_k, stride_n, k_off, n_off, g.Ks, g.Ns, g.KT, chunks, out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -137,7 +139,7 @@ hipError_t launch_pack_q4(const PackGeom &g, const uint8_t *codes, int64_t strid
     const int64_t entries = g.Nt * GP * 16;
     hipLaunchKernelGGL(pack_q4_sb_kernel, dim3(blocks_for(entries, 256)), dim3(256), 0, stream,
                        scales, biases, sb_stride_g, sb_stride_n, k_off / 64, n_off, g.Ks / 64,
-                       g.Ns, GP, entries, sb_out);
+                       g.Ns, GP, entries, out);
     return hipGetLastError();
 }
 

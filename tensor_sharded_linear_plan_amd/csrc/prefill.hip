@@ -309,9 +309,8 @@ gemm_kernel(GemmGroup grp) {
 
 // ---- prep: 4-bit weights -> binary16 fragments, ragged-K activations -> padded copy ----
 struct PrepItem {
-    // weights (4-bit items): codes and scale/bias pairs -> fragments
-    const u32x4 *codes;
-    const uint32_t *sb;
+    // weights (4-bit items): packed records (codes, scale/bias pairs) -> fragments
+    const char *q4;
     u32x4 *w_out;
     // activations (K not a multiple of 64): rows of ldx_in -> rows of Kpad
     const uint16_t *x_in;
@@ -319,7 +318,7 @@ struct PrepItem {
     int64_t ldx_in;
     int64_t w_chunks;  // 16-byte code chunks
     int64_t x_units;   // 8-element output units (M * Kpad / 8)
-    int32_t KB, GP, Gs;
+    int32_t KB, Gs;
     int32_t Ks, Kpad;
     int32_t w_blocks;  // workgroups [start, start + w_blocks) do weights
     int32_t start, pad_;
@@ -352,13 +351,15 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepGroup grp) {
         const int lane = (int)(c & 63);
         const int64_t t = c >> 6;
         const int64_t nt = t / p.KB, blk = t % p.KB;
-        const u32x4 w = p.codes[c];
+        const char *rec = p.q4 + t * kQ4Record; // record (nt, blk)
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(rec + lane * 16);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int64_t g = 2 * blk + h;
             if (g >= p.Gs)
                 break; // pad group of a half-filled last block: never read
-            const uint32_t sbp = p.sb[(nt * p.GP + g) * 16 + (lane & 15)];
+            const uint32_t sbp =
+                *reinterpret_cast<const uint32_t *>(rec + kQ4PairsAt + ((lane & 15) * 2 + h) * 4);
             const float s = bf16_lo(sbp);
             const float cb = __builtin_fmaf(-1024.f, s, bf16_hi(sbp));
 #pragma unroll
@@ -538,9 +539,7 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
             if (!q4 && !xcopy)
                 continue;
             PrepItem &a = pg.it[pg.n++];
-            a.codes = static_cast<const u32x4 *>(L.packed);
-            a.sb = reinterpret_cast<const uint32_t *>(static_cast<const char *>(L.packed) +
-                                                      g.codes_bytes);
+            a.q4 = static_cast<const char *>(L.packed);
             a.w_out = reinterpret_cast<u32x4 *>(ws + p.w_off[c0 + i]);
             a.x_in = static_cast<const uint16_t *>(L.X);
             a.x_out = reinterpret_cast<uint16_t *>(ws + p.x_off[c0 + i]);
@@ -549,7 +548,6 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
             a.Kpad = (int32_t)kpad64(g.Ks);
             a.x_units = xcopy ? M * (a.Kpad / 8) : 0;
             a.KB = (int32_t)g.KT;
-            a.GP = (int32_t)(g.KT * 2);
             a.Gs = (int32_t)(g.Ks / 64);
             a.Ks = (int32_t)g.Ks;
             a.w_blocks = (int32_t)((a.w_chunks + 255) / 256);

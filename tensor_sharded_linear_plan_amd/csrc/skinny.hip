@@ -36,15 +36,13 @@ namespace {
 enum { W_F32 = 0, W_BF16 = 1, W_Q4 = 2 };
 
 struct SkinnyItem {
-    const void *B;       // packed weights (codes for Q4)
-    const uint32_t *SB;  // Q4 scale/bias pairs
+    const void *B;       // packed weights
     const void *X;
     void *Y;
     float *P;            // workspace partials [ks][M][Ns] (ks > 1)
     int64_t ldx, ldy;
     int32_t Ks, Ns, Nt;
     int32_t KC;          // chunks along k (16, 32 or 128 k each)
-    int32_t GP;          // Q4: groups per column in the packed pairs
     int32_t ks, n_groups;
     int32_t start;       // first workgroup of this item
     int32_t accumulate, y_bf16;
@@ -256,22 +254,22 @@ __global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
     const int b0 = (int)((int64_t)ksi * nblk / a.ks);
     const int b1 = (int)((int64_t)(ksi + 1) * nblk / a.ks);
 
-    // this wave's tiles (clamped in range; tiles past the shard are not stored)
-    const u32x4 *B = static_cast<const u32x4 *>(a.B);
-    const u32x4 *wsrc[NTW];
-    const uint32_t *ssrc[NTW];
+    // this wave's tiles (clamped in range; tiles past the shard are not
+    // stored): a chunk is one 16-byte load per lane, and for 4-bit weights
+    // the (scale, bias) pairs of its two groups follow it in the same record
+    constexpr int64_t CS = WT == W_Q4 ? kQ4Record : 1024; // bytes per chunk
+    const char *wsrc[NTW];
     int64_t ntile[NTW];
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
         ntile[j] = ((int64_t)tg * 4 + wave) * NTW + j;
         const int64_t nt = ntile[j] < a.Nt - 1 ? ntile[j] : a.Nt - 1;
-        wsrc[j] = B + nt * (int64_t)a.KC * 64 + lane;
-        ssrc[j] = WT == W_Q4 ? a.SB + nt * (int64_t)a.GP * 16 + (lane & 15) : nullptr;
+        wsrc[j] = static_cast<const char *>(a.B) + nt * (int64_t)a.KC * CS;
     }
 
     // weight ring: [slot][tile][load], plus scale/bias pairs for 4-bit
     u32x4 cw[3][NTW][S::LPB];
-    uint32_t sbw[3][NTW][S::LPB][2];
+    u32x2 sbw[3][NTW][S::LPB];
     auto load_w = [&](auto SLOT, int b) __attribute__((always_inline)) {
         constexpr int s = decltype(SLOT)::value;
 #pragma unroll
@@ -280,11 +278,11 @@ __global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
             for (int l = 0; l < S::LPB; ++l) {
                 const int c = b * S::LPB + l; // chunk (4-bit) or 32-k tile (bf16)
                 const int cc = c < a.KC ? c : a.KC - 1;
-                cw[s][j][l] = wsrc[j][(int64_t)cc * 64];
-                if constexpr (WT == W_Q4) {
-                    sbw[s][j][l][0] = ssrc[j][(int64_t)(2 * cc) * 16];
-                    sbw[s][j][l][1] = ssrc[j][(int64_t)(2 * cc + 1) * 16];
-                }
+                const char *rec = wsrc[j] + (int64_t)cc * CS;
+                cw[s][j][l] = *reinterpret_cast<const u32x4 *>(rec + lane * 16);
+                if constexpr (WT == W_Q4) // both groups of the chunk in one load
+                    sbw[s][j][l] =
+                        *reinterpret_cast<const u32x2 *>(rec + kQ4PairsAt + (lane & 15) * 8);
             }
     };
 
@@ -673,9 +671,6 @@ hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, ts
             const LinearItem &L = items[c0 + i];
             SkinnyItem &a = grp.it[i];
             a.B = L.packed;
-            a.SB = wdtype == TSL_Q4G64 ? reinterpret_cast<const uint32_t *>(
-                                             static_cast<const char *>(L.packed) + L.g.codes_bytes)
-                                       : nullptr;
             a.X = L.X;
             a.Y = L.Y;
             a.P = reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ws_off[c0 + i]);
@@ -685,7 +680,6 @@ hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, ts
             a.Ns = (int32_t)L.g.Ns;
             a.Nt = (int32_t)L.g.Nt;
             a.KC = (int32_t)L.g.KT;
-            a.GP = (int32_t)(L.g.KT * 2);
             a.ks = p.ks[c0 + i];
             a.n_groups = (int32_t)p.n_groups[c0 + i];
             a.accumulate = L.accumulate;

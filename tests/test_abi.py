@@ -140,7 +140,7 @@ def test_pack_shard_size_geometry(tsl_lib):
     assert tsl_lib.pack_shard_size(s, tsl_lib.F32) == 64 * 64 * 64 * 16
     assert tsl_lib.pack_shard_size(s, tsl_lib.BF16) == 64 * 32 * 64 * 16
     # Q4: codes 64 tiles x 8 blocks x 1 KiB, pairs 64 x 16 groups x 16 x 4 bytes
-    assert tsl_lib.pack_shard_size(s, tsl_lib.Q4G64) == 64 * 8 * 1024 + 64 * 16 * 64
+    assert tsl_lib.pack_shard_size(s, tsl_lib.Q4G64) == 64 * 8 * 1152  # records of codes + pairs
     # ragged: 100 x 30 bf16 -> 2 tiles of 16 columns, k padded to 128 (4 tiles of 32)
     r = tsl_lib.plan_linear(100, 30, 1, tsl_lib.COLUMN)[0]
     assert tsl_lib.pack_shard_size(r, tsl_lib.BF16) == 2 * 4 * 1024

@@ -33,8 +33,9 @@ def decode_q4(buf, Ks, Ns):
     Nt = (Ns + 15) // 16
     KB = (Ks + 127) // 128
     raw = buf.cpu().numpy()
-    code_bytes = -(-Nt * KB * 1024 // 256) * 256
-    words = raw[:Nt * KB * 1024].view(np.uint32).reshape(Nt, KB, 64, 4)
+    # records of 1152 bytes: codes [64][4] u32, then pairs [16][2] u32
+    rec = raw[:Nt * KB * 1152].reshape(Nt, KB, 1152)
+    words = np.ascontiguousarray(rec[:, :, :1024]).view(np.uint32).reshape(Nt, KB, 64, 4)
     codes = np.zeros((KB * 128, Nt * 16), dtype=np.uint8)
     for lane in range(64):
         n = np.arange(Nt)[:, None] * 16 + lane % 16
@@ -44,12 +45,14 @@ def decode_q4(buf, Ks, Ns):
                 shift = 16 + 4 * (j // 2) if j % 2 else 4 * (j // 2)
                 k = np.arange(KB)[None, :] * 128 + t * 32 + (lane // 16) * 8 + j
                 codes[k, n] = (w >> shift) & 0xF
-    pairs = raw[code_bytes:code_bytes + Nt * KB * 2 * 16 * 4].view(np.uint32).reshape(Nt, KB * 2, 16)
+    # the two groups of a 128-k block side by side per column
+    pairs = np.ascontiguousarray(rec[:, :, 1024:]).view(np.uint32).reshape(Nt, KB, 16, 2)
     sc = np.zeros((KB * 2, Nt * 16), dtype=np.uint16)
     bi = np.zeros_like(sc)
     for i in range(16):
-        sc[:, np.arange(Nt) * 16 + i] = (pairs[:, :, i] & 0xFFFF).T
-        bi[:, np.arange(Nt) * 16 + i] = (pairs[:, :, i] >> 16).T
+        for h in range(2):
+            sc[h::2, np.arange(Nt) * 16 + i] = (pairs[:, :, i, h] & 0xFFFF).T
+            bi[h::2, np.arange(Nt) * 16 + i] = (pairs[:, :, i, h] >> 16).T
     return codes, sc, bi
 
 
