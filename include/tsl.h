@@ -325,6 +325,40 @@ tsl_status combine_partials(tsl_combine mode, int32_t n_parts, const void *const
                             tsl_dtype pdtype, int64_t M, int64_t n_each, int64_t ld_part,
                             tsl_dtype ydtype, void *Y, int64_t ldy, void *stream);
 
+/* The collectives that join rank outputs (see combine_to_ranks). */
+typedef enum tsl_collective {
+    TSL_ALL_REDUCE = 0,     /* every rank: the full ordered sum            */
+    TSL_REDUCE_SCATTER = 1, /* rank r: its block of rows of that sum       */
+    TSL_ALL_GATHER = 2      /* every rank: the parts concatenated along N  */
+} tsl_collective;
+
+/*
+ * combine_to_ranks -- every rank's result of a collective over rank outputs
+ * that all live on this one GPU ([mlxcel] "Communication patterns": the
+ * ring all-reduce = reduce-scatter then all-gather, after row-parallel
+ * layers; all-gather of column shards; reduce-scatter when the next op
+ * needs only a shard of the reduced output).
+ *   parts: HOST array of n DEVICE pointers; part r is [M][n_each], row
+ *          stride ld_part, type pdtype.
+ *   outs:  HOST array of n DEVICE pointers; outs[r] is rank r's result,
+ *          row stride ldo, type odtype.
+ *   ALL_REDUCE:     outs[r][m][j] = (((P_0 + P_1) + P_2) + ...)[m][j] for
+ *                   every r (binary32 adds in rank order, rounded once to
+ *                   odtype); pdtype F32, odtype F32 or BF16.
+ *   REDUCE_SCATTER: the same sum, rank r keeping rows lo_r <= m < hi_r with
+ *                   lo_r = floor(r M / n), at outs[r][m - lo_r] (the ring's
+ *                   n chunks in memory order, as whole rows).
+ *   ALL_GATHER:     outs[r][m][q n_each + j] = P_q[m][j] for every r;
+ *                   pdtype == odtype (a copy), F32 or BF16.
+ * No output may share an element with a part or another output
+ * (TSL_ERR_INVALID_ARG).  1 <= n <= 64.  M == 0 or n_each == 0 enqueues
+ * nothing.  Errors: TSL_ERR_INVALID_ARG, TSL_ERR_UNSUPPORTED,
+ * TSL_ERR_MISALIGNED (pointers aligned to their element size), TSL_ERR_HIP.
+ */
+tsl_status combine_to_ranks(tsl_collective op, int32_t n, const void *const *parts,
+                            tsl_dtype pdtype, int64_t M, int64_t n_each, int64_t ld_part,
+                            tsl_dtype odtype, void *const *outs, int64_t ldo, void *stream);
+
 /* A static, human-readable description of a status code. */
 const char *tsl_status_string(tsl_status status);
 

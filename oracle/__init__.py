@@ -228,3 +228,38 @@ def sum_f32_seq(parts):
     Y = np.empty(P.shape[1:], dtype=np.float32)
     lib().oracle_sum_f32_seq(pp, R, Y.size, Y.ctypes.data_as(ctypes.c_void_p))
     return Y
+
+
+# ---- the collectives' results, every rank's buffer (mlxcel manual, "Tensor
+# parallelism", "Communication patterns": all-reduce = reduce-scatter then
+# all-gather; all-gather: every rank ends with the full tensor; reduce-
+# scatter: every rank ends with 1/N of the reduced tensor) ----
+
+def rank_rows(M, n_ranks, r):
+    """Rows [lo, hi) of an [M][n] tensor held by rank r after a
+    reduce-scatter: the ring splits the tensor into n_ranks chunks in memory
+    order, read here as balanced blocks of whole rows."""
+    return (r * M) // n_ranks, ((r + 1) * M) // n_ranks
+
+
+def all_reduce(parts, n_ranks, sum_fn=None):
+    """Every rank's buffer after an all-reduce: the full sum."""
+    total = (sum_fn or combine_sum)(parts)
+    return [total.copy() for _ in range(n_ranks)]
+
+
+def reduce_scatter(parts, n_ranks, sum_fn=None):
+    """Every rank's buffer after a reduce-scatter: its row block of the sum."""
+    total = (sum_fn or combine_sum)(parts)
+    M = total.shape[0]
+    out = []
+    for r in range(n_ranks):
+        lo, hi = rank_rows(M, n_ranks, r)
+        out.append(total[lo:hi].copy())
+    return out
+
+
+def all_gather(parts, n_ranks):
+    """Every rank's buffer after an all-gather: the concatenated tensor."""
+    full = combine_concat(parts)
+    return [full.copy() for _ in range(n_ranks)]

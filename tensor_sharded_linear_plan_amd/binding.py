@@ -44,6 +44,7 @@ Q, K, V, O, GATE, UP, DOWN = range(7)
 NPROJ = 7
 LINEAR = 7
 F32, BF16, Q4G64 = 0, 1, 2
+ALL_REDUCE, REDUCE_SCATTER, ALL_GATHER = 0, 1, 2
 MAX_PARTS = 64
 
 
@@ -107,18 +108,20 @@ _lib.shard_linear_group.argtypes = [_i32, _P_ITEM, ctypes.c_int, ctypes.c_int, _
                                     _vp]
 _lib.combine_partials.argtypes = [ctypes.c_int, _i32, ctypes.POINTER(_vp), ctypes.c_int, _i64,
                                   _i64, _i64, ctypes.c_int, _vp, _i64, _vp]
+_lib.combine_to_ranks.argtypes = [ctypes.c_int, _i32, ctypes.POINTER(_vp), ctypes.c_int, _i64,
+                                  _i64, _i64, ctypes.c_int, ctypes.POINTER(_vp), _i64, _vp]
 _lib.tsl_status_string.argtypes = [ctypes.c_int]
 _lib.tsl_status_string.restype = ctypes.c_char_p
 _lib.tsl_last_hip_error_string.argtypes = []
 _lib.tsl_last_hip_error_string.restype = ctypes.c_char_p
 for _f in ("plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
            "shard_linear_workspace_size", "shard_linear", "shard_linear_group_workspace_size",
-           "shard_linear_group", "combine_partials"):
+           "shard_linear_group", "combine_partials", "combine_to_ranks"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
            "shard_linear_workspace_size", "shard_linear", "shard_linear_group_workspace_size",
-           "shard_linear_group", "combine_partials", "tsl_status_string",
+           "shard_linear_group", "combine_partials", "combine_to_ranks", "tsl_status_string",
            "tsl_last_hip_error_string")
 
 
@@ -234,3 +237,13 @@ def combine_partials(mode, parts, pdtype, M, n_each, ld_part, ydtype, Y, ldy, st
     arr = (_vp * max(len(parts), 1))(*[_ptr(p) for p in parts])
     _check(_lib.combine_partials(mode, len(parts), arr, pdtype, M, n_each, ld_part, ydtype,
                                  _ptr(Y), ldy, _stream(stream)), "combine_partials")
+
+
+def combine_to_ranks(op, parts, pdtype, M, n_each, ld_part, odtype, outs, ldo, stream=None):
+    n = len(parts)
+    parr = (_vp * max(n, 1))(*[_ptr(p) for p in parts])
+    oarr = (_vp * max(len(outs), 1))(*[_ptr(o) for o in outs])
+    if len(outs) != n:
+        raise ValueError("combine_to_ranks: one output per part")
+    _check(_lib.combine_to_ranks(op, n, parr, pdtype, M, n_each, ld_part, odtype, oarr, ldo,
+                                 _stream(stream)), "combine_to_ranks")

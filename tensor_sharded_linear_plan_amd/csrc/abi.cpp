@@ -278,25 +278,26 @@ size_t split_sets(std::vector<LinearItem> *items, int64_t M, char *ws) {
 size_t span(int64_t M, int64_t n, int64_t ld, size_t elem);
 bool overlaps(const void *a, size_t na, const void *b, size_t nb);
 
-// Whether two [M][w] row-strided matrices share a byte (M > 0).  With equal
-// strides this is exact -- column blocks of one output matrix written by
-// different items do not overlap -- otherwise it compares address ranges.
-bool matrices_overlap(const void *pa, int64_t wa, int64_t lda, size_t ea, const void *pb,
-                      int64_t wb, int64_t ldb, size_t eb, int64_t M) {
+// Whether an [Ma][wa] and an [Mb][wb] row-strided matrix share a byte
+// (Ma, Mb > 0).  With equal strides this is exact -- column blocks or row
+// blocks of one matrix held by different owners do not overlap -- otherwise
+// it compares address ranges.
+bool matrices_overlap(const void *pa, int64_t Ma, int64_t wa, int64_t lda, size_t ea,
+                      const void *pb, int64_t Mb, int64_t wb, int64_t ldb, size_t eb) {
     const int64_t L = lda * (int64_t)ea;
     const int64_t Wa = wa * (int64_t)ea, Wb = wb * (int64_t)eb;
     if (L != ldb * (int64_t)eb || Wa > L || Wb > L)
-        return overlaps(pa, span(M, wa, lda, ea), pb, span(M, wb, ldb, eb));
+        return overlaps(pa, span(Ma, wa, lda, ea), pb, span(Mb, wb, ldb, eb));
     // b - a = q L + rem, 0 <= rem < L: rows r1 - r2 = q need rem < Wa, rows
-    // r1 - r2 = q + 1 need L - rem < Wb, each with |r1 - r2| < M
+    // r1 - r2 = q + 1 need L - rem < Wb, each with -Mb < r1 - r2 < Ma
     const int64_t d = (int64_t)(reinterpret_cast<uintptr_t>(pb) - reinterpret_cast<uintptr_t>(pa));
     int64_t q = d / L, rem = d % L;
     if (rem < 0) {
         rem += L;
         q -= 1;
     }
-    const bool same_row = (q > -M && q < M) && rem < Wa;
-    const bool next_row = (q + 1 > -M && q + 1 < M) && L - rem < Wb;
+    const bool same_row = (q > -Mb && q < Ma) && rem < Wa;
+    const bool next_row = (q + 1 > -Mb && q + 1 < Ma) && L - rem < Wb;
     return same_row || next_row;
 }
 
@@ -433,10 +434,10 @@ tsl_status gather(int32_t n_items, const tsl_linear_item *items, tsl_dtype wdtyp
         for (int32_t j = 0; j < n_items; ++j) {
             const LinearItem &b = (*out)[j];
             const size_t eb = b.ydtype == TSL_F32 ? 4 : 2;
-            if (matrices_overlap(a.Y, a.g.Ns, a.ldy, ea, b.X, b.g.Ks, b.ldx, xe, M))
+            if (matrices_overlap(a.Y, M, a.g.Ns, a.ldy, ea, b.X, M, b.g.Ks, b.ldx, xe))
                 return TSL_ERR_INVALID_ARG;
             if (j > i && b.Y &&
-                matrices_overlap(a.Y, a.g.Ns, a.ldy, ea, b.Y, b.g.Ns, b.ldy, eb, M))
+                matrices_overlap(a.Y, M, a.g.Ns, a.ldy, ea, b.Y, M, b.g.Ns, b.ldy, eb))
                 return TSL_ERR_INVALID_ARG;
         }
     }
@@ -586,6 +587,56 @@ extern "C" tsl_status combine_partials(tsl_combine mode, int32_t n_parts, const 
         return from_hip(launch_combine_concat(n_parts, parts, ea, M, n_each, ld_part, Y, ldy, s));
     }
     return TSL_ERR_INVALID_ARG;
+}
+
+extern "C" tsl_status combine_to_ranks(tsl_collective op, int32_t n, const void *const *parts,
+                                       tsl_dtype pdtype, int64_t M, int64_t n_each,
+                                       int64_t ld_part, tsl_dtype odtype, void *const *outs,
+                                       int64_t ldo, void *stream) {
+    if (!parts || !outs || n < 1 || n > kMaxParts || M < 0 || n_each < 0 || ld_part < n_each)
+        return TSL_ERR_INVALID_ARG;
+    if (op != TSL_ALL_REDUCE && op != TSL_REDUCE_SCATTER && op != TSL_ALL_GATHER)
+        return TSL_ERR_INVALID_ARG;
+    if ((pdtype != TSL_F32 && pdtype != TSL_BF16) || (odtype != TSL_F32 && odtype != TSL_BF16))
+        return TSL_ERR_INVALID_ARG;
+    for (int r = 0; r < n; ++r)
+        if (!parts[r] || !outs[r])
+            return TSL_ERR_INVALID_ARG;
+    const bool gather = op == TSL_ALL_GATHER;
+    if (gather ? pdtype != odtype : pdtype != TSL_F32)
+        return TSL_ERR_UNSUPPORTED;
+    const int64_t width = gather ? n_each * n : n_each; // columns of each output
+    if (ldo < width)
+        return TSL_ERR_INVALID_ARG;
+    const size_t pe = pdtype == TSL_F32 ? 4 : 2, oe = odtype == TSL_F32 ? 4 : 2;
+    for (int r = 0; r < n; ++r)
+        if (!aligned(parts[r], pe) || !aligned(outs[r], oe))
+            return TSL_ERR_MISALIGNED;
+    if (M == 0 || n_each == 0)
+        return TSL_OK;
+    // rows of rank r's output
+    auto rows = [&](int r) {
+        return op == TSL_REDUCE_SCATTER ? ((int64_t)(r + 1) * M) / n - ((int64_t)r * M) / n : M;
+    };
+    for (int r = 0; r < n; ++r) {
+        if (rows(r) == 0)
+            continue;
+        for (int q = 0; q < n; ++q) {
+            if (matrices_overlap(outs[r], rows(r), width, ldo, oe, parts[q], M, n_each, ld_part,
+                                 pe))
+                return TSL_ERR_INVALID_ARG;
+            if (q > r && rows(q) > 0 &&
+                matrices_overlap(outs[r], rows(r), width, ldo, oe, outs[q], rows(q), width, ldo,
+                                 oe))
+                return TSL_ERR_INVALID_ARG;
+        }
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gather)
+        return from_hip(launch_gather_to_ranks(n, parts, pe, M, n_each, ld_part, outs, ldo, s));
+    return from_hip(launch_reduce_to_ranks(n, reinterpret_cast<const float *const *>(parts), M,
+                                           n_each, ld_part, op == TSL_REDUCE_SCATTER, odtype, outs,
+                                           ldo, s));
 }
 
 extern "C" const char *tsl_last_hip_error_string(void) { return hipGetErrorString(g_last_hip); }

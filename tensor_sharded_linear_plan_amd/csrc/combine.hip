@@ -162,6 +162,72 @@ __global__ void __launch_bounds__(256) sum_sets_kernel(SumSets g, int64_t M) {
     }
 }
 
+// ---- every rank's result of a collective ----
+struct OutPtrs {
+    void *p[kMaxParts];
+};
+
+// First row of rank r's block of an [M][n] tensor split over n ranks.
+__device__ __forceinline__ int64_t block_lo(int r, int64_t M, int n) {
+    return ((int64_t)r * M) / n;
+}
+
+// Ordered binary32 sum of the parts at (m, j..j+V-1), written to every
+// output (all-reduce) or to the owner of row m (reduce-scatter).
+template <typename TY, int V>
+__global__ void __launch_bounds__(256) reduce_ranks_kernel(PartPtrs parts, int n, int64_t M,
+                                                           int64_t n_each, int64_t ld_part,
+                                                           OutPtrs outs, int64_t ldo,
+                                                           int scatter) {
+    const int64_t j = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
+    if (j >= n_each)
+        return;
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+        const int64_t off = m * ld_part + j;
+        float acc[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            acc[e] = static_cast<const float *>(parts.p[0])[off + e];
+        for (int r = 1; r < n; ++r)
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                acc[e] = acc[e] + static_cast<const float *>(parts.p[r])[off + e];
+        int r0 = 0, r1 = n;
+        if (scatter) { // the rank whose block holds row m
+            int r = (int)((m * n) / M);
+            while (r + 1 < n && m >= block_lo(r + 1, M, n))
+                ++r;
+            while (r > 0 && m < block_lo(r, M, n))
+                --r;
+            r0 = r;
+            r1 = r + 1;
+        }
+        for (int r = r0; r < r1; ++r) {
+            const int64_t row = scatter ? m - block_lo(r, M, n) : m;
+            TY *y = static_cast<TY *>(outs.p[r]) + row * ldo + j;
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                store1(y + e, acc[e]);
+        }
+    }
+}
+
+// Part q's element (m, j) into column q n_each + j of every output.
+template <typename T>
+__global__ void __launch_bounds__(256) gather_ranks_kernel(PartPtrs parts, int n, int64_t M,
+                                                           int64_t n_each, int64_t ld_part,
+                                                           OutPtrs outs, int64_t ldo) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int q = blockIdx.z;
+    if (j >= n_each)
+        return;
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+        const T v = static_cast<const T *>(parts.p[q])[m * ld_part + j];
+        for (int r = 0; r < n; ++r)
+            static_cast<T *>(outs.p[r])[m * ldo + (int64_t)q * n_each + j] = v;
+    }
+}
+
 inline unsigned rows_grid(int64_t M) { return (unsigned)(M < 65535 ? M : 65535); }
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -264,6 +330,55 @@ hipError_t launch_sum_sets(int n_sets, const SumSpec *sets, int64_t M, hipStream
             return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_reduce_to_ranks(int n, const float *const *parts, int64_t M, int64_t n_each,
+                                  int64_t ld_part, int scatter, tsl_dtype odtype,
+                                  void *const *outs, int64_t ldo, hipStream_t stream) {
+    PartPtrs pp{};
+    OutPtrs op{};
+    for (int r = 0; r < n; ++r) {
+        pp.p[r] = parts[r];
+        op.p[r] = outs[r];
+    }
+    const bool vec = n_each % 4 == 0 && ld_part % 4 == 0 && ldo % 4 == 0;
+    const int V = vec ? 4 : 1;
+    dim3 grid((unsigned)((n_each / V + 255) / 256), rows_grid(M));
+    if (odtype == TSL_F32) {
+        if (vec)
+            hipLaunchKernelGGL((reduce_ranks_kernel<float, 4>), grid, dim3(256), 0, stream, pp, n,
+                               M, n_each, ld_part, op, ldo, scatter);
+        else
+            hipLaunchKernelGGL((reduce_ranks_kernel<float, 1>), grid, dim3(256), 0, stream, pp, n,
+                               M, n_each, ld_part, op, ldo, scatter);
+    } else {
+        if (vec)
+            hipLaunchKernelGGL((reduce_ranks_kernel<uint16_t, 4>), grid, dim3(256), 0, stream, pp,
+                               n, M, n_each, ld_part, op, ldo, scatter);
+        else
+            hipLaunchKernelGGL((reduce_ranks_kernel<uint16_t, 1>), grid, dim3(256), 0, stream, pp,
+                               n, M, n_each, ld_part, op, ldo, scatter);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_to_ranks(int n, const void *const *parts, size_t elem_bytes, int64_t M,
+                                  int64_t n_each, int64_t ld_part, void *const *outs, int64_t ldo,
+                                  hipStream_t stream) {
+    PartPtrs pp{};
+    OutPtrs op{};
+    for (int r = 0; r < n; ++r) {
+        pp.p[r] = parts[r];
+        op.p[r] = outs[r];
+    }
+    dim3 grid((unsigned)((n_each + 255) / 256), rows_grid(M), (unsigned)n);
+    if (elem_bytes == 4)
+        hipLaunchKernelGGL(gather_ranks_kernel<uint32_t>, grid, dim3(256), 0, stream, pp, n, M,
+                           n_each, ld_part, op, ldo);
+    else
+        hipLaunchKernelGGL(gather_ranks_kernel<uint16_t>, grid, dim3(256), 0, stream, pp, n, M,
+                           n_each, ld_part, op, ldo);
+    return hipGetLastError();
 }
 
 hipError_t launch_splitk_reduce(const float *P, int ks, int64_t M, int64_t N, tsl_dtype ydtype,

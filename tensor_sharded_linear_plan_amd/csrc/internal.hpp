@@ -60,6 +60,15 @@ struct SumSpec {
     tsl_dtype ydtype = TSL_F32;
 };
 hipError_t launch_sum_sets(int n_sets, const SumSpec *sets, int64_t M, hipStream_t stream);
+// Every rank's result of a collective (combine_to_ranks in tsl.h):
+// scatter 0 writes the ordered sum to every output, 1 each output its row
+// block; the gather copies the parts side by side into every output.
+hipError_t launch_reduce_to_ranks(int n, const float *const *parts, int64_t M, int64_t n_each,
+                                  int64_t ld_part, int scatter, tsl_dtype odtype,
+                                  void *const *outs, int64_t ldo, hipStream_t stream);
+hipError_t launch_gather_to_ranks(int n, const void *const *parts, size_t elem_bytes, int64_t M,
+                                  int64_t n_each, int64_t ld_part, void *const *outs, int64_t ldo,
+                                  hipStream_t stream);
 // Y (+)= sum_{s < ks} P[s], P is [ks][M][N] f32 contiguous, ascending s.
 hipError_t launch_splitk_reduce(const float *P, int ks, int64_t M, int64_t N, tsl_dtype ydtype,
                                 void *Y, int64_t ldy, int accumulate, hipStream_t stream);

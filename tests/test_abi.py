@@ -27,7 +27,8 @@ def test_library_exports_every_declared_symbol(tsl_lib):
     assert set(names) == {"plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
                           "shard_linear_workspace_size", "shard_linear",
                           "shard_linear_group_workspace_size", "shard_linear_group",
-                          "combine_partials", "tsl_status_string", "tsl_last_hip_error_string"}
+                          "combine_partials", "combine_to_ranks", "tsl_status_string",
+                          "tsl_last_hip_error_string"}
     lib = ctypes.CDLL(tsl_lib.LIBRARY)
     for n in names:
         assert hasattr(lib, n), n
@@ -369,3 +370,39 @@ def test_sum_set_rules(tsl_lib):
     with pytest.raises(tsl_lib.TslError) as e:
         call(items())
     assert e.value.status == tsl_lib.ERR_BUFFER_TOO_SMALL
+
+
+def test_combine_to_ranks_rejections(tsl_lib):
+    """Per-rank collectives: argument checks before any launch.  Accepted
+    layouts are probed with M == 0 (validated, nothing enqueued) or via an
+    unsupported type that is only reported after the layout passed."""
+    n, M, N = 4, 10, 64
+    parts = [(1 << 24) + r * (1 << 20) for r in range(n)]
+    Y = 1 << 28
+    call = lambda op, outs, **kw: tsl_lib.combine_to_ranks(
+        op, parts, kw.get("pdtype", tsl_lib.F32), kw.get("M", M), N, N,
+        kw.get("odtype", tsl_lib.F32), outs, kw.get("ldo", N))
+    # reduce-scatter: the rank blocks of one [M][N] buffer side by side are fine
+    rs_outs = [Y + 4 * N * ((r * M) // n) for r in range(n)]
+    call(tsl_lib.REDUCE_SCATTER, rs_outs, M=0)
+    bad = [
+        (tsl_lib.ALL_REDUCE, rs_outs, {}),                        # full-size outputs overlap
+        (tsl_lib.REDUCE_SCATTER, [Y] * n, {}),                    # the same block twice
+        (tsl_lib.REDUCE_SCATTER, [parts[1] + 64] + rs_outs[1:], {}),  # output inside a part
+        (tsl_lib.ALL_GATHER, [Y + r * 4 * N * n * M for r in range(n)], dict(ldo=N)),  # ldo < n N
+        (7, rs_outs, {}),
+    ]
+    for op, outs, kw in bad:
+        with pytest.raises(tsl_lib.TslError) as e:
+            call(op, outs, **kw)
+        assert e.value.status == tsl_lib.ERR_INVALID_ARG, (op, kw)
+    with pytest.raises(tsl_lib.TslError) as e:  # sums need binary32 parts
+        call(tsl_lib.ALL_REDUCE, [Y + r * 4 * N * M for r in range(n)], pdtype=tsl_lib.BF16)
+    assert e.value.status == tsl_lib.ERR_UNSUPPORTED
+    with pytest.raises(tsl_lib.TslError) as e:  # a gather copies: same types
+        call(tsl_lib.ALL_GATHER, [Y + r * 4 * N * n * M for r in range(n)], ldo=n * N,
+             odtype=tsl_lib.BF16)
+    assert e.value.status == tsl_lib.ERR_UNSUPPORTED
+    with pytest.raises(tsl_lib.TslError) as e:
+        call(tsl_lib.ALL_REDUCE, [Y + 2] + [Y + r * 4 * N * M for r in range(1, n)])
+    assert e.value.status == tsl_lib.ERR_MISALIGNED

@@ -386,3 +386,32 @@ def test_slice_q4_commutes_with_dequant():
             s = dict(zip(oracle.FIELDS, map(int, p[r])))
             got = oracle.dequant_q4(*oracle.slice_q4(codes, sc, bi, s))
             assert np.array_equal(got, oracle.slice_weight(full, s))
+
+
+def test_collectives_results():
+    """The three collectives' per-rank results against what fixes them: an
+    all-reduce is a reduce-scatter followed by an all-gather (the pages'
+    ring description), the reduce-scatter blocks tile the rows exactly
+    once, the all-gather is the concat on every rank, and integer parts sum
+    exactly."""
+    rng = np.random.default_rng(91)
+    for M, R in ((7, 4), (1, 4), (8, 8), (32, 2), (5, 3)):
+        parts = [rng.integers(-3, 4, size=(M, 6)).astype(np.float64) for _ in range(R)]
+        exact = np.sum(np.stack(parts), axis=0)
+        rs = oracle.reduce_scatter(parts, R)
+        # blocks are contiguous, disjoint, ordered and cover every row
+        bounds = [oracle.rank_rows(M, R, r) for r in range(R)]
+        assert bounds[0][0] == 0 and bounds[-1][1] == M
+        assert all(bounds[r][1] == bounds[r + 1][0] for r in range(R - 1))
+        assert all(0 <= hi - lo - M // R <= 1 for lo, hi in bounds)
+        assert np.array_equal(np.concatenate(rs, axis=0), exact)
+        # all-reduce == all-gather of the reduce-scatter blocks (as rows)
+        ar = oracle.all_reduce(parts, R)
+        gathered = np.concatenate(rs, axis=0)
+        assert len(ar) == R and all(np.array_equal(a, gathered) for a in ar)
+        ag = oracle.all_gather(parts, R)
+        assert len(ag) == R and all(np.array_equal(a, np.hstack(parts)) for a in ag)
+    # binary32 ordered sum flows through unchanged
+    parts = [rng.standard_normal((6, 5)).astype(np.float32) for _ in range(3)]
+    rs = oracle.reduce_scatter(parts, 3, sum_fn=oracle.sum_f32_seq)
+    assert np.array_equal(np.concatenate(rs), oracle.sum_f32_seq(parts))
