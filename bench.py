@@ -243,6 +243,50 @@ def prefill_bench(args, tsl, torch, synth, configs):
                 nitems=nitems, separate_ms=sep_ms)
 
 
+def collectives_bench(tsl, torch):
+    """Every rank's result of the three collectives over the prefill
+    layer's row-layer partials (4 ranks x [2048, 5120] fp32 -> bf16, or the
+    bf16 concat for the gather), GB/s of algorithmic bytes."""
+    R, M, n = 4, 2048, 5120
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    parts = [torch.randn((M, n), generator=g, device="cuda") for _ in range(R)]
+    shards = [p.to(torch.bfloat16) for p in parts]
+    full = [torch.empty((M, n), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    blocks = torch.empty((M, n), dtype=torch.bfloat16, device="cuda")
+    rs_outs = [blocks[(r * M) // R:] for r in range(R)]
+    gath = [torch.empty((M, R * n), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    cases = {
+        "all_reduce": (lambda: tsl.combine_to_ranks(tsl.ALL_REDUCE, parts, tsl.F32, M, n, n,
+                                                    tsl.BF16, full, n),
+                       R * M * n * 4 + R * M * n * 2),
+        "reduce_scatter": (lambda: tsl.combine_to_ranks(tsl.REDUCE_SCATTER, parts, tsl.F32, M, n,
+                                                        n, tsl.BF16, rs_outs, n),
+                           R * M * n * 4 + M * n * 2),
+        "all_gather": (lambda: tsl.combine_to_ranks(tsl.ALL_GATHER, shards, tsl.BF16, M, n, n,
+                                                    tsl.BF16, gath, R * n),
+                       R * M * n * 2 + R * R * M * n * 2),
+    }
+    out = {"workload": "4 ranks x [2048, 5120] row-layer partials (fp32 in, bf16 out; bf16 "
+                       "shards for the gather), every rank's buffer on one GPU",
+           "unit": "GB/s", "peak": PEAK_HBM}
+    for name, (fn, nbytes) in cases.items():
+        for _ in range(3):
+            fn()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(10):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        us = start.elapsed_time(end) * 1e3 / 10
+        out[name] = {"us": round(us, 1), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM, 4), "bytes": nbytes}
+        log("collective %s: %.1f us, %.0f GB/s" % (name, us, out[name]["GB/s"]))
+    return out
+
+
 def decode_bench(args, tsl, torch, synth, configs):
     layer = configs.DEC7B
     # weights of the whole layer (all ranks) are ~131 MB: 4 copies > 256 MB MALL + L2
@@ -356,6 +400,7 @@ def main():
 
     pre = prefill_bench(args, tsl, torch, synth, configs)
     dec = [] if args.no_decode else decode_bench(args, tsl, torch, synth, configs)
+    coll = None if args.no_decode else collectives_bench(tsl, torch)
     cpu = None
     if not args.no_cpu_baseline:
         sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
@@ -390,6 +435,7 @@ def main():
                                "the o/down rank sums in one shard_linear_group call per step, "
                                "HIP-graph replay over 4 weight copies",
                    "unit": "GB/s", "peak": PEAK_HBM, "rows": dec},
+        "collectives": coll,
         "pack_GBps": round(pre["pack_gbs"], 1),
         "prefill_separate_calls_ms_per_step": round(pre["separate_ms"], 4),
         "wall_s_timed": round(pre["wall"], 3),

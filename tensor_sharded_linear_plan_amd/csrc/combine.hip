@@ -212,19 +212,25 @@ __global__ void __launch_bounds__(256) reduce_ranks_kernel(PartPtrs parts, int n
     }
 }
 
-// Part q's element (m, j) into column q n_each + j of every output.
-template <typename T>
+// Row m of part q into columns [q n_each, (q+1) n_each) of row m of every
+// output, in VEC-byte units (16 when every row start is 16-byte aligned):
+// one load, n stores.
+template <int VEC>
 __global__ void __launch_bounds__(256) gather_ranks_kernel(PartPtrs parts, int n, int64_t M,
-                                                           int64_t n_each, int64_t ld_part,
-                                                           OutPtrs outs, int64_t ldo) {
-    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+                                                           int64_t row_units, int64_t ld_part_bytes,
+                                                           OutPtrs outs, int64_t ldo_bytes,
+                                                           int64_t part_bytes) {
+    typedef uint8_t unit_t __attribute__((ext_vector_type(VEC)));
     const int q = blockIdx.z;
-    if (j >= n_each)
+    const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= row_units)
         return;
     for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
-        const T v = static_cast<const T *>(parts.p[q])[m * ld_part + j];
+        const unit_t v = *reinterpret_cast<const unit_t *>(static_cast<const char *>(parts.p[q]) +
+                                                           m * ld_part_bytes + u * VEC);
+        const int64_t off = m * ldo_bytes + (int64_t)q * part_bytes + u * VEC;
         for (int r = 0; r < n; ++r)
-            static_cast<T *>(outs.p[r])[m * ldo + (int64_t)q * n_each + j] = v;
+            *reinterpret_cast<unit_t *>(static_cast<char *>(outs.p[r]) + off) = v;
     }
 }
 
@@ -371,13 +377,25 @@ hipError_t launch_gather_to_ranks(int n, const void *const *parts, size_t elem_b
         pp.p[r] = parts[r];
         op.p[r] = outs[r];
     }
-    dim3 grid((unsigned)((n_each + 255) / 256), rows_grid(M), (unsigned)n);
-    if (elem_bytes == 4)
-        hipLaunchKernelGGL(gather_ranks_kernel<uint32_t>, grid, dim3(256), 0, stream, pp, n, M,
-                           n_each, ld_part, op, ldo);
-    else
-        hipLaunchKernelGGL(gather_ranks_kernel<uint16_t>, grid, dim3(256), 0, stream, pp, n, M,
-                           n_each, ld_part, op, ldo);
+    const int64_t row_bytes = n_each * (int64_t)elem_bytes;
+    const int64_t ldp_b = ld_part * (int64_t)elem_bytes, ldo_b = ldo * (int64_t)elem_bytes;
+    bool vec = (row_bytes % 16 == 0) && (ldp_b % 16 == 0) && (ldo_b % 16 == 0);
+    for (int r = 0; r < n; ++r)
+        vec = vec && aligned16(parts[r]) && aligned16(outs[r]);
+    if (vec) {
+        const int64_t units = row_bytes / 16;
+        dim3 grid((unsigned)((units + 255) / 256), rows_grid(M), (unsigned)n);
+        hipLaunchKernelGGL(gather_ranks_kernel<16>, grid, dim3(256), 0, stream, pp, n, M, units,
+                           ldp_b, op, ldo_b, row_bytes);
+    } else {
+        dim3 grid((unsigned)((n_each + 255) / 256), rows_grid(M), (unsigned)n);
+        if (elem_bytes == 4)
+            hipLaunchKernelGGL(gather_ranks_kernel<4>, grid, dim3(256), 0, stream, pp, n, M,
+                               n_each, ldp_b, op, ldo_b, row_bytes);
+        else
+            hipLaunchKernelGGL(gather_ranks_kernel<2>, grid, dim3(256), 0, stream, pp, n, M,
+                               n_each, ldp_b, op, ldo_b, row_bytes);
+    }
     return hipGetLastError();
 }
 

@@ -50,9 +50,12 @@ def test_all_reduce_and_reduce_scatter(R, M, n, ld, ydt):
     assert np.array_equal(got(Y), want(want32))  # the blocks tile the whole sum
 
 
+@pytest.mark.parametrize("pad", [4, 8])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("R,M,n,ld", SHAPES[:-2] + [(16, 4, 24, 24)])
-def test_all_gather(R, M, n, ld, dt):
+def test_all_gather(R, M, n, ld, dt, pad):
+    # pad 8 keeps bf16 output rows 16-byte aligned (the 16-byte path), pad 4
+    # does not for bf16
     t = torch()
     if dt == "f32":
         parts = [synth.normal_f32(800 + r, (M, ld)) for r in range(R)]
@@ -62,8 +65,8 @@ def test_all_gather(R, M, n, ld, dt):
         code, tdt = tsl.BF16, t.bfloat16
     d = [dev(p) for p in parts]
     width = R * n
-    outs = [t.zeros((M, width + 4), dtype=tdt, device="cuda") for _ in range(R)]
-    tsl.combine_to_ranks(tsl.ALL_GATHER, d, code, M, n, ld, code, outs, width + 4)
+    outs = [t.zeros((M, width + pad), dtype=tdt, device="cuda") for _ in range(R)]
+    tsl.combine_to_ranks(tsl.ALL_GATHER, d, code, M, n, ld, code, outs, width + pad)
     for r, ag in enumerate(oracle.all_gather([p[:, :n] for p in parts], R)):
         g = outs[r].cpu().numpy() if dt == "f32" else host_bits(outs[r])
         assert np.array_equal(g[:, :width], ag), r
