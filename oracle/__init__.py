@@ -58,6 +58,8 @@ def lib():
         L.oracle_plan.restype = ctypes.c_int
         L.oracle_plan_linear.argtypes = [i64, i64, i32, i32, i32, vp, i64]
         L.oracle_plan_linear.restype = ctypes.c_int
+        L.oracle_plan_vocab.argtypes = [i64, i64, i32, i32, vp, i64]
+        L.oracle_plan_vocab.restype = ctypes.c_int
         L.oracle_bf16_to_f64.argtypes = [vp, vp, i64]
         L.oracle_f64_to_bf16_rne.argtypes = [vp, vp, i64]
         L.oracle_dequant_q4.argtypes = [vp, vp, vp, i64, i64, i64, vp]
@@ -95,6 +97,17 @@ def plan_linear(K, N, tp, strategy, group=0):
     out = np.zeros((max(tp, 1), len(FIELDS)), dtype=np.int64)
     rc = lib().oracle_plan_linear(K, N, tp, strategy, group,
                                   out.ctypes.data_as(ctypes.c_void_p), out.size)
+    if rc != OK:
+        raise OracleError(rc)
+    return out
+
+
+def plan_vocab(vocab, hidden, tp, group=0):
+    """Vocabulary-parallel shards: int64 array [tp][2][12], entry [r][0] the
+    embedding's row block, [r][1] the LM head's column block."""
+    out = np.zeros((max(tp, 1), 2, len(FIELDS)), dtype=np.int64)
+    rc = lib().oracle_plan_vocab(vocab, hidden, tp, group,
+                                 out.ctypes.data_as(ctypes.c_void_p), out.size)
     if rc != OK:
         raise OracleError(rc)
     return out
@@ -203,6 +216,21 @@ def slice_input(X, s):
 def shard_forward(s, X, W):
     """One rank's output: slice_input(X) @ slice_weight(W), in double."""
     return gemm(slice_input(X, s), slice_weight(W, s))
+
+
+def embed_lookup(E, tokens, s):
+    """One rank's partial of a vocabulary-parallel lookup (mlxcel manual
+    "Vocab Parallel": a rank looks up only the tokens of its own vocabulary
+    slice).  E is the full table [vocab][hidden]; s the rank's block
+    [k_off, k_off + k_len) x [n_off, n_off + n_len).  Row m is E[t][n-block]
+    for an owned token t = tokens[m], else zero; in double."""
+    E = np.asarray(E, dtype=np.float64)
+    out = np.zeros((len(tokens), s["n_len"]), dtype=np.float64)
+    for m, t in enumerate(tokens):
+        t = int(t)
+        if s["k_off"] <= t < s["k_off"] + s["k_len"]:
+            out[m] = E[t, s["n_off"]:s["n_off"] + s["n_len"]]
+    return out
 
 
 def combine_concat(parts):

@@ -198,6 +198,41 @@ int oracle_plan_linear(int64_t K, int64_t N, int32_t tp, int32_t strategy, int32
     return OR_OK;
 }
 
+/*
+ * Vocabulary-parallel shards of the token embedding and the LM head
+ * ([mlxcel] "Weight sharding strategy", "Vocab Parallel"; "Embedding and
+ * LM head sharding", mode vocab_parallel): the vocabulary is cut into tp
+ * contiguous slices in rank order.  The embedding table E[vocab][hidden] is
+ * read as W[K = vocab][N = hidden], so its slice is a row block whose
+ * partial lookups are summed; the LM head W[K = hidden][N = vocab] is
+ * column-split and its logits concatenated.  tp a power of two, vocab % tp
+ * == 0; group > 0 (a 4-bit LM head) needs hidden % group == 0.
+ * Output: tp * 2 records (embedding, LM head) of FIELDS int64, rank-major;
+ * proj 8 is the embedding, 9 the LM head, head fields -1.
+ */
+int oracle_plan_vocab(int64_t vocab, int64_t hidden, int32_t tp, int32_t group, int64_t *out,
+                      int64_t out_len)
+{
+    if (vocab < 1 || hidden < 1 || tp < 1 || (group != 0 && group != 64))
+        return OR_INVALID;
+    if (out == 0 || out_len < (int64_t)tp * 2 * FIELDS)
+        return OR_INVALID;
+    if ((tp & (tp - 1)) != 0)
+        return OR_TP_NOT_POW2;
+    if (vocab % tp != 0)
+        return OR_NOT_DIVISIBLE;
+    if (group > 0 && hidden % group != 0)
+        return OR_GROUP_ALIGN;
+    int64_t slice = vocab / tp;
+    for (int64_t r = 0; r < tp; ++r) {
+        put(out + (2 * r) * FIELDS, 8, r, S_ROW, C_SUM, vocab, hidden, r * slice, slice, 0, hidden,
+            -1, -1);
+        put(out + (2 * r + 1) * FIELDS, 9, r, S_COLUMN, C_CONCAT, hidden, vocab, 0, hidden,
+            r * slice, slice, -1, -1);
+    }
+    return OR_OK;
+}
+
 /* bf16 -> double: a bf16 value is the upper half of an IEEE binary32. */
 void oracle_bf16_to_f64(const uint16_t *in, double *out, int64_t n)
 {

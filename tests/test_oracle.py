@@ -415,3 +415,79 @@ def test_collectives_results():
     parts = [rng.standard_normal((6, 5)).astype(np.float32) for _ in range(3)]
     rs = oracle.reduce_scatter(parts, 3, sum_fn=oracle.sum_f32_seq)
     assert np.array_equal(np.concatenate(rs), oracle.sum_f32_seq(parts))
+
+
+# --------------------------------------------------------------------------
+# vocabulary-parallel embedding and LM head
+# --------------------------------------------------------------------------
+
+def test_plan_vocab_slices_and_rejections():
+    # mlxcel "Vocab Parallel": every rank owns one contiguous slice of the
+    # vocabulary; slices in rank order tile [0, vocab) without overlap
+    for vocab, hidden, tp in itertools.product((8, 64, 1024, 152064), (64, 3584), (1, 2, 4, 8)):
+        if vocab % tp:
+            continue
+        p = oracle.plan_vocab(vocab, hidden, tp)
+        ends = 0
+        for r in range(tp):
+            e, h = oracle.spec(p, r, 0), oracle.spec(p, r, 1)
+            assert (e["proj"], e["strategy"], e["combine"]) == (8, oracle.ROW, oracle.SUM)
+            assert (h["proj"], h["strategy"], h["combine"]) == (9, oracle.COLUMN, oracle.CONCAT)
+            assert (e["K"], e["N"], h["K"], h["N"]) == (vocab, hidden, hidden, vocab)
+            assert e["k_off"] == ends and h["n_off"] == ends  # contiguous, rank order
+            assert e["k_len"] == h["n_len"] == vocab // tp
+            assert (e["n_off"], e["n_len"], h["k_off"], h["k_len"]) == (0, hidden, 0, hidden)
+            ends += e["k_len"]
+        assert ends == vocab
+    for args, code in (((100, 64, 8), oracle.NOT_DIVISIBLE), ((96, 64, 3), oracle.TP_NOT_POW2),
+                       ((96, 64, 0), oracle.INVALID), ((0, 64, 2), oracle.INVALID)):
+        with pytest.raises(oracle.OracleError) as ei:
+            oracle.plan_vocab(*args)
+        assert ei.value.code == code, args
+    with pytest.raises(oracle.OracleError) as ei:
+        oracle.plan_vocab(96, 96, 2, group=64)
+    assert ei.value.code == oracle.GROUP_ALIGN
+    oracle.plan_vocab(96, 128, 2, group=64)
+
+
+def test_embed_lookup_is_one_hot_product_and_partials_sum_to_rows():
+    # a lookup is the one-hot row of the token times the table (numpy
+    # matmul, exact for one-hot rows); the rank partials of a token are zero
+    # except on its owner, so they add up to the full row
+    rng = np.random.default_rng(11)
+    vocab, hidden, tp = 64, 24, 4
+    E = rng.standard_normal((vocab, hidden))
+    tokens = np.array([0, 15, 16, 63, 31, 32, 5, 5, -1, 64, 200], dtype=np.int64)
+    full = np.zeros((len(tokens), hidden))
+    for m, t in enumerate(tokens):
+        if 0 <= t < vocab:
+            full[m] = E[t]
+    p = oracle.plan_vocab(vocab, hidden, tp)
+    total = np.zeros_like(full)
+    for r in range(tp):
+        s = oracle.spec(p, r, 0)
+        part = oracle.embed_lookup(E, tokens, s)
+        onehot = np.zeros((len(tokens), vocab))
+        for m, t in enumerate(tokens):
+            if s["k_off"] <= t < s["k_off"] + s["k_len"]:
+                onehot[m, t] = 1.0
+        assert np.array_equal(part, onehot @ E)
+        owned = (tokens >= s["k_off"]) & (tokens < s["k_off"] + s["k_len"])
+        assert not part[~owned].any()
+        total += part
+    assert np.array_equal(total, full)
+    assert not total[-3:].any()  # ids outside the vocabulary belong to no rank
+    # a column block of the table keeps only its columns
+    s = dict(oracle.spec(p, 1, 0), n_off=8, n_len=10)
+    assert np.array_equal(oracle.embed_lookup(E, tokens, s)[2], E[16, 8:18])
+
+
+def test_lm_head_shards_concat_to_full_logits():
+    # column shards over the vocabulary: concat of the rank logits == X W
+    rng = np.random.default_rng(12)
+    vocab, hidden, tp = 96, 32, 4
+    X = rng.integers(-3, 4, (5, hidden)).astype(np.float64)
+    W = rng.integers(-3, 4, (hidden, vocab)).astype(np.float64)
+    p = oracle.plan_vocab(vocab, hidden, tp)
+    parts = [oracle.shard_forward(oracle.spec(p, r, 1), X, W) for r in range(tp)]
+    assert np.array_equal(oracle.combine_concat(parts), X @ W)
