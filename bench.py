@@ -331,6 +331,123 @@ def decode_bench(args, tsl, torch, synth, configs):
     return res
 
 
+def vocab_bench(args, tsl, torch, synth, configs):
+    """vocab7b: the 4-bit LM head at decode (every rank's vocabulary slice in
+    one grouped call, writing its slice of the full f32 logits), HIP-graph
+    replay over 2 weight copies; and the embedding lookup of 2048 ids
+    (every rank's masked lookup into f32 partials, then their sum into bf16
+    rows), GB/s of algorithmic bytes."""
+    c = configs.VOCAB7B
+    t0 = time.perf_counter()
+    plan = tsl.plan_vocab(c.vocab, c.hidden, c.tp, 64)
+    heads, embeds = plan[1::2], plan[0::2]
+    seed = lambda tt: synth.seed_of(c.index, 1, tt)
+    codes = torch.from_numpy(synth.q4_codes(seed(synth.T_CODES), (c.hidden, c.vocab))).cuda()
+    sc = torch.from_numpy(synth.uniform_bf16(seed(synth.T_SCALES), (c.hidden // 64, c.vocab),
+                                             c.scale_lo, c.scale_hi).view("int16")).cuda()
+    bi = torch.from_numpy(synth.normal_bf16(seed(synth.T_BIASES), (c.hidden // 64, c.vocab),
+                                            c.bias_std).view("int16")).cuda()
+    copies = 2
+    packs = []
+    for _ in range(copies):
+        row = []
+        for sh in heads:
+            nb = tsl.pack_shard_size(sh, tsl.Q4G64)
+            buf = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            tsl.pack_shard(sh, tsl.Q4G64, codes, c.vocab, 1, sc, bi, c.vocab, 1, buf, nb)
+            row.append((buf, nb))
+        packs.append(row)
+    del codes, sc, bi
+    torch.cuda.synchronize()
+    log("vocab: packed the LM head x%d (%.1f s)" % (copies, time.perf_counter() - t0))
+    wbytes = c.hidden * c.vocab // 2 + (c.hidden // 64) * c.vocab * 4
+    out = {"workload": "vocab7b: vocabulary 152064 split over tp=4 at hidden 3584; LM head 4-bit "
+                       "g64 -> f32 logits (all 4 vocabulary slices in one shard_linear_group "
+                       "call, HIP-graph replay over 2 weight copies); embedding bf16 table, 2048 "
+                       "uniform ids, 4 masked lookups into f32 partials + their sum into bf16",
+           "unit": "GB/s", "peak": PEAK_HBM, "lm_head": []}
+    for M in c.head_ms:
+        X = torch.from_numpy(synth.normal_bf16(seed(synth.T_X) + M, (M, c.hidden))
+                             .view("int16")).cuda().view(torch.bfloat16)
+        logits = torch.empty((M, c.vocab), dtype=torch.float32, device="cuda")
+        groups = []
+        for cp in range(copies):
+            items = [dict(shard=sh, packed=buf, packed_bytes=nb, X=X, ldx=c.hidden,
+                          Y=logits[:, sh.n_off:], ldy=c.vocab)
+                     for sh, (buf, nb) in zip(heads, packs[cp])]
+            arr = tsl._items(items)
+            ws = tsl.shard_linear_group_workspace_size(items, tsl.Q4G64, M)
+            wsb = torch.empty(max(ws, 256), dtype=torch.uint8, device="cuda")
+            groups.append((arr, wsb, ws))
+
+        def run(cp, stream):
+            (arr, n), wsb, ws = groups[cp]
+            tsl._check(tsl._lib.shard_linear_group(n, arr, tsl.Q4G64, tsl.BF16, M, wsb.data_ptr(),
+                                                   ws, stream), "shard_linear_group")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for cp in range(copies):
+                run(cp, side.cuda_stream)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream().cuda_stream
+            for cp in range(copies):
+                run(cp, cap)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        reps = max(5, args.steps)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        us = start.elapsed_time(end) * 1e3 / (reps * copies)
+        nbytes = wbytes + M * c.hidden * 2 + M * c.vocab * 4
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out["lm_head"].append({"M": M, "us_per_step": round(us, 2), "GB/s": round(gbs, 1),
+                               "frac": round(gbs / PEAK_HBM, 4), "bytes_per_step": nbytes})
+        log("vocab LM head M=%d: %.1f us/step, %.0f GB/s" % (M, us, gbs))
+        del graph
+    del packs
+    # embedding lookup
+    E = torch.from_numpy(synth.normal_bf16(synth.seed_of(c.index, 0, synth.T_W),
+                                           (c.vocab, c.hidden), c.e_std).view("int16")).cuda()
+    tokens = torch.from_numpy(synth.token_ids(synth.seed_of(c.index, 0, synth.T_X), c.lookup_m,
+                                              c.vocab)).cuda()
+    M, H = c.lookup_m, c.hidden
+    parts = [torch.empty((M, H), dtype=torch.float32, device="cuda") for _ in embeds]
+    Y = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+
+    def lookup():
+        for sh, P in zip(embeds, parts):
+            tsl.embed_lookup(sh, tsl.BF16, E[sh.k_off:], H, tokens, M, tsl.F32, P, H)
+        tsl.combine_partials(tsl.COMBINE_SUM, parts, tsl.F32, M, H, H, tsl.BF16, Y, H)
+    for _ in range(3):
+        lookup()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(10):
+        lookup()
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / 10
+    R = len(embeds)
+    nbytes = M * 4 + M * H * 2 + R * M * H * 4 + R * M * H * 4 + M * H * 2
+    gbs = nbytes / (us * 1e-6) / 1e9
+    out["embed"] = {"M": M, "us_per_step": round(us, 1), "GB/s": round(gbs, 1),
+                    "frac": round(gbs / PEAK_HBM, 4), "bytes_per_step": nbytes,
+                    "bytes": "ids + owned table rows + 4 f32 partials written and read + bf16 rows"}
+    log("vocab embedding M=%d: %.1f us/step, %.0f GB/s" % (M, us, gbs))
+    return out
+
+
 def cpu_baseline(synth, configs):
     """The oracle, as it stands, on a bounded sample of the prefill workload:
     rank 0's gate shard (5120 -> 4352, 4-bit), dequantised and multiplied
@@ -401,6 +518,7 @@ def main():
     pre = prefill_bench(args, tsl, torch, synth, configs)
     dec = [] if args.no_decode else decode_bench(args, tsl, torch, synth, configs)
     coll = None if args.no_decode else collectives_bench(tsl, torch)
+    voc = None if args.no_decode else vocab_bench(args, tsl, torch, synth, configs)
     cpu = None
     if not args.no_cpu_baseline:
         sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
@@ -436,6 +554,7 @@ def main():
                                "HIP-graph replay over 4 weight copies",
                    "unit": "GB/s", "peak": PEAK_HBM, "rows": dec},
         "collectives": coll,
+        "vocab": voc,
         "pack_GBps": round(pre["pack_gbs"], 1),
         "prefill_separate_calls_ms_per_step": round(pre["separate_ms"], 4),
         "wall_s_timed": round(pre["wall"], 3),

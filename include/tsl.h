@@ -70,12 +70,15 @@ typedef enum tsl_combine {
 } tsl_combine;
 
 /* Projections of a standard transformer layer, in plan order; TSL_LINEAR
- * tags a lone linear layer planned with plan_linear(). */
+ * tags a lone linear layer planned with plan_linear(), TSL_EMBED and
+ * TSL_LM_HEAD the vocabulary-indexed weights planned with plan_vocab(). */
 typedef enum tsl_proj {
     TSL_Q = 0, TSL_K = 1, TSL_V = 2, TSL_O = 3,
     TSL_GATE = 4, TSL_UP = 5, TSL_DOWN = 6,
     TSL_NPROJ = 7,
-    TSL_LINEAR = 7
+    TSL_LINEAR = 7,
+    TSL_EMBED = 8,
+    TSL_LM_HEAD = 9
 } tsl_proj;
 
 typedef enum tsl_dtype {
@@ -148,6 +151,30 @@ tsl_status plan_shards(const tsl_dims *dims, tsl_shard *out, int64_t out_len);
  */
 tsl_status plan_linear(int64_t K, int64_t N, int32_t tp_size, int32_t strategy,
                        int32_t group_size, tsl_shard *out, int64_t out_len);
+
+/*
+ * plan_vocab -- the vocabulary-parallel shards of the token embedding and
+ * the LM head ([mlxcel] "Weight sharding strategy", "Vocab Parallel": the
+ * vocabulary dimension of both is split across ranks, each rank owning one
+ * contiguous slice; "Embedding and LM head sharding", mode vocab_parallel).
+ * Rank r owns tokens [r*vocab/tp, (r+1)*vocab/tp).
+ *   out[2r]     TSL_EMBED: the table E[vocab][hidden] read as a linear
+ *               layer W[K = vocab][N = hidden] (a lookup is a one-hot row
+ *               times W), row shard over rank r's tokens, combine SUM: the
+ *               rank partials of a lookup add up to the full row
+ *               (embed_lookup).
+ *   out[2r + 1] TSL_LM_HEAD: W[K = hidden][N = vocab], column shard over
+ *               rank r's tokens, combine CONCAT (the logits' all-gather);
+ *               a shard_linear weight like any other column shard.
+ * head_off/head_cnt are -1.  group_size 64 (4-bit LM head) requires
+ * hidden % 64 == 0; the embedding table itself is dense (embed_lookup).
+ * Errors, in this order: TSL_ERR_INVALID_ARG (null, vocab/hidden/tp < 1,
+ * group_size not 0 or 64, out_len < 2*tp), TSL_ERR_TP_NOT_POW2,
+ * TSL_ERR_NOT_DIVISIBLE (vocab % tp; pad the vocabulary to a multiple of
+ * tp), TSL_ERR_GROUP_ALIGN.  Host only.
+ */
+tsl_status plan_vocab(int64_t vocab, int64_t hidden, int32_t tp_size, int32_t group_size,
+                      tsl_shard *out, int64_t out_len);
 
 /*
  * pack_shard_size -- bytes of the packed, kernel-ready copy of a shard.
@@ -358,6 +385,31 @@ typedef enum tsl_collective {
 tsl_status combine_to_ranks(tsl_collective op, int32_t n, const void *const *parts,
                             tsl_dtype pdtype, int64_t M, int64_t n_each, int64_t ld_part,
                             tsl_dtype odtype, void *const *outs, int64_t ldo, void *stream);
+
+/*
+ * embed_lookup -- one rank's share of a vocabulary-parallel embedding
+ * lookup ([mlxcel] "Vocab Parallel": each rank looks up the tokens of its
+ * vocabulary slice; the joined result is every token's full row).
+ *   shard:  the rank's block W[k_off : k_off + k_len, n_off : n_off + n_len]
+ *           of the table W[K = vocab][N = hidden] (TSL_EMBED records of
+ *           plan_vocab; any strategy is accepted).
+ *   table:  DEVICE, that block as k_len rows of n_len elements, row stride
+ *           ld_table >= n_len, type tdtype (F32 or BF16).
+ *   tokens: DEVICE int32 [M], token ids.
+ *   Y:      DEVICE [M][ldy], ldy >= n_len, type ydtype (F32 or BF16).
+ * Y[m][j] = W[t][n_off + j] for t = tokens[m] when k_off <= t < k_off +
+ * k_len (widened exactly, or rounded to nearest-even for F32 -> BF16);
+ * otherwise -0.0, the additive identity of IEEE round-to-nearest, so the
+ * rank-ordered binary32 SUM of the partials (combine_partials,
+ * combine_to_ranks) reproduces the owning rank's row bit for bit.  Ids
+ * outside [0, vocab) are owned by no rank and give -0.0 rows everywhere.
+ * M == 0 enqueues nothing.  Y must not overlap table or tokens.  Errors:
+ * TSL_ERR_INVALID_ARG, TSL_ERR_MISALIGNED (pointers aligned to their
+ * element size), TSL_ERR_HIP.
+ */
+tsl_status embed_lookup(const tsl_shard *shard, tsl_dtype tdtype, const void *table,
+                        int64_t ld_table, const int32_t *tokens, int64_t M, tsl_dtype ydtype,
+                        void *Y, int64_t ldy, void *stream);
 
 /* A static, human-readable description of a status code. */
 const char *tsl_status_string(tsl_status status);

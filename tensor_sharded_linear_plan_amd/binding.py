@@ -43,6 +43,7 @@ COMBINE_NONE, COMBINE_CONCAT, COMBINE_SUM = 0, 1, 2
 Q, K, V, O, GATE, UP, DOWN = range(7)
 NPROJ = 7
 LINEAR = 7
+EMBED, LM_HEAD = 8, 9
 F32, BF16, Q4G64 = 0, 1, 2
 ALL_REDUCE, REDUCE_SCATTER, ALL_GATHER = 0, 1, 2
 MAX_PARTS = 64
@@ -110,19 +111,23 @@ _lib.combine_partials.argtypes = [ctypes.c_int, _i32, ctypes.POINTER(_vp), ctype
                                   _i64, _i64, ctypes.c_int, _vp, _i64, _vp]
 _lib.combine_to_ranks.argtypes = [ctypes.c_int, _i32, ctypes.POINTER(_vp), ctypes.c_int, _i64,
                                   _i64, _i64, ctypes.c_int, ctypes.POINTER(_vp), _i64, _vp]
+_lib.plan_vocab.argtypes = [_i64, _i64, _i32, _i32, _P_SHARD, _i64]
+_lib.embed_lookup.argtypes = [_P_SHARD, ctypes.c_int, _vp, _i64, _vp, _i64, ctypes.c_int, _vp,
+                              _i64, _vp]
 _lib.tsl_status_string.argtypes = [ctypes.c_int]
 _lib.tsl_status_string.restype = ctypes.c_char_p
 _lib.tsl_last_hip_error_string.argtypes = []
 _lib.tsl_last_hip_error_string.restype = ctypes.c_char_p
 for _f in ("plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
            "shard_linear_workspace_size", "shard_linear", "shard_linear_group_workspace_size",
-           "shard_linear_group", "combine_partials", "combine_to_ranks"):
+           "shard_linear_group", "combine_partials", "combine_to_ranks", "plan_vocab",
+           "embed_lookup"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
            "shard_linear_workspace_size", "shard_linear", "shard_linear_group_workspace_size",
-           "shard_linear_group", "combine_partials", "combine_to_ranks", "tsl_status_string",
-           "tsl_last_hip_error_string")
+           "shard_linear_group", "combine_partials", "combine_to_ranks", "plan_vocab",
+           "embed_lookup", "tsl_status_string", "tsl_last_hip_error_string")
 
 
 def _check(status, where):
@@ -168,6 +173,19 @@ def plan_linear(K, N, tp_size, strategy, group_size=0):
     out = (Shard * n)()
     _check(_lib.plan_linear(K, N, tp_size, strategy, group_size, out, n), "plan_linear")
     return list(out)
+
+
+def plan_vocab(vocab, hidden, tp_size, group_size=0):
+    """[embedding shard, LM-head shard] of every rank: a list of 2*tp shards."""
+    n = 2 * max(int(tp_size), 1)
+    out = (Shard * n)()
+    _check(_lib.plan_vocab(vocab, hidden, tp_size, group_size, out, n), "plan_vocab")
+    return list(out)
+
+
+def embed_lookup(shard, tdtype, table, ld_table, tokens, M, ydtype, Y, ldy, stream=None):
+    _check(_lib.embed_lookup(ctypes.byref(shard), tdtype, _ptr(table), ld_table, _ptr(tokens), M,
+                             ydtype, _ptr(Y), ldy, _stream(stream)), "embed_lookup")
 
 
 def pack_shard_size(shard, wdtype):

@@ -15,6 +15,12 @@ Plain data; no arithmetic of the method lives here.
   gqa8     the GQA replication case: tp=8, hidden 4096, 32 Q / 4 KV heads of
            128 (K/V replicated), FFN 14336, bf16; M = 64 (decode) and 512
            (prefill).
+Vocabulary-parallel workloads (embedding table and LM head split over the
+vocabulary, which the pages recommend past about 100k tokens):
+  vocab7b  vocabulary 152064 at dec7b's width (hidden 3584), tp=4: a 4-bit
+           LM head at decode (M = 1, 4, 16 token rows of N(0, 1) bf16
+           activations) and a bf16 N(0, 0.02) embedding table looked up by
+           M = 2048 uniformly drawn token ids.
 """
 from dataclasses import dataclass, field
 
@@ -67,3 +73,22 @@ GQA8 = Layer("gqa8", 4, 4096, 32, 4, 128, 14336, 8, BF16, (64, 512))
 
 LAYERS = (LLAMA2K, DEC7B, PRE27B, GQA8)
 PROJS = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+@dataclass(frozen=True)
+class Vocab:
+    """A vocabulary-parallel embedding + LM head workload."""
+    name: str
+    index: int           # config number used in the input seeds
+    vocab: int
+    hidden: int
+    tp: int
+    head_ms: tuple       # LM-head token rows (decode)
+    lookup_m: int        # embedding lookups per call
+    e_std: float = 0.02  # embedding table ~ N(0, e_std^2), bf16
+    scale_lo: float = 0.005
+    scale_hi: float = 0.02
+    bias_std: float = 0.05
+
+
+VOCAB7B = Vocab("vocab7b", 5, 152064, 3584, 4, (1, 4, 16), 2048)

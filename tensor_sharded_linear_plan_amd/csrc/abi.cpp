@@ -639,6 +639,32 @@ extern "C" tsl_status combine_to_ranks(tsl_collective op, int32_t n, const void 
                                            ldo, s));
 }
 
+extern "C" tsl_status embed_lookup(const tsl_shard *shard, tsl_dtype tdtype, const void *table,
+                                   int64_t ld_table, const int32_t *tokens, int64_t M,
+                                   tsl_dtype ydtype, void *Y, int64_t ldy, void *stream) {
+    tsl_status st = check_shard(shard);
+    if (st != TSL_OK)
+        return st;
+    if (!table || !tokens || !Y || M < 0)
+        return TSL_ERR_INVALID_ARG;
+    if ((tdtype != TSL_F32 && tdtype != TSL_BF16) || (ydtype != TSL_F32 && ydtype != TSL_BF16))
+        return TSL_ERR_INVALID_ARG;
+    const int64_t n_len = shard->n_len;
+    if (ld_table < n_len || ldy < n_len)
+        return TSL_ERR_INVALID_ARG;
+    const size_t te = tdtype == TSL_F32 ? 4 : 2, ye = ydtype == TSL_F32 ? 4 : 2;
+    if (!aligned(table, te) || !aligned(tokens, 4) || !aligned(Y, ye))
+        return TSL_ERR_MISALIGNED;
+    if (M == 0)
+        return TSL_OK;
+    if (matrices_overlap(Y, M, n_len, ldy, ye, table, shard->k_len, n_len, ld_table, te) ||
+        overlaps(Y, span(M, n_len, ldy, ye), tokens, (size_t)M * 4))
+        return TSL_ERR_INVALID_ARG;
+    return from_hip(launch_embed_lookup(tdtype, table, ld_table, tokens, M, shard->k_off,
+                                        shard->k_len, n_len, ydtype, Y, ldy,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 extern "C" const char *tsl_last_hip_error_string(void) { return hipGetErrorString(g_last_hip); }
 
 extern "C" const char *tsl_status_string(tsl_status status) {

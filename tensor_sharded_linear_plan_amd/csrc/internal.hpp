@@ -73,6 +73,14 @@ hipError_t launch_gather_to_ranks(int n, const void *const *parts, size_t elem_b
 hipError_t launch_splitk_reduce(const float *P, int ks, int64_t M, int64_t N, tsl_dtype ydtype,
                                 void *Y, int64_t ldy, int accumulate, hipStream_t stream);
 
+// ---- embed.hip ----
+// Y[m][j] = table[(tokens[m] - k_off) * ld_table + j] when the token lies in
+// [k_off, k_off + k_len), else -0.0; j < n_len.  Types F32 / BF16.
+hipError_t launch_embed_lookup(tsl_dtype tdtype, const void *table, int64_t ld_table,
+                               const int32_t *tokens, int64_t M, int64_t k_off, int64_t k_len,
+                               int64_t n_len, tsl_dtype ydtype, void *Y, int64_t ldy,
+                               hipStream_t stream);
+
 // One shard product of a (possibly grouped) shard_linear call, validated.
 struct LinearItem {
     PackGeom g;

@@ -185,3 +185,36 @@ extern "C" tsl_status plan_linear(int64_t K, int64_t N, int32_t tp, int32_t stra
     }
     return TSL_OK;
 }
+
+// Vocabulary-parallel embedding and LM head: the vocabulary dimension of
+// both is cut into tp contiguous slices in rank order (mlxcel "Vocab
+// Parallel").  The table E[vocab][hidden] is a linear W[vocab][hidden] fed a
+// one-hot row, so its vocabulary slice is a row shard joined by a sum; the
+// LM head W[hidden][vocab] is a column shard joined by a concat.
+extern "C" tsl_status plan_vocab(int64_t vocab, int64_t hidden, int32_t tp, int32_t group_size,
+                                 tsl_shard *out, int64_t out_len) {
+    if (!out || vocab < 1 || hidden < 1 || tp < 1)
+        return TSL_ERR_INVALID_ARG;
+    if (group_size != 0 && group_size != 64)
+        return TSL_ERR_INVALID_ARG;
+    if (out_len < 2 * (int64_t)tp)
+        return TSL_ERR_INVALID_ARG;
+    if (!pow2(tp))
+        return TSL_ERR_TP_NOT_POW2;
+    if (vocab % tp)
+        return TSL_ERR_NOT_DIVISIBLE;
+    if (group_size && hidden % group_size)
+        return TSL_ERR_GROUP_ALIGN;
+    for (int32_t r = 0; r < tp; ++r) {
+        const Block b = block_of(vocab, tp, r);
+        tsl_shard e = make(TSL_EMBED, r, TSL_ROW, TSL_COMBINE_SUM, vocab, hidden);
+        e.k_off = b.off;
+        e.k_len = b.len;
+        tsl_shard h = make(TSL_LM_HEAD, r, TSL_COLUMN, TSL_COMBINE_CONCAT, hidden, vocab);
+        h.n_off = b.off;
+        h.n_len = b.len;
+        out[2 * r] = e;
+        out[2 * r + 1] = h;
+    }
+    return TSL_OK;
+}

@@ -69,3 +69,8 @@ def uniform_bf16(seed, shape, lo, hi):
 
 def const_bf16(shape, value):
     return np.full(shape, f32_to_bf16_bits(np.float32(value)), dtype=np.uint16)
+
+
+def token_ids(seed, M, vocab):
+    """M token ids uniform on 0..vocab-1, int32."""
+    return rng(seed).integers(0, vocab, size=M, dtype=np.int32)

@@ -27,8 +27,8 @@ def test_library_exports_every_declared_symbol(tsl_lib):
     assert set(names) == {"plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
                           "shard_linear_workspace_size", "shard_linear",
                           "shard_linear_group_workspace_size", "shard_linear_group",
-                          "combine_partials", "combine_to_ranks", "tsl_status_string",
-                          "tsl_last_hip_error_string"}
+                          "combine_partials", "combine_to_ranks", "plan_vocab",
+                          "embed_lookup", "tsl_status_string", "tsl_last_hip_error_string"}
     lib = ctypes.CDLL(tsl_lib.LIBRARY)
     for n in names:
         assert hasattr(lib, n), n
@@ -406,3 +406,58 @@ def test_combine_to_ranks_rejections(tsl_lib):
     with pytest.raises(tsl_lib.TslError) as e:
         call(tsl_lib.ALL_REDUCE, [Y + 2] + [Y + r * 4 * N * M for r in range(1, n)])
     assert e.value.status == tsl_lib.ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("tp", [1, 2, 4, 8])
+def test_plan_vocab_vs_oracle(tsl_lib, tp):
+    for vocab, hidden, group in ((152064, 3584, 64), (32000, 4096, 0), (100, 64, 0),
+                                 (96, 96, 64), (8, 128, 64)):
+        try:
+            want = oracle.plan_vocab(vocab, hidden, tp, group)
+        except oracle.OracleError as e:
+            with pytest.raises(tsl_lib.TslError) as got:
+                tsl_lib.plan_vocab(vocab, hidden, tp, group)
+            assert got.value.status == e.code
+            continue
+        got = np.array([s.as_tuple() for s in tsl_lib.plan_vocab(vocab, hidden, tp, group)])
+        assert np.array_equal(got, want.reshape(2 * tp, -1)), (vocab, hidden, tp, group)
+    with pytest.raises(tsl_lib.TslError) as e:
+        tsl_lib.plan_vocab(96, 64, 3)
+    assert e.value.status == tsl_lib.ERR_TP_NOT_POW2
+
+
+def test_embed_lookup_rejections(tsl_lib):
+    """Argument checks before any launch; accepted layouts are probed with
+    M == 0 (validated, nothing enqueued)."""
+    e_sh = tsl_lib.plan_vocab(1024, 64, 4)[2]  # rank 1's 256 x 64 slice
+    table, tokens, Y = 1 << 24, 1 << 26, 1 << 28
+    call = lambda **kw: tsl_lib.embed_lookup(
+        kw.get("shard", e_sh), kw.get("tdtype", tsl_lib.BF16), kw.get("table", table),
+        kw.get("ld_table", 64), kw.get("tokens", tokens), kw.get("M", 0),
+        kw.get("ydtype", tsl_lib.F32), kw.get("Y", Y), kw.get("ldy", 64))
+    call()
+    call(tdtype=tsl_lib.F32, ydtype=tsl_lib.BF16, ld_table=65, ldy=70)
+    bad = [
+        (dict(table=None), tsl_lib.ERR_INVALID_ARG),
+        (dict(tokens=None), tsl_lib.ERR_INVALID_ARG),
+        (dict(Y=None), tsl_lib.ERR_INVALID_ARG),
+        (dict(M=-1), tsl_lib.ERR_INVALID_ARG),
+        (dict(tdtype=tsl_lib.Q4G64), tsl_lib.ERR_INVALID_ARG),
+        (dict(ydtype=5), tsl_lib.ERR_INVALID_ARG),
+        (dict(ld_table=63), tsl_lib.ERR_INVALID_ARG),
+        (dict(ldy=32), tsl_lib.ERR_INVALID_ARG),
+        (dict(table=table + 1), tsl_lib.ERR_MISALIGNED),
+        (dict(tokens=tokens + 2), tsl_lib.ERR_MISALIGNED),
+        (dict(Y=Y + 2), tsl_lib.ERR_MISALIGNED),
+        (dict(M=4, Y=table + 128), tsl_lib.ERR_INVALID_ARG),       # output inside the table
+        (dict(M=4, Y=tokens - 4 * 64 * 2), tsl_lib.ERR_INVALID_ARG),  # last row over the ids
+    ]
+    for kw, code in bad:
+        with pytest.raises(tsl_lib.TslError) as e:
+            call(**kw)
+        assert e.value.status == code, kw
+    broken = tsl_lib.plan_vocab(1024, 64, 4)[2]
+    broken.k_len = 2000  # past the end of W
+    with pytest.raises(tsl_lib.TslError) as e:
+        call(shard=broken)
+    assert e.value.status == tsl_lib.ERR_INVALID_ARG
