@@ -31,7 +31,7 @@ _LIB = None
 FIELDS = ("proj", "rank", "strategy", "combine", "K", "N", "k_off", "k_len",
           "n_off", "n_len", "head_off", "head_cnt")
 PROJS = ("q", "k", "v", "o", "gate", "up", "down")
-COLUMN, ROW, REPLICATED = 0, 1, 2
+COLUMN, ROW, REPLICATED, EXPERT = 0, 1, 2, 3
 NONE, CONCAT, SUM = 0, 1, 2
 
 # error classes of oracle_plan
@@ -60,6 +60,8 @@ def lib():
         L.oracle_plan_linear.restype = ctypes.c_int
         L.oracle_plan_vocab.argtypes = [i64, i64, i32, i32, vp, i64]
         L.oracle_plan_vocab.restype = ctypes.c_int
+        L.oracle_plan_experts.argtypes = [i32, i64, i64, i32, i32, i32, vp, i64]
+        L.oracle_plan_experts.restype = i64
         L.oracle_bf16_to_f64.argtypes = [vp, vp, i64]
         L.oracle_f64_to_bf16_rne.argtypes = [vp, vp, i64]
         L.oracle_dequant_q4.argtypes = [vp, vp, vp, i64, i64, i64, vp]
@@ -111,6 +113,25 @@ def plan_vocab(vocab, hidden, tp, group=0):
     if rc != OK:
         raise OracleError(rc)
     return out
+
+
+def plan_experts(n_experts, hidden, ffn, tp, mode, group=0):
+    """MoE FFN shards: a list of (expert, rank, {"gate": spec, "up": spec,
+    "down": spec}) in rank-major, expert-ascending order."""
+    rec_len = 2 + 3 * len(FIELDS)
+    count = n_experts * (tp if mode == 1 else 1)
+    out = np.zeros((max(count, 1), rec_len), dtype=np.int64)
+    rc = lib().oracle_plan_experts(n_experts, hidden, ffn, tp, mode, group,
+                                   out.ctypes.data_as(ctypes.c_void_p), out.size)
+    if rc < 0:
+        raise OracleError(int(rc))
+    res = []
+    for row in out[:rc]:
+        sh = {p: dict(zip(FIELDS, (int(v) for v in row[2 + i * len(FIELDS):
+                                                          2 + (i + 1) * len(FIELDS)])))
+              for i, p in enumerate(("gate", "up", "down"))}
+        res.append((int(row[0]), int(row[1]), sh))
+    return res
 
 
 def spec(plan_array, rank, proj):

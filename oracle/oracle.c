@@ -233,6 +233,60 @@ int oracle_plan_vocab(int64_t vocab, int64_t hidden, int32_t tp, int32_t group, 
     return OR_OK;
 }
 
+/*
+ * Mixture-of-experts FFN shards ([mlxcel] "MoE expert parallelization").
+ * mode 0, expert parallel: expert e is held whole by rank e % tp (strategy
+ * 3, "expert"), gate/up not joined, down summed over ranks.  mode 1,
+ * within-expert: every rank holds every expert split like the dense FFN
+ * ([mlxcel] table "Standard transformer": gate/up column, down row, summed).
+ * Records: rank-major, experts ascending; each record is the expert index,
+ * the rank, then three FIELDS-long shard records (gate, up, down).
+ * Returns the number of records, or a negative error class.
+ */
+int64_t oracle_plan_experts(int32_t n_experts, int64_t hidden, int64_t ffn, int32_t tp,
+                            int32_t mode, int32_t group, int64_t *out, int64_t out_len)
+{
+    if (n_experts < 1 || hidden < 1 || ffn < 1 || tp < 1 || (mode != 0 && mode != 1) ||
+        (group != 0 && group != 64))
+        return OR_INVALID;
+    int64_t count = mode == 0 ? n_experts : (int64_t)tp * n_experts;
+    int64_t rec_len = 2 + 3 * FIELDS;
+    if (out == 0 || out_len < count * rec_len)
+        return OR_INVALID;
+    if ((tp & (tp - 1)) != 0)
+        return OR_TP_NOT_POW2;
+    if (mode == 1 && ffn % tp != 0)
+        return OR_NOT_DIVISIBLE;
+    if (group > 0 && (hidden % group != 0 || ffn % group != 0 ||
+                      (mode == 1 && (ffn / tp) % group != 0)))
+        return OR_GROUP_ALIGN;
+    int64_t k = 0;
+    for (int64_t r = 0; r < tp; ++r) {
+        for (int64_t e = 0; e < n_experts; ++e) {
+            if (mode == 0 && e % tp != r)
+                continue;
+            int64_t *rec = out + k * rec_len;
+            rec[0] = e;
+            rec[1] = r;
+            if (mode == 0) {
+                put(rec + 2, P_GATE, r, 3, C_NONE, hidden, ffn, 0, hidden, 0, ffn, -1, -1);
+                put(rec + 2 + FIELDS, P_UP, r, 3, C_NONE, hidden, ffn, 0, hidden, 0, ffn, -1, -1);
+                put(rec + 2 + 2 * FIELDS, P_DOWN, r, 3, C_SUM, ffn, hidden, 0, ffn, 0, hidden, -1,
+                    -1);
+            } else {
+                int64_t w = ffn / tp;
+                put(rec + 2, P_GATE, r, S_COLUMN, C_NONE, hidden, ffn, 0, hidden, r * w, w, -1, -1);
+                put(rec + 2 + FIELDS, P_UP, r, S_COLUMN, C_NONE, hidden, ffn, 0, hidden, r * w, w,
+                    -1, -1);
+                put(rec + 2 + 2 * FIELDS, P_DOWN, r, S_ROW, C_SUM, ffn, hidden, r * w, w, 0, hidden,
+                    -1, -1);
+            }
+            ++k;
+        }
+    }
+    return k;
+}
+
 /* bf16 -> double: a bf16 value is the upper half of an IEEE binary32. */
 void oracle_bf16_to_f64(const uint16_t *in, double *out, int64_t n)
 {

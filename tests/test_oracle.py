@@ -491,3 +491,60 @@ def test_lm_head_shards_concat_to_full_logits():
     p = oracle.plan_vocab(vocab, hidden, tp)
     parts = [oracle.shard_forward(oracle.spec(p, r, 1), X, W) for r in range(tp)]
     assert np.array_equal(oracle.combine_concat(parts), X @ W)
+
+
+# --------------------------------------------------------------------------
+# mixture-of-experts plans
+# --------------------------------------------------------------------------
+
+def test_plan_experts_page_example():
+    # mlxcel "MoE expert parallelization", Expert Parallel figure
+    for tp, ne, rank, held in golden_rows("moe_examples.txt"):
+        plan = oracle.plan_experts(int(ne), 64, 128, int(tp), 0)
+        got = [e for e, r, _ in plan if r == int(rank)]
+        assert got == [int(x) for x in held.split(",")]
+
+
+def test_plan_experts_expert_parallel_properties():
+    # expert i whole on rank i % tp, each expert exactly once, ranks past the
+    # expert count empty; gate/up not joined, down summed over ranks
+    for ne, tp in itertools.product((1, 3, 8, 64, 128), (1, 2, 4, 8)):
+        plan = oracle.plan_experts(ne, 256, 384, tp, 0, group=64)
+        assert sorted(e for e, _, _ in plan) == list(range(ne))
+        ranks = [r for _, r, _ in plan]
+        assert ranks == sorted(ranks)  # rank-major
+        for e, r, sh in plan:
+            assert r == e % tp
+            for p, (K, N, cb) in (("gate", (256, 384, oracle.NONE)), ("up", (256, 384, oracle.NONE)),
+                                  ("down", (384, 256, oracle.SUM))):
+                s = sh[p]
+                assert (s["strategy"], s["combine"], s["K"], s["N"], s["rank"]) == \
+                    (oracle.EXPERT, cb, K, N, r)
+                assert (s["k_off"], s["k_len"], s["n_off"], s["n_len"]) == (0, K, 0, N)
+            assert (sh["gate"]["proj"], sh["up"]["proj"], sh["down"]["proj"]) == (4, 5, 6)
+
+
+def test_plan_experts_within_expert_matches_dense_ffn():
+    # within-expert: each expert split like the dense FFN of the standard
+    # plan (gate/up column, down row over the same ffn block, summed)
+    ne, hidden, ffn = 5, 256, 512
+    for tp in (1, 2, 4, 8):
+        plan = oracle.plan_experts(ne, hidden, ffn, tp, 1, group=64)
+        assert len(plan) == tp * ne
+        dense = oracle.plan(hidden, 8, 8, 64, ffn, tp, 64)
+        for i, (e, r, sh) in enumerate(plan):
+            assert (e, r) == (i % ne, i // ne)
+            for p in ("gate", "up", "down"):
+                assert sh[p] == oracle.spec(dense, r, p), (tp, e, p)
+
+
+def test_plan_experts_rejections():
+    cases = [((4, 64, 128, 2, 2), oracle.INVALID), ((0, 64, 128, 2, 0), oracle.INVALID),
+             ((4, 64, 128, 3, 0), oracle.TP_NOT_POW2), ((4, 64, 100, 8, 1), oracle.NOT_DIVISIBLE),
+             ((4, 64, 96, 2, 0, 64), oracle.GROUP_ALIGN), ((4, 64, 128, 4, 1, 64),
+                                                           oracle.GROUP_ALIGN)]
+    for args, code in cases:
+        with pytest.raises(oracle.OracleError) as ei:
+            oracle.plan_experts(*args)
+        assert ei.value.code == code, args
+    oracle.plan_experts(4, 64, 128, 4, 0, 64)  # whole experts: 128 is a multiple of 64
