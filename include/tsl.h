@@ -57,7 +57,8 @@ typedef enum tsl_status {
 typedef enum tsl_strategy {
     TSL_COLUMN = 0,    /* rank r holds W[:, n_off : n_off + n_len] ("Column Parallel") */
     TSL_ROW = 1,       /* rank r holds W[k_off : k_off + k_len, :] ("Row Parallel")    */
-    TSL_REPLICATED = 2 /* every rank holds the whole W ("Replicated")                  */
+    TSL_REPLICATED = 2, /* every rank holds the whole W ("Replicated")                 */
+    TSL_EXPERT = 3      /* the whole W of one MoE expert, on its owner rank only       */
 } tsl_strategy;
 
 /* How rank outputs are joined ([mlxcel] "Communication patterns"): the
@@ -175,6 +176,44 @@ tsl_status plan_linear(int64_t K, int64_t N, int32_t tp_size, int32_t strategy,
  */
 tsl_status plan_vocab(int64_t vocab, int64_t hidden, int32_t tp_size, int32_t group_size,
                       tsl_shard *out, int64_t out_len);
+
+/* MoE sharding modes ([mlxcel] "MoE expert parallelization"). */
+typedef enum tsl_moe_mode {
+    TSL_MOE_EXPERT_PARALLEL = 0, /* expert e lives whole on rank e % tp     */
+    TSL_MOE_WITHIN_EXPERT = 1    /* every expert's FFN split like a dense one */
+} tsl_moe_mode;
+
+/* The three FFN weights of one expert as held by one rank. */
+typedef struct tsl_expert_shard {
+    int32_t expert; /* expert index e, 0 <= e < n_experts */
+    int32_t rank;   /* rank holding these shards */
+    tsl_shard gate, up, down;
+} tsl_expert_shard;
+
+/*
+ * plan_experts -- the shard plan of a mixture-of-experts FFN with
+ * n_experts experts of width expert_ffn ([mlxcel] "MoE expert
+ * parallelization", modes "Expert Parallel" and "Within-Expert Parallel").
+ *   TSL_MOE_EXPERT_PARALLEL: experts are dealt round-robin, expert e whole
+ *     on rank e % tp; its gate/up (W[hidden][expert_ffn]) and down
+ *     (W[expert_ffn][hidden]) carry strategy TSL_EXPERT; gate/up combine
+ *     NONE, down combine SUM (a token's experts sit on different ranks,
+ *     so the rank outputs are summed).  Ranks past n_experts hold none.
+ *   TSL_MOE_WITHIN_EXPERT: every rank holds every expert, whose gate/up
+ *     are column shards over [r*f/tp, (r+1)*f/tp) of expert_ffn (combine
+ *     NONE) and whose down is the matching row shard (combine SUM), the
+ *     dense FFN pattern of plan_shards.
+ * Records go rank-major, experts ascending within a rank; *n_out receives
+ * the count (n_experts, or tp * n_experts).  proj is TSL_GATE / TSL_UP /
+ * TSL_DOWN, heads -1.  Errors, in this order: TSL_ERR_INVALID_ARG (null,
+ * a size < 1, bad mode, group_size not 0 or 64, out_len short),
+ * TSL_ERR_TP_NOT_POW2, TSL_ERR_NOT_DIVISIBLE (within-expert with
+ * expert_ffn % tp), TSL_ERR_GROUP_ALIGN (group_size 64 with hidden or
+ * expert_ffn, or a within-expert slice, not a multiple of 64).  Host only.
+ */
+tsl_status plan_experts(int32_t n_experts, int64_t hidden, int64_t expert_ffn, int32_t tp_size,
+                        int32_t mode, int32_t group_size, tsl_expert_shard *out, int64_t out_len,
+                        int64_t *n_out);
 
 /*
  * pack_shard_size -- bytes of the packed, kernel-ready copy of a shard.

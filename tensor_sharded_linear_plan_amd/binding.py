@@ -38,7 +38,8 @@ _lib = ctypes.CDLL(LIBRARY)
 OK = 0
 ERR_INVALID_ARG, ERR_NOT_DIVISIBLE, ERR_TP_NOT_POW2, ERR_GROUP_ALIGN = -1, -2, -3, -4
 ERR_BUFFER_TOO_SMALL, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP = -5, -6, -7, -8
-COLUMN, ROW, REPLICATED = 0, 1, 2
+COLUMN, ROW, REPLICATED, EXPERT = 0, 1, 2, 3
+MOE_EXPERT_PARALLEL, MOE_WITHIN_EXPERT = 0, 1
 COMBINE_NONE, COMBINE_CONCAT, COMBINE_SUM = 0, 1, 2
 Q, K, V, O, GATE, UP, DOWN = range(7)
 NPROJ = 7
@@ -83,6 +84,12 @@ class Shard(ctypes.Structure):
         return "Shard(%s)" % ", ".join("%s=%d" % (f, getattr(self, f)) for f in self.FIELDS)
 
 
+class ExpertShard(ctypes.Structure):
+    """The gate/up/down shards of one expert on one rank (tsl_expert_shard)."""
+    _fields_ = [("expert", ctypes.c_int32), ("rank", ctypes.c_int32), ("gate", Shard),
+                ("up", Shard), ("down", Shard)]
+
+
 class LinearItem(ctypes.Structure):
     """One product of shard_linear_group (tsl_linear_item)."""
     _fields_ = [("shard", ctypes.POINTER(Shard)), ("packed", ctypes.c_void_p),
@@ -111,6 +118,8 @@ _lib.combine_partials.argtypes = [ctypes.c_int, _i32, ctypes.POINTER(_vp), ctype
                                   _i64, _i64, ctypes.c_int, _vp, _i64, _vp]
 _lib.combine_to_ranks.argtypes = [ctypes.c_int, _i32, ctypes.POINTER(_vp), ctypes.c_int, _i64,
                                   _i64, _i64, ctypes.c_int, ctypes.POINTER(_vp), _i64, _vp]
+_lib.plan_experts.argtypes = [_i32, _i64, _i64, _i32, _i32, _i32, ctypes.POINTER(ExpertShard),
+                              _i64, ctypes.POINTER(_i64)]
 _lib.plan_vocab.argtypes = [_i64, _i64, _i32, _i32, _P_SHARD, _i64]
 _lib.embed_lookup.argtypes = [_P_SHARD, ctypes.c_int, _vp, _i64, _vp, _i64, ctypes.c_int, _vp,
                               _i64, _vp]
@@ -121,13 +130,13 @@ _lib.tsl_last_hip_error_string.restype = ctypes.c_char_p
 for _f in ("plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
            "shard_linear_workspace_size", "shard_linear", "shard_linear_group_workspace_size",
            "shard_linear_group", "combine_partials", "combine_to_ranks", "plan_vocab",
-           "embed_lookup"):
+           "embed_lookup", "plan_experts"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
            "shard_linear_workspace_size", "shard_linear", "shard_linear_group_workspace_size",
            "shard_linear_group", "combine_partials", "combine_to_ranks", "plan_vocab",
-           "embed_lookup", "tsl_status_string", "tsl_last_hip_error_string")
+           "embed_lookup", "plan_experts", "tsl_status_string", "tsl_last_hip_error_string")
 
 
 def _check(status, where):
@@ -181,6 +190,16 @@ def plan_vocab(vocab, hidden, tp_size, group_size=0):
     out = (Shard * n)()
     _check(_lib.plan_vocab(vocab, hidden, tp_size, group_size, out, n), "plan_vocab")
     return list(out)
+
+
+def plan_experts(n_experts, hidden, expert_ffn, tp_size, mode, group_size=0):
+    """Every rank's expert shards, rank-major: a list of ExpertShard."""
+    n = n_experts * (max(int(tp_size), 1) if mode == MOE_WITHIN_EXPERT else 1)
+    out = (ExpertShard * max(n, 1))()
+    got = _i64(0)
+    _check(_lib.plan_experts(n_experts, hidden, expert_ffn, tp_size, mode, group_size, out, n,
+                             ctypes.byref(got)), "plan_experts")
+    return list(out)[:got.value]
 
 
 def embed_lookup(shard, tdtype, table, ld_table, tokens, M, ydtype, Y, ldy, stream=None):

@@ -38,6 +38,7 @@ tsl_status check_shard(const tsl_shard *s) {
             return TSL_ERR_INVALID_ARG;
         break;
     case TSL_REPLICATED:
+    case TSL_EXPERT:
         if (s->k_off != 0 || s->k_len != s->K || s->n_off != 0 || s->n_len != s->N)
             return TSL_ERR_INVALID_ARG;
         break;

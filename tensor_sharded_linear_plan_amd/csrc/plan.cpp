@@ -218,3 +218,56 @@ extern "C" tsl_status plan_vocab(int64_t vocab, int64_t hidden, int32_t tp, int3
     }
     return TSL_OK;
 }
+
+// Mixture-of-experts FFN (mlxcel "MoE expert parallelization").  Expert
+// parallel: experts dealt round-robin, expert e whole on rank e % tp, so
+// each rank runs only its own experts and the token outputs of the ranks
+// are summed.  Within-expert: each expert's gate/up/down split across all
+// ranks exactly like the dense FFN (column gate/up, row down, sum).
+extern "C" tsl_status plan_experts(int32_t n_experts, int64_t hidden, int64_t expert_ffn,
+                                   int32_t tp, int32_t mode, int32_t group_size,
+                                   tsl_expert_shard *out, int64_t out_len, int64_t *n_out) {
+    if (!out || !n_out || n_experts < 1 || hidden < 1 || expert_ffn < 1 || tp < 1)
+        return TSL_ERR_INVALID_ARG;
+    if (mode != TSL_MOE_EXPERT_PARALLEL && mode != TSL_MOE_WITHIN_EXPERT)
+        return TSL_ERR_INVALID_ARG;
+    if (group_size != 0 && group_size != 64)
+        return TSL_ERR_INVALID_ARG;
+    const bool ep = mode == TSL_MOE_EXPERT_PARALLEL;
+    const int64_t count = ep ? (int64_t)n_experts : (int64_t)tp * n_experts;
+    if (out_len < count)
+        return TSL_ERR_INVALID_ARG;
+    if (!pow2(tp))
+        return TSL_ERR_TP_NOT_POW2;
+    if (!ep && expert_ffn % tp)
+        return TSL_ERR_NOT_DIVISIBLE;
+    if (group_size &&
+        (hidden % group_size || expert_ffn % group_size || (!ep && (expert_ffn / tp) % group_size)))
+        return TSL_ERR_GROUP_ALIGN;
+    int64_t k = 0;
+    for (int32_t r = 0; r < tp; ++r) {
+        for (int32_t e = ep ? r : 0; e < n_experts; e += ep ? tp : 1) {
+            tsl_expert_shard x;
+            x.expert = e;
+            x.rank = r;
+            if (ep) {
+                x.gate = make(TSL_GATE, r, TSL_EXPERT, TSL_COMBINE_NONE, hidden, expert_ffn);
+                x.up = make(TSL_UP, r, TSL_EXPERT, TSL_COMBINE_NONE, hidden, expert_ffn);
+                x.down = make(TSL_DOWN, r, TSL_EXPERT, TSL_COMBINE_SUM, expert_ffn, hidden);
+            } else {
+                const Block b = block_of(expert_ffn, tp, r);
+                x.gate = make(TSL_GATE, r, TSL_COLUMN, TSL_COMBINE_NONE, hidden, expert_ffn);
+                x.gate.n_off = b.off;
+                x.gate.n_len = b.len;
+                x.up = x.gate;
+                x.up.proj = TSL_UP;
+                x.down = make(TSL_DOWN, r, TSL_ROW, TSL_COMBINE_SUM, expert_ffn, hidden);
+                x.down.k_off = b.off;
+                x.down.k_len = b.len;
+            }
+            out[k++] = x;
+        }
+    }
+    *n_out = k;
+    return TSL_OK;
+}

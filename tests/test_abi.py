@@ -28,7 +28,8 @@ def test_library_exports_every_declared_symbol(tsl_lib):
                           "shard_linear_workspace_size", "shard_linear",
                           "shard_linear_group_workspace_size", "shard_linear_group",
                           "combine_partials", "combine_to_ranks", "plan_vocab",
-                          "embed_lookup", "tsl_status_string", "tsl_last_hip_error_string"}
+                          "embed_lookup", "plan_experts", "tsl_status_string",
+                          "tsl_last_hip_error_string"}
     lib = ctypes.CDLL(tsl_lib.LIBRARY)
     for n in names:
         assert hasattr(lib, n), n
@@ -460,4 +461,27 @@ def test_embed_lookup_rejections(tsl_lib):
     broken.k_len = 2000  # past the end of W
     with pytest.raises(tsl_lib.TslError) as e:
         call(shard=broken)
+    assert e.value.status == tsl_lib.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_plan_experts_vs_oracle(tsl_lib, mode):
+    for ne, hidden, ffn, tp, group in ((128, 2048, 768, 4, 64), (8, 4096, 14336, 4, 0),
+                                       (3, 64, 128, 8, 64), (4, 64, 100, 8, 0),
+                                       (4, 64, 96, 2, 64), (5, 64, 128, 3, 0)):
+        try:
+            want = oracle.plan_experts(ne, hidden, ffn, tp, mode, group)
+        except oracle.OracleError as e:
+            with pytest.raises(tsl_lib.TslError) as got:
+                tsl_lib.plan_experts(ne, hidden, ffn, tp, mode, group)
+            assert got.value.status == e.code
+            continue
+        got = tsl_lib.plan_experts(ne, hidden, ffn, tp, mode, group)
+        assert len(got) == len(want)
+        for g, (e, r, sh) in zip(got, want):
+            assert (g.expert, g.rank) == (e, r)
+            for p in ("gate", "up", "down"):
+                assert getattr(g, p).as_tuple() == tuple(sh[p][f] for f in oracle.FIELDS)
+    with pytest.raises(tsl_lib.TslError) as e:
+        tsl_lib.plan_experts(4, 64, 128, 2, 7)
     assert e.value.status == tsl_lib.ERR_INVALID_ARG
