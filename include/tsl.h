@@ -322,9 +322,15 @@ tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, const void *pa
  * combine_partials(SUM).  All items of a set have the same n_len; the first
  * item's Y, ldy and ydtype apply and its accumulate must be 0; the Y, ldy,
  * ydtype and accumulate of the other items are ignored.  The last item of
- * a call has sum_next = 0.  reserved must be 0.  The products of a set go
- * to binary32 partials in the workspace (M x n_len x 4 bytes each, counted
- * by shard_linear_group_workspace_size); one more launch adds them.
+ * a call has sum_next = 0.  The products of a set go to binary32 partials
+ * in the workspace (rows x n_len x 4 bytes each, counted by
+ * shard_linear_group_workspace_size); one more launch adds them.
+ *
+ * rows: the item's token rows, 1 <= rows <= M (0 means M): it reads rows
+ * [0, rows) of X and writes rows [0, rows) of Y.  Items of different row
+ * counts share one launch -- the per-expert products of a mixture-of-
+ * experts layer, each over the tokens routed to its expert ([mlxcel] "MoE
+ * expert parallelization").  The members of a sum set have equal rows.
  */
 typedef struct {
     const tsl_shard *shard;
@@ -337,21 +343,21 @@ typedef struct {
     int32_t ydtype;
     int32_t accumulate;
     int32_t sum_next;
-    int32_t reserved;
+    int32_t rows;
 } tsl_linear_item;
 
 /*
  * shard_linear_group_workspace_size -- workspace bytes shard_linear_group
- * needs for these items (only their shards and sum_next are read), weight
- * type and M.  An upper bound: a call whose items read the same X (same
+ * needs for these items (only their shards, sum_next and rows are read),
+ * weight type and M.  An upper bound: a call whose items read the same X (same
  * pointer, ldx and k_len) shares one activation copy and uses less.
  */
 tsl_status shard_linear_group_workspace_size(int32_t n_items, const tsl_linear_item *items,
                                              tsl_dtype wdtype, int64_t M, size_t *bytes);
 
 /*
- * shard_linear_group -- several shard products with the same M, weight and
- * activation types in one pass: the projections that read the same input
+ * shard_linear_group -- several shard products with the same weight and
+ * activation types, each over M rows or its own row count, in one pass: the projections that read the same input
  * (q, k and v, or gate and up, of a column-parallel block; [wiki]
  * "Details" §1, [mlxcel] "Column Parallel"), or the shards of every rank
  * when all ranks' shares run on one GPU.  Each item computes what
@@ -360,7 +366,8 @@ tsl_status shard_linear_group_workspace_size(int32_t n_items, const tsl_linear_i
  * equal to separate calls).  The items run in no particular order: no
  * item's Y may share an element with another item's Y or any item's X
  * (TSL_ERR_INVALID_ARG); column blocks of one output matrix with a common
- * ldy are fine.  Up to 32 items share one kernel launch;
+ * ldy are fine.  The kernels are chosen by M (the largest row count).
+ * Up to 32 items share one kernel launch;
  * 1 <= n_items <= 4096.  items is a HOST array.
  * Errors: as shard_linear, for any item.
  */

@@ -96,7 +96,7 @@ class LinearItem(ctypes.Structure):
                 ("packed_bytes", ctypes.c_size_t), ("X", ctypes.c_void_p),
                 ("ldx", ctypes.c_int64), ("Y", ctypes.c_void_p), ("ldy", ctypes.c_int64),
                 ("ydtype", ctypes.c_int32), ("accumulate", ctypes.c_int32),
-                ("sum_next", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("sum_next", ctypes.c_int32), ("rows", ctypes.c_int32)]
 
 
 _i32, _i64, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
@@ -251,7 +251,7 @@ def _items(items):
         arr[i] = LinearItem(ctypes.pointer(sh), _ptr(it["packed"]), it["packed_bytes"],
                             _ptr(it["X"]), it["ldx"], _ptr(it.get("Y")), it.get("ldy", 0),
                             it.get("ydtype", F32), it.get("accumulate", 0),
-                            it.get("sum_next", 0), it.get("reserved", 0))
+                            it.get("sum_next", 0), it.get("rows", 0))
     arr._keep = keep
     return arr, len(items)
 

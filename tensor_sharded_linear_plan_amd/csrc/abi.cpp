@@ -207,6 +207,7 @@ tsl_status check_item(const tsl_shard *shard, tsl_dtype wdtype, const void *pack
     if (!use_skinny(wdtype, M) && (ldx >= kPrefillMaxStride || g.Kpad >= kPrefillMaxStride))
         return TSL_ERR_UNSUPPORTED;
     out->g = g;
+    out->M = M;
     out->packed = packed;
     out->X = X;
     out->ldx = ldx;
@@ -268,7 +269,7 @@ size_t split_sets(std::vector<LinearItem> *items, int64_t M, char *ws) {
                 L.accumulate = 0;
                 L.set_len = 1;
                 L.set_pos = 0;
-                off += ((size_t)M * (size_t)L.g.Ns * 4 + 255) / 256 * 256;
+                off += ((size_t)L.M * (size_t)L.g.Ns * 4 + 255) / 256 * 256;
             }
         }
         i += len;
@@ -366,7 +367,7 @@ tsl_status run_group(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_
             const float *p[kMaxParts];
             for (int r = 0; r < L.set_len; ++r)
                 p[r] = static_cast<const float *>(items[i + r].Y);
-            e = launch_combine_sum(L.set_len, p, M, L.g.Ns, L.g.Ns, L.ydtype, L.Y, L.ldy, s);
+            e = launch_combine_sum(L.set_len, p, L.M, L.g.Ns, L.g.Ns, L.ydtype, L.Y, L.ldy, s);
             if (e != hipSuccess)
                 return from_hip(e);
             continue;
@@ -375,6 +376,7 @@ tsl_status run_group(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_
         for (int r = 0; r < L.set_len; ++r)
             sp.parts[r] = static_cast<const float *>(items[i + r].Y);
         sp.n_parts = L.set_len;
+        sp.M = L.M;
         sp.n = L.g.Ns;
         sp.Y = L.Y;
         sp.ldy = L.ldy;
@@ -399,7 +401,7 @@ tsl_status gather(int32_t n_items, const tsl_linear_item *items, tsl_dtype wdtyp
     for (int32_t i = 0; i < n_items; ++i) {
         const tsl_linear_item &it = items[i];
         const bool member = i > first;
-        if ((it.sum_next != 0 && it.sum_next != 1) || it.reserved != 0)
+        if ((it.sum_next != 0 && it.sum_next != 1) || it.rows < 0 || it.rows > M)
             return TSL_ERR_INVALID_ARG;
         if (it.sum_next && i == n_items - 1)
             return TSL_ERR_INVALID_ARG;
@@ -409,7 +411,8 @@ tsl_status gather(int32_t n_items, const tsl_linear_item *items, tsl_dtype wdtyp
             return st;
         LinearItem &L = (*out)[i];
         L.set_pos = i - first;
-        if (member && L.g.Ns != (*out)[first].g.Ns)
+        L.M = it.rows ? it.rows : M;
+        if (member && (L.g.Ns != (*out)[first].g.Ns || L.M != (*out)[first].M))
             return TSL_ERR_INVALID_ARG;
         if (!it.sum_next) { // the set [first, i] is complete
             (*out)[first].set_len = i - first + 1;
@@ -435,10 +438,10 @@ tsl_status gather(int32_t n_items, const tsl_linear_item *items, tsl_dtype wdtyp
         for (int32_t j = 0; j < n_items; ++j) {
             const LinearItem &b = (*out)[j];
             const size_t eb = b.ydtype == TSL_F32 ? 4 : 2;
-            if (matrices_overlap(a.Y, M, a.g.Ns, a.ldy, ea, b.X, M, b.g.Ks, b.ldx, xe))
+            if (matrices_overlap(a.Y, a.M, a.g.Ns, a.ldy, ea, b.X, b.M, b.g.Ks, b.ldx, xe))
                 return TSL_ERR_INVALID_ARG;
             if (j > i && b.Y &&
-                matrices_overlap(a.Y, M, a.g.Ns, a.ldy, ea, b.Y, M, b.g.Ns, b.ldy, eb))
+                matrices_overlap(a.Y, a.M, a.g.Ns, a.ldy, ea, b.Y, b.M, b.g.Ns, b.ldy, eb))
                 return TSL_ERR_INVALID_ARG;
         }
     }
@@ -455,6 +458,7 @@ extern "C" tsl_status shard_linear_workspace_size(const tsl_shard *shard, tsl_dt
     tsl_status st = geometry(*shard, wdtype, &items[0].g);
     if (st != TSL_OK)
         return st;
+    items[0].M = M;
     *bytes = group_workspace(items, wdtype, M);
     return TSL_OK;
 }
@@ -486,11 +490,13 @@ extern "C" tsl_status shard_linear_group_workspace_size(int32_t n_items,
     std::vector<LinearItem> v(n_items);
     int32_t first = 0;
     for (int32_t i = 0; i < n_items; ++i) {
-        if (!items[i].shard || (items[i].sum_next != 0 && items[i].sum_next != 1))
+        if (!items[i].shard || (items[i].sum_next != 0 && items[i].sum_next != 1) ||
+            items[i].rows < 0 || items[i].rows > M)
             return TSL_ERR_INVALID_ARG;
         tsl_status st = geometry(*items[i].shard, wdtype, &v[i].g);
         if (st != TSL_OK)
             return st;
+        v[i].M = items[i].rows ? items[i].rows : M;
         v[i].set_pos = i - first;
         if (!items[i].sum_next || i == n_items - 1) {
             v[first].set_len = i - first + 1;

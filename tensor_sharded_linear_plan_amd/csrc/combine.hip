@@ -111,6 +111,7 @@ struct SumSet {
     const float *p[kSetParts];
     void *Y;
     int64_t ldy, n;
+    int64_t M;           // rows of this set
     int32_t n_parts, y_bf16;
     int32_t start, pad_; // first workgroup of the set
 };
@@ -120,7 +121,7 @@ struct SumSets {
 };
 
 template <bool VEC>
-__global__ void __launch_bounds__(256) sum_sets_kernel(SumSets g, int64_t M) {
+__global__ void __launch_bounds__(256) sum_sets_kernel(SumSets g) {
     const int bid = blockIdx.x;
     int lo = 0, hi = g.n - 1;
     while (lo < hi) {
@@ -135,7 +136,7 @@ __global__ void __launch_bounds__(256) sum_sets_kernel(SumSets g, int64_t M) {
     const int64_t j = ((int64_t)(bid - st.start) * 256 + threadIdx.x) * E;
     if (j >= st.n)
         return;
-    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+    for (int64_t m = blockIdx.y; m < st.M; m += gridDim.y) {
         const int64_t off = m * st.n + j;
         if constexpr (VEC) {
             f32x4 acc = *reinterpret_cast<const f32x4 *>(st.p[0] + off);
@@ -321,6 +322,7 @@ hipError_t launch_sum_sets(int n_sets, const SumSpec *sets, int64_t M, hipStream
             st.Y = sp.Y;
             st.ldy = sp.ldy;
             st.n = sp.n;
+            st.M = sp.M;
             st.n_parts = sp.n_parts;
             st.y_bf16 = sp.ydtype == TSL_BF16;
             st.start = (int32_t)blocks;
@@ -328,9 +330,9 @@ hipError_t launch_sum_sets(int n_sets, const SumSpec *sets, int64_t M, hipStream
         }
         dim3 grid((unsigned)blocks, rows_grid(M));
         if (vec)
-            hipLaunchKernelGGL(sum_sets_kernel<true>, grid, dim3(256), 0, stream, g, M);
+            hipLaunchKernelGGL(sum_sets_kernel<true>, grid, dim3(256), 0, stream, g);
         else
-            hipLaunchKernelGGL(sum_sets_kernel<false>, grid, dim3(256), 0, stream, g, M);
+            hipLaunchKernelGGL(sum_sets_kernel<false>, grid, dim3(256), 0, stream, g);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;

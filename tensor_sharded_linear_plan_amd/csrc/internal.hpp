@@ -47,13 +47,14 @@ hipError_t launch_combine_concat(int n_parts, const void *const *parts, size_t e
                                  int64_t M, int64_t n_each, int64_t ld_part, void *Y, int64_t ldy,
                                  hipStream_t stream);
 // Rank sums of several sum sets in one launch: set i adds its n_parts
-// contiguous [M][n] binary32 parts in order into Y (row stride ldy, F32 or
-// BF16).  n_parts <= kSetParts.
+// contiguous [M_i][n] binary32 parts in order into Y (row stride ldy, F32 or
+// BF16).  n_parts <= kSetParts; M is the largest M_i.
 constexpr int kSetParts = 8;
 constexpr int kMaxSets = 16;
 struct SumSpec {
     const float *parts[kSetParts];
     int n_parts = 0;
+    int64_t M = 0; // rows of this set
     int64_t n = 0;
     void *Y = nullptr;
     int64_t ldy = 0;
@@ -96,6 +97,8 @@ struct LinearItem {
     // item its position in the set
     int set_len = 1;
     int set_pos = 0;
+    // token rows of this product (the call's M unless the item sets its own)
+    int64_t M = 0;
 };
 
 // Items per kernel launch (the item table travels in the kernel arguments);
@@ -112,7 +115,7 @@ struct SkinnyPlan {
     int xstr = 0;          // ... LDS bytes per activation row
     int xsum_off = 0;      // ... LDS offset of the 4-bit group sums
     size_t lds_bytes = 0;  // dynamic LDS per workgroup
-    int64_t m_blocks = 0;
+    std::vector<int64_t> m_blocks; // per item: row blocks of 16 * mt
     // per item: workgroups across its columns, k-split across workgroups
     // (partials go to the workspace) and the byte offset of its partials
     std::vector<int64_t> n_groups;

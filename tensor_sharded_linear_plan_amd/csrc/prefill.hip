@@ -29,8 +29,8 @@
 // the copy) in the workspace.  bf16 activations are copied, zero-padded,
 // only when K is not a multiple of 64.  Accumulation is binary32.
 //
-// One launch serves a group of shard products with the same M and types;
-// the item table rides in the kernel arguments.  Each item's tiles take a
+// One launch serves a group of shard products of the same types, each over
+// its own rows; the item table rides in the kernel arguments.  Each item's tiles take a
 // run of workgroups starting at a multiple of 8.  Workgroups reach the 8
 // XCDs round-robin, so XCD x takes the x-th eighth of the item's tiles in
 // band order (bands of up to 8 m-blocks, m fastest), a compact patch whose
@@ -63,6 +63,7 @@ struct GemmItem {
     int32_t T8;        // tiles per XCD, ceil(MB * NB / 8)
     int32_t start;     // first workgroup (a multiple of 8)
     int32_t accumulate, y_bf16;
+    int64_t M;         // rows of this item
 };
 
 struct GemmGroup {
@@ -152,7 +153,7 @@ gemm_kernel(GemmGroup grp) {
             hi = mid - 1;
     }
     const GemmItem &a = grp.it[lo];
-    const int64_t M = grp.M;
+    const int64_t M = a.M;
     const int local = bid - a.start;
     const int t = (local & 7) * a.T8 + (local >> 3); // tile in band order
     if (t >= a.MB * a.NB)
@@ -435,26 +436,27 @@ double variant_cost(const Variant &v, const LinearItem *items, int n, int64_t M)
     const double l2 = 4096.0 * (v.bm + v.bn) * 2 / flops / 40.0;
     double pen = lds > l2 ? lds : l2;
     pen = pen > 1.0 ? pen : 1.0;
-    const int64_t mbk = (M + v.bm - 1) / v.bm;
+    (void)M;
+    auto mbk = [&](int i) { return (items[i].M + v.bm - 1) / v.bm; };
     std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
     for (int i = 0; i < 256; ++i)
         cu.push(0.0);
     double span = 0.0;
     int64_t tiles = 0;
     for (int i = 0; i < n; ++i)
-        tiles += mbk * ((items[i].g.Ns + v.bn - 1) / v.bn);
+        tiles += mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn);
     if (tiles > 16384) { // large: every CU busy to the end, to a tile
         double work = 0.0, longest = 0.0;
         for (int i = 0; i < n; ++i) {
             const double len = (double)kpad64(items[i].g.Ks) / 64.0;
-            work += (double)(mbk * ((items[i].g.Ns + v.bn - 1) / v.bn)) * len;
+            work += (double)(mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn)) * len;
             longest = len > longest ? len : longest;
         }
         span = work / 256.0 + longest;
     } else {
         for (int i = 0; i < n; ++i) {
             const double len = (double)kpad64(items[i].g.Ks) / 64.0;
-            const int64_t T = mbk * ((items[i].g.Ns + v.bn - 1) / v.bn);
+            const int64_t T = mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn);
             for (int64_t t = 0; t < T; ++t) {
                 const double f = cu.top() + len;
                 cu.pop();
@@ -485,7 +487,7 @@ PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64
     }
     // workspace: binary16 weight fragments of 4-bit items; activation
     // copies (binary16 for 4-bit items, zero-padded bf16 for ragged-K bf16
-    // items), one per distinct (X, ldx, K) -- items without a known X
+    // items), one per distinct (X, ldx, K, rows) -- items without a known X
     // (sizing) never share
     best.w_off.assign(n, 0);
     best.x_off.assign(n, 0);
@@ -501,14 +503,14 @@ PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64
             int first = i;
             for (int j = 0; j < i && items[i].X; ++j)
                 if (items[j].X == items[i].X && items[j].ldx == items[i].ldx &&
-                    items[j].g.Ks == g.Ks && best.x_first[j] == j) {
+                    items[j].g.Ks == g.Ks && items[j].M == items[i].M && best.x_first[j] == j) {
                     first = j;
                     break;
                 }
             best.x_first[i] = first;
             if (first == i) {
                 best.x_off[i] = off;
-                off += ((size_t)M * (size_t)kpad64(g.Ks) * 2 + 255) / 256 * 256;
+                off += ((size_t)items[i].M * (size_t)kpad64(g.Ks) * 2 + 255) / 256 * 256;
             } else {
                 best.x_off[i] = best.x_off[first];
             }
@@ -546,7 +548,7 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
             a.ldx_in = L.ldx;
             a.w_chunks = q4 ? g.Nt * g.KT * 64 : 0;
             a.Kpad = (int32_t)kpad64(g.Ks);
-            a.x_units = xcopy ? M * (a.Kpad / 8) : 0;
+            a.x_units = xcopy ? L.M * (a.Kpad / 8) : 0;
             a.KB = (int32_t)g.KT;
             a.Gs = (int32_t)(g.Ks / 64);
             a.Ks = (int32_t)g.Ks;
@@ -581,7 +583,8 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
             a.Nt16 = (int32_t)g.Nt;
             a.KT32 = (int32_t)(q4 ? g.KT * 4 : g.KT);
             a.KT64 = (int32_t)(kpad64(g.Ks) / 64);
-            a.MB = (int32_t)((M + p.bm - 1) / p.bm);
+            a.M = L.M;
+            a.MB = (int32_t)((L.M + p.bm - 1) / p.bm);
             a.NB = (int32_t)((g.Ns + p.bn - 1) / p.bn);
             a.T8 = (a.MB * a.NB + 7) / 8;
             a.start = (int32_t)blocks;
@@ -602,7 +605,7 @@ int64_t prefill_blocks(const PrefillPlan &p, const LinearItem *items, int n, int
     for (int c0 = 0; c0 < n; c0 += kGroupMax) {
         int64_t blocks = 0;
         for (int i = c0; i < n && i < c0 + kGroupMax; ++i) {
-            const int64_t T = ((M + p.bm - 1) / p.bm) * ((items[i].g.Ns + p.bn - 1) / p.bn);
+            const int64_t T = ((items[i].M + p.bm - 1) / p.bm) * ((items[i].g.Ns + p.bn - 1) / p.bn);
             blocks += 8 * ((T + 7) / 8);
         }
         most = blocks > most ? blocks : most;

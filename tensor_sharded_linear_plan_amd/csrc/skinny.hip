@@ -46,6 +46,7 @@ struct SkinnyItem {
     int32_t ks, n_groups;
     int32_t start;       // first workgroup of this item
     int32_t accumulate, y_bf16;
+    int64_t M;           // rows of this item
 };
 
 struct SkinnyGroup {
@@ -94,7 +95,7 @@ __global__ void __launch_bounds__(256) f32_kernel(SkinnyGroup grp) {
             hi = mid - 1;
     }
     const SkinnyItem &a = grp.it[lo];
-    const int64_t M = grp.M;
+    const int64_t M = a.M;
     const int u = bid - a.start;
     const int64_t nt = u % a.n_groups;
     const int ksi = (u / a.n_groups) % a.ks;
@@ -244,7 +245,7 @@ __global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
             hi = mid - 1;
     }
     const SkinnyItem &a = grp.it[lo];
-    const int64_t M = grp.M;
+    const int64_t M = a.M;
     const int u = bid - a.start;
     const int tg = u % a.n_groups;
     const int ksi = (u / a.n_groups) % a.ks;
@@ -569,7 +570,9 @@ SkinnyPlan skinny_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t
     SkinnyPlan p;
     const int64_t rows = M < 64 ? M : 64;
     p.mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
-    p.m_blocks = (M + 16 * p.mt - 1) / (16 * p.mt);
+    p.m_blocks.resize(n);
+    for (int i = 0; i < n; ++i)
+        p.m_blocks[i] = (items[i].M + 16 * p.mt - 1) / (16 * p.mt);
     p.stream = wdtype != TSL_F32;
     p.ks.resize(n);
     p.ws_off.resize(n);
@@ -583,7 +586,7 @@ SkinnyPlan skinny_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t
         int64_t base = 0;
         for (int i = 0; i < n; ++i) {
             p.n_groups[i] = (items[i].g.Nt + 4 * p.ntw - 1) / (4 * p.ntw);
-            base += p.n_groups[i] * p.m_blocks;
+            base += p.n_groups[i] * p.m_blocks[i];
         }
         const int64_t ks_want = base > 0 ? (512 + base - 1) / base : 1;
         for (int i = 0; i < n; ++i) {
@@ -618,7 +621,7 @@ SkinnyPlan skinny_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t
         int64_t base = 0;
         for (int i = 0; i < n; ++i) {
             p.n_groups[i] = items[i].g.Nt;
-            base += p.n_groups[i] * p.m_blocks;
+            base += p.n_groups[i] * p.m_blocks[i];
         }
         const int64_t ks_want = base > 0 ? (200 + base - 1) / base : 1;
         for (int i = 0; i < n; ++i) {
@@ -633,8 +636,8 @@ SkinnyPlan skinny_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t
     for (int i = 0; i < n; ++i) {
         p.ws_off[i] = off;
         if (p.ks[i] > 1)
-            off += ((size_t)p.ks[i] * (size_t)M * (size_t)items[i].g.Ns * sizeof(float) + 255) /
-                   256 * 256;
+            off += ((size_t)p.ks[i] * (size_t)items[i].M * (size_t)items[i].g.Ns * sizeof(float) +
+                    255) / 256 * 256;
     }
     p.ws_bytes = off;
     return p;
@@ -646,7 +649,7 @@ int64_t skinny_blocks(const SkinnyPlan &p, const LinearItem *items, int n) {
     for (int c0 = 0; c0 < n; c0 += kGroupMax) {
         int64_t blocks = 0;
         for (int i = c0; i < n && i < c0 + kGroupMax; ++i)
-            blocks += p.n_groups[i] * p.ks[i] * p.m_blocks;
+            blocks += p.n_groups[i] * p.ks[i] * p.m_blocks[i];
         most = blocks > most ? blocks : most;
     }
     return most;
@@ -684,8 +687,9 @@ hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, ts
             a.n_groups = (int32_t)p.n_groups[c0 + i];
             a.accumulate = L.accumulate;
             a.y_bf16 = L.ydtype == TSL_BF16;
+            a.M = L.M;
             a.start = (int32_t)blocks;
-            blocks += (int64_t)a.n_groups * a.ks * p.m_blocks;
+            blocks += (int64_t)a.n_groups * a.ks * p.m_blocks[c0 + i];
         }
         if (p.lds_bytes > 64 * 1024) {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
@@ -702,7 +706,7 @@ hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, ts
             const SkinnyItem &a = grp.it[i];
             if (a.ks == 1)
                 continue;
-            e = launch_splitk_reduce(a.P, a.ks, M, a.Ns, items[c0 + i].ydtype, a.Y, a.ldy,
+            e = launch_splitk_reduce(a.P, a.ks, a.M, a.Ns, items[c0 + i].ydtype, a.Y, a.ldy,
                                      a.accumulate, stream);
             if (e != hipSuccess)
                 return e;

@@ -43,7 +43,7 @@ def test_shard_struct_layout_matches_header(tsl_lib):
     # tsl_linear_item: seven 8-byte fields, then four int32
     assert ctypes.sizeof(tsl_lib.LinearItem) == 72
     assert tsl_lib.LinearItem.ldy.offset == 48 and tsl_lib.LinearItem.ydtype.offset == 56
-    assert tsl_lib.LinearItem.sum_next.offset == 64
+    assert tsl_lib.LinearItem.sum_next.offset == 64 and tsl_lib.LinearItem.rows.offset == 68
 
 
 def _lib_plan(tsl_lib, hidden, hq, hkv, hd, ffn, tp, group=0):
@@ -352,10 +352,16 @@ def test_sum_set_rules(tsl_lib):
         w + tp * M * N * 4
     # decode: the same partials (the products themselves need no workspace here)
     assert tsl_lib.shard_linear_group_workspace_size(items(), tsl_lib.Q4G64, 4) == tp * 4 * N * 4
+    # a set of 3-row items inside a 4-row call: partials of 3 rows
+    rows3 = items({r: dict(rows=3) for r in range(tp)})
+    assert tsl_lib.shard_linear_group_workspace_size(rows3, tsl_lib.Q4G64, 4) == \
+        tp * ((3 * N * 4 + 255) // 256 * 256)
     call = lambda its, M=M: tsl_lib.shard_linear_group(its, tsl_lib.Q4G64, tsl_lib.BF16, M)
     bad = [items({3: dict(sum_next=1)}),                 # the last item links on
            items({1: dict(sum_next=2)}),
-           items({2: dict(reserved=1)}),
+           items({2: dict(rows=1)}),                     # members' rows differ
+           items({1: dict(rows=M + 1)}),                 # more rows than M
+           items({1: dict(rows=-1)}),
            items({0: dict(accumulate=1)}),               # a set's output cannot accumulate
            items({0: dict(Y=None)})]
     for its in bad:
