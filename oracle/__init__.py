@@ -312,3 +312,58 @@ def all_gather(parts, n_ranks):
     """Every rank's buffer after an all-gather: the concatenated tensor."""
     full = combine_concat(parts)
     return [full.copy() for _ in range(n_ranks)]
+
+
+def moe_dispatch(topk, experts):
+    """Rows of a rank's expert products (mlxcel manual "MoE expert
+    parallelization": the router runs everywhere, each rank runs only the
+    experts it holds).  topk is [T][k] expert ids; experts lists the rank's
+    experts in the order their products are laid out.  A row is one
+    (token, choice) slot s = t*k + j whose expert the rank holds; the rows
+    of expert experts[i] are its slots in ascending order and come after
+    those of experts[:i].  Returns (offsets [n+1], row_slot [rows],
+    slot_row [T*k], -1 for slots of other ranks' experts)."""
+    topk = np.asarray(topk)
+    T, k = topk.shape
+    offsets, row_slot = [0], []
+    slot_row = np.full(T * k, -1, dtype=np.int64)
+    for e in experts:
+        for t in range(T):
+            for j in range(k):
+                if topk[t, j] == e:
+                    slot_row[t * k + j] = len(row_slot)
+                    row_slot.append(t * k + j)
+        offsets.append(len(row_slot))
+    return np.array(offsets, dtype=np.int64), np.array(row_slot, dtype=np.int64), slot_row
+
+
+def moe_combine(y_slots, weights, slot_mask=None):
+    """A token's MoE output: sum_j weights[t][j] * y_slots[t][j] over its k
+    choices (those in slot_mask when given), j ascending, in double."""
+    y_slots = np.asarray(y_slots, dtype=np.float64)
+    T, k = weights.shape
+    out = np.zeros((T, y_slots.shape[-1]))
+    for t in range(T):
+        for j in range(k):
+            if slot_mask is None or slot_mask[t, j]:
+                out[t] += float(weights[t, j]) * y_slots[t, j]
+    return out
+
+
+def moe_linear_slots(x_slots, topk, shard_weight, n):
+    """y[t][j] = x_slots[t][j] . W_e for e = topk[t][j], where
+    shard_weight(e) is the rank's block (n output columns) of expert e's
+    weight, or None when the rank does not hold e (y = 0), and x_slots[t][j]
+    the matching input block; in double."""
+    topk = np.asarray(topk)
+    T, k = topk.shape
+    out = np.zeros((T, k, n))
+    for e in sorted(set(int(v) for v in topk.ravel())):
+        W = shard_weight(e)
+        if W is None:
+            continue
+        sel = [(t, j) for t in range(T) for j in range(k) if topk[t, j] == e]
+        ys = gemm(np.stack([x_slots[t][j] for t, j in sel]), W)
+        for (t, j), y in zip(sel, ys):
+            out[t, j] = y
+    return out

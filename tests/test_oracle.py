@@ -548,3 +548,94 @@ def test_plan_experts_rejections():
             oracle.plan_experts(*args)
         assert ei.value.code == code, args
     oracle.plan_experts(4, 64, 128, 4, 0, 64)  # whole experts: 128 is a multiple of 64
+
+
+def test_moe_dispatch_worked_and_brute_force():
+    # hand-worked: tokens pick (0, 2), (2, 1), (0, 0); the rank holds 2 and 0
+    off, row_slot, slot_row = oracle.moe_dispatch([[0, 2], [2, 1], [0, 0]], [2, 0])
+    assert off.tolist() == [0, 2, 5]
+    assert row_slot.tolist() == [1, 2, 0, 4, 5]
+    assert slot_row.tolist() == [2, 0, 1, -1, 3, 4]
+    rng = np.random.default_rng(5)
+    for T, k, E in ((1, 1, 1), (7, 2, 8), (40, 8, 16), (33, 3, 5)):
+        topk = rng.integers(0, E, (T, k))
+        held = [e for e in rng.permutation(E)[: max(1, E // 2)]]
+        off, row_slot, slot_row = oracle.moe_dispatch(topk, held)
+        flat = topk.ravel()
+        assert off[0] == 0 and np.all(np.diff(off) >= 0)
+        for i, e in enumerate(held):
+            seg = row_slot[off[i]:off[i + 1]]
+            assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+            assert len(seg) == np.count_nonzero(flat == e)
+        owned = np.isin(flat, held)
+        assert np.array_equal(np.sort(row_slot), np.nonzero(owned)[0])
+        assert np.all(slot_row[~owned] == -1)
+        assert np.array_equal(row_slot[slot_row[owned]], np.nonzero(owned)[0])
+
+
+def _moe_case(T=9, k=2, E=6, K=64, N=40, seed=21):
+    rng = np.random.default_rng(seed)
+    topk = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    wts = rng.random((T, k))
+    wts /= wts.sum(axis=1, keepdims=True)
+    X = rng.standard_normal((T, K))
+    W = [rng.standard_normal((K, N)) for _ in range(E)]
+    return topk, wts, X, W
+
+
+def test_moe_combine_and_slots_closed_forms():
+    topk, wts, X, W = _moe_case()
+    T, k = topk.shape
+    xs = np.repeat(X[:, None, :], k, axis=1)
+    ys = oracle.moe_linear_slots(xs, topk, lambda e: W[e], W[0].shape[1])
+    # per token with numpy matmul: sum_j w_tj x_t W_{e_tj}
+    want = np.stack([sum(wts[t, j] * (X[t] @ W[topk[t, j]]) for j in range(k))
+                     for t in range(T)])
+    assert np.allclose(oracle.moe_combine(ys, wts), want, rtol=1e-12, atol=1e-12)
+    # one-hot weights pick one choice; equal slot values with unit weight
+    # sums give that value back
+    one = np.zeros_like(wts)
+    one[:, 1] = 1.0
+    assert np.array_equal(oracle.moe_combine(ys, one), ys[:, 1])
+    same = np.repeat(ys[:, :1], k, axis=1)
+    assert np.allclose(oracle.moe_combine(same, wts), ys[:, 0], rtol=1e-12, atol=1e-12)
+    # an expert nobody holds contributes zero
+    z = oracle.moe_linear_slots(xs, topk, lambda e: None, 40)
+    assert z.shape == (T, k, 40) and not z.any()
+
+
+@pytest.mark.parametrize("tp", [1, 2, 4])
+def test_moe_sharded_outputs_sum_to_unsharded(tp):
+    # expert parallel: each slot is computed on exactly one rank, so the
+    # rank outputs add up to the unsharded MoE; within-expert: the row
+    # shards of down add up, the column shards of gate concatenate
+    topk, wts, X, W = _moe_case(E=8)
+    T, k = topk.shape
+    K, N = W[0].shape
+    xs = np.repeat(X[:, None, :], k, axis=1)
+    full = oracle.moe_combine(oracle.moe_linear_slots(xs, topk, lambda e: W[e], N), wts)
+    ep = oracle.plan_experts(8, N, K, tp, 0)  # down: W[K = ffn][N = hidden]
+    total = np.zeros_like(full)
+    for r in range(tp):
+        held = {e for e, rr, _ in ep if rr == r}
+        ys = oracle.moe_linear_slots(xs, topk, lambda e: W[e] if e in held else None, N)
+        total += oracle.moe_combine(ys, wts, np.isin(topk, list(held)))
+    assert np.allclose(total, full, rtol=1e-12, atol=1e-12)
+    wep = oracle.plan_experts(8, N, K, tp, 1)
+    total = np.zeros_like(full)
+    for r in range(tp):
+        sh = next(s for e, rr, s in wep if rr == r)["down"]
+        xr = xs[:, :, sh["k_off"]:sh["k_off"] + sh["k_len"]]
+        ys = oracle.moe_linear_slots(xr, topk, lambda e: oracle.slice_weight(W[e], sh), N)
+        total += oracle.moe_combine(ys, wts)
+    assert np.allclose(total, full, rtol=1e-12, atol=1e-12)
+    # gate W[hidden = N][ffn = K] of expert e: the transpose of its down
+    xg = np.repeat(X[:, None, :N], k, axis=1)  # token inputs of width hidden
+    Wg = [w.T for w in W]
+    gates = []
+    for r in range(tp):
+        sh = next(s for e, rr, s in wep if rr == r)["gate"]
+        gates.append(oracle.moe_linear_slots(xg, topk, lambda e: oracle.slice_weight(Wg[e], sh),
+                                             sh["n_len"]))
+    fullg = oracle.moe_linear_slots(xg, topk, lambda e: Wg[e], K)
+    assert np.array_equal(np.concatenate(gates, axis=2), fullg)
