@@ -457,6 +457,66 @@ tsl_status embed_lookup(const tsl_shard *shard, tsl_dtype tdtype, const void *ta
                         int64_t ld_table, const int32_t *tokens, int64_t M, tsl_dtype ydtype,
                         void *Y, int64_t ldy, void *stream);
 
+/*
+ * moe_dispatch -- the rows of one rank's expert products for a batch of
+ * routed tokens ([mlxcel] "MoE expert parallelization": the router runs on
+ * every rank, each rank runs only the experts it holds).  Host only.
+ *   topk:    HOST int32 [T][k], token t's k chosen experts (router output).
+ *   experts: HOST int32 [n_local], the experts this rank holds, in the
+ *            order their products are laid out (distinct, < n_experts).
+ * A row is one slot s = t*k + j whose expert the rank holds.  Rows are
+ * grouped by expert in `experts` order, slots ascending within an expert:
+ *   offsets:  HOST int64 [n_local + 1], expert i owns rows
+ *             [offsets[i], offsets[i+1]).
+ *   row_slot: HOST int32 [T*k] (first offsets[n_local] entries written),
+ *             the slot of each row (its token is row_slot / k).
+ *   slot_row: HOST int32 [T*k], the row of each slot, -1 for slots whose
+ *             expert another rank holds.
+ * T == 0 is allowed (offsets all 0).  Errors: TSL_ERR_INVALID_ARG (null,
+ * T < 0, k < 1, T*k >= 2^31, n_experts < 1, n_local < 0, an id in topk or
+ * experts outside [0, n_experts), an expert listed twice).
+ */
+tsl_status moe_dispatch(const int32_t *topk, int64_t T, int32_t k, int32_t n_experts,
+                        const int32_t *experts, int32_t n_local, int64_t *offsets,
+                        int32_t *row_slot, int32_t *slot_row);
+
+/*
+ * moe_gather -- out[i][:] = src[idx[i]][:] for i < n, width elements per
+ * row: the activations of a rank's expert rows in the layout moe_dispatch
+ * gives (idx = row_slot / k for token inputs, or row_slot for per-slot
+ * inputs).  src DEVICE [n_src][ld_src], out DEVICE [n][ldo], both of
+ * type dtype (F32 or BF16, copied bit for bit); idx DEVICE int32 [n].  An
+ * index outside [0, n_src) gives a row of -0.0.  out must not overlap src
+ * or idx.  n == 0 enqueues nothing.  Errors: TSL_ERR_INVALID_ARG,
+ * TSL_ERR_MISALIGNED (pointers aligned to their element size), TSL_ERR_HIP.
+ */
+tsl_status moe_gather(const void *src, int64_t ld_src, int64_t n_src, tsl_dtype dtype,
+                      const int32_t *idx, int64_t n, int64_t width, void *out, int64_t ldo,
+                      void *stream);
+
+/*
+ * moe_combine -- one rank's share of the MoE output: each token's weighted
+ * sum over its choices whose expert the rank holds ([mlxcel] "MoE expert
+ * parallelization"; the rank shares add up over ranks like row-parallel
+ * partials, combine_partials SUM):
+ *   Y[t][j] = sum over s < k with 0 <= r = slot_row[t*k+s] < n_rows of
+ *             weights[t*k+s] * P[r][j]
+ * in binary32, s ascending, each term a fused multiply-add onto the
+ * running sum, which starts at -0.0 (a token with no held choice gets
+ * -0.0, the additive identity); rounded once to ydtype.
+ *   P:        DEVICE binary32 [n_rows][ldp], the expert rows (e.g. the
+ *             down products of shard_linear_group).
+ *   slot_row: DEVICE int32 [T*k] (moe_dispatch); weights DEVICE binary32
+ *             [T*k], the router weights.
+ *   Y:        DEVICE [T][ldy], ydtype F32 or BF16; must not overlap the
+ *             inputs.
+ * T == 0 or n == 0 enqueues nothing.  Errors: TSL_ERR_INVALID_ARG,
+ * TSL_ERR_MISALIGNED, TSL_ERR_HIP.
+ */
+tsl_status moe_combine(const float *P, int64_t ldp, int64_t n_rows, const int32_t *slot_row,
+                       const float *weights, int64_t T, int32_t k, int64_t n, tsl_dtype ydtype,
+                       void *Y, int64_t ldy, void *stream);
+
 /* A static, human-readable description of a status code. */
 const char *tsl_status_string(tsl_status status);
 

@@ -120,6 +120,10 @@ _lib.combine_to_ranks.argtypes = [ctypes.c_int, _i32, ctypes.POINTER(_vp), ctype
                                   _i64, _i64, ctypes.c_int, ctypes.POINTER(_vp), _i64, _vp]
 _lib.plan_experts.argtypes = [_i32, _i64, _i64, _i32, _i32, _i32, ctypes.POINTER(ExpertShard),
                               _i64, ctypes.POINTER(_i64)]
+_lib.moe_dispatch.argtypes = [_vp, _i64, _i32, _i32, _vp, _i32, _vp, _vp, _vp]
+_lib.moe_gather.argtypes = [_vp, _i64, _i64, ctypes.c_int, _vp, _i64, _i64, _vp, _i64, _vp]
+_lib.moe_combine.argtypes = [_vp, _i64, _i64, _vp, _vp, _i64, _i32, _i64, ctypes.c_int, _vp, _i64,
+                             _vp]
 _lib.plan_vocab.argtypes = [_i64, _i64, _i32, _i32, _P_SHARD, _i64]
 _lib.embed_lookup.argtypes = [_P_SHARD, ctypes.c_int, _vp, _i64, _vp, _i64, ctypes.c_int, _vp,
                               _i64, _vp]
@@ -130,13 +134,14 @@ _lib.tsl_last_hip_error_string.restype = ctypes.c_char_p
 for _f in ("plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
            "shard_linear_workspace_size", "shard_linear", "shard_linear_group_workspace_size",
            "shard_linear_group", "combine_partials", "combine_to_ranks", "plan_vocab",
-           "embed_lookup", "plan_experts"):
+           "embed_lookup", "plan_experts", "moe_dispatch", "moe_gather", "moe_combine"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
            "shard_linear_workspace_size", "shard_linear", "shard_linear_group_workspace_size",
            "shard_linear_group", "combine_partials", "combine_to_ranks", "plan_vocab",
-           "embed_lookup", "plan_experts", "tsl_status_string", "tsl_last_hip_error_string")
+           "embed_lookup", "plan_experts", "moe_dispatch", "moe_gather", "moe_combine",
+           "tsl_status_string", "tsl_last_hip_error_string")
 
 
 def _check(status, where):
@@ -200,6 +205,32 @@ def plan_experts(n_experts, hidden, expert_ffn, tp_size, mode, group_size=0):
     _check(_lib.plan_experts(n_experts, hidden, expert_ffn, tp_size, mode, group_size, out, n,
                              ctypes.byref(got)), "plan_experts")
     return list(out)[:got.value]
+
+
+def moe_dispatch(topk, n_experts, experts):
+    """Host routing -> (offsets int64 [n_local + 1], row_slot int32 [rows],
+    slot_row int32 [T*k]); topk is an int32 array [T][k] (host)."""
+    import numpy as np
+    topk = np.ascontiguousarray(topk, dtype=np.int32)
+    T, k = topk.shape
+    ex = np.ascontiguousarray(experts, dtype=np.int32)
+    offsets = np.zeros(len(ex) + 1, dtype=np.int64)
+    row_slot = np.zeros(max(T * k, 1), dtype=np.int32)
+    slot_row = np.zeros(max(T * k, 1), dtype=np.int32)
+    _check(_lib.moe_dispatch(topk.ctypes.data, T, k, n_experts, ex.ctypes.data if len(ex) else None,
+                             len(ex), offsets.ctypes.data, row_slot.ctypes.data,
+                             slot_row.ctypes.data), "moe_dispatch")
+    return offsets, row_slot[:offsets[-1]].copy(), slot_row[:T * k].copy()
+
+
+def moe_gather(src, ld_src, n_src, dtype, idx, n, width, out, ldo, stream=None):
+    _check(_lib.moe_gather(_ptr(src), ld_src, n_src, dtype, _ptr(idx), n, width, _ptr(out), ldo,
+                           _stream(stream)), "moe_gather")
+
+
+def moe_combine(P, ldp, n_rows, slot_row, weights, T, k, n, ydtype, Y, ldy, stream=None):
+    _check(_lib.moe_combine(_ptr(P), ldp, n_rows, _ptr(slot_row), _ptr(weights), T, k, n, ydtype,
+                            _ptr(Y), ldy, _stream(stream)), "moe_combine")
 
 
 def embed_lookup(shard, tdtype, table, ld_table, tokens, M, ydtype, Y, ldy, stream=None):

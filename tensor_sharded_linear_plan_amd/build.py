@@ -19,7 +19,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libtsl.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["abi.cpp", "plan.cpp", "pack.hip", "combine.hip", "embed.hip", "skinny.hip", "prefill.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "pack.hip", "combine.hip", "embed.hip", "moe.hip", "skinny.hip", "prefill.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-mcode-object-version=5", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          # the LDS-copy asm in prefill.hip sets m0 and lists it as clobbered on purpose

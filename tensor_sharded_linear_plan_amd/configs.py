@@ -92,3 +92,24 @@ class Vocab:
 
 
 VOCAB7B = Vocab("vocab7b", 5, 152064, 3584, 4, (1, 4, 16), 2048)
+
+
+@dataclass(frozen=True)
+class Moe:
+    """A mixture-of-experts FFN workload."""
+    name: str
+    index: int           # config number used in the input seeds
+    n_experts: int
+    top_k: int
+    hidden: int
+    expert_ffn: int
+    tp: int
+    tokens: tuple        # token counts T
+    x_std: float = 1.0
+    scale_lo: float = 0.005
+    scale_hi: float = 0.02
+    bias_std: float = 0.05
+
+
+MOE30B = Moe("moe30b", 6, 128, 8, 2048, 768, 4, (2048, 16))
+MOE_SMALL = Moe("moe_small", 7, 16, 4, 384, 256, 2, (37, 5))

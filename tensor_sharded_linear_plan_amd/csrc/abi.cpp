@@ -672,6 +672,50 @@ extern "C" tsl_status embed_lookup(const tsl_shard *shard, tsl_dtype tdtype, con
                                         static_cast<hipStream_t>(stream)));
 }
 
+extern "C" tsl_status moe_gather(const void *src, int64_t ld_src, int64_t n_src, tsl_dtype dtype,
+                                 const int32_t *idx, int64_t n, int64_t width, void *out,
+                                 int64_t ldo, void *stream) {
+    if (!src || !idx || !out || n_src < 1 || n < 0 || width < 1 || ld_src < width || ldo < width)
+        return TSL_ERR_INVALID_ARG;
+    if (dtype != TSL_F32 && dtype != TSL_BF16)
+        return TSL_ERR_INVALID_ARG;
+    const size_t e = dtype == TSL_F32 ? 4 : 2;
+    if (!aligned(src, e) || !aligned(out, e) || !aligned(idx, 4))
+        return TSL_ERR_MISALIGNED;
+    if (n == 0)
+        return TSL_OK;
+    if (matrices_overlap(out, n, width, ldo, e, src, n_src, width, ld_src, e) ||
+        overlaps(out, span(n, width, ldo, e), idx, (size_t)n * 4))
+        return TSL_ERR_INVALID_ARG;
+    // a row gather is a lookup into a table of n_src rows that one rank owns whole
+    return from_hip(launch_embed_lookup(dtype, src, ld_src, idx, n, 0, n_src, width, dtype, out,
+                                        ldo, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" tsl_status moe_combine(const float *P, int64_t ldp, int64_t n_rows,
+                                  const int32_t *slot_row, const float *weights, int64_t T,
+                                  int32_t k, int64_t n, tsl_dtype ydtype, void *Y, int64_t ldy,
+                                  void *stream) {
+    if (!slot_row || !weights || !Y || T < 0 || k < 1 || n < 0 || n_rows < 0 || ldy < n)
+        return TSL_ERR_INVALID_ARG;
+    if (n_rows > 0 && (!P || ldp < n))
+        return TSL_ERR_INVALID_ARG;
+    if (ydtype != TSL_F32 && ydtype != TSL_BF16)
+        return TSL_ERR_INVALID_ARG;
+    const size_t ye = ydtype == TSL_F32 ? 4 : 2;
+    if ((P && !aligned(P, 4)) || !aligned(slot_row, 4) || !aligned(weights, 4) || !aligned(Y, ye))
+        return TSL_ERR_MISALIGNED;
+    if (T == 0 || n == 0)
+        return TSL_OK;
+    const size_t ybytes = span(T, n, ldy, ye);
+    if ((n_rows > 0 && matrices_overlap(Y, T, n, ldy, ye, P, n_rows, n, ldp, 4)) ||
+        overlaps(Y, ybytes, slot_row, (size_t)T * k * 4) ||
+        overlaps(Y, ybytes, weights, (size_t)T * k * 4))
+        return TSL_ERR_INVALID_ARG;
+    return from_hip(launch_moe_combine(P, ldp, n_rows, slot_row, weights, T, k, n, ydtype, Y, ldy,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 extern "C" const char *tsl_last_hip_error_string(void) { return hipGetErrorString(g_last_hip); }
 
 extern "C" const char *tsl_status_string(tsl_status status) {

@@ -82,6 +82,13 @@ hipError_t launch_embed_lookup(tsl_dtype tdtype, const void *table, int64_t ld_t
                                int64_t n_len, tsl_dtype ydtype, void *Y, int64_t ldy,
                                hipStream_t stream);
 
+// ---- moe.hip ----
+// Y[t][j] = sum over held slots s < k of weights[t k + s] * P[slot_row[t k + s]][j],
+// binary32 fused multiply-adds from -0.0, rounded once to ydtype.
+hipError_t launch_moe_combine(const float *P, int64_t ldp, int64_t n_rows, const int32_t *slot_row,
+                              const float *weights, int64_t T, int k, int64_t n, tsl_dtype ydtype,
+                              void *Y, int64_t ldy, hipStream_t stream);
+
 // One shard product of a (possibly grouped) shard_linear call, validated.
 struct LinearItem {
     PackGeom g;

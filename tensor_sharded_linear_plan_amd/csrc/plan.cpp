@@ -7,6 +7,8 @@
 // "Configuration" (--tp-size is a power of two).
 #include <stdint.h>
 
+#include <vector>
+
 #include "tsl.h"
 
 namespace {
@@ -269,5 +271,53 @@ extern "C" tsl_status plan_experts(int32_t n_experts, int64_t hidden, int64_t ex
         }
     }
     *n_out = k;
+    return TSL_OK;
+}
+
+// The rows of a rank's expert products (mlxcel "MoE expert
+// parallelization": every rank routes every token and runs its own
+// experts): a counting sort of the slots t*k + j by expert, stable in slot
+// order, over the experts the rank holds.
+extern "C" tsl_status moe_dispatch(const int32_t *topk, int64_t T, int32_t k, int32_t n_experts,
+                                   const int32_t *experts, int32_t n_local, int64_t *offsets,
+                                   int32_t *row_slot, int32_t *slot_row) {
+    if (T < 0 || k < 1 || n_experts < 1 || n_local < 0 || !offsets)
+        return TSL_ERR_INVALID_ARG;
+    if (T > (int64_t)(INT32_MAX - 1) / k)
+        return TSL_ERR_INVALID_ARG;
+    const int64_t S = T * k;
+    if (S > 0 && (!topk || !row_slot || !slot_row))
+        return TSL_ERR_INVALID_ARG;
+    if (n_local > 0 && !experts)
+        return TSL_ERR_INVALID_ARG;
+    std::vector<int32_t> local(n_experts, -1); // expert -> index in `experts`
+    for (int32_t i = 0; i < n_local; ++i) {
+        const int32_t e = experts[i];
+        if (e < 0 || e >= n_experts || local[e] >= 0)
+            return TSL_ERR_INVALID_ARG;
+        local[e] = i;
+    }
+    std::vector<int64_t> count(n_local + 1, 0);
+    for (int64_t s = 0; s < S; ++s) {
+        const int32_t e = topk[s];
+        if (e < 0 || e >= n_experts)
+            return TSL_ERR_INVALID_ARG;
+        if (local[e] >= 0)
+            ++count[local[e] + 1];
+    }
+    offsets[0] = 0;
+    for (int32_t i = 0; i < n_local; ++i)
+        offsets[i + 1] = offsets[i] + count[i + 1];
+    std::vector<int64_t> next(offsets, offsets + n_local + 1);
+    for (int64_t s = 0; s < S; ++s) {
+        const int32_t li = local[topk[s]];
+        if (li < 0) {
+            slot_row[s] = -1;
+            continue;
+        }
+        const int64_t r = next[li]++;
+        row_slot[r] = (int32_t)s;
+        slot_row[s] = (int32_t)r;
+    }
     return TSL_OK;
 }

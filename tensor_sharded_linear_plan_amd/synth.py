@@ -74,3 +74,14 @@ def const_bf16(shape, value):
 def token_ids(seed, M, vocab):
     """M token ids uniform on 0..vocab-1, int32."""
     return rng(seed).integers(0, vocab, size=M, dtype=np.int32)
+
+
+def router(seed, T, k, n_experts):
+    """Router outputs: each token's k distinct experts (uniform), int32
+    [T][k], and their weights, a softmax of N(0, 1) logits over the k
+    choices, binary32 [T][k]."""
+    g = rng(seed)
+    topk = np.argsort(g.random((T, n_experts)), axis=1)[:, :k].astype(np.int32)
+    logits = g.standard_normal((T, k))
+    w = np.exp(logits - logits.max(axis=1, keepdims=True))
+    return topk, (w / w.sum(axis=1, keepdims=True)).astype(np.float32)

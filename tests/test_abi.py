@@ -28,8 +28,8 @@ def test_library_exports_every_declared_symbol(tsl_lib):
                           "shard_linear_workspace_size", "shard_linear",
                           "shard_linear_group_workspace_size", "shard_linear_group",
                           "combine_partials", "combine_to_ranks", "plan_vocab",
-                          "embed_lookup", "plan_experts", "tsl_status_string",
-                          "tsl_last_hip_error_string"}
+                          "embed_lookup", "plan_experts", "moe_dispatch", "moe_gather",
+                          "moe_combine", "tsl_status_string", "tsl_last_hip_error_string"}
     lib = ctypes.CDLL(tsl_lib.LIBRARY)
     for n in names:
         assert hasattr(lib, n), n
@@ -491,3 +491,58 @@ def test_plan_experts_vs_oracle(tsl_lib, mode):
     with pytest.raises(tsl_lib.TslError) as e:
         tsl_lib.plan_experts(4, 64, 128, 2, 7)
     assert e.value.status == tsl_lib.ERR_INVALID_ARG
+
+
+def test_moe_dispatch_vs_oracle(tsl_lib):
+    rng = np.random.default_rng(9)
+    cases = [(np.array([[0, 2], [2, 1], [0, 0]]), 3, [2, 0])]
+    for T, k, E in ((0, 2, 4), (1, 1, 1), (37, 2, 8), (2048, 8, 128), (5, 3, 6)):
+        topk = np.stack([rng.permutation(E)[:k] for _ in range(T)]) if T else \
+            np.zeros((0, k), dtype=np.int64)
+        for tp in (1, 4):
+            for r in range(min(tp, 2)):
+                cases.append((topk, E, [e for e in range(E) if e % tp == r]))
+        cases.append((rng.integers(0, E, (T, k)), E, list(rng.permutation(E)[: E // 2])))
+    for topk, E, held in cases:
+        off, row_slot, slot_row = tsl_lib.moe_dispatch(topk, E, held)
+        w_off, w_rs, w_sr = oracle.moe_dispatch(topk, held)
+        assert np.array_equal(off, w_off)
+        assert np.array_equal(row_slot, w_rs) and np.array_equal(slot_row, w_sr)
+    bad = [(np.array([[0, 5]]), 4, [0]),      # routed to an expert that does not exist
+           (np.array([[0, 1]]), 4, [1, 1]),   # an expert listed twice
+           (np.array([[0, 1]]), 4, [4]),      # a held expert out of range
+           (np.array([[0, -1]]), 4, [0])]
+    for topk, E, held in bad:
+        with pytest.raises(tsl_lib.TslError) as e:
+            tsl_lib.moe_dispatch(topk, E, held)
+        assert e.value.status == tsl_lib.ERR_INVALID_ARG
+
+
+def test_moe_gather_and_combine_rejections(tsl_lib):
+    src, idx, out = 1 << 24, 1 << 26, 1 << 28
+    g = lambda **kw: tsl_lib.moe_gather(kw.get("src", src), kw.get("ld", 64), 100,
+                                        kw.get("dt", tsl_lib.BF16), kw.get("idx", idx),
+                                        kw.get("n", 0), 64, kw.get("out", out), kw.get("ldo", 64))
+    g()
+    for kw, code in ((dict(src=None), tsl_lib.ERR_INVALID_ARG), (dict(ld=32), tsl_lib.ERR_INVALID_ARG),
+                     (dict(dt=tsl_lib.Q4G64), tsl_lib.ERR_INVALID_ARG),
+                     (dict(ldo=8), tsl_lib.ERR_INVALID_ARG), (dict(out=out + 1), tsl_lib.ERR_MISALIGNED),
+                     (dict(n=5, out=src + 256), tsl_lib.ERR_INVALID_ARG)):
+        with pytest.raises(tsl_lib.TslError) as e:
+            g(**kw)
+        assert e.value.status == code, kw
+    P, sr, w, Y = 1 << 24, 1 << 26, (1 << 26) + 4096, 1 << 28
+    c = lambda **kw: tsl_lib.moe_combine(kw.get("P", P), 64, kw.get("rows", 10), kw.get("sr", sr),
+                                         kw.get("w", w), kw.get("T", 0), kw.get("k", 2), 64,
+                                         kw.get("yd", tsl_lib.F32), kw.get("Y", Y),
+                                         kw.get("ldy", 64))
+    c()
+    c(P=None, rows=0)  # no rows held: every token gets -0.0
+    for kw, code in ((dict(k=0), tsl_lib.ERR_INVALID_ARG), (dict(P=None), tsl_lib.ERR_INVALID_ARG),
+                     (dict(ldy=63), tsl_lib.ERR_INVALID_ARG), (dict(yd=tsl_lib.Q4G64), tsl_lib.ERR_INVALID_ARG),
+                     (dict(Y=Y + 2), tsl_lib.ERR_MISALIGNED),
+                     (dict(T=4, Y=P + 256), tsl_lib.ERR_INVALID_ARG),
+                     (dict(T=4, Y=w - 64), tsl_lib.ERR_INVALID_ARG)):
+        with pytest.raises(tsl_lib.TslError) as e:
+            c(**kw)
+        assert e.value.status == code, kw

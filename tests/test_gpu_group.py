@@ -184,3 +184,51 @@ def test_sum_set_equals_products_then_combine(M):
             assert t.equal(Y, want)
         else:
             assert np.array_equal(host_bits(Y), oracle.f64_to_bf16(host(want)))
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "q4"])
+@pytest.mark.parametrize("M,rows", [(300, (300, 1, 77, 256, 129, 65)), (16, (16, 1, 7, 3)),
+                                    (4, (1, 4, 2))])
+def test_items_with_their_own_rows(wdtype, M, rows):
+    """Items of one call over different row counts (the per-expert products
+    of a MoE layer): each equals the oracle over its own rows, nothing is
+    written past them, and in the GEMM regime each equals a separate call
+    over the same rows bit for bit when that call also takes the GEMM."""
+    t = torch()
+    K, N = 384, 200
+    items, keep = [], []
+    for i, rw in enumerate(rows):
+        sh = tsl.plan_linear(K, N, 1, tsl.COLUMN, 64)[0]
+        for integer in (False, True):
+            seed = 3000 + 10 * i + integer
+            if wdtype == "q4":
+                w = Q4Weight(K, N, seed, seed + 1, seed + 2, integer=integer)
+                buf, nb = w.pack(sh)
+                Wf = w.shard_f64(spec_dict(sh))
+                code = tsl.Q4G64
+            else:
+                W = synth.small_int_bf16(seed, (K, N)) if integer else \
+                    synth.normal_bf16(seed, (K, N), 0.02)
+                from gpu_util import pack
+                buf, nb = pack(sh, tsl.BF16, dev(W), N, 1)
+                Wf = oracle.bf16_to_f64(W)
+                code = tsl.BF16
+            X = synth.small_int_bf16(seed + 5, (M, K)) if integer else \
+                synth.normal_bf16(seed + 5, (M, K))
+            dX = dev(X)
+            Y = t.full((M, N), float("nan"), dtype=t.float32, device="cuda")
+            items.append(dict(shard=sh, packed=buf, packed_bytes=nb, X=dX, ldx=K, Y=Y, ldy=N,
+                              rows=rw if rw != M or i % 2 else 0))
+            keep.append((rw, integer, X, Wf, Y, sh, buf, nb, dX))
+    run_group(items, code, M)
+    for rw, integer, X, Wf, Y, sh, buf, nb, dX in keep:
+        got = host(Y)
+        assert np.isnan(got[rw:]).all(), rw  # rows past the item's own untouched
+        ref = oracle.gemm(oracle.bf16_to_f64(X[:rw]), Wf)
+        if integer:
+            assert np.array_equal(got[:rw], ref), rw
+        else:
+            assert normwise(got[:rw], ref) <= TOL, rw
+        if M > 64 and rw > 64:
+            single = linear(sh, code, buf, nb, tsl.BF16, dX, K, rw)
+            assert t.equal(single[:rw], Y[:rw]), rw
