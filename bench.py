@@ -448,6 +448,156 @@ def vocab_bench(args, tsl, torch, synth, configs):
     return out
 
 
+def moe_bench(args, tsl, torch, synth, configs):
+    """moe30b, expert parallel, every rank of the layer on one GPU: per
+    step the rows of all ranks gathered (one moe_gather for the token
+    inputs, one for the per-slot down inputs), every held expert's gate and
+    up products in one shard_linear_group call, the down products in
+    another, each rank's moe_combine and the sum of the rank outputs.
+    Routing (moe_dispatch) is host work on the router's output and is done
+    before the timed region.  T = 2048: TFLOP/s of the expert products;
+    T = 16: GB/s of the weights of the experts the step touches, HIP-graph
+    replay over 2 weight copies."""
+    import numpy as np
+    c = configs.MOE30B
+    t0 = time.perf_counter()
+    plan = tsl.plan_experts(c.n_experts, c.hidden, c.expert_ffn, c.tp, tsl.MOE_EXPERT_PARALLEL, 64)
+    by_expert = {x.expert: x for x in plan}
+    copies = 2
+    packs = [dict() for _ in range(copies)]
+    for x in plan:
+        for pi, p in enumerate(("gate", "up", "down")):
+            sh = getattr(x, p)
+            K, N = sh.K, sh.N
+            sd = synth.seed_of(c.index, 10 * x.expert + pi, 0)
+            codes = torch.from_numpy(synth.q4_codes(sd + synth.T_CODES, (K, N))).cuda()
+            sc = torch.from_numpy(synth.uniform_bf16(sd + synth.T_SCALES, (K // 64, N), c.scale_lo,
+                                                     c.scale_hi).view("int16")).cuda()
+            bi = torch.from_numpy(synth.normal_bf16(sd + synth.T_BIASES, (K // 64, N),
+                                                    c.bias_std).view("int16")).cuda()
+            nb = tsl.pack_shard_size(sh, tsl.Q4G64)
+            for cp in range(copies):
+                buf = torch.empty(nb, dtype=torch.uint8, device="cuda")
+                tsl.pack_shard(sh, tsl.Q4G64, codes, N, 1, sc, bi, N, 1, buf, nb)
+                packs[cp][x.expert, p] = (buf, nb)
+    torch.cuda.synchronize()
+    log("moe: packed %d experts x3 x%d (%.1f s)" % (c.n_experts, copies, time.perf_counter() - t0))
+    wbytes = lambda K, N: K * N // 2 + (K // 64) * N * 4
+    out = {"workload": "moe30b: 128 experts of width 768, top-8, hidden 2048, expert parallel "
+                       "over tp=4 (32 experts per rank), 4-bit g64, all ranks on one GPU; per "
+                       "step: gathers, the gate+up and the down products of every held expert "
+                       "(two shard_linear_group calls), 4 moe_combine and the rank sum",
+           "rows": []}
+    for T in c.tokens:
+        xs = synth.seed_of(c.index, 0, synth.T_X) + T
+        topk, w = synth.router(xs + 2, T, c.top_k, c.n_experts)
+        k = c.top_k
+        X = torch.from_numpy(synth.normal_bf16(xs, (T, c.hidden)).view("int16")).cuda() \
+            .view(torch.bfloat16)
+        H = torch.from_numpy(synth.normal_bf16(xs + 1, (T * k, c.expert_ffn)).view("int16")) \
+            .cuda().view(torch.bfloat16)
+        dw = torch.from_numpy(w.ravel()).cuda()
+        ranks, tok_idx, slot_idx = [], [], []
+        base = 0
+        for r in range(c.tp):
+            held = [x.expert for x in plan if x.rank == r]
+            off, row_slot, slot_row = tsl.moe_dispatch(topk, c.n_experts, held)
+            ranks.append((held, off + base, torch.from_numpy(slot_row).cuda(), base,
+                          int(off[-1])))
+            tok_idx.append(row_slot // k)
+            slot_idx.append(row_slot)
+            base += int(off[-1])
+        R = base
+        d_tok = torch.from_numpy(np.concatenate(tok_idx).astype(np.int32)).cuda()
+        d_slot = torch.from_numpy(np.concatenate(slot_idx).astype(np.int32)).cuda()
+        Xp = torch.empty((R, c.hidden), dtype=torch.bfloat16, device="cuda")
+        Hp = torch.empty((R, c.expert_ffn), dtype=torch.bfloat16, device="cuda")
+        G = torch.empty((R, c.expert_ffn), dtype=torch.bfloat16, device="cuda")
+        U = torch.empty((R, c.expert_ffn), dtype=torch.bfloat16, device="cuda")
+        P = torch.empty((R, c.hidden), dtype=torch.float32, device="cuda")
+        Yr = [torch.empty((T, c.hidden), dtype=torch.float32, device="cuda") for _ in ranks]
+        Y = torch.empty((T, c.hidden), dtype=torch.bfloat16, device="cuda")
+        calls, flops, touched = [], 0, 0
+        counts = np.concatenate([np.diff(o) for _, o, _, _, _ in ranks])
+        Mmax = int(counts.max())
+        for cp in range(copies):
+            gu, dn = [], []
+            for held, off, _, _, _ in ranks:
+                for i, e in enumerate(held):
+                    rows = int(off[i + 1] - off[i])
+                    if rows == 0:
+                        continue
+                    o = int(off[i])
+                    x = by_expert[e]
+                    for p, Yb in (("gate", G), ("up", U)):
+                        buf, nb = packs[cp][e, p]
+                        gu.append(dict(shard=getattr(x, p), packed=buf, packed_bytes=nb,
+                                       X=Xp[o:], ldx=c.hidden, Y=Yb[o:], ldy=c.expert_ffn,
+                                       ydtype=tsl.BF16, rows=rows))
+                    buf, nb = packs[cp][e, "down"]
+                    dn.append(dict(shard=x.down, packed=buf, packed_bytes=nb, X=Hp[o:],
+                                   ldx=c.expert_ffn, Y=P[o:], ldy=c.hidden, rows=rows))
+                    if cp == 0:
+                        flops += 6 * rows * c.hidden * c.expert_ffn
+                        touched += 3 * wbytes(c.hidden, c.expert_ffn)
+            groups = []
+            for items in (gu, dn):
+                arr = tsl._items(items)
+                ws = tsl.shard_linear_group_workspace_size(items, tsl.Q4G64, Mmax)
+                groups.append((arr, torch.empty(max(ws, 256), dtype=torch.uint8, device="cuda"),
+                               ws))
+            calls.append(groups)
+
+        def step(cp, stream):
+            tsl.moe_gather(X, c.hidden, T, tsl.BF16, d_tok, R, c.hidden, Xp, c.hidden, stream)
+            tsl.moe_gather(H, c.expert_ffn, T * k, tsl.BF16, d_slot, R, c.expert_ffn, Hp,
+                           c.expert_ffn, stream)
+            for (arr, n), wsb, ws in calls[cp]:
+                tsl._check(tsl._lib.shard_linear_group(n, arr, tsl.Q4G64, tsl.BF16, Mmax,
+                                                       wsb.data_ptr(), ws, stream),
+                           "shard_linear_group")
+            for (held, off, d_sr, b, rr), Yo in zip(ranks, Yr):
+                tsl.moe_combine(P[b:], c.hidden, rr, d_sr, dw, T, k, c.hidden, tsl.F32, Yo,
+                                c.hidden, stream)
+            tsl.combine_partials(tsl.COMBINE_SUM, Yr, tsl.F32, T, c.hidden, c.hidden, tsl.BF16,
+                                 Y, c.hidden, stream)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for cp in range(copies):
+                step(cp, side.cuda_stream)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream().cuda_stream
+            for cp in range(copies):
+                step(cp, cap)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        reps = max(5, args.steps)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        us = start.elapsed_time(end) * 1e3 / (reps * copies)
+        row = {"T": T, "us_per_step": round(us, 1), "TFLOP/s": round(flops / us / 1e6, 1),
+               "mfma_frac": round(flops / us / 1e6 / PEAK_MFMA_F16, 4),
+               "touched_weight_GB/s": round(touched / (us * 1e-6) / 1e9, 1),
+               "hbm_frac": round(touched / (us * 1e-6) / 1e9 / PEAK_HBM, 4),
+               "expert_rows": R, "experts_touched": int((counts > 0).sum()),
+               "flops_per_step": flops, "weight_bytes_touched": touched}
+        out["rows"].append(row)
+        log("moe T=%d: %.1f us/step, %.1f TFLOP/s, %.0f GB/s of touched weights"
+            % (T, us, row["TFLOP/s"], row["touched_weight_GB/s"]))
+        del graph
+    return out
+
+
 def cpu_baseline(synth, configs):
     """The oracle, as it stands, on a bounded sample of the prefill workload:
     rank 0's gate shard (5120 -> 4352, 4-bit), dequantised and multiplied
@@ -519,6 +669,7 @@ def main():
     dec = [] if args.no_decode else decode_bench(args, tsl, torch, synth, configs)
     coll = None if args.no_decode else collectives_bench(tsl, torch)
     voc = None if args.no_decode else vocab_bench(args, tsl, torch, synth, configs)
+    moe = None if args.no_decode else moe_bench(args, tsl, torch, synth, configs)
     cpu = None
     if not args.no_cpu_baseline:
         sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
@@ -555,6 +706,7 @@ def main():
                    "unit": "GB/s", "peak": PEAK_HBM, "rows": dec},
         "collectives": coll,
         "vocab": voc,
+        "moe": moe,
         "pack_GBps": round(pre["pack_gbs"], 1),
         "prefill_separate_calls_ms_per_step": round(pre["separate_ms"], 4),
         "wall_s_timed": round(pre["wall"], 3),
