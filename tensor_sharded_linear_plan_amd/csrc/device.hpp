@@ -44,13 +44,20 @@ __device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t p) {
 // so (w >> 4j) & 0x000F000F isolates the pair (k = 2j, 2j + 1).
 
 // Word -> four bf16 pairs holding 128 + q (0x4300 is bf16 128.0 and its 7
-// mantissa bits count units of 1 there).
+// mantissa bits count units of 1 there).  gfx9 VOP3 encodings take no
+// literal operand and at most one scalar one, so with the two constants
+// visible the compiler spends a separate AND and OR per pair; loaded
+// opaquely (the mask into a vector register, the other into a scalar one)
+// they let it select one v_and_or_b32 per pair.
 __device__ __forceinline__ bf16x8 q4_to_bf16_plus128(uint32_t w) {
+    uint32_t m, o;
+    asm("v_mov_b32 %0, 0x000f000f" : "=v"(m));
+    asm("s_mov_b32 %0, 0x43004300" : "=s"(o));
     u32x4 r;
-    r.x = (w & 0x000F000Fu) | 0x43004300u;
-    r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-    r.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-    r.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    r.x = (w & m) | o;
+    r.y = ((w >> 4) & m) | o;
+    r.z = ((w >> 8) & m) | o;
+    r.w = ((w >> 12) & m) | o;
     return __builtin_bit_cast(bf16x8, r);
 }
 

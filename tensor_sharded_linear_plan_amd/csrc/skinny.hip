@@ -228,13 +228,17 @@ struct SB {
     static constexpr int XU = (UNITS + 255) / 256;               // per thread
 };
 
-template <int WT, int MT, int NTW, bool XRES>
+// ONE: a single token row (M == 1, resident activations): only the first
+// accumulator row of each lane is ever stored, so the group epilogue
+// updates that one alone.
+template <int WT, int MT, int NTW, bool XRES, bool ONE = false>
 __global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
     using S = SB<WT, MT>;
     // XRES: [M rows][xstr bytes] sized at launch; else two [ROWS][XROW] windows
     extern __shared__ __attribute__((aligned(16))) char xl[];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave-uniform: tile and record addresses stay in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int bid = blockIdx.x;
     int lo = 0, hi = grp.n - 1; // last item whose first workgroup is <= bid
     while (lo < hi) {
@@ -415,7 +419,7 @@ __global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
 #pragma unroll
                             for (int i = 0; i < MT; ++i)
 #pragma unroll
-                                for (int r = 0; r < 4; ++r) {
+                                for (int r = 0; r < (ONE ? 1 : 4); ++r) {
                                     acc[i][j][r] = __builtin_fmaf(sc, ag[i][j][r], acc[i][j][r]);
                                     acc[i][j][r] = __builtin_fmaf(cb, xs[i][r], acc[i][j][r]);
                                 }
@@ -475,16 +479,25 @@ __global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
             if constexpr (WT == W_Q4) {
                 lds_barrier();
                 const int groups = (b1 - b0) * (S::BK / 64);
-                for (int e = threadIdx.x; e < groups * 16; e += 256) {
-                    const int g = e >> 4, r = e & 15;
-                    float sum = 0.f;
-                    if (r < rows) {
-                        const uint16_t *xp =
-                            reinterpret_cast<const uint16_t *>(&xl[r * grp.xstr + g * 128]);
-                        for (int k = 0; k < 64; ++k)
-                            sum += __uint_as_float((uint32_t)xp[k] << 16);
-                    }
-                    xsum[e] = sum;
+                const int nr = (int)rows; // resident rows, 1 .. kResidentRows
+                // rows past M sum to zero (their outputs are never stored)
+                for (int e = threadIdx.x; e < groups * 16; e += 256)
+                    if ((e & 15) >= nr)
+                        xsum[e] = 0.f;
+                // each (group, row) entry: 8 lanes add 8 activations each,
+                // then a butterfly over those 8 lanes
+                const int sub = threadIdx.x & 7;
+                for (int ent = threadIdx.x >> 3; ent < groups * nr; ent += 32) {
+                    const int g = ent / nr, r = ent - g * nr;
+                    const u32x4 v =
+                        *reinterpret_cast<const u32x4 *>(&xl[r * grp.xstr + g * 128 + sub * 16]);
+                    float sum = (bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y));
+                    sum += (bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w));
+                    sum += __shfl_xor(sum, 1, 8);
+                    sum += __shfl_xor(sum, 2, 8);
+                    sum += __shfl_xor(sum, 4, 8);
+                    if (sub == 0)
+                        xsum[g * 16 + r] = sum;
                 }
             }
         } else {
@@ -554,7 +567,9 @@ SkinnyFn pick_stream_ntw(int ntw) {
 }
 
 template <int WT>
-SkinnyFn pick_stream(int mt, int ntw, bool resident) {
+SkinnyFn pick_stream(int mt, int ntw, bool resident, bool one) {
+    if (resident && one && ntw == 1)
+        return stream_kernel<WT, 1, 1, true, true>;
     if (resident)
         return ntw == 1 ? stream_kernel<WT, 1, 1, true> : stream_kernel<WT, 1, 2, true>;
     switch (mt) {
@@ -658,8 +673,8 @@ int64_t skinny_blocks(const SkinnyPlan &p, const LinearItem *items, int n) {
 hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, tsl_dtype wdtype,
                          int64_t M, void *workspace, hipStream_t stream) {
     SkinnyFn fn = wdtype == TSL_F32    ? pick_f32(p.mt)
-                  : wdtype == TSL_BF16 ? pick_stream<W_BF16>(p.mt, p.ntw, p.resident)
-                                       : pick_stream<W_Q4>(p.mt, p.ntw, p.resident);
+                  : wdtype == TSL_BF16 ? pick_stream<W_BF16>(p.mt, p.ntw, p.resident, M == 1)
+                                       : pick_stream<W_Q4>(p.mt, p.ntw, p.resident, M == 1);
     if (!fn)
         return hipErrorInvalidValue;
     for (int c0 = 0; c0 < n; c0 += kGroupMax) {
