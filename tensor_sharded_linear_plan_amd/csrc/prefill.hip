@@ -438,34 +438,41 @@ double variant_cost(const Variant &v, const LinearItem *items, int n, int64_t M)
     pen = pen > 1.0 ? pen : 1.0;
     (void)M;
     auto mbk = [&](int i) { return (items[i].M + v.bm - 1) / v.bm; };
-    std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
-    for (int i = 0; i < 256; ++i)
-        cu.push(0.0);
-    double span = 0.0;
-    int64_t tiles = 0;
-    for (int i = 0; i < n; ++i)
-        tiles += mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn);
-    if (tiles > 16384) { // large: every CU busy to the end, to a tile
-        double work = 0.0, longest = 0.0;
-        for (int i = 0; i < n; ++i) {
-            const double len = (double)kpad64(items[i].g.Ks) / 64.0;
-            work += (double)(mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn)) * len;
-            longest = len > longest ? len : longest;
-        }
-        span = work / 256.0 + longest;
-    } else {
-        for (int i = 0; i < n; ++i) {
-            const double len = (double)kpad64(items[i].g.Ks) / 64.0;
-            const int64_t T = mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn);
-            for (int64_t t = 0; t < T; ++t) {
-                const double f = cu.top() + len;
-                cu.pop();
-                cu.push(f);
-                span = f > span ? f : span;
+    // every launch (kGroupMax items) drains before the next starts: the
+    // spans of the launches add up
+    double total = 0.0;
+    for (int c0 = 0; c0 < n; c0 += kGroupMax) {
+        const int c1 = n - c0 < kGroupMax ? n : c0 + kGroupMax;
+        double span = 0.0;
+        int64_t tiles = 0;
+        for (int i = c0; i < c1; ++i)
+            tiles += mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn);
+        if (tiles > 16384) { // large: every CU busy to the end, to a tile
+            double work = 0.0, longest = 0.0;
+            for (int i = c0; i < c1; ++i) {
+                const double len = (double)kpad64(items[i].g.Ks) / 64.0;
+                work += (double)(mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn)) * len;
+                longest = len > longest ? len : longest;
+            }
+            span = work / 256.0 + longest;
+        } else {
+            std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
+            for (int i = 0; i < 256; ++i)
+                cu.push(0.0);
+            for (int i = c0; i < c1; ++i) {
+                const double len = (double)kpad64(items[i].g.Ks) / 64.0;
+                const int64_t T = mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn);
+                for (int64_t t = 0; t < T; ++t) {
+                    const double f = cu.top() + len;
+                    cu.pop();
+                    cu.push(f);
+                    span = f > span ? f : span;
+                }
             }
         }
+        total += span;
     }
-    return span * (double)(v.bm * v.bn) * pen;
+    return total * (double)(v.bm * v.bn) * pen;
 }
 
 } // namespace
