@@ -448,6 +448,145 @@ def vocab_bench(args, tsl, torch, synth, configs):
     return out
 
 
+def graph_time(torch, run, copies, reps):
+    """Microseconds per call of run(copy, stream), replayed from a HIP graph
+    over `copies` weight copies."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for cp in range(copies):
+            run(cp, side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream().cuda_stream
+        for cp in range(copies):
+            run(cp, cap)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / (reps * copies)
+
+
+def dense_bench(args, tsl, torch, configs):
+    """The dense workloads, every rank of one layer per step as one
+    shard_linear_group call (rank sums of the row shards as sum sets,
+    column shards concat-free, replicated K/V into per-rank buffers): llama2k
+    (bf16, tp=4) at M = 1, 16, 256, gqa8 (bf16, tp=8, K/V replicated) at
+    M = 64, 512, and the wiki example (fp32, 1024 -> 2048 on 2 ranks, column
+    and row) at M = 32.  Weights N(0, 0.02^2) from torch's seeded generator,
+    HIP-graph replay over enough copies (at most 8) to exceed the 256 MB
+    last-level cache -- the 8 MB example stays cache-resident; each row
+    against its own roofline max(flops / 2.5 PF (fp32:
+    157.3 TF), bytes / 8 TB/s)."""
+    rows = []
+    g = torch.Generator(device="cuda")
+    cases = [(configs.LLAMA2K, tsl.BF16), (configs.GQA8, tsl.BF16), (configs.WORKED, tsl.F32)]
+    for layer, wd in cases:
+        dt = torch.bfloat16 if wd == tsl.BF16 else torch.float32
+        eb = 2 if wd == tsl.BF16 else 4
+        g.manual_seed(900 + layer.index)
+        if layer is configs.WORKED:
+            projs = [("col", tsl.plan_linear(layer.K, layer.N, layer.tp, tsl.COLUMN)),
+                     ("row", tsl.plan_linear(layer.K, layer.N, layer.tp, tsl.ROW))]
+            ms = (layer.M,)
+            name = "worked: fp32 X[32, 1024] x W 1024 -> 2048 on 2 ranks, column (concat) and " \
+                   "row (sum) shards"
+        else:
+            sh = tsl.plan_shards(layer.hidden, layer.n_q_heads, layer.n_kv_heads, layer.head_dim,
+                                 layer.ffn, layer.tp, layer.group)
+            projs = [(p, sh[i::tsl.NPROJ]) for i, p in enumerate(configs.PROJS)]
+            ms = layer.ms
+            name = "%s: every rank of one tp=%d layer (hidden %d, ffn %d, %d Q / %d KV heads of " \
+                   "%d), bf16" % (layer.name, layer.tp, layer.hidden, layer.ffn, layer.n_q_heads,
+                                  layer.n_kv_heads, layer.head_dim)
+        full = {}
+        wbytes = 0
+        for p, shards in projs:
+            s0 = shards[0]
+            full[p] = (torch.randn((s0.K, s0.N), generator=g, device="cuda") * 0.02).to(dt)
+            wbytes += sum(s.k_len * s.n_len * eb for s in shards)
+        copies = min(8, max(2, int(-(-600e6 // max(wbytes, 1)))))
+        packs = []
+        for _ in range(copies):
+            pk = {}
+            for p, shards in projs:
+                for s in shards:
+                    nb = tsl.pack_shard_size(s, wd)
+                    buf = torch.empty(nb, dtype=torch.uint8, device="cuda")
+                    tsl.pack_shard(s, wd, full[p], s.N, 1, None, None, 0, 0, buf, nb)
+                    pk[p, s.rank] = (buf, nb)
+            packs.append(pk)
+        del full
+        for M in ms:
+            X = {p: torch.randn((M, sh[0].K), generator=g, device="cuda").to(dt)
+                 for p, sh in projs}
+            outs, items_per_copy = {}, []
+            flops, nbytes = 0.0, 0
+            for cp in range(copies):
+                items = []
+                for p, shards in projs:
+                    s0 = shards[0]
+                    if s0.strategy == tsl.ROW:  # one sum set into the full f32/bf16 output
+                        Y = outs.setdefault(p, torch.empty((M, s0.N), dtype=dt, device="cuda"))
+                        for r, s in enumerate(shards):
+                            buf, nb = packs[cp][p, s.rank]
+                            items.append(dict(shard=s, packed=buf, packed_bytes=nb,
+                                              X=X[p][:, s.k_off:], ldx=s.K,
+                                              Y=Y if r == 0 else None, ldy=s.N,
+                                              ydtype=wd, sum_next=int(r < len(shards) - 1)))
+                    elif s0.strategy == tsl.COLUMN:  # concat-free into the full output
+                        Y = outs.setdefault(p, torch.empty((M, s0.N), dtype=dt, device="cuda"))
+                        for s in shards:
+                            buf, nb = packs[cp][p, s.rank]
+                            items.append(dict(shard=s, packed=buf, packed_bytes=nb, X=X[p],
+                                              ldx=s.K, Y=Y[:, s.n_off:], ldy=s.N, ydtype=wd))
+                    else:  # replicated: every rank its own full output
+                        for s in shards:
+                            Y = outs.setdefault((p, s.rank), torch.empty((M, s.N), dtype=dt,
+                                                                         device="cuda"))
+                            buf, nb = packs[cp][p, s.rank]
+                            items.append(dict(shard=s, packed=buf, packed_bytes=nb, X=X[p],
+                                              ldx=s.K, Y=Y, ldy=s.N, ydtype=wd))
+                    if cp == 0:
+                        for s in shards:
+                            flops += 2.0 * M * s.k_len * s.n_len
+                            nbytes += s.k_len * s.n_len * eb + M * s.k_len * eb
+                        nbytes += M * s0.N * eb * (1 if s0.strategy != tsl.REPLICATED
+                                                   else len(shards))
+                ws = tsl.shard_linear_group_workspace_size(items, wd, M)
+                items_per_copy.append((tsl._items(items),
+                                       torch.empty(max(ws, 256), dtype=torch.uint8,
+                                                   device="cuda"), ws))
+
+            def run(cp, stream):
+                (arr, n), wsb, ws = items_per_copy[cp]
+                tsl._check(tsl._lib.shard_linear_group(n, arr, wd, wd, M, wsb.data_ptr(), ws,
+                                                       stream), "shard_linear_group")
+            us = graph_time(torch, run, copies, max(5, args.steps))
+            peak = PEAK_MFMA_F16 if wd == tsl.BF16 else 157.3
+            t_roof = max(flops / (peak * 1e12), nbytes / (PEAK_HBM * 1e9)) * 1e6
+            rows.append({"workload": name, "M": M, "us_per_step": round(us, 2),
+                         "TFLOP/s": round(flops / us / 1e6, 2),
+                         "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                         "bound": "mfma" if flops / (peak * 1e12) > nbytes / (PEAK_HBM * 1e9)
+                         else "hbm", "roofline_frac": round(t_roof / us, 4),
+                         "flops": flops, "bytes": nbytes, "weight_copies": copies})
+            log("dense %s M=%d: %.1f us/step, %.1f TFLOP/s, %.0f GB/s, %.0f%% of roofline"
+                % (layer.name, M, us, flops / us / 1e6, nbytes / (us * 1e-6) / 1e9,
+                   100 * t_roof / us))
+        del packs
+    return rows
+
+
 def moe_bench(args, tsl, torch, synth, configs):
     """moe30b, expert parallel, every rank of the layer on one GPU: per
     step the rows of all ranks gathered (one moe_gather for the token
@@ -670,6 +809,7 @@ def main():
     coll = None if args.no_decode else collectives_bench(tsl, torch)
     voc = None if args.no_decode else vocab_bench(args, tsl, torch, synth, configs)
     moe = None if args.no_decode else moe_bench(args, tsl, torch, synth, configs)
+    dense = None if args.no_decode else dense_bench(args, tsl, torch, configs)
     cpu = None
     if not args.no_cpu_baseline:
         sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
@@ -707,6 +847,7 @@ def main():
         "collectives": coll,
         "vocab": voc,
         "moe": moe,
+        "dense": dense,
         "pack_GBps": round(pre["pack_gbs"], 1),
         "prefill_separate_calls_ms_per_step": round(pre["separate_ms"], 4),
         "wall_s_timed": round(pre["wall"], 3),
