@@ -108,9 +108,9 @@ struct LinearItem {
     int64_t M = 0;
 };
 
-// Items per kernel launch (the item table travels in the kernel arguments);
-// longer groups are launched in chunks of this size.
-constexpr int kGroupMax = 32;
+// Items per kernel launch (the item table travels in the kernel arguments,
+// up to ~13 KB of them); longer groups are launched in chunks of this size.
+constexpr int kGroupMax = 128;
 
 // ---- skinny.hip: decode-sized M (streams the weights once per 64 rows) ----
 struct SkinnyPlan {

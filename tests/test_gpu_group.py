@@ -82,10 +82,10 @@ def test_layer_group_two_ranks(layer, M, variant):
 @pytest.mark.parametrize("M", [1, 5, 64, 65, 300])
 @pytest.mark.parametrize("wdtype", [tsl.Q4G64, tsl.BF16])
 def test_long_group_concat_free(M, wdtype):
-    """40 column shards (more than one launch holds) of 5 weights, each
+    """160 column shards (more than one launch holds) of 5 weights, each
     writing its block of the weight's full bf16 output (ldy = N)."""
     t = torch()
-    K, N, tp = 384, 320, 8
+    K, N, tp = 384, 320, 32
     X = synth.normal_bf16(3100 + M, (M, K))
     dX = dev(X)
     items, checks = [], []
@@ -107,7 +107,7 @@ def test_long_group_concat_free(M, wdtype):
             items.append(dict(shard=sh, packed=buf, packed_bytes=nb, X=dX, ldx=K,
                               Y=outs[:, sh.n_off:], ldy=N, ydtype=tsl.BF16))
         checks.append((outs, full))
-    assert len(items) == 40
+    assert len(items) == 160
     run_group(items, wdtype, M)
     ref_x = oracle.bf16_to_f64(X)
     for outs, full in checks:
