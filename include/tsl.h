@@ -317,8 +317,9 @@ tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, const void *pa
  * ([mlxcel] "Communication patterns", all-reduce after row shards; [wiki]
  * "Details" §1):
  *     Y = (((X_0 W_0 + X_1 W_1) + X_2 W_2) + ...)
- * each product in binary32, the sum in item order, rounded once to the first
- * item's ydtype -- the result of shard_linear for each item followed by
+ * each product in binary32 (its k-partials, if the launch splits k, added
+ * in k order first), the sum in item order, rounded once to the first
+ * item's ydtype -- the result of the same products followed by
  * combine_partials(SUM).  All items of a set have the same n_len; the first
  * item's Y, ldy and ydtype apply and its accumulate must be 0; the Y, ldy,
  * ydtype and accumulate of the other items are ignored.  The last item of
@@ -361,9 +362,10 @@ tsl_status shard_linear_group_workspace_size(int32_t n_items, const tsl_linear_i
  * (q, k and v, or gate and up, of a column-parallel block; [wiki]
  * "Details" §1, [mlxcel] "Column Parallel"), or the shards of every rank
  * when all ranks' shares run on one GPU.  Each item computes what
- * shard_linear computes for its arguments, to the same accuracy (the
- * decode path may split k differently, so results need not be bitwise
- * equal to separate calls).  The items run in no particular order: no
+ * shard_linear computes for its arguments, to the same accuracy (a call
+ * too small to fill the chip splits k -- decode-sized M, or a GEMM launch
+ * of few tiles -- so a group and separate calls may add k-partials in
+ * different groupings and need not agree bitwise).  The items run in no particular order: no
  * item's Y may share an element with another item's Y or any item's X
  * (TSL_ERR_INVALID_ARG); column blocks of one output matrix with a common
  * ldy are fine.  The kernels are chosen by M (the largest row count).

@@ -269,6 +269,8 @@ size_t split_sets(std::vector<LinearItem> *items, int64_t M, char *ws) {
                 L.accumulate = 0;
                 L.set_len = 1;
                 L.set_pos = 0;
+                L.no_split = len > (size_t)kSetParts; // summed by launch_combine_sum
+
                 off += ((size_t)L.M * (size_t)L.g.Ns * 4 + 255) / 256 * 256;
             }
         }
@@ -354,11 +356,39 @@ tsl_status run_group(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_
             return TSL_ERR_INVALID_ARG;
     hipError_t e = skinny ? launch_skinny(sp, items.data(), n, wdtype, M, ws + parts, s)
                           : launch_prefill(pp, items.data(), n, wdtype, M, ws + parts, s);
-    if (e != hipSuccess || !parts)
+    if (e != hipSuccess)
         return from_hip(e);
+    // k-split GEMM products: each product's k-partials, in k order
+    auto kparts = [&](size_t i) {
+        return !skinny && pp.ks[i] > 1
+                   ? reinterpret_cast<const float *>(ws + parts + pp.p_off[i])
+                   : static_cast<const float *>(items[i].Y);
+    };
+    auto kcount = [&](size_t i) { return !skinny ? pp.ks[i] : 1; };
+    std::vector<SumSpec> sums;
+    for (size_t i = 0; i < ordered.size();) {
+        const size_t len = ordered[i].set_len;
+        if (len == 1 && kcount(i) > 1) { // a lone product: its k-partials into its Y
+            SumSpec sp1;
+            sp1.parts[0] = kparts(i);
+            sp1.ks[0] = kcount(i);
+            sp1.n_parts = 1;
+            sp1.M = items[i].M;
+            sp1.n = items[i].g.Ns;
+            sp1.Y = items[i].Y;
+            sp1.ldy = items[i].ldy;
+            sp1.ydtype = items[i].ydtype;
+            sums.push_back(sp1);
+        }
+        i += len;
+    }
+    if (!parts) {
+        if (!sums.empty())
+            e = launch_sum_sets((int)sums.size(), sums.data(), M, s);
+        return from_hip(e);
+    }
     // the rank sums of the split sets, in item order: sets of up to
     // kSetParts members share one launch, longer ones get their own
-    std::vector<SumSpec> sums;
     for (size_t i = 0; i < ordered.size(); i += ordered[i].set_len) {
         const LinearItem &L = ordered[i];
         if (L.set_len == 1)
@@ -373,8 +403,10 @@ tsl_status run_group(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_
             continue;
         }
         SumSpec sp;
-        for (int r = 0; r < L.set_len; ++r)
-            sp.parts[r] = static_cast<const float *>(items[i + r].Y);
+        for (int r = 0; r < L.set_len; ++r) {
+            sp.parts[r] = kparts(i + r);
+            sp.ks[r] = kcount(i + r);
+        }
         sp.n_parts = L.set_len;
         sp.M = L.M;
         sp.n = L.g.Ns;

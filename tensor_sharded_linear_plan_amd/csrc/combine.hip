@@ -109,6 +109,7 @@ __global__ void __launch_bounds__(256) splitk_kernel(const float *__restrict__ P
 // its own output; workgroup x -> (set, 1024-column block) by binary search.
 struct SumSet {
     const float *p[kSetParts];
+    int32_t ks[kSetParts]; // k-partials of each product
     void *Y;
     int64_t ldy, n;
     int64_t M;           // rows of this set
@@ -136,12 +137,25 @@ __global__ void __launch_bounds__(256) sum_sets_kernel(SumSets g) {
     const int64_t j = ((int64_t)(bid - st.start) * 256 + threadIdx.x) * E;
     if (j >= st.n)
         return;
+    const int64_t plane = st.M * st.n; // one k-partial
     for (int64_t m = blockIdx.y; m < st.M; m += gridDim.y) {
         const int64_t off = m * st.n + j;
         if constexpr (VEC) {
-            f32x4 acc = *reinterpret_cast<const f32x4 *>(st.p[0] + off);
+            // product r: its k-partials added in k order
+            auto product = [&](int r) {
+                f32x4 v = *reinterpret_cast<const f32x4 *>(st.p[r] + off);
+                for (int q = 1; q < st.ks[r]; ++q) {
+                    const f32x4 w = *reinterpret_cast<const f32x4 *>(st.p[r] + q * plane + off);
+                    v.x = v.x + w.x;
+                    v.y = v.y + w.y;
+                    v.z = v.z + w.z;
+                    v.w = v.w + w.w;
+                }
+                return v;
+            };
+            f32x4 acc = product(0);
             for (int r = 1; r < st.n_parts; ++r) {
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(st.p[r] + off);
+                const f32x4 v = product(r);
                 acc.x = acc.x + v.x;
                 acc.y = acc.y + v.y;
                 acc.z = acc.z + v.z;
@@ -152,9 +166,15 @@ __global__ void __launch_bounds__(256) sum_sets_kernel(SumSets g) {
             else
                 store4(static_cast<float *>(st.Y) + m * st.ldy + j, acc);
         } else {
-            float acc = st.p[0][off];
+            auto product = [&](int r) {
+                float v = st.p[r][off];
+                for (int q = 1; q < st.ks[r]; ++q)
+                    v = v + st.p[r][q * plane + off];
+                return v;
+            };
+            float acc = product(0);
             for (int r = 1; r < st.n_parts; ++r)
-                acc = acc + st.p[r][off];
+                acc = acc + product(r);
             if (st.y_bf16)
                 store1(static_cast<uint16_t *>(st.Y) + m * st.ldy + j, acc);
             else
@@ -317,8 +337,10 @@ hipError_t launch_sum_sets(int n_sets, const SumSpec *sets, int64_t M, hipStream
         for (int i = 0; i < cn; ++i) {
             const SumSpec &sp = sets[c0 + i];
             SumSet &st = g.s[i];
-            for (int r = 0; r < sp.n_parts; ++r)
+            for (int r = 0; r < sp.n_parts; ++r) {
                 st.p[r] = sp.parts[r];
+                st.ks[r] = sp.ks[r];
+            }
             st.Y = sp.Y;
             st.ldy = sp.ldy;
             st.n = sp.n;

@@ -47,12 +47,15 @@ hipError_t launch_combine_concat(int n_parts, const void *const *parts, size_t e
                                  int64_t M, int64_t n_each, int64_t ld_part, void *Y, int64_t ldy,
                                  hipStream_t stream);
 // Rank sums of several sum sets in one launch: set i adds its n_parts
-// contiguous [M_i][n] binary32 parts in order into Y (row stride ldy, F32 or
-// BF16).  n_parts <= kSetParts; M is the largest M_i.
+// products in order into Y (row stride ldy, F32 or BF16); product r is the
+// sum, in k order, of ks[r] contiguous [M_i][n] binary32 k-partials starting
+// at parts[r] (ks[r] == 1: the product itself).  n_parts <= kSetParts; M is
+// the largest M_i.
 constexpr int kSetParts = 8;
-constexpr int kMaxSets = 16;
+constexpr int kMaxSets = 64;
 struct SumSpec {
     const float *parts[kSetParts];
+    int ks[kSetParts] = {1, 1, 1, 1, 1, 1, 1, 1};
     int n_parts = 0;
     int64_t M = 0; // rows of this set
     int64_t n = 0;
@@ -106,6 +109,9 @@ struct LinearItem {
     int set_pos = 0;
     // token rows of this product (the call's M unless the item sets its own)
     int64_t M = 0;
+    // the GEMM path may not split this product's k (a member of a sum set
+    // too long for one sum launch)
+    bool no_split = false;
 };
 
 // Items per kernel launch (the item table travels in the kernel arguments,
@@ -146,6 +152,10 @@ struct PrefillPlan {
     // copy it reads (itself for the first reader of an X; -1: no copy)
     std::vector<size_t> w_off, x_off;
     std::vector<int> x_first;
+    // per item: k-splits (1: none) and the byte offset of its [ks][M][Ns]
+    // binary32 k-partials, which a sum launch then adds in k order
+    std::vector<int> ks;
+    std::vector<size_t> p_off;
     size_t ws_bytes = 0;
 };
 bool prefill_supported(tsl_dtype wdtype);

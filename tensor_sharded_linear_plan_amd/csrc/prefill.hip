@@ -64,6 +64,8 @@ struct GemmItem {
     int32_t start;     // first workgroup (a multiple of 8)
     int32_t accumulate, y_bf16;
     int64_t M;         // rows of this item
+    float *P;          // ks > 1: binary32 k-partials [ks][M][Ns]
+    int32_t ks, pad_;  // k-splits: tile t of split q covers stages [q nst / ks, (q+1) nst / ks)
 };
 
 struct GemmGroup {
@@ -155,16 +157,20 @@ gemm_kernel(GemmGroup grp) {
     const GemmItem &a = grp.it[lo];
     const int64_t M = a.M;
     const int local = bid - a.start;
-    const int t = (local & 7) * a.T8 + (local >> 3); // tile in band order
-    if (t >= a.MB * a.NB)
+    const int tk = (local & 7) * a.T8 + (local >> 3); // (split, tile) in band order
+    const int tiles = a.MB * a.NB;
+    if (tk >= tiles * a.ks)
         return; // padding workgroup
+    const int ksi = tk / tiles, t = tk - ksi * tiles;
     const int band = t / (8 * a.NB);
     const int first_m = band * 8;
     const int bm_cnt = a.MB - first_m < 8 ? a.MB - first_m : 8;
     const int in_band = t - band * 8 * a.NB;
     const int64_t mb = first_m + in_band % bm_cnt, nb = in_band / bm_cnt;
     const int64_t m0 = mb * BM, n0 = nb * BN;
-    const int nst = a.KT64 * (64 / C::BK); // stages
+    const int nst_all = a.KT64 * (64 / C::BK); // stages of the whole k-range
+    const int kb = ksi * nst_all / a.ks;       // this split's first stage
+    const int nst = (ksi + 1) * nst_all / a.ks - kb;
 
     // Sources of this wave's LDS blocks: block f = wave + 4 j < AF holds
     // activation rows RPB f .. RPB f + RPB - 1 of the tile, the others weight
@@ -192,8 +198,8 @@ gemm_kernel(GemmGroup grp) {
     constexpr int TPJ = 2 * (4 / C::S16); // 16-column tiles per weight block step
     const uint32_t lds0 = (uint32_t)(uintptr_t)(void __attribute__((address_space(3))) *)lds;
     auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
-        const char *xb = xbase + kt * (C::BK * 2);
-        const char *bb = bbase + kt * (C::BK / 32 * 1024);
+        const char *xb = xbase + (kt + kb) * (C::BK * 2);
+        const char *bb = bbase + (kt + kb) * (C::BK / 32 * 1024);
         const uint32_t dst = lds0 + slot * C::STAGE + wave * 1024;
         uint32_t a0 = aoff0, b0 = boff0;
         asm volatile("" : "+v"(a0), "+v"(b0)); // keep the per-j offsets out of registers
@@ -277,9 +283,16 @@ gemm_kernel(GemmGroup grp) {
     // compile-time row/column step times the (uniform) row stride.
     const int64_t row0 = m0 + wm * C::MT * 32 + 4 * (lane >> 5);
     const int64_t col0 = n0 + wn * C::NT * 32 + (lane & 31);
-    const int esz = a.y_bf16 ? 2 : 4;
-    char *ybase = static_cast<char *>(a.Y) + (row0 * a.ldy + col0) * esz;
-    const int64_t rstride = a.ldy * esz;
+    // a k-split writes its binary32 partial, [M][Ns] at split ksi
+    const bool part = a.ks > 1;
+    const bool ybf = part ? false : a.y_bf16;
+    const bool accu = part ? false : a.accumulate;
+    const int64_t ldy = part ? a.Ns : a.ldy;
+    char *yb0 = part ? reinterpret_cast<char *>(a.P + (int64_t)ksi * M * a.Ns)
+                     : static_cast<char *>(a.Y);
+    const int esz = ybf ? 2 : 4;
+    char *ybase = yb0 + (row0 * ldy + col0) * esz;
+    const int64_t rstride = ldy * esz;
     bool colok[C::NT];
 #pragma unroll
     for (int j = 0; j < C::NT; ++j)
@@ -297,12 +310,12 @@ gemm_kernel(GemmGroup grp) {
                 if (!colok[j])
                     continue;
                 const float v = acc[i][j][r];
-                if (a.y_bf16) {
+                if (ybf) {
                     __bf16 h = (__bf16)v;
                     *reinterpret_cast<uint16_t *>(yr + j * 64) = __builtin_bit_cast(uint16_t, h);
                 } else {
                     float *y = reinterpret_cast<float *>(yr + j * 128);
-                    *y = a.accumulate ? *y + v : v;
+                    *y = accu ? *y + v : v;
                 }
             }
         }
@@ -429,50 +442,89 @@ inline int64_t kpad64(int64_t k) { return (k + 63) / 64 * 64; }
 // LDS traffic (fragment reads of (TM + TN) x 2 bytes per k per wave plus
 // the (BM + BN) x 2 bytes the copies write, at 128 B/clk) and L2 delivery
 // ((BM + BN) x 2 bytes per 2 BM BN flops at a sustained ~40 B/clk).
-double variant_cost(const Variant &v, const LinearItem *items, int n, int64_t M) {
+// k-splits of the products of launch [c0, c1): each long product's k-range
+// in `factor` parts (at least 8 stages of 64 k each, at most 8 parts);
+// products that accumulate into Y or belong to a sum set too long for one
+// sum launch are not split.
+void split_ks(const LinearItem *items, int c0, int c1, int factor, int *ks) {
+    for (int i = c0; i < c1; ++i) {
+        ks[i - c0] = 1;
+        if (factor <= 1 || items[i].accumulate || items[i].no_split)
+            continue;
+        const int64_t cap = kpad64(items[i].g.Ks) / 64 / 8;
+        const int64_t k = factor < cap ? factor : cap;
+        ks[i - c0] = (int)(k < 1 ? 1 : (k > 8 ? 8 : k));
+    }
+}
+
+// A launch with fewer tiles than this -- a quarter of the CUs -- splits the
+// k-range of its long products toward one tile per CU.
+constexpr int64_t kSplitBelow = 64;
+
+// Modelled cost of one launch [c0, c1) with k-split factor `factor`.
+double chunk_cost(const Variant &v, double pen, const LinearItem *items, int c0, int c1,
+                  int factor) {
+    int ks[kGroupMax];
+    split_ks(items, c0, c1, factor, ks);
+    auto mbk = [&](int i) { return (items[i].M + v.bm - 1) / v.bm; };
+    double span = 0.0, extra = 0.0;
+    int64_t tiles = 0;
+    for (int i = c0; i < c1; ++i) {
+        tiles += mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn) * ks[i - c0];
+        if (ks[i - c0] > 1) // partials written and read once, ~3.3 KB per clock
+            extra += 2.0 * ks[i - c0] * (double)items[i].M * (double)items[i].g.Ns * 4 / 3333.0;
+    }
+    if (tiles > 16384) { // large: every CU busy to the end, to a tile
+        double work = 0.0, longest = 0.0;
+        for (int i = c0; i < c1; ++i) {
+            const double len = (double)kpad64(items[i].g.Ks) / 64.0 / ks[i - c0];
+            work += (double)(mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn) * ks[i - c0]) * len;
+            longest = len > longest ? len : longest;
+        }
+        span = work / 256.0 + longest;
+    } else {
+        std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
+        for (int i = 0; i < 256; ++i)
+            cu.push(0.0);
+        for (int i = c0; i < c1; ++i) {
+            const double len = (double)kpad64(items[i].g.Ks) / 64.0 / ks[i - c0];
+            const int64_t T = mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn) * ks[i - c0];
+            for (int64_t t = 0; t < T; ++t) {
+                const double f = cu.top() + len;
+                cu.pop();
+                cu.push(f);
+                span = f > span ? f : span;
+            }
+        }
+    }
+    // a stage of a bm x bn tile is bm bn / 32 clocks of MFMA
+    return span * (double)(v.bm * v.bn) * pen + extra * 32.0;
+}
+
+// Modelled cost of a variant over a group, each launch (kGroupMax items;
+// every launch drains before the next starts) with its k-split factor
+// (1 unless the launch has fewer than kSplitBelow tiles), which *factors
+// receives.
+double variant_cost(const Variant &v, const LinearItem *items, int n, std::vector<int> *factors) {
     const double TM = v.bm / v.wm, TN = v.bn / v.wn;
     const double flops = 2.0 * v.bm * v.bn; // per k
     const double lds = 4096.0 * (4.0 * (TM + TN) * 2 + (v.bm + v.bn) * 2) / flops / 128.0;
     const double l2 = 4096.0 * (v.bm + v.bn) * 2 / flops / 40.0;
     double pen = lds > l2 ? lds : l2;
     pen = pen > 1.0 ? pen : 1.0;
-    (void)M;
-    auto mbk = [&](int i) { return (items[i].M + v.bm - 1) / v.bm; };
-    // every launch (kGroupMax items) drains before the next starts: the
-    // spans of the launches add up
     double total = 0.0;
+    factors->clear();
     for (int c0 = 0; c0 < n; c0 += kGroupMax) {
         const int c1 = n - c0 < kGroupMax ? n : c0 + kGroupMax;
-        double span = 0.0;
         int64_t tiles = 0;
         for (int i = c0; i < c1; ++i)
-            tiles += mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn);
-        if (tiles > 16384) { // large: every CU busy to the end, to a tile
-            double work = 0.0, longest = 0.0;
-            for (int i = c0; i < c1; ++i) {
-                const double len = (double)kpad64(items[i].g.Ks) / 64.0;
-                work += (double)(mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn)) * len;
-                longest = len > longest ? len : longest;
-            }
-            span = work / 256.0 + longest;
-        } else {
-            std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
-            for (int i = 0; i < 256; ++i)
-                cu.push(0.0);
-            for (int i = c0; i < c1; ++i) {
-                const double len = (double)kpad64(items[i].g.Ks) / 64.0;
-                const int64_t T = mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn);
-                for (int64_t t = 0; t < T; ++t) {
-                    const double f = cu.top() + len;
-                    cu.pop();
-                    cu.push(f);
-                    span = f > span ? f : span;
-                }
-            }
-        }
-        total += span;
+            tiles += ((items[i].M + v.bm - 1) / v.bm) * ((items[i].g.Ns + v.bn - 1) / v.bn);
+        const int bf = tiles < kSplitBelow ? (int)((256 + tiles - 1) / tiles) : 1;
+        const double best = chunk_cost(v, pen, items, c0, c1, bf);
+        factors->push_back(bf);
+        total += best;
     }
-    return total * (double)(v.bm * v.bn) * pen;
+    return total;
 }
 
 } // namespace
@@ -480,16 +532,19 @@ double variant_cost(const Variant &v, const LinearItem *items, int n, int64_t M)
 bool prefill_supported(tsl_dtype wdtype) { return wdtype == TSL_BF16 || wdtype == TSL_Q4G64; }
 
 PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t M) {
+    (void)M;
     PrefillPlan best;
     double best_cost = 1e300;
+    std::vector<int> factors, best_factors;
     for (const Variant &v : kVariants) {
-        const double cost = variant_cost(v, items, n, M);
+        const double cost = variant_cost(v, items, n, &factors);
         if (cost < best_cost - 1e-9) {
             best_cost = cost;
             best.bm = v.bm;
             best.bn = v.bn;
             best.wm = v.wm;
             best.wn = v.wn;
+            best_factors = factors;
         }
     }
     // workspace: binary16 weight fragments of 4-bit items; activation
@@ -522,6 +577,20 @@ PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64
                 best.x_off[i] = best.x_off[first];
             }
         }
+    }
+    // k-splits (split_ks with the launch's modelled factor), their binary32
+    // partials after the other copies
+    best.ks.assign(n, 1);
+    best.p_off.assign(n, 0);
+    for (int c0 = 0, c = 0; c0 < n; c0 += kGroupMax, ++c) {
+        const int c1 = n - c0 < kGroupMax ? n : c0 + kGroupMax;
+        split_ks(items, c0, c1, best_factors[c], &best.ks[c0]);
+        for (int i = c0; i < c1; ++i)
+            if (best.ks[i] > 1) {
+                best.p_off[i] = off;
+                off += ((size_t)best.ks[i] * (size_t)items[i].M * (size_t)items[i].g.Ns * 4 + 255) /
+                       256 * 256;
+            }
     }
     best.ws_bytes = off;
     return best;
@@ -593,7 +662,9 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
             a.M = L.M;
             a.MB = (int32_t)((L.M + p.bm - 1) / p.bm);
             a.NB = (int32_t)((g.Ns + p.bn - 1) / p.bn);
-            a.T8 = (a.MB * a.NB + 7) / 8;
+            a.ks = p.ks[c0 + i];
+            a.P = reinterpret_cast<float *>(ws + p.p_off[c0 + i]);
+            a.T8 = (a.MB * a.NB * a.ks + 7) / 8;
             a.start = (int32_t)blocks;
             a.accumulate = L.accumulate;
             a.y_bf16 = L.ydtype == TSL_BF16;
@@ -612,7 +683,8 @@ int64_t prefill_blocks(const PrefillPlan &p, const LinearItem *items, int n, int
     for (int c0 = 0; c0 < n; c0 += kGroupMax) {
         int64_t blocks = 0;
         for (int i = c0; i < n && i < c0 + kGroupMax; ++i) {
-            const int64_t T = ((items[i].M + p.bm - 1) / p.bm) * ((items[i].g.Ns + p.bn - 1) / p.bn);
+            const int64_t T = ((items[i].M + p.bm - 1) / p.bm) *
+                              ((items[i].g.Ns + p.bn - 1) / p.bn) * p.ks[i];
             blocks += 8 * ((T + 7) / 8);
         }
         most = blocks > most ? blocks : most;

@@ -5,7 +5,9 @@ one activation matrix, gate and up another, o and down their own rank
 blocks), each output checked against the oracle like a single call; groups
 longer than one launch's item table; column shards writing disjoint blocks
 of one output (concat-free); and in the GEMM regime the group's results
-equal separate shard_linear calls bit for bit (same kernels, same k order).
+match separate shard_linear calls to binary32 rounding (the same kernels;
+a launch too small to fill the chip splits k, so a lone call may add its
+k-partials in other groupings).
 """
 import numpy as np
 import pytest
@@ -74,9 +76,12 @@ def test_layer_group_two_ranks(layer, M, variant):
             continue
         check(host(Y)[rows], ref, variant, what)
         if M > 64 and proj in ("k", "down"):
-            # GEMM regime: the group equals a separate call bit for bit
+            # GEMM regime: a separate call computes the same products
             single = linear(sh, wdtype, buf, nb, tsl.BF16, dX[src[proj]][:, sh.k_off:], sh.K, M)
-            assert t.equal(single, Y), (proj, r)
+            if variant == "integer":
+                assert t.equal(single, Y), (proj, r)
+            else:
+                assert normwise(host(single), host(Y)) <= 1e-5, (proj, r)
 
 
 @pytest.mark.parametrize("M", [1, 5, 64, 65, 300])
@@ -192,8 +197,9 @@ def test_sum_set_equals_products_then_combine(M):
 def test_items_with_their_own_rows(wdtype, M, rows):
     """Items of one call over different row counts (the per-expert products
     of a MoE layer): each equals the oracle over its own rows, nothing is
-    written past them, and in the GEMM regime each equals a separate call
-    over the same rows bit for bit when that call also takes the GEMM."""
+    written past them, and in the GEMM regime each matches a separate call
+    over the same rows (bit for bit on integers, to binary32 rounding
+    otherwise) when that call also takes the GEMM."""
     t = torch()
     K, N = 384, 200
     items, keep = [], []
@@ -231,4 +237,7 @@ def test_items_with_their_own_rows(wdtype, M, rows):
             assert normwise(got[:rw], ref) <= TOL, rw
         if M > 64 and rw > 64:
             single = linear(sh, code, buf, nb, tsl.BF16, dX, K, rw)
-            assert t.equal(single[:rw], Y[:rw]), rw
+            if integer:
+                assert t.equal(single[:rw], Y[:rw]), rw
+            else:
+                assert normwise(host(single)[:rw], got[:rw]) <= 1e-5, rw
