@@ -161,15 +161,17 @@ def test_row_layers_as_sum_sets(layer, M, variant):
             check(host(Y)[rows], ref, variant, what)
 
 
-@pytest.mark.parametrize("M", [1, 3, 16, 100])
-def test_sum_set_equals_products_then_combine(M):
+@pytest.mark.parametrize("M,K,N", [(1, 2048, 4096), (3, 2048, 4096), (16, 2048, 4096),
+                                   (100, 2048, 4096), (100, 8192, 512)])
+def test_sum_set_equals_products_then_combine(M, K, N):
     """A sum set gives the ordered binary32 sum of its members' products:
     bit for bit what separate products + combine_partials(SUM) give when the
-    products are computed the same way (here: one group without sets, with
-    every item large enough to need no k split), and the bf16 output is that
-    sum rounded once."""
+    products are computed the same way (here: one group of the same items
+    without sets -- at K = 8192, N = 512 a launch of 8 tiles, whose
+    products the GEMM splits into k-partials in both calls), and the bf16
+    output is that sum rounded once; the set also matches the oracle."""
     t = torch()
-    K, N, tp = 2048, 4096, 4
+    tp = 4
     w = Q4Weight(K, N, 3300, 3301, 3302)
     X = dev(synth.normal_bf16(3303 + M, (M, K)))
     shards = tsl.plan_linear(K, N, tp, tsl.ROW, 64)
@@ -187,6 +189,9 @@ def test_sum_set_equals_products_then_combine(M):
         run_group(sets, tsl.Q4G64, M)
         if ydt == tsl.F32:
             assert t.equal(Y, want)
+            Xf = oracle.bf16_to_f64(X.view(t.int16).cpu().numpy().view(np.uint16))
+            ref = oracle.gemm(Xf, oracle.dequant_q4(w.codes, w.scales, w.biases))
+            assert normwise(host(Y), ref) <= TOL
         else:
             assert np.array_equal(host_bits(Y), oracle.f64_to_bf16(host(want)))
 
