@@ -238,9 +238,44 @@ def prefill_bench(args, tsl, torch, synth, configs):
     torch.cuda.synchronize()
     sep_ms = start.elapsed_time(end) / 5
     log("prefill: %.3f ms/step as %d separate shard_linear calls" % (sep_ms, nitems))
+    per = per_projection(layer, M, packs, tsl, torch, configs, 5)
     return dict(ms=ms, flops=flops, bytes=nbytes, wall=wall, kernel_ms=k_ms,
                 kernel_tflops=flops / (k_ms * 1e-3) / 1e12, pack_gbs=pack_bytes / pack_s / 1e9,
-                nitems=nitems, separate_ms=sep_ms)
+                nitems=nitems, separate_ms=sep_ms, per_projection=per)
+
+
+def per_projection(layer, M, packs, tsl, torch, configs, reps):
+    """Rank 0's seven projections of a 4-bit layer, each as its own
+    shard_linear call into an f32 output, HIP-graph replay over the weight
+    copies in `packs`: time, TFLOP/s, GB/s of algorithmic bytes and the
+    fraction of the product's own roofline."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77 + M)
+    out = []
+    for proj in configs.PROJS:
+        sh = packs[0][(0, proj)][0]
+        X = torch.randn((M, sh.k_len), generator=g, device="cuda").to(torch.bfloat16)
+        Y = torch.empty((M, sh.n_len), dtype=torch.float32, device="cuda")
+        ws = tsl.shard_linear_workspace_size(sh, tsl.Q4G64, M)
+        wsb = torch.empty(max(ws, 256), dtype=torch.uint8, device="cuda")
+
+        def run(cp, stream):
+            _, buf, nb = packs[cp][(0, proj)]
+            tsl.shard_linear(sh, tsl.Q4G64, buf, nb, tsl.BF16, X, sh.k_len, M, tsl.F32, Y,
+                             sh.n_len, 0, wsb, ws, stream)
+        us = graph_time(torch, run, len(packs), reps)
+        flops = 2.0 * M * sh.k_len * sh.n_len
+        nbytes = (sh.k_len * sh.n_len // 2 + (sh.k_len // 64) * sh.n_len * 4 + M * sh.k_len * 2
+                  + M * sh.n_len * 4)
+        t_roof = max(flops / (PEAK_MFMA_F16 * 1e12), nbytes / (PEAK_HBM * 1e9)) * 1e6
+        out.append({"proj": proj, "K": sh.k_len, "N": sh.n_len, "us": round(us, 2),
+                    "TFLOP/s": round(flops / us / 1e6, 1),
+                    "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                    "bound": "mfma" if flops / (PEAK_MFMA_F16 * 1e12) > nbytes / (PEAK_HBM * 1e9)
+                    else "hbm", "roofline_frac": round(t_roof / us, 4)})
+    log("%s M=%d rank 0 per projection: %s" % (layer.name, M, ", ".join(
+        "%s %.1f us" % (r["proj"], r["us"]) for r in out)))
+    return out
 
 
 def collectives_bench(tsl, torch):
@@ -328,6 +363,9 @@ def decode_bench(args, tsl, torch, synth, configs):
                     "bytes_per_step": nbytes})
         log("decode M=%d: %.1f us/step, %.0f GB/s" % (M, us, gbs))
         del graph
+        if M == 1:
+            res[-1]["rank0_per_projection"] = per_projection(layer, M, packs, tsl, torch,
+                                                             configs, max(5, args.steps))
     return res
 
 
@@ -850,6 +888,7 @@ def main():
         "dense": dense,
         "pack_GBps": round(pre["pack_gbs"], 1),
         "prefill_separate_calls_ms_per_step": round(pre["separate_ms"], 4),
+        "prefill_rank0_per_projection": pre["per_projection"],
         "wall_s_timed": round(pre["wall"], 3),
     }
     print(json.dumps(line), flush=True)
