@@ -777,38 +777,40 @@ def moe_bench(args, tsl, torch, synth, configs):
 
 def cpu_baseline(synth, configs):
     """The oracle, as it stands, on a bounded sample of the prefill workload:
-    rank 0's gate shard (5120 -> 4352, 4-bit), dequantised and multiplied
-    for the first R token rows, R sized for ~10 s of host work."""
-    import numpy as np
+    the layer's shards in plan order (rank 0's q, k, v, o, gate, up, down,
+    then rank 1's, ...), each dequantised and multiplied over all 2048
+    token rows, until about 10 s of host work have been spent."""
     import oracle
     layer = configs.PRE27B
-    sh = oracle.spec(oracle.plan(layer.hidden, layer.n_q_heads, layer.n_kv_heads, layer.head_dim,
-                                 layer.ffn, layer.tp, layer.group), 0, "gate")
-    pi = configs.PROJS.index("gate")
-    seed = lambda t: synth.seed_of(layer.index, pi, t)
-    K, N = sh["K"], sh["N"]
-    codes = synth.q4_codes(seed(synth.T_CODES), (K, N))
-    sc = synth.uniform_bf16(seed(synth.T_SCALES), (K // 64, N), layer.scale_lo, layer.scale_hi)
-    bi = synth.normal_bf16(seed(synth.T_BIASES), (K // 64, N), layer.bias_std)
-    X = oracle.bf16_to_f64(synth.normal_bf16(seed(synth.T_X), (layer.ms[0], K)))
-    t0 = time.perf_counter()
-    W = oracle.dequant_q4(*oracle.slice_q4(codes, sc, bi, sh))
-    t_deq = time.perf_counter() - t0
-    probe = 32
-    t0 = time.perf_counter()
-    oracle.gemm(X[:probe], W)
-    t_probe = time.perf_counter() - t0
-    R = int(min(layer.ms[0], max(probe, probe * 10.0 / max(t_probe, 1e-3))))
-    t0 = time.perf_counter()
-    oracle.gemm(X[:R], W)
-    t = time.perf_counter() - t0 + t_deq
-    Ks, Ns = sh["k_len"], sh["n_len"]
+    M = layer.ms[0]
+    plan = oracle.plan(layer.hidden, layer.n_q_heads, layer.n_kv_heads, layer.head_dim,
+                       layer.ffn, layer.tp, layer.group)
+    flops, t, done = 0.0, 0.0, []
+    for r in range(layer.tp):
+        for pi, proj in enumerate(configs.PROJS):
+            if t >= 10.0:
+                break
+            sh = oracle.spec(plan, r, proj)
+            seed = lambda tt: synth.seed_of(layer.index, pi, tt)
+            K, N = sh["K"], sh["N"]
+            codes = synth.q4_codes(seed(synth.T_CODES), (K, N))
+            sc = synth.uniform_bf16(seed(synth.T_SCALES), (K // 64, N), layer.scale_lo,
+                                    layer.scale_hi)
+            bi = synth.normal_bf16(seed(synth.T_BIASES), (K // 64, N), layer.bias_std)
+            X = oracle.bf16_to_f64(synth.normal_bf16(seed(synth.T_X), (M, K)))
+            Xr = oracle.slice_input(X, sh)
+            t0 = time.perf_counter()
+            W = oracle.dequant_q4(*oracle.slice_q4(codes, sc, bi, sh))
+            oracle.gemm(Xr, W)
+            t += time.perf_counter() - t0
+            flops += 2.0 * M * sh["k_len"] * sh["n_len"]
+            done.append("%d:%s" % (r, proj))
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-    return {"value": round(2.0 * R * Ks * Ns / t / 1e12, 5), "unit": "TFLOP/s",
-            "cores": threads, "kind": "oracle",
-            "sample": "rank-0 gate shard of the prefill workload (%d->%d, 4-bit g64): dequantise "
-                      "+ naive fp64 GEMM over the first %d of %d token rows, %.1f s"
-                      % (Ks, Ns, R, layer.ms[0], t)}
+    return {"value": round(flops / t / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of the prefill workload's 28 shards (%s; 4-bit g64, all %d token "
+                      "rows): dequantise + naive fp64 GEMM, %.1f s" % (len(done), " ".join(done),
+                                                                         M, t)}
 
 
 def main():
