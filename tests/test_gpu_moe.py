@@ -212,3 +212,21 @@ def test_moe30b_expert_parallel_sampled():
             ref[i] += float(w[tk, j]) * (Hf[tk, j][None, :] @ ex.f64(
                 e, "down", {"strategy": oracle.REPLICATED}, cols))[0]
     assert normwise(host(Y)[np.ix_(toks, cols)], ref) <= TOL
+
+
+def test_moe_combine_many_tokens_and_scalar_path():
+    """More tokens than one launch's grid height, and a width that takes the
+    one-column path: the router-weighted sum against the oracle."""
+    t = torch()
+    for T, k, n, R in ((70001, 2, 8, 1000), (300, 3, 10, 500)):
+        rng = synth.rng(T + n)
+        P = synth.normal_f32(T, (R, n))
+        slot_row = rng.integers(-1, R, size=T * k).astype(np.int32)
+        w = synth.normal_f32(T + 1, (T, k))
+        Y = t.full((T, n), float("nan"), dtype=t.float32, device="cuda")
+        tsl.moe_combine(dev(P), n, R, dev(slot_row), dev(w.ravel()), T, k, n, tsl.F32, Y, n)
+        ys = np.zeros((T, k, n))
+        held = slot_row.reshape(T, k) >= 0
+        ys[held] = P[slot_row.reshape(T, k)[held]]
+        want = oracle.moe_combine(ys, w, held)
+        assert normwise(host(Y), want) <= 1e-6, (T, n)

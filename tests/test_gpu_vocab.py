@@ -199,3 +199,19 @@ def test_lm_head_logits_vocab_parallel(lm_head, M, variant):
         assert np.array_equal(got[:, cols], ref)
     else:
         assert normwise(got[:, cols], ref) <= TOL
+
+
+def test_embed_lookup_many_rows():
+    """More token rows than one launch's grid height (65535): the rows loop."""
+    t = torch()
+    vocab, hidden, tp, M = 512, 8, 2, 70001
+    E = synth.normal_bf16(41, (vocab, hidden))
+    tokens = synth.token_ids(42, M, vocab)
+    sh = tsl.plan_vocab(vocab, hidden, tp)[2]  # rank 1
+    Y = t.full((M, hidden), float("nan"), dtype=t.float32, device="cuda")
+    tsl.embed_lookup(sh, tsl.BF16, dev(E)[sh.k_off:], hidden, dev(tokens), M, tsl.F32, Y, hidden)
+    want = oracle.embed_lookup(oracle.bf16_to_f64(E), tokens, spec_dict(sh))
+    got = Y.cpu().numpy()
+    owned = tokens >= sh.k_off
+    assert np.array_equal(got[owned].astype(np.float64), want[owned])
+    assert np.all(got[~owned].view(np.uint32) == NEG0_F32)
