@@ -264,7 +264,9 @@ tsl_status pack_shard(const tsl_shard *shard, tsl_dtype wdtype, const void *W, i
  * partial sums for decode-sized M; with M > 64, for 4-bit weights the shard
  * expanded to binary16 (2 bytes per weight) and a binary16 copy of the
  * activations (M x k_len x 2 bytes), for BF16 weights a zero-padded copy of
- * the activations when k_len is not a multiple of 64.
+ * the activations when k_len is not a multiple of 64, and when the product
+ * is too small to fill the chip the binary32 partials of its k-splits
+ * (splits x M x n_len x 4 bytes).
  */
 tsl_status shard_linear_workspace_size(const tsl_shard *shard, tsl_dtype wdtype, int64_t M,
                                        size_t *bytes);
