@@ -595,8 +595,13 @@ SkinnyPlan skinny_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t
     if (p.stream) {
         // 4 waves x NTW tiles per workgroup, each wave over the whole k-range;
         // k split across workgroups only when the group is too small to put
-        // ~2 workgroups on every CU
-        p.ntw = rows <= 16 ? 1 : 2;
+        // ~2 workgroups on every CU.  Two tiles per wave halve the
+        // activation reads per weight byte: for more than 16 rows always,
+        // for 5..16 rows when the group still has >= 8 workgroups per CU
+        int64_t wg1 = 0;
+        for (int i = 0; i < n; ++i)
+            wg1 += (items[i].g.Nt + 3) / 4 * p.m_blocks[i];
+        p.ntw = rows > 16 || (rows > 4 && wg1 >= 2048) ? 2 : 1;
         const int bk = stream_bk(wdtype == TSL_Q4G64 ? W_Q4 : W_BF16);
         int64_t base = 0;
         for (int i = 0; i < n; ++i) {
