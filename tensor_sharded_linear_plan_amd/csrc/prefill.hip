@@ -16,11 +16,13 @@
 //     16-byte chunk, so a 32-column x 16-k MFMA fragment is two 512-byte
 //     runs.
 // A stage covers 64 k (32 k when three 64-k stages would not fit in 160 KB)
-// and stages rotate through up to 4 LDS slots: the copies of stage k + S - 1
-// (S slots) are issued right after the barrier that opens stage k and the
-// first fragment reads, and each wave waits only for its own copies of
-// stage k before that barrier.  Inside a stage the fragments of the next
-// 16-k step are read while the MFMAs of the current one run.
+// and stages rotate through S <= 4 LDS slots.  Fragment reads run one 16-k
+// step ahead of the MFMAs.  The barrier that publishes stage k + 1 sits
+// before the last 16-k step of stage k: each wave first waits for its own
+// copies of stage k + 1 and for its own reads of stage k; after the barrier
+// it reads the first fragments of stage k + 1 and, between the MFMAs of the
+// last step of stage k, issues the copies of stage k + S into the slot of
+// stage k, which no wave reads any more.
 //
 // Operands: bf16 x bf16, or f16 x f16 for 4-bit weights.  For the latter a
 // prep kernel first expands the weights to binary16 fragments (w = s q + b
@@ -96,6 +98,7 @@ struct G {
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 tiles");
     static_assert(AF % 4 == 0 && BF % 4 == 0, "LDS blocks must divide over 4 waves");
     static_assert(NS >= 2, "two stages must fit in LDS");
+    static_assert(S16 % 2 == 0, "fragment buffers alternate by step parity");
     static_assert(FPW * (NS - 2) < 64, "vmcnt range");
 };
 
@@ -133,6 +136,9 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
 }
+
+// s_waitcnt lgkmcnt(0) leaving the other counters alone.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14)); }
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -197,24 +203,24 @@ gemm_kernel(GemmGroup grp) {
     const int tfirst = 2 * (wave / C::S16) + ((lane & 31) >> 4);
     constexpr int TPJ = 2 * (4 / C::S16); // 16-column tiles per weight block step
     const uint32_t lds0 = (uint32_t)(uintptr_t)(void __attribute__((address_space(3))) *)lds;
-    auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
-        const char *xb = xbase + (kt + kb) * (C::BK * 2);
-        const char *bb = bbase + (kt + kb) * (C::BK / 32 * 1024);
-        const uint32_t dst = lds0 + slot * C::STAGE + wave * 1024;
+    // copy j (0 <= j < FPW) of this wave for stage kt into LDS slot `slot`
+    auto issue1 = [&](int kt, int slot, int j) __attribute__((always_inline)) {
+        const uint32_t dst = lds0 + slot * C::STAGE + wave * 1024 + 4 * j * 1024;
         uint32_t a0 = aoff0, b0 = boff0;
         asm volatile("" : "+v"(a0), "+v"(b0)); // keep the per-j offsets out of registers
-#pragma unroll
-        for (int j = 0; j < C::FPW; ++j) {
-            uint32_t off;
-            if (j < C::AF / 4) {
-                const uint32_t o = a0 + (uint32_t)j * astep;
-                off = o < alim ? o : alim;
-            } else {
-                const int tt = tfirst + TPJ * (j - C::AF / 4);
-                off = b0 + (uint32_t)(tt < tmax ? tt : tmax) * tstep;
-            }
-            dma16(j < C::AF / 4 ? xb : bb, off, dst + 4 * j * 1024);
+        if (j < C::AF / 4) {
+            const uint32_t o = a0 + (uint32_t)j * astep;
+            dma16(xbase + (kt + kb) * (C::BK * 2), o < alim ? o : alim, dst);
+        } else {
+            const int tt = tfirst + TPJ * (j - C::AF / 4);
+            dma16(bbase + (kt + kb) * (C::BK / 32 * 1024),
+                  b0 + (uint32_t)(tt < tmax ? tt : tmax) * tstep, dst);
         }
+    };
+    auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < C::FPW; ++j)
+            issue1(kt, slot, j);
     };
 
     f32x16 acc[C::MT][C::NT];
@@ -226,10 +232,27 @@ gemm_kernel(GemmGroup grp) {
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.f;
 
+    // fragments of 16-k step s of the stage in `slot`
     u32x4 af[2][C::MT], bfr[2][C::NT];
-    auto stage = [&](int kt, int slot) __attribute__((always_inline)) {
-        // this wave's copies of stage kt are done once only the younger
-        // stages' copies (at most NS - 2) may still be in flight
+    auto rd = [&](int slot, int s, u32x4 (&x)[C::MT], u32x4 (&y)[C::NT]) __attribute__((always_inline)) {
+        const char *As = lds + slot * C::STAGE;
+        const char *Bs = As + C::AF * 1024;
+#pragma unroll
+        for (int i = 0; i < C::MT; ++i) {
+            const int r = (wm * C::MT + i) * 32 + (lane & 31); // row in the block tile
+            const int k8 = 2 * s + (lane >> 5);                // 8-k run in the stage
+            const int rb = r % C::RPB;
+            x[i] = *reinterpret_cast<const u32x4 *>(As + (r / C::RPB) * 1024 + rb * (C::BK * 2) +
+                                                    ((k8 ^ swz<C::CPR>(rb)) * 16));
+        }
+#pragma unroll
+        for (int j = 0; j < C::NT; ++j)
+            y[j] = *reinterpret_cast<const u32x4 *>(
+                Bs + (((wn * C::NT + j) * C::S16 + s) * 64 + lane) * 16);
+    };
+    // this wave's copies of stage kt are done once only the younger stages'
+    // copies (at most NS - 2) may still be in flight
+    auto wait_stage = [&](int kt) __attribute__((always_inline)) {
         const int younger = nst - 1 - kt < C::NS - 2 ? nst - 1 - kt : C::NS - 2;
         if (C::NS >= 4 && younger >= 2)
             wait_vmcnt<C::FPW * 2>();
@@ -237,45 +260,54 @@ gemm_kernel(GemmGroup grp) {
             wait_vmcnt<C::FPW>();
         else
             wait_vmcnt<0>();
-        barrier();
-        const char *As = lds + slot * C::STAGE;
-        const char *Bs = As + C::AF * 1024;
-        auto rd = [&](int s, u32x4 (&x)[C::MT], u32x4 (&y)[C::NT]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < C::MT; ++i) {
-                const int r = (wm * C::MT + i) * 32 + (lane & 31); // row in the block tile
-                const int k8 = 2 * s + (lane >> 5);                // 8-k run in the stage
-                const int rb = r % C::RPB;
-                x[i] = *reinterpret_cast<const u32x4 *>(As + (r / C::RPB) * 1024 + rb * (C::BK * 2) +
-                                                        ((k8 ^ swz<C::CPR>(rb)) * 16));
-            }
-#pragma unroll
-            for (int j = 0; j < C::NT; ++j)
-                y[j] = *reinterpret_cast<const u32x4 *>(
-                    Bs + (((wn * C::NT + j) * C::S16 + s) * 64 + lane) * 16);
-        };
-        rd(0, af[0], bfr[0]);
-        // the copies of stage kt + NS - 1 go into the slot read in stage kt - 1
-        if (kt + C::NS - 1 < nst)
-            issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1);
-#pragma unroll
-        for (int s = 0; s < C::S16; ++s) {
-            if (s + 1 < C::S16)
-                rd(s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
-#pragma unroll
-            for (int i = 0; i < C::MT; ++i)
-#pragma unroll
-                for (int j = 0; j < C::NT; ++j)
-                    acc[i][j] = mfma32(af[s & 1][i], bfr[s & 1][j], acc[i][j], OP);
-        }
     };
 
-    for (int k = 0; k < C::NS - 1 && k < nst; ++k)
+    for (int k = 0; k < C::NS && k < nst; ++k)
         issue(k, k);
+    wait_stage(0);
+    barrier();
+    rd(0, 0, af[0], bfr[0]);
     int slot = 0;
     for (int kt = 0; kt < nst; ++kt) {
-        stage(kt, slot);
-        slot = slot + 1 == C::NS ? 0 : slot + 1;
+        const int next = slot + 1 == C::NS ? 0 : slot + 1;
+#pragma unroll
+        for (int s = 0; s < C::S16; ++s) {
+            const int b = s & 1; // S16 is even, so step parity is s parity
+            bool copies = false;
+            if (s + 1 < C::S16) {
+                rd(slot, s + 1, af[b ^ 1], bfr[b ^ 1]);
+            } else {
+                // this wave's reads of stage kt have landed (on every path,
+                // so that the MFMAs below wait for nothing newer)
+                wait_lgkm0();
+                if (kt + 1 < nst) {
+                    wait_stage(kt + 1);
+                    barrier();
+                    rd(next, 0, af[b ^ 1], bfr[b ^ 1]);
+                    copies = kt + C::NS < nst;
+                }
+            }
+            // the copies of stage kt + NS go into the slot of stage kt,
+            // spread between the MFMAs of the last step so that they issue
+            // in their shadow
+#pragma unroll
+            for (int q = 0; q < C::MT * C::NT; ++q) {
+                const int i = q / C::NT, j = q % C::NT;
+                acc[i][j] = mfma32(af[b][i], bfr[b][j], acc[i][j], OP);
+                if (s + 1 == C::S16) {
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int f = q * C::FPW / (C::MT * C::NT); f < (q + 1) * C::FPW / (C::MT * C::NT); ++f)
+                        if (copies)
+                            issue1(kt + C::NS, slot, f);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // keep the steps in this order: the scheduler would otherwise
+            // sink MFMAs below the waits and the barrier of the next step
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        slot = next;
     }
 
     // ---- epilogue: acc reg r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32 ----
