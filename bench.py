@@ -239,9 +239,45 @@ def prefill_bench(args, tsl, torch, synth, configs):
     sep_ms = start.elapsed_time(end) / 5
     log("prefill: %.3f ms/step as %d separate shard_linear calls" % (sep_ms, nitems))
     per = per_projection(layer, M, packs, tsl, torch, configs, 5)
+    lib = library_gemm(M, [sh for sh, _, _ in packs[0].values()], torch)
+    log("prefill: the same %d products as torch.matmul, dense f16 operands: %.1f us, %.0f TFLOP/s"
+        % (len(packs[0]), lib["us"], lib["TFLOP/s"]))
     return dict(ms=ms, flops=flops, bytes=nbytes, wall=wall, kernel_ms=k_ms,
                 kernel_tflops=flops / (k_ms * 1e-3) / 1e12, pack_gbs=pack_bytes / pack_s / 1e9,
-                nitems=nitems, separate_ms=sep_ms, per_projection=per)
+                nitems=nitems, separate_ms=sep_ms, per_projection=per, library=lib)
+
+
+def library_gemm(M, shards, torch, reps=5):
+    """Context for the prefill figure: the step's shard products as plain
+    torch.matmul calls (the vendor GEMM library) on dense random f16
+    operands of the same shapes -- no 4-bit expansion, no rank sums."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    xs = {}
+    ops = []
+    for sh in shards:
+        if sh.k_len not in xs:
+            xs[sh.k_len] = torch.randn((M, sh.k_len), generator=g, device="cuda",
+                                       dtype=torch.float16)
+        ops.append((xs[sh.k_len], torch.randn((sh.k_len, sh.n_len), generator=g, device="cuda",
+                                              dtype=torch.float16)))
+    flops = sum(2.0 * M * b.shape[0] * b.shape[1] for _, b in ops)
+    for _ in range(2):
+        for a, b in ops:
+            torch.matmul(a, b)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        for a, b in ops:
+            torch.matmul(a, b)
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / reps
+    del xs, ops
+    return {"what": "torch.matmul of the same shard products, dense random f16 operands",
+            "us": round(us, 1), "TFLOP/s": round(flops / us / 1e6, 1)}
 
 
 def per_projection(layer, M, packs, tsl, torch, configs, reps):
@@ -891,6 +927,7 @@ def main():
         "pack_GBps": round(pre["pack_gbs"], 1),
         "prefill_separate_calls_ms_per_step": round(pre["separate_ms"], 4),
         "prefill_rank0_per_projection": pre["per_projection"],
+        "prefill_library_gemm": pre["library"],
         "wall_s_timed": round(pre["wall"], 3),
     }
     print(json.dumps(line), flush=True)
