@@ -7,8 +7,9 @@ rank's shards and runs them in lockstep), here for one tp=4 layer of a
 27B-class model with 4-bit weights at M = 2048 prefill tokens: for every
 rank r and projection p, shard_linear(r, p) -- column outputs written
 straight into their block of the full output (the concat), the 4 o and
-the 4 down shards each a sum set (their on-device rank sum) -- all 28
-products in one shard_linear_group call.
+the 4 down shards each a sum set (their on-device rank sum, which the
+4-bit GEMM regime accumulates inside one product over the ranks' k-ranges
+end to end) -- all 28 products in one shard_linear_group call.
 The plan is recomputed each step (host only); packing is load-time work
 and is timed separately.
 
@@ -911,8 +912,10 @@ def main():
                      "frac": round(pre["kernel_tflops"] / PEAK_MFMA_F16, 4),
                      "traffic": measured_traffic(),
                      "kernel": "the step's shard_linear_group call: prep_kernel (4-bit -> "
-                               "f16 weights, activations -> f16), gemm_kernel (f16 MFMA, all 28 "
-                               "shard GEMMs), sum_sets_kernel (the o and down rank sums)",
+                               "f16 weights, activations -> f16), gemm_kernel (f16 MFMA: the 20 "
+                               "column-shard GEMMs, and the 4 o and the 4 down shards each as "
+                               "one GEMM over the ranks' k-ranges end to end, the rank sum "
+                               "accumulated in the GEMM)",
                      "avg_launch_us": round(pre["kernel_ms"] * 1e3, 2)},
         "cpu_baseline": cpu,
         "decode": {"workload": "dec7b: every rank of one tp=4 7B-class layer (hidden 3584, ffn "

@@ -328,6 +328,13 @@ tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, const void *pa
  * a call has sum_next = 0.  The products of a set go to binary32 partials
  * in the workspace (rows x n_len x 4 bytes each, counted by
  * shard_linear_group_workspace_size); one more launch adds them.
+ * Exception, Q4G64 weights with M > 64: a set of at most 8 members whose
+ * k_len are equal multiples of 128 is ONE product over the members'
+ * k-ranges laid end to end in item order, Y = [X_0 X_1 ...] [W_0; W_1; ...]
+ * -- the same sum, accumulated in binary32 in that k order inside the GEMM
+ * and rounded once (bit for bit the product of the unsharded weight over
+ * the whole X when the members are the row shards of one weight), with no
+ * partials and no sum launch.
  *
  * rows: the item's token rows, 1 <= rows <= M (0 means M): it reads rows
  * [0, rows) of X and writes rows [0, rows) of Y.  Items of different row

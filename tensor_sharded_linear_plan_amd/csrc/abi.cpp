@@ -247,6 +247,53 @@ std::vector<LinearItem> launch_order(const std::vector<LinearItem> &items) {
     return v;
 }
 
+// 4-bit weights in the GEMM regime: a sum set whose members have equal
+// k-ranges of whole 128-k records becomes one product over the members'
+// k-ranges laid end to end in set order, Y = [X_0 X_1 ...] [W_0; W_1; ...]
+// -- the rank sum accumulated inside the GEMM, with no binary32 partials
+// and no sum launch (the prep pass writes each member's binary16 weights
+// and activations at its k offset of the joined operands).  Other sets, and
+// every set of other weight types or of the decode regime, pass unchanged.
+std::vector<LinearItem> concat_sets(const std::vector<LinearItem> &in, tsl_dtype wdtype,
+                                    int64_t M) {
+    if (wdtype != TSL_Q4G64 || use_skinny(wdtype, M))
+        return in;
+    std::vector<LinearItem> out;
+    out.reserve(in.size());
+    for (size_t i = 0; i < in.size();) {
+        const size_t len = in[i].set_len;
+        bool join = len > 1 && len <= (size_t)kSetParts &&
+                    (int64_t)len * in[i].g.Kpad < kPrefillMaxStride;
+        for (size_t r = 0; join && r < len; ++r)
+            join = in[i + r].g.Ks % 128 == 0 && in[i + r].g.Ks == in[i].g.Ks;
+        if (!join) {
+            for (size_t r = 0; r < len; ++r)
+                out.push_back(in[i + r]);
+            i += len;
+            continue;
+        }
+        LinearItem c = in[i];
+        c.cat = (int)len;
+        c.set_len = 1;
+        c.set_pos = 0;
+        c.g.Ks *= (int64_t)len;
+        c.g.KT *= (int64_t)len;
+        c.g.Kpad *= (int64_t)len;
+        c.g.total_bytes = 0; // no packed buffer of its own
+        c.packed = nullptr;
+        c.X = nullptr; // never shares an activation copy
+        c.ldx = 0;
+        for (size_t r = 0; r < len; ++r) {
+            c.seg_packed[r] = in[i + r].packed;
+            c.seg_X[r] = in[i + r].X;
+            c.seg_ldx[r] = in[i + r].ldx;
+        }
+        out.push_back(c);
+        i += len;
+    }
+    return out;
+}
+
 // Sum sets: each member of a set runs into its own binary32 partial (in
 // the workspace, ahead of what the plan needs), balanced with every other
 // product of the group; one more launch then adds the partials of all sets
@@ -309,7 +356,7 @@ bool matrices_overlap(const void *pa, int64_t Ma, int64_t wa, int64_t lda, size_
 size_t group_workspace(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_t M) {
     if (M == 0 || in.empty())
         return 0;
-    std::vector<LinearItem> items = launch_order(in);
+    std::vector<LinearItem> items = launch_order(concat_sets(in, wdtype, M));
     const size_t parts = split_sets(&items, M, nullptr);
     if (use_skinny(wdtype, M))
         return parts + skinny_plan(items.data(), (int)items.size(), wdtype, M).ws_bytes;
@@ -321,7 +368,7 @@ tsl_status run_group(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_
                      void *workspace, size_t ws_bytes, void *stream) {
     if (M == 0)
         return TSL_OK;
-    const std::vector<LinearItem> ordered = launch_order(in);
+    const std::vector<LinearItem> ordered = launch_order(concat_sets(in, wdtype, M));
     std::vector<LinearItem> items = ordered;
     // (a null or short workspace is rejected below, before any launch)
     char *ws = static_cast<char *>(workspace);

@@ -112,6 +112,14 @@ struct LinearItem {
     // the GEMM path may not split this product's k (a member of a sum set
     // too long for one sum launch)
     bool no_split = false;
+    // a sum set computed as ONE product over its members' k-ranges laid end
+    // to end in set order (4-bit weights, GEMM regime): cat members of equal
+    // k_len; g, Y, ldy, ydtype describe the joined product, seg_* each
+    // member's packed weights and activations (X and packed unused)
+    int cat = 1;
+    const void *seg_packed[kSetParts] = {};
+    const void *seg_X[kSetParts] = {};
+    int64_t seg_ldx[kSetParts] = {};
 };
 
 // Items per kernel launch (the item table travels in the kernel arguments,

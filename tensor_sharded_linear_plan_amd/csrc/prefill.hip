@@ -354,20 +354,26 @@ gemm_kernel(GemmGroup grp) {
 }
 
 // ---- prep: 4-bit weights -> binary16 fragments, ragged-K activations -> padded copy ----
+// One piece of the prep pass: a product's weights and activation copy, or
+// one member's share of a joined sum set (written at its k offset).
 struct PrepItem {
-    // weights (4-bit items): packed records (codes, scale/bias pairs) -> fragments
+    // weights (4-bit items): packed records (codes, scale/bias pairs) ->
+    // fragments; column tile nt's 32-k fragments start at nt * kt_ld, this
+    // piece's at kt_off within them
     const char *q4;
     u32x4 *w_out;
-    // activations (K not a multiple of 64): rows of ldx_in -> rows of Kpad
+    // activations: Ks columns of rows of ldx_in -> Kpad columns (zero past
+    // Ks) of rows of x_ld
     const uint16_t *x_in;
     uint16_t *x_out;
-    int64_t ldx_in;
+    int64_t ldx_in, x_ld;
     int64_t w_chunks;  // 16-byte code chunks
     int64_t x_units;   // 8-element output units (M * Kpad / 8)
     int32_t KB, Gs;
     int32_t Ks, Kpad;
+    int32_t kt_ld, kt_off;
     int32_t w_blocks;  // workgroups [start, start + w_blocks) do weights
-    int32_t start, pad_;
+    int32_t start;
 };
 
 struct PrepGroup {
@@ -412,7 +418,7 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepGroup grp) {
             for (int q = 0; q < 2; ++q) {
                 const int tt = 2 * h + q;
                 const f16x8 v = q4_dequant_f16(w[tt], s, cb);
-                p.w_out[((nt * ((int64_t)p.KB * 4) + blk * 4 + tt) * 64) + lane] =
+                p.w_out[((nt * (int64_t)p.kt_ld + p.kt_off + blk * 4 + tt) * 64) + lane] =
                     __builtin_bit_cast(u32x4, v);
             }
         }
@@ -441,7 +447,7 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepGroup grp) {
         for (int j = 0; j < 4; ++j)
             v[j] = bf16pair_to_f16pair(v[j]);
     }
-    *reinterpret_cast<u32x4 *>(p.x_out + m * p.Kpad + k) = v;
+    *reinterpret_cast<u32x4 *>(p.x_out + m * p.x_ld + k) = v;
 }
 
 typedef void (*GemmFn)(GemmGroup);
@@ -637,10 +643,9 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
     char *ws = static_cast<char *>(workspace);
     for (int c0 = 0; c0 < n; c0 += kGroupMax) {
         const int cn = n - c0 < kGroupMax ? n - c0 : kGroupMax;
-        // 1. prep: expand 4-bit weights, copy activations (once per X)
-        PrepGroup pg{};
-        pg.to_f16 = wdtype == TSL_Q4G64;
-        int64_t pblocks = 0;
+        // 1. prep: expand 4-bit weights, copy activations (once per X); a
+        // joined sum set is one piece per member, at the member's k offset
+        std::vector<PrepItem> pieces;
         for (int i = 0; i < cn; ++i) {
             const LinearItem &L = items[c0 + i];
             const PackGeom &g = L.g;
@@ -648,23 +653,38 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
             const bool xcopy = p.x_first[c0 + i] == c0 + i;
             if (!q4 && !xcopy)
                 continue;
-            PrepItem &a = pg.it[pg.n++];
-            a.q4 = static_cast<const char *>(L.packed);
-            a.w_out = reinterpret_cast<u32x4 *>(ws + p.w_off[c0 + i]);
-            a.x_in = static_cast<const uint16_t *>(L.X);
-            a.x_out = reinterpret_cast<uint16_t *>(ws + p.x_off[c0 + i]);
-            a.ldx_in = L.ldx;
-            a.w_chunks = q4 ? g.Nt * g.KT * 64 : 0;
-            a.Kpad = (int32_t)kpad64(g.Ks);
-            a.x_units = xcopy ? L.M * (a.Kpad / 8) : 0;
-            a.KB = (int32_t)g.KT;
-            a.Gs = (int32_t)(g.Ks / 64);
-            a.Ks = (int32_t)g.Ks;
-            a.w_blocks = (int32_t)((a.w_chunks + 255) / 256);
-            a.start = (int32_t)pblocks;
-            pblocks += a.w_blocks + (a.x_units + 255) / 256;
+            const int R = L.cat;
+            const int64_t kseg = g.Ks / R, kbseg = g.KT / R; // per member
+            for (int r = 0; r < R; ++r) {
+                PrepItem a{};
+                a.q4 = static_cast<const char *>(R > 1 ? L.seg_packed[r] : L.packed);
+                a.w_out = reinterpret_cast<u32x4 *>(ws + p.w_off[c0 + i]);
+                a.kt_ld = (int32_t)(g.KT * 4);
+                a.kt_off = (int32_t)(r * kbseg * 4);
+                a.x_in = static_cast<const uint16_t *>(R > 1 ? L.seg_X[r] : L.X);
+                a.x_out = reinterpret_cast<uint16_t *>(ws + p.x_off[c0 + i]) + r * kseg;
+                a.ldx_in = R > 1 ? L.seg_ldx[r] : L.ldx;
+                a.x_ld = kpad64(g.Ks);
+                a.w_chunks = q4 ? g.Nt * kbseg * 64 : 0;
+                a.Kpad = (int32_t)(R > 1 ? kseg : kpad64(g.Ks));
+                a.x_units = xcopy ? L.M * (a.Kpad / 8) : 0;
+                a.KB = (int32_t)kbseg;
+                a.Gs = (int32_t)(kseg / 64);
+                a.Ks = (int32_t)kseg;
+                a.w_blocks = (int32_t)((a.w_chunks + 255) / 256);
+                pieces.push_back(a);
+            }
         }
-        if (pg.n > 0) {
+        for (size_t q0 = 0; q0 < pieces.size(); q0 += kGroupMax) {
+            PrepGroup pg{};
+            pg.to_f16 = wdtype == TSL_Q4G64;
+            int64_t pblocks = 0;
+            for (size_t q = q0; q < pieces.size() && q < q0 + kGroupMax; ++q) {
+                PrepItem &a = pg.it[pg.n++];
+                a = pieces[q];
+                a.start = (int32_t)pblocks;
+                pblocks += a.w_blocks + (a.x_units + 255) / 256;
+            }
             hipLaunchKernelGGL(prep_kernel, dim3((unsigned)pblocks), dim3(256), 0, stream, pg);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess)

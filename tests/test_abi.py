@@ -347,10 +347,19 @@ def test_sum_set_rules(tsl_lib):
             out.append(it)
         return out
 
-    # prefill: the set's products go to binary32 partials in the workspace
-    # first (M x N x 4 bytes each), then the binary16 weights
-    w = sum(tsl_lib.shard_linear_workspace_size(s, tsl_lib.Q4G64, M) for s in sh)
+    # prefill, members of whole 128-k records: the set is one product over
+    # the members' k-ranges end to end -- the workspace of the unsharded
+    # product (its binary16 weights, activation copy and k-partials), no
+    # rank partials
+    full = tsl_lib.plan_linear(K, N, 1, tsl_lib.ROW, 64)[0]
     assert tsl_lib.shard_linear_group_workspace_size(items(), tsl_lib.Q4G64, M) == \
+        tsl_lib.shard_linear_workspace_size(full, tsl_lib.Q4G64, M)
+    # prefill, 192-k members: the products go to binary32 partials in the
+    # workspace first (M x N x 4 bytes each), then the binary16 weights
+    sh192 = tsl_lib.plan_linear(768, N, tp, tsl_lib.ROW, 64)
+    w = sum(tsl_lib.shard_linear_workspace_size(s, tsl_lib.Q4G64, M) for s in sh192)
+    odd = [dict(it, shard=s) for it, s in zip(items(), sh192)]
+    assert tsl_lib.shard_linear_group_workspace_size(odd, tsl_lib.Q4G64, M) == \
         w + tp * M * N * 4
     # decode: the same partials (the products themselves need no workspace here)
     assert tsl_lib.shard_linear_group_workspace_size(items(), tsl_lib.Q4G64, 4) == tp * 4 * N * 4

@@ -162,14 +162,15 @@ def test_row_layers_as_sum_sets(layer, M, variant):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 2048, 4096), (3, 2048, 4096), (16, 2048, 4096),
-                                   (100, 2048, 4096), (100, 8192, 512)])
+                                   (100, 1280, 4096), (100, 768, 512)])
 def test_sum_set_equals_products_then_combine(M, K, N):
     """A sum set gives the ordered binary32 sum of its members' products:
     bit for bit what separate products + combine_partials(SUM) give when the
     products are computed the same way (here: one group of the same items
-    without sets -- at K = 8192, N = 512 a launch of 8 tiles, whose
-    products the GEMM splits into k-partials in both calls), and the bf16
-    output is that sum rounded once; the set also matches the oracle."""
+    without sets -- at M = 100 the members' 320- and 192-k ranges are not
+    joined into one product, and at K = 768, N = 512 the launch has 4 tiles,
+    whose products the GEMM splits into k-partials in both calls), and the
+    bf16 output is that sum rounded once; the set also matches the oracle."""
     t = torch()
     tp = 4
     w = Q4Weight(K, N, 3300, 3301, 3302)
@@ -194,6 +195,42 @@ def test_sum_set_equals_products_then_combine(M, K, N):
             assert normwise(host(Y), ref) <= TOL
         else:
             assert np.array_equal(host_bits(Y), oracle.f64_to_bf16(host(want)))
+
+
+@pytest.mark.parametrize("M,K,N,tp", [(100, 2048, 4096, 4), (100, 8192, 512, 4),
+                                      (300, 4608, 640, 4), (65, 1024, 264, 8)])
+def test_joined_sum_set_equals_unsharded_product(M, K, N, tp):
+    """4-bit weights above 64 rows: a sum set of row shards whose k-ranges
+    are whole 128-k records runs as one product over the members' k-ranges
+    end to end -- bit for bit the product of the unsharded weight over the
+    whole X (same plan, same k-splits: at K = 8192, N = 512 a launch of 8
+    tiles split into k-partials), f32 and bf16 outputs; and the oracle's
+    rank sum to the 4-bit tolerance."""
+    t = torch()
+    w = Q4Weight(K, N, 3400, 3401, 3402)
+    X = dev(synth.normal_bf16(3403 + M, (M, K)))
+    shards = tsl.plan_linear(K, N, tp, tsl.ROW, 64)
+    assert all(sh.k_len % 128 == 0 for sh in shards)
+    packs = [w.pack(sh) for sh in shards]
+    full = tsl.plan_linear(K, N, 1, tsl.ROW, 64)[0]
+    fbuf, fnb = w.pack(full)
+    Xf = oracle.bf16_to_f64(X.view(t.int16).cpu().numpy().view(np.uint16))
+    refs = []
+    for sh in shards:
+        s = spec_dict(sh)
+        refs.append(oracle.gemm(oracle.slice_input(Xf, s), w.shard_f64(s)))
+    ref = oracle.combine_sum(refs)
+    for ydt, tdt in ((tsl.F32, t.float32), (tsl.BF16, t.bfloat16)):
+        want = t.full((M, N), float("nan"), dtype=tdt, device="cuda")
+        run_group([dict(shard=full, packed=fbuf, packed_bytes=fnb, X=X, ldx=K, Y=want, ldy=N,
+                        ydtype=ydt)], tsl.Q4G64, M)
+        Y = t.full((M, N), float("nan"), dtype=tdt, device="cuda")
+        sets = [dict(shard=sh, packed=b, packed_bytes=nb, X=X[:, sh.k_off:], ldx=K,
+                     Y=Y if r == 0 else None, ldy=N, ydtype=ydt, sum_next=int(r < tp - 1))
+                for r, (sh, (b, nb)) in enumerate(zip(shards, packs))]
+        run_group(sets, tsl.Q4G64, M)
+        assert np.array_equal(host_bits(Y), host_bits(want)), (M, K, N, ydt)
+        assert normwise(host(Y), ref) <= TOL + (2.0 ** -9 if ydt == tsl.BF16 else 0.0)
 
 
 @pytest.mark.parametrize("wdtype", ["bf16", "q4"])
