@@ -53,3 +53,52 @@ def test_graph_replays_match_eager(M):
         step()  # eager work between replays
         t.cuda.synchronize()
         assert t.equal(out, eager)
+
+
+def test_graph_replays_of_a_large_grouped_prefill_call():
+    """A 4-bit grouped call of 512 GEMM tiles (prep pass, then one GEMM
+    launch over items of two k lengths): captured in a graph, every replay
+    matches the eager call bit for bit, with eager calls in between."""
+    t = torch()
+    M, N = 2048, 4096
+    ks = (3072, 2048, 2048, 2048)
+    items, outs, keep = [], [], []
+    for i, K in enumerate(ks):
+        w = Q4Weight(K, N, 1300 + i, 1301, 1302)
+        sh = tsl.plan_linear(K, N, 1, tsl.COLUMN, 64)[0]
+        buf, nb = w.pack(sh)
+        X = dev(synth.normal_bf16(1310 + i, (M, K)))
+        Y = t.empty((M, N), dtype=t.bfloat16, device="cuda")
+        keep += [buf, X]
+        outs.append(Y)
+        items.append(dict(shard=sh, packed=buf, packed_bytes=nb, X=X, ldx=K, Y=Y, ldy=N,
+                          ydtype=tsl.BF16))
+    ws = tsl.shard_linear_group_workspace_size(items, tsl.Q4G64, M)
+    wb = empty_bytes(ws)
+
+    def step():
+        tsl.shard_linear_group(items, tsl.Q4G64, tsl.BF16, M, wb, ws,
+                               stream=t.cuda.current_stream().cuda_stream)
+
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        step()
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+    eager = [Y.clone() for Y in outs]
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        step()
+    for i in range(3):
+        for Y in outs:
+            Y.fill_(float("nan"))
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        for Y, E in zip(outs, eager):
+            assert t.equal(Y, E), "replay %d" % i
+        step()
+        t.cuda.synchronize()
+        for Y, E in zip(outs, eager):
+            assert t.equal(Y, E)
