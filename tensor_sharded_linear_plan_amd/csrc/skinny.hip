@@ -324,6 +324,24 @@ __global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
             xr[s][i] = unit < S::UNITS ? xload(r, (int64_t)b * S::BK + cu * 8) : u32x4{0, 0, 0, 0};
         }
     };
+    // the same for a block that lies wholly inside K: every lane issues one
+    // 16-byte load (rows past M and units past the window read clamped,
+    // in-bounds addresses; those rows are then zero, those units unused),
+    // so every steady-state step issues the same loads
+    auto load_x_whole = [&](auto SLOT, int b) __attribute__((always_inline)) {
+        constexpr int s = decltype(SLOT)::value;
+#pragma unroll
+        for (int i = 0; i < XU; ++i) {
+            const int u0 = threadIdx.x + 256 * i;
+            const int unit = u0 < S::UNITS ? u0 : S::UNITS - 1;
+            const int r = unit / (S::BK / 8), cu = unit % (S::BK / 8);
+            const int64_t row = m0 + r;
+            const int64_t rr = row < M ? row : M - 1;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(
+                X + rr * a.ldx + (int64_t)b * S::BK + cu * 8);
+            xr[s][i] = row < M ? v : u32x4{0, 0, 0, 0};
+        }
+    };
     auto store_x = [&](auto SLOT, int buf) __attribute__((always_inline)) {
         constexpr int s = decltype(SLOT)::value;
 #pragma unroll
@@ -435,20 +453,32 @@ __global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
     using I2 = std::integral_constant<int, 2>;
     // one block in slot SLOT: prefetch block b + 2 into slot NEXT2, compute b,
     // (window mode) publish the activations of b + 1 from slot NEXT1
-    auto step = [&](auto SLOT, auto NEXT1, auto NEXT2, int b) __attribute__((always_inline)) {
+    // FULL: a steady-state step, b + 2 < b1 known -- every such step issues
+    // the same loads, so the wait counts the compiler derives at the loop
+    // head are exact (with a conditional prefetch it must assume the path
+    // that issued none and waits for nearly every load in flight)
+    auto step = [&](auto SLOT, auto NEXT1, auto NEXT2, int b, auto FULL)
+                    __attribute__((always_inline)) {
+        constexpr bool full = decltype(FULL)::value;
         const int buf = (b - b0) & 1;
-        if (b + 2 < b1) {
-            if constexpr (!XRES)
-                load_x(NEXT2, b + 2);
+        if (full || b + 2 < b1) {
+            if constexpr (!XRES) {
+                if constexpr (full)
+                    load_x_whole(NEXT2, b + 2);
+                else
+                    load_x(NEXT2, b + 2);
+            }
             load_w(NEXT2, b + 2);
         }
         compute(SLOT, buf, b);
         if constexpr (!XRES) {
-            if (b + 1 < b1)
+            if (full || b + 1 < b1)
                 store_x(NEXT1, buf ^ 1);
             lds_barrier();
         }
     };
+    using Full = std::true_type;
+    using Tail = std::false_type;
 
     if (b0 < b1) {
         if constexpr (XRES) {
@@ -511,15 +541,25 @@ __global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
         }
         lds_barrier();
         int b = b0;
+        // steady state: the three steps prefetch blocks up to b + 4, all
+        // inside the k-range and (window mode) wholly inside K.  Not for
+        // 64-row tiles, where the scheduler spreads the prefetches through
+        // the MFMA stream and the conditional form measured faster.
+        const int bsteady = MT > 2 ? b0 : XRES ? b1 : (b1 < a.Ks / S::BK ? b1 : a.Ks / S::BK);
+        for (; b + 5 <= bsteady; b += 3) {
+            step(I0{}, I1{}, I2{}, b, Full{});
+            step(I1{}, I2{}, I0{}, b + 1, Full{});
+            step(I2{}, I0{}, I1{}, b + 2, Full{});
+        }
         for (; b + 3 <= b1; b += 3) {
-            step(I0{}, I1{}, I2{}, b);
-            step(I1{}, I2{}, I0{}, b + 1);
-            step(I2{}, I0{}, I1{}, b + 2);
+            step(I0{}, I1{}, I2{}, b, Tail{});
+            step(I1{}, I2{}, I0{}, b + 1, Tail{});
+            step(I2{}, I0{}, I1{}, b + 2, Tail{});
         }
         if (b < b1)
-            step(I0{}, I1{}, I2{}, b);
+            step(I0{}, I1{}, I2{}, b, Tail{});
         if (b + 1 < b1)
-            step(I1{}, I2{}, I0{}, b + 1);
+            step(I1{}, I2{}, I0{}, b + 1, Tail{});
     }
 
     // acc[i][j] lane l: rows 16 i + 4 (l / 16) + r, column l % 16 of tile j
