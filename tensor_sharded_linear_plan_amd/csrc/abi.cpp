@@ -308,8 +308,16 @@ size_t split_sets(std::vector<LinearItem> *items, int64_t M, char *ws) {
     for (size_t i = 0; i < items->size();) {
         const size_t len = (*items)[i].set_len;
         if (len > 1) {
+            void *const sY = (*items)[i].Y;
+            const int64_t sldy = (*items)[i].ldy;
+            const tsl_dtype sy = (*items)[i].ydtype;
             for (size_t r = 0; r < len; ++r) {
                 LinearItem &L = (*items)[i + r];
+                L.fset_len = (int)len;
+                L.fset_pos = (int)r;
+                L.fset_Y = sY;
+                L.fset_ldy = sldy;
+                L.fset_ydtype = sy;
                 L.Y = ws ? ws + off : nullptr;
                 L.ldy = L.g.Ns;
                 L.ydtype = TSL_F32;
@@ -440,6 +448,8 @@ tsl_status run_group(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_
         const LinearItem &L = ordered[i];
         if (L.set_len == 1)
             continue;
+        if (skinny && sp.fset[i] >= 0)
+            continue; // added up by the streaming launch itself
         if (L.set_len > kSetParts) {
             const float *p[kMaxParts];
             for (int r = 0; r < L.set_len; ++r)

@@ -112,6 +112,12 @@ struct LinearItem {
     // the GEMM path may not split this product's k (a member of a sum set
     // too long for one sum launch)
     bool no_split = false;
+    // member fset_pos of a sum set of fset_len products that split_sets
+    // turned into lone items (0: none), and the set's own output
+    int fset_len = 0, fset_pos = 0;
+    void *fset_Y = nullptr;
+    int64_t fset_ldy = 0;
+    tsl_dtype fset_ydtype = TSL_F32;
     // a sum set computed as ONE product over its members' k-ranges laid end
     // to end in set order (4-bit weights, GEMM regime): cat members of equal
     // k_len; g, Y, ldy, ydtype describe the joined product, seg_* each
@@ -142,6 +148,15 @@ struct SkinnyPlan {
     std::vector<int64_t> n_groups;
     std::vector<int> ks;
     std::vector<size_t> ws_off;
+    // sum sets the streaming launch adds up itself (members unsplit, all in
+    // one launch): per item its set (index into fsets) or -1; per set its
+    // first item and the workspace offset of its per-tile counters
+    std::vector<int> fset;
+    struct FSet {
+        int first = 0, len = 0;
+        size_t ctr_off = 0;
+    };
+    std::vector<FSet> fsets;
     size_t ws_bytes = 0;
 };
 SkinnyPlan skinny_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t M);

@@ -25,6 +25,9 @@
 // per group the accumulator takes s * sum(x (128 + q)) + (b - 128 s) * sum(x),
 // sum(x) coming from one extra MFMA against a ones operand.  This is the
 // group-sum identity of the affine format, evaluated in binary32.
+#include <atomic>
+#include <chrono>
+#include <random>
 #include <type_traits>
 
 #include "device.hpp"
@@ -46,8 +49,24 @@ struct SkinnyItem {
     int32_t ks, n_groups;
     int32_t start;       // first workgroup of this item
     int32_t accumulate, y_bf16;
+    int32_t fset, fpos;  // member fpos of rank-sum set fset of the launch (-1: none)
     int64_t M;           // rows of this item
 };
+
+// A sum set whose rank sum the streaming launch finishes itself: member r
+// (an item of the launch, ks 1) writes its binary32 product to
+// P0 + r * pstride ([M][Ns], row stride Ns), and whichever wave completes
+// a 16-column tile last (a counter per tile, tagged with the call's
+// ticket) adds the members' tiles in rank order into Y.
+struct FusedSet {
+    float *P0;
+    int64_t pstride;      // elements between members' products
+    unsigned long long *ctr; // per 16-column tile: ticket << 16 | arrivals
+    void *Y;
+    int64_t ldy;
+    int32_t R, y_bf16;
+};
+constexpr int kMaxFused = 16;
 
 struct SkinnyGroup {
     int64_t M;
@@ -55,7 +74,9 @@ struct SkinnyGroup {
     int32_t xstr;     // streaming kernel, resident activations: LDS bytes per row
     int32_t xsum_off; // ... and LDS byte offset of the 4-bit group sums
     int32_t pad_;
+    unsigned long long ticket; // 48 bits, distinct per enqueued call
     SkinnyItem it[kGroupMax];
+    FusedSet fs[kMaxFused];
 };
 
 // Activation fragment, f32: 4 consecutive k of one row (zero outside).
@@ -578,6 +599,9 @@ __global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
                 const float v = acc[i][j][r];
                 if (a.ks > 1) {
                     a.P[((int64_t)ksi * M + row) * a.Ns + col] = v;
+                } else if (a.fset >= 0) { // a set member's product: written through
+                    __hip_atomic_store(static_cast<float *>(a.Y) + row * a.ldy + col, v,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 } else if (a.y_bf16) {
                     __bf16 h = (__bf16)v;
                     static_cast<uint16_t *>(a.Y)[row * a.ldy + col] =
@@ -588,9 +612,87 @@ __global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
                 }
             }
     }
+    if (a.fset < 0)
+        return;
+
+    // Rank-sum set member: this wave's partial tiles are stored (a.Y is the
+    // member's binary32 product, written with agent-scope stores, which go
+    // through to the point of coherence of all XCDs); once they have
+    // completed, count the arrival, and the last member to arrive at a tile
+    // adds the R products in rank order, read with agent-scope loads.  (An
+    // agent-scope fence would write back and invalidate the whole L2 of the
+    // XCD at every member wave.)  The counter word is ticket << 16 |
+    // arrivals; a word tagged with another ticket (an earlier call, or
+    // never written) counts as zero, and the last arrival leaves ticket <<
+    // 16 | 0, so a replay of the same enqueued call starts from zero too.
+    const FusedSet &fs = grp.fs[a.fset];
+    const unsigned long long tag = grp.ticket << 16;
+    const int64_t mb = m0 / (16 * MT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): the product stores have completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+        if (ntile[j] >= a.Nt)
+            continue; // a clamped duplicate tile of the last column group
+        unsigned long long *ctr = fs.ctr + mb * a.Nt + ntile[j];
+        int last = 0;
+        if (lane == 0) {
+            unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+            for (int tries = 0; tries < 4096; ++tries) {
+                const unsigned long long base = (old & ~0xFFFFull) == tag ? old : tag;
+                if (__hip_atomic_compare_exchange_strong(ctr, &old, base + 1, __ATOMIC_RELAXED,
+                                                         __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT)) {
+                    last = (int)((base + 1) & 0xFFFF) == fs.R;
+                    break;
+                }
+            }
+        }
+        last = __builtin_amdgcn_readfirstlane(__shfl(last, 0));
+        if (!last)
+            continue;
+        const int64_t col = ntile[j] * 16 + (lane & 15);
+        if (col < a.Ns) {
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t row = m0 + 16 * i + 4 * kg + r;
+                    if (row >= M)
+                        continue;
+                    float *p = fs.P0 + row * a.Ns + col;
+                    float v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int q = 1; q < fs.R; ++q)
+                        v = v + __hip_atomic_load(p + q * fs.pstride, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+                    if (fs.y_bf16) {
+                        __bf16 h = (__bf16)v;
+                        static_cast<uint16_t *>(fs.Y)[row * fs.ldy + col] =
+                            __builtin_bit_cast(uint16_t, h);
+                    } else {
+                        static_cast<float *>(fs.Y)[row * fs.ldy + col] = v;
+                    }
+                }
+        }
+        if (lane == 0)
+            __hip_atomic_store(ctr, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 typedef void (*SkinnyFn)(SkinnyGroup);
+
+// 48-bit tickets, distinct for every enqueued streaming launch of the
+// process (a random start, then consecutive)
+unsigned long long next_ticket() {
+    static std::atomic<unsigned long long> next{[] {
+        std::random_device rd;
+        return ((unsigned long long)rd() << 32) ^ (unsigned long long)rd() ^
+               (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+    }()};
+    return next.fetch_add(1) & ((1ull << 48) - 1);
+}
 
 // fp32 weights: the k-split kernel (4 waves split k, LDS reduction)
 SkinnyFn pick_f32(int mt) {
@@ -699,6 +801,39 @@ SkinnyPlan skinny_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t
             off += ((size_t)p.ks[i] * (size_t)items[i].M * (size_t)items[i].g.Ns * sizeof(float) +
                     255) / 256 * 256;
     }
+    // sum sets the streaming launch finishes: resident launches (a few token
+    // rows; with more rows the written-through products and their reads
+    // cost more than the separate sum launch, measured), every member
+    // unsplit and in the same launch, at most kMaxFused per launch; a
+    // counter per (row block, 16-column tile)
+    p.fset.assign(n, -1);
+    int in_chunk = 0, chunk = -1;
+    for (int i = 0; p.stream && p.resident && i < n;) {
+        const int len = items[i].fset_len;
+        if (len < 2 || items[i].fset_pos != 0) {
+            ++i;
+            continue;
+        }
+        bool ok = i + len <= n && len <= kSetParts && i / kGroupMax == (i + len - 1) / kGroupMax;
+        for (int r = 0; ok && r < len; ++r)
+            ok = p.ks[i + r] == 1 && items[i + r].fset_pos == r;
+        if (i / kGroupMax != chunk) {
+            chunk = i / kGroupMax;
+            in_chunk = 0;
+        }
+        if (ok && in_chunk < kMaxFused) {
+            SkinnyPlan::FSet f;
+            f.first = i;
+            f.len = len;
+            f.ctr_off = off;
+            off += ((size_t)p.m_blocks[i] * (size_t)items[i].g.Nt * 8 + 255) / 256 * 256;
+            for (int r = 0; r < len; ++r)
+                p.fset[i + r] = (int)p.fsets.size();
+            p.fsets.push_back(f);
+            ++in_chunk;
+        }
+        i += len;
+    }
     p.ws_bytes = off;
     return p;
 }
@@ -729,6 +864,33 @@ hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, ts
         grp.n = cn;
         grp.xstr = p.xstr;
         grp.xsum_off = p.xsum_off;
+        grp.ticket = next_ticket();
+        // this launch's finished sum sets, in plan order
+        int nfs = 0, fs0 = -1;
+        for (size_t f = 0; f < p.fsets.size(); ++f) {
+            const SkinnyPlan::FSet &F = p.fsets[f];
+            if (F.first < c0 || F.first >= c0 + cn)
+                continue;
+            if (fs0 < 0)
+                fs0 = (int)f;
+            const LinearItem &L0 = items[F.first];
+            FusedSet &d = grp.fs[nfs++];
+            d.P0 = static_cast<float *>(L0.Y);
+            d.pstride = F.len > 1 ? (static_cast<const float *>(items[F.first + 1].Y) -
+                                     static_cast<const float *>(L0.Y))
+                                  : 0;
+            d.ctr = reinterpret_cast<unsigned long long *>(static_cast<char *>(workspace) +
+                                                           F.ctr_off);
+            d.Y = L0.fset_Y;
+            d.ldy = L0.fset_ldy;
+            d.R = F.len;
+            d.y_bf16 = L0.fset_ydtype == TSL_BF16;
+            // the members' products lie at equal strides (split_sets)
+            for (int r = 1; r < F.len; ++r)
+                if (static_cast<const float *>(items[F.first + r].Y) !=
+                    d.P0 + r * d.pstride)
+                    return hipErrorInvalidValue;
+        }
         int64_t blocks = 0;
         for (int i = 0; i < cn; ++i) {
             const LinearItem &L = items[c0 + i];
@@ -748,6 +910,8 @@ hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, ts
             a.accumulate = L.accumulate;
             a.y_bf16 = L.ydtype == TSL_BF16;
             a.M = L.M;
+            a.fset = p.fset[c0 + i] < 0 ? -1 : p.fset[c0 + i] - fs0;
+            a.fpos = L.fset_pos;
             a.start = (int32_t)blocks;
             blocks += (int64_t)a.n_groups * a.ks * p.m_blocks[c0 + i];
         }

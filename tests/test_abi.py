@@ -361,12 +361,16 @@ def test_sum_set_rules(tsl_lib):
     odd = [dict(it, shard=s) for it, s in zip(items(), sh192)]
     assert tsl_lib.shard_linear_group_workspace_size(odd, tsl_lib.Q4G64, M) == \
         w + tp * M * N * 4
-    # decode: the same partials (the products themselves need no workspace here)
-    assert tsl_lib.shard_linear_group_workspace_size(items(), tsl_lib.Q4G64, 4) == tp * 4 * N * 4
+    # decode: the same partials (the products themselves need no workspace
+    # here) and, as the streaming launch adds the set up itself, a counter
+    # of 8 bytes per 16-column tile (rounded up to 256 bytes)
+    ctr = (N // 16 * 8 + 255) // 256 * 256
+    assert tsl_lib.shard_linear_group_workspace_size(items(), tsl_lib.Q4G64, 4) == \
+        tp * 4 * N * 4 + ctr
     # a set of 3-row items inside a 4-row call: partials of 3 rows
     rows3 = items({r: dict(rows=3) for r in range(tp)})
     assert tsl_lib.shard_linear_group_workspace_size(rows3, tsl_lib.Q4G64, 4) == \
-        tp * ((3 * N * 4 + 255) // 256 * 256)
+        tp * ((3 * N * 4 + 255) // 256 * 256) + ctr
     call = lambda its, M=M: tsl_lib.shard_linear_group(its, tsl_lib.Q4G64, tsl_lib.BF16, M)
     bad = [items({3: dict(sum_next=1)}),                 # the last item links on
            items({1: dict(sum_next=2)}),

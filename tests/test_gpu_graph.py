@@ -102,3 +102,70 @@ def test_graph_replays_of_a_large_grouped_prefill_call():
         t.cuda.synchronize()
         for Y, E in zip(outs, eager):
             assert t.equal(Y, E)
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_graph_replays_of_decode_sum_sets(M):
+    """Decode-sized grouped call whose two sum sets (4 row shards each) are
+    added up inside the streaming launch (per-tile arrival counters tagged
+    with the call's ticket): every replay of the captured call, eager calls
+    of the same items in between, matches the eager result bit for bit, and
+    that result is the row shards' products followed by combine_partials."""
+    t = torch()
+    K, N, tp = 2048, 1024, 4
+    outs, items, plain, parts, keep = [], [], [], [], []
+    for s in range(2):
+        w = Q4Weight(K, N, 1400 + s, 1401, 1402)
+        X = dev(synth.normal_bf16(1410 + 10 * s + M, (M, K)))
+        Y = t.empty((M, N), dtype=t.bfloat16 if s else t.float32, device="cuda")
+        outs.append(Y)
+        shards = tsl.plan_linear(K, N, tp, tsl.ROW, 64)
+        for r, sh in enumerate(shards):
+            buf, nb = w.pack(sh)
+            P = t.empty((M, N), dtype=t.float32, device="cuda")
+            keep += [buf, X]
+            parts.append(P)
+            items.append(dict(shard=sh, packed=buf, packed_bytes=nb, X=X[:, sh.k_off:], ldx=K,
+                              Y=Y if r == 0 else None, ldy=N,
+                              ydtype=tsl.BF16 if s else tsl.F32, sum_next=int(r < tp - 1)))
+            plain.append(dict(shard=sh, packed=buf, packed_bytes=nb, X=X[:, sh.k_off:], ldx=K,
+                              Y=P, ldy=N))
+    ws = tsl.shard_linear_group_workspace_size(items, tsl.Q4G64, M)
+    wb = empty_bytes(ws)
+
+    def step():
+        tsl.shard_linear_group(items, tsl.Q4G64, tsl.BF16, M, wb, ws,
+                               stream=t.cuda.current_stream().cuda_stream)
+
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        step()
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+    eager = [Y.clone() for Y in outs]
+    # the same products, then the ordered sums
+    pws = tsl.shard_linear_group_workspace_size(plain, tsl.Q4G64, M)
+    pwb = empty_bytes(pws) if pws else None
+    tsl.shard_linear_group(plain, tsl.Q4G64, tsl.BF16, M, pwb, pws)
+    for s, Y in enumerate(outs):
+        want = t.empty_like(Y)
+        tsl.combine_partials(tsl.COMBINE_SUM, parts[4 * s:4 * s + 4], tsl.F32, M, N, N,
+                             tsl.BF16 if s else tsl.F32, want, N)
+        t.cuda.synchronize()
+        assert t.equal(eager[s], want), s
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        step()
+    for i in range(3):
+        for Y in outs:
+            Y.fill_(float("nan"))
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        for Y, E in zip(outs, eager):
+            assert t.equal(Y, E), "replay %d" % i
+        step()
+        t.cuda.synchronize()
+        for Y, E in zip(outs, eager):
+            assert t.equal(Y, E)
