@@ -335,6 +335,17 @@ tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, const void *pa
  * and rounded once (bit for bit the product of the unsharded weight over
  * the whole X when the members are the row shards of one weight), with no
  * partials and no sum launch.
+ * Decode-sized M whose activation rows the streaming launch holds in LDS
+ * (one to four token rows, as far as they fit): the launch adds each set of
+ * at most 8 unsplit members itself -- the members' binary32 products are
+ * written through to device-coherent memory, a counter per 16-column tile
+ * (8 bytes each in the workspace) counts their arrival, and the last to
+ * arrive adds them in item order, the same sum bit for bit.  A counter
+ * word holds a 48-bit ticket drawn afresh for every call (a graph replay
+ * repeats its call's ticket and finds the counters reset to zero); a word
+ * that any other use of the workspace left behind counts as zero unless
+ * it happens to hold this call's ticket (odds 2^-48 per tile).  Calls that
+ * overlap in time must not share a workspace.
  *
  * rows: the item's token rows, 1 <= rows <= M (0 means M): it reads rows
  * [0, rows) of X and writes rows [0, rows) of Y.  Items of different row
