@@ -283,3 +283,84 @@ def test_items_with_their_own_rows(wdtype, M, rows):
                 assert t.equal(single[:rw], Y[:rw]), rw
             else:
                 assert normwise(host(single)[:rw], got[:rw]) <= 1e-5, rw
+
+
+@pytest.mark.parametrize("M,K,N,tp", [(1, 1024, 1000, 8), (2, 512, 264, 2), (3, 4096, 4112, 4),
+                                      (4, 2048, 64, 8)])
+def test_decode_sum_sets_in_launch(M, K, N, tp):
+    """Decode rows whose activations stay resident in LDS: the streaming
+    launch adds each sum set itself (2, 4 or 8 members, ragged last
+    column tiles, a bf16 and an f32 set in one call) -- bit for bit the
+    members' products followed by combine_partials(SUM), and the oracle's
+    rank sum to the 4-bit tolerance."""
+    t = torch()
+    items, plain, parts, checks, keep = [], [], [], [], []
+    for s_i, ydt in enumerate((tsl.F32, tsl.BF16)):
+        w = Q4Weight(K, N, 3500 + 10 * s_i, 3501, 3502)
+        X = dev(synth.normal_bf16(3503 + 10 * s_i + M, (M, K)))
+        Y = t.full((M, N), float("nan"), dtype=t.bfloat16 if ydt == tsl.BF16 else t.float32,
+                   device="cuda")
+        shards = tsl.plan_linear(K, N, tp, tsl.ROW, 64)
+        Xf = oracle.bf16_to_f64(X.view(t.int16).cpu().numpy().view(np.uint16))
+        refs, ps = [], []
+        for r, sh in enumerate(shards):
+            buf, nb = w.pack(sh)
+            keep += [buf, X]
+            P = t.full((M, N), float("nan"), dtype=t.float32, device="cuda")
+            ps.append(P)
+            items.append(dict(shard=sh, packed=buf, packed_bytes=nb, X=X[:, sh.k_off:], ldx=K,
+                              Y=Y if r == 0 else None, ldy=N, ydtype=ydt,
+                              sum_next=int(r < tp - 1)))
+            plain.append(dict(shard=sh, packed=buf, packed_bytes=nb, X=X[:, sh.k_off:], ldx=K,
+                              Y=P, ldy=N))
+            s = spec_dict(sh)
+            refs.append(oracle.gemm(oracle.slice_input(Xf, s), w.shard_f64(s)))
+        parts.append(ps)
+        checks.append((Y, ydt, oracle.combine_sum(refs)))
+    run_group(items, tsl.Q4G64, M)
+    run_group(plain, tsl.Q4G64, M)
+    for (Y, ydt, ref), ps in zip(checks, parts):
+        want = t.empty_like(Y)
+        tsl.combine_partials(tsl.COMBINE_SUM, ps, tsl.F32, M, N, N, ydt, want, N)
+        t.cuda.synchronize()
+        assert np.array_equal(host_bits(Y), host_bits(want)), (M, K, N, tp, ydt)
+        assert normwise(host(Y), ref) <= TOL + (2.0 ** -9 if ydt == tsl.BF16 else 0.0)
+
+
+def test_decode_sum_set_across_launches():
+    """A decode group of 130 items whose last sum set straddles the
+    128-item launch boundary (added by the sum launch) while the set
+    before it lies inside the first launch (added in the launch): both
+    give the ordered sum of the members' products bit for bit."""
+    t = torch()
+    M, K, N, tp = 1, 512, 256, 4
+    w = Q4Weight(K, N, 3600, 3601, 3602)
+    X = dev(synth.normal_bf16(3603, (M, K)))
+    shards = tsl.plan_linear(K, N, tp, tsl.ROW, 64)
+    packs = [w.pack(sh) for sh in shards]
+    col = tsl.plan_linear(K, N, 2, tsl.COLUMN, 64)[0]
+    cbuf, cnb = w.pack(col)
+    items, keep = [], []
+    # 122 lone column products, then a set at items 122..125 and one at
+    # 126..129 (the second launch starts at item 128)
+    for i in range(122):
+        Yc = t.empty((M, col.n_len), dtype=t.float32, device="cuda")
+        keep.append(Yc)
+        items.append(dict(shard=col, packed=cbuf, packed_bytes=cnb, X=X, ldx=K, Y=Yc,
+                          ldy=col.n_len))
+    outs = []
+    for s_i in range(2):
+        Y = t.full((M, N), float("nan"), dtype=t.float32, device="cuda")
+        outs.append(Y)
+        for r, (sh, (buf, nb)) in enumerate(zip(shards, packs)):
+            items.append(dict(shard=sh, packed=buf, packed_bytes=nb, X=X[:, sh.k_off:], ldx=K,
+                              Y=Y if r == 0 else None, ldy=N, sum_next=int(r < tp - 1)))
+    run_group(items, tsl.Q4G64, M)
+    ps = [t.empty((M, N), dtype=t.float32, device="cuda") for _ in shards]
+    run_group([dict(shard=sh, packed=b, packed_bytes=nb, X=X[:, sh.k_off:], ldx=K, Y=P, ldy=N)
+               for sh, (b, nb), P in zip(shards, packs, ps)], tsl.Q4G64, M)
+    want = t.empty((M, N), dtype=t.float32, device="cuda")
+    tsl.combine_partials(tsl.COMBINE_SUM, ps, tsl.F32, M, N, N, tsl.F32, want, N)
+    t.cuda.synchronize()
+    for Y in outs:
+        assert t.equal(Y, want)
