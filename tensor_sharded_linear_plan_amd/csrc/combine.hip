@@ -21,6 +21,15 @@ __device__ __forceinline__ void store4(uint16_t *y, f32x4 v) {
     u32x2 w = {pack_bf16(v.x, v.y), pack_bf16(v.z, v.w)};
     *reinterpret_cast<u32x2 *>(y) = w;
 }
+// Streaming (non-temporal) stores of 4 consecutive outputs: for outputs
+// that the launch does not read back.  y aligned to 4 elements.
+__device__ __forceinline__ void store4_nt(float *y, f32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(y));
+}
+__device__ __forceinline__ void store4_nt(uint16_t *y, f32x4 v) {
+    u32x2 w = {pack_bf16(v.x, v.y), pack_bf16(v.z, v.w)};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(y));
+}
 __device__ __forceinline__ void store1(float *y, float v) { *y = v; }
 __device__ __forceinline__ void store1(uint16_t *y, float v) {
     __bf16 b = (__bf16)v;
@@ -194,8 +203,10 @@ __device__ __forceinline__ int64_t block_lo(int r, int64_t M, int n) {
 }
 
 // Ordered binary32 sum of the parts at (m, j..j+V-1), written to every
-// output (all-reduce) or to the owner of row m (reduce-scatter).
-template <typename TY, int V>
+// output (all-reduce) or to the owner of row m (reduce-scatter).  VST: V is
+// 4 and every output row start is aligned to 4 elements, so each output
+// takes one streaming vector store.
+template <typename TY, int V, bool VST = false>
 __global__ void __launch_bounds__(256) reduce_ranks_kernel(PartPtrs parts, int n, int64_t M,
                                                            int64_t n_each, int64_t ld_part,
                                                            OutPtrs outs, int64_t ldo,
@@ -226,9 +237,13 @@ __global__ void __launch_bounds__(256) reduce_ranks_kernel(PartPtrs parts, int n
         for (int r = r0; r < r1; ++r) {
             const int64_t row = scatter ? m - block_lo(r, M, n) : m;
             TY *y = static_cast<TY *>(outs.p[r]) + row * ldo + j;
+            if constexpr (VST) {
+                store4_nt(y, f32x4{acc[0], acc[1], acc[2], acc[3]});
+            } else {
 #pragma unroll
-            for (int e = 0; e < V; ++e)
-                store1(y + e, acc[e]);
+                for (int e = 0; e < V; ++e)
+                    store1(y + e, acc[e]);
+            }
         }
     }
 }
@@ -250,8 +265,9 @@ __global__ void __launch_bounds__(256) gather_ranks_kernel(PartPtrs parts, int n
         const unit_t v = *reinterpret_cast<const unit_t *>(static_cast<const char *>(parts.p[q]) +
                                                            m * ld_part_bytes + u * VEC);
         const int64_t off = m * ldo_bytes + (int64_t)q * part_bytes + u * VEC;
+        // streaming stores: the n copies are not read back by this launch
         for (int r = 0; r < n; ++r)
-            *reinterpret_cast<unit_t *>(static_cast<char *>(outs.p[r]) + off) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<unit_t *>(static_cast<char *>(outs.p[r]) + off));
     }
 }
 
@@ -372,17 +388,28 @@ hipError_t launch_reduce_to_ranks(int n, const float *const *parts, int64_t M, i
         op.p[r] = outs[r];
     }
     const bool vec = n_each % 4 == 0 && ld_part % 4 == 0 && ldo % 4 == 0;
+    // vector stores: every output base aligned to 4 elements (rows then are too)
+    bool vst = vec;
+    const uintptr_t oalign = odtype == TSL_F32 ? 16 : 8;
+    for (int r = 0; r < n; ++r)
+        vst = vst && (reinterpret_cast<uintptr_t>(outs[r]) % oalign) == 0;
     const int V = vec ? 4 : 1;
     dim3 grid((unsigned)((n_each / V + 255) / 256), rows_grid(M));
     if (odtype == TSL_F32) {
-        if (vec)
+        if (vst)
+            hipLaunchKernelGGL((reduce_ranks_kernel<float, 4, true>), grid, dim3(256), 0, stream,
+                               pp, n, M, n_each, ld_part, op, ldo, scatter);
+        else if (vec)
             hipLaunchKernelGGL((reduce_ranks_kernel<float, 4>), grid, dim3(256), 0, stream, pp, n,
                                M, n_each, ld_part, op, ldo, scatter);
         else
             hipLaunchKernelGGL((reduce_ranks_kernel<float, 1>), grid, dim3(256), 0, stream, pp, n,
                                M, n_each, ld_part, op, ldo, scatter);
     } else {
-        if (vec)
+        if (vst)
+            hipLaunchKernelGGL((reduce_ranks_kernel<uint16_t, 4, true>), grid, dim3(256), 0,
+                               stream, pp, n, M, n_each, ld_part, op, ldo, scatter);
+        else if (vec)
             hipLaunchKernelGGL((reduce_ranks_kernel<uint16_t, 4>), grid, dim3(256), 0, stream, pp,
                                n, M, n_each, ld_part, op, ldo, scatter);
         else
