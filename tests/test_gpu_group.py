@@ -364,3 +364,42 @@ def test_decode_sum_set_across_launches():
     t.cuda.synchronize()
     for Y in outs:
         assert t.equal(Y, want)
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "q4"])
+@pytest.mark.parametrize("M", [1, 100])
+def test_sum_set_of_16_ranks(wdtype, M):
+    """A sum set of 16 row shards -- longer than one sum launch takes, so
+    its members are never split along k and a combine launch of its own
+    adds them: bit for bit the members' products followed by
+    combine_partials(SUM) (the same products: one group without the set),
+    and the oracle's rank sum to the tolerance of the weight type."""
+    t = torch()
+    K, N, tp = 4096, 512, 16
+    X = synth.normal_bf16(3700 + M, (M, K))
+    dX = dev(X)
+    Xf = oracle.bf16_to_f64(X)
+    shards = tsl.plan_linear(K, N, tp, tsl.ROW, 64)
+    if wdtype == "q4":
+        w = Q4Weight(K, N, 3701, 3702, 3703)
+        packs = [w.pack(sh) for sh in shards]
+        Wf = oracle.dequant_q4(w.codes, w.scales, w.biases)
+        code, tol = tsl.Q4G64, TOL
+    else:
+        from gpu_util import pack
+        Wb = synth.normal_bf16(3704, (K, N), 0.02)
+        dW = dev(Wb)
+        packs = [pack(sh, tsl.BF16, dW, N, 1) for sh in shards]
+        Wf = oracle.bf16_to_f64(Wb)
+        code, tol = tsl.BF16, TOL
+    ps = [t.full((M, N), float("nan"), dtype=t.float32, device="cuda") for _ in shards]
+    run_group([dict(shard=sh, packed=b, packed_bytes=nb, X=dX[:, sh.k_off:], ldx=K, Y=P, ldy=N)
+               for sh, (b, nb), P in zip(shards, packs, ps)], code, M)
+    want = t.empty((M, N), dtype=t.float32, device="cuda")
+    tsl.combine_partials(tsl.COMBINE_SUM, ps, tsl.F32, M, N, N, tsl.F32, want, N)
+    Y = t.full((M, N), float("nan"), dtype=t.float32, device="cuda")
+    run_group([dict(shard=sh, packed=b, packed_bytes=nb, X=dX[:, sh.k_off:], ldx=K,
+                    Y=Y if r == 0 else None, ldy=N, sum_next=int(r < tp - 1))
+               for r, (sh, (b, nb)) in enumerate(zip(shards, packs))], code, M)
+    assert t.equal(Y, want)
+    assert normwise(host(Y), oracle.gemm(Xf, Wf)) <= tol
