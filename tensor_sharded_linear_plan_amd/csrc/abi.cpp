@@ -414,12 +414,18 @@ tsl_status run_group(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_
     if (e != hipSuccess)
         return from_hip(e);
     // k-split GEMM products: each product's k-partials, in k order
-    auto kparts = [&](size_t i) {
-        return !skinny && pp.ks[i] > 1
-                   ? reinterpret_cast<const float *>(ws + parts + pp.p_off[i])
-                   : static_cast<const float *>(items[i].Y);
+    // k-split products (decode regime: those that neither accumulate into
+    // Y nor belong to a sum set too long for one sum launch; launch_skinny
+    // finished the others)
+    auto kcount = [&](size_t i) {
+        return !skinny ? pp.ks[i]
+                       : (items[i].accumulate || items[i].no_split ? 1 : sp.ks[i]);
     };
-    auto kcount = [&](size_t i) { return !skinny ? pp.ks[i] : 1; };
+    auto kparts = [&](size_t i) {
+        return kcount(i) > 1 ? reinterpret_cast<const float *>(
+                                   ws + parts + (skinny ? sp.ws_off[i] : pp.p_off[i]))
+                             : static_cast<const float *>(items[i].Y);
+    };
     std::vector<SumSpec> sums;
     for (size_t i = 0; i < ordered.size();) {
         const size_t len = ordered[i].set_len;

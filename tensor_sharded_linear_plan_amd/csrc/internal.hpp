@@ -162,6 +162,11 @@ struct SkinnyPlan {
 SkinnyPlan skinny_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t M);
 // most workgroups any one launch of the group takes (bounded by the host)
 int64_t skinny_blocks(const SkinnyPlan &p, const LinearItem *items, int n);
+// Enqueues the group.  A product split along k (ks > 1) leaves its binary32
+// k-partials [ks][M][Ns] at workspace + ws_off[i] for the caller's sum
+// launch to add in k order, unless it accumulates into Y or is a member of
+// a sum set longer than kSetParts (no_split): those are finished by a
+// launch of their own.
 hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, tsl_dtype wdtype,
                          int64_t M, void *workspace, hipStream_t stream);
 

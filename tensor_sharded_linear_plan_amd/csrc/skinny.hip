@@ -776,7 +776,7 @@ SkinnyPlan skinny_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t
         }
     } else {
         // fp32: a workgroup owns one 16-column tile and one k-range split
-        // over its 4 waves; k split further for ~200 workgroups (and as far
+        // over its 4 waves; k split further for ~1024 workgroups (and as far
         // as the register budget of a wave requires)
         p.ntw = 1;
         p.cmax = 16;
@@ -785,7 +785,7 @@ SkinnyPlan skinny_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t
             p.n_groups[i] = items[i].g.Nt;
             base += p.n_groups[i] * p.m_blocks[i];
         }
-        const int64_t ks_want = base > 0 ? (200 + base - 1) / base : 1;
+        const int64_t ks_want = base > 0 ? (1024 + base - 1) / base : 1;
         for (int i = 0; i < n; ++i) {
             const int64_t KC = items[i].g.KT;
             const int64_t ks_min = (KC + 4 * p.cmax - 1) / (4 * p.cmax);
@@ -926,9 +926,12 @@ hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, ts
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
+        // k-partials of products that accumulate into Y or belong to a sum
+        // set too long for one sum launch; the others' are added by the
+        // caller's one sum launch
         for (int i = 0; i < cn; ++i) {
             const SkinnyItem &a = grp.it[i];
-            if (a.ks == 1)
+            if (a.ks == 1 || !(a.accumulate || items[c0 + i].no_split))
                 continue;
             e = launch_splitk_reduce(a.P, a.ks, a.M, a.Ns, items[c0 + i].ydtype, a.Y, a.ldy,
                                      a.accumulate, stream);
