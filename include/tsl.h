@@ -223,14 +223,18 @@ tsl_status plan_experts(int32_t n_experts, int64_t hidden, int64_t expert_ffn, i
  *             sits in tile (n/16, k/16), lane ((k%16)/4)*16 + n%16, slot k%4.
  *   TSL_BF16  [Nt][ceil(Ks/64)*2][64][8] bf16: tile (n/16, k/32),
  *             lane ((k%32)/8)*16 + n%16, slot k%8.
- *   TSL_Q4G64 records [Nt][ceil(Ks/128)] of 1152 bytes (total rounded up
- *             to 256): codes [64][4] u32, then scale/bias pairs [16][2] u32
- *             (bf16 scale in the low half, bf16 bias in the high half).
+ *   TSL_Q4G64 records [Nt][ceil(Ks/128)] of 1152 bytes (rounded up to
+ *             256 bytes): codes [64][4] u32, then scale/bias pairs [16][2]
+ *             u32 (bf16 scale in the low half, bf16 bias in the high half).
  *             Code (k, n): record (n/16, k/128); with kk = k%128, word
  *             kk/32 of lane ((kk%32)/8)*16 + n%16; with j = kk%8 the nibble
  *             at bit 4*(j/2) for even j and 16 + 4*(j/2) for odd j.
  *             Pair (g, n) for group g = k/64: record (n/16, g/2), entry
  *             [n%16][g%2] (the two groups of a 128-k block side by side).
+ *             Then the column exponents [Nt*16] int32 (rounded up to 256
+ *             bytes): f_n = ilogb(max over the column's groups of
+ *             15|s| + |b|, in binary32) - 14, and 0 for a column whose
+ *             groups are all zero or not finite (and for padding columns).
  * Errors: TSL_ERR_INVALID_ARG, TSL_ERR_GROUP_ALIGN (Q4 with k_len % 64).
  */
 tsl_status pack_shard_size(const tsl_shard *shard, tsl_dtype wdtype, size_t *bytes);
@@ -262,8 +266,9 @@ tsl_status pack_shard(const tsl_shard *shard, tsl_dtype wdtype, const void *W, i
  * shard_linear_workspace_size -- workspace bytes shard_linear needs for
  * this shard, weight type and row count (0 when none is needed): split-K
  * partial sums for decode-sized M; with M > 64, for 4-bit weights the shard
- * expanded to binary16 (2 bytes per weight) and a binary16 copy of the
- * activations (M x k_len x 2 bytes), for BF16 weights a zero-padded copy of
+ * expanded to binary16 (2 bytes per weight), a binary16 copy of the
+ * activations (M x k_len x 2 bytes) and their row exponents (M x 4 bytes),
+ * for BF16 weights a zero-padded copy of
  * the activations when k_len is not a multiple of 64, and when the product
  * is too small to fill the chip the binary32 partials of its k-splits
  * (splits x M x n_len x 4 bytes).
@@ -291,10 +296,19 @@ tsl_status shard_linear_workspace_size(const tsl_shard *shard, tsl_dtype wdtype,
  * Supported types: (wdtype, xdtype) = (F32, F32), (BF16, BF16),
  * (Q4G64, BF16); ydtype F32 or BF16 (round to nearest even).  Products
  * accumulate in binary32.  Q4G64 with M <= 64 applies the affine groups
- * exactly (binary32 group sums); with M > 64 the weights are expanded to
- * binary16 (s * q + b rounded once) and the activations narrowed to
- * binary16, exact for |x| < 65536 (bf16 values from 65536 up overflow, and
- * magnitudes below 2^-17 lose low bits).  M may be 0 (nothing is enqueued).
+ * exactly: the matrix cores multiply bf16 activations by 128 + q and each
+ * group adds s * sum(x (128 + q)) + (b - 128 s) * sum(x) in binary32, so
+ * activations must stay below 2^114 in magnitude (larger ones overflow
+ * those group sums).  Q4G64 with M > 64 runs on binary16 operands, scaled
+ * by powers of two for any finite bf16 input: activation row m becomes
+ * x * 2^-e_m with e_m = ilogb(max_k |x[m][k]|) - 15 and weight column n
+ * becomes (s * q + b) * 2^-f_n with f_n the packed column exponent, each
+ * rounded to nearest binary16 (weights via binary32), and the binary32
+ * result is multiplied by 2^(e_m + f_n).  Values within 2^29 of their
+ * row's (column's) largest keep binary16 precision (relative error
+ * <= 2^-11); smaller ones carry an absolute error of at most 2^(e_m - 25)
+ * (2^(f_n - 25)).  Non-finite inputs give non-finite outputs.  M may be 0
+ * (nothing is enqueued).
  * BF16 and Q4G64 weights with M > 64 require ldx and the shard's K below
  * 2^22 elements (else TSL_ERR_UNSUPPORTED).
  * Errors: TSL_ERR_INVALID_ARG, TSL_ERR_UNSUPPORTED,

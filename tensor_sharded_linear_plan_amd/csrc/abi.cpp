@@ -86,7 +86,8 @@ tsl_status geometry(const tsl_shard &s, tsl_dtype wdtype, PackGeom *g) {
             return TSL_ERR_GROUP_ALIGN;
         r.KT = (r.Ks + 127) / 128;
         r.Kpad = r.KT * 128;
-        r.total_bytes = round_up((size_t)r.Nt * (size_t)r.KT * kQ4Record, 256);
+        r.exp_off = round_up((size_t)r.Nt * (size_t)r.KT * kQ4Record, 256);
+        r.total_bytes = r.exp_off + round_up((size_t)r.Nt * 16 * 4, 256);
         break;
     }
     *g = r;

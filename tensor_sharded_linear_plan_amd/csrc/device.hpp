@@ -29,15 +29,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
            ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// A bf16 pair -> f16 pair.  Exact for |x| < 65520 (bf16 carries 8
-// significant bits, binary16 11); truncation toward zero never alters an
-// exactly representable value.
-__device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t p) {
-    typedef __fp16 h2 __attribute__((ext_vector_type(2)));
-    h2 v = __builtin_amdgcn_cvt_pkrtz(bf16_lo(p), bf16_hi(p));
-    return __builtin_bit_cast(uint32_t, v);
-}
-
 // ---- 4-bit codes ------------------------------------------------------------
 // A packed code word holds eight consecutive k of one column: even k in the
 // low half-word (nibbles 0..3), odd k in the high half-word (nibbles 4..7),
@@ -61,20 +52,19 @@ __device__ __forceinline__ bf16x8 q4_to_bf16_plus128(uint32_t w) {
     return __builtin_bit_cast(bf16x8, r);
 }
 
-// Word -> eight binary16 weights s * q + b, each rounded once to nearest
-// even: 0x6400 is f16 1024.0 with unit mantissa steps, so the pair
-// (w >> 4j) & 0x000F000F | 0x64006400 holds 1024 + q exactly and
-// fma(s, 1024 + q, b - 1024 s) = s q + b up to the rounding of c.
-__device__ __forceinline__ f16x8 q4_dequant_f16(uint32_t w, float s, float c) {
+// Word -> eight binary16 weights s q + b: q is an exact binary32 integer,
+// s q is exact (8 + 4 significant bits), the sum is rounded to binary32 and
+// then to nearest binary16 (a double rounding whose extra error is at most
+// 2^-24 relative).
+__device__ __forceinline__ f16x8 q4_dequant_f16(uint32_t w, float s, float b) {
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     u32x4 out;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        uint32_t p = ((w >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-        h2 v = __builtin_bit_cast(h2, p);
+        const uint32_t p = (w >> (4 * j)) & 0x000F000Fu;
         h2 r;
-        r.x = (_Float16)__builtin_fmaf(s, (float)v.x, c);
-        r.y = (_Float16)__builtin_fmaf(s, (float)v.y, c);
+        r.x = (_Float16)__builtin_fmaf(s, (float)(p & 0xFFu), b);
+        r.y = (_Float16)__builtin_fmaf(s, (float)(p >> 16), b);
         out[j] = __builtin_bit_cast(uint32_t, r);
     }
     return __builtin_bit_cast(f16x8, out);

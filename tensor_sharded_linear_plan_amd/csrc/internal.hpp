@@ -20,6 +20,9 @@ struct PackGeom {
     // F32: 16-k tiles; BF16: 32-k tiles; Q4G64: 128-k blocks
     int64_t KT = 0;
     size_t total_bytes = 0;
+    // Q4G64: byte offset of the column exponents ([Nt * 16] int32 after
+    // the records), see launch_pack_q4
+    size_t exp_off = 0;
 };
 
 tsl_status geometry(const tsl_shard &s, tsl_dtype wdtype, PackGeom *g);
@@ -28,6 +31,16 @@ tsl_status geometry(const tsl_shard &s, tsl_dtype wdtype, PackGeom *g);
 // bytes of (scale, bias) pairs of its two 64-k groups.
 constexpr int kQ4Record = 1152;
 constexpr int kQ4PairsAt = 1024;
+
+// Binary16 operands of the GEMM regime.  Column n of a 4-bit shard carries
+// an exponent f_n with every weight (s q + b) 2^-f_n below 2^15 in
+// magnitude (ilogb of the column's largest 15 |s| + |b|, minus 14); an
+// activation row m is scaled by 2^-e_m with e_m = ilogb(max |x|) - 15, so
+// its largest element lies in [2^15, 2^16), below the binary16 maximum
+// 65504 for every bf16 value.  The GEMM's binary32 result is multiplied
+// back by 2^(e_m + f_n).
+constexpr int kWeightExpBias = 14;
+constexpr int kActExpBias = 15;
 
 // ---- pack.hip ----
 hipError_t launch_pack_dense(const PackGeom &g, tsl_dtype wdtype, const void *W, int64_t stride_k,
@@ -175,9 +188,10 @@ struct PrefillPlan {
     int bm = 256, bn = 160; // block tile
     int wm = 4, wn = 1;     // wave grid
     // per item: byte offsets in the workspace of its binary16 weights (4-bit
-    // shards) and of its activation copy (binary16 for 4-bit shards,
-    // zero-padded bf16 when K is not a multiple of 64), and the item whose
-    // copy it reads (itself for the first reader of an X; -1: no copy)
+    // shards, followed by their column exponents) and of its activation copy
+    // (binary16 for 4-bit shards, followed by its row exponents; zero-padded
+    // bf16 when K is not a multiple of 64), and the item whose copy it reads
+    // (itself for the first reader of an X; -1: no copy)
     std::vector<size_t> w_off, x_off;
     std::vector<int> x_first;
     // per item: k-splits (1: none) and the byte offset of its [ks][M][Ns]

@@ -99,6 +99,36 @@ __global__ void __launch_bounds__(256) pack_q4_sb_kernel(const uint16_t *__restr
     *reinterpret_cast<uint32_t *>(out + t * kQ4Record + kQ4PairsAt + (e & 31) * 4) = v;
 }
 
+// Q4 column exponents: f_n = ilogb(max over the column's groups of
+// 15 |s| + |b|) - kWeightExpBias, 0 for a column whose groups are all zero
+// (or not finite).  Every weight s q + b of the column then satisfies
+// |(s q + b) 2^-f_n| <= 15 |s| 2^-f_n + |b| 2^-f_n < 2^15: the binary16
+// form of the GEMM regime holds the column's largest weights at full
+// precision whatever the magnitude of its scales and biases.
+__global__ void __launch_bounds__(256) pack_q4_exp_kernel(const uint16_t *__restrict__ scales,
+                                                          const uint16_t *__restrict__ biases,
+                                                          int64_t sb_stride_g, int64_t sb_stride_n,
+                                                          int64_t g_off, int64_t n_off, int64_t Gs,
+                                                          int64_t Ns, int64_t NP,
+                                                          int32_t *__restrict__ out) {
+    const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= NP)
+        return;
+    float m = 0.f;
+    if (n < Ns) {
+        for (int64_t g = 0; g < Gs; ++g) {
+            const int64_t at = (g_off + g) * sb_stride_g + (n_off + n) * sb_stride_n;
+            const float sc = __uint_as_float((uint32_t)scales[at] << 16);
+            const float bi = __uint_as_float((uint32_t)biases[at] << 16);
+            m = fmaxf(m, __builtin_fmaf(15.f, fabsf(sc), fabsf(bi)));
+        }
+    }
+    // frexp's exponent is ilogb + 1 for finite non-zero m
+    out[n] = (m > 0.f && m <= 3.4028234663852886e38f)
+                 ? __builtin_amdgcn_frexp_expf(m) - 1 - kWeightExpBias
+                 : 0;
+}
+
 inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
 
 } // namespace
@@ -140,6 +170,13 @@ hipError_t launch_pack_q4(const PackGeom &g, const uint8_t *codes, int64_t strid
     hipLaunchKernelGGL(pack_q4_sb_kernel, dim3(blocks_for(entries, 256)), dim3(256), 0, stream,
                        scales, biases, sb_stride_g, sb_stride_n, k_off / 64, n_off, g.Ks / 64,
                        g.Ns, GP, entries, out);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t NP = g.Nt * 16;
+    hipLaunchKernelGGL(pack_q4_exp_kernel, dim3(blocks_for(NP, 256)), dim3(256), 0, stream, scales,
+                       biases, sb_stride_g, sb_stride_n, k_off / 64, n_off, g.Ks / 64, g.Ns, NP,
+                       reinterpret_cast<int32_t *>(out + g.exp_off));
     return hipGetLastError();
 }
 

@@ -41,6 +41,7 @@
 
 #include <functional>
 #include <queue>
+#include <type_traits>
 #include <vector>
 
 #include "device.hpp"
@@ -64,11 +65,18 @@ struct GemmItem {
     int32_t MB, NB;    // tile grid
     int32_t T8;        // tiles per XCD, ceil(MB * NB / 8)
     int32_t start;     // first workgroup (a multiple of 8)
-    int32_t accumulate, y_bf16;
+    int32_t accumulate;
+    // bit 0: bf16 output.  Binary16 operands (4-bit weights) are scaled by
+    // powers of two: the row exponents follow the activation copy ([M]
+    // int32 at X + M ldx, padded to whole 256-row tiles), the column
+    // exponents the weight fragments ([Nt16 16] int32 at B + Nt16 KT32 64)
+    int32_t flags;
     int64_t M;         // rows of this item
     float *P;          // ks > 1: binary32 k-partials [ks][M][Ns]
     int32_t ks, pad_;  // k-splits: tile t of split q covers stages [q nst / ks, (q+1) nst / ks)
 };
+static_assert(sizeof(GemmItem) == 104, "item table size");
+constexpr int kYBf16 = 1;
 
 struct GemmGroup {
     int64_t M;
@@ -186,8 +194,9 @@ gemm_kernel(GemmGroup grp) {
     // recomputed at every issue (a few VALU ops) rather than held in
     // registers.  Rows past M and columns past the shard are clamped to the
     // last valid ones: in bounds, and those outputs are never stored.
-    // Offsets stay below 2^32 because the activation row stride and K are
-    // below 2^22 elements (checked by the caller).
+    // Offsets stay below 2^32 because a tile spans at most 256 rows and the
+    // activation row stride and K are below 2^22 elements (checked by the
+    // caller); the clamp limit counts only the tile's own rows.
     const char *xbase = reinterpret_cast<const char *>(a.X + m0 * a.ldx);
     const int64_t t0 = n0 >> 4;
     const char *bbase = reinterpret_cast<const char *>(a.B + t0 * (int64_t)a.KT32 * 64);
@@ -195,7 +204,8 @@ gemm_kernel(GemmGroup grp) {
     const uint32_t chunk = 8 * ((lane % C::CPR) ^ swz<C::CPR>(arow));
     const uint32_t aoff0 = ((uint32_t)(C::RPB * wave + arow) * (uint32_t)a.ldx + chunk) * 2;
     const uint32_t astep = 4 * C::RPB * (uint32_t)a.ldx * 2;
-    const uint32_t alim = ((uint32_t)(M - 1 - m0) * (uint32_t)a.ldx + chunk) * 2;
+    const int64_t last_row = M - 1 - m0 < BM - 1 ? M - 1 - m0 : BM - 1;
+    const uint32_t alim = ((uint32_t)last_row * (uint32_t)a.ldx + chunk) * 2;
     const int kr = 2 * (wave % C::S16) + (lane >> 5); // 8-k run of this wave's weight blocks
     const uint32_t boff0 = ((uint32_t)((kr >> 2) * 64 + (kr & 3) * 16 + (lane & 15))) * 16;
     const uint32_t tstep = (uint32_t)a.KT32 * 1024; // one 16-column tile
@@ -317,7 +327,7 @@ gemm_kernel(GemmGroup grp) {
     const int64_t col0 = n0 + wn * C::NT * 32 + (lane & 31);
     // a k-split writes its binary32 partial, [M][Ns] at split ksi
     const bool part = a.ks > 1;
-    const bool ybf = part ? false : a.y_bf16;
+    const bool ybf = part ? false : (a.flags & kYBf16) != 0;
     const bool accu = part ? false : a.accumulate;
     const int64_t ldy = part ? a.Ns : a.ldy;
     char *yb0 = part ? reinterpret_cast<char *>(a.P + (int64_t)ksi * M * a.Ns)
@@ -329,56 +339,96 @@ gemm_kernel(GemmGroup grp) {
 #pragma unroll
     for (int j = 0; j < C::NT; ++j)
         colok[j] = col0 + 32 * j < a.Ns;
+    // the store loop, without (bf16 operands) or with (binary16) the
+    // operand scales, each instance compiled for one of the two
+    auto store = [&](auto SCALED) __attribute__((always_inline)) {
+        constexpr bool sc = decltype(SCALED)::value;
+        // Exponents, all loaded before the first store (vmcnt counts stores
+        // too, so a load issued between stores would wait for them): one
+        // per column tile, and per 32-row block one load in which lane l
+        // takes row l of the block (the row exponents are padded to whole
+        // 256-row tiles); each lane then reads its rows, 4 (lane / 32)
+        // apart, from the lanes that hold them.
+        int cexp[C::NT], rblk[C::MT];
+        const bool hi = (lane >> 5) != 0;
+        if constexpr (sc) {
+            const int32_t *ce =
+                reinterpret_cast<const int32_t *>(a.B + (int64_t)a.Nt16 * a.KT32 * 64);
+            const int32_t *re = reinterpret_cast<const int32_t *>(a.X + M * a.ldx);
+            const int64_t rbase = m0 + wm * C::MT * 32;
 #pragma unroll
-    for (int i = 0; i < C::MT; ++i)
+            for (int j = 0; j < C::NT; ++j)
+                cexp[j] = colok[j] ? ce[col0 + 32 * j] : 0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int rr = i * 32 + 8 * (r >> 2) + (r & 3); // row step from row0
-            if (row0 + rr >= M)
-                continue;
-            char *yr = ybase + rr * rstride;
+            for (int i = 0; i < C::MT; ++i)
+                rblk[i] = re[rbase + i * 32 + (lane & 31)];
+        }
 #pragma unroll
-            for (int j = 0; j < C::NT; ++j) {
-                if (!colok[j])
+        for (int i = 0; i < C::MT; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rr = i * 32 + 8 * (r >> 2) + (r & 3); // row step from row0
+                if (row0 + rr >= M)
                     continue;
-                const float v = acc[i][j][r];
-                if (ybf) {
-                    __bf16 h = (__bf16)v;
-                    *reinterpret_cast<uint16_t *>(yr + j * 64) = __builtin_bit_cast(uint16_t, h);
-                } else {
-                    float *y = reinterpret_cast<float *>(yr + j * 128);
-                    *y = accu ? *y + v : v;
+                char *yr = ybase + rr * rstride;
+                int rexp = 0;
+                if constexpr (sc) {
+                    const int q = 8 * (r >> 2) + (r & 3);
+                    const int lo_e = __builtin_amdgcn_readlane(rblk[i], q);
+                    const int hi_e = __builtin_amdgcn_readlane(rblk[i], q + 4);
+                    rexp = hi ? hi_e : lo_e;
+                }
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j) {
+                    if (!colok[j])
+                        continue;
+                    float v = acc[i][j][r];
+                    // undo the operand scales: one exact power-of-two step
+                    // (rounded only where the result leaves the normal range)
+                    if constexpr (sc)
+                        v = __builtin_amdgcn_ldexpf(v, rexp + cexp[j]);
+                    if (ybf) {
+                        __bf16 h = (__bf16)v;
+                        *reinterpret_cast<uint16_t *>(yr + j * 64) =
+                            __builtin_bit_cast(uint16_t, h);
+                    } else {
+                        float *y = reinterpret_cast<float *>(yr + j * 128);
+                        *y = accu ? *y + v : v;
+                    }
                 }
             }
         }
+    };
+    // binary16 operands come only from 4-bit weights, which are always
+    // scaled; bf16 operands never are
+    if constexpr (OP == OP_F16)
+        store(std::true_type{});
+    else
+        store(std::false_type{});
 }
 
-// ---- prep: 4-bit weights -> binary16 fragments, ragged-K activations -> padded copy ----
-// One piece of the prep pass: a product's weights and activation copy, or
-// one member's share of a joined sum set (written at its k offset).
+// ---- prep: 4-bit weights -> binary16 fragments --------------------------
+// One piece of the weight pass: a product's weights, or one member's share
+// of a joined sum set (written at its k offset).  The members of a joined
+// set are consecutive pieces (pos 0 .. R - 1) and share one column
+// exponent, the largest of theirs; piece 0's first block stores it after
+// the fragments for the GEMM's epilogue.
 struct PrepItem {
-    // weights (4-bit items): packed records (codes, scale/bias pairs) ->
-    // fragments; column tile nt's 32-k fragments start at nt * kt_ld, this
-    // piece's at kt_off within them
+    // packed records (codes, scale/bias pairs) -> fragments; column tile
+    // nt's 32-k fragments start at nt * kt_ld, this piece's at kt_off
     const char *q4;
-    u32x4 *w_out;
-    // activations: Ks columns of rows of ldx_in -> Kpad columns (zero past
-    // Ks) of rows of x_ld
-    const uint16_t *x_in;
-    uint16_t *x_out;
-    int64_t ldx_in, x_ld;
-    int64_t w_chunks;  // 16-byte code chunks
-    int64_t x_units;   // 8-element output units (M * Kpad / 8)
+    u32x4 *w_out;        // fragments, then the column exponents [Nt 16] int32
+    const int32_t *fexp; // this member's column exponents (packed array)
+    int64_t w_chunks;    // 16-byte code chunks
     int32_t KB, Gs;
-    int32_t Ks, Kpad;
     int32_t kt_ld, kt_off;
-    int32_t w_blocks;  // workgroups [start, start + w_blocks) do weights
+    int32_t R, pos;      // members of the set (1: a lone product), this one's place
+    int32_t Ns;
     int32_t start;
 };
 
 struct PrepGroup {
-    int32_t n;
-    int32_t to_f16; // activations narrowed to binary16 (4-bit weights)
+    int32_t n, pad_;
     PrepItem it[kGroupMax];
 };
 
@@ -393,61 +443,162 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepGroup grp) {
             hi = mid - 1;
     }
     const PrepItem &p = grp.it[lo];
-    const int local = bid - p.start;
-    if (local < p.w_blocks) {
-        // one thread per packed 16-byte code chunk (16 columns x 128 k per
-        // 64 lanes), writing the four 32-k fragments it covers
-        const int64_t c = (int64_t)local * blockDim.x + threadIdx.x;
-        if (c >= p.w_chunks)
-            return;
-        const int lane = (int)(c & 63);
-        const int64_t t = c >> 6;
-        const int64_t nt = t / p.KB, blk = t % p.KB;
-        const char *rec = p.q4 + t * kQ4Record; // record (nt, blk)
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(rec + lane * 16);
+    // one thread per packed 16-byte code chunk (16 columns x 128 k per 64
+    // lanes), writing the four 32-k fragments it covers
+    const int64_t c = (int64_t)(bid - p.start) * blockDim.x + threadIdx.x;
+    if (c >= p.w_chunks)
+        return;
+    const int lane = (int)(c & 63);
+    const int64_t t = c >> 6;
+    const int64_t nt = t / p.KB, blk = t % p.KB;
+    const int64_t n = nt * 16 + (lane & 15);
+    // the column exponent (the set's largest, for a joined set)
+    int f = p.fexp[n];
+    for (int r = 0; r < p.R; ++r) {
+        const int fr = grp.it[lo - p.pos + r].fexp[n];
+        f = fr > f ? fr : f;
+    }
+    if (p.pos == 0 && blk == 0 && lane < 16)
+        reinterpret_cast<int32_t *>(p.w_out + (int64_t)(p.w_chunks / p.KB / 64) * p.kt_ld * 64)[n] =
+            f;
+    const char *rec = p.q4 + t * kQ4Record; // record (nt, blk)
+    const u32x4 w = *reinterpret_cast<const u32x4 *>(rec + lane * 16);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int64_t g = 2 * blk + h;
-            if (g >= p.Gs)
-                break; // pad group of a half-filled last block: never read
-            const uint32_t sbp =
-                *reinterpret_cast<const uint32_t *>(rec + kQ4PairsAt + ((lane & 15) * 2 + h) * 4);
-            const float s = bf16_lo(sbp);
-            const float cb = __builtin_fmaf(-1024.f, s, bf16_hi(sbp));
+    for (int h = 0; h < 2; ++h) {
+        const int64_t g = 2 * blk + h;
+        if (g >= p.Gs)
+            break; // pad group of a half-filled last block: never read
+        const uint32_t sbp =
+            *reinterpret_cast<const uint32_t *>(rec + kQ4PairsAt + ((lane & 15) * 2 + h) * 4);
+        // s 2^-f and b 2^-f are exact (bf16 significands) unless they fall
+        // below the binary32 range, far under the column's largest weight
+        const float s = __builtin_amdgcn_ldexpf(bf16_lo(sbp), -f);
+        const float b = __builtin_amdgcn_ldexpf(bf16_hi(sbp), -f);
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int tt = 2 * h + q;
-                const f16x8 v = q4_dequant_f16(w[tt], s, cb);
-                p.w_out[((nt * (int64_t)p.kt_ld + p.kt_off + blk * 4 + tt) * 64) + lane] =
-                    __builtin_bit_cast(u32x4, v);
+        for (int q = 0; q < 2; ++q) {
+            const int tt = 2 * h + q;
+            const f16x8 v = q4_dequant_f16(w[tt], s, b);
+            p.w_out[((nt * (int64_t)p.kt_ld + p.kt_off + blk * 4 + tt) * 64) + lane] =
+                __builtin_bit_cast(u32x4, v);
+        }
+    }
+}
+
+// ---- prep: activation copies ----------------------------------------------
+// One job per distinct activation matrix of a launch: a product's X, or the
+// members' blocks X_0, X_1, ... of a joined sum set side by side.  A
+// workgroup takes one row.  Binary16 copies (4-bit weights): the row's
+// largest magnitude fixes e_m (kActExpBias below its ilogb), every element
+// becomes x 2^-e_m rounded to nearest binary16, and e_m goes to rexp[m].
+// Plain copies (bf16 weights with ragged K) only zero-pad.  Segment r is
+// the piece at pos r of the job; columns past its Ks up to Kw are zero.
+struct XPiece {
+    const uint16_t *x_in;
+    uint16_t *x_out;  // this segment's first output column
+    int32_t *rexp;    // row exponents (binary16 copy), null for a plain copy
+    int64_t ldx_in;
+    int32_t x_ld;     // output row stride (elements)
+    int32_t Ks, Kw;   // columns read / written by this segment
+    int32_t R, pos;   // segments of the job, this one's place
+    int32_t M;        // rows
+    int32_t start;    // first workgroup of the job (the same for its pieces)
+    int32_t pad_;
+};
+
+struct XPrepGroup {
+    int32_t n, pad_;
+    XPiece it[kGroupMax];
+};
+
+// |x| of a bf16 pair, bit patterns (magnitude order is integer order)
+__device__ __forceinline__ uint32_t pair_max_abs(uint32_t m, uint32_t v) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    const us2 a = __builtin_bit_cast(us2, m), b = __builtin_bit_cast(us2, v & 0x7FFF7FFFu);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+}
+
+__global__ void __launch_bounds__(256) xprep_kernel(XPrepGroup grp) {
+    __shared__ uint32_t red[4];
+    const int bid = blockIdx.x;
+    int lo = 0, hi = grp.n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (grp.it[mid].start <= bid)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const int first = lo - grp.it[lo].pos;
+    const XPiece &j0 = grp.it[first];
+    const int64_t m = bid - j0.start;
+    const bool to_f16 = j0.rexp != nullptr;
+    int e = 0;
+    if (to_f16) {
+        uint32_t mx = 0;
+        for (int r = 0; r < j0.R; ++r) {
+            const XPiece &p = grp.it[first + r];
+            const uint16_t *src = p.x_in + m * p.ldx_in;
+            for (int k = threadIdx.x * 8; k < p.Ks; k += 256 * 8) {
+                if (k + 8 <= p.Ks) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(src + k);
+                    mx = pair_max_abs(mx, v.x);
+                    mx = pair_max_abs(mx, v.y);
+                    mx = pair_max_abs(mx, v.z);
+                    mx = pair_max_abs(mx, v.w);
+                } else {
+                    for (int q = k; q < p.Ks; ++q)
+                        mx = pair_max_abs(mx, src[q]);
+                }
             }
         }
-        return;
-    }
-    // activations: one thread per 8 output elements
-    const int64_t units = p.Kpad / 8;
-    const int64_t u = (int64_t)(local - p.w_blocks) * blockDim.x + threadIdx.x;
-    if (u >= p.x_units)
-        return;
-    const int64_t m = u / units, k = (u % units) * 8;
-    const uint16_t *src = p.x_in + m * p.ldx_in + k;
-    u32x4 v = {0, 0, 0, 0};
-    if (k + 8 <= p.Ks) {
-        v = *reinterpret_cast<const u32x4 *>(src);
-    } else if (k < p.Ks) {
+        uint32_t h = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t lo2 = (k + 2 * j < p.Ks) ? src[2 * j] : 0u;
-            const uint32_t hi2 = (k + 2 * j + 1 < p.Ks) ? src[2 * j + 1] : 0u;
-            v[j] = lo2 | (hi2 << 16);
+        for (int o = 32; o >= 1; o >>= 1) {
+            const uint32_t x = __shfl_xor(h, o, 64);
+            h = x > h ? x : h;
+        }
+        if ((threadIdx.x & 63) == 0)
+            red[threadIdx.x >> 6] = h;
+        __syncthreads();
+        h = red[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w)
+            h = red[w] > h ? red[w] : h;
+        // a row of zeros (or non-finite values) keeps e = 0
+        if (h != 0 && h < 0x7F80u)
+            e = __builtin_amdgcn_frexp_expf(__uint_as_float(h << 16)) - 1 - kActExpBias;
+        if (threadIdx.x == 0)
+            j0.rexp[m] = e;
+    }
+    for (int r = 0; r < j0.R; ++r) {
+        const XPiece &p = grp.it[first + r];
+        const uint16_t *src = p.x_in + m * p.ldx_in;
+        uint16_t *dst = p.x_out + m * (int64_t)p.x_ld;
+        for (int k = threadIdx.x * 8; k < p.Kw; k += 256 * 8) {
+            u32x4 v = {0, 0, 0, 0};
+            if (k + 8 <= p.Ks) {
+                v = *reinterpret_cast<const u32x4 *>(src + k);
+            } else if (k < p.Ks) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t lo2 = (k + 2 * q < p.Ks) ? src[k + 2 * q] : 0u;
+                    const uint32_t hi2 = (k + 2 * q + 1 < p.Ks) ? src[k + 2 * q + 1] : 0u;
+                    v[q] = lo2 | (hi2 << 16);
+                }
+            }
+            if (to_f16) {
+                typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    h2 o;
+                    o.x = (_Float16)__builtin_amdgcn_ldexpf(bf16_lo(v[q]), -e);
+                    o.y = (_Float16)__builtin_amdgcn_ldexpf(bf16_hi(v[q]), -e);
+                    v[q] = __builtin_bit_cast(uint32_t, o);
+                }
+            }
+            *reinterpret_cast<u32x4 *>(dst + k) = v;
         }
     }
-    if (grp.to_f16) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            v[j] = bf16pair_to_f16pair(v[j]);
-    }
-    *reinterpret_cast<u32x4 *>(p.x_out + m * p.x_ld + k) = v;
 }
 
 typedef void (*GemmFn)(GemmGroup);
@@ -585,21 +736,26 @@ PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64
             best_factors = factors;
         }
     }
-    // workspace: binary16 weight fragments of 4-bit items; activation
-    // copies (binary16 for 4-bit items, zero-padded bf16 for ragged-K bf16
-    // items), one per distinct (X, ldx, K, rows) -- items without a known X
-    // (sizing) never share
+    // workspace: binary16 weight fragments of 4-bit items with their column
+    // exponents; activation copies (binary16 for 4-bit items, with their row
+    // exponents; zero-padded bf16 for ragged-K bf16 items), one per distinct
+    // (X, ldx, K, rows) -- items without a known X (sizing, joined sets)
+    // never share
     best.w_off.assign(n, 0);
     best.x_off.assign(n, 0);
     best.x_first.assign(n, -1);
     size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) / 256 * 256;
+        return at;
+    };
     for (int i = 0; i < n; ++i) {
         const PackGeom &g = items[i].g;
-        if (wdtype == TSL_Q4G64) {
-            best.w_off[i] = off;
-            off += (size_t)g.Nt * (size_t)g.KT * 4 * 1024;
-        }
-        if (wdtype == TSL_Q4G64 || g.Ks % 64 != 0) {
+        const bool q4 = wdtype == TSL_Q4G64;
+        if (q4) // binary16 fragments, then the column exponents
+            best.w_off[i] = take((size_t)g.Nt * (size_t)g.KT * 4 * 1024 + (size_t)g.Nt * 16 * 4);
+        if (q4 || g.Ks % 64 != 0) {
             int first = i;
             for (int j = 0; j < i && items[i].X; ++j)
                 if (items[j].X == items[i].X && items[j].ldx == items[i].ldx &&
@@ -608,12 +764,12 @@ PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64
                     break;
                 }
             best.x_first[i] = first;
-            if (first == i) {
-                best.x_off[i] = off;
-                off += ((size_t)items[i].M * (size_t)kpad64(g.Ks) * 2 + 255) / 256 * 256;
-            } else {
-                best.x_off[i] = best.x_off[first];
-            }
+            // the copy, then (binary16) its row exponents, padded to whole
+            // 256-row tiles (the GEMM reads them by the tile)
+            best.x_off[i] = first == i ? take((size_t)items[i].M * (size_t)kpad64(g.Ks) * 2 +
+                                              (q4 ? (size_t)(items[i].M + 255) / 256 * 256 * 4
+                                                  : 0))
+                                       : best.x_off[first];
         }
     }
     // k-splits (split_ks with the launch's modelled factor), their binary32
@@ -634,63 +790,119 @@ PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64
     return best;
 }
 
+// Byte offset of the column exponents in a 4-bit shard packed as Nt column
+// tiles of KT 128-k records (the records, rounded up to 256 bytes).
+inline size_t q4_exp_off(int64_t Nt, int64_t KT) {
+    return ((size_t)Nt * (size_t)KT * kQ4Record + 255) / 256 * 256;
+}
+
 hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, tsl_dtype wdtype,
                           int64_t M, void *workspace, hipStream_t stream) {
     const Variant v{p.bm, p.bn, p.wm, p.wn};
-    GemmFn fn = wdtype == TSL_Q4G64 ? pick<OP_F16>(v) : pick<OP_BF16>(v);
+    const bool q4 = wdtype == TSL_Q4G64;
+    GemmFn fn = q4 ? pick<OP_F16>(v) : pick<OP_BF16>(v);
     if (!fn)
         return hipErrorInvalidValue;
     char *ws = static_cast<char *>(workspace);
     for (int c0 = 0; c0 < n; c0 += kGroupMax) {
         const int cn = n - c0 < kGroupMax ? n - c0 : kGroupMax;
-        // 1. prep: expand 4-bit weights, copy activations (once per X); a
-        // joined sum set is one piece per member, at the member's k offset
-        std::vector<PrepItem> pieces;
+        // 1. activation copies, one job per distinct X (a joined set's job
+        // has a piece per member), launched in groups of whole jobs
+        std::vector<XPiece> xp;
+        std::vector<int> xjob_rows;
         for (int i = 0; i < cn; ++i) {
             const LinearItem &L = items[c0 + i];
-            const PackGeom &g = L.g;
-            const bool q4 = wdtype == TSL_Q4G64;
-            const bool xcopy = p.x_first[c0 + i] == c0 + i;
-            if (!q4 && !xcopy)
+            if (p.x_first[c0 + i] != c0 + i)
                 continue;
+            const PackGeom &g = L.g;
+            const int R = L.cat;
+            const int64_t kseg = g.Ks / R;
+            for (int r = 0; r < R; ++r) {
+                XPiece x{};
+                x.x_in = static_cast<const uint16_t *>(R > 1 ? L.seg_X[r] : L.X);
+                x.ldx_in = R > 1 ? L.seg_ldx[r] : L.ldx;
+                x.x_out = reinterpret_cast<uint16_t *>(ws + p.x_off[c0 + i]) + r * kseg;
+                // row exponents right after the copy's M rows
+                x.rexp = q4 ? reinterpret_cast<int32_t *>(reinterpret_cast<uint16_t *>(
+                                                               ws + p.x_off[c0 + i]) +
+                                                           L.M * kpad64(g.Ks))
+                            : nullptr;
+                x.x_ld = (int32_t)kpad64(g.Ks);
+                x.Ks = (int32_t)kseg;
+                x.Kw = (int32_t)(R > 1 ? kseg : kpad64(g.Ks));
+                x.R = R;
+                x.pos = r;
+                x.M = (int32_t)L.M;
+                xp.push_back(x);
+            }
+        }
+        for (size_t q0 = 0; q0 < xp.size();) {
+            XPrepGroup xg{};
+            int64_t blocks = 0;
+            size_t q = q0;
+            while (q < xp.size() && q - q0 + xp[q].R <= (size_t)kGroupMax) {
+                for (int r = 0; r < xp[q].R; ++r) {
+                    XPiece &x = xg.it[xg.n++];
+                    x = xp[q + r];
+                    x.start = (int32_t)blocks;
+                }
+                blocks += xp[q].M;
+                q += xp[q].R;
+            }
+            if (blocks > 0) {
+                hipLaunchKernelGGL(xprep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, xg);
+                hipError_t e = hipGetLastError();
+                if (e != hipSuccess)
+                    return e;
+            }
+            q0 = q;
+        }
+        // 2. 4-bit weights -> binary16 fragments, a piece per member, in
+        // groups of whole sets
+        std::vector<PrepItem> pieces;
+        for (int i = 0; q4 && i < cn; ++i) {
+            const LinearItem &L = items[c0 + i];
+            const PackGeom &g = L.g;
             const int R = L.cat;
             const int64_t kseg = g.Ks / R, kbseg = g.KT / R; // per member
             for (int r = 0; r < R; ++r) {
                 PrepItem a{};
                 a.q4 = static_cast<const char *>(R > 1 ? L.seg_packed[r] : L.packed);
                 a.w_out = reinterpret_cast<u32x4 *>(ws + p.w_off[c0 + i]);
+                a.fexp = reinterpret_cast<const int32_t *>(a.q4 + q4_exp_off(g.Nt, kbseg));
                 a.kt_ld = (int32_t)(g.KT * 4);
                 a.kt_off = (int32_t)(r * kbseg * 4);
-                a.x_in = static_cast<const uint16_t *>(R > 1 ? L.seg_X[r] : L.X);
-                a.x_out = reinterpret_cast<uint16_t *>(ws + p.x_off[c0 + i]) + r * kseg;
-                a.ldx_in = R > 1 ? L.seg_ldx[r] : L.ldx;
-                a.x_ld = kpad64(g.Ks);
-                a.w_chunks = q4 ? g.Nt * kbseg * 64 : 0;
-                a.Kpad = (int32_t)(R > 1 ? kseg : kpad64(g.Ks));
-                a.x_units = xcopy ? L.M * (a.Kpad / 8) : 0;
+                a.w_chunks = g.Nt * kbseg * 64;
                 a.KB = (int32_t)kbseg;
                 a.Gs = (int32_t)(kseg / 64);
-                a.Ks = (int32_t)kseg;
-                a.w_blocks = (int32_t)((a.w_chunks + 255) / 256);
+                a.R = R;
+                a.pos = r;
+                a.Ns = (int32_t)g.Ns;
                 pieces.push_back(a);
             }
         }
-        for (size_t q0 = 0; q0 < pieces.size(); q0 += kGroupMax) {
+        for (size_t q0 = 0; q0 < pieces.size();) {
             PrepGroup pg{};
-            pg.to_f16 = wdtype == TSL_Q4G64;
             int64_t pblocks = 0;
-            for (size_t q = q0; q < pieces.size() && q < q0 + kGroupMax; ++q) {
-                PrepItem &a = pg.it[pg.n++];
-                a = pieces[q];
-                a.start = (int32_t)pblocks;
-                pblocks += a.w_blocks + (a.x_units + 255) / 256;
+            size_t q = q0;
+            while (q < pieces.size() && q - q0 + pieces[q].R <= (size_t)kGroupMax) {
+                for (int r = 0; r < pieces[q].R; ++r) {
+                    PrepItem &a = pg.it[pg.n++];
+                    a = pieces[q + r];
+                    a.start = (int32_t)pblocks;
+                    pblocks += (a.w_chunks + 255) / 256;
+                }
+                q += pieces[q].R;
             }
-            hipLaunchKernelGGL(prep_kernel, dim3((unsigned)pblocks), dim3(256), 0, stream, pg);
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess)
-                return e;
+            if (pblocks > 0) {
+                hipLaunchKernelGGL(prep_kernel, dim3((unsigned)pblocks), dim3(256), 0, stream, pg);
+                hipError_t e = hipGetLastError();
+                if (e != hipSuccess)
+                    return e;
+            }
+            q0 = q;
         }
-        // 2. the GEMM over every item's tiles
+        // 3. the GEMM over every item's tiles
         GemmGroup grp{};
         grp.M = M;
         grp.n = cn;
@@ -699,7 +911,7 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
             const LinearItem &L = items[c0 + i];
             const PackGeom &g = L.g;
             GemmItem &a = grp.it[i];
-            const bool q4 = wdtype == TSL_Q4G64, copied = p.x_first[c0 + i] >= 0;
+            const bool copied = p.x_first[c0 + i] >= 0;
             a.B = static_cast<const u32x4 *>(q4 ? static_cast<const void *>(ws + p.w_off[c0 + i])
                                                 : L.packed);
             a.X = copied ? reinterpret_cast<const uint16_t *>(ws + p.x_off[c0 + i])
@@ -719,7 +931,7 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
             a.T8 = (a.MB * a.NB * a.ks + 7) / 8;
             a.start = (int32_t)blocks;
             a.accumulate = L.accumulate;
-            a.y_bf16 = L.ydtype == TSL_BF16;
+            a.flags = L.ydtype == TSL_BF16 ? kYBf16 : 0;
             blocks += 8 * (int64_t)a.T8;
         }
         hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, stream, grp);

@@ -85,3 +85,52 @@ def router(seed, T, k, n_experts):
     logits = g.standard_normal((T, k))
     w = np.exp(logits - logits.max(axis=1, keepdims=True))
     return topk, (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def wide_rows_bf16(seed, M, K):
+    """bf16 activations whose rows span the bf16 range: row m is N(0, 1)
+    scaled by a pattern chosen by m % 7 -- 1e6; 1e-30; N(0, 1) with one
+    element set to +-3e38; 2^U(-60, 60) per element; plain N(0, 1); 1e-39
+    (bf16 subnormals); N(0, 1) with one element 65536 (just past binary16)."""
+    g = rng(seed)
+    x = g.standard_normal((M, K), dtype=np.float32)
+    kind = np.arange(M) % 7
+    x[kind == 0] *= np.float32(1e6)
+    x[kind == 1] *= np.float32(1e-30)
+    big = np.nonzero(kind == 2)[0]
+    x[big, g.integers(0, K, size=big.size)] = np.where(g.random(big.size) < 0.5, -3e38, 3e38)
+    mixed = np.nonzero(kind == 3)[0]
+    x[mixed] *= np.exp2(g.uniform(-60, 60, size=(mixed.size, K))).astype(np.float32)
+    x[kind == 5] *= np.float32(1e-39)
+    edge = np.nonzero(kind == 6)[0]
+    x[edge, g.integers(0, K, size=edge.size)] = np.float32(65536.0)
+    return f32_to_bf16_bits(x)
+
+
+def wide_scales_bf16(seed, shape, lo=0.005, hi=0.02):
+    """4-bit group scales U(lo, hi) times a per-column 10^U(-30, 30), and per
+    group a further 2^U(-20, 20): columns and groups far apart in magnitude."""
+    g = rng(seed)
+    G, N = shape
+    s = g.uniform(lo, hi, size=shape)
+    s *= 10.0 ** g.uniform(-30, 30, size=(1, N))
+    s *= np.exp2(g.uniform(-20, 20, size=shape))
+    return f32_to_bf16_bits(s.astype(np.float32))
+
+
+def wide_biases_bf16(seed, scales_bits, std=3.0):
+    """Biases N(0, std^2) times the group's own scale (same magnitude class)."""
+    s = bf16_bits_to_f32(scales_bits).astype(np.float64)
+    b = rng(seed).standard_normal(s.shape) * std * s
+    return f32_to_bf16_bits(b.astype(np.float32))
+
+
+def big_int_rows_bf16(seed, M, K, top=20):
+    """Integers in {-3..3} with one element per row replaced by +-2^j, j
+    uniform on 0..top: integer-valued rows up to 2^top in magnitude."""
+    g = rng(seed)
+    x = g.integers(-3, 4, size=(M, K)).astype(np.float32)
+    j = g.integers(0, top + 1, size=M)
+    sign = np.where(g.random(M) < 0.5, -1.0, 1.0)
+    x[np.arange(M), g.integers(0, K, size=M)] = (sign * np.exp2(j)).astype(np.float32)
+    return f32_to_bf16_bits(x)

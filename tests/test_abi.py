@@ -141,8 +141,9 @@ def test_pack_shard_size_geometry(tsl_lib):
     # f32: Nt=64 tiles, 64 k-tiles of 16, 64 lanes x 16 bytes
     assert tsl_lib.pack_shard_size(s, tsl_lib.F32) == 64 * 64 * 64 * 16
     assert tsl_lib.pack_shard_size(s, tsl_lib.BF16) == 64 * 32 * 64 * 16
-    # Q4: codes 64 tiles x 8 blocks x 1 KiB, pairs 64 x 16 groups x 16 x 4 bytes
-    assert tsl_lib.pack_shard_size(s, tsl_lib.Q4G64) == 64 * 8 * 1152  # records of codes + pairs
+    # Q4: records (codes + scale/bias pairs) of 64 tiles x 8 blocks, then the
+    # column exponents, 64 x 16 int32
+    assert tsl_lib.pack_shard_size(s, tsl_lib.Q4G64) == 64 * 8 * 1152 + 64 * 16 * 4
     # ragged: 100 x 30 bf16 -> 2 tiles of 16 columns, k padded to 128 (4 tiles of 32)
     r = tsl_lib.plan_linear(100, 30, 1, tsl_lib.COLUMN)[0]
     assert tsl_lib.pack_shard_size(r, tsl_lib.BF16) == 2 * 4 * 1024
@@ -265,12 +266,12 @@ def test_group_rejections_and_workspace(tsl_lib):
 
     good = [item(sh[0], P0, Y0), item(sh[1], P1, Y1)]
     # the group's workspace is the sum of its items' (4-bit prefill: binary16
-    # weights and a binary16 copy of the activations -- a size query sees no
-    # X pointers, so it never counts a copy as shared -- and, the launch
-    # being far too small to fill the chip, the binary32 partials of two
-    # k-splits of 8 stages each)
+    # weights and their column exponents, a binary16 copy of the activations
+    # and its row exponents -- a size query sees no X pointers, so it never
+    # counts a copy as shared -- and, the launch being far too small to fill
+    # the chip, the binary32 partials of two k-splits of 8 stages each)
     w = [tsl_lib.shard_linear_workspace_size(s, tsl_lib.Q4G64, M) for s in sh]
-    assert w[0] == 1024 * 256 * 2 + M * 1024 * 2 + 2 * M * 256 * 4
+    assert w[0] == 1024 * 256 * 2 + 256 * 4 + M * 1024 * 2 + M * 4 + 2 * M * 256 * 4
     assert tsl_lib.shard_linear_group_workspace_size(good, tsl_lib.Q4G64, M) == sum(w)
     assert tsl_lib.shard_linear_group_workspace_size(good[:1], tsl_lib.Q4G64, 4) == \
         tsl_lib.shard_linear_workspace_size(sh[0], tsl_lib.Q4G64, 4)
@@ -349,8 +350,8 @@ def test_sum_set_rules(tsl_lib):
 
     # prefill, members of whole 128-k records: the set is one product over
     # the members' k-ranges end to end -- the workspace of the unsharded
-    # product (its binary16 weights, activation copy and k-partials), no
-    # rank partials
+    # product (its binary16 weights with the set's column exponents, the
+    # activation copy with its row exponents, k-partials), no rank partials
     full = tsl_lib.plan_linear(K, N, 1, tsl_lib.ROW, 64)[0]
     assert tsl_lib.shard_linear_group_workspace_size(items(), tsl_lib.Q4G64, M) == \
         tsl_lib.shard_linear_workspace_size(full, tsl_lib.Q4G64, M)

@@ -56,6 +56,24 @@ def decode_q4(buf, Ks, Ns):
     return codes, sc, bi
 
 
+def decode_q4_exponents(buf, Ks, Ns):
+    """The column exponents after the records (records rounded up to 256 bytes)."""
+    Nt = (Ns + 15) // 16
+    KB = (Ks + 127) // 128
+    at = (Nt * KB * 1152 + 255) // 256 * 256
+    return buf.cpu().numpy()[at:at + Nt * 64].view(np.int32)
+
+
+def column_exponents(sc, bi, Ns_pad):
+    """Documented rule, in numpy: ilogb of the column's largest
+    15 |s| + |b| (binary32, the product exact), minus 14; 0 for zero columns."""
+    s = np.abs(oracle.bf16_to_f64(sc)).astype(np.float32)
+    b = np.abs(oracle.bf16_to_f64(bi)).astype(np.float32)
+    m = np.max(np.float32(15.0) * s + b, axis=0)
+    e = np.where(m > 0, np.frexp(m)[1] - 1 - 14, 0).astype(np.int32)
+    return np.concatenate([e, np.zeros(Ns_pad - e.size, dtype=np.int32)])
+
+
 @pytest.mark.parametrize("wdtype", ["f32", "bf16"])
 @pytest.mark.parametrize("K,N,tp,strategy", [(1024, 2048, 2, 0), (1024, 2048, 2, 1),
                                              (100, 30, 1, 0), (96, 80, 2, 1), (200, 48, 4, 2)])
@@ -94,3 +112,19 @@ def test_pack_q4_layout(K, N, tp, strategy):
         assert np.array_equal(bi[:Ks // 64, :Ns], b_want)
         assert not codes[Ks:].any() and not codes[:, Ns:].any()
         assert not sc[Ks // 64:].any() and not sc[:, Ns:].any()
+        want_e = column_exponents(s_want, b_want, (Ns + 15) // 16 * 16)
+        assert np.array_equal(decode_q4_exponents(buf, Ks, Ns), want_e)
+
+
+def test_pack_q4_column_exponents_wide_scales():
+    # columns 10^+-30 apart, groups 2^+-20 apart within a column
+    K, N = 640, 72
+    w = Q4Weight(K, N, 620, 621, 622)
+    w.scales = synth.wide_scales_bf16(623, (K // 64, N))
+    w.biases = synth.wide_biases_bf16(624, w.scales)
+    w.d_scales, w.d_biases = dev(w.scales), dev(w.biases)
+    sh = tsl.plan_linear(K, N, 1, tsl.COLUMN, 64)[0]
+    buf, nb = w.pack(sh)
+    want = column_exponents(w.scales, w.biases, 80)
+    assert np.array_equal(decode_q4_exponents(buf, K, N), want)
+    assert want.min() < -100 and want.max() > 80
