@@ -206,8 +206,12 @@ def prefill_bench(args, tsl, torch, synth, configs):
     layer = configs.PRE27B
     M = layer.ms[0]
     t0 = time.perf_counter()
-    shards, packs, pack_s, pack_bytes = build_layer(layer, M, 1, tsl, torch, synth, configs)
-    log("prefill: packed %d shards (%.1f s)" % (len(packs[0]), time.perf_counter() - t0))
+    # two copies of every rank's packed weights (2 x 203.5 MB), alternated
+    # step by step, so that no step finds its weights in the 256 MB
+    # last-level cache
+    shards, packs, pack_s, pack_bytes = build_layer(layer, M, 2, tsl, torch, synth, configs)
+    log("prefill: packed %d shards x %d copies (%.1f s)" % (len(packs[0]), len(packs),
+                                                           time.perf_counter() - t0))
     run, run_separate, flops, nbytes, nitems = make_step(layer, M, shards, packs, tsl, torch,
                                                          configs, 31)
     stream = torch.cuda.current_stream().cuda_stream

@@ -41,6 +41,12 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden symbol visibility; the declarations of
+ * this header are its only exported names. */
+#if defined(__GNUC__)
+#pragma GCC visibility push(default)
+#endif
+
 typedef enum tsl_status {
     TSL_OK = 0,
     TSL_ERR_INVALID_ARG = -1,      /* null pointer, non-positive size, bad enum */
@@ -559,6 +565,10 @@ const char *tsl_status_string(tsl_status status);
 /* The HIP runtime's description of the error behind the most recent
  * TSL_ERR_HIP returned on the calling thread ("no error" if none). */
 const char *tsl_last_hip_error_string(void);
+
+#if defined(__GNUC__)
+#pragma GCC visibility pop
+#endif
 
 #ifdef __cplusplus
 }

@@ -8,6 +8,7 @@ Objects go to _build/ at the repository root.
 """
 import concurrent.futures
 import os
+import re
 import subprocess
 import sys
 
@@ -21,6 +22,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["abi.cpp", "plan.cpp", "pack.hip", "combine.hip", "embed.hip", "moe.hip", "skinny.hip", "prefill.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-mcode-object-version=5", "-Wall",
+         # only the C ABI of include/tsl.h is exported (it sets default visibility)
+         "-fvisibility=hidden", "-fvisibility-inlines-hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          # the LDS-copy asm in prefill.hip sets m0 and lists it as clobbered on purpose
          "-Wno-inline-asm",
@@ -39,6 +42,22 @@ def _compile(src):
     return obj, err
 
 
+def exported_names():
+    """The entry points include/tsl.h declares (its only exported names)."""
+    with open(os.path.join(INCLUDE, "tsl.h")) as f:
+        header = f.read()
+    return re.findall(r"^(?:tsl_status|const char \*)\s*(\w+)\(", header, re.M)
+
+
+def _version_script():
+    path = os.path.join(OBJDIR, "tsl.map")
+    body = "".join("    %s;\n" % n for n in exported_names())
+    with open(path, "w") as f:
+        # the HIP compiler's per-unit ids stay as they are emitted
+        f.write("{\n  global:\n%s    __hip_cuid_*;\n  local: *;\n};\n" % body)
+    return path
+
+
 def build(verbose=False, jobs=None):
     """Compile all sources and link libtsl.so; returns its path."""
     os.makedirs(OBJDIR, exist_ok=True)
@@ -50,7 +69,8 @@ def build(verbose=False, jobs=None):
             if err.strip():
                 print(err, file=sys.stderr)
     tmp = LIBRARY + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + [o for o, _ in results]
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950",
+           "-Wl,--version-script=" + _version_script(), "-o", tmp] + [o for o, _ in results]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)

@@ -625,6 +625,18 @@ __global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
     // arrivals; a word tagged with another ticket (an earlier call, or
     // never written) counts as zero, and the last arrival leaves ticket <<
     // 16 | 0, so a replay of the same enqueued call starts from zero too.
+    //
+    // Ordering, on gfx950's instructions rather than C++ acquire/release
+    // (which would cost the L2 write-back and invalidate above): the
+    // partials are "global_store_dword ... sc1" (written through to the
+    // device-coherent level); "s_waitcnt vmcnt(0)" below returns only once
+    // those stores are acknowledged there; the counter update is a device-
+    // scope "global_atomic_cmpswap_x2", performed at that same level after
+    // the wait; the last arrival's reads are "global_load_dword ... sc1"
+    // (they miss the non-coherent L2) and issue only after its swap has
+    // returned, behind a branch on the swap's result.  So every member's
+    // stores are visible before the count that admits the last arrival,
+    // and that arrival's reads come after it.
     const FusedSet &fs = grp.fs[a.fset];
     const unsigned long long tag = grp.ticket << 16;
     const int64_t mb = m0 / (16 * MT);
@@ -638,9 +650,15 @@ __global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
         unsigned long long *ctr = fs.ctr + mb * a.Nt + ntile[j];
         int last = 0;
         if (lane == 0) {
+            // A failed swap means another member's swap on this word
+            // succeeded in between (the word changes only by a member's
+            // increment or the last arrival's reset, which follows every
+            // increment of this call), so the loop ends after at most R - 1
+            // failures; it never gives up, since a lost arrival would leave
+            // the tile's sum unwritten.
             unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT);
-            for (int tries = 0; tries < 4096; ++tries) {
+            for (;;) {
                 const unsigned long long base = (old & ~0xFFFFull) == tag ? old : tag;
                 if (__hip_atomic_compare_exchange_strong(ctr, &old, base + 1, __ATOMIC_RELAXED,
                                                          __ATOMIC_RELAXED,

@@ -36,6 +36,17 @@ def test_library_exports_every_declared_symbol(tsl_lib):
     assert set(tsl_lib.EXPORTS) == set(names)
 
 
+def test_library_exports_nothing_else(tsl_lib):
+    # the kernels' C++ internals are hidden: the dynamic symbol table holds
+    # the header's entry points and the HIP compiler's per-unit ids only
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", tsl_lib.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    defined = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    others = {n for n in defined if not n.startswith("__hip_cuid_")}
+    assert others == set(declared_functions())
+
+
 def test_shard_struct_layout_matches_header(tsl_lib):
     assert ctypes.sizeof(tsl_lib.Shard) == 72
     assert tsl_lib.Shard.K.offset == 16 and tsl_lib.Shard.head_off.offset == 64
