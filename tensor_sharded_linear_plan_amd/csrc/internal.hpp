@@ -187,12 +187,11 @@ hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, ts
 struct PrefillPlan {
     int bm = 256, bn = 160; // block tile
     int wm = 4, wn = 1;     // wave grid
-    // per item: byte offsets in the workspace of its binary16 weights (4-bit
-    // shards, followed by their column exponents) and of its activation copy
+    // per item: byte offset in the workspace of its activation copy
     // (binary16 for 4-bit shards, followed by its row exponents; zero-padded
     // bf16 when K is not a multiple of 64), and the item whose copy it reads
     // (itself for the first reader of an X; -1: no copy)
-    std::vector<size_t> w_off, x_off;
+    std::vector<size_t> x_off;
     std::vector<int> x_first;
     // per item: k-splits (1: none) and the byte offset of its [ks][M][Ns]
     // binary32 k-partials, which a sum launch then adds in k order
@@ -206,6 +205,12 @@ PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64
 int64_t prefill_blocks(const PrefillPlan &p, const LinearItem *items, int n, int64_t M);
 hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, tsl_dtype wdtype,
                           int64_t M, void *workspace, hipStream_t stream);
+
+// ---- q4gemm.hip: the fused 4-bit GEMM (records expanded in registers) ----
+// Enqueues the GEMM of every item (their binary16 activation copies at
+// ws + p.x_off[i], already written by the activation pass).
+hipError_t launch_q4_gemm(const PrefillPlan &p, const LinearItem *items, int n, const char *ws,
+                          hipStream_t stream);
 
 // Bound (elements, exclusive) on the activation row stride and padded K of
 // the prefill path, which keeps its 32-bit operand offsets in range.

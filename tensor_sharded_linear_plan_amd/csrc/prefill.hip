@@ -24,12 +24,12 @@
 // last step of stage k, issues the copies of stage k + S into the slot of
 // stage k, which no wave reads any more.
 //
-// Operands: bf16 x bf16, or f16 x f16 for 4-bit weights.  For the latter a
-// prep kernel first expands the weights to binary16 fragments (w = s q + b
-// rounded once) and narrows each distinct activation matrix once to
-// binary16 (exact below 65536 in magnitude; items reading the same X share
-// the copy) in the workspace.  bf16 activations are copied, zero-padded,
-// only when K is not a multiple of 64.  Accumulation is binary32.
+// Operands: bf16 x bf16, accumulated in binary32.  bf16 activations are
+// copied, zero-padded, only when K is not a multiple of 64.  4-bit weights
+// run in q4gemm.hip's fused kernel; this file also holds what the two share:
+// the activation pass (which for 4-bit weights writes each distinct
+// activation matrix once as binary16, every row scaled by a power of two),
+// the tile-shape cost model and the launch sequence.
 //
 // One launch serves a group of shard products of the same types, each over
 // its own rows; the item table rides in the kernel arguments.  Each item's tiles take a
@@ -41,18 +41,14 @@
 
 #include <functional>
 #include <queue>
-#include <type_traits>
 #include <vector>
 
 #include "device.hpp"
+#include "gemm_common.hpp"
 #include "internal.hpp"
 
 namespace tsl {
 namespace {
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-enum { OP_BF16 = 0, OP_F16 = 1 };
 
 struct GemmItem {
     const u32x4 *B;    // fragment-packed weights [Nt16][KT32][64] x 16 B (bf16 or f16)
@@ -84,13 +80,11 @@ struct GemmGroup {
     GemmItem it[kGroupMax];
 };
 
-constexpr int kLdsLimit = 160 * 1024;
-
 // Tile geometry.  A stage covers BK k: 64, or 32 when three 64-k stages do
 // not fit in LDS (then four 32-k stages do).  Activation rows are copied in
 // 1 KB LDS blocks of RPB rows (RPB x BK x 2 bytes); weight blocks are 32
 // columns x 16 k.
-template <int OP, int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN>
 struct G {
     static constexpr int TM = BM / WM, TN = BN / WN; // wave tile
     static constexpr int MT = TM / 32, NT = TN / 32; // 32x32 tiles per wave
@@ -110,50 +104,15 @@ struct G {
     static_assert(FPW * (NS - 2) < 64, "vmcnt range");
 };
 
-// XOR swizzle of an activation row's 16-byte chunks in its LDS block, so
-// that the 32 rows of a fragment read spread over all banks.
-template <int CPR>
-__device__ __forceinline__ int swz(int row_in_block) {
-    return CPR == 8 ? (row_in_block & 7) : ((row_in_block >> 2) & 3);
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c, int op) {
-    if (op == OP_BF16)
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-// One wave instruction: lane l copies the 16 bytes at base + off (base
-// wave-uniform, off a per-lane 32-bit byte offset) into LDS at lds + 16 l
-// (lds wave-uniform).  Issued as inline assembly so that the compiler's
-// wait-count tracking does not drain every outstanding copy before each LDS
-// read; completion is awaited explicitly (vmcnt) before the barrier that
-// publishes a stage.
-__device__ __forceinline__ void dma16(const char *base, uint32_t off, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(lds), "v"(off), "s"(base)
-                 : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
-}
-
-// s_waitcnt lgkmcnt(0) leaving the other counters alone.
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14)); }
-
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-template <int OP, int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_kernel(GemmGroup grp) {
-    using C = G<OP, BM, BN, WM, WN>;
+    using C = G<BM, BN, WM, WN>;
     __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // scalar
@@ -303,7 +262,7 @@ gemm_kernel(GemmGroup grp) {
 #pragma unroll
             for (int q = 0; q < C::MT * C::NT; ++q) {
                 const int i = q / C::NT, j = q % C::NT;
-                acc[i][j] = mfma32(af[b][i], bfr[b][j], acc[i][j], OP);
+                acc[i][j] = mfma32(af[b][i], bfr[b][j], acc[i][j]);
                 if (s + 1 == C::S16) {
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -339,149 +298,28 @@ gemm_kernel(GemmGroup grp) {
 #pragma unroll
     for (int j = 0; j < C::NT; ++j)
         colok[j] = col0 + 32 * j < a.Ns;
-    // the store loop, without (bf16 operands) or with (binary16) the
-    // operand scales, each instance compiled for one of the two
-    auto store = [&](auto SCALED) __attribute__((always_inline)) {
-        constexpr bool sc = decltype(SCALED)::value;
-        // Exponents, all loaded before the first store (vmcnt counts stores
-        // too, so a load issued between stores would wait for them): one
-        // per column tile, and per 32-row block one load in which lane l
-        // takes row l of the block (the row exponents are padded to whole
-        // 256-row tiles); each lane then reads its rows, 4 (lane / 32)
-        // apart, from the lanes that hold them.
-        int cexp[C::NT], rblk[C::MT];
-        const bool hi = (lane >> 5) != 0;
-        if constexpr (sc) {
-            const int32_t *ce =
-                reinterpret_cast<const int32_t *>(a.B + (int64_t)a.Nt16 * a.KT32 * 64);
-            const int32_t *re = reinterpret_cast<const int32_t *>(a.X + M * a.ldx);
-            const int64_t rbase = m0 + wm * C::MT * 32;
 #pragma unroll
-            for (int j = 0; j < C::NT; ++j)
-                cexp[j] = colok[j] ? ce[col0 + 32 * j] : 0;
+    for (int i = 0; i < C::MT; ++i)
 #pragma unroll
-            for (int i = 0; i < C::MT; ++i)
-                rblk[i] = re[rbase + i * 32 + (lane & 31)];
-        }
+        for (int r = 0; r < 16; ++r) {
+            const int rr = i * 32 + 8 * (r >> 2) + (r & 3); // row step from row0
+            if (row0 + rr >= M)
+                continue;
+            char *yr = ybase + rr * rstride;
 #pragma unroll
-        for (int i = 0; i < C::MT; ++i) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rr = i * 32 + 8 * (r >> 2) + (r & 3); // row step from row0
-                if (row0 + rr >= M)
+            for (int j = 0; j < C::NT; ++j) {
+                if (!colok[j])
                     continue;
-                char *yr = ybase + rr * rstride;
-                int rexp = 0;
-                if constexpr (sc) {
-                    const int q = 8 * (r >> 2) + (r & 3);
-                    const int lo_e = __builtin_amdgcn_readlane(rblk[i], q);
-                    const int hi_e = __builtin_amdgcn_readlane(rblk[i], q + 4);
-                    rexp = hi ? hi_e : lo_e;
-                }
-#pragma unroll
-                for (int j = 0; j < C::NT; ++j) {
-                    if (!colok[j])
-                        continue;
-                    float v = acc[i][j][r];
-                    // undo the operand scales: one exact power-of-two step
-                    // (rounded only where the result leaves the normal range)
-                    if constexpr (sc)
-                        v = __builtin_amdgcn_ldexpf(v, rexp + cexp[j]);
-                    if (ybf) {
-                        __bf16 h = (__bf16)v;
-                        *reinterpret_cast<uint16_t *>(yr + j * 64) =
-                            __builtin_bit_cast(uint16_t, h);
-                    } else {
-                        float *y = reinterpret_cast<float *>(yr + j * 128);
-                        *y = accu ? *y + v : v;
-                    }
+                const float v = acc[i][j][r];
+                if (ybf) {
+                    __bf16 h = (__bf16)v;
+                    *reinterpret_cast<uint16_t *>(yr + j * 64) = __builtin_bit_cast(uint16_t, h);
+                } else {
+                    float *y = reinterpret_cast<float *>(yr + j * 128);
+                    *y = accu ? *y + v : v;
                 }
             }
         }
-    };
-    // binary16 operands come only from 4-bit weights, which are always
-    // scaled; bf16 operands never are
-    if constexpr (OP == OP_F16)
-        store(std::true_type{});
-    else
-        store(std::false_type{});
-}
-
-// ---- prep: 4-bit weights -> binary16 fragments --------------------------
-// One piece of the weight pass: a product's weights, or one member's share
-// of a joined sum set (written at its k offset).  The members of a joined
-// set are consecutive pieces (pos 0 .. R - 1) and share one column
-// exponent, the largest of theirs; piece 0's first block stores it after
-// the fragments for the GEMM's epilogue.
-struct PrepItem {
-    // packed records (codes, scale/bias pairs) -> fragments; column tile
-    // nt's 32-k fragments start at nt * kt_ld, this piece's at kt_off
-    const char *q4;
-    u32x4 *w_out;        // fragments, then the column exponents [Nt 16] int32
-    const int32_t *fexp; // this member's column exponents (packed array)
-    int64_t w_chunks;    // 16-byte code chunks
-    int32_t KB, Gs;
-    int32_t kt_ld, kt_off;
-    int32_t R, pos;      // members of the set (1: a lone product), this one's place
-    int32_t Ns;
-    int32_t start;
-};
-
-struct PrepGroup {
-    int32_t n, pad_;
-    PrepItem it[kGroupMax];
-};
-
-__global__ void __launch_bounds__(256) prep_kernel(PrepGroup grp) {
-    const int bid = blockIdx.x;
-    int lo = 0, hi = grp.n - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (grp.it[mid].start <= bid)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    const PrepItem &p = grp.it[lo];
-    // one thread per packed 16-byte code chunk (16 columns x 128 k per 64
-    // lanes), writing the four 32-k fragments it covers
-    const int64_t c = (int64_t)(bid - p.start) * blockDim.x + threadIdx.x;
-    if (c >= p.w_chunks)
-        return;
-    const int lane = (int)(c & 63);
-    const int64_t t = c >> 6;
-    const int64_t nt = t / p.KB, blk = t % p.KB;
-    const int64_t n = nt * 16 + (lane & 15);
-    // the column exponent (the set's largest, for a joined set)
-    int f = p.fexp[n];
-    for (int r = 0; r < p.R; ++r) {
-        const int fr = grp.it[lo - p.pos + r].fexp[n];
-        f = fr > f ? fr : f;
-    }
-    if (p.pos == 0 && blk == 0 && lane < 16)
-        reinterpret_cast<int32_t *>(p.w_out + (int64_t)(p.w_chunks / p.KB / 64) * p.kt_ld * 64)[n] =
-            f;
-    const char *rec = p.q4 + t * kQ4Record; // record (nt, blk)
-    const u32x4 w = *reinterpret_cast<const u32x4 *>(rec + lane * 16);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int64_t g = 2 * blk + h;
-        if (g >= p.Gs)
-            break; // pad group of a half-filled last block: never read
-        const uint32_t sbp =
-            *reinterpret_cast<const uint32_t *>(rec + kQ4PairsAt + ((lane & 15) * 2 + h) * 4);
-        // s 2^-f and b 2^-f are exact (bf16 significands) unless they fall
-        // below the binary32 range, far under the column's largest weight
-        const float s = __builtin_amdgcn_ldexpf(bf16_lo(sbp), -f);
-        const float b = __builtin_amdgcn_ldexpf(bf16_hi(sbp), -f);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int tt = 2 * h + q;
-            const f16x8 v = q4_dequant_f16(w[tt], s, b);
-            p.w_out[((nt * (int64_t)p.kt_ld + p.kt_off + blk * 4 + tt) * 64) + lane] =
-                __builtin_bit_cast(u32x4, v);
-        }
-    }
 }
 
 // ---- prep: activation copies ----------------------------------------------
@@ -606,16 +444,18 @@ typedef void (*GemmFn)(GemmGroup);
 struct Variant {
     int bm, bn, wm, wn;
 };
-// tile shapes with a kernel instance
+// tile shapes with a kernel instance: bf16 operands, and the fused 4-bit
+// kernel (its waves always 1 x 4)
 constexpr Variant kVariants[] = {{256, 256, 2, 2}, {256, 160, 4, 1}, {256, 128, 2, 2},
                                  {128, 256, 2, 2}, {128, 128, 2, 2}, {256, 64, 4, 1},
                                  {128, 64, 2, 2},  {64, 64, 2, 2}};
+constexpr Variant kQ4Variants[6] = {{256, 256, 1, 4}, {256, 128, 1, 4}, {128, 256, 1, 4},
+                                    {128, 128, 1, 4}, {64, 256, 1, 4},  {64, 128, 1, 4}};
 
-template <int OP>
 GemmFn pick(const Variant &v) {
 #define TSL_CASE(BM_, BN_, WM_, WN_)                                                               \
     if (v.bm == BM_ && v.bn == BN_ && v.wm == WM_ && v.wn == WN_)                                  \
-        return gemm_kernel<OP, BM_, BN_, WM_, WN_>;
+        return gemm_kernel<BM_, BN_, WM_, WN_>;
     TSL_CASE(256, 256, 2, 2) TSL_CASE(256, 160, 4, 1) TSL_CASE(256, 128, 2, 2)
     TSL_CASE(128, 256, 2, 2) TSL_CASE(128, 128, 2, 2) TSL_CASE(256, 64, 4, 1)
     TSL_CASE(128, 64, 2, 2) TSL_CASE(64, 64, 2, 2)
@@ -694,12 +534,29 @@ double chunk_cost(const Variant &v, double pen, const LinearItem *items, int c0,
 // every launch drains before the next starts) with its k-split factor
 // (1 unless the launch has fewer than kSplitBelow tiles), which *factors
 // receives.
-double variant_cost(const Variant &v, const LinearItem *items, int n, std::vector<int> *factors) {
+double variant_cost(const Variant &v, const LinearItem *items, int n, std::vector<int> *factors,
+                    bool q4) {
     const double TM = v.bm / v.wm, TN = v.bn / v.wn;
     const double flops = 2.0 * v.bm * v.bn; // per k
-    const double lds = 4096.0 * (4.0 * (TM + TN) * 2 + (v.bm + v.bn) * 2) / flops / 128.0;
-    const double l2 = 4096.0 * (v.bm + v.bn) * 2 / flops / 40.0;
-    double pen = lds > l2 ? lds : l2;
+    double pen;
+    if (!q4) {
+        const double lds = 4096.0 * (4.0 * (TM + TN) * 2 + (v.bm + v.bn) * 2) / flops / 128.0;
+        const double l2 = 4096.0 * (v.bm + v.bn) * 2 / flops / 40.0;
+        pen = lds > l2 ? lds : l2;
+    } else {
+        // the fused 4-bit kernel (1 x 4 waves): LDS reads of binary16
+        // activations by all four waves and of code words, copies of
+        // activations and records; L2 delivery of both
+        const double lds = 4096.0 * (4.0 * v.bm * 2 + v.bn * 0.5 + v.bm * 2 + v.bn * 0.5625) /
+                           flops / 128.0;
+        const double l2 = 4096.0 * (v.bm * 2 + v.bn * 0.5625) / flops / 40.0;
+        pen = lds > l2 ? lds : l2;
+        pen = pen > 1.0 ? pen : 1.0;
+        // plus the issue cycles every 16-k step costs a wave besides its
+        // MFMAs (reads, expansion, copies, waits: ~120), against the step's
+        // MT NT MFMAs of 32 clocks
+        pen += 120.0 / ((v.bm / 32) * (v.bn / 4 / 32) * 32.0);
+    }
     pen = pen > 1.0 ? pen : 1.0;
     double total = 0.0;
     factors->clear();
@@ -725,8 +582,13 @@ PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64
     PrefillPlan best;
     double best_cost = 1e300;
     std::vector<int> factors, best_factors;
-    for (const Variant &v : kVariants) {
-        const double cost = variant_cost(v, items, n, &factors);
+    const bool q4 = wdtype == TSL_Q4G64;
+    const Variant *vs = q4 ? kQ4Variants : kVariants;
+    const int nv = q4 ? (int)(sizeof(kQ4Variants) / sizeof(Variant))
+                      : (int)(sizeof(kVariants) / sizeof(Variant));
+    for (int vi = 0; vi < nv; ++vi) {
+        const Variant &v = vs[vi];
+        const double cost = variant_cost(v, items, n, &factors, q4);
         if (cost < best_cost - 1e-9) {
             best_cost = cost;
             best.bm = v.bm;
@@ -736,12 +598,10 @@ PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64
             best_factors = factors;
         }
     }
-    // workspace: binary16 weight fragments of 4-bit items with their column
-    // exponents; activation copies (binary16 for 4-bit items, with their row
-    // exponents; zero-padded bf16 for ragged-K bf16 items), one per distinct
-    // (X, ldx, K, rows) -- items without a known X (sizing, joined sets)
-    // never share
-    best.w_off.assign(n, 0);
+    // workspace: activation copies (binary16 for 4-bit items, with their
+    // row exponents; zero-padded bf16 for ragged-K bf16 items), one per
+    // distinct (X, ldx, K, rows) -- items without a known X (sizing, joined
+    // sets) never share; the 4-bit weights are read from their records
     best.x_off.assign(n, 0);
     best.x_first.assign(n, -1);
     size_t off = 0;
@@ -753,8 +613,6 @@ PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64
     for (int i = 0; i < n; ++i) {
         const PackGeom &g = items[i].g;
         const bool q4 = wdtype == TSL_Q4G64;
-        if (q4) // binary16 fragments, then the column exponents
-            best.w_off[i] = take((size_t)g.Nt * (size_t)g.KT * 4 * 1024 + (size_t)g.Nt * 16 * 4);
         if (q4 || g.Ks % 64 != 0) {
             int first = i;
             for (int j = 0; j < i && items[i].X; ++j)
@@ -790,119 +648,79 @@ PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64
     return best;
 }
 
-// Byte offset of the column exponents in a 4-bit shard packed as Nt column
-// tiles of KT 128-k records (the records, rounded up to 256 bytes).
-inline size_t q4_exp_off(int64_t Nt, int64_t KT) {
-    return ((size_t)Nt * (size_t)KT * kQ4Record + 255) / 256 * 256;
+// The activation pass of items [c0, c1): a job per distinct X (a joined
+// set's job has a piece per member), launched in groups of whole jobs.
+hipError_t launch_xprep(const PrefillPlan &p, const LinearItem *items, int c0, int c1, bool q4,
+                        char *ws, hipStream_t stream) {
+    std::vector<XPiece> xp;
+    for (int i = c0; i < c1; ++i) {
+        const LinearItem &L = items[i];
+        if (p.x_first[i] != i)
+            continue;
+        const PackGeom &g = L.g;
+        const int R = L.cat;
+        const int64_t kseg = g.Ks / R;
+        for (int r = 0; r < R; ++r) {
+            XPiece x{};
+            x.x_in = static_cast<const uint16_t *>(R > 1 ? L.seg_X[r] : L.X);
+            x.ldx_in = R > 1 ? L.seg_ldx[r] : L.ldx;
+            x.x_out = reinterpret_cast<uint16_t *>(ws + p.x_off[i]) + r * kseg;
+            // row exponents right after the copy's M rows
+            x.rexp = q4 ? reinterpret_cast<int32_t *>(reinterpret_cast<uint16_t *>(ws + p.x_off[i]) +
+                                                      L.M * kpad64(g.Ks))
+                        : nullptr;
+            x.x_ld = (int32_t)kpad64(g.Ks);
+            x.Ks = (int32_t)kseg;
+            x.Kw = (int32_t)(R > 1 ? kseg : kpad64(g.Ks));
+            x.R = R;
+            x.pos = r;
+            x.M = (int32_t)L.M;
+            xp.push_back(x);
+        }
+    }
+    for (size_t q0 = 0; q0 < xp.size();) {
+        XPrepGroup xg{};
+        int64_t blocks = 0;
+        size_t q = q0;
+        while (q < xp.size() && q - q0 + xp[q].R <= (size_t)kGroupMax) {
+            for (int r = 0; r < xp[q].R; ++r) {
+                XPiece &x = xg.it[xg.n++];
+                x = xp[q + r];
+                x.start = (int32_t)blocks;
+            }
+            blocks += xp[q].M;
+            q += xp[q].R;
+        }
+        if (blocks > 0) {
+            hipLaunchKernelGGL(xprep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, xg);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+        q0 = q;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, tsl_dtype wdtype,
                           int64_t M, void *workspace, hipStream_t stream) {
-    const Variant v{p.bm, p.bn, p.wm, p.wn};
-    const bool q4 = wdtype == TSL_Q4G64;
-    GemmFn fn = q4 ? pick<OP_F16>(v) : pick<OP_BF16>(v);
+    (void)M;
+    char *ws = static_cast<char *>(workspace);
+    if (wdtype == TSL_Q4G64) {
+        // the activation pass for every item, then the fused 4-bit GEMM
+        hipError_t e = launch_xprep(p, items, 0, n, true, ws, stream);
+        return e != hipSuccess ? e : launch_q4_gemm(p, items, n, ws, stream);
+    }
+    GemmFn fn = pick(Variant{p.bm, p.bn, p.wm, p.wn});
     if (!fn)
         return hipErrorInvalidValue;
-    char *ws = static_cast<char *>(workspace);
     for (int c0 = 0; c0 < n; c0 += kGroupMax) {
         const int cn = n - c0 < kGroupMax ? n - c0 : kGroupMax;
-        // 1. activation copies, one job per distinct X (a joined set's job
-        // has a piece per member), launched in groups of whole jobs
-        std::vector<XPiece> xp;
-        std::vector<int> xjob_rows;
-        for (int i = 0; i < cn; ++i) {
-            const LinearItem &L = items[c0 + i];
-            if (p.x_first[c0 + i] != c0 + i)
-                continue;
-            const PackGeom &g = L.g;
-            const int R = L.cat;
-            const int64_t kseg = g.Ks / R;
-            for (int r = 0; r < R; ++r) {
-                XPiece x{};
-                x.x_in = static_cast<const uint16_t *>(R > 1 ? L.seg_X[r] : L.X);
-                x.ldx_in = R > 1 ? L.seg_ldx[r] : L.ldx;
-                x.x_out = reinterpret_cast<uint16_t *>(ws + p.x_off[c0 + i]) + r * kseg;
-                // row exponents right after the copy's M rows
-                x.rexp = q4 ? reinterpret_cast<int32_t *>(reinterpret_cast<uint16_t *>(
-                                                               ws + p.x_off[c0 + i]) +
-                                                           L.M * kpad64(g.Ks))
-                            : nullptr;
-                x.x_ld = (int32_t)kpad64(g.Ks);
-                x.Ks = (int32_t)kseg;
-                x.Kw = (int32_t)(R > 1 ? kseg : kpad64(g.Ks));
-                x.R = R;
-                x.pos = r;
-                x.M = (int32_t)L.M;
-                xp.push_back(x);
-            }
-        }
-        for (size_t q0 = 0; q0 < xp.size();) {
-            XPrepGroup xg{};
-            int64_t blocks = 0;
-            size_t q = q0;
-            while (q < xp.size() && q - q0 + xp[q].R <= (size_t)kGroupMax) {
-                for (int r = 0; r < xp[q].R; ++r) {
-                    XPiece &x = xg.it[xg.n++];
-                    x = xp[q + r];
-                    x.start = (int32_t)blocks;
-                }
-                blocks += xp[q].M;
-                q += xp[q].R;
-            }
-            if (blocks > 0) {
-                hipLaunchKernelGGL(xprep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, xg);
-                hipError_t e = hipGetLastError();
-                if (e != hipSuccess)
-                    return e;
-            }
-            q0 = q;
-        }
-        // 2. 4-bit weights -> binary16 fragments, a piece per member, in
-        // groups of whole sets
-        std::vector<PrepItem> pieces;
-        for (int i = 0; q4 && i < cn; ++i) {
-            const LinearItem &L = items[c0 + i];
-            const PackGeom &g = L.g;
-            const int R = L.cat;
-            const int64_t kseg = g.Ks / R, kbseg = g.KT / R; // per member
-            for (int r = 0; r < R; ++r) {
-                PrepItem a{};
-                a.q4 = static_cast<const char *>(R > 1 ? L.seg_packed[r] : L.packed);
-                a.w_out = reinterpret_cast<u32x4 *>(ws + p.w_off[c0 + i]);
-                a.fexp = reinterpret_cast<const int32_t *>(a.q4 + q4_exp_off(g.Nt, kbseg));
-                a.kt_ld = (int32_t)(g.KT * 4);
-                a.kt_off = (int32_t)(r * kbseg * 4);
-                a.w_chunks = g.Nt * kbseg * 64;
-                a.KB = (int32_t)kbseg;
-                a.Gs = (int32_t)(kseg / 64);
-                a.R = R;
-                a.pos = r;
-                a.Ns = (int32_t)g.Ns;
-                pieces.push_back(a);
-            }
-        }
-        for (size_t q0 = 0; q0 < pieces.size();) {
-            PrepGroup pg{};
-            int64_t pblocks = 0;
-            size_t q = q0;
-            while (q < pieces.size() && q - q0 + pieces[q].R <= (size_t)kGroupMax) {
-                for (int r = 0; r < pieces[q].R; ++r) {
-                    PrepItem &a = pg.it[pg.n++];
-                    a = pieces[q + r];
-                    a.start = (int32_t)pblocks;
-                    pblocks += (a.w_chunks + 255) / 256;
-                }
-                q += pieces[q].R;
-            }
-            if (pblocks > 0) {
-                hipLaunchKernelGGL(prep_kernel, dim3((unsigned)pblocks), dim3(256), 0, stream, pg);
-                hipError_t e = hipGetLastError();
-                if (e != hipSuccess)
-                    return e;
-            }
-            q0 = q;
-        }
-        // 3. the GEMM over every item's tiles
+        // 1. zero-padded copies of ragged-K activations
+        hipError_t e = launch_xprep(p, items, c0, c0 + cn, false, ws, stream);
+        if (e != hipSuccess)
+            return e;
+        // 2. the GEMM over every item's tiles
         GemmGroup grp{};
         grp.M = M;
         grp.n = cn;
@@ -912,8 +730,7 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
             const PackGeom &g = L.g;
             GemmItem &a = grp.it[i];
             const bool copied = p.x_first[c0 + i] >= 0;
-            a.B = static_cast<const u32x4 *>(q4 ? static_cast<const void *>(ws + p.w_off[c0 + i])
-                                                : L.packed);
+            a.B = static_cast<const u32x4 *>(L.packed);
             a.X = copied ? reinterpret_cast<const uint16_t *>(ws + p.x_off[c0 + i])
                          : static_cast<const uint16_t *>(L.X);
             a.ldx = copied ? kpad64(g.Ks) : L.ldx;
@@ -921,7 +738,7 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
             a.ldy = L.ldy;
             a.Ns = (int32_t)g.Ns;
             a.Nt16 = (int32_t)g.Nt;
-            a.KT32 = (int32_t)(q4 ? g.KT * 4 : g.KT);
+            a.KT32 = (int32_t)g.KT;
             a.KT64 = (int32_t)(kpad64(g.Ks) / 64);
             a.M = L.M;
             a.MB = (int32_t)((L.M + p.bm - 1) / p.bm);
@@ -935,7 +752,7 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
             blocks += 8 * (int64_t)a.T8;
         }
         hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, stream, grp);
-        hipError_t e = hipGetLastError();
+        e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }

@@ -276,13 +276,14 @@ def test_group_rejections_and_workspace(tsl_lib):
         return dict(dict(shard=s, packed=P, packed_bytes=nb, X=X, ldx=1024, Y=Y, ldy=256), **kw)
 
     good = [item(sh[0], P0, Y0), item(sh[1], P1, Y1)]
-    # the group's workspace is the sum of its items' (4-bit prefill: binary16
-    # weights and their column exponents, a binary16 copy of the activations
-    # and its row exponents -- a size query sees no X pointers, so it never
-    # counts a copy as shared -- and, the launch being far too small to fill
-    # the chip, the binary32 partials of two k-splits of 8 stages each)
+    # the group's workspace is the sum of its items' (4-bit prefill: a
+    # binary16 copy of the activations and its row exponents, padded to whole
+    # 256-row tiles -- a size query sees no X pointers, so it never counts a
+    # copy as shared -- and, the launch being far too small to fill the chip,
+    # the binary32 partials of two k-splits of 8 stages each; the weights are
+    # read from their 4-bit records)
     w = [tsl_lib.shard_linear_workspace_size(s, tsl_lib.Q4G64, M) for s in sh]
-    assert w[0] == 1024 * 256 * 2 + 256 * 4 + M * 1024 * 2 + M * 4 + 2 * M * 256 * 4
+    assert w[0] == M * 1024 * 2 + M * 4 + 2 * M * 256 * 4
     assert tsl_lib.shard_linear_group_workspace_size(good, tsl_lib.Q4G64, M) == sum(w)
     assert tsl_lib.shard_linear_group_workspace_size(good[:1], tsl_lib.Q4G64, 4) == \
         tsl_lib.shard_linear_workspace_size(sh[0], tsl_lib.Q4G64, 4)
@@ -301,7 +302,7 @@ def test_group_rejections_and_workspace(tsl_lib):
              ([item(sh[0], P0, Y0, ldx=1 << 22)], {}, tsl_lib.ERR_UNSUPPORTED),
              (good, dict(xdtype=tsl_lib.F32), tsl_lib.ERR_UNSUPPORTED),
              (good, dict(M=-1), tsl_lib.ERR_INVALID_ARG),
-             (good, {}, tsl_lib.ERR_BUFFER_TOO_SMALL),  # no workspace for the binary16 weights
+             (good, {}, tsl_lib.ERR_BUFFER_TOO_SMALL),  # no workspace for the activation copy
              ([], {}, tsl_lib.ERR_INVALID_ARG)]
     for items, kw, status in cases:
         with pytest.raises(tsl_lib.TslError) as e:
