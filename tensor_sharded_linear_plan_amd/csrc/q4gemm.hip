@@ -12,15 +12,17 @@
 // scaled by a power of two), copied global -> LDS in 32-k stages as in the
 // bf16 GEMM.
 //
-// Waves are laid out 1 x 4: wave w owns every row of the block tile and
-// columns [w BN/4, (w+1) BN/4), so every weight of the tile is expanded by
-// exactly one wave, once.  A wave's 32x32x16 f16 MFMA B fragment is one
-// 32-bit code word per lane (8 consecutive k of the lane's column); the
-// expansion is, per pair of codes, one v_and_or_b32 (and a shift), one
-// v_pk_add_f16 and one v_pk_fma_f16 -- 1024 + q becomes q exactly, then
-// q s' + b' rounds once to binary16, where s' = s 2^-f and b' = b 2^-f are
-// the group's scale and bias scaled by the column exponent f (exact unless
-// they fall out of binary16 range, far below the column's largest weight).
+// Waves are laid out WM x 4 (WM = 2 for 256 x 256 tiles, two waves per
+// SIMD; else 1): wave (wm, wn) owns rows [wm BM/WM, (wm+1) BM/WM) and
+// columns [wn BN/4, (wn+1) BN/4) of the block tile, so each weight is
+// expanded by WM waves (once per row half).  A wave's 32x32x16 f16 MFMA B
+// fragment is one 32-bit code word per lane (8 consecutive k of the lane's
+// column); the expansion is, per pair of codes, one v_and_or_b32 (plus one
+// shift per two pairs), one v_pk_add_f16 and one v_pk_fma_f16 -- 1024 + q
+// (or 64 + q) becomes q exactly, then q s' + b' rounds once to binary16,
+// where s' = s 2^-f and b' = b 2^-f are the group's scale and bias scaled by
+// the column exponent f (exact unless they fall out of binary16 range, far
+// below the column's largest weight).
 //
 // Pipeline: NS activation stages of 32 k and three record slots of 128 k
 // rotate through LDS; the copies of a record block travel in the same batch
@@ -71,23 +73,26 @@ struct Q4Group {
     const char *segw[kMaxJoined][kSetParts];
 };
 
-template <int BM, int BN>
+// Block tile BM x BN, waves WM x 4 (WM per SIMD): wave (wm, wn) owns rows
+// [wm BM/WM, (wm+1) BM/WM) and columns [wn BN/4, (wn+1) BN/4).
+template <int BM, int BN, int WM>
 struct Q4G {
-    static constexpr int TN = BN / 4;                // columns per wave
-    static constexpr int MT = BM / 32, NT = TN / 32; // 32x32 tiles per wave
+    static constexpr int NW = 4 * WM;                // waves
+    static constexpr int TM = BM / WM, TN = BN / 4;  // wave tile
+    static constexpr int MT = TM / 32, NT = TN / 32; // 32x32 tiles per wave
     static constexpr int ASLOT = BM * 64;            // a 32-k stage: BM rows x 64 bytes
     static constexpr int AF = BM / 16;               // its 1 KB blocks (16 rows each)
-    static constexpr int ACW = AF / 4;               // activation copies per wave per stage
+    static constexpr int ACW = AF / NW;              // activation copies per wave per stage
     static constexpr int NR = BN / 16;               // records per 128-k block
     static constexpr int BSLOT = NR * kQ4Record;     // codes [NR][1 KB], then pairs [NR][128 B]
-    static constexpr int CCW = NR / 4;               // code copies (1 KB) per wave per block
-    static constexpr int PCW = NR / 8;               // pair copies (256 B, two records) per wave
+    static constexpr int CCW = NR / NW;              // code copies (1 KB) per wave per block
+    static constexpr int PCW = NR / 2 / NW;          // pair copies (256 B, two records) per wave
     static constexpr int BCW = CCW + PCW;
     static constexpr int NBS = 3;                    // record slots
     static constexpr int NSA = (kLdsLimit - NBS * BSLOT) / ASLOT;
     static constexpr int NS = NSA > 8 ? 8 : NSA;     // activation slots
     static_assert(MT >= 2 && NT >= 1 && TN % 32 == 0, "whole 32x32 tiles, two or more per step");
-    static_assert(AF % 4 == 0 && NR % 8 == 0, "copies divide over 4 waves");
+    static_assert(AF % NW == 0 && NR % (2 * NW) == 0, "copies divide over the waves");
     static_assert(NS >= 4, "activation stages in flight");
     static_assert((NS - 2) * ACW + 2 * BCW < 64, "vmcnt range");
 };
@@ -104,14 +109,15 @@ __device__ __forceinline__ void q4_pair(uint32_t sb, int f, uint32_t &ss, uint32
     bb = (u >> 16) * 0x10001u;
 }
 
-template <int BM, int BN>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN, int WM>
+__global__ void __launch_bounds__(256 * WM) __attribute__((amdgpu_waves_per_eu(WM, WM)))
 q4_gemm_kernel(Q4Group grp) {
-    using C = Q4G<BM, BN>;
+    using C = Q4G<BM, BN, WM>;
     __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::ASLOT + C::NBS * C::BSLOT];
     __shared__ const char *mtab[kSetParts];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // scalar
+    const int wm = wave >> 2, wn = wave & 3;
 
     const int bid = blockIdx.x;
     int lo = 0, hi = grp.n - 1; // last item whose first workgroup is <= bid
@@ -144,13 +150,13 @@ q4_gemm_kernel(Q4Group grp) {
     const int nst = (4 * blk1 < a.nst ? 4 * blk1 : a.nst) - st0;
 
     // ---- activation copies (as the bf16 GEMM's, 32-k stages) ----
-    // block f = wave + 4 j of a stage holds rows 16 f .. 16 f + 15; rows past
+    // block f = wave + NW j of a stage holds rows 16 f .. 16 f + 15; rows past
     // M read the last valid row (never stored)
     const char *xbase = reinterpret_cast<const char *>(a.X + m0 * a.ldx);
     const int arow = lane >> 2;
     const uint32_t chunk = 8 * ((lane & 3) ^ swz<4>(arow));
     const uint32_t aoff0 = ((uint32_t)(16 * wave + arow) * (uint32_t)a.ldx + chunk) * 2;
-    const uint32_t astep = 64 * (uint32_t)a.ldx * 2;
+    const uint32_t astep = 16 * C::NW * (uint32_t)a.ldx * 2;
     const int64_t last_row = M - 1 - m0 < BM - 1 ? M - 1 - m0 : BM - 1;
     const uint32_t alim = ((uint32_t)last_row * (uint32_t)a.ldx + chunk) * 2;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(void __attribute__((address_space(3))) *)lds;
@@ -161,7 +167,7 @@ q4_gemm_kernel(Q4Group grp) {
         asm volatile("" : "+v"(o)); // recomputed per issue, not held
         o += (uint32_t)j * astep;
         dma16(xbase + (int64_t)(st0 + kt) * 64, o < alim ? o : alim,
-              lds0 + aslot * C::ASLOT + (wave + 4 * j) * 1024);
+              lds0 + aslot * C::ASLOT + (wave + C::NW * j) * 1024);
     };
 
     // ---- record copies: block b of the split (global block blk0 + b) ----
@@ -184,17 +190,17 @@ q4_gemm_kernel(Q4Group grp) {
         return mtab[r];
     };
     // copy c < BCW of this wave for a block into record slot bslot: the
-    // first CCW copy the codes (1 KB) of records wave + 4 c, the others the
-    // (scale, bias) pairs of records 2 p, 2 p + 1 with p = wave + 4 (c - CCW)
+    // first CCW copy the codes (1 KB) of records wave + NW c, the others the
+    // (scale, bias) pairs of records 2 p, 2 p + 1 with p = wave + NW (c - CCW)
     auto copy_b = [&](const char *base, int lb, int bslot, int c) __attribute__((always_inline)) {
         const uint32_t dst = ldsb + bslot * C::BSLOT;
         if (c < C::CCW) {
-            const int rr = wave + 4 * c;
+            const int rr = wave + C::NW * c;
             const int nt = t0 + rr < tmax ? t0 + rr : tmax;
             const uint32_t off = (uint32_t)((nt * KBm + lb) * kQ4Record) + 16 * (uint32_t)lane;
             dma16_at(base + off, dst + rr * 1024);
         } else {
-            const int p = wave + 4 * (c - C::CCW);
+            const int p = wave + C::NW * (c - C::CCW);
             const int rr = 2 * p + (lane >> 5);
             const int nt = t0 + rr < tmax ? t0 + rr : tmax;
             const uint32_t off = (uint32_t)((nt * KBm + lb) * kQ4Record) + kQ4PairsAt +
@@ -239,7 +245,7 @@ q4_gemm_kernel(Q4Group grp) {
         const size_t eoff = ((size_t)a.Nt16 * a.KBm * kQ4Record + 255) / 256 * 256;
 #pragma unroll
         for (int j = 0; j < C::NT; ++j) {
-            int64_t n = n0 + C::TN * wave + 32 * j + (lane & 31);
+            int64_t n = n0 + C::TN * wn + 32 * j + (lane & 31);
             n = n < (int64_t)a.Nt16 * 16 ? n : (int64_t)a.Nt16 * 16 - 1;
             int f = -1000;
             for (int r = 0; r < a.R; ++r) {
@@ -266,10 +272,15 @@ q4_gemm_kernel(Q4Group grp) {
     u32x4 af[2][C::MT], bfr[2][C::NT];
     uint32_t braw[C::NT], praw[C::NT], ss[C::NT], bb[C::NT];
     // the constants of the expansion, held opaquely so that each code pair
-    // takes one v_and_or_b32 (gfx9 VOP3 encodings take no literal)
-    uint32_t cmask, cbias;
+    // takes one v_and_or_b32 (gfx9 VOP3 encodings take no literal): nibble
+    // pairs 0 and 2 of a word land on binary16 1024 + q (0x6400 | q), pairs
+    // 1 and 3 on 64 + q (0x5400 | q << 4, the mantissa's unit there being
+    // 1/16), so only pairs 2 and 3 need a shift, one for both
+    uint32_t cmask, cmask4, cbias, cbias4;
     asm("v_mov_b32 %0, 0x000f000f" : "=v"(cmask));
+    asm("v_mov_b32 %0, 0x00f000f0" : "=v"(cmask4));
     asm("s_mov_b32 %0, 0x64006400" : "=s"(cbias));
+    asm("s_mov_b32 %0, 0x54005400" : "=s"(cbias4));
     // LDS reads for step g from activation slot aslot and record slot
     // bslot: code words first, then the columns' scale/bias pairs of the
     // step's 64-k group (read every step, the same pair for the group's four
@@ -279,13 +290,14 @@ q4_gemm_kernel(Q4Group grp) {
     // the compiler does not hoist one address per unrolled step out of the
     // loop and run out of registers)
     const int rl = (lane & 31) >> 4;
-    const uint32_t bw_lane = ((C::TN / 16) * wave + rl) * 1024 + ((lane >> 5) * 16 + (lane & 15)) * 16;
-    const uint32_t bp_lane = C::NR * 1024 + ((C::TN / 16) * wave + rl) * 128 + (lane & 15) * 8;
+    const uint32_t bw_lane = ((C::TN / 16) * wn + rl) * 1024 + ((lane >> 5) * 16 + (lane & 15)) * 16;
+    const uint32_t bp_lane = C::NR * 1024 + ((C::TN / 16) * wn + rl) * 128 + (lane & 15) * 8;
     const int rb = lane & 15;
     uint32_t a_lane[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
-        a_lane[s2] = ((lane & 31) >> 4) * 1024 + rb * 64 + (((2 * s2 + (lane >> 5)) ^ swz<4>(rb)) * 16);
+        a_lane[s2] = (wm * C::MT * 2 + ((lane & 31) >> 4)) * 1024 + rb * 64 +
+                     (((2 * s2 + (lane >> 5)) ^ swz<4>(rb)) * 16);
     auto read = [&](int g, int aslot, int bslot, u32x4 (&x)[C::MT]) __attribute__((always_inline)) {
         const int bs = g & 7; // step within the block
         uint32_t bw = bw_lane, bp = bp_lane, al = a_lane[g & 1];
@@ -304,11 +316,11 @@ q4_gemm_kernel(Q4Group grp) {
             x[i] = *reinterpret_cast<const u32x4 *>(As + al + i * 2048);
     };
     // part c of step g's expansion: c == 0 converts the group's scale/bias
-    // pairs (when step g opens a group), c = 1 + 4 j + p expands code pair p
-    // of column tile j; each result is pinned where it is computed
-    // (otherwise the compiler sinks the expansion to its first use, behind
-    // the MFMAs)
-    constexpr int NC = 1 + 4 * C::NT;
+    // pairs (when step g opens a group), c = 1 + 2 j + h expands code pairs
+    // 2 h and 2 h + 1 of column tile j, interleaved; each result is pinned
+    // where it is computed (otherwise the compiler sinks the expansion to
+    // its first use, behind the MFMAs)
+    constexpr int NC = 1 + 2 * C::NT;
     auto expand = [&](int g, int c, u32x4 (&y)[C::NT]) __attribute__((always_inline)) {
         typedef _Float16 h2 __attribute__((ext_vector_type(2)));
         if (c == 0) {
@@ -320,15 +332,18 @@ q4_gemm_kernel(Q4Group grp) {
                 }
             }
         } else {
-            const int j = (c - 1) >> 2, p = (c - 1) & 3;
-            const uint32_t v = ((braw[j] >> (4 * p)) & cmask) | cbias;
-            const h2 off = {(_Float16)-1024.f, (_Float16)-1024.f};
-            const h2 q = __builtin_bit_cast(h2, v) + off;
-            uint32_t e = __builtin_bit_cast(
-                uint32_t, __builtin_elementwise_fma(q, __builtin_bit_cast(h2, ss[j]),
-                                                    __builtin_bit_cast(h2, bb[j])));
-            asm volatile("" : "+v"(e));
-            y[j][p] = e;
+            const int j = (c - 1) >> 1, h = (c - 1) & 1;
+            const uint32_t w = h ? braw[j] >> 8 : braw[j];
+            const uint32_t v0 = (w & cmask) | cbias, v1 = (w & cmask4) | cbias4;
+            const h2 o0 = {(_Float16)-1024.f, (_Float16)-1024.f};
+            const h2 o1 = {(_Float16)-64.f, (_Float16)-64.f};
+            const h2 q0 = __builtin_bit_cast(h2, v0) + o0, q1 = __builtin_bit_cast(h2, v1) + o1;
+            const h2 s2 = __builtin_bit_cast(h2, ss[j]), b2 = __builtin_bit_cast(h2, bb[j]);
+            uint32_t e0 = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q0, s2, b2));
+            uint32_t e1 = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q1, s2, b2));
+            asm volatile("" : "+v"(e0), "+v"(e1));
+            y[j][2 * h] = e0;
+            y[j][2 * h + 1] = e1;
         }
     };
 
@@ -459,8 +474,8 @@ q4_gemm_kernel(Q4Group grp) {
     }
 
     // ---- epilogue: acc reg r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32 ----
-    const int64_t row0 = m0 + 4 * (lane >> 5);
-    const int64_t col0 = n0 + C::TN * wave + (lane & 31);
+    const int64_t row0 = m0 + wm * C::TM + 4 * (lane >> 5);
+    const int64_t col0 = n0 + C::TN * wn + (lane & 31);
     const bool part = a.ks > 1;
     const bool ybf = part ? false : (a.flags & kQ4YBf16) != 0;
     const bool accu = part ? false : (a.flags & kQ4Accumulate) != 0;
@@ -483,7 +498,7 @@ q4_gemm_kernel(Q4Group grp) {
         const int32_t *re = reinterpret_cast<const int32_t *>(a.X + M * a.ldx);
 #pragma unroll
         for (int i = 0; i < C::MT; ++i)
-            rblk[i] = re[m0 + i * 32 + (lane & 31)];
+            rblk[i] = re[m0 + wm * C::TM + i * 32 + (lane & 31)];
     }
     const bool hi_half = (lane >> 5) != 0;
 #pragma unroll
@@ -519,12 +534,17 @@ q4_gemm_kernel(Q4Group grp) {
 
 typedef void (*Q4Fn)(Q4Group);
 
-Q4Fn pick_q4(int bm, int bn) {
-#define TSL_Q4(BM_, BN_)                                                                           \
-    if (bm == BM_ && bn == BN_)                                                                    \
-        return q4_gemm_kernel<BM_, BN_>;
-    TSL_Q4(256, 256) TSL_Q4(256, 128) TSL_Q4(128, 256) TSL_Q4(128, 128) TSL_Q4(64, 256)
-    TSL_Q4(64, 128)
+// the kernel of a tile shape and its workgroup size: 256 x 256 tiles run
+// eight waves (two per SIMD, so that one covers the other's stalls), the
+// others four
+Q4Fn pick_q4(int bm, int bn, int *threads) {
+#define TSL_Q4(BM_, BN_, WM_)                                                                      \
+    if (bm == BM_ && bn == BN_) {                                                                  \
+        *threads = 256 * WM_;                                                                      \
+        return q4_gemm_kernel<BM_, BN_, WM_>;                                                      \
+    }
+    TSL_Q4(256, 256, 2) TSL_Q4(256, 128, 1) TSL_Q4(128, 256, 1) TSL_Q4(128, 128, 1)
+    TSL_Q4(64, 256, 1) TSL_Q4(64, 128, 1)
 #undef TSL_Q4
     return nullptr;
 }
@@ -533,7 +553,8 @@ Q4Fn pick_q4(int bm, int bn) {
 
 hipError_t launch_q4_gemm(const PrefillPlan &p, const LinearItem *items, int n, const char *ws,
                           hipStream_t stream) {
-    Q4Fn fn = pick_q4(p.bm, p.bn);
+    int threads = 0;
+    Q4Fn fn = pick_q4(p.bm, p.bn, &threads);
     if (!fn)
         return hipErrorInvalidValue;
     for (int c0 = 0; c0 < n;) {
@@ -574,7 +595,7 @@ hipError_t launch_q4_gemm(const PrefillPlan &p, const LinearItem *items, int n, 
             a.flags = (L.ydtype == TSL_BF16 ? kQ4YBf16 : 0) | (L.accumulate ? kQ4Accumulate : 0);
             blocks += 8 * (int64_t)a.T8;
         }
-        hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, stream, grp);
+        hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), 0, stream, grp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
