@@ -270,7 +270,10 @@ q4_gemm_kernel(Q4Group grp) {
     // from LDS and expanded in registers.  Step g of the split is in stage
     // g / 2 and record block g / 8.
     u32x4 af[2][C::MT], bfr[2][C::NT];
-    uint32_t braw[C::NT], praw[C::NT], ss[C::NT], bb[C::NT];
+    // bq[h][j]: column tile j's code words for the block's steps of parity
+    // h (word t serves step 2 t + h), read once per block
+    u32x4 bq[2][C::NT];
+    uint32_t praw[C::NT], ss[C::NT], bb[C::NT];
     // the constants of the expansion, held opaquely so that each code pair
     // takes one v_and_or_b32 (gfx9 VOP3 encodings take no literal): nibble
     // pairs 0 and 2 of a word land on binary16 1024 + q (0x6400 | q), pairs
@@ -281,14 +284,16 @@ q4_gemm_kernel(Q4Group grp) {
     asm("v_mov_b32 %0, 0x00f000f0" : "=v"(cmask4));
     asm("s_mov_b32 %0, 0x64006400" : "=s"(cbias));
     asm("s_mov_b32 %0, 0x54005400" : "=s"(cbias4));
-    // LDS reads for step g from activation slot aslot and record slot
-    // bslot: code words first, then the columns' scale/bias pairs of the
-    // step's 64-k group (read every step, the same pair for the group's four
-    // steps, so that the reads in flight and their waits do not depend on
-    // the step), then the activation fragments
-    // lane parts of the read addresses (re-made opaque at each use, so that
-    // the compiler does not hoist one address per unrolled step out of the
-    // loop and run out of registers)
+    // LDS reads for the step at position pos (0..7) of its record block,
+    // from activation slot aslot and record slot bslot: at positions 0 and 1
+    // the code words of the block's even / odd steps (one 16-byte read per
+    // column tile: lanes 16 bytes apart, no bank conflicts), then the
+    // columns' scale/bias pairs of the step's 64-k group (read every step,
+    // the same pair for the group's four steps, so that the reads in flight
+    // and their waits depend on the position only), then the activation
+    // fragments.  Lane parts of the read addresses are re-made opaque at
+    // each use, so that the compiler does not hoist one address per unrolled
+    // step out of the loop and run out of registers.
     const int rl = (lane & 31) >> 4;
     const uint32_t bw_lane = ((C::TN / 16) * wn + rl) * 1024 + ((lane >> 5) * 16 + (lane & 15)) * 16;
     const uint32_t bp_lane = C::NR * 1024 + ((C::TN / 16) * wn + rl) * 128 + (lane & 15) * 8;
@@ -298,33 +303,40 @@ q4_gemm_kernel(Q4Group grp) {
     for (int s2 = 0; s2 < 2; ++s2)
         a_lane[s2] = (wm * C::MT * 2 + ((lane & 31) >> 4)) * 1024 + rb * 64 +
                      (((2 * s2 + (lane >> 5)) ^ swz<4>(rb)) * 16);
-    auto read = [&](int g, int aslot, int bslot, u32x4 (&x)[C::MT]) __attribute__((always_inline)) {
-        const int bs = g & 7; // step within the block
-        uint32_t bw = bw_lane, bp = bp_lane, al = a_lane[g & 1];
+    auto read = [&](int pos, int aslot, int bslot, u32x4 (&x)[C::MT]) __attribute__((always_inline)) {
+        uint32_t bw = bw_lane, bp = bp_lane, al = a_lane[pos & 1];
         asm volatile("" : "+v"(bw), "+v"(bp), "+v"(al));
         const char *Bs = lds + C::NS * C::ASLOT + bslot * C::BSLOT;
+        if (pos < 2) {
+#pragma unroll
+            for (int j = 0; j < C::NT; ++j)
+                bq[pos][j] = *reinterpret_cast<const u32x4 *>(Bs + bw + j * 2048 + pos * 512);
+        }
 #pragma unroll
         for (int j = 0; j < C::NT; ++j)
-            braw[j] = *reinterpret_cast<const uint32_t *>(Bs + bw + j * 2048 + (bs & 1) * 512 +
-                                                          (bs >> 1) * 4);
-#pragma unroll
-        for (int j = 0; j < C::NT; ++j)
-            praw[j] = *reinterpret_cast<const uint32_t *>(Bs + bp + j * 256 + (bs >> 2) * 4);
+            praw[j] = *reinterpret_cast<const uint32_t *>(Bs + bp + j * 256 + (pos >> 2) * 4);
         const char *As = lds + aslot * C::ASLOT;
 #pragma unroll
         for (int i = 0; i < C::MT; ++i)
             x[i] = *reinterpret_cast<const u32x4 *>(As + al + i * 2048);
     };
-    // part c of step g's expansion: c == 0 converts the group's scale/bias
-    // pairs (when step g opens a group), c = 1 + 2 j + h expands code pairs
+    // code word of column tile j for the step at position pos
+    auto word = [&](int pos, int j) __attribute__((always_inline)) {
+        const u32x4 v = (pos & 1) ? bq[1][j] : bq[0][j];
+        const int t = pos >> 1;
+        return t == 0 ? v[0] : t == 1 ? v[1] : t == 2 ? v[2] : v[3];
+    };
+    // part c of the expansion of the step at position pos: c == 0 converts
+    // the group's scale/bias pairs (when the step opens a 64-k group),
+    // c = 1 + 2 j + h expands code pairs
     // 2 h and 2 h + 1 of column tile j, interleaved; each result is pinned
     // where it is computed (otherwise the compiler sinks the expansion to
     // its first use, behind the MFMAs)
     constexpr int NC = 1 + 2 * C::NT;
-    auto expand = [&](int g, int c, u32x4 (&y)[C::NT]) __attribute__((always_inline)) {
+    auto expand = [&](int pos, int c, u32x4 (&y)[C::NT]) __attribute__((always_inline)) {
         typedef _Float16 h2 __attribute__((ext_vector_type(2)));
         if (c == 0) {
-            if ((g & 3) == 0) {
+            if ((pos & 3) == 0) {
 #pragma unroll
                 for (int j = 0; j < C::NT; ++j) {
                     q4_pair(praw[j], fcol[j], ss[j], bb[j]);
@@ -333,7 +345,8 @@ q4_gemm_kernel(Q4Group grp) {
             }
         } else {
             const int j = (c - 1) >> 1, h = (c - 1) & 1;
-            const uint32_t w = h ? braw[j] >> 8 : braw[j];
+            const uint32_t wd = word(pos, j);
+            const uint32_t w = h ? wd >> 8 : wd;
             const uint32_t v0 = (w & cmask) | cbias, v1 = (w & cmask4) | cbias4;
             const h2 o0 = {(_Float16)-1024.f, (_Float16)-1024.f};
             const h2 o1 = {(_Float16)-64.f, (_Float16)-64.f};
@@ -364,7 +377,9 @@ q4_gemm_kernel(Q4Group grp) {
         const bool bcopy = p >= 0 ? decltype(BCOPY)::value : rbcopy;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const int g = 2 * kt + s;
+            // (step g = 2 kt + s) position of step g + 1 in its record block (a constant
+            // in the steady state)
+            const int pos1 = p >= 0 ? (2 * p + s + 1) & 7 : (2 * kt + s + 1) & 7;
             const int cur = s, nxt = s ^ 1; // buffers alternate by step parity
             if (s == 1) {
                 // this wave's reads of stage kt have landed; stage kt + 1
@@ -388,7 +403,7 @@ q4_gemm_kernel(Q4Group grp) {
             // the reads and expansion of step g + 1 -- after the last step
             // too, where they read stale LDS (in range) and their values go
             // unused, so that no step branches on them
-            read(g + 1, s == 0 ? as_cur : as_nxt, s == 0 ? bs_cur : bs_nxt, af[nxt]);
+            read(pos1, s == 0 ? as_cur : as_nxt, s == 0 ? bs_cur : bs_nxt, af[nxt]);
             // the MFMAs of step g; between them, the expansion of step g + 1
             // (starting one MFMA in, so that its LDS reads have landed) and,
             // at the last step of a stage, the copies
@@ -404,7 +419,7 @@ q4_gemm_kernel(Q4Group grp) {
                 if (q >= 1) {
 #pragma unroll
                     for (int c = (q - 1) * NC / (NMF - 1); c < q * NC / (NMF - 1); ++c)
-                        expand(g + 1, c, bfr[nxt]);
+                        expand(pos1, c, bfr[nxt]);
                 }
                 if (s == 1 && copy) {
 #pragma unroll
