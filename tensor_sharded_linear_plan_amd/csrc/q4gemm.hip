@@ -73,12 +73,12 @@ struct Q4Group {
     const char *segw[kMaxJoined][kSetParts];
 };
 
-// Block tile BM x BN, waves WM x 4 (WM per SIMD): wave (wm, wn) owns rows
-// [wm BM/WM, (wm+1) BM/WM) and columns [wn BN/4, (wn+1) BN/4).
-template <int BM, int BN, int WM>
+// Block tile BM x BN, waves WM x WN (WM WN / 4 per SIMD): wave (wm, wn)
+// owns rows [wm BM/WM, (wm+1) BM/WM) and columns [wn BN/WN, (wn+1) BN/WN).
+template <int BM, int BN, int WM, int WN>
 struct Q4G {
-    static constexpr int NW = 4 * WM;                // waves
-    static constexpr int TM = BM / WM, TN = BN / 4;  // wave tile
+    static constexpr int NW = WM * WN;               // waves
+    static constexpr int TM = BM / WM, TN = BN / WN; // wave tile
     static constexpr int MT = TM / 32, NT = TN / 32; // 32x32 tiles per wave
     static constexpr int ASLOT = BM * 64;            // a 32-k stage: BM rows x 64 bytes
     static constexpr int AF = BM / 16;               // its 1 KB blocks (16 rows each)
@@ -109,15 +109,15 @@ __device__ __forceinline__ void q4_pair(uint32_t sb, int f, uint32_t &ss, uint32
     bb = (u >> 16) * 0x10001u;
 }
 
-template <int BM, int BN, int WM>
-__global__ void __launch_bounds__(256 * WM) __attribute__((amdgpu_waves_per_eu(WM, WM)))
-q4_gemm_kernel(Q4Group grp) {
-    using C = Q4G<BM, BN, WM>;
+template <int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN)
+    __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) q4_gemm_kernel(Q4Group grp) {
+    using C = Q4G<BM, BN, WM, WN>;
     __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::ASLOT + C::NBS * C::BSLOT];
     __shared__ const char *mtab[kSetParts];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // scalar
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / WN, wn = wave % WN;
 
     const int bid = blockIdx.x;
     int lo = 0, hi = grp.n - 1; // last item whose first workgroup is <= bid
@@ -287,11 +287,9 @@ q4_gemm_kernel(Q4Group grp) {
     // LDS reads for the step at position pos (0..7) of its record block,
     // from activation slot aslot and record slot bslot: at positions 0 and 1
     // the code words of the block's even / odd steps (one 16-byte read per
-    // column tile: lanes 16 bytes apart, no bank conflicts), then the
-    // columns' scale/bias pairs of the step's 64-k group (read every step,
-    // the same pair for the group's four steps, so that the reads in flight
-    // and their waits depend on the position only), then the activation
-    // fragments.  Lane parts of the read addresses are re-made opaque at
+    // column tile: lanes 16 bytes apart, no bank conflicts), at positions 0
+    // and 4 the columns' scale/bias pairs of the 64-k group the step opens,
+    // then the activation fragments.  Lane parts of the read addresses are re-made opaque at
     // each use, so that the compiler does not hoist one address per unrolled
     // step out of the loop and run out of registers.
     const int rl = (lane & 31) >> 4;
@@ -312,9 +310,11 @@ q4_gemm_kernel(Q4Group grp) {
             for (int j = 0; j < C::NT; ++j)
                 bq[pos][j] = *reinterpret_cast<const u32x4 *>(Bs + bw + j * 2048 + pos * 512);
         }
+        if ((pos & 3) == 0) {
 #pragma unroll
-        for (int j = 0; j < C::NT; ++j)
-            praw[j] = *reinterpret_cast<const uint32_t *>(Bs + bp + j * 256 + (pos >> 2) * 4);
+            for (int j = 0; j < C::NT; ++j)
+                praw[j] = *reinterpret_cast<const uint32_t *>(Bs + bp + j * 256 + (pos >> 2) * 4);
+        }
         const char *As = lds + aslot * C::ASLOT;
 #pragma unroll
         for (int i = 0; i < C::MT; ++i)
@@ -553,13 +553,13 @@ typedef void (*Q4Fn)(Q4Group);
 // eight waves (two per SIMD, so that one covers the other's stalls), the
 // others four
 Q4Fn pick_q4(int bm, int bn, int *threads) {
-#define TSL_Q4(BM_, BN_, WM_)                                                                      \
+#define TSL_Q4(BM_, BN_, WM_, WN_)                                                                 \
     if (bm == BM_ && bn == BN_) {                                                                  \
-        *threads = 256 * WM_;                                                                      \
-        return q4_gemm_kernel<BM_, BN_, WM_>;                                                      \
+        *threads = 64 * WM_ * WN_;                                                                 \
+        return q4_gemm_kernel<BM_, BN_, WM_, WN_>;                                                 \
     }
-    TSL_Q4(256, 256, 2) TSL_Q4(256, 128, 1) TSL_Q4(128, 256, 1) TSL_Q4(128, 128, 1)
-    TSL_Q4(64, 256, 1) TSL_Q4(64, 128, 1)
+    TSL_Q4(256, 256, 2, 4) TSL_Q4(256, 128, 1, 4) TSL_Q4(128, 256, 1, 4) TSL_Q4(128, 128, 1, 4)
+    TSL_Q4(64, 256, 1, 4) TSL_Q4(64, 128, 1, 4)
 #undef TSL_Q4
     return nullptr;
 }
