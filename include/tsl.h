@@ -271,10 +271,10 @@ tsl_status pack_shard(const tsl_shard *shard, tsl_dtype wdtype, const void *W, i
 /*
  * shard_linear_workspace_size -- workspace bytes shard_linear needs for
  * this shard, weight type and row count (0 when none is needed): split-K
- * partial sums for decode-sized M; with M > 64, for 4-bit weights the shard
- * expanded to binary16 (2 bytes per weight), a binary16 copy of the
- * activations (M x k_len x 2 bytes) and their row exponents (M x 4 bytes),
- * for BF16 weights a zero-padded copy of
+ * partial sums for decode-sized M; with M > 64, for 4-bit weights a
+ * binary16 copy of the activations (M x k_len x 2 bytes, k_len rounded up
+ * to 64) and their row exponents (4 bytes per row, rows rounded up to 256)
+ * -- the weights stay packed -- for BF16 weights a zero-padded copy of
  * the activations when k_len is not a multiple of 64, and when the product
  * is too small to fill the chip the binary32 partials of its k-splits
  * (splits x M x n_len x 4 bytes).
