@@ -418,6 +418,27 @@ tsl_status shard_linear_group(int32_t n_items, const tsl_linear_item *items, tsl
                               void *stream);
 
 /*
+ * shard_linear_group_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): shard_linear_group with no workspace argument.  Its
+ * workspace is a fixed device array of TSL_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on (one copy per device, from the
+ * library's first use there until the process ends); the call allocates no
+ * device memory.  Items, types, results and errors are those of
+ * shard_linear_group; a call whose workspace would exceed the array (the
+ * exact amount for these items: products that read the same X count their
+ * activation copy once) returns TSL_ERR_BUFFER_TOO_SMALL before anything is
+ * enqueued.  Every call on one GPU uses that GPU's one array, which keeps
+ * the previous call's contents (none of them is read as input): calls on
+ * one stream are ordered, but calls that overlap in time on one GPU (other
+ * streams, other threads) race on the array and must not be issued.
+ */
+#define TSL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+tsl_status shard_linear_group_noalloc(int32_t n_items, const tsl_linear_item *items,
+                                      tsl_dtype wdtype, tsl_dtype xdtype, int64_t M,
+                                      void *stream);
+
+/*
  * combine_partials -- join rank outputs that all live on this one GPU
  * ([mlxcel] "Communication patterns": all-gather after column shards,
  * all-reduce after row shards; [wiki] "Details" §1 and "Examples" §1).

@@ -38,6 +38,9 @@ _lib = ctypes.CDLL(LIBRARY)
 OK = 0
 ERR_INVALID_ARG, ERR_NOT_DIVISIBLE, ERR_TP_NOT_POW2, ERR_GROUP_ALIGN = -1, -2, -3, -4
 ERR_BUFFER_TOO_SMALL, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP = -5, -6, -7, -8
+
+# bytes of the fixed device scratch behind shard_linear_group_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
 COLUMN, ROW, REPLICATED, EXPERT = 0, 1, 2, 3
 MOE_EXPERT_PARALLEL, MOE_WITHIN_EXPERT = 0, 1
 COMBINE_NONE, COMBINE_CONCAT, COMBINE_SUM = 0, 1, 2
@@ -114,6 +117,7 @@ _lib.shard_linear_group_workspace_size.argtypes = [_i32, _P_ITEM, ctypes.c_int, 
                                                    ctypes.POINTER(_sz)]
 _lib.shard_linear_group.argtypes = [_i32, _P_ITEM, ctypes.c_int, ctypes.c_int, _i64, _vp, _sz,
                                     _vp]
+_lib.shard_linear_group_noalloc.argtypes = [_i32, _P_ITEM, ctypes.c_int, ctypes.c_int, _i64, _vp]
 _lib.combine_partials.argtypes = [ctypes.c_int, _i32, ctypes.POINTER(_vp), ctypes.c_int, _i64,
                                   _i64, _i64, ctypes.c_int, _vp, _i64, _vp]
 _lib.combine_to_ranks.argtypes = [ctypes.c_int, _i32, ctypes.POINTER(_vp), ctypes.c_int, _i64,
@@ -133,13 +137,15 @@ _lib.tsl_last_hip_error_string.argtypes = []
 _lib.tsl_last_hip_error_string.restype = ctypes.c_char_p
 for _f in ("plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
            "shard_linear_workspace_size", "shard_linear", "shard_linear_group_workspace_size",
-           "shard_linear_group", "combine_partials", "combine_to_ranks", "plan_vocab",
+           "shard_linear_group", "shard_linear_group_noalloc", "combine_partials",
+           "combine_to_ranks", "plan_vocab",
            "embed_lookup", "plan_experts", "moe_dispatch", "moe_gather", "moe_combine"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
            "shard_linear_workspace_size", "shard_linear", "shard_linear_group_workspace_size",
-           "shard_linear_group", "combine_partials", "combine_to_ranks", "plan_vocab",
+           "shard_linear_group", "shard_linear_group_noalloc", "combine_partials",
+           "combine_to_ranks", "plan_vocab",
            "embed_lookup", "plan_experts", "moe_dispatch", "moe_gather", "moe_combine",
            "tsl_status_string", "tsl_last_hip_error_string")
 
@@ -299,6 +305,12 @@ def shard_linear_group(items, wdtype, xdtype, M, workspace=None, ws_bytes=0, str
     arr, n = _items(items)
     _check(_lib.shard_linear_group(n, arr, wdtype, xdtype, M, _ptr(workspace), ws_bytes,
                                    _stream(stream)), "shard_linear_group")
+
+
+def shard_linear_group_noalloc(items, wdtype, xdtype, M, stream=None):
+    arr, n = _items(items)
+    _check(_lib.shard_linear_group_noalloc(n, arr, wdtype, xdtype, M, _stream(stream)),
+           "shard_linear_group_noalloc")
 
 
 def combine_partials(mode, parts, pdtype, M, n_each, ld_part, ydtype, Y, ldy, stream=None):

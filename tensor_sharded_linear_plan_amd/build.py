@@ -20,7 +20,8 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libtsl.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["abi.cpp", "plan.cpp", "pack.hip", "combine.hip", "embed.hip", "moe.hip", "skinny.hip", "prefill.hip", "q4gemm.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "pack.hip", "combine.hip", "embed.hip", "moe.hip", "skinny.hip", "prefill.hip", "q4gemm.hip",
+           "noalloc.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-mcode-object-version=5", "-Wall",
          # only the C ABI of include/tsl.h is exported (it sets default visibility)
          "-fvisibility=hidden", "-fvisibility-inlines-hidden",

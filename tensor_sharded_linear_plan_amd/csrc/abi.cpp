@@ -615,6 +615,28 @@ extern "C" tsl_status shard_linear_group(int32_t n_items, const tsl_linear_item 
     return run_group(v, wdtype, M, workspace, ws_bytes, stream);
 }
 
+extern "C" tsl_status shard_linear_group_noalloc(int32_t n_items, const tsl_linear_item *items,
+                                                 tsl_dtype wdtype, tsl_dtype xdtype, int64_t M,
+                                                 void *stream) {
+    std::vector<LinearItem> v;
+    tsl_status st = gather(n_items, items, wdtype, xdtype, M, &v);
+    if (st != TSL_OK)
+        return st;
+    // the exact workspace of this call (its items carry their X pointers, so
+    // shared activation copies are counted once), checked before any device
+    // call
+    const size_t need = group_workspace(v, wdtype, M);
+    if (need > kNoAllocScratchBytes)
+        return TSL_ERR_BUFFER_TOO_SMALL;
+    void *scr = nullptr;
+    if (need > 0) {
+        hipError_t e = noalloc_scratch(&scr);
+        if (e != hipSuccess)
+            return from_hip(e);
+    }
+    return run_group(v, wdtype, M, scr, need > 0 ? kNoAllocScratchBytes : 0, stream);
+}
+
 namespace {
 
 // Bytes from the first to one past the last element of an [M][n] matrix

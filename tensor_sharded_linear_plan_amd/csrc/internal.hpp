@@ -141,6 +141,12 @@ struct LinearItem {
     int64_t seg_ldx[kSetParts] = {};
 };
 
+// ---- noalloc.hip: the fixed device scratch of shard_linear_group_noalloc ----
+constexpr size_t kNoAllocScratchBytes = TSL_NOALLOC_SCRATCH_BYTES;
+// The current device's copy of the scratch array (its address looked up once
+// per device, on first use).
+hipError_t noalloc_scratch(void **ptr);
+
 // Items per kernel launch (the item table travels in the kernel arguments,
 // up to ~13 KB of them); longer groups are launched in chunks of this size.
 constexpr int kGroupMax = 128;

@@ -27,6 +27,7 @@ def test_library_exports_every_declared_symbol(tsl_lib):
     assert set(names) == {"plan_shards", "plan_linear", "pack_shard_size", "pack_shard",
                           "shard_linear_workspace_size", "shard_linear",
                           "shard_linear_group_workspace_size", "shard_linear_group",
+                          "shard_linear_group_noalloc",
                           "combine_partials", "combine_to_ranks", "plan_vocab",
                           "embed_lookup", "plan_experts", "moe_dispatch", "moe_gather",
                           "moe_combine", "tsl_status_string", "tsl_last_hip_error_string"}
