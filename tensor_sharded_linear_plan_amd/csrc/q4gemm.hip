@@ -109,6 +109,12 @@ __device__ __forceinline__ void q4_pair(uint32_t sb, int f, uint32_t &ss, uint32
     bb = (u >> 16) * 0x10001u;
 }
 
+// Tile order of an item: bands of kBandM row tiles, each band column tile by
+// column tile (row tiles fastest); the workgroups of one XCD take a
+// contiguous run of this order, so an XCD's concurrent tiles share kBandM
+// row tiles' activations and a few column tiles' records in its L2.
+constexpr int kBandM = 2;
+
 template <int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(64 * WM * WN)
     __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) q4_gemm_kernel(Q4Group grp) {
@@ -136,10 +142,10 @@ __global__ void __launch_bounds__(64 * WM * WN)
     if (tk >= tiles * a.ks)
         return; // padding workgroup
     const int ksi = tk / tiles, t = tk - ksi * tiles;
-    const int band = t / (8 * a.NB);
-    const int first_m = band * 8;
-    const int bm_cnt = a.MB - first_m < 8 ? a.MB - first_m : 8;
-    const int in_band = t - band * 8 * a.NB;
+    const int band = t / (kBandM * a.NB);
+    const int first_m = band * kBandM;
+    const int bm_cnt = a.MB - first_m < kBandM ? a.MB - first_m : kBandM;
+    const int in_band = t - band * kBandM * a.NB;
     const int64_t mb = first_m + in_band % bm_cnt, nb = in_band / bm_cnt;
     const int64_t m0 = mb * BM, n0 = nb * BN;
     // this split's k-range, in whole 128-k record blocks

@@ -147,3 +147,30 @@ def test_tp1_is_the_unsharded_layer():
         assert (s.k_len, s.n_len) == (s.K, s.N)
     for y, ref in dense_case(256, 512, 40, tsl.BF16, tp=1, seed=980, integer=True):
         assert np.array_equal(y, ref)
+
+
+@pytest.mark.parametrize("wdtype", [tsl.BF16, tsl.Q4G64])
+def test_row_offsets_past_4_gib(wdtype):
+    """M = 1100 rows of a 2^21-element row stride: the activation rows of
+    the first m-band start 2^32 bytes and more past X, beyond 32-bit
+    offsets; each tile's own row offsets stay small and must be the ones
+    used (integer draws, bit-exact)."""
+    t = torch()
+    M, K, N, ldx = 1100, 128, 64, 1 << 21
+    Xs = synth.small_int_bf16(990, (M, K))
+    dX = t.empty((M, ldx), dtype=t.bfloat16, device="cuda")  # 4.6 GB, only K columns read
+    dX[:, :K] = dev(Xs)
+    sh = tsl.plan_linear(K, N, 1, tsl.COLUMN, 64)[0]
+    if wdtype == tsl.BF16:
+        W = synth.small_int_bf16(991, (K, N))
+        buf, nb = pack(sh, wdtype, dev(W), N, 1)
+        Wf = oracle.bf16_to_f64(W)
+    else:
+        w = Q4Weight(K, N, 992, 993, 994, integer=True)
+        buf, nb = w.pack(sh)
+        Wf = w.shard_f64(spec_dict(sh))
+    print("row offsets past 4 GiB: wdtype %d M %d ldx %d" % (wdtype, M, ldx), flush=True)
+    Y = host(linear(sh, wdtype, buf, nb, tsl.BF16, dX, ldx, M))
+    ref = oracle.gemm(oracle.bf16_to_f64(Xs), Wf)
+    assert np.array_equal(Y, ref)
+    del dX
