@@ -21,6 +21,7 @@ Infinity Cache) is reported beside it in GB/s.
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -32,8 +33,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # WRITE_SIZE runs scaled by a plain copy's readings; valid only for the
 # kernel sources it was measured on (their SHA-256 is recorded with it)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pre27b.json")
-TRAFFIC_SOURCES = ("tensor_sharded_linear_plan_amd/csrc/prefill.hip",
-                   "tensor_sharded_linear_plan_amd/csrc/combine.hip",
+TRAFFIC_SOURCES = ("tensor_sharded_linear_plan_amd/csrc/q4gemm.hip",
+                   "tensor_sharded_linear_plan_amd/csrc/prefill.hip",
+                   "tensor_sharded_linear_plan_amd/csrc/gemm_common.hpp",
+                   "tensor_sharded_linear_plan_amd/csrc/device.hpp",
+                   "tensor_sharded_linear_plan_amd/csrc/internal.hpp",
                    "tensor_sharded_linear_plan_amd/csrc/abi.cpp")
 PEAK_MFMA_F16 = 2500.0  # TFLOP/s, dense fp16/bf16 MFMA, MI355X
 PEAK_HBM = 8000.0       # GB/s, MI355X HBM3E
@@ -58,9 +62,10 @@ def sources_digest():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """Bytes per grouped call from the committed counter runs, or None when
-    the kernels have changed since they were taken."""
+def measured_traffic(kernel):
+    """HBM bytes (fetched + written) per launch of the named kernel of the
+    grouped call, from the committed counter runs, or None when the kernel
+    sources have changed since they were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -68,7 +73,8 @@ def measured_traffic():
         return None
     if rec.get("sources_sha256") != sources_digest():
         return None
-    return rec.get("bytes_per_call")
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k["fetch_bytes"] + k["write_bytes"]
 
 
 def build_layer(layer, M, copies, tsl, torch, synth, configs):
@@ -202,6 +208,131 @@ def make_step(layer, M, shards, packs, tsl, torch, configs, seed_base):
     return run, run_separate, flops, nbytes, len(steps[0][2])
 
 
+class _KernelNodeParams(ctypes.Structure):
+    """hipKernelNodeParams (hip_runtime_api.h), with room to spare."""
+    _fields_ = [("blockDim", ctypes.c_uint * 3), ("extra", ctypes.c_void_p),
+                ("func", ctypes.c_void_p), ("gridDim", ctypes.c_uint * 3),
+                ("kernelParams", ctypes.c_void_p), ("sharedMemBytes", ctypes.c_uint),
+                ("_spare", ctypes.c_char * 64)]
+
+
+def _hip_runtime():
+    """The HIP runtime this process already loaded (torch's, which the
+    library shares)."""
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                return ctypes.CDLL(line.split()[-1])
+    raise RuntimeError("no HIP runtime loaded")
+
+
+def kernel_times(torch, call, reps):
+    """Each kernel of one call, timed on its own: the call is captured into a
+    HIP graph on a side stream; for each of its kernel nodes, in launch
+    order, a copy of the graph that keeps only that node is replayed reps
+    times between two HIP events recorded on that stream.  The replays read
+    what the eager calls before them left in the workspace.  Returns
+    [(kernel name, grid workgroups, average microseconds)]."""
+    hip = _hip_runtime()
+    vp = ctypes.c_void_p
+    pvp, psz = ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_size_t)
+    sigs = {"hipStreamBeginCapture": [vp, ctypes.c_int], "hipStreamEndCapture": [vp, pvp],
+            "hipGraphGetNodes": [vp, vp, psz], "hipGraphNodeGetType": [vp, ctypes.c_void_p],
+            "hipGraphNodeGetDependencies": [vp, vp, psz],
+            "hipGraphKernelNodeGetParams": [vp, ctypes.c_void_p], "hipGraphClone": [pvp, vp],
+            "hipGraphNodeFindInClone": [pvp, vp, vp], "hipGraphDestroyNode": [vp],
+            "hipGraphInstantiate": [pvp, vp, vp, ctypes.c_char_p, ctypes.c_size_t],
+            "hipGraphLaunch": [vp, vp], "hipGraphExecDestroy": [vp], "hipGraphDestroy": [vp]}
+    for f, a in sigs.items():
+        getattr(hip, f).restype = ctypes.c_int
+        getattr(hip, f).argtypes = a
+    hip.hipKernelNameRefByPtr.restype = ctypes.c_char_p
+    hip.hipKernelNameRefByPtr.argtypes = [vp, vp]
+
+    def ok(e, what):
+        if e != 0:
+            raise RuntimeError("%s failed (HIP error %d)" % (what, e))
+
+    side = torch.cuda.Stream()
+    sp = vp(side.cuda_stream)
+    torch.cuda.synchronize()
+    graph = vp()
+    ok(hip.hipStreamBeginCapture(sp, 2), "hipStreamBeginCapture")  # relaxed mode
+    try:
+        call(side.cuda_stream)
+    finally:
+        ok(hip.hipStreamEndCapture(sp, ctypes.byref(graph)), "hipStreamEndCapture")
+    n = ctypes.c_size_t(0)
+    ok(hip.hipGraphGetNodes(graph, None, ctypes.byref(n)), "hipGraphGetNodes")
+    nodes = (vp * n.value)()
+    ok(hip.hipGraphGetNodes(graph, nodes, ctypes.byref(n)), "hipGraphGetNodes")
+    nodes = [vp(x) for x in nodes]
+    depth = {}
+
+    def node_depth(nd):
+        if nd.value not in depth:
+            m = ctypes.c_size_t(0)
+            ok(hip.hipGraphNodeGetDependencies(nd, None, ctypes.byref(m)), "dependencies")
+            deps = (vp * max(m.value, 1))()
+            if m.value:
+                ok(hip.hipGraphNodeGetDependencies(nd, deps, ctypes.byref(m)), "dependencies")
+            depth[nd.value] = 1 + max([node_depth(vp(d)) for d in deps[:m.value]] or [0])
+        return depth[nd.value]
+
+    kernels = []
+    for nd in nodes:
+        t = ctypes.c_int(-1)
+        ok(hip.hipGraphNodeGetType(nd, ctypes.byref(t)), "hipGraphNodeGetType")
+        if t.value == 0:  # hipGraphNodeTypeKernel
+            kernels.append(nd)
+    kernels.sort(key=node_depth)
+    out = []
+    for k in kernels:
+        prm = _KernelNodeParams()
+        ok(hip.hipGraphKernelNodeGetParams(k, ctypes.byref(prm)), "hipGraphKernelNodeGetParams")
+        name = hip.hipKernelNameRefByPtr(prm.func, sp)
+        name = name.decode(errors="replace") if name else "?"
+        wgs = prm.gridDim[0] * prm.gridDim[1] * prm.gridDim[2]
+        clone = vp()
+        ok(hip.hipGraphClone(ctypes.byref(clone), graph), "hipGraphClone")
+        for other in nodes:
+            if other.value != k.value:
+                c = vp()
+                ok(hip.hipGraphNodeFindInClone(ctypes.byref(c), other, clone), "FindInClone")
+                ok(hip.hipGraphDestroyNode(c), "hipGraphDestroyNode")
+        exe = vp()
+        ok(hip.hipGraphInstantiate(ctypes.byref(exe), clone, None, None, 0), "hipGraphInstantiate")
+        for _ in range(2):
+            ok(hip.hipGraphLaunch(exe, sp), "hipGraphLaunch")
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(side)
+        for _ in range(reps):
+            ok(hip.hipGraphLaunch(exe, sp), "hipGraphLaunch")
+        e1.record(side)
+        torch.cuda.synchronize()
+        out.append((name, wgs, e0.elapsed_time(e1) * 1e3 / reps))
+        ok(hip.hipGraphExecDestroy(exe), "hipGraphExecDestroy")
+        ok(hip.hipGraphDestroy(clone), "hipGraphDestroy")
+    ok(hip.hipGraphDestroy(graph), "hipGraphDestroy")
+    return out
+
+
+def short_kernel_name(name):
+    """q4_gemm_kernel<256, 256, 2, 4> from a mangled or demangled name."""
+    import re
+    m = re.search(r"(\w+_kernel)<([\d, ]+)>", name)  # demangled
+    if m:
+        return "%s<%s>" % (m.group(1), m.group(2))
+    # mangled: <length><identifier>, integer template arguments as Li256E
+    m = re.search(r"\d+([a-z][a-z0-9_]*_kernel)(I(?:Li-?\d+E)+E)?", name)
+    if not m:
+        m = re.search(r"(\w+_kernel)\b", name)  # demangled, no template arguments
+        return m.group(1) if m else name
+    args = re.findall(r"Li(-?\d+)E", m.group(2) or "")
+    return "%s<%s>" % (m.group(1), ", ".join(args)) if args else m.group(1)
+
+
 def prefill_bench(args, tsl, torch, synth, configs):
     layer = configs.PRE27B
     M = layer.ms[0]
@@ -233,6 +364,10 @@ def prefill_bench(args, tsl, torch, synth, configs):
     k_ms = sum(e0.elapsed_time(e1) for e0, e1 in timers) / len(timers)
     log("prefill: %.3f ms/step (%d shard products in one group call, %.3f ms), wall %.2f s"
         % (ms, nitems, k_ms, wall))
+    # each kernel of the call on its own (HIP events around graph replays)
+    kt = kernel_times(torch, lambda s: run(0, s), 10)
+    for name, wgs, us in kt:
+        log("prefill: kernel %s (%d workgroups): %.1f us" % (short_kernel_name(name), wgs, us))
     # context: the same pass as separate calls
     for i in range(2):
         run_separate(i, stream)
@@ -249,7 +384,8 @@ def prefill_bench(args, tsl, torch, synth, configs):
         % (len(packs[0]), lib["us"], lib["TFLOP/s"]))
     return dict(ms=ms, flops=flops, bytes=nbytes, wall=wall, kernel_ms=k_ms,
                 kernel_tflops=flops / (k_ms * 1e-3) / 1e12, pack_gbs=pack_bytes / pack_s / 1e9,
-                nitems=nitems, separate_ms=sep_ms, per_projection=per, library=lib)
+                nitems=nitems, separate_ms=sep_ms, per_projection=per, library=lib,
+                kernels=kt)
 
 
 def library_gemm(M, shards, torch, reps=5):
@@ -898,6 +1034,10 @@ def main():
         log("cpu baseline:", cpu["sample"])
 
     value = pre["flops"] / (pre["ms"] * 1e-3) / 1e12
+    # the dominant kernel: the longest launch of the grouped call
+    dom_full, _, dom_us = max(pre["kernels"], key=lambda k: k[2])
+    dom_name = short_kernel_name(dom_full)
+    dom_tflops = pre["flops"] / (dom_us * 1e-6) / 1e12
     layer = configs.PRE27B
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -911,16 +1051,20 @@ def main():
                                "o and down, all in one shard_linear_group call" % pre["nitems"],
                    "tp": layer.tp, "M": layer.ms[0], "weights": "q4g64", "activations": "bf16",
                    "parallelism": "tp4 in-process on 1 GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(pre["kernel_tflops"], 2),
+        "roofline": {"bound": "mfma", "achieved": round(dom_tflops, 2),
                      "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                     "frac": round(pre["kernel_tflops"] / PEAK_MFMA_F16, 4),
-                     "traffic": measured_traffic(),
-                     "kernel": "the step's shard_linear_group call: prep_kernel (4-bit -> "
-                               "f16 weights, activations -> f16), gemm_kernel (f16 MFMA: the 20 "
-                               "column-shard GEMMs, and the 4 o and the 4 down shards each as "
-                               "one GEMM over the ranks' k-ranges end to end, the rank sum "
-                               "accumulated in the GEMM)",
-                     "avg_launch_us": round(pre["kernel_ms"] * 1e3, 2)},
+                     "frac": round(dom_tflops / PEAK_MFMA_F16, 4),
+                     "traffic": measured_traffic(dom_name),
+                     "kernel": dom_name,
+                     "what": "the fused 4-bit GEMM launch of the step's shard_linear_group "
+                             "call: the 20 column-shard products and the o and down rank "
+                             "sums (each as one GEMM over the ranks' k-ranges end to end), "
+                             "codes expanded in registers, f16 MFMA, f32 accumulate; "
+                             "algorithmic flops of the whole step / its own duration",
+                     "avg_launch_us": round(dom_us, 2),
+                     "other_kernels_us": {short_kernel_name(n): round(u, 2)
+                                          for n, _, u in pre["kernels"] if n != dom_full},
+                     "call_us": round(pre["kernel_ms"] * 1e3, 2)},
         "cpu_baseline": cpu,
         "decode": {"workload": "dec7b: every rank of one tp=4 7B-class layer (hidden 3584, ffn "
                                "18944, 28 Q / 4 KV heads of 128), 4-bit g64, 28 shard GEMVs and "
