@@ -75,16 +75,6 @@ def normwise(y, r):
     return float(np.max(np.abs(y - r)) / den) if den > 0 else float(np.max(np.abs(y - r), initial=0.0))
 
 
-def bf16_ulp_err(y_bits, r):
-    """|y - RNE_bf16(r)| in units of the bf16 ulp at RNE_bf16(r)."""
-    rb = oracle.f64_to_bf16(r)
-    rv = oracle.bf16_to_f64(rb)
-    yv = oracle.bf16_to_f64(y_bits)
-    e = (rb.astype(np.int32) >> 7) & 0xFF
-    ulp = np.ldexp(1.0, np.maximum(e, 1) - 127 - 7)
-    return float(np.max(np.abs(yv - rv) / ulp)) if rb.size else 0.0
-
-
 class Q4Weight:
     """A full logical 4-bit weight: codes [K][N] (bytes), bf16 scale and
     bias [K/64][N] (bits), and its device copies."""

@@ -83,6 +83,9 @@ def test_integer_rows_to_2_pow_20_bit_exact(M):
     ref = oracle.gemm(Xf, w.shard_f64(spec_dict(sh)))
     assert np.max(np.abs(ref)) < 2 ** 24
     assert np.array_equal(Y, ref)
+    # bf16 output: the exact product rounded once, nearest even
+    Yb = host(linear(sh, tsl.Q4G64, buf, nb, tsl.BF16, dev(X), K, M, ydtype=tsl.BF16))
+    assert np.array_equal(Yb, oracle.bf16_to_f64(oracle.f64_to_bf16(ref)))
 
 
 def run_group(items, M):
