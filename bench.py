@@ -1000,9 +1000,10 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB five times (the reference "
                          "for scaling HBM byte counters)")
-    ap.add_argument("--only", choices=("all", "decode"), default="all",
-                    help="profiling aid: 'decode' runs the dec7b decode rows alone and prints "
-                         "them as the line (value: GB/s at M = 1)")
+    ap.add_argument("--only", choices=("all", "decode", "moe"), default="all",
+                    help="profiling aid: 'decode' runs the dec7b decode rows alone (value: GB/s "
+                         "at M = 1), 'moe' the moe30b rows (value: TFLOP/s at T = 2048), and "
+                         "prints them as the line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs every rank's shard on a single "
@@ -1031,6 +1032,14 @@ def main():
                           "steps": args.steps, "warmup": args.warmup,
                           "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
                           "rows": dec}), flush=True)
+        return
+    if args.only == "moe":
+        moe = moe_bench(args, tsl, torch, synth, configs)
+        print(json.dumps({"metric": "moe30b step, 4-bit expert products of every rank",
+                          "value": moe["rows"][0]["TFLOP/s"], "unit": "TFLOP/s", "n_gpus": 1,
+                          "steps": args.steps, "warmup": args.warmup,
+                          "higher_is_better": True, "dtype": "f16", "data": "synthetic",
+                          "moe": moe}), flush=True)
         return
     pre = prefill_bench(args, tsl, torch, synth, configs)
     dec = [] if args.no_decode else decode_bench(args, tsl, torch, synth, configs)

@@ -141,6 +141,14 @@ struct LinearItem {
     int64_t seg_ldx[kSetParts] = {};
 };
 
+// Workgroups per CU of the fused 4-bit GEMM for a bm x bn tile with wm row
+// waves: two when one row wave per SIMD leaves room for a second workgroup
+// in half the LDS (at least four 32-k activation stages beside three
+// record slots), else one.
+constexpr int q4_tiles_per_cu(int bm, int bn, int wm) {
+    return wm == 1 && (160 * 1024 / 2 - 3 * (bn / 16) * kQ4Record) / (bm * 64) >= 4 ? 2 : 1;
+}
+
 // ---- noalloc.hip: the fixed device scratch of shard_linear_group_noalloc ----
 constexpr size_t kNoAllocScratchBytes = TSL_NOALLOC_SCRATCH_BYTES;
 // The current device's copy of the scratch array (its address looked up once

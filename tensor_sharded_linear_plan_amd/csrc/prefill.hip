@@ -445,12 +445,14 @@ struct Variant {
     int bm, bn, wm, wn;
 };
 // tile shapes with a kernel instance: bf16 operands, and the fused 4-bit
-// kernel (its waves always 1 x 4)
+// kernel (waves WM x 4; two workgroups per CU where they fit)
 constexpr Variant kVariants[] = {{256, 256, 2, 2}, {256, 160, 4, 1}, {256, 128, 2, 2},
                                  {128, 256, 2, 2}, {128, 128, 2, 2}, {256, 64, 4, 1},
                                  {128, 64, 2, 2},  {64, 64, 2, 2}};
-constexpr Variant kQ4Variants[6] = {{256, 256, 1, 4}, {256, 128, 1, 4}, {128, 256, 1, 4},
+constexpr Variant kQ4Variants[6] = {{256, 256, 2, 4}, {256, 128, 1, 4}, {128, 256, 2, 4},
                                     {128, 128, 1, 4}, {64, 256, 1, 4},  {64, 128, 1, 4}};
+// workgroups of a 4-bit tile shape per CU
+int q4_per_cu(const Variant &v) { return q4_tiles_per_cu(v.bm, v.bn, v.wm); }
 
 GemmFn pick(const Variant &v) {
 #define TSL_CASE(BM_, BN_, WM_, WN_)                                                               \
@@ -492,7 +494,7 @@ constexpr int64_t kSplitBelow = 64;
 
 // Modelled cost of one launch [c0, c1) with k-split factor `factor`.
 double chunk_cost(const Variant &v, double pen, const LinearItem *items, int c0, int c1,
-                  int factor) {
+                  int factor, int per_cu) {
     int ks[kGroupMax];
     split_ks(items, c0, c1, factor, ks);
     auto mbk = [&](int i) { return (items[i].M + v.bm - 1) / v.bm; };
@@ -512,11 +514,12 @@ double chunk_cost(const Variant &v, double pen, const LinearItem *items, int c0,
         }
         span = work / 256.0 + longest;
     } else {
+        // per_cu workgroups share a CU, each at 1 / per_cu of its rate
         std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
-        for (int i = 0; i < 256; ++i)
+        for (int i = 0; i < 256 * per_cu; ++i)
             cu.push(0.0);
         for (int i = c0; i < c1; ++i) {
-            const double len = (double)kpad64(items[i].g.Ks) / 64.0 / ks[i - c0];
+            const double len = (double)kpad64(items[i].g.Ks) / 64.0 / ks[i - c0] * per_cu;
             const int64_t T = mbk(i) * ((items[i].g.Ns + v.bn - 1) / v.bn) * ks[i - c0];
             for (int64_t t = 0; t < T; ++t) {
                 const double f = cu.top() + len;
@@ -544,18 +547,20 @@ double variant_cost(const Variant &v, const LinearItem *items, int n, std::vecto
         const double l2 = 4096.0 * (v.bm + v.bn) * 2 / flops / 40.0;
         pen = lds > l2 ? lds : l2;
     } else {
-        // the fused 4-bit kernel (1 x 4 waves): LDS reads of binary16
-        // activations by all four waves and of code words, copies of
-        // activations and records; L2 delivery of both
+        // the fused 4-bit kernel: LDS reads of binary16 activations by the
+        // four column waves and of code words, copies of activations and
+        // records; L2 delivery of both
         const double lds = 4096.0 * (4.0 * v.bm * 2 + v.bn * 0.5 + v.bm * 2 + v.bn * 0.5625) /
                            flops / 128.0;
         const double l2 = 4096.0 * (v.bm * 2 + v.bn * 0.5625) / flops / 40.0;
         pen = lds > l2 ? lds : l2;
         pen = pen > 1.0 ? pen : 1.0;
         // plus the issue cycles every 16-k step costs a wave besides its
-        // MFMAs (reads, expansion, copies, waits: ~120), against the step's
-        // MT NT MFMAs of 32 clocks
-        pen += 120.0 / ((v.bm / 32) * (v.bn / 4 / 32) * 32.0);
+        // MFMAs (reads, expansion, copies, waits: ~120), against the SIMD's
+        // bm bn / 4096 MFMAs of 32 clocks per step; a second wave per SIMD
+        // (two row waves, or two workgroups per CU) covers half of it
+        const int waves = v.wm * q4_per_cu(v);
+        pen += 120.0 / ((v.bm / 32) * (v.bn / 4 / 32) * 32.0) / (waves > 1 ? 2.0 : 1.0);
     }
     pen = pen > 1.0 ? pen : 1.0;
     double total = 0.0;
@@ -566,7 +571,7 @@ double variant_cost(const Variant &v, const LinearItem *items, int n, std::vecto
         for (int i = c0; i < c1; ++i)
             tiles += ((items[i].M + v.bm - 1) / v.bm) * ((items[i].g.Ns + v.bn - 1) / v.bn);
         const int bf = tiles < kSplitBelow ? (int)((256 + tiles - 1) / tiles) : 1;
-        const double best = chunk_cost(v, pen, items, c0, c1, bf);
+        const double best = chunk_cost(v, pen, items, c0, c1, bf, q4 ? q4_per_cu(v) : 1);
         factors->push_back(bf);
         total += best;
     }

@@ -89,7 +89,10 @@ struct Q4G {
     static constexpr int PCW = NR / 2 / NW;          // pair copies (256 B, two records) per wave
     static constexpr int BCW = CCW + PCW;
     static constexpr int NBS = 3;                    // record slots
-    static constexpr int NSA = (kLdsLimit - NBS * BSLOT) / ASLOT;
+    // two workgroups per CU where they fit (each within half the LDS), so
+    // that one's pipeline fill and epilogue overlap the other's MFMAs
+    static constexpr int WPC = q4_tiles_per_cu(BM, BN, WM);
+    static constexpr int NSA = (kLdsLimit / WPC - NBS * BSLOT) / ASLOT;
     static constexpr int NS = NSA > 8 ? 8 : NSA;     // activation slots
     static_assert(MT >= 2 && NT >= 1 && TN % 32 == 0, "whole 32x32 tiles, two or more per step");
     static_assert(AF % NW == 0 && NR % (2 * NW) == 0, "copies divide over the waves");
@@ -117,7 +120,9 @@ constexpr int kBandM = 2;
 
 template <int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(64 * WM * WN)
-    __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) q4_gemm_kernel(Q4Group grp) {
+    __attribute__((amdgpu_waves_per_eu(WM * WN / 4 * q4_tiles_per_cu(BM, BN, WM),
+                                       WM * WN / 4 * q4_tiles_per_cu(BM, BN, WM))))
+    q4_gemm_kernel(Q4Group grp) {
     using C = Q4G<BM, BN, WM, WN>;
     __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::ASLOT + C::NBS * C::BSLOT];
     __shared__ const char *mtab[kSetParts];
@@ -555,16 +560,17 @@ __global__ void __launch_bounds__(64 * WM * WN)
 
 typedef void (*Q4Fn)(Q4Group);
 
-// the kernel of a tile shape and its workgroup size: 256 x 256 tiles run
-// eight waves (two per SIMD, so that one covers the other's stalls), the
-// others four
+// the kernel of a tile shape and its workgroup size: 256 x 256 and
+// 128 x 256 tiles run eight waves (two per SIMD, so that one covers the
+// other's stalls), the others four (two workgroups per CU where the LDS
+// holds them)
 Q4Fn pick_q4(int bm, int bn, int *threads) {
 #define TSL_Q4(BM_, BN_, WM_, WN_)                                                                 \
     if (bm == BM_ && bn == BN_) {                                                                  \
         *threads = 64 * WM_ * WN_;                                                                 \
         return q4_gemm_kernel<BM_, BN_, WM_, WN_>;                                                 \
     }
-    TSL_Q4(256, 256, 2, 4) TSL_Q4(256, 128, 1, 4) TSL_Q4(128, 256, 1, 4) TSL_Q4(128, 128, 1, 4)
+    TSL_Q4(256, 256, 2, 4) TSL_Q4(256, 128, 1, 4) TSL_Q4(128, 256, 2, 4) TSL_Q4(128, 128, 1, 4)
     TSL_Q4(64, 256, 1, 4) TSL_Q4(64, 128, 1, 4)
 #undef TSL_Q4
     return nullptr;
