@@ -1000,10 +1000,11 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB five times (the reference "
                          "for scaling HBM byte counters)")
-    ap.add_argument("--only", choices=("all", "decode", "moe"), default="all",
+    ap.add_argument("--only", choices=("all", "decode", "moe", "dense"), default="all",
                     help="profiling aid: 'decode' runs the dec7b decode rows alone (value: GB/s "
-                         "at M = 1), 'moe' the moe30b rows (value: TFLOP/s at T = 2048), and "
-                         "prints them as the line")
+                         "at M = 1), 'moe' the moe30b rows (value: TFLOP/s at T = 2048), 'dense' "
+                         "the bf16 / fp32 layer rows (value: gqa8 M = 512 TFLOP/s), and prints "
+                         "them as the line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs every rank's shard on a single "
@@ -1032,6 +1033,15 @@ def main():
                           "steps": args.steps, "warmup": args.warmup,
                           "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
                           "rows": dec}), flush=True)
+        return
+    if args.only == "dense":
+        dense = dense_bench(args, tsl, torch, configs)
+        g = [r for r in dense if r["workload"].startswith("gqa8") and r["M"] == 512]
+        print(json.dumps({"metric": "dense bf16 / fp32 layer steps, every rank",
+                          "value": g[0]["TFLOP/s"] if g else None, "unit": "TFLOP/s",
+                          "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+                          "dense": dense}), flush=True)
         return
     if args.only == "moe":
         moe = moe_bench(args, tsl, torch, synth, configs)

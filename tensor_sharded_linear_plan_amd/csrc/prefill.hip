@@ -94,11 +94,13 @@ struct G {
     static constexpr int RPB = 64 / CPR;            // activation rows per 1 KB block
     static constexpr int AF = BM / RPB;             // activation blocks per stage
     static constexpr int BF = (BN / 32) * S16;      // weight blocks per stage
-    static constexpr int FPW = (AF + BF) / 4;       // copy instructions per wave per stage
+    static constexpr int NW = WM * WN;              // waves
+    static constexpr int FPW = (AF + BF) / NW;      // copy instructions per wave per stage
     static constexpr int STAGE = (AF + BF) * 1024;
     static constexpr int NS = kLdsLimit / STAGE >= 4 ? 4 : kLdsLimit / STAGE;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 tiles");
-    static_assert(AF % 4 == 0 && BF % 4 == 0, "LDS blocks must divide over 4 waves");
+    static_assert(AF % NW == 0 && BF % NW == 0, "LDS blocks must divide over the waves");
+    static_assert(NW % S16 == 0, "a wave's weight blocks keep one 16-k step");
     static_assert(NS >= 2, "two stages must fit in LDS");
     static_assert(S16 % 2 == 0, "fragment buffers alternate by step parity");
     static_assert(FPW * (NS - 2) < 64, "vmcnt range");
@@ -110,8 +112,8 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 template <int BM, int BN, int WM, int WN>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_kernel(GemmGroup grp) {
+__global__ void __launch_bounds__(64 * WM * WN)
+    __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) gemm_kernel(GemmGroup grp) {
     using C = G<BM, BN, WM, WN>;
     __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE];
     const int lane = threadIdx.x & 63;
@@ -145,10 +147,10 @@ gemm_kernel(GemmGroup grp) {
     const int kb = ksi * nst_all / a.ks;       // this split's first stage
     const int nst = (ksi + 1) * nst_all / a.ks - kb;
 
-    // Sources of this wave's LDS blocks: block f = wave + 4 j < AF holds
+    // Sources of this wave's LDS blocks: block f = wave + NW j < AF holds
     // activation rows RPB f .. RPB f + RPB - 1 of the tile, the others weight
     // blocks g = f - AF (columns 32 (g / S16) of the tile, 16-k step g % S16;
-    // f < AF exactly when j < AF / 4).  Each is a per-lane byte offset from a
+    // f < AF exactly when j < AF / NW).  Each is a per-lane byte offset from a
     // tile base that advances by a constant per stage; the offsets are
     // recomputed at every issue (a few VALU ops) rather than held in
     // registers.  Rows past M and columns past the shard are clamped to the
@@ -162,7 +164,7 @@ gemm_kernel(GemmGroup grp) {
     const int arow = lane / C::CPR; // row of this lane in its block
     const uint32_t chunk = 8 * ((lane % C::CPR) ^ swz<C::CPR>(arow));
     const uint32_t aoff0 = ((uint32_t)(C::RPB * wave + arow) * (uint32_t)a.ldx + chunk) * 2;
-    const uint32_t astep = 4 * C::RPB * (uint32_t)a.ldx * 2;
+    const uint32_t astep = C::NW * C::RPB * (uint32_t)a.ldx * 2;
     const int64_t last_row = M - 1 - m0 < BM - 1 ? M - 1 - m0 : BM - 1;
     const uint32_t alim = ((uint32_t)last_row * (uint32_t)a.ldx + chunk) * 2;
     const int kr = 2 * (wave % C::S16) + (lane >> 5); // 8-k run of this wave's weight blocks
@@ -170,18 +172,18 @@ gemm_kernel(GemmGroup grp) {
     const uint32_t tstep = (uint32_t)a.KT32 * 1024; // one 16-column tile
     const int tmax = (int)(a.Nt16 - 1 - t0);
     const int tfirst = 2 * (wave / C::S16) + ((lane & 31) >> 4);
-    constexpr int TPJ = 2 * (4 / C::S16); // 16-column tiles per weight block step
+    constexpr int TPJ = 2 * (C::NW / C::S16); // 16-column tiles per weight block step
     const uint32_t lds0 = (uint32_t)(uintptr_t)(void __attribute__((address_space(3))) *)lds;
     // copy j (0 <= j < FPW) of this wave for stage kt into LDS slot `slot`
     auto issue1 = [&](int kt, int slot, int j) __attribute__((always_inline)) {
-        const uint32_t dst = lds0 + slot * C::STAGE + wave * 1024 + 4 * j * 1024;
+        const uint32_t dst = lds0 + slot * C::STAGE + wave * 1024 + C::NW * j * 1024;
         uint32_t a0 = aoff0, b0 = boff0;
         asm volatile("" : "+v"(a0), "+v"(b0)); // keep the per-j offsets out of registers
-        if (j < C::AF / 4) {
+        if (j < C::AF / C::NW) {
             const uint32_t o = a0 + (uint32_t)j * astep;
             dma16(xbase + (kt + kb) * (C::BK * 2), o < alim ? o : alim, dst);
         } else {
-            const int tt = tfirst + TPJ * (j - C::AF / 4);
+            const int tt = tfirst + TPJ * (j - C::AF / C::NW);
             dma16(bbase + (kt + kb) * (C::BK / 32 * 1024),
                   b0 + (uint32_t)(tt < tmax ? tt : tmax) * tstep, dst);
         }
@@ -446,7 +448,7 @@ struct Variant {
 };
 // tile shapes with a kernel instance: bf16 operands, and the fused 4-bit
 // kernel (waves WM x 4; two workgroups per CU where they fit)
-constexpr Variant kVariants[] = {{256, 256, 2, 2}, {256, 160, 4, 1}, {256, 128, 2, 2},
+constexpr Variant kVariants[] = {{256, 256, 2, 4}, {256, 160, 4, 1}, {256, 128, 2, 2},
                                  {128, 256, 2, 2}, {128, 128, 2, 2}, {256, 64, 4, 1},
                                  {128, 64, 2, 2},  {64, 64, 2, 2}};
 constexpr Variant kQ4Variants[6] = {{256, 256, 2, 4}, {256, 128, 1, 4}, {128, 256, 2, 4},
@@ -458,7 +460,7 @@ GemmFn pick(const Variant &v) {
 #define TSL_CASE(BM_, BN_, WM_, WN_)                                                               \
     if (v.bm == BM_ && v.bn == BN_ && v.wm == WM_ && v.wn == WN_)                                  \
         return gemm_kernel<BM_, BN_, WM_, WN_>;
-    TSL_CASE(256, 256, 2, 2) TSL_CASE(256, 160, 4, 1) TSL_CASE(256, 128, 2, 2)
+    TSL_CASE(256, 256, 2, 4) TSL_CASE(256, 160, 4, 1) TSL_CASE(256, 128, 2, 2)
     TSL_CASE(128, 256, 2, 2) TSL_CASE(128, 128, 2, 2) TSL_CASE(256, 64, 4, 1)
     TSL_CASE(128, 64, 2, 2) TSL_CASE(64, 64, 2, 2)
 #undef TSL_CASE
@@ -756,7 +758,7 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
             a.flags = L.ydtype == TSL_BF16 ? kYBf16 : 0;
             blocks += 8 * (int64_t)a.T8;
         }
-        hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, stream, grp);
+        hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * p.wm * p.wn), 0, stream, grp);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
