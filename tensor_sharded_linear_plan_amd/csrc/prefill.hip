@@ -448,8 +448,8 @@ struct Variant {
 };
 // tile shapes with a kernel instance: bf16 operands, and the fused 4-bit
 // kernel (waves WM x 4; two workgroups per CU where they fit)
-constexpr Variant kVariants[] = {{256, 256, 2, 4}, {256, 160, 4, 1}, {256, 128, 2, 2},
-                                 {128, 256, 2, 2}, {128, 128, 2, 2}, {256, 64, 4, 1},
+constexpr Variant kVariants[] = {{256, 256, 2, 4}, {256, 160, 4, 1}, {256, 128, 4, 2},
+                                 {128, 256, 2, 4}, {128, 128, 2, 2}, {256, 64, 4, 1},
                                  {128, 64, 2, 2},  {64, 64, 2, 2}};
 constexpr Variant kQ4Variants[6] = {{256, 256, 2, 4}, {256, 128, 1, 4}, {128, 256, 2, 4},
                                     {128, 128, 1, 4}, {64, 256, 1, 4},  {64, 128, 1, 4}};
@@ -460,8 +460,8 @@ GemmFn pick(const Variant &v) {
 #define TSL_CASE(BM_, BN_, WM_, WN_)                                                               \
     if (v.bm == BM_ && v.bn == BN_ && v.wm == WM_ && v.wn == WN_)                                  \
         return gemm_kernel<BM_, BN_, WM_, WN_>;
-    TSL_CASE(256, 256, 2, 4) TSL_CASE(256, 160, 4, 1) TSL_CASE(256, 128, 2, 2)
-    TSL_CASE(128, 256, 2, 2) TSL_CASE(128, 128, 2, 2) TSL_CASE(256, 64, 4, 1)
+    TSL_CASE(256, 256, 2, 4) TSL_CASE(256, 160, 4, 1) TSL_CASE(256, 128, 4, 2)
+    TSL_CASE(128, 256, 2, 4) TSL_CASE(128, 128, 2, 2) TSL_CASE(256, 64, 4, 1)
     TSL_CASE(128, 64, 2, 2) TSL_CASE(64, 64, 2, 2)
 #undef TSL_CASE
     return nullptr;
