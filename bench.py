@@ -446,6 +446,7 @@ def per_projection(layer, M, packs, tsl, torch, configs, reps):
                   + M * sh.n_len * 4)
         t_roof = max(flops / (PEAK_MFMA_F16 * 1e12), nbytes / (PEAK_HBM * 1e9)) * 1e6
         out.append({"proj": proj, "K": sh.k_len, "N": sh.n_len, "us": round(us, 2),
+                    "flops": flops, "bytes": nbytes,
                     "TFLOP/s": round(flops / us / 1e6, 1),
                     "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
                     "bound": "mfma" if flops / (PEAK_MFMA_F16 * 1e12) > nbytes / (PEAK_HBM * 1e9)
@@ -537,7 +538,7 @@ def decode_bench(args, tsl, torch, synth, configs):
         gbs = nbytes / (us * 1e-6) / 1e9
         res.append({"M": M, "us_per_step": round(us, 2), "GB/s": round(gbs, 1),
                     "frac": round(gbs / PEAK_HBM, 4), "shard_products_per_step": nitems,
-                    "bytes_per_step": nbytes})
+                    "bytes_per_step": nbytes, "flops_per_step": flops})
         log("decode M=%d: %.1f us/step, %.0f GB/s" % (M, us, gbs))
         del graph
         if M == 1:
@@ -990,6 +991,60 @@ def cpu_baseline(synth, configs):
                                                                          M, t)}
 
 
+def environment(torch):
+    """The device and its clocks as rocm-smi reports them (best effort)."""
+    import subprocess
+    props = torch.cuda.get_device_properties(0)
+    env = {"device": props.name, "compute_units": props.multi_processor_count,
+           "memory_GB": round(props.total_memory / 2**30, 1)}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        card = next(iter(json.loads(r.stdout).values()))
+        env["clocks_at_start"] = {k: v for k, v in card.items()
+                                  if "sclk" in k or "mclk" in k or "Power" in k}
+    except Exception as e:  # the tool is context only
+        env["clocks_at_start"] = "unavailable (%s)" % type(e).__name__
+    return env
+
+
+def results_rows(line, layer_pre, layer_dec):
+    """Per-row records in the survey's report format: one per measured row
+    (cfg, row, M, shard shape, flops, bytes, time, rates, bound, fraction of
+    the row's own roofline)."""
+    rows = []
+
+    def rec(cfg, row, M, K, N, dtype, flops, nbytes, us, bound=None):
+        t_roof = max(flops / (PEAK_MFMA_F16 * 1e12), nbytes / (PEAK_HBM * 1e9)) * 1e6
+        b = bound or ("mfma" if flops / (PEAK_MFMA_F16 * 1e12) > nbytes / (PEAK_HBM * 1e9)
+                      else "hbm")
+        rows.append({"cfg": cfg, "row": row, "M": M, "K_s": K, "N_s": N, "dtype": dtype,
+                     "flops": flops, "bytes": nbytes, "t_gpu_us": round(us, 2),
+                     "tflops": round(flops / us / 1e6, 2),
+                     "gbs": round(nbytes / us / 1e3, 1) if nbytes else None, "bound": b,
+                     "pct_roofline": round(100 * t_roof / us, 2)})
+
+    pre = line["roofline"]
+    rec("C3", "pre27b step, one grouped call", layer_pre.ms[0], None, None, "q4g64 x bf16",
+        line["step_flops"], line["step_bytes"], line["ms_per_step"] * 1e3, "mfma")
+    rec("C3", "pre27b fused GEMM launch", layer_pre.ms[0], None, None, "q4g64 x bf16",
+        line["step_flops"], pre["traffic"] or 0, pre["avg_launch_us"], "mfma")
+    for r in line["prefill_rank0_per_projection"]:
+        rec("C3", "rank 0 %s" % r["proj"], layer_pre.ms[0], r["K"], r["N"], "q4g64 x bf16",
+            r["flops"], r["bytes"], r["us"])
+    for d in line["decode"]["rows"]:
+        rec("C2", "dec7b step, one grouped call", d["M"], None, None, "q4g64 x bf16",
+            d["flops_per_step"], d["bytes_per_step"], d["us_per_step"], "hbm")
+        for r in d.get("rank0_per_projection", []):
+            rec("C2", "rank 0 %s" % r["proj"], d["M"], r["K"], r["N"], "q4g64 x bf16",
+                r["flops"], r["bytes"], r["us"])
+    for r in line["dense"] or []:
+        cfg = {"llama2k": "C1", "gqa8": "C4", "worked": "C0"}.get(r["workload"].split(":")[0])
+        rec(cfg, r["workload"].split(":")[0] + " step, one grouped call", r["M"], None, None,
+            "bf16" if cfg != "C0" else "f32", r["flops"], r["bytes"], r["us_per_step"], r["bound"])
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -1005,6 +1060,8 @@ def main():
                          "at M = 1), 'moe' the moe30b rows (value: TFLOP/s at T = 2048), 'dense' "
                          "the bf16 / fp32 layer rows (value: gqa8 M = 512 TFLOP/s), and prints "
                          "them as the line")
+    ap.add_argument("--results", metavar="PATH",
+                    help="also append one record per measured row to PATH (JSON lines)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs every rank's shard on a single "
@@ -1115,8 +1172,15 @@ def main():
         "prefill_rank0_per_projection": pre["per_projection"],
         "prefill_library_gemm": pre["library"],
         "wall_s_timed": round(pre["wall"], 3),
+        "step_flops": pre["flops"],
+        "step_bytes": pre["bytes"],
+        "env": environment(torch),
     }
     print(json.dumps(line), flush=True)
+    if args.results:
+        with open(args.results, "a") as f:
+            for r in results_rows(line, configs.PRE27B, configs.DEC7B):
+                f.write(json.dumps(r) + "\n")
 
 
 if __name__ == "__main__":
