@@ -252,8 +252,9 @@ std::vector<LinearItem> launch_order(const std::vector<LinearItem> &items) {
 // k-ranges of whole 128-k records becomes one product over the members'
 // k-ranges laid end to end in set order, Y = [X_0 X_1 ...] [W_0; W_1; ...]
 // -- the rank sum accumulated inside the GEMM, with no binary32 partials
-// and no sum launch (the prep pass writes each member's binary16 weights
-// and activations at its k offset of the joined operands).  Other sets, and
+// and no sum launch (the activation pass writes each member's binary16
+// activations at its k offset of the joined row, and the GEMM reads each
+// 128-k block's records from its member's packed buffer).  Other sets, and
 // every set of other weight types or of the decode regime, pass unchanged.
 std::vector<LinearItem> concat_sets(const std::vector<LinearItem> &in, tsl_dtype wdtype,
                                     int64_t M) {

@@ -52,24 +52,6 @@ __device__ __forceinline__ bf16x8 q4_to_bf16_plus128(uint32_t w) {
     return __builtin_bit_cast(bf16x8, r);
 }
 
-// Word -> eight binary16 weights s q + b: q is an exact binary32 integer,
-// s q is exact (8 + 4 significant bits), the sum is rounded to binary32 and
-// then to nearest binary16 (a double rounding whose extra error is at most
-// 2^-24 relative).
-__device__ __forceinline__ f16x8 q4_dequant_f16(uint32_t w, float s, float b) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    u32x4 out;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t p = (w >> (4 * j)) & 0x000F000Fu;
-        h2 r;
-        r.x = (_Float16)__builtin_fmaf(s, (float)(p & 0xFFu), b);
-        r.y = (_Float16)__builtin_fmaf(s, (float)(p >> 16), b);
-        out[j] = __builtin_bit_cast(uint32_t, r);
-    }
-    return __builtin_bit_cast(f16x8, out);
-}
-
 // ---- MFMA ---------------------------------------------------------------------
 // 16x16 output tile per wave.  Operand lane layout (as used by every kernel
 // here): lane l feeds row (A) / column (B) l % 16 with a run of k values

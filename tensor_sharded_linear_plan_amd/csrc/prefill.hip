@@ -36,7 +36,8 @@
 // run of workgroups starting at a multiple of 8.  Workgroups reach the 8
 // XCDs round-robin, so XCD x takes the x-th eighth of the item's tiles in
 // band order (bands of up to 8 m-blocks, m fastest), a compact patch whose
-// activation rows and weight columns stay in that XCD's L2.
+// activation rows and weight columns stay in that XCD's L2 (the fused 4-bit
+// kernel uses bands of 2 m-blocks).
 #include <hip/hip_runtime.h>
 
 #include <functional>
@@ -51,7 +52,7 @@ namespace tsl {
 namespace {
 
 struct GemmItem {
-    const u32x4 *B;    // fragment-packed weights [Nt16][KT32][64] x 16 B (bf16 or f16)
+    const u32x4 *B;    // fragment-packed bf16 weights [Nt16][KT32][64] x 16 B
     const uint16_t *X; // bf16 activations, K padded to 64
     void *Y;
     int64_t ldx, ldy;
@@ -62,11 +63,7 @@ struct GemmItem {
     int32_t T8;        // tiles per XCD, ceil(MB * NB / 8)
     int32_t start;     // first workgroup (a multiple of 8)
     int32_t accumulate;
-    // bit 0: bf16 output.  Binary16 operands (4-bit weights) are scaled by
-    // powers of two: the row exponents follow the activation copy ([M]
-    // int32 at X + M ldx, padded to whole 256-row tiles), the column
-    // exponents the weight fragments ([Nt16 16] int32 at B + Nt16 KT32 64)
-    int32_t flags;
+    int32_t flags;     // bit 0: bf16 output
     int64_t M;         // rows of this item
     float *P;          // ks > 1: binary32 k-partials [ks][M][Ns]
     int32_t ks, pad_;  // k-splits: tile t of split q covers stages [q nst / ks, (q+1) nst / ks)
