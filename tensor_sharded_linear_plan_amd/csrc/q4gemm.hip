@@ -10,10 +10,12 @@
 // expands the codes of its own columns in registers, s q + b per 16-k MFMA
 // step.  Activations are the binary16 copy of the activation pass (each row
 // scaled by a power of two), copied global -> LDS in 32-k stages as in the
-// bf16 GEMM.
+// bf16 GEMM.  The epilogue multiplies each result by 2^(e_m + f_n), the
+// row's and the column's exponents (exact), and stores bf16 or binary32.
 //
-// Waves are laid out WM x 4 (WM = 2 for 256 x 256 tiles, two waves per
-// SIMD; else 1): wave (wm, wn) owns rows [wm BM/WM, (wm+1) BM/WM) and
+// Waves are laid out WM x 4 (WM = 2 for 256 x 256 and 128 x 256 tiles,
+// two waves per SIMD; else 1, with two workgroups per CU where half the LDS
+// holds a tile's pipeline): wave (wm, wn) owns rows [wm BM/WM, (wm+1) BM/WM) and
 // columns [wn BN/4, (wn+1) BN/4) of the block tile, so each weight is
 // expanded by WM waves (once per row half).  A wave's 32x32x16 f16 MFMA B
 // fragment is one 32-bit code word per lane (8 consecutive k of the lane's
