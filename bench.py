@@ -141,10 +141,11 @@ def step_items(layer, M, pk, bufs, tsl, configs, sets=True):
     return items, flops, nbytes
 
 
-def make_step(layer, M, shards, packs, tsl, torch, configs, seed_base):
+def make_step(layer, M, shards, packs, tsl, torch, configs, seed_base, buffers=None):
     """Buffers and the calls of one multi-rank layer pass: one
     shard_linear_group over every rank's 7 projections, the rank sums of o
-    and down included (sum sets)."""
+    and down included (sum sets).  `buffers`, a dict, receives the inputs
+    and outputs (the parity test of this configuration reads them)."""
     hq_hd = layer.n_q_heads * layer.head_dim
     kv = layer.n_kv_heads * layer.head_dim
     g = torch.Generator(device="cuda")
@@ -162,6 +163,8 @@ def make_step(layer, M, shards, packs, tsl, torch, configs, seed_base):
                     "down": torch.empty((M, layer.hidden), dtype=bf, device="cuda")},
             "parts": {p: [torch.empty((M, layer.hidden), dtype=torch.float32, device="cuda")
                           for _ in range(layer.tp)] for p in ("o", "down")}}
+    if buffers is not None:
+        buffers.update(bufs)
     steps = []
     ws_max = 0
     for pk in packs:
