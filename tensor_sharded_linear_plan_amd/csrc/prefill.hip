@@ -32,16 +32,23 @@
 // the tile-shape cost model and the launch sequence.
 //
 // One launch serves a group of shard products of the same types, each over
-// its own rows; the item table rides in the kernel arguments.  Each item's tiles take a
-// run of workgroups starting at a multiple of 8.  Workgroups reach the 8
-// XCDs round-robin, so XCD x takes the x-th eighth of the item's tiles in
-// band order (bands of up to 8 m-blocks, m fastest), a compact patch whose
+// its own rows; the item table rides in the kernel arguments.  Each item's
+// tiles take a run of workgroups right after the previous item's.
+// Workgroups reach the 8 XCDs round-robin, so an item's workgroups go on
+// round the XCDs from where the previous item's ended (items of a few tiles
+// spread over all XCDs instead of piling onto the first), and the
+// workgroups of one XCD take a contiguous run of the item's tiles in band
+// order (bands of up to 8 m-blocks, m fastest), a compact patch whose
 // activation rows and weight columns stay in that XCD's L2 (the fused 4-bit
 // kernel uses bands of 2 m-blocks).
 #include <hip/hip_runtime.h>
 
+#include <cstring>
 #include <functional>
+#include <mutex>
 #include <queue>
+#include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "device.hpp"
@@ -60,8 +67,8 @@ struct GemmItem {
     int32_t KT32;      // 32-k tiles per column tile in B
     int32_t KT64;      // 64-k stages
     int32_t MB, NB;    // tile grid
-    int32_t T8;        // tiles per XCD, ceil(MB * NB / 8)
-    int32_t start;     // first workgroup (a multiple of 8)
+    int32_t pad0_;
+    int32_t start;     // first workgroup
     int32_t accumulate;
     int32_t flags;     // bit 0: bf16 output
     int64_t M;         // rows of this item
@@ -129,10 +136,12 @@ __global__ void __launch_bounds__(64 * WM * WN)
     const GemmItem &a = grp.it[lo];
     const int64_t M = a.M;
     const int local = bid - a.start;
-    const int tk = (local & 7) * a.T8 + (local >> 3); // (split, tile) in band order
+    // (split, tile) in band order: block b runs on XCD b mod 8, an item's
+    // blocks go on round the XCDs from where the previous item's ended, and
+    // the blocks of one XCD take a contiguous run of the order
     const int tiles = a.MB * a.NB;
-    if (tk >= tiles * a.ks)
-        return; // padding workgroup
+    const int nk = tiles * a.ks, x = local & 7, q8 = nk >> 3, r8 = nk & 7;
+    const int tk = x * q8 + (x < r8 ? x : r8) + (local >> 3);
     const int ksi = tk / tiles, t = tk - ksi * tiles;
     const int band = t / (8 * a.NB);
     const int first_m = band * 8;
@@ -491,11 +500,10 @@ void split_ks(const LinearItem *items, int c0, int c1, int factor, int *ks) {
 // k-range of its long products toward one tile per CU.
 constexpr int64_t kSplitBelow = 64;
 
-// Modelled cost of one launch [c0, c1) with k-split factor `factor`.
+// Modelled cost of one launch [c0, c1) whose items are split ks[i - c0]
+// ways along k.
 double chunk_cost(const Variant &v, double pen, const LinearItem *items, int c0, int c1,
-                  int factor, int per_cu) {
-    int ks[kGroupMax];
-    split_ks(items, c0, c1, factor, ks);
+                  const int *ks, int per_cu) {
     auto mbk = [&](int i) { return (items[i].M + v.bm - 1) / v.bm; };
     double span = 0.0, extra = 0.0;
     int64_t tiles = 0;
@@ -532,11 +540,18 @@ double chunk_cost(const Variant &v, double pen, const LinearItem *items, int c0,
     return span * (double)(v.bm * v.bn) * pen + extra * 32.0;
 }
 
+// bf16 launches of fewer tiles than this -- four per CU -- try k-split
+// factors up to 8 and keep the one the list schedule models shortest (the
+// partials' traffic included): a launch of one or two waves of long tiles
+// otherwise ends with most CUs idle.
+constexpr int64_t kSplitSearchBelow = 1024;
+
 // Modelled cost of a variant over a group, each launch (kGroupMax items;
-// every launch drains before the next starts) with its k-split factor
-// (1 unless the launch has fewer than kSplitBelow tiles), which *factors
-// receives.
-double variant_cost(const Variant &v, const LinearItem *items, int n, std::vector<int> *factors,
+// every launch drains before the next starts) with its k-splits, which
+// *ks receives per item: a launch of fewer than kSplitBelow tiles splits
+// its long products toward one tile per CU; a bf16 launch of fewer than
+// kSplitSearchBelow tiles takes the modelled best factor.
+double variant_cost(const Variant &v, const LinearItem *items, int n, std::vector<int> *ks,
                     bool q4) {
     const double TM = v.bm / v.wm, TN = v.bn / v.wn;
     const double flops = 2.0 * v.bm * v.bn; // per k
@@ -563,18 +578,59 @@ double variant_cost(const Variant &v, const LinearItem *items, int n, std::vecto
     }
     pen = pen > 1.0 ? pen : 1.0;
     double total = 0.0;
-    factors->clear();
+    ks->assign(n, 1);
     for (int c0 = 0; c0 < n; c0 += kGroupMax) {
         const int c1 = n - c0 < kGroupMax ? n : c0 + kGroupMax;
+        const int per_cu = q4 ? q4_per_cu(v) : 1;
         int64_t tiles = 0;
         for (int i = c0; i < c1; ++i)
             tiles += ((items[i].M + v.bm - 1) / v.bm) * ((items[i].g.Ns + v.bn - 1) / v.bn);
-        const int bf = tiles < kSplitBelow ? (int)((256 + tiles - 1) / tiles) : 1;
-        const double best = chunk_cost(v, pen, items, c0, c1, bf, q4 ? q4_per_cu(v) : 1);
-        factors->push_back(bf);
+        int *kc = &(*ks)[c0];
+        if (tiles < kSplitBelow)
+            split_ks(items, c0, c1, (int)((256 + tiles - 1) / tiles), kc);
+        double best = chunk_cost(v, pen, items, c0, c1, kc, per_cu);
+        if (!q4 && tiles >= kSplitBelow && tiles < kSplitSearchBelow) {
+            int trial[kGroupMax];
+            for (int f : {2, 3, 4, 6, 8}) {
+                split_ks(items, c0, c1, f, trial);
+                const double c = chunk_cost(v, pen, items, c0, c1, trial, per_cu);
+                if (c < best * 0.98) {
+                    best = c;
+                    std::memcpy(kc, trial, sizeof(int) * (c1 - c0));
+                }
+            }
+        }
         total += best;
     }
     return total;
+}
+
+// The tile shape and k-splits of a group's geometry, remembered: the cost
+// model (a list schedule per variant and split factor) runs once per
+// distinct geometry, and repeated calls of one layer's group reuse it.
+struct PlanChoice {
+    Variant v;
+    std::vector<int> ks;
+};
+std::mutex g_plan_mu;
+std::unordered_map<std::string, PlanChoice> g_plans;
+constexpr size_t kPlanCacheMax = 256;
+
+// what the choice depends on: weight type, and per item rows, k, columns
+// and whether it may be split
+std::string plan_key(const LinearItem *items, int n, tsl_dtype wdtype) {
+    std::string key(sizeof(int32_t) + (size_t)n * 25, '\0');
+    char *p = &key[0];
+    const int32_t w = (int32_t)wdtype;
+    std::memcpy(p, &w, 4);
+    p += 4;
+    for (int i = 0; i < n; ++i) {
+        const int64_t f[3] = {items[i].M, items[i].g.Ks, items[i].g.Ns};
+        std::memcpy(p, f, 24);
+        p[24] = (char)((items[i].accumulate ? 1 : 0) | (items[i].no_split ? 2 : 0));
+        p += 25;
+    }
+    return key;
 }
 
 } // namespace
@@ -584,24 +640,41 @@ bool prefill_supported(tsl_dtype wdtype) { return wdtype == TSL_BF16 || wdtype =
 PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64_t M) {
     (void)M;
     PrefillPlan best;
-    double best_cost = 1e300;
-    std::vector<int> factors, best_factors;
     const bool q4 = wdtype == TSL_Q4G64;
-    const Variant *vs = q4 ? kQ4Variants : kVariants;
-    const int nv = q4 ? (int)(sizeof(kQ4Variants) / sizeof(Variant))
-                      : (int)(sizeof(kVariants) / sizeof(Variant));
-    for (int vi = 0; vi < nv; ++vi) {
-        const Variant &v = vs[vi];
-        const double cost = variant_cost(v, items, n, &factors, q4);
-        if (cost < best_cost - 1e-9) {
-            best_cost = cost;
-            best.bm = v.bm;
-            best.bn = v.bn;
-            best.wm = v.wm;
-            best.wn = v.wn;
-            best_factors = factors;
+    const std::string key = plan_key(items, n, wdtype);
+    PlanChoice choice;
+    bool cached = false;
+    {
+        std::lock_guard<std::mutex> lock(g_plan_mu);
+        auto it = g_plans.find(key);
+        if (it != g_plans.end()) {
+            choice = it->second;
+            cached = true;
         }
     }
+    if (!cached) {
+        double best_cost = 1e300;
+        std::vector<int> ks;
+        const Variant *vs = q4 ? kQ4Variants : kVariants;
+        const int nv = q4 ? (int)(sizeof(kQ4Variants) / sizeof(Variant))
+                          : (int)(sizeof(kVariants) / sizeof(Variant));
+        for (int vi = 0; vi < nv; ++vi) {
+            const double cost = variant_cost(vs[vi], items, n, &ks, q4);
+            if (cost < best_cost - 1e-9) {
+                best_cost = cost;
+                choice.v = vs[vi];
+                choice.ks = ks;
+            }
+        }
+        std::lock_guard<std::mutex> lock(g_plan_mu);
+        if (g_plans.size() >= kPlanCacheMax)
+            g_plans.clear();
+        g_plans.emplace(key, choice);
+    }
+    best.bm = choice.v.bm;
+    best.bn = choice.v.bn;
+    best.wm = choice.v.wm;
+    best.wn = choice.v.wn;
     // workspace: activation copies (binary16 for 4-bit items, with their
     // row exponents; zero-padded bf16 for ragged-K bf16 items), one per
     // distinct (X, ldx, K, rows) -- items without a known X (sizing, joined
@@ -634,20 +707,16 @@ PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64
                                        : best.x_off[first];
         }
     }
-    // k-splits (split_ks with the launch's modelled factor), their binary32
-    // partials after the other copies
-    best.ks.assign(n, 1);
+    // k-splits (as modelled), their binary32 partials after the other
+    // copies
+    best.ks = choice.ks;
     best.p_off.assign(n, 0);
-    for (int c0 = 0, c = 0; c0 < n; c0 += kGroupMax, ++c) {
-        const int c1 = n - c0 < kGroupMax ? n : c0 + kGroupMax;
-        split_ks(items, c0, c1, best_factors[c], &best.ks[c0]);
-        for (int i = c0; i < c1; ++i)
-            if (best.ks[i] > 1) {
-                best.p_off[i] = off;
-                off += ((size_t)best.ks[i] * (size_t)items[i].M * (size_t)items[i].g.Ns * 4 + 255) /
-                       256 * 256;
-            }
-    }
+    for (int i = 0; i < n; ++i)
+        if (best.ks[i] > 1) {
+            best.p_off[i] = off;
+            off += ((size_t)best.ks[i] * (size_t)items[i].M * (size_t)items[i].g.Ns * 4 + 255) /
+                   256 * 256;
+        }
     best.ws_bytes = off;
     return best;
 }
@@ -749,11 +818,10 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
             a.NB = (int32_t)((g.Ns + p.bn - 1) / p.bn);
             a.ks = p.ks[c0 + i];
             a.P = reinterpret_cast<float *>(ws + p.p_off[c0 + i]);
-            a.T8 = (a.MB * a.NB * a.ks + 7) / 8;
             a.start = (int32_t)blocks;
             a.accumulate = L.accumulate;
             a.flags = L.ydtype == TSL_BF16 ? kYBf16 : 0;
-            blocks += 8 * (int64_t)a.T8;
+            blocks += (int64_t)a.MB * a.NB * a.ks;
         }
         hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * p.wm * p.wn), 0, stream, grp);
         e = hipGetLastError();
@@ -770,7 +838,7 @@ int64_t prefill_blocks(const PrefillPlan &p, const LinearItem *items, int n, int
         for (int i = c0; i < n && i < c0 + kGroupMax; ++i) {
             const int64_t T = ((items[i].M + p.bm - 1) / p.bm) *
                               ((items[i].g.Ns + p.bn - 1) / p.bn) * p.ks[i];
-            blocks += 8 * ((T + 7) / 8);
+            blocks += T;
         }
         most = blocks > most ? blocks : most;
     }

@@ -58,7 +58,7 @@ struct Q4Item {
     int32_t KBm;       // 128-k records per column tile of one member
     int32_t nst;       // 32-k activation stages of the whole k-range
     int32_t MB, NB;    // tile grid
-    int32_t T8, start; // tiles per XCD; first workgroup (a multiple of 8)
+    int32_t pad0_, start; // first workgroup
     int32_t flags, ks; // flags: bit 0 bf16 output, bit 1 accumulate
     int32_t seg, R;    // joined sum set: member table row (-1: none) and member count
 };
@@ -144,10 +144,12 @@ __global__ void __launch_bounds__(64 * WM * WN)
     const Q4Item &a = grp.it[lo];
     const int64_t M = a.M;
     const int local = bid - a.start;
-    const int tk = (local & 7) * a.T8 + (local >> 3); // (split, tile) in band order
+    // (split, tile) in band order: block b runs on XCD b mod 8, an item's
+    // blocks go on round the XCDs from where the previous item's ended, and
+    // the blocks of one XCD take a contiguous run of the order
     const int tiles = a.MB * a.NB;
-    if (tk >= tiles * a.ks)
-        return; // padding workgroup
+    const int nk = tiles * a.ks, x = local & 7, q8 = nk >> 3, r8 = nk & 7;
+    const int tk = x * q8 + (x < r8 ? x : r8) + (local >> 3);
     const int ksi = tk / tiles, t = tk - ksi * tiles;
     const int band = t / (kBandM * a.NB);
     const int first_m = band * kBandM;
@@ -619,10 +621,9 @@ hipError_t launch_q4_gemm(const PrefillPlan &p, const LinearItem *items, int n, 
             a.NB = (int32_t)((g.Ns + p.bn - 1) / p.bn);
             a.ks = p.ks[c];
             a.P = reinterpret_cast<float *>(const_cast<char *>(ws) + p.p_off[c]);
-            a.T8 = (a.MB * a.NB * a.ks + 7) / 8;
             a.start = (int32_t)blocks;
             a.flags = (L.ydtype == TSL_BF16 ? kQ4YBf16 : 0) | (L.accumulate ? kQ4Accumulate : 0);
-            blocks += 8 * (int64_t)a.T8;
+            blocks += (int64_t)a.MB * a.NB * a.ks;
         }
         hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), 0, stream, grp);
         hipError_t e = hipGetLastError();
