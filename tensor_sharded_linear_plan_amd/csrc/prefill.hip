@@ -540,8 +540,8 @@ double chunk_cost(const Variant &v, double pen, const LinearItem *items, int c0,
     return span * (double)(v.bm * v.bn) * pen + extra * 32.0;
 }
 
-// bf16 launches of fewer tiles than this -- four per CU -- try k-split
-// factors up to 8 and keep the one the list schedule models shortest (the
+// Launches of fewer tiles than this -- four per CU -- try k-split factors
+// up to 8 and keep the one the list schedule models shortest (the
 // partials' traffic included): a launch of one or two waves of long tiles
 // otherwise ends with most CUs idle.
 constexpr int64_t kSplitSearchBelow = 1024;
@@ -549,7 +549,7 @@ constexpr int64_t kSplitSearchBelow = 1024;
 // Modelled cost of a variant over a group, each launch (kGroupMax items;
 // every launch drains before the next starts) with its k-splits, which
 // *ks receives per item: a launch of fewer than kSplitBelow tiles splits
-// its long products toward one tile per CU; a bf16 launch of fewer than
+// its long products toward one tile per CU; a launch of fewer than
 // kSplitSearchBelow tiles takes the modelled best factor.
 double variant_cost(const Variant &v, const LinearItem *items, int n, std::vector<int> *ks,
                     bool q4) {
@@ -589,7 +589,7 @@ double variant_cost(const Variant &v, const LinearItem *items, int n, std::vecto
         if (tiles < kSplitBelow)
             split_ks(items, c0, c1, (int)((256 + tiles - 1) / tiles), kc);
         double best = chunk_cost(v, pen, items, c0, c1, kc, per_cu);
-        if (!q4 && tiles >= kSplitBelow && tiles < kSplitSearchBelow) {
+        if (tiles >= kSplitBelow && tiles < kSplitSearchBelow) {
             int trial[kGroupMax];
             for (int f : {2, 3, 4, 6, 8}) {
                 split_ks(items, c0, c1, f, trial);
