@@ -409,7 +409,7 @@ tsl_status shard_linear_group_workspace_size(int32_t n_items, const tsl_linear_i
  * item's Y may share an element with another item's Y or any item's X
  * (TSL_ERR_INVALID_ARG); column blocks of one output matrix with a common
  * ldy are fine.  The kernels are chosen by M (the largest row count).
- * Up to 128 items share one kernel launch;
+ * Up to 128 items share one kernel launch (256 in the prefill regime);
  * 1 <= n_items <= 4096.  items is a HOST array.
  * Errors: as shard_linear, for any item.
  */

@@ -158,6 +158,10 @@ hipError_t noalloc_scratch(void **ptr);
 // Items per kernel launch (the item table travels in the kernel arguments,
 // up to ~13 KB of them); longer groups are launched in chunks of this size.
 constexpr int kGroupMax = 128;
+// ... for the prefill GEMMs and their activation pass: 256 (up to ~27 KB of
+// kernel arguments, within the 32 KB this runtime launches correctly), so
+// that e.g. the gate and up products of 128 experts share one launch.
+constexpr int kPrefillGroupMax = 256;
 
 // ---- skinny.hip: decode-sized M (streams the weights once per 64 rows) ----
 struct SkinnyPlan {

@@ -81,7 +81,7 @@ constexpr int kYBf16 = 1;
 struct GemmGroup {
     int64_t M;
     int32_t n, pad_;
-    GemmItem it[kGroupMax];
+    GemmItem it[kPrefillGroupMax];
 };
 
 // Tile geometry.  A stage covers BK k: 64, or 32 when three 64-k stages do
@@ -353,7 +353,7 @@ struct XPiece {
 
 struct XPrepGroup {
     int32_t n, pad_;
-    XPiece it[kGroupMax];
+    XPiece it[kPrefillGroupMax];
 };
 
 // |x| of a bf16 pair, bit patterns (magnitude order is integer order)
@@ -546,7 +546,7 @@ double chunk_cost(const Variant &v, double pen, const LinearItem *items, int c0,
 // otherwise ends with most CUs idle.
 constexpr int64_t kSplitSearchBelow = 1024;
 
-// Modelled cost of a variant over a group, each launch (kGroupMax items;
+// Modelled cost of a variant over a group, each launch (kPrefillGroupMax items;
 // every launch drains before the next starts) with its k-splits, which
 // *ks receives per item: a launch of fewer than kSplitBelow tiles splits
 // its long products toward one tile per CU; a launch of fewer than
@@ -579,8 +579,8 @@ double variant_cost(const Variant &v, const LinearItem *items, int n, std::vecto
     pen = pen > 1.0 ? pen : 1.0;
     double total = 0.0;
     ks->assign(n, 1);
-    for (int c0 = 0; c0 < n; c0 += kGroupMax) {
-        const int c1 = n - c0 < kGroupMax ? n : c0 + kGroupMax;
+    for (int c0 = 0; c0 < n; c0 += kPrefillGroupMax) {
+        const int c1 = n - c0 < kPrefillGroupMax ? n : c0 + kPrefillGroupMax;
         const int per_cu = q4 ? q4_per_cu(v) : 1;
         int64_t tiles = 0;
         for (int i = c0; i < c1; ++i)
@@ -590,7 +590,7 @@ double variant_cost(const Variant &v, const LinearItem *items, int n, std::vecto
             split_ks(items, c0, c1, (int)((256 + tiles - 1) / tiles), kc);
         double best = chunk_cost(v, pen, items, c0, c1, kc, per_cu);
         if (tiles >= kSplitBelow && tiles < kSplitSearchBelow) {
-            int trial[kGroupMax];
+            int trial[kPrefillGroupMax];
             for (int f : {2, 3, 4, 6, 8}) {
                 split_ks(items, c0, c1, f, trial);
                 const double c = chunk_cost(v, pen, items, c0, c1, trial, per_cu);
@@ -755,7 +755,7 @@ hipError_t launch_xprep(const PrefillPlan &p, const LinearItem *items, int c0, i
         XPrepGroup xg{};
         int64_t blocks = 0;
         size_t q = q0;
-        while (q < xp.size() && q - q0 + xp[q].R <= (size_t)kGroupMax) {
+        while (q < xp.size() && q - q0 + xp[q].R <= (size_t)kPrefillGroupMax) {
             for (int r = 0; r < xp[q].R; ++r) {
                 XPiece &x = xg.it[xg.n++];
                 x = xp[q + r];
@@ -787,8 +787,8 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
     GemmFn fn = pick(Variant{p.bm, p.bn, p.wm, p.wn});
     if (!fn)
         return hipErrorInvalidValue;
-    for (int c0 = 0; c0 < n; c0 += kGroupMax) {
-        const int cn = n - c0 < kGroupMax ? n - c0 : kGroupMax;
+    for (int c0 = 0; c0 < n; c0 += kPrefillGroupMax) {
+        const int cn = n - c0 < kPrefillGroupMax ? n - c0 : kPrefillGroupMax;
         // 1. zero-padded copies of ragged-K activations
         hipError_t e = launch_xprep(p, items, c0, c0 + cn, false, ws, stream);
         if (e != hipSuccess)
@@ -833,9 +833,9 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
 
 int64_t prefill_blocks(const PrefillPlan &p, const LinearItem *items, int n, int64_t M) {
     int64_t most = 0;
-    for (int c0 = 0; c0 < n; c0 += kGroupMax) {
+    for (int c0 = 0; c0 < n; c0 += kPrefillGroupMax) {
         int64_t blocks = 0;
-        for (int i = c0; i < n && i < c0 + kGroupMax; ++i) {
+        for (int i = c0; i < n && i < c0 + kPrefillGroupMax; ++i) {
             const int64_t T = ((items[i].M + p.bm - 1) / p.bm) *
                               ((items[i].g.Ns + p.bn - 1) / p.bn) * p.ks[i];
             blocks += T;

@@ -71,7 +71,7 @@ constexpr int kMaxJoined = 16;
 
 struct Q4Group {
     int32_t n, pad_;
-    Q4Item it[kGroupMax];
+    Q4Item it[kPrefillGroupMax];
     const char *segw[kMaxJoined][kSetParts];
 };
 
@@ -593,7 +593,7 @@ hipError_t launch_q4_gemm(const PrefillPlan &p, const LinearItem *items, int n, 
         int joined = 0;
         int64_t blocks = 0;
         int c = c0;
-        for (; c < n && grp.n < kGroupMax; ++c) {
+        for (; c < n && grp.n < kPrefillGroupMax; ++c) {
             const LinearItem &L = items[c];
             if (L.cat > 1 && joined == kMaxJoined)
                 break;
