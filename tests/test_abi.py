@@ -575,3 +575,42 @@ def test_moe_gather_and_combine_rejections(tsl_lib):
         with pytest.raises(tsl_lib.TslError) as e:
             c(**kw)
         assert e.value.status == code, kw
+
+
+def test_plan_choices_are_remembered_per_geometry_and_thread_safe(tsl_lib):
+    """The GEMM regime's tile-shape and k-split choices are cached per group
+    geometry (weight type; each item's rows, k, columns and flags): queries
+    from many threads at once give the sizes the same queries give one at a
+    time, groups that differ only in rows, columns or a flag get their own
+    plans, and the cache stays bounded past its 256 entries."""
+    import concurrent.futures
+    sh = tsl_lib.plan_linear(2048, 4096, 4, tsl_lib.COLUMN, 64)
+    nb = tsl_lib.pack_shard_size(sh[0], tsl_lib.Q4G64)
+
+    def group(M, rows=None, acc=0, n=4, wd=None):
+        wd = wd or tsl_lib.Q4G64
+        items = []
+        for r in range(n):
+            it = dict(shard=sh[r % 4], packed=(1 << 24) + r * (1 << 22), packed_bytes=nb,
+                      X=(1 << 40) + r * (1 << 30), ldx=2048, Y=(1 << 42) + r * (1 << 30),
+                      ldy=sh[0].n_len, ydtype=tsl_lib.F32, accumulate=acc)
+            if rows is not None:
+                it["rows"] = rows[r % len(rows)]
+            items.append(it)
+        return items, wd, M
+
+    cases = [group(M) for M in (65, 100, 300, 1000, 2048)]
+    cases += [group(300, rows=(300, 77)), group(300, acc=1), group(2048, n=17)]
+    serial = [tsl_lib.shard_linear_group_workspace_size(*c) for c in cases]
+    # each variant of the same base geometry is planned on its own
+    assert len({(c[2], tuple(i.get("rows", -1) for i in c[0]), c[0][0]["accumulate"], len(c[0]))
+                for c in cases}) == len(cases)
+    with concurrent.futures.ThreadPoolExecutor(8) as ex:
+        for _ in range(3):
+            got = list(ex.map(lambda c: tsl_lib.shard_linear_group_workspace_size(*c),
+                              cases * 8))
+            assert got == serial * 8
+    # more than 256 distinct geometries: the cache starts over, sizes unchanged
+    for M in range(65, 65 + 300):
+        tsl_lib.shard_linear_group_workspace_size(*group(M))
+    assert [tsl_lib.shard_linear_group_workspace_size(*c) for c in cases] == serial
