@@ -995,18 +995,22 @@ def cpu_baseline(synth, configs):
 
 
 def environment(torch):
-    """The device and its clocks as rocm-smi reports them (best effort)."""
-    import subprocess
+    """The device and its current clock levels, read from the driver's sysfs
+    files for its PCI address (best effort; no helper program is started, so
+    nothing here forks or execs once the GPU is in use)."""
     props = torch.cuda.get_device_properties(0)
     env = {"device": props.name, "compute_units": props.multi_processor_count,
            "memory_GB": round(props.total_memory / 2**30, 1)}
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
-                           capture_output=True, text=True, timeout=20)
-        card = next(iter(json.loads(r.stdout).values()))
-        env["clocks_at_start"] = {k: v for k, v in card.items()
-                                  if "sclk" in k or "mclk" in k or "Power" in k}
-    except Exception as e:  # the tool is context only
+        base = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (
+            props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+        clocks = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            with open(os.path.join(base, name)) as f:
+                cur = [ln.split(":", 1)[1].strip(" *\n") for ln in f if ln.rstrip().endswith("*")]
+            clocks[name[-4:]] = cur[0] if cur else None
+        env["clocks_at_start"] = clocks
+    except Exception as e:  # the clocks are context only
         env["clocks_at_start"] = "unavailable (%s)" % type(e).__name__
     return env
 
