@@ -248,18 +248,22 @@ std::vector<LinearItem> launch_order(const std::vector<LinearItem> &items) {
     return v;
 }
 
-// 4-bit weights in the GEMM regime: a sum set whose members have equal
-// k-ranges of whole 128-k records becomes one product over the members'
-// k-ranges laid end to end in set order, Y = [X_0 X_1 ...] [W_0; W_1; ...]
-// -- the rank sum accumulated inside the GEMM, with no binary32 partials
-// and no sum launch (the activation pass writes each member's binary16
-// activations at its k offset of the joined row, and the GEMM reads each
-// 128-k block's records from its member's packed buffer).  Other sets, and
-// every set of other weight types or of the decode regime, pass unchanged.
+// The GEMM regime: a sum set whose members have equal k-ranges becomes one
+// product over the members' k-ranges laid end to end in set order,
+// Y = [X_0 X_1 ...] [W_0; W_1; ...] -- the rank sum accumulated inside the
+// GEMM, with no binary32 partials and no sum launch.  4-bit weights: k-
+// ranges of whole 128-k records (the activation pass writes each member's
+// binary16 activations at its k offset of the joined row, and the GEMM
+// reads each 128-k block's records from its member's packed buffer).
+// bf16 weights: k-ranges of whole 64-k stages and one activation row
+// stride (the GEMM reads each stage's activations and weights from its
+// member's own buffers).  Other sets, and every set of fp32 weights or of
+// the decode regime, pass unchanged.
 std::vector<LinearItem> concat_sets(const std::vector<LinearItem> &in, tsl_dtype wdtype,
                                     int64_t M) {
-    if (wdtype != TSL_Q4G64 || use_skinny(wdtype, M))
+    if ((wdtype != TSL_Q4G64 && wdtype != TSL_BF16) || use_skinny(wdtype, M))
         return in;
+    const int64_t unit = wdtype == TSL_Q4G64 ? 128 : 64;
     std::vector<LinearItem> out;
     out.reserve(in.size());
     for (size_t i = 0; i < in.size();) {
@@ -267,7 +271,8 @@ std::vector<LinearItem> concat_sets(const std::vector<LinearItem> &in, tsl_dtype
         bool join = len > 1 && len <= (size_t)kSetParts &&
                     (int64_t)len * in[i].g.Kpad < kPrefillMaxStride;
         for (size_t r = 0; join && r < len; ++r)
-            join = in[i + r].g.Ks % 128 == 0 && in[i + r].g.Ks == in[i].g.Ks;
+            join = in[i + r].g.Ks % unit == 0 && in[i + r].g.Ks == in[i].g.Ks &&
+                   (wdtype == TSL_Q4G64 || in[i + r].ldx == in[i].ldx);
         if (!join) {
             for (size_t r = 0; r < len; ++r)
                 out.push_back(in[i + r]);

@@ -162,6 +162,17 @@ constexpr int kGroupMax = 128;
 // kernel arguments, within the 32 KB this runtime launches correctly), so
 // that e.g. the gate and up products of 128 experts share one launch.
 constexpr int kPrefillGroupMax = 256;
+// ... of them joined sum sets (their member tables ride in the kernel
+// arguments too)
+constexpr int kMaxJoined = 16;
+// The end of the prefill launch that starts at item c0: at most
+// kPrefillGroupMax items, of them at most kMaxJoined joined sets.
+inline int prefill_chunk_end(const LinearItem *items, int n, int c0) {
+    int c1 = c0, joined = 0;
+    while (c1 < n && c1 - c0 < kPrefillGroupMax && !(items[c1].cat > 1 && joined == kMaxJoined))
+        joined += items[c1++].cat > 1 ? 1 : 0;
+    return c1;
+}
 
 // ---- skinny.hip: decode-sized M (streams the weights once per 64 rows) ----
 struct SkinnyPlan {

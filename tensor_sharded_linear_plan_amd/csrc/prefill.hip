@@ -43,6 +43,7 @@
 // kernel uses bands of 2 m-blocks).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstring>
 #include <functional>
 #include <mutex>
@@ -67,13 +68,14 @@ struct GemmItem {
     int32_t KT32;      // 32-k tiles per column tile in B
     int32_t KT64;      // 64-k stages
     int32_t MB, NB;    // tile grid
-    int32_t pad0_;
+    int32_t R;         // members of a joined sum set (1: a lone product)
     int32_t start;     // first workgroup
     int32_t accumulate;
     int32_t flags;     // bit 0: bf16 output
     int64_t M;         // rows of this item
     float *P;          // ks > 1: binary32 k-partials [ks][M][Ns]
-    int32_t ks, pad_;  // k-splits: tile t of split q covers stages [q nst / ks, (q+1) nst / ks)
+    int32_t ks;        // k-splits: tile t of split q covers stages [q nst / ks, (q+1) nst / ks)
+    int32_t seg;       // R > 1: the set's row of the member tables
 };
 static_assert(sizeof(GemmItem) == 104, "item table size");
 constexpr int kYBf16 = 1;
@@ -82,6 +84,10 @@ struct GemmGroup {
     int64_t M;
     int32_t n, pad_;
     GemmItem it[kPrefillGroupMax];
+    // joined sum set j, member r: its packed weights and its activations
+    // (every member has the set's activation row stride)
+    const char *segb[kMaxJoined][kSetParts];
+    const char *segx[kMaxJoined][kSetParts];
 };
 
 // Tile geometry.  A stage covers BK k: 64, or 32 when three 64-k stages do
@@ -164,9 +170,41 @@ __global__ void __launch_bounds__(64 * WM * WN)
     // Offsets stay below 2^32 because a tile spans at most 256 rows and the
     // activation row stride and K are below 2^22 elements (checked by the
     // caller); the clamp limit counts only the tile's own rows.
-    const char *xbase = reinterpret_cast<const char *>(a.X + m0 * a.ldx);
     const int64_t t0 = n0 >> 4;
-    const char *bbase = reinterpret_cast<const char *>(a.B + t0 * (int64_t)a.KT32 * 64);
+    // Where stage g of the product reads.  A joined sum set (R members of
+    // equal k-range, spm stages each) runs the members' k-ranges end to
+    // end: stage g is stage g - r spm of member r.  Lane r of xr / br holds
+    // member r's activation and record bases for this tile (lane 0 a lone
+    // product's), picked per stage with v_readlane, so the block loop reads
+    // no table from memory.
+    const int spm = a.R > 1 ? nst_all / a.R : nst_all;
+    uint32_t xr[2], br[2];
+    {
+        const int seg = a.R > 1 ? a.seg : 0;
+        const int r = lane < a.R ? lane : 0;
+        const char *xm = a.R > 1 ? grp.segx[seg][r] : reinterpret_cast<const char *>(a.X);
+        const char *wm0 = a.R > 1 ? grp.segb[seg][r] : reinterpret_cast<const char *>(a.B);
+        const uint64_t xv = (uint64_t)(uintptr_t)(xm + m0 * a.ldx * 2);
+        const uint64_t bv = (uint64_t)(uintptr_t)(wm0 + t0 * (int64_t)a.KT32 * 1024);
+        xr[0] = (uint32_t)xv;
+        xr[1] = (uint32_t)(xv >> 32);
+        br[0] = (uint32_t)bv;
+        br[1] = (uint32_t)(bv >> 32);
+    }
+    // the activation and record bases of stage kt of this split
+    auto src = [&](int kt, const char *&xs, const char *&bs) __attribute__((always_inline)) {
+        int r = 0, gl = kt + kb;
+        while (gl >= spm) { // uniform, at most R - 1 + NS / spm steps
+            gl -= spm;
+            ++r;
+        }
+        const uint64_t xv = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)xr[0], r) |
+                            ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)xr[1], r) << 32);
+        const uint64_t bv = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)br[0], r) |
+                            ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)br[1], r) << 32);
+        xs = reinterpret_cast<const char *>((uintptr_t)xv) + gl * (C::BK * 2);
+        bs = reinterpret_cast<const char *>((uintptr_t)bv) + gl * (C::BK / 32 * 1024);
+    };
     const int arow = lane / C::CPR; // row of this lane in its block
     const uint32_t chunk = 8 * ((lane % C::CPR) ^ swz<C::CPR>(arow));
     const uint32_t aoff0 = ((uint32_t)(C::RPB * wave + arow) * (uint32_t)a.ldx + chunk) * 2;
@@ -180,24 +218,27 @@ __global__ void __launch_bounds__(64 * WM * WN)
     const int tfirst = 2 * (wave / C::S16) + ((lane & 31) >> 4);
     constexpr int TPJ = 2 * (C::NW / C::S16); // 16-column tiles per weight block step
     const uint32_t lds0 = (uint32_t)(uintptr_t)(void __attribute__((address_space(3))) *)lds;
-    // copy j (0 <= j < FPW) of this wave for stage kt into LDS slot `slot`
-    auto issue1 = [&](int kt, int slot, int j) __attribute__((always_inline)) {
+    // copy j (0 <= j < FPW) of this wave for the stage whose bases are xs,
+    // bs into LDS slot `slot`
+    auto issue1 = [&](const char *xs, const char *bs, int slot, int j)
+                      __attribute__((always_inline)) {
         const uint32_t dst = lds0 + slot * C::STAGE + wave * 1024 + C::NW * j * 1024;
         uint32_t a0 = aoff0, b0 = boff0;
         asm volatile("" : "+v"(a0), "+v"(b0)); // keep the per-j offsets out of registers
         if (j < C::AF / C::NW) {
             const uint32_t o = a0 + (uint32_t)j * astep;
-            dma16(xbase + (kt + kb) * (C::BK * 2), o < alim ? o : alim, dst);
+            dma16(xs, o < alim ? o : alim, dst);
         } else {
             const int tt = tfirst + TPJ * (j - C::AF / C::NW);
-            dma16(bbase + (kt + kb) * (C::BK / 32 * 1024),
-                  b0 + (uint32_t)(tt < tmax ? tt : tmax) * tstep, dst);
+            dma16(bs, b0 + (uint32_t)(tt < tmax ? tt : tmax) * tstep, dst);
         }
     };
     auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
+        const char *xs, *bs;
+        src(kt, xs, bs);
 #pragma unroll
         for (int j = 0; j < C::FPW; ++j)
-            issue1(kt, slot, j);
+            issue1(xs, bs, slot, j);
     };
 
     f32x16 acc[C::MT][C::NT];
@@ -247,6 +288,7 @@ __global__ void __launch_bounds__(64 * WM * WN)
     int slot = 0;
     for (int kt = 0; kt < nst; ++kt) {
         const int next = slot + 1 == C::NS ? 0 : slot + 1;
+        const char *cxs = nullptr, *cbs = nullptr; // stage kt + NS's bases
 #pragma unroll
         for (int s = 0; s < C::S16; ++s) {
             const int b = s & 1; // S16 is even, so step parity is s parity
@@ -262,6 +304,8 @@ __global__ void __launch_bounds__(64 * WM * WN)
                     barrier();
                     rd(next, 0, af[b ^ 1], bfr[b ^ 1]);
                     copies = kt + C::NS < nst;
+                    if (copies)
+                        src(kt + C::NS, cxs, cbs);
                 }
             }
             // the copies of stage kt + NS go into the slot of stage kt,
@@ -276,7 +320,7 @@ __global__ void __launch_bounds__(64 * WM * WN)
 #pragma unroll
                     for (int f = q * C::FPW / (C::MT * C::NT); f < (q + 1) * C::FPW / (C::MT * C::NT); ++f)
                         if (copies)
-                            issue1(kt + C::NS, slot, f);
+                            issue1(cxs, cbs, slot, f);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -496,6 +540,23 @@ void split_ks(const LinearItem *items, int c0, int c1, int factor, int *ks) {
     }
 }
 
+// ... or each long product's k-range into as many parts as bring it to at
+// most `len` stages of 64 k (same limits), so that a launch of products of
+// unequal k-ranges (a joined sum set among single products) splits only
+// its longest ones.
+void split_to_length(const LinearItem *items, int c0, int c1, int64_t len, int *ks) {
+    for (int i = c0; i < c1; ++i) {
+        ks[i - c0] = 1;
+        if (items[i].accumulate || items[i].no_split)
+            continue;
+        const int64_t st = kpad64(items[i].g.Ks) / 64;
+        int64_t k = (st + len - 1) / len;
+        const int64_t cap = st / 8;
+        k = k < cap ? k : cap;
+        ks[i - c0] = (int)(k < 1 ? 1 : (k > 8 ? 8 : k));
+    }
+}
+
 // A launch with fewer tiles than this -- a quarter of the CUs -- splits the
 // k-range of its long products toward one tile per CU.
 constexpr int64_t kSplitBelow = 64;
@@ -541,9 +602,10 @@ double chunk_cost(const Variant &v, double pen, const LinearItem *items, int c0,
 }
 
 // Launches of fewer tiles than this -- four per CU -- try k-split factors
-// up to 8 and keep the one the list schedule models shortest (the
-// partials' traffic included): a launch of one or two waves of long tiles
-// otherwise ends with most CUs idle.
+// up to 8, and splits of the products longer than each k-range the launch
+// holds down to it, and keep the one the list schedule models shortest
+// (the partials' traffic included): a launch of one or two waves of long
+// tiles otherwise ends with most CUs idle.
 constexpr int64_t kSplitSearchBelow = 1024;
 
 // Modelled cost of a variant over a group, each launch (kPrefillGroupMax items;
@@ -579,8 +641,8 @@ double variant_cost(const Variant &v, const LinearItem *items, int n, std::vecto
     pen = pen > 1.0 ? pen : 1.0;
     double total = 0.0;
     ks->assign(n, 1);
-    for (int c0 = 0; c0 < n; c0 += kPrefillGroupMax) {
-        const int c1 = n - c0 < kPrefillGroupMax ? n : c0 + kPrefillGroupMax;
+    for (int c0 = 0; c0 < n;) {
+        const int c1 = prefill_chunk_end(items, n, c0);
         const int per_cu = q4 ? q4_per_cu(v) : 1;
         int64_t tiles = 0;
         for (int i = c0; i < c1; ++i)
@@ -591,16 +653,29 @@ double variant_cost(const Variant &v, const LinearItem *items, int n, std::vecto
         double best = chunk_cost(v, pen, items, c0, c1, kc, per_cu);
         if (tiles >= kSplitBelow && tiles < kSplitSearchBelow) {
             int trial[kPrefillGroupMax];
-            for (int f : {2, 3, 4, 6, 8}) {
-                split_ks(items, c0, c1, f, trial);
+            auto consider = [&]() {
                 const double c = chunk_cost(v, pen, items, c0, c1, trial, per_cu);
                 if (c < best * 0.98) {
                     best = c;
                     std::memcpy(kc, trial, sizeof(int) * (c1 - c0));
                 }
+            };
+            for (int f : {2, 3, 4, 6, 8}) {
+                split_ks(items, c0, c1, f, trial);
+                consider();
+            }
+            std::vector<int64_t> lens;
+            for (int i = c0; i < c1; ++i)
+                lens.push_back(kpad64(items[i].g.Ks) / 64);
+            std::sort(lens.begin(), lens.end());
+            lens.erase(std::unique(lens.begin(), lens.end()), lens.end());
+            for (size_t q = 0; q + 1 < lens.size(); ++q) { // the longest splits nothing
+                split_to_length(items, c0, c1, lens[q], trial);
+                consider();
             }
         }
         total += best;
+        c0 = c1;
     }
     return total;
 }
@@ -787,31 +862,45 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
     GemmFn fn = pick(Variant{p.bm, p.bn, p.wm, p.wn});
     if (!fn)
         return hipErrorInvalidValue;
-    for (int c0 = 0; c0 < n; c0 += kPrefillGroupMax) {
-        const int cn = n - c0 < kPrefillGroupMax ? n - c0 : kPrefillGroupMax;
+    for (int c0 = 0; c0 < n;) {
+        const int c1 = prefill_chunk_end(items, n, c0);
         // 1. zero-padded copies of ragged-K activations
-        hipError_t e = launch_xprep(p, items, c0, c0 + cn, false, ws, stream);
+        hipError_t e = launch_xprep(p, items, c0, c1, false, ws, stream);
         if (e != hipSuccess)
             return e;
         // 2. the GEMM over every item's tiles
         GemmGroup grp{};
         grp.M = M;
-        grp.n = cn;
+        grp.n = c1 - c0;
+        int joined = 0;
         int64_t blocks = 0;
-        for (int i = 0; i < cn; ++i) {
+        for (int i = 0; i < c1 - c0; ++i) {
             const LinearItem &L = items[c0 + i];
             const PackGeom &g = L.g;
             GemmItem &a = grp.it[i];
             const bool copied = p.x_first[c0 + i] >= 0;
-            a.B = static_cast<const u32x4 *>(L.packed);
-            a.X = copied ? reinterpret_cast<const uint16_t *>(ws + p.x_off[c0 + i])
-                         : static_cast<const uint16_t *>(L.X);
-            a.ldx = copied ? kpad64(g.Ks) : L.ldx;
+            a.R = L.cat;
+            a.seg = 0;
+            if (L.cat > 1) { // members never need a copy: whole 64-k stages
+                a.seg = joined++;
+                for (int r = 0; r < L.cat; ++r) {
+                    grp.segb[a.seg][r] = static_cast<const char *>(L.seg_packed[r]);
+                    grp.segx[a.seg][r] = static_cast<const char *>(L.seg_X[r]);
+                }
+                a.B = static_cast<const u32x4 *>(L.seg_packed[0]);
+                a.X = static_cast<const uint16_t *>(L.seg_X[0]);
+                a.ldx = L.seg_ldx[0];
+            } else {
+                a.B = static_cast<const u32x4 *>(L.packed);
+                a.X = copied ? reinterpret_cast<const uint16_t *>(ws + p.x_off[c0 + i])
+                             : static_cast<const uint16_t *>(L.X);
+                a.ldx = copied ? kpad64(g.Ks) : L.ldx;
+            }
             a.Y = L.Y;
             a.ldy = L.ldy;
             a.Ns = (int32_t)g.Ns;
             a.Nt16 = (int32_t)g.Nt;
-            a.KT32 = (int32_t)g.KT;
+            a.KT32 = (int32_t)(g.KT / L.cat); // a member's
             a.KT64 = (int32_t)(kpad64(g.Ks) / 64);
             a.M = L.M;
             a.MB = (int32_t)((L.M + p.bm - 1) / p.bm);
@@ -827,20 +916,22 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
+        c0 = c1;
     }
     return hipSuccess;
 }
 
 int64_t prefill_blocks(const PrefillPlan &p, const LinearItem *items, int n, int64_t M) {
+    (void)M;
     int64_t most = 0;
-    for (int c0 = 0; c0 < n; c0 += kPrefillGroupMax) {
+    for (int c0 = 0; c0 < n;) {
+        const int c1 = prefill_chunk_end(items, n, c0);
         int64_t blocks = 0;
-        for (int i = c0; i < n && i < c0 + kPrefillGroupMax; ++i) {
-            const int64_t T = ((items[i].M + p.bm - 1) / p.bm) *
-                              ((items[i].g.Ns + p.bn - 1) / p.bn) * p.ks[i];
-            blocks += T;
-        }
+        for (int i = c0; i < c1; ++i)
+            blocks += ((items[i].M + p.bm - 1) / p.bm) * ((items[i].g.Ns + p.bn - 1) / p.bn) *
+                      p.ks[i];
         most = blocks > most ? blocks : most;
+        c0 = c1;
     }
     return most;
 }

@@ -67,7 +67,6 @@ constexpr int kQ4YBf16 = 1, kQ4Accumulate = 2;
 
 // Joined sum sets of a launch: member r's records (the product runs over the
 // members' k-ranges laid end to end).
-constexpr int kMaxJoined = 16;
 
 struct Q4Group {
     int32_t n, pad_;
@@ -592,11 +591,10 @@ hipError_t launch_q4_gemm(const PrefillPlan &p, const LinearItem *items, int n, 
         Q4Group grp{};
         int joined = 0;
         int64_t blocks = 0;
+        const int c1 = prefill_chunk_end(items, n, c0);
         int c = c0;
-        for (; c < n && grp.n < kPrefillGroupMax; ++c) {
+        for (; c < c1; ++c) {
             const LinearItem &L = items[c];
-            if (L.cat > 1 && joined == kMaxJoined)
-                break;
             const PackGeom &g = L.g;
             Q4Item &a = grp.it[grp.n++];
             a.R = L.cat;

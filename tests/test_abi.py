@@ -408,6 +408,31 @@ def test_sum_set_rules(tsl_lib):
     assert e.value.status == tsl_lib.ERR_BUFFER_TOO_SMALL
 
 
+def test_bf16_sum_sets_join_in_the_gemm_regime(tsl_lib):
+    """bf16 weights above 64 rows: a sum set whose members hold whole 64-k
+    stages and share one activation row stride is one product over the
+    members' k-ranges end to end -- the workspace of the unsharded product,
+    no rank partials; a member with another row stride keeps the set's
+    binary32 rank partials (M x N x 4 bytes per member at least)."""
+    K, N, tp, M = 2048, 512, 4, 256
+    sh = tsl_lib.plan_linear(K, N, tp, tsl_lib.ROW, 64)
+    nb = tsl_lib.pack_shard_size(sh[0], tsl_lib.BF16)
+    X, Y = 1 << 26, 1 << 27
+
+    def items(ldx0=K):
+        return [dict(shard=s, packed=(1 << 24) + r * (1 << 20), packed_bytes=nb,
+                     X=X + 2 * s.k_off, ldx=ldx0 if r == 0 else K, Y=Y if r == 0 else None,
+                     ldy=N, sum_next=1 if r < tp - 1 else 0) for r, s in enumerate(sh)]
+
+    full = tsl_lib.plan_linear(K, N, 1, tsl_lib.ROW, 64)[0]
+    ws = tsl_lib.shard_linear_group_workspace_size
+    assert ws(items(), tsl_lib.BF16, M) == tsl_lib.shard_linear_workspace_size(
+        full, tsl_lib.BF16, M)
+    assert ws(items(K + 64), tsl_lib.BF16, M) >= tp * M * N * 4
+    # decode-sized calls never join: the rank partials are there
+    assert ws(items(), tsl_lib.BF16, 16) >= tp * 16 * N * 4
+
+
 def test_combine_to_ranks_rejections(tsl_lib):
     """Per-rank collectives: argument checks before any launch.  Accepted
     layouts are probed with M == 0 (validated, nothing enqueued) or via an
