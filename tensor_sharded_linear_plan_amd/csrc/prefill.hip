@@ -377,11 +377,14 @@ __global__ void __launch_bounds__(64 * WM * WN)
 // ---- prep: activation copies ----------------------------------------------
 // One job per distinct activation matrix of a launch: a product's X, or the
 // members' blocks X_0, X_1, ... of a joined sum set side by side.  A
-// workgroup takes one row.  Binary16 copies (4-bit weights): the row's
-// largest magnitude fixes e_m (kActExpBias below its ilogb), every element
-// becomes x 2^-e_m rounded to nearest binary16, and e_m goes to rexp[m].
-// Plain copies (bf16 weights with ragged K) only zero-pad.  Segment r is
-// the piece at pos r of the job; columns past its Ks up to Kw are zero.
+// workgroup of four waves takes one row of a wide job (rows of 4096
+// columns and more) and four rows, a wave each, of a narrow one, so that
+// rows of a few hundred columns still keep every lane busy.  Binary16
+// copies (4-bit weights): the row's largest magnitude fixes e_m
+// (kActExpBias below its ilogb), every element becomes x 2^-e_m rounded to
+// nearest binary16, and e_m goes to rexp[m].  Plain copies (bf16 weights
+// with ragged K) only zero-pad.  Segment r is the piece at pos r of the
+// job; columns past its Ks up to Kw are zero.
 struct XPiece {
     const uint16_t *x_in;
     uint16_t *x_out;  // this segment's first output column
@@ -392,13 +395,14 @@ struct XPiece {
     int32_t R, pos;   // segments of the job, this one's place
     int32_t M;        // rows
     int32_t start;    // first workgroup of the job (the same for its pieces)
-    int32_t pad_;
+    int32_t wide;     // the job's rows take a workgroup each (else a wave each)
 };
 
 struct XPrepGroup {
     int32_t n, pad_;
     XPiece it[kPrefillGroupMax];
 };
+constexpr int kXPrepWideColumns = 4096;
 
 // |x| of a bf16 pair, bit patterns (magnitude order is integer order)
 __device__ __forceinline__ uint32_t pair_max_abs(uint32_t m, uint32_t v) {
@@ -420,7 +424,15 @@ __global__ void __launch_bounds__(256) xprep_kernel(XPrepGroup grp) {
     }
     const int first = lo - grp.it[lo].pos;
     const XPiece &j0 = grp.it[first];
-    const int64_t m = bid - j0.start;
+    // the whole workgroup on one row (wide jobs), or a wave on each of four
+    const bool wide = j0.wide != 0;
+    const int tid = wide ? (int)threadIdx.x : (int)(threadIdx.x & 63);
+    const int nthr = wide ? 256 : 64;
+    const int64_t m = wide ? (int64_t)(bid - j0.start)
+                           : (int64_t)(bid - j0.start) * 4 +
+                                 __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    if (m >= j0.M)
+        return; // narrow jobs only (a wide job's workgroups are its rows): no barrier follows
     const bool to_f16 = j0.rexp != nullptr;
     int e = 0;
     if (to_f16) {
@@ -428,7 +440,7 @@ __global__ void __launch_bounds__(256) xprep_kernel(XPrepGroup grp) {
         for (int r = 0; r < j0.R; ++r) {
             const XPiece &p = grp.it[first + r];
             const uint16_t *src = p.x_in + m * p.ldx_in;
-            for (int k = threadIdx.x * 8; k < p.Ks; k += 256 * 8) {
+            for (int k = tid * 8; k < p.Ks; k += nthr * 8) {
                 if (k + 8 <= p.Ks) {
                     const u32x4 v = *reinterpret_cast<const u32x4 *>(src + k);
                     mx = pair_max_abs(mx, v.x);
@@ -447,24 +459,26 @@ __global__ void __launch_bounds__(256) xprep_kernel(XPrepGroup grp) {
             const uint32_t x = __shfl_xor(h, o, 64);
             h = x > h ? x : h;
         }
-        if ((threadIdx.x & 63) == 0)
-            red[threadIdx.x >> 6] = h;
-        __syncthreads();
-        h = red[0];
+        if (wide) { // the row's four waves agree
+            if ((threadIdx.x & 63) == 0)
+                red[threadIdx.x >> 6] = h;
+            __syncthreads();
+            h = red[0];
 #pragma unroll
-        for (int w = 1; w < 4; ++w)
-            h = red[w] > h ? red[w] : h;
+            for (int w = 1; w < 4; ++w)
+                h = red[w] > h ? red[w] : h;
+        }
         // a row of zeros (or non-finite values) keeps e = 0
         if (h != 0 && h < 0x7F80u)
             e = __builtin_amdgcn_frexp_expf(__uint_as_float(h << 16)) - 1 - kActExpBias;
-        if (threadIdx.x == 0)
+        if (tid == 0)
             j0.rexp[m] = e;
     }
     for (int r = 0; r < j0.R; ++r) {
         const XPiece &p = grp.it[first + r];
         const uint16_t *src = p.x_in + m * p.ldx_in;
         uint16_t *dst = p.x_out + m * (int64_t)p.x_ld;
-        for (int k = threadIdx.x * 8; k < p.Kw; k += 256 * 8) {
+        for (int k = tid * 8; k < p.Kw; k += nthr * 8) {
             u32x4 v = {0, 0, 0, 0};
             if (k + 8 <= p.Ks) {
                 v = *reinterpret_cast<const u32x4 *>(src + k);
@@ -831,12 +845,17 @@ hipError_t launch_xprep(const PrefillPlan &p, const LinearItem *items, int c0, i
         int64_t blocks = 0;
         size_t q = q0;
         while (q < xp.size() && q - q0 + xp[q].R <= (size_t)kPrefillGroupMax) {
+            int64_t width = 0;
+            for (int r = 0; r < xp[q].R; ++r)
+                width += xp[q + r].Kw;
+            const bool wide = width >= kXPrepWideColumns;
             for (int r = 0; r < xp[q].R; ++r) {
                 XPiece &x = xg.it[xg.n++];
                 x = xp[q + r];
                 x.start = (int32_t)blocks;
+                x.wide = wide ? 1 : 0;
             }
-            blocks += xp[q].M;
+            blocks += wide ? xp[q].M : (xp[q].M + 3) / 4;
             q += xp[q].R;
         }
         if (blocks > 0) {
