@@ -808,10 +808,11 @@ def dense_bench(args, tsl, torch, configs):
 
 def moe_bench(args, tsl, torch, synth, configs):
     """moe30b, expert parallel, every rank of the layer on one GPU: per
-    step the rows of all ranks gathered (one moe_gather for the token
-    inputs, one for the per-slot down inputs), every held expert's gate and
-    up products in one shard_linear_group call, the down products in
-    another, each rank's moe_combine and the sum of the rank outputs.
+    step every held expert's gate and up products in one
+    shard_linear_group call, the down products in another (each product
+    reads its rows -- the tokens, or the per-slot down inputs, routed to
+    its expert -- through moe_dispatch's row index, with no gather pass),
+    each rank's moe_combine and the sum of the rank outputs.
     Routing (moe_dispatch) is host work on the router's output and is done
     before the timed region.  T = 2048: TFLOP/s of the expert products;
     T = 16: GB/s of the weights of the experts the step touches, HIP-graph
@@ -843,8 +844,9 @@ def moe_bench(args, tsl, torch, synth, configs):
     wbytes = lambda K, N: K * N // 2 + (K // 64) * N * 4
     out = {"workload": "moe30b: 128 experts of width 768, top-8, hidden 2048, expert parallel "
                        "over tp=4 (32 experts per rank), 4-bit g64, all ranks on one GPU; per "
-                       "step: gathers, the gate+up and the down products of every held expert "
-                       "(two shard_linear_group calls), 4 moe_combine and the rank sum",
+                       "step: the gate+up and the down products of every held expert (two "
+                       "shard_linear_group calls, rows read through the routing's row "
+                       "index), 4 moe_combine and the rank sum",
            "rows": []}
     for T in c.tokens:
         xs = synth.seed_of(c.index, 0, synth.T_X) + T
@@ -868,8 +870,6 @@ def moe_bench(args, tsl, torch, synth, configs):
         R = base
         d_tok = torch.from_numpy(np.concatenate(tok_idx).astype(np.int32)).cuda()
         d_slot = torch.from_numpy(np.concatenate(slot_idx).astype(np.int32)).cuda()
-        Xp = torch.empty((R, c.hidden), dtype=torch.bfloat16, device="cuda")
-        Hp = torch.empty((R, c.expert_ffn), dtype=torch.bfloat16, device="cuda")
         G = torch.empty((R, c.expert_ffn), dtype=torch.bfloat16, device="cuda")
         U = torch.empty((R, c.expert_ffn), dtype=torch.bfloat16, device="cuda")
         P = torch.empty((R, c.hidden), dtype=torch.float32, device="cuda")
@@ -890,11 +890,13 @@ def moe_bench(args, tsl, torch, synth, configs):
                     for p, Yb in (("gate", G), ("up", U)):
                         buf, nb = packs[cp][e, p]
                         gu.append(dict(shard=getattr(x, p), packed=buf, packed_bytes=nb,
-                                       X=Xp[o:], ldx=c.hidden, Y=Yb[o:], ldy=c.expert_ffn,
-                                       ydtype=tsl.BF16, rows=rows))
+                                       X=X, ldx=c.hidden, Y=Yb[o:], ldy=c.expert_ffn,
+                                       ydtype=tsl.BF16, rows=rows, row_index=d_tok[o:],
+                                       x_rows=T))
                     buf, nb = packs[cp][e, "down"]
-                    dn.append(dict(shard=x.down, packed=buf, packed_bytes=nb, X=Hp[o:],
-                                   ldx=c.expert_ffn, Y=P[o:], ldy=c.hidden, rows=rows))
+                    dn.append(dict(shard=x.down, packed=buf, packed_bytes=nb, X=H,
+                                   ldx=c.expert_ffn, Y=P[o:], ldy=c.hidden, rows=rows,
+                                   row_index=d_slot[o:], x_rows=T * k))
                     if cp == 0:
                         flops += 6 * rows * c.hidden * c.expert_ffn
                         touched += 3 * wbytes(c.hidden, c.expert_ffn)
@@ -907,9 +909,6 @@ def moe_bench(args, tsl, torch, synth, configs):
             calls.append(groups)
 
         def step(cp, stream):
-            tsl.moe_gather(X, c.hidden, T, tsl.BF16, d_tok, R, c.hidden, Xp, c.hidden, stream)
-            tsl.moe_gather(H, c.expert_ffn, T * k, tsl.BF16, d_slot, R, c.expert_ffn, Hp,
-                           c.expert_ffn, stream)
             for (arr, n), wsb, ws in calls[cp]:
                 tsl._check(tsl._lib.shard_linear_group(n, arr, tsl.Q4G64, tsl.BF16, Mmax,
                                                        wsb.data_ptr(), ws, stream),

@@ -373,6 +373,17 @@ tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, const void *pa
  * counts share one launch -- the per-expert products of a mixture-of-
  * experts layer, each over the tokens routed to its expert ([mlxcel] "MoE
  * expert parallelization").  The members of a sum set have equal rows.
+ *
+ * row_index: null, or DEVICE int32 [rows]: row i of the product reads row
+ * row_index[i] of X, which then has x_rows rows (1 <= x_rows < 2^31); an
+ * index outside [0, x_rows) reads a row of zeros.  The tokens routed to an
+ * expert are read where they lie, with no gather pass of their own
+ * ([mlxcel] "MoE expert parallelization"; moe_gather's idx has the same
+ * meaning): with Q4G64 weights above 64 rows the activation pass reads
+ * them; otherwise the call first gathers each distinct (X, ldx, k_len,
+ * row_index, rows) into its workspace (a bf16 / fp32 copy, zeros for
+ * out-of-range rows).  row_index must be 4-byte aligned and must not
+ * overlap any output; x_rows is ignored when row_index is null.
  */
 typedef struct {
     const tsl_shard *shard;
@@ -386,13 +397,16 @@ typedef struct {
     int32_t accumulate;
     int32_t sum_next;
     int32_t rows;
+    const int32_t *row_index;
+    int64_t x_rows;
 } tsl_linear_item;
 
 /*
  * shard_linear_group_workspace_size -- workspace bytes shard_linear_group
- * needs for these items (only their shards, sum_next and rows are read),
- * weight type and M.  An upper bound: a call whose items read the same X (same
- * pointer, ldx and k_len) shares one activation copy and uses less.
+ * needs for these items (only their shards, sum_next, rows and whether
+ * row_index is null are read), weight type and M.  An upper bound: a call
+ * whose items read the same X (same pointer, ldx, k_len and row_index)
+ * shares one activation copy and uses less.
  */
 tsl_status shard_linear_group_workspace_size(int32_t n_items, const tsl_linear_item *items,
                                              tsl_dtype wdtype, int64_t M, size_t *bytes);

@@ -99,7 +99,8 @@ class LinearItem(ctypes.Structure):
                 ("packed_bytes", ctypes.c_size_t), ("X", ctypes.c_void_p),
                 ("ldx", ctypes.c_int64), ("Y", ctypes.c_void_p), ("ldy", ctypes.c_int64),
                 ("ydtype", ctypes.c_int32), ("accumulate", ctypes.c_int32),
-                ("sum_next", ctypes.c_int32), ("rows", ctypes.c_int32)]
+                ("sum_next", ctypes.c_int32), ("rows", ctypes.c_int32),
+                ("row_index", ctypes.c_void_p), ("x_rows", ctypes.c_int64)]
 
 
 _i32, _i64, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
@@ -273,8 +274,8 @@ def shard_linear(shard, wdtype, packed, packed_bytes, xdtype, X, ldx, M, ydtype,
 
 def _items(items):
     """items: sequence of dicts (or LinearItem) with the tsl_linear_item
-    fields (ydtype defaults to F32, accumulate and sum_next to 0); shard is
-    a Shard; a set member's Y may be None.
+    fields (ydtype defaults to F32, accumulate, sum_next and rows to 0,
+    row_index to None); shard is a Shard; a set member's Y may be None.
     Returns the ctypes array (which keeps the shard copies alive) and its
     length."""
     arr = (LinearItem * max(len(items), 1))()
@@ -288,7 +289,8 @@ def _items(items):
         arr[i] = LinearItem(ctypes.pointer(sh), _ptr(it["packed"]), it["packed_bytes"],
                             _ptr(it["X"]), it["ldx"], _ptr(it.get("Y")), it.get("ldy", 0),
                             it.get("ydtype", F32), it.get("accumulate", 0),
-                            it.get("sum_next", 0), it.get("rows", 0))
+                            it.get("sum_next", 0), it.get("rows", 0),
+                            _ptr(it.get("row_index")), it.get("x_rows", 0))
     arr._keep = keep
     return arr, len(items)
 

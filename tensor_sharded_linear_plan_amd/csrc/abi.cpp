@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <vector>
 
 #include "internal.hpp"
@@ -147,6 +148,12 @@ extern "C" tsl_status pack_shard(const tsl_shard *shard, tsl_dtype wdtype, const
     return from_hip(e);
 }
 
+// the item table's layout is part of the ABI
+static_assert(sizeof(tsl_linear_item) == 88 && offsetof(tsl_linear_item, rows) == 68 &&
+                  offsetof(tsl_linear_item, row_index) == 72 &&
+                  offsetof(tsl_linear_item, x_rows) == 80,
+              "tsl_linear_item layout");
+
 namespace {
 
 // Which kernel family serves a product of M rows.
@@ -255,10 +262,11 @@ std::vector<LinearItem> launch_order(const std::vector<LinearItem> &items) {
 // ranges of whole 128-k records (the activation pass writes each member's
 // binary16 activations at its k offset of the joined row, and the GEMM
 // reads each 128-k block's records from its member's packed buffer).
-// bf16 weights: k-ranges of whole 64-k stages and one activation row
-// stride (the GEMM reads each stage's activations and weights from its
-// member's own buffers).  Other sets, and every set of fp32 weights or of
-// the decode regime, pass unchanged.
+// bf16 weights: k-ranges of whole 64-k stages, activations not read through
+// a row index (the GEMM reads each stage's activations, at their member's
+// row stride, and weights from the member's own buffers).  The rule reads
+// nothing the workspace query does not see.  Other sets, and every set of
+// fp32 weights or of the decode regime, pass unchanged.
 std::vector<LinearItem> concat_sets(const std::vector<LinearItem> &in, tsl_dtype wdtype,
                                     int64_t M) {
     if ((wdtype != TSL_Q4G64 && wdtype != TSL_BF16) || use_skinny(wdtype, M))
@@ -272,7 +280,7 @@ std::vector<LinearItem> concat_sets(const std::vector<LinearItem> &in, tsl_dtype
                     (int64_t)len * in[i].g.Kpad < kPrefillMaxStride;
         for (size_t r = 0; join && r < len; ++r)
             join = in[i + r].g.Ks % unit == 0 && in[i + r].g.Ks == in[i].g.Ks &&
-                   (wdtype == TSL_Q4G64 || in[i + r].ldx == in[i].ldx);
+                   (wdtype == TSL_Q4G64 || !in[i + r].ridx);
         if (!join) {
             for (size_t r = 0; r < len; ++r)
                 out.push_back(in[i + r]);
@@ -290,10 +298,14 @@ std::vector<LinearItem> concat_sets(const std::vector<LinearItem> &in, tsl_dtype
         c.packed = nullptr;
         c.X = nullptr; // never shares an activation copy
         c.ldx = 0;
+        c.ridx = nullptr;
+        c.x_rows = 0;
         for (size_t r = 0; r < len; ++r) {
             c.seg_packed[r] = in[i + r].packed;
             c.seg_X[r] = in[i + r].X;
             c.seg_ldx[r] = in[i + r].ldx;
+            c.seg_ridx[r] = in[i + r].ridx;
+            c.seg_xrows[r] = in[i + r].x_rows;
         }
         out.push_back(c);
         i += len;
@@ -367,15 +379,56 @@ bool matrices_overlap(const void *pa, int64_t Ma, int64_t wa, int64_t lda, size_
     return same_row || next_row;
 }
 
+// Rows read through an index.  With 4-bit weights above 64 rows the
+// activation pass reads them where they lie; every other kernel reads its X
+// rows directly, so each distinct (X, ldx, k_len, row index, rows) is first
+// gathered into a dense copy at the front of the workspace (all of a
+// call's gathers in one launch), and the items read the copy.
+// Rewrites the indexed items of *items that need a gathered copy to read
+// it (ws + ...; null ws: sizing, every item its own copy) and returns the
+// bytes the copies take; *jobs receives the gathers to enqueue.
+size_t plan_row_gathers(std::vector<LinearItem> *items, tsl_dtype wdtype, int64_t M, char *ws,
+                        std::vector<RowGather> *jobs) {
+    if (wdtype == TSL_Q4G64 && !use_skinny(wdtype, M))
+        return 0;
+    const size_t e = wdtype == TSL_F32 ? 4 : 2;
+    const int64_t xa = wdtype == TSL_F32 ? 4 : 8; // row strides of 16 bytes
+    size_t off = 0;
+    for (LinearItem &L : *items) {
+        if (!L.ridx)
+            continue;
+        const int64_t Kc = (L.g.Ks + xa - 1) / xa * xa;
+        const RowGather *same = nullptr;
+        for (const RowGather &j : *jobs)
+            if (ws && j.X == L.X && j.ldx == L.ldx && j.ridx == L.ridx && j.x_rows == L.x_rows &&
+                j.M == L.M && j.Ks == L.g.Ks)
+                same = &j;
+        if (!same) {
+            jobs->push_back(RowGather{L.X, L.ldx, L.ridx, L.x_rows, L.M, L.g.Ks,
+                                      ws ? ws + off : nullptr, Kc});
+            off += ((size_t)L.M * (size_t)Kc * e + 255) / 256 * 256;
+            same = &jobs->back();
+        }
+        L.X = same->out;
+        L.ldx = Kc;
+        L.ridx = nullptr;
+        L.x_rows = 0;
+    }
+    return off;
+}
+
 // Workspace bytes of a validated group.
 size_t group_workspace(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_t M) {
     if (M == 0 || in.empty())
         return 0;
-    std::vector<LinearItem> items = launch_order(concat_sets(in, wdtype, M));
+    std::vector<LinearItem> src = in;
+    std::vector<RowGather> jobs;
+    const size_t gathered = plan_row_gathers(&src, wdtype, M, nullptr, &jobs);
+    std::vector<LinearItem> items = launch_order(concat_sets(src, wdtype, M));
     const size_t parts = split_sets(&items, M, nullptr);
     if (use_skinny(wdtype, M))
-        return parts + skinny_plan(items.data(), (int)items.size(), wdtype, M).ws_bytes;
-    return parts + prefill_plan(items.data(), (int)items.size(), wdtype, M).ws_bytes;
+        return gathered + parts + skinny_plan(items.data(), (int)items.size(), wdtype, M).ws_bytes;
+    return gathered + parts + prefill_plan(items.data(), (int)items.size(), wdtype, M).ws_bytes;
 }
 
 // Plans and enqueues a validated group.
@@ -383,10 +436,14 @@ tsl_status run_group(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_
                      void *workspace, size_t ws_bytes, void *stream) {
     if (M == 0)
         return TSL_OK;
-    const std::vector<LinearItem> ordered = launch_order(concat_sets(in, wdtype, M));
-    std::vector<LinearItem> items = ordered;
     // (a null or short workspace is rejected below, before any launch)
-    char *ws = static_cast<char *>(workspace);
+    char *const ws0 = static_cast<char *>(workspace);
+    std::vector<LinearItem> src = in;
+    std::vector<RowGather> gathers;
+    const size_t gathered = plan_row_gathers(&src, wdtype, M, ws0, &gathers);
+    char *ws = ws0 ? ws0 + gathered : nullptr; // the rank partials, then the plan's
+    const std::vector<LinearItem> ordered = launch_order(concat_sets(src, wdtype, M));
+    std::vector<LinearItem> items = ordered;
     const size_t parts = split_sets(&items, M, ws);
     const int n = (int)items.size();
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -397,11 +454,11 @@ tsl_status run_group(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_
     const bool skinny = use_skinny(wdtype, M);
     if (skinny) {
         sp = skinny_plan(items.data(), n, wdtype, M);
-        need = parts + sp.ws_bytes;
+        need = gathered + parts + sp.ws_bytes;
         blocks = skinny_blocks(sp, items.data(), n);
     } else {
         pp = prefill_plan(items.data(), n, wdtype, M);
-        need = parts + pp.ws_bytes;
+        need = gathered + parts + pp.ws_bytes;
         blocks = prefill_blocks(pp, items.data(), n, M);
     }
     if (blocks > kMaxBlocks)
@@ -416,6 +473,13 @@ tsl_status run_group(const std::vector<LinearItem> &in, tsl_dtype wdtype, int64_
     for (const LinearItem &L : items)
         if (!L.Y)
             return TSL_ERR_INVALID_ARG;
+    // the rows read through an index, gathered (an index outside [0, x_rows)
+    // gives a row of zeros)
+    if (!gathers.empty()) {
+        const hipError_t ge = launch_row_gathers(gathers, wdtype == TSL_F32 ? 4 : 2, s);
+        if (ge != hipSuccess)
+            return from_hip(ge);
+    }
     hipError_t e = skinny ? launch_skinny(sp, items.data(), n, wdtype, M, ws + parts, s)
                           : launch_prefill(pp, items.data(), n, wdtype, M, ws + parts, s);
     if (e != hipSuccess)
@@ -514,6 +578,14 @@ tsl_status gather(int32_t n_items, const tsl_linear_item *items, tsl_dtype wdtyp
         LinearItem &L = (*out)[i];
         L.set_pos = i - first;
         L.M = it.rows ? it.rows : M;
+        if (it.row_index) { // rows read through an index
+            if (it.x_rows < 1 || it.x_rows > INT32_MAX)
+                return TSL_ERR_INVALID_ARG;
+            if (!aligned(it.row_index, 4))
+                return TSL_ERR_MISALIGNED;
+            L.ridx = it.row_index;
+            L.x_rows = it.x_rows;
+        }
         if (member && (L.g.Ns != (*out)[first].g.Ns || L.M != (*out)[first].M))
             return TSL_ERR_INVALID_ARG;
         if (!it.sum_next) { // the set [first, i] is complete
@@ -540,7 +612,10 @@ tsl_status gather(int32_t n_items, const tsl_linear_item *items, tsl_dtype wdtyp
         for (int32_t j = 0; j < n_items; ++j) {
             const LinearItem &b = (*out)[j];
             const size_t eb = b.ydtype == TSL_F32 ? 4 : 2;
-            if (matrices_overlap(a.Y, a.M, a.g.Ns, a.ldy, ea, b.X, b.M, b.g.Ks, b.ldx, xe))
+            if (matrices_overlap(a.Y, a.M, a.g.Ns, a.ldy, ea, b.X, b.ridx ? b.x_rows : b.M, b.g.Ks,
+                                 b.ldx, xe))
+                return TSL_ERR_INVALID_ARG;
+            if (b.ridx && overlaps(a.Y, span(a.M, a.g.Ns, a.ldy, ea), b.ridx, (size_t)b.M * 4))
                 return TSL_ERR_INVALID_ARG;
             if (j > i && b.Y &&
                 matrices_overlap(a.Y, a.M, a.g.Ns, a.ldy, ea, b.Y, b.M, b.g.Ns, b.ldy, eb))
@@ -599,6 +674,8 @@ extern "C" tsl_status shard_linear_group_workspace_size(int32_t n_items,
         if (st != TSL_OK)
             return st;
         v[i].M = items[i].rows ? items[i].rows : M;
+        v[i].ridx = items[i].row_index; // only whether it is null matters here
+        v[i].x_rows = 1;
         v[i].set_pos = i - first;
         if (!items[i].sum_next || i == n_items - 1) {
             v[first].set_len = i - first + 1;

@@ -122,6 +122,10 @@ struct LinearItem {
     int set_pos = 0;
     // token rows of this product (the call's M unless the item sets its own)
     int64_t M = 0;
+    // row i of the product reads row ridx[i] of X (x_rows rows; an index
+    // outside [0, x_rows) reads zeros); null: row i
+    const int32_t *ridx = nullptr;
+    int64_t x_rows = 0;
     // the GEMM path may not split this product's k (a member of a sum set
     // too long for one sum launch)
     bool no_split = false;
@@ -132,13 +136,15 @@ struct LinearItem {
     int64_t fset_ldy = 0;
     tsl_dtype fset_ydtype = TSL_F32;
     // a sum set computed as ONE product over its members' k-ranges laid end
-    // to end in set order (4-bit weights, GEMM regime): cat members of equal
-    // k_len; g, Y, ldy, ydtype describe the joined product, seg_* each
-    // member's packed weights and activations (X and packed unused)
+    // to end in set order (GEMM regime): cat members of equal k_len; g, Y,
+    // ldy, ydtype describe the joined product, seg_* each member's packed
+    // weights and activations (X, ldx, ridx and packed unused)
     int cat = 1;
     const void *seg_packed[kSetParts] = {};
     const void *seg_X[kSetParts] = {};
     int64_t seg_ldx[kSetParts] = {};
+    const int32_t *seg_ridx[kSetParts] = {};
+    int64_t seg_xrows[kSetParts] = {};
 };
 
 // Workgroups per CU of the fused 4-bit GEMM for a bm x bn tile with wm row
@@ -173,6 +179,21 @@ inline int prefill_chunk_end(const LinearItem *items, int n, int c0) {
         joined += items[c1++].cat > 1 ? 1 : 0;
     return c1;
 }
+
+// A dense copy [M][ldo] of rows of X [x_rows][ldx] read through an index
+// (out row m = X row ridx[m], zeros when that lies outside [0, x_rows);
+// columns Ks .. ldo zero), for products whose kernels read X rows directly.
+struct RowGather {
+    const void *X;
+    int64_t ldx;
+    const int32_t *ridx;
+    int64_t x_rows, M, Ks;
+    void *out;
+    int64_t ldo;
+};
+// All of them, bit for bit, elem_bytes 2 or 4 (rows 16-byte aligned).
+hipError_t launch_row_gathers(const std::vector<RowGather> &jobs, size_t elem_bytes,
+                              hipStream_t stream);
 
 // ---- skinny.hip: decode-sized M (streams the weights once per 64 rows) ----
 struct SkinnyPlan {

@@ -84,10 +84,11 @@ struct GemmGroup {
     int64_t M;
     int32_t n, pad_;
     GemmItem it[kPrefillGroupMax];
-    // joined sum set j, member r: its packed weights and its activations
-    // (every member has the set's activation row stride)
+    // joined sum set j, member r: its packed weights, its activations and
+    // their row stride
     const char *segb[kMaxJoined][kSetParts];
     const char *segx[kMaxJoined][kSetParts];
+    int32_t segld[kMaxJoined][kSetParts];
 };
 
 // Tile geometry.  A stage covers BK k: 64, or 32 when three 64-k stages do
@@ -167,37 +168,43 @@ __global__ void __launch_bounds__(64 * WM * WN)
     // recomputed at every issue (a few VALU ops) rather than held in
     // registers.  Rows past M and columns past the shard are clamped to the
     // last valid ones: in bounds, and those outputs are never stored.
-    // Offsets stay below 2^32 because a tile spans at most 256 rows and the
+    // Offsets stay below 2^32 because a lane's row, clamped to the tile's
+    // last valid one before it meets the row stride, is below 256 and the
     // activation row stride and K are below 2^22 elements (checked by the
-    // caller); the clamp limit counts only the tile's own rows.
+    // caller).
     const int64_t t0 = n0 >> 4;
     // Where stage g of the product reads.  A joined sum set (R members of
     // equal k-range, spm stages each) runs the members' k-ranges end to
-    // end: stage g is stage g - r spm of member r.  Lane r of xr / br holds
-    // member r's activation and record bases for this tile (lane 0 a lone
-    // product's), picked per stage with v_readlane, so the block loop reads
-    // no table from memory.
+    // end: stage g is stage g - r spm of member r.  Lane r of xr / br / xl
+    // holds member r's activation and record bases for this tile and its
+    // activation row stride (lane 0 a lone product's), picked per stage
+    // with v_readlane, so the block loop reads no table from memory.
     const int spm = a.R > 1 ? nst_all / a.R : nst_all;
-    uint32_t xr[2], br[2];
+    uint32_t xr[2], br[2], xl;
     {
         const int seg = a.R > 1 ? a.seg : 0;
         const int r = lane < a.R ? lane : 0;
         const char *xm = a.R > 1 ? grp.segx[seg][r] : reinterpret_cast<const char *>(a.X);
         const char *wm0 = a.R > 1 ? grp.segb[seg][r] : reinterpret_cast<const char *>(a.B);
-        const uint64_t xv = (uint64_t)(uintptr_t)(xm + m0 * a.ldx * 2);
+        const int64_t ld = a.R > 1 ? (int64_t)grp.segld[seg][r] : a.ldx;
+        const uint64_t xv = (uint64_t)(uintptr_t)(xm + m0 * ld * 2);
         const uint64_t bv = (uint64_t)(uintptr_t)(wm0 + t0 * (int64_t)a.KT32 * 1024);
         xr[0] = (uint32_t)xv;
         xr[1] = (uint32_t)(xv >> 32);
         br[0] = (uint32_t)bv;
         br[1] = (uint32_t)(bv >> 32);
+        xl = (uint32_t)ld;
     }
-    // the activation and record bases of stage kt of this split
-    auto src = [&](int kt, const char *&xs, const char *&bs) __attribute__((always_inline)) {
+    // the activation and record bases and the activation row stride of
+    // stage kt of this split
+    auto src = [&](int kt, const char *&xs, const char *&bs, uint32_t &xld)
+                   __attribute__((always_inline)) {
         int r = 0, gl = kt + kb;
         while (gl >= spm) { // uniform, at most R - 1 + NS / spm steps
             gl -= spm;
             ++r;
         }
+        xld = (uint32_t)__builtin_amdgcn_readlane((int)xl, r);
         const uint64_t xv = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)xr[0], r) |
                             ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)xr[1], r) << 32);
         const uint64_t bv = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)br[0], r) |
@@ -207,10 +214,8 @@ __global__ void __launch_bounds__(64 * WM * WN)
     };
     const int arow = lane / C::CPR; // row of this lane in its block
     const uint32_t chunk = 8 * ((lane % C::CPR) ^ swz<C::CPR>(arow));
-    const uint32_t aoff0 = ((uint32_t)(C::RPB * wave + arow) * (uint32_t)a.ldx + chunk) * 2;
-    const uint32_t astep = C::NW * C::RPB * (uint32_t)a.ldx * 2;
-    const int64_t last_row = M - 1 - m0 < BM - 1 ? M - 1 - m0 : BM - 1;
-    const uint32_t alim = ((uint32_t)last_row * (uint32_t)a.ldx + chunk) * 2;
+    const uint32_t arow0 = (uint32_t)(C::RPB * wave + arow); // in copy 0
+    const uint32_t last_row = (uint32_t)(M - 1 - m0 < BM - 1 ? M - 1 - m0 : BM - 1);
     const int kr = 2 * (wave % C::S16) + (lane >> 5); // 8-k run of this wave's weight blocks
     const uint32_t boff0 = ((uint32_t)((kr >> 2) * 64 + (kr & 3) * 16 + (lane & 15))) * 16;
     const uint32_t tstep = (uint32_t)a.KT32 * 1024; // one 16-column tile
@@ -219,15 +224,15 @@ __global__ void __launch_bounds__(64 * WM * WN)
     constexpr int TPJ = 2 * (C::NW / C::S16); // 16-column tiles per weight block step
     const uint32_t lds0 = (uint32_t)(uintptr_t)(void __attribute__((address_space(3))) *)lds;
     // copy j (0 <= j < FPW) of this wave for the stage whose bases are xs,
-    // bs into LDS slot `slot`
-    auto issue1 = [&](const char *xs, const char *bs, int slot, int j)
+    // bs (activation row stride xld) into LDS slot `slot`
+    auto issue1 = [&](const char *xs, const char *bs, uint32_t xld, int slot, int j)
                       __attribute__((always_inline)) {
         const uint32_t dst = lds0 + slot * C::STAGE + wave * 1024 + C::NW * j * 1024;
-        uint32_t a0 = aoff0, b0 = boff0;
+        uint32_t a0 = arow0, b0 = boff0;
         asm volatile("" : "+v"(a0), "+v"(b0)); // keep the per-j offsets out of registers
         if (j < C::AF / C::NW) {
-            const uint32_t o = a0 + (uint32_t)j * astep;
-            dma16(xs, o < alim ? o : alim, dst);
+            const uint32_t row = a0 + (uint32_t)(j * C::NW * C::RPB);
+            dma16(xs, ((row < last_row ? row : last_row) * xld + chunk) * 2, dst);
         } else {
             const int tt = tfirst + TPJ * (j - C::AF / C::NW);
             dma16(bs, b0 + (uint32_t)(tt < tmax ? tt : tmax) * tstep, dst);
@@ -235,10 +240,11 @@ __global__ void __launch_bounds__(64 * WM * WN)
     };
     auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
         const char *xs, *bs;
-        src(kt, xs, bs);
+        uint32_t xld;
+        src(kt, xs, bs, xld);
 #pragma unroll
         for (int j = 0; j < C::FPW; ++j)
-            issue1(xs, bs, slot, j);
+            issue1(xs, bs, xld, slot, j);
     };
 
     f32x16 acc[C::MT][C::NT];
@@ -289,6 +295,7 @@ __global__ void __launch_bounds__(64 * WM * WN)
     for (int kt = 0; kt < nst; ++kt) {
         const int next = slot + 1 == C::NS ? 0 : slot + 1;
         const char *cxs = nullptr, *cbs = nullptr; // stage kt + NS's bases
+        uint32_t cxld = 0;
 #pragma unroll
         for (int s = 0; s < C::S16; ++s) {
             const int b = s & 1; // S16 is even, so step parity is s parity
@@ -305,7 +312,7 @@ __global__ void __launch_bounds__(64 * WM * WN)
                     rd(next, 0, af[b ^ 1], bfr[b ^ 1]);
                     copies = kt + C::NS < nst;
                     if (copies)
-                        src(kt + C::NS, cxs, cbs);
+                        src(kt + C::NS, cxs, cbs, cxld);
                 }
             }
             // the copies of stage kt + NS go into the slot of stage kt,
@@ -320,7 +327,7 @@ __global__ void __launch_bounds__(64 * WM * WN)
 #pragma unroll
                     for (int f = q * C::FPW / (C::MT * C::NT); f < (q + 1) * C::FPW / (C::MT * C::NT); ++f)
                         if (copies)
-                            issue1(cxs, cbs, slot, f);
+                            issue1(cxs, cbs, cxld, slot, f);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -384,9 +391,13 @@ __global__ void __launch_bounds__(64 * WM * WN)
 // (kActExpBias below its ilogb), every element becomes x 2^-e_m rounded to
 // nearest binary16, and e_m goes to rexp[m].  Plain copies (bf16 weights
 // with ragged K) only zero-pad.  Segment r is the piece at pos r of the
-// job; columns past its Ks up to Kw are zero.
+// job; columns past its Ks up to Kw are zero.  A segment with a row index
+// reads its row m from row ridx[m] of x_in (a row of zeros when that lies
+// outside [0, x_rows)).
 struct XPiece {
     const uint16_t *x_in;
+    const int32_t *ridx; // null: row m of x_in
+    int64_t x_rows;
     uint16_t *x_out;  // this segment's first output column
     int32_t *rexp;    // row exponents (binary16 copy), null for a plain copy
     int64_t ldx_in;
@@ -411,8 +422,9 @@ __device__ __forceinline__ uint32_t pair_max_abs(uint32_t m, uint32_t v) {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
 }
 
-__global__ void __launch_bounds__(256) xprep_kernel(XPrepGroup grp) {
-    __shared__ uint32_t red[4];
+// The rows of one launch: its jobs' pieces in grp.it[0 .. grp.n).
+template <class Group>
+__device__ __forceinline__ void xprep_rows(const Group &grp, uint32_t *red) {
     const int bid = blockIdx.x;
     int lo = 0, hi = grp.n - 1;
     while (lo < hi) {
@@ -434,12 +446,24 @@ __global__ void __launch_bounds__(256) xprep_kernel(XPrepGroup grp) {
     if (m >= j0.M)
         return; // narrow jobs only (a wide job's workgroups are its rows): no barrier follows
     const bool to_f16 = j0.rexp != nullptr;
+    // the source row of segment p (null: a row of zeros)
+    auto src_row = [&](const XPiece &p) -> const uint16_t * {
+        int64_t row = m;
+        if (p.ridx) {
+            row = p.ridx[m];
+            if (row < 0 || row >= p.x_rows)
+                return nullptr;
+        }
+        return p.x_in + row * p.ldx_in;
+    };
     int e = 0;
     if (to_f16) {
         uint32_t mx = 0;
         for (int r = 0; r < j0.R; ++r) {
             const XPiece &p = grp.it[first + r];
-            const uint16_t *src = p.x_in + m * p.ldx_in;
+            const uint16_t *src = src_row(p);
+            if (!src)
+                continue;
             for (int k = tid * 8; k < p.Ks; k += nthr * 8) {
                 if (k + 8 <= p.Ks) {
                     const u32x4 v = *reinterpret_cast<const u32x4 *>(src + k);
@@ -476,17 +500,18 @@ __global__ void __launch_bounds__(256) xprep_kernel(XPrepGroup grp) {
     }
     for (int r = 0; r < j0.R; ++r) {
         const XPiece &p = grp.it[first + r];
-        const uint16_t *src = p.x_in + m * p.ldx_in;
+        const uint16_t *src = src_row(p);
+        const int ks = src ? p.Ks : 0; // columns read
         uint16_t *dst = p.x_out + m * (int64_t)p.x_ld;
         for (int k = tid * 8; k < p.Kw; k += nthr * 8) {
             u32x4 v = {0, 0, 0, 0};
-            if (k + 8 <= p.Ks) {
+            if (k + 8 <= ks) {
                 v = *reinterpret_cast<const u32x4 *>(src + k);
-            } else if (k < p.Ks) {
+            } else if (k < ks) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const uint32_t lo2 = (k + 2 * q < p.Ks) ? src[k + 2 * q] : 0u;
-                    const uint32_t hi2 = (k + 2 * q + 1 < p.Ks) ? src[k + 2 * q + 1] : 0u;
+                    const uint32_t lo2 = (k + 2 * q < ks) ? src[k + 2 * q] : 0u;
+                    const uint32_t hi2 = (k + 2 * q + 1 < ks) ? src[k + 2 * q + 1] : 0u;
                     v[q] = lo2 | (hi2 << 16);
                 }
             }
@@ -503,6 +528,25 @@ __global__ void __launch_bounds__(256) xprep_kernel(XPrepGroup grp) {
             *reinterpret_cast<u32x4 *>(dst + k) = v;
         }
     }
+}
+
+__global__ void __launch_bounds__(256) xprep_kernel(XPrepGroup grp) {
+    __shared__ uint32_t red[4];
+    xprep_rows(grp, red);
+}
+
+// Row gathers (plain copies through a row index) take a short job table:
+// a call has few distinct gathers, and a launch's arguments are copied
+// whole whatever the table holds.
+constexpr int kGatherJobs = 16;
+struct GatherGroup {
+    int32_t n, pad_;
+    XPiece it[kGatherJobs];
+};
+
+__global__ void __launch_bounds__(256) gather_rows_kernel(GatherGroup grp) {
+    __shared__ uint32_t red[4];
+    xprep_rows(grp, red);
 }
 
 typedef void (*GemmFn)(GemmGroup);
@@ -783,6 +827,7 @@ PrefillPlan prefill_plan(const LinearItem *items, int n, tsl_dtype wdtype, int64
             int first = i;
             for (int j = 0; j < i && items[i].X; ++j)
                 if (items[j].X == items[i].X && items[j].ldx == items[i].ldx &&
+                    items[j].ridx == items[i].ridx && items[j].x_rows == items[i].x_rows &&
                     items[j].g.Ks == g.Ks && items[j].M == items[i].M && best.x_first[j] == j) {
                     first = j;
                     break;
@@ -826,6 +871,8 @@ hipError_t launch_xprep(const PrefillPlan &p, const LinearItem *items, int c0, i
             XPiece x{};
             x.x_in = static_cast<const uint16_t *>(R > 1 ? L.seg_X[r] : L.X);
             x.ldx_in = R > 1 ? L.seg_ldx[r] : L.ldx;
+            x.ridx = R > 1 ? L.seg_ridx[r] : L.ridx;
+            x.x_rows = R > 1 ? L.seg_xrows[r] : L.x_rows;
             x.x_out = reinterpret_cast<uint16_t *>(ws + p.x_off[i]) + r * kseg;
             // row exponents right after the copy's M rows
             x.rexp = q4 ? reinterpret_cast<int32_t *>(reinterpret_cast<uint16_t *>(ws + p.x_off[i]) +
@@ -860,6 +907,63 @@ hipError_t launch_xprep(const PrefillPlan &p, const LinearItem *items, int c0, i
         }
         if (blocks > 0) {
             hipLaunchKernelGGL(xprep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, xg);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+        q0 = q;
+    }
+    return hipSuccess;
+}
+
+// Row gathers: plain copies (no binary16) through the activation pass's
+// row code, a 16-bit word of the copy per element half of fp32 data.  Jobs
+// that continue one another -- the same X, the next run of the index, the
+// next rows of one copy (the per-expert runs of a routing's row layout) --
+// merge into one.
+hipError_t launch_row_gathers(const std::vector<RowGather> &jobs, size_t elem_bytes,
+                              hipStream_t stream) {
+    const int64_t h = (int64_t)elem_bytes / 2; // 16-bit words per element
+    std::vector<RowGather> merged;
+    for (const RowGather &g : jobs) {
+        if (!merged.empty()) {
+            RowGather &m = merged.back();
+            if (m.X == g.X && m.ldx == g.ldx && m.x_rows == g.x_rows && m.Ks == g.Ks &&
+                m.ldo == g.ldo && m.ridx + m.M == g.ridx &&
+                static_cast<char *>(m.out) + m.M * m.ldo * (int64_t)elem_bytes == g.out &&
+                m.M + g.M <= INT32_MAX) {
+                m.M += g.M;
+                continue;
+            }
+        }
+        merged.push_back(g);
+    }
+    for (size_t q0 = 0; q0 < merged.size();) {
+        GatherGroup xg{};
+        int64_t blocks = 0;
+        size_t q = q0;
+        for (; q < merged.size() && xg.n < kGatherJobs; ++q) {
+            const RowGather &g = merged[q];
+            XPiece &x = xg.it[xg.n++];
+            x.x_in = static_cast<const uint16_t *>(g.X);
+            x.ridx = g.ridx;
+            x.x_rows = g.x_rows;
+            x.ldx_in = g.ldx * h;
+            x.x_out = static_cast<uint16_t *>(g.out);
+            x.rexp = nullptr;
+            x.x_ld = (int32_t)(g.ldo * h);
+            x.Ks = (int32_t)(g.Ks * h);
+            x.Kw = (int32_t)(g.ldo * h);
+            x.R = 1;
+            x.pos = 0;
+            x.M = (int32_t)g.M;
+            x.start = (int32_t)blocks;
+            x.wide = x.Kw >= kXPrepWideColumns ? 1 : 0;
+            blocks += x.wide ? g.M : (g.M + 3) / 4;
+        }
+        if (blocks > 0) {
+            hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                               xg);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess)
                 return e;
@@ -905,6 +1009,7 @@ hipError_t launch_prefill(const PrefillPlan &p, const LinearItem *items, int n, 
                 for (int r = 0; r < L.cat; ++r) {
                     grp.segb[a.seg][r] = static_cast<const char *>(L.seg_packed[r]);
                     grp.segx[a.seg][r] = static_cast<const char *>(L.seg_X[r]);
+                    grp.segld[a.seg][r] = (int32_t)L.seg_ldx[r];
                 }
                 a.B = static_cast<const u32x4 *>(L.seg_packed[0]);
                 a.X = static_cast<const uint16_t *>(L.seg_X[0]);

@@ -52,10 +52,12 @@ def test_shard_struct_layout_matches_header(tsl_lib):
     assert ctypes.sizeof(tsl_lib.Shard) == 72
     assert tsl_lib.Shard.K.offset == 16 and tsl_lib.Shard.head_off.offset == 64
     assert ctypes.sizeof(tsl_lib.Dims) == 28
-    # tsl_linear_item: seven 8-byte fields, then four int32
-    assert ctypes.sizeof(tsl_lib.LinearItem) == 72
+    # tsl_linear_item: seven 8-byte fields, four int32, then the row index
+    # pointer and x_rows
+    assert ctypes.sizeof(tsl_lib.LinearItem) == 88
     assert tsl_lib.LinearItem.ldy.offset == 48 and tsl_lib.LinearItem.ydtype.offset == 56
     assert tsl_lib.LinearItem.sum_next.offset == 64 and tsl_lib.LinearItem.rows.offset == 68
+    assert tsl_lib.LinearItem.row_index.offset == 72 and tsl_lib.LinearItem.x_rows.offset == 80
 
 
 def _lib_plan(tsl_lib, hidden, hq, hkv, hd, ffn, tp, group=0):
@@ -410,25 +412,29 @@ def test_sum_set_rules(tsl_lib):
 
 def test_bf16_sum_sets_join_in_the_gemm_regime(tsl_lib):
     """bf16 weights above 64 rows: a sum set whose members hold whole 64-k
-    stages and share one activation row stride is one product over the
-    members' k-ranges end to end -- the workspace of the unsharded product,
-    no rank partials; a member with another row stride keeps the set's
-    binary32 rank partials (M x N x 4 bytes per member at least)."""
+    stages is one product over the members' k-ranges end to end -- the
+    workspace of the unsharded product, no rank partials, whatever the
+    members' activation row strides (the workspace query does not see
+    them); a member read through a row index first has its rows gathered
+    into the workspace (M x k_len x 2 bytes), and the set still joins."""
     K, N, tp, M = 2048, 512, 4, 256
     sh = tsl_lib.plan_linear(K, N, tp, tsl_lib.ROW, 64)
     nb = tsl_lib.pack_shard_size(sh[0], tsl_lib.BF16)
     X, Y = 1 << 26, 1 << 27
 
-    def items(ldx0=K):
+    def items(ldx0=K, **kw):
         return [dict(shard=s, packed=(1 << 24) + r * (1 << 20), packed_bytes=nb,
                      X=X + 2 * s.k_off, ldx=ldx0 if r == 0 else K, Y=Y if r == 0 else None,
-                     ldy=N, sum_next=1 if r < tp - 1 else 0) for r, s in enumerate(sh)]
+                     ldy=N, sum_next=1 if r < tp - 1 else 0, **(kw if r == 1 else {}))
+                for r, s in enumerate(sh)]
 
     full = tsl_lib.plan_linear(K, N, 1, tsl_lib.ROW, 64)[0]
     ws = tsl_lib.shard_linear_group_workspace_size
-    assert ws(items(), tsl_lib.BF16, M) == tsl_lib.shard_linear_workspace_size(
-        full, tsl_lib.BF16, M)
-    assert ws(items(K + 64), tsl_lib.BF16, M) >= tp * M * N * 4
+    joined = tsl_lib.shard_linear_workspace_size(full, tsl_lib.BF16, M)
+    assert ws(items(), tsl_lib.BF16, M) == joined
+    assert ws(items(K + 64), tsl_lib.BF16, M) == joined
+    indexed = ws(items(row_index=1 << 28, x_rows=M), tsl_lib.BF16, M)
+    assert indexed == joined + M * (K // tp) * 2
     # decode-sized calls never join: the rank partials are there
     assert ws(items(), tsl_lib.BF16, 16) >= tp * 16 * N * 4
 

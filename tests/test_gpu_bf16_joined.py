@@ -1,12 +1,13 @@
 """bf16 weights above 64 rows: a sum set of row shards (mlxcel manual
 "Tensor parallelism", "Row Parallel": the ranks' partial products added
-into one output) whose members' k-ranges are whole 64-k stages and share
-one activation row stride runs as one GEMM over the members' k-ranges end
-to end -- the rank sum happens inside the GEMM, with no binary32 rank
-partials.  Such a set gives bit for bit the unsharded product of the same
-plan (the same k-splits, so the same accumulation order) and the oracle's
-rank sum to the bf16 tolerance; sets that cannot be joined keep the
-partials and give the members' products followed by the ordered sum."""
+into one output) whose members' k-ranges are whole 64-k stages runs as one
+GEMM over the members' k-ranges end to end -- the rank sum happens inside
+the GEMM, with no binary32 rank partials, each member's activations read
+at their own row stride.  Such a set gives bit for bit the unsharded
+product of the same plan (the same k-splits, so the same accumulation
+order) and the oracle's rank sum to the bf16 tolerance; a set that cannot
+be joined keeps the partials and gives the members' products followed by
+the ordered sum."""
 import numpy as np
 import pytest
 
@@ -102,36 +103,53 @@ def test_joined_bf16_members_in_their_own_buffers():
     assert normwise(host(Y), ref) <= TOL
 
 
-@pytest.mark.parametrize("M,K,N,tp,odd", [(300, 4096, 640, 4, "stride"),
-                                          (200, 1152, 512, 4, "k")])
-def test_bf16_sum_sets_that_are_not_joined(M, K, N, tp, odd):
-    """A member with another activation row stride, or members whose
-    k-ranges are not whole 64-k stages (K = 1152 over 4 ranks: 288 k):
-    the set keeps its binary32 rank partials -- bit for bit the members'
-    products followed by combine_partials(SUM), and the oracle's sum."""
+def test_joined_bf16_members_with_different_row_strides():
+    """Member 0 reads its activations from a wider copy (row stride
+    K + 64), the others from X (stride K): the set still joins (its
+    members' strides travel with their bases) -- bit for bit the unsharded
+    product over X."""
     t = torch()
+    M, K, N, tp = 300, 4096, 640, 4
     Wb, Xb = weights_and_input(M, K, N, 8300 + K, False)
-    dW = dev(Wb)
-    shards = tsl.plan_linear(K, N, tp, tsl.ROW, 0 if odd == "k" else 64)
-    if odd == "k":
-        assert all(sh.k_len == K // tp and sh.k_len % 64 for sh in shards)
+    dW, dX = dev(Wb), dev(Xb)
+    shards = tsl.plan_linear(K, N, tp, tsl.ROW, 64)
     packs = [pack(sh, tsl.BF16, dW, N, 1) for sh in shards]
-    dX = dev(Xb)
     wide = np.zeros((M, K + 64), dtype=np.uint16)
     wide[:, :K] = Xb
     dWide = dev(wide)
-    # member 0 reads its rows from the wider copy when the strides differ
-    xs = [(dWide if (odd == "stride" and r == 0) else dX, K + 64 if (odd == "stride" and r == 0)
-           else K) for r in range(tp)]
+    full = tsl.plan_linear(K, N, 1, tsl.ROW, 64)[0]
+    fbuf, fnb = pack(full, tsl.BF16, dW, N, 1)
+    want = t.full((M, N), float("nan"), dtype=t.float32, device="cuda")
+    run_group([dict(shard=full, packed=fbuf, packed_bytes=fnb, X=dX, ldx=K, Y=want, ldy=N)], M)
+    Y = t.full((M, N), float("nan"), dtype=t.float32, device="cuda")
+    run_group([dict(shard=sh, packed=b, packed_bytes=nb,
+                    X=(dWide if r == 0 else dX)[:, sh.k_off:], ldx=K + 64 if r == 0 else K,
+                    Y=Y if r == 0 else None, ldy=N, sum_next=int(r < tp - 1))
+               for r, (sh, (b, nb)) in enumerate(zip(shards, packs))], M)
+    assert t.equal(Y, want)
+
+
+def test_bf16_sum_set_that_is_not_joined():
+    """Members whose k-ranges are not whole 64-k stages (K = 1152 over 4
+    ranks: 288 k): the set keeps its binary32 rank partials -- bit for bit
+    the members' products followed by combine_partials(SUM), and the
+    oracle's sum."""
+    t = torch()
+    M, K, N, tp = 200, 1152, 512, 4
+    Wb, Xb = weights_and_input(M, K, N, 8300 + K, False)
+    dW, dX = dev(Wb), dev(Xb)
+    shards = tsl.plan_linear(K, N, tp, tsl.ROW, 0)
+    assert all(sh.k_len == K // tp and sh.k_len % 64 for sh in shards)
+    packs = [pack(sh, tsl.BF16, dW, N, 1) for sh in shards]
     ps = [t.full((M, N), float("nan"), dtype=t.float32, device="cuda") for _ in shards]
-    run_group([dict(shard=sh, packed=b, packed_bytes=nb, X=x[:, sh.k_off:], ldx=ld, Y=P, ldy=N)
-               for sh, (b, nb), (x, ld), P in zip(shards, packs, xs, ps)], M)
+    run_group([dict(shard=sh, packed=b, packed_bytes=nb, X=dX[:, sh.k_off:], ldx=K, Y=P, ldy=N)
+               for sh, (b, nb), P in zip(shards, packs, ps)], M)
     want = t.empty((M, N), dtype=t.float32, device="cuda")
     tsl.combine_partials(tsl.COMBINE_SUM, ps, tsl.F32, M, N, N, tsl.F32, want, N)
     Y = t.full((M, N), float("nan"), dtype=t.float32, device="cuda")
-    run_group([dict(shard=sh, packed=b, packed_bytes=nb, X=x[:, sh.k_off:], ldx=ld,
+    run_group([dict(shard=sh, packed=b, packed_bytes=nb, X=dX[:, sh.k_off:], ldx=K,
                     Y=Y if r == 0 else None, ldy=N, sum_next=int(r < tp - 1))
-               for r, (sh, (b, nb), (x, ld)) in enumerate(zip(shards, packs, xs))], M)
+               for r, (sh, (b, nb)) in enumerate(zip(shards, packs))], M)
     assert t.equal(Y, want)
     ref = oracle.gemm(oracle.bf16_to_f64(Xb), oracle.bf16_to_f64(Wb))
     assert normwise(host(Y), ref) <= TOL
