@@ -349,8 +349,8 @@ tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, const void *pa
  * in the workspace (rows x n_len x 4 bytes each, counted by
  * shard_linear_group_workspace_size); one more launch adds them.
  * Exception, M > 64: a set of at most 8 members whose k_len are equal
- * multiples of 128 (Q4G64 weights), or equal multiples of 64 with equal
- * ldx (BF16 weights), is ONE product over the members'
+ * multiples of 128 (Q4G64 weights) or of 64 (BF16 weights) is ONE product
+ * over the members'
  * k-ranges laid end to end in item order, Y = [X_0 X_1 ...] [W_0; W_1; ...]
  * -- the same sum, accumulated in binary32 in that k order inside the GEMM
  * and rounded once (bit for bit the product of the unsharded weight over
