@@ -457,6 +457,59 @@ __device__ __forceinline__ void xprep_rows(const Group &grp, uint32_t *red) {
         return p.x_in + row * p.ldx_in;
     };
     int e = 0;
+    // a narrow lone row of up to 2048 columns: read once into registers,
+    // then its largest magnitude and its binary16 copy from them
+    if (to_f16 && !wide && j0.R == 1 && j0.Kw <= 4 * 64 * 8) {
+        const uint16_t *src = src_row(j0);
+        const int ks = src ? j0.Ks : 0; // columns read
+        u32x4 v[4];
+        uint32_t mx = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = tid * 8 + i * 64 * 8;
+            v[i] = u32x4{0, 0, 0, 0};
+            if (k + 8 <= ks) {
+                v[i] = *reinterpret_cast<const u32x4 *>(src + k);
+            } else if (k < ks) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t lo2 = (k + 2 * q < ks) ? src[k + 2 * q] : 0u;
+                    const uint32_t hi2 = (k + 2 * q + 1 < ks) ? src[k + 2 * q + 1] : 0u;
+                    v[i][q] = lo2 | (hi2 << 16);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                mx = pair_max_abs(mx, v[i][q]); // zero columns leave it as it is
+        }
+        uint32_t h = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const uint32_t x = __shfl_xor(h, o, 64);
+            h = x > h ? x : h;
+        }
+        if (h != 0 && h < 0x7F80u)
+            e = __builtin_amdgcn_frexp_expf(__uint_as_float(h << 16)) - 1 - kActExpBias;
+        if (tid == 0)
+            j0.rexp[m] = e;
+        uint16_t *dst = j0.x_out + m * (int64_t)j0.x_ld;
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = tid * 8 + i * 64 * 8;
+            if (k < j0.Kw) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    h2 o;
+                    o.x = (_Float16)__builtin_amdgcn_ldexpf(bf16_lo(v[i][q]), -e);
+                    o.y = (_Float16)__builtin_amdgcn_ldexpf(bf16_hi(v[i][q]), -e);
+                    v[i][q] = __builtin_bit_cast(uint32_t, o);
+                }
+                *reinterpret_cast<u32x4 *>(dst + k) = v[i];
+            }
+        }
+        return;
+    }
     if (to_f16) {
         uint32_t mx = 0;
         for (int r = 0; r < j0.R; ++r) {
