@@ -271,7 +271,9 @@ tsl_status pack_shard(const tsl_shard *shard, tsl_dtype wdtype, const void *W, i
 /*
  * shard_linear_workspace_size -- workspace bytes shard_linear needs for
  * this shard, weight type and row count (0 when none is needed): split-K
- * partial sums for decode-sized M; with M > 64, for 4-bit weights a
+ * partial sums for decode-sized M (every M for F32 weights, M <= 64 for
+ * Q4G64, M <= 32 for BF16: the weights are streamed); above that (the
+ * GEMM regime), for 4-bit weights a
  * binary16 copy of the activations (M x k_len x 2 bytes, k_len rounded up
  * to 64) and their row exponents (4 bytes per row, rows rounded up to 256)
  * -- the weights stay packed -- for BF16 weights a zero-padded copy of
@@ -315,8 +317,9 @@ tsl_status shard_linear_workspace_size(const tsl_shard *shard, tsl_dtype wdtype,
  * <= 2^-11); smaller ones carry an absolute error of at most 2^(e_m - 25)
  * (2^(f_n - 25)).  Non-finite inputs give non-finite outputs.  M may be 0
  * (nothing is enqueued).
- * BF16 and Q4G64 weights with M > 64 require ldx and the shard's K below
- * 2^22 elements (else TSL_ERR_UNSUPPORTED).
+ * BF16 weights with M > 32 and Q4G64 weights with M > 64 (the GEMM regime)
+ * require ldx and the shard's K below 2^22 elements (else
+ * TSL_ERR_UNSUPPORTED).
  * Errors: TSL_ERR_INVALID_ARG, TSL_ERR_UNSUPPORTED,
  * TSL_ERR_BUFFER_TOO_SMALL, TSL_ERR_MISALIGNED (X, Y 16-byte aligned;
  * ldx, ldy multiples of 8 for 16-bit and of 4 for 32-bit types), TSL_ERR_HIP.
@@ -348,10 +351,10 @@ tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, const void *pa
  * a call has sum_next = 0.  The products of a set go to binary32 partials
  * in the workspace (rows x n_len x 4 bytes each, counted by
  * shard_linear_group_workspace_size); one more launch adds them.
- * Exception, M > 64: a set of at most 8 members whose k_len are equal
- * multiples of 128 (Q4G64 weights) or of 64 (BF16 weights) is ONE product
- * over the members'
- * k-ranges laid end to end in item order, Y = [X_0 X_1 ...] [W_0; W_1; ...]
+ * Exception, the GEMM regime (M > 64 for Q4G64, M > 32 for BF16): a set of
+ * at most 8 members whose k_len are equal multiples of 128 (Q4G64 weights)
+ * or of 64 (BF16 weights) is ONE product over the members' k-ranges laid
+ * end to end in item order, Y = [X_0 X_1 ...] [W_0; W_1; ...]
  * -- the same sum, accumulated in binary32 in that k order inside the GEMM
  * and rounded once (bit for bit the product of the unsharded weight over
  * the whole X when the members are the row shards of one weight), with no

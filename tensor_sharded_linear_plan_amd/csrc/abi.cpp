@@ -157,7 +157,9 @@ static_assert(sizeof(tsl_linear_item) == 88 && offsetof(tsl_linear_item, rows) =
 namespace {
 
 // Which kernel family serves a product of M rows.
-bool use_skinny(tsl_dtype wdtype, int64_t M) { return wdtype == TSL_F32 || M <= kSkinnyMaxM; }
+bool use_skinny(tsl_dtype wdtype, int64_t M) {
+    return wdtype == TSL_F32 || M <= (wdtype == TSL_BF16 ? kSkinnyMaxMBf16 : kSkinnyMaxM);
+}
 
 // Most items one grouped call takes.
 constexpr int32_t kMaxItems = 4096;

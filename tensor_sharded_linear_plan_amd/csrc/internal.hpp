@@ -266,7 +266,13 @@ hipError_t launch_q4_gemm(const PrefillPlan &p, const LinearItem *items, int n, 
 // the prefill path, which keeps its 32-bit operand offsets in range.
 constexpr int64_t kPrefillMaxStride = int64_t(1) << 22;
 
-// Rows at or below which shard_linear takes the skinny (decode) path.
+// Rows at or below which shard_linear takes the skinny (decode) path: 64
+// for 4-bit weights (whose GEMM regime is 2x slower at 4 and 16 rows);
+// 32 for bf16 weights, whose GEMM (one 64-row tile per column tile, the
+// weights streamed once) is faster from about 32 rows on (gqa8 layer,
+// M = 32 / 64: 111 / 113 -> 97 / 101 us; llama2k M = 64: 38 -> 35 us;
+// llama2k M = 16 / 24 stay faster streamed: 26 / 30 vs 34 / 36 us).
 constexpr int64_t kSkinnyMaxM = 64;
+constexpr int64_t kSkinnyMaxMBf16 = 32;
 
 } // namespace tsl
