@@ -382,10 +382,11 @@ tsl_status shard_linear(const tsl_shard *shard, tsl_dtype wdtype, const void *pa
  * index outside [0, x_rows) reads a row of zeros.  The tokens routed to an
  * expert are read where they lie, with no gather pass of their own
  * ([mlxcel] "MoE expert parallelization"; moe_gather's idx has the same
- * meaning): with Q4G64 weights above 64 rows the activation pass reads
- * them; otherwise the call first gathers each distinct (X, ldx, k_len,
- * row_index, rows) into its workspace (a bf16 / fp32 copy, zeros for
- * out-of-range rows).  row_index must be 4-byte aligned and must not
+ * meaning): with Q4G64 weights above 64 rows, and in calls of a few
+ * decode-sized rows whose activations the streaming kernel keeps in LDS,
+ * the kernels read them where they lie; otherwise the call first gathers
+ * each distinct (X, ldx, k_len, row_index, rows) into its workspace (a
+ * bf16 / fp32 copy, zeros for out-of-range rows).  row_index must be 4-byte aligned and must not
  * overlap any output; x_rows is ignored when row_index is null.
  */
 typedef struct {

@@ -381,17 +381,24 @@ bool matrices_overlap(const void *pa, int64_t Ma, int64_t wa, int64_t lda, size_
     return same_row || next_row;
 }
 
-// Rows read through an index.  With 4-bit weights above 64 rows the
-// activation pass reads them where they lie; every other kernel reads its X
-// rows directly, so each distinct (X, ldx, k_len, row index, rows) is first
-// gathered into a dense copy at the front of the workspace (all of a
-// call's gathers in one launch), and the items read the copy.
+// Rows read through an index.  The 4-bit activation pass (GEMM regime) and
+// the resident streaming kernel (a few decode rows, bf16 and 4-bit
+// weights) read them where they lie; the other kernels read X rows at
+// fixed strides, so for them each distinct (X, ldx, k_len, row index,
+// rows) is first gathered into a dense copy at the front of the workspace
+// (all of a call's gathers in one launch), and the items read the copy.
 // Rewrites the indexed items of *items that need a gathered copy to read
 // it (ws + ...; null ws: sizing, every item its own copy) and returns the
 // bytes the copies take; *jobs receives the gathers to enqueue.
 size_t plan_row_gathers(std::vector<LinearItem> *items, tsl_dtype wdtype, int64_t M, char *ws,
                         std::vector<RowGather> *jobs) {
+    // the 4-bit activation pass reads through the index itself, and so do
+    // the streaming kernels that hold a call's rows in LDS (a few rows: the
+    // plan's resident calls, decided by the items' shapes alone)
     if (wdtype == TSL_Q4G64 && !use_skinny(wdtype, M))
+        return 0;
+    if (wdtype != TSL_F32 && use_skinny(wdtype, M) &&
+        skinny_plan(items->data(), (int)items->size(), wdtype, M).resident)
         return 0;
     const size_t e = wdtype == TSL_F32 ? 4 : 2;
     const int64_t xa = wdtype == TSL_F32 ? 4 : 8; // row strides of 16 bytes

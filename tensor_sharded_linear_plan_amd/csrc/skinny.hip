@@ -51,6 +51,8 @@ struct SkinnyItem {
     int32_t accumulate, y_bf16;
     int32_t fset, fpos;  // member fpos of rank-sum set fset of the launch (-1: none)
     int64_t M;           // rows of this item
+    const int32_t *ridx; // row m reads X row ridx[m] (zeros outside [0, x_rows)); null: row m
+    int64_t x_rows;
 };
 
 // A sum set whose rank sum the streaming launch finishes itself: member r
@@ -252,8 +254,11 @@ struct SB {
 // ONE: a single token row (M == 1, resident activations): only the first
 // accumulator row of each lane is ever stored, so the group epilogue
 // updates that one alone.
-template <int WT, int MT, int NTW, bool XRES, bool ONE = false>
+template <int WT, int MT, int NTW, bool XRES, bool ONE = false, bool IDX = false>
 __global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
+    // IDX: items may read their rows through an index; only resident
+    // kernels stage rows that way (once per workgroup, through xload)
+    static_assert(!IDX || XRES, "rows through an index need the resident kernel");
     using S = SB<WT, MT>;
     // XRES: [M rows][xstr bytes] sized at launch; else two [ROWS][XROW] windows
     extern __shared__ __attribute__((aligned(16))) char xl[];
@@ -312,13 +317,28 @@ __global__ void __launch_bounds__(256) stream_kernel(SkinnyGroup grp) {
             }
     };
 
-    // 16 bytes of activations: row m0 + r, k .. k + 7 (zero past M and K)
+    // where row `row` of the product reads X: row ridx[row] when the item
+    // reads its rows through an index (null for an index outside
+    // [0, x_rows): a row of zeros)
     const uint16_t *X = static_cast<const uint16_t *>(a.X);
+    auto xsrc = [&](int64_t row) __attribute__((always_inline)) -> const uint16_t * {
+        const int64_t s = a.ridx[row];
+        return s >= 0 && s < a.x_rows ? X + s * a.ldx : nullptr;
+    };
+    // 16 bytes of activations: row m0 + r, k .. k + 7 (zero past M and K)
     auto xload = [&](int64_t r, int64_t k) __attribute__((always_inline)) {
         const int64_t row = m0 + r;
         u32x4 v = {0, 0, 0, 0};
         if (row < M) {
             const uint16_t *p = X + row * a.ldx + k;
+            if constexpr (IDX) {
+                if (a.ridx) {
+                    const uint16_t *x0 = xsrc(row);
+                    if (!x0)
+                        return v;
+                    p = x0 + k;
+                }
+            }
             if (k + 8 <= a.Ks) {
                 v = *reinterpret_cast<const u32x4 *>(p);
             } else if (k < a.Ks) {
@@ -727,7 +747,11 @@ SkinnyFn pick_stream_ntw(int ntw) {
 }
 
 template <int WT>
-SkinnyFn pick_stream(int mt, int ntw, bool resident, bool one) {
+SkinnyFn pick_stream(int mt, int ntw, bool resident, bool one, bool idx) {
+    if (resident && idx) // some item reads its rows through an index
+        return one && ntw == 1 ? stream_kernel<WT, 1, 1, true, true, true>
+               : ntw == 1      ? stream_kernel<WT, 1, 1, true, false, true>
+                               : stream_kernel<WT, 1, 2, true, false, true>;
     if (resident && one && ntw == 1)
         return stream_kernel<WT, 1, 1, true, true>;
     if (resident)
@@ -870,9 +894,16 @@ int64_t skinny_blocks(const SkinnyPlan &p, const LinearItem *items, int n) {
 
 hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, tsl_dtype wdtype,
                          int64_t M, void *workspace, hipStream_t stream) {
+    // items read through a row index only in resident calls (the caller
+    // gathers the rows of the others)
+    bool idx = false;
+    for (int i = 0; i < n; ++i)
+        idx = idx || items[i].ridx != nullptr;
+    if (idx && (!p.stream || !p.resident))
+        return hipErrorInvalidValue;
     SkinnyFn fn = wdtype == TSL_F32    ? pick_f32(p.mt)
-                  : wdtype == TSL_BF16 ? pick_stream<W_BF16>(p.mt, p.ntw, p.resident, M == 1)
-                                       : pick_stream<W_Q4>(p.mt, p.ntw, p.resident, M == 1);
+                  : wdtype == TSL_BF16 ? pick_stream<W_BF16>(p.mt, p.ntw, p.resident, M == 1, idx)
+                                       : pick_stream<W_Q4>(p.mt, p.ntw, p.resident, M == 1, idx);
     if (!fn)
         return hipErrorInvalidValue;
     for (int c0 = 0; c0 < n; c0 += kGroupMax) {
@@ -915,6 +946,8 @@ hipError_t launch_skinny(const SkinnyPlan &p, const LinearItem *items, int n, ts
             SkinnyItem &a = grp.it[i];
             a.B = L.packed;
             a.X = L.X;
+            a.ridx = L.ridx;
+            a.x_rows = L.x_rows;
             a.Y = L.Y;
             a.P = reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ws_off[c0 + i]);
             a.ldx = L.ldx;
