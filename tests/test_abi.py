@@ -315,6 +315,40 @@ def test_group_rejections_and_workspace(tsl_lib):
     call(good, M=0)
 
 
+def test_row_index_rules(tsl_lib):
+    """Items that read their rows through a row index: validation before
+    launch, and their workspace -- none where the kernels read through the
+    index (4-bit weights above 64 rows; a call of a few decode rows whose
+    activations stay in LDS), else a gathered copy per indexed item
+    (M x k_len, 2 bytes per element, rounded to 256 bytes)."""
+    K, N, M = 1024, 512, 256
+    sh = tsl_lib.plan_linear(K, N, 1, tsl_lib.COLUMN, 64)[0]
+    P, X, Y, R = 1 << 24, 1 << 26, 1 << 27, 1 << 28  # fake, aligned: never dereferenced
+    ws = tsl_lib.shard_linear_group_workspace_size
+
+    def item(wdtype=tsl_lib.Q4G64, **kw):
+        nb = tsl_lib.pack_shard_size(sh, wdtype)
+        return dict(dict(shard=sh, packed=P, packed_bytes=nb, X=X, ldx=K, Y=Y, ldy=N,
+                         row_index=R, x_rows=100), **kw)
+
+    plain = lambda wd, m: ws([dict(item(wd), row_index=None)], wd, m)
+    assert ws([item()], tsl_lib.Q4G64, M) == plain(tsl_lib.Q4G64, M)
+    assert ws([item()], tsl_lib.Q4G64, 2) == plain(tsl_lib.Q4G64, 2)
+    assert ws([item(tsl_lib.BF16)], tsl_lib.BF16, M) == plain(tsl_lib.BF16, M) + M * K * 2
+    call = lambda items, wd=tsl_lib.Q4G64, m=M: tsl_lib.shard_linear_group(
+        items, wd, tsl_lib.BF16, m)
+    cases = [(item(row_index=R + 2), tsl_lib.ERR_MISALIGNED),
+             (item(x_rows=0), tsl_lib.ERR_INVALID_ARG),
+             (item(x_rows=1 << 31), tsl_lib.ERR_INVALID_ARG),
+             (item(row_index=Y + 64), tsl_lib.ERR_INVALID_ARG),  # inside the output
+             (item(X=Y + N * 2 * M), tsl_lib.ERR_INVALID_ARG),   # X's 100 rows meet Y
+             (item(), tsl_lib.ERR_BUFFER_TOO_SMALL)]             # no workspace given
+    for it, status in cases:
+        with pytest.raises(tsl_lib.TslError) as e:
+            call([it])
+        assert e.value.status == status, it
+
+
 def test_group_output_overlap_rule(tsl_lib):
     """Items may write disjoint column blocks of one output (same stride);
     any shared element is rejected.  Checked with a group whose workspace is
