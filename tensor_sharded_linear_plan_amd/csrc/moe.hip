@@ -4,7 +4,9 @@
 // the ranks' shares add up like row-parallel partials).  One pass over the
 // output: thread (token t, 4 columns) walks the token's k slots in order
 // and accumulates weight * expert row with fused multiply-adds in
-// binary32, starting from -0.0.
+// binary32, starting from -0.0.  Eight slots at a time: their rows and
+// weights first, then the held slots' expert rows all in flight together,
+// then the adds in slot order.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -26,20 +28,41 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const float *__restric
 #pragma unroll
         for (int i = 0; i < V; ++i)
             acc[i] = -0.0f;
-        for (int s = 0; s < k; ++s) {
-            const int64_t r = slot_row[t * k + s];
-            if (r < 0 || r >= n_rows)
-                continue; // another rank's expert
-            const float w = weights[t * k + s];
-            const float *p = P + r * ldp + j;
-            if constexpr (V == 4) {
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
-                acc[0] = __builtin_fmaf(w, v.x, acc[0]);
-                acc[1] = __builtin_fmaf(w, v.y, acc[1]);
-                acc[2] = __builtin_fmaf(w, v.z, acc[2]);
-                acc[3] = __builtin_fmaf(w, v.w, acc[3]);
-            } else {
-                acc[0] = __builtin_fmaf(w, p[0], acc[0]);
+        constexpr int KU = 8;
+        for (int s0 = 0; s0 < k; s0 += KU) {
+            int64_t rr[KU];
+            float ww[KU];
+            bool held[KU];
+#pragma unroll
+            for (int u = 0; u < KU; ++u) {
+                const int s = s0 + u;
+                rr[u] = s < k ? slot_row[t * k + s] : -1;
+                held[u] = rr[u] >= 0 && rr[u] < n_rows; // else another rank's expert
+                ww[u] = held[u] ? weights[t * k + s] : 0.f;
+            }
+            float vv[KU][V];
+#pragma unroll
+            for (int u = 0; u < KU; ++u) {
+                if (!held[u])
+                    continue;
+                const float *p = P + rr[u] * ldp + j;
+                if constexpr (V == 4) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+                    vv[u][0] = v.x;
+                    vv[u][1] = v.y;
+                    vv[u][2] = v.z;
+                    vv[u][3] = v.w;
+                } else {
+                    vv[u][0] = p[0];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < KU; ++u) {
+                if (!held[u])
+                    continue;
+#pragma unroll
+                for (int i = 0; i < V; ++i)
+                    acc[i] = __builtin_fmaf(ww[u], vv[u][i], acc[i]);
             }
         }
         TY *y = Y + t * ldy + j;
