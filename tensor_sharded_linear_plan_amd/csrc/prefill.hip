@@ -16,7 +16,7 @@
 //     16-byte chunk, so a 32-column x 16-k MFMA fragment is two 512-byte
 //     runs.
 // A stage covers 64 k (32 k when three 64-k stages would not fit in 160 KB)
-// and stages rotate through S <= 4 LDS slots.  Fragment reads run one 16-k
+// and stages rotate through S <= 4 LDS slots (5 of 32 k).  Fragment reads run one 16-k
 // step ahead of the MFMAs.  The barrier that publishes stage k + 1 sits
 // before the last 16-k step of stage k: each wave first waits for its own
 // copies of stage k + 1 and for its own reads of stage k; after the barrier
@@ -108,7 +108,11 @@ struct G {
     static constexpr int NW = WM * WN;              // waves
     static constexpr int FPW = (AF + BF) / NW;      // copy instructions per wave per stage
     static constexpr int STAGE = (AF + BF) * 1024;
-    static constexpr int NS = kLdsLimit / STAGE >= 4 ? 4 : kLdsLimit / STAGE;
+    // slots: up to four 64-k stages, or five 32-k ones (the 256 x 256 tile:
+    // its weight copies, read from HBM, then start four stages ahead of
+    // their use -- gqa8 layer M = 512: 342-353 -> 333-338 us)
+    static constexpr int NSMAX = BK == 32 ? 5 : 4;
+    static constexpr int NS = kLdsLimit / STAGE >= NSMAX ? NSMAX : kLdsLimit / STAGE;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 tiles");
     static_assert(AF % NW == 0 && BF % NW == 0, "LDS blocks must divide over the waves");
     static_assert(NW % S16 == 0, "a wave's weight blocks keep one 16-k step");
@@ -278,7 +282,9 @@ __global__ void __launch_bounds__(64 * WM * WN)
     // copies (at most NS - 2) may still be in flight
     auto wait_stage = [&](int kt) __attribute__((always_inline)) {
         const int younger = nst - 1 - kt < C::NS - 2 ? nst - 1 - kt : C::NS - 2;
-        if (C::NS >= 4 && younger >= 2)
+        if (C::NS >= 5 && younger >= 3)
+            wait_vmcnt<C::FPW * 3>();
+        else if (C::NS >= 4 && younger >= 2)
             wait_vmcnt<C::FPW * 2>();
         else if (C::NS >= 3 && younger >= 1)
             wait_vmcnt<C::FPW>();
