@@ -125,15 +125,18 @@ def test_row_index_in_a_joined_sum_set(wdtype):
     assert t.equal(outs[0], outs[1])
 
 
-@pytest.mark.parametrize("T", [600, 8])
-def test_row_index_in_the_moe_layout(T):
-    """16 experts, top-2 routing, 4-bit weights, one rank holding 8
-    experts (about 75 rows each at T = 600: the GEMM regime; at most a few
-    at T = 8: decode-sized): every held expert's gate product reads its
-    tokens through
-    its run of moe_dispatch's row layout (row_slot / k) -- the same
-    outputs as moe_gather followed by the products over the gathered
-    rows."""
+@pytest.mark.parametrize("wdtype,T", [("q4", 600), ("q4", 8), ("q4", 160), ("bf16", 160),
+                                      ("bf16", 400)])
+def test_row_index_in_the_moe_layout(wdtype, T):
+    """16 experts, top-2 routing, one rank holding 8 experts: every held
+    expert's gate product reads its tokens through its run of
+    moe_dispatch's row layout (row_slot / k) -- the same outputs as
+    moe_gather followed by the products over the gathered rows.  4-bit
+    weights: about 75 rows an expert at T = 600 (the activation pass reads
+    through the index), at most a few at T = 8 (the resident streaming
+    kernel does), about 20 at T = 160 (windowed: the call gathers); bf16
+    weights: about 20 and 50 rows (the call gathers; the experts' runs
+    follow one another, so their gathers merge into one)."""
     t = torch()
     n_exp, k, H, F = 16, 2, 1024, 256
     rng = np.random.default_rng(9300 + T)
@@ -145,8 +148,14 @@ def test_row_index_in_the_moe_layout(T):
     X = dev(synth.normal_bf16(9301 + T, (T, H)))
     Xp = gathered(X, H, T, tsl.BF16, tok, R, H)
     sh = tsl.plan_linear(H, F, 1, tsl.COLUMN, 64)[0]
-    ws_ = [Q4Weight(H, F, 9310 + 3 * e, 9311 + 3 * e, 9312 + 3 * e) for e in held]
-    packs = [w.pack(sh) for w in ws_]
+    if wdtype == "q4":
+        code = tsl.Q4G64
+        ws_ = [Q4Weight(H, F, 9310 + 3 * e, 9311 + 3 * e, 9312 + 3 * e) for e in held]
+        packs = [w.pack(sh) for w in ws_]
+    else:
+        code = tsl.BF16
+        Ws = [dev(synth.normal_bf16(9310 + e, (H, F), 0.02)) for e in held]
+        packs = [pack(sh, tsl.BF16, W, F, 1) for W in Ws]
     Mmax = max(int(off[i + 1] - off[i]) for i in range(len(held)))
     Ya = t.full((R, F), float("nan"), dtype=t.float32, device="cuda")
     Yb = t.full((R, F), float("nan"), dtype=t.float32, device="cuda")
@@ -160,6 +169,6 @@ def test_row_index_in_the_moe_layout(T):
                        rows=rows, row_index=tok[o:], x_rows=T))
         ib.append(dict(shard=sh, packed=b, packed_bytes=nb, X=Xp[o:], ldx=H, Y=Yb[o:], ldy=F,
                        rows=rows))
-    run_group(ia, tsl.Q4G64, Mmax)
-    run_group(ib, tsl.Q4G64, Mmax)
-    assert t.equal(Ya, Yb)
+    run_group(ia, code, Mmax)
+    run_group(ib, code, Mmax)
+    assert t.equal(Ya, Yb), (wdtype, T, Mmax)
