@@ -8,8 +8,10 @@ outputs; the ranks' outputs are then summed (combine_partials).  Checked:
 the gathered rows bit for bit, gate/up rows and the joined output against
 the oracle (random draws max|y - r| / max|r| <= 2e-3, integer draws
 bit-exact), in both sharding modes, and at the moe30b size on sampled
-tokens and columns.  The activation between gate/up and down is not part of
-the path: down reads its own per-slot inputs.
+tokens and columns; each also with the products reading their rows
+through the routing's row index instead of gathered copies (as the bench
+does).  The activation between gate/up and down is not part of the path:
+down reads its own per-slot inputs.
 """
 import numpy as np
 import pytest
@@ -63,9 +65,11 @@ def inputs(c, T, integer):
     return X, H, topk, w
 
 
-def run_rank(c, ex, plan, r, T, dX, dH, topk, dw):
+def run_rank(c, ex, plan, r, T, dX, dH, topk, dw, via_index=False):
     """One rank's MoE products; returns (rows layout, gathered inputs, gate
-    and up rows, the rank's token outputs)."""
+    and up rows, the rank's token outputs).  via_index: the products read
+    their rows through the routing's row index (tsl_linear_item.row_index)
+    instead of the gathered copies."""
     t = torch()
     mine = [(e, sh) for e, rr, sh in plan if rr == r]
     held = [e for e, _ in mine]
@@ -95,14 +99,18 @@ def run_rank(c, ex, plan, r, T, dX, dH, topk, dw):
         if rows == 0:
             continue
         o = int(off[i])
+        xin = dict(X=dX, ldx=c.hidden, row_index=d_tok[o:], x_rows=T) if via_index else \
+            dict(X=Xp[o:], ldx=c.hidden)
+        hin = dict(X=dH[:, kd.k_off:], ldx=c.expert_ffn, row_index=d_slot[o:], x_rows=T * k) \
+            if via_index else dict(X=Hp[o:], ldx=kd.k_len)
         for p, Y in (("gate", G), ("up", U)):
             s = getattr(sh, p)
             buf, nb = ex.w[e, p].pack(s)
-            gu.append(dict(shard=s, packed=buf, packed_bytes=nb, X=Xp[o:], ldx=c.hidden,
-                           Y=Y[o:], ldy=f, rows=rows))
+            gu.append(dict(shard=s, packed=buf, packed_bytes=nb, Y=Y[o:], ldy=f, rows=rows,
+                           **xin))
         buf, nb = ex.w[e, "down"].pack(sh.down)
-        dn.append(dict(shard=sh.down, packed=buf, packed_bytes=nb, X=Hp[o:], ldx=kd.k_len,
-                       Y=P[o:], ldy=c.hidden, rows=rows))
+        dn.append(dict(shard=sh.down, packed=buf, packed_bytes=nb, Y=P[o:], ldy=c.hidden,
+                       rows=rows, **hin))
     Mmax = int(np.max(np.diff(off)))
     for items in (gu, dn):
         ws = tsl.shard_linear_group_workspace_size(items, tsl.Q4G64, Mmax)
@@ -120,10 +128,11 @@ def check(got, ref, integer, what):
         assert err <= TOL, "%s: %.3g" % (what, err)
 
 
+@pytest.mark.parametrize("via_index", [False, True], ids=["gathered", "row_index"])
 @pytest.mark.parametrize("integer", [False, True])
 @pytest.mark.parametrize("mode", [tsl.MOE_EXPERT_PARALLEL, tsl.MOE_WITHIN_EXPERT])
 @pytest.mark.parametrize("T", configs.MOE_SMALL.tokens)
-def test_moe_ranks_against_oracle(T, mode, integer):
+def test_moe_ranks_against_oracle(T, mode, integer, via_index):
     t = torch()
     c = configs.MOE_SMALL
     ex = Experts(c, integer)
@@ -138,7 +147,7 @@ def test_moe_ranks_against_oracle(T, mode, integer):
     hs = Hf.reshape(T, k, -1)
     parts = []
     for r in range(c.tp):
-        off, row_slot, Xp, G, U, Yr = run_rank(c, ex, plan, r, T, dX, dH, topk, dw)
+        off, row_slot, Xp, G, U, Yr = run_rank(c, ex, plan, r, T, dX, dH, topk, dw, via_index)
         specs = {e: s for e, rr, s in oplan if rr == r}
         if Xp is not None:
             # gathered inputs: bit for bit the token rows of each slot
@@ -169,9 +178,11 @@ def test_moe_ranks_against_oracle(T, mode, integer):
     check(host(Y), full, integer, "joined output")
 
 
-def test_moe30b_expert_parallel_sampled():
-    """moe30b prefill size, expert parallel: every rank's products; the
-    joined output on sampled tokens and columns."""
+@pytest.mark.parametrize("via_index", [False, True], ids=["gathered", "row_index"])
+def test_moe30b_expert_parallel_sampled(via_index):
+    """moe30b prefill size, expert parallel: every rank's products (rows
+    gathered first, or read through the routing's row index as the bench
+    does); the joined output on sampled tokens and columns."""
     t = torch()
     c = configs.MOE30B
     T = c.tokens[0]
@@ -184,7 +195,7 @@ def test_moe30b_expert_parallel_sampled():
     parts = []
     rng = synth.rng(606)
     for r in range(c.tp):
-        off, row_slot, Xp, G, U, Yr = run_rank(c, ex, plan, r, T, dX, dH, topk, dw)
+        off, row_slot, Xp, G, U, Yr = run_rank(c, ex, plan, r, T, dX, dH, topk, dw, via_index)
         parts.append(Yr)
         # gate rows of a sample: first and last rows of a few experts
         k = c.top_k
