@@ -6,7 +6,9 @@ shard_linear_group with a caller workspace on the same items (the same
 plan and kernels run; only the workspace address differs): a prefill-sized
 call (binary16 activation copies, a joined sum set) followed by a smaller,
 decode-sized call (k-partials and the in-launch rank-sum counters, in the
-array the first call left behind), then the first again.  On the CPU: a
+array the first call left behind), then the first again; and calls whose
+products read their rows through a row index (gathered into the array,
+or read by the activation pass).  On the CPU: a
 call whose workspace would not fit the array is rejected before any device
 work."""
 import re
@@ -101,3 +103,47 @@ def test_noalloc_matches_workspace_entry_point_on_consecutive_calls():
     _check_call(4, 1)
     print("noalloc: prefill-sized call again M=300", flush=True)
     _check_call(300, 2)
+
+
+def _indexed_check(wdtype, M, seed):
+    """Three column products reading X [150, 1024] through row indices
+    (two share one): the no-alloc call against the workspace call."""
+    from gpu_util import Q4Weight, dev, empty_bytes, pack, torch
+    t = torch()
+    K, N, x_rows = 1024, 256, 150
+    X = dev(synth.normal_bf16(seed, (x_rows, K)))
+    rng = np.random.default_rng(seed + 1)
+    idx = [dev(rng.integers(-2, x_rows + 2, M).astype(np.int32)) for _ in range(2)]
+    sh = tsl.plan_linear(K, N, 1, tsl.COLUMN, 64)[0]
+    if wdtype == tsl.Q4G64:
+        buf, nb = Q4Weight(K, N, seed + 2, seed + 3, seed + 4).pack(sh)
+    else:
+        buf, nb = pack(sh, tsl.BF16, dev(synth.normal_bf16(seed + 2, (K, N), 0.02)), N, 1)
+    outs = [[t.full((M, N), float("nan"), dtype=t.float32, device="cuda") for _ in range(3)]
+            for _ in range(2)]
+    items = [[dict(shard=sh, packed=buf, packed_bytes=nb, X=X, ldx=K, Y=Y, ldy=N,
+                   row_index=idx[w], x_rows=x_rows) for w, Y in zip((0, 0, 1), ys)]
+             for ys in outs]
+    ws = tsl.shard_linear_group_workspace_size(items[1], wdtype, M)
+    assert 0 < ws <= tsl.NOALLOC_SCRATCH_BYTES
+    tsl.shard_linear_group(items[1], wdtype, tsl.BF16, M, empty_bytes(ws), ws)
+    tsl.shard_linear_group_noalloc(items[0], wdtype, tsl.BF16, M)
+    t.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert not t.isnan(a).any()
+        assert t.equal(a.view(t.int32), b.view(t.int32)), (wdtype, M)
+
+
+@pytest.mark.gpu
+def test_noalloc_with_rows_read_through_an_index():
+    """Row-indexed products (some indices out of range): a decode-sized
+    bf16 call whose rows the call gathers into the fixed array, a
+    prefill-sized 4-bit call whose activation pass reads through the index,
+    then the first again -- each bit for bit the workspace entry point's
+    outputs."""
+    print("noalloc: row-indexed bf16 call M=24 (gathered)", flush=True)
+    _indexed_check(tsl.BF16, 24, 9500)
+    print("noalloc: row-indexed 4-bit call M=300", flush=True)
+    _indexed_check(tsl.Q4G64, 300, 9510)
+    print("noalloc: row-indexed bf16 call M=24 again", flush=True)
+    _indexed_check(tsl.BF16, 24, 9520)
